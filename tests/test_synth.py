@@ -1,0 +1,119 @@
+"""Synthetic input recipe and the oracle's batch plumbing -- CPU only."""
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+from conftest import to_np
+from sparse_self_speculative_pillarattn_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def test_topk_count_golden():
+    with open(os.path.join(GOLDEN, "topk_count.json")) as f:
+        g = json.load(f)
+    for c in g["cases"]:
+        assert synth.topk_count(c["L"], Fraction(c["s_num"], c["s_den"])) == c["K"], c
+
+
+def test_generator_is_deterministic():
+    a = synth.make_batch(synth.TINY)
+    b = synth.make_batch(synth.TINY)
+    for name in ("q", "k_pool", "v_pool", "page_table", "idx"):
+        assert torch.equal(getattr(a, name), getattr(b, name)), name
+    c = synth.make_batch(synth.TINY, seed=99)
+    assert not torch.equal(a.q, c.q)
+
+
+@pytest.mark.parametrize("w", synth.ORDERED[1:], ids=lambda w: w.name)
+def test_batch_composition(w):
+    """Verify share 1/(k+1); query rows close to (2k+1)/(k+1) * B (review,
+    观察 3 and the unified batch scheduler)."""
+    m = synth.make_meta(w)
+    B, k = w.batch, w.spec_k
+    assert sum(m.is_verify) == max(1, round(B / (k + 1)))
+    rows = m.q_indptr[-1]
+    assert abs(rows - (2 * k + 1) / (k + 1) * B) <= k + 1
+    assert m.num_slots == 2 * sum(m.seq_lens)
+    for r in range(B):
+        assert m.idx_count[r] == synth.topk_count(m.seq_lens[r], w.sparsity)
+
+
+def test_page_table_is_injective():
+    b = synth.make_batch(synth.TINY)
+    used = np.concatenate([to_np(b.page_table)[r, :b.seq_lens[r]] for r in range(b.B)])
+    assert len(np.unique(used)) == len(used)
+    assert used.min() >= 0 and used.max() < b.num_slots
+
+
+def test_draft_lists_hold_pillars_and_are_sorted():
+    b = synth.make_batch(synth.TINY)
+    for r in range(b.B):
+        if b.is_verify[r]:
+            continue
+        K = b.idx_count[r]
+        for g in range(synth.TINY.num_kv_heads):
+            lst = to_np(b.idx)[b.idx_off[r] + g * K: b.idx_off[r] + (g + 1) * K]
+            assert np.all(np.diff(lst) > 0)
+            assert set(b.pillar_pos[r][g].tolist()) <= set(lst.tolist())
+
+
+def _oracle_inputs(b):
+    return dict(k=b.w.spec_k, Hq=b.w.num_qo_heads, Hkv=b.w.num_kv_heads,
+                sm_scale=1.0 / np.sqrt(b.w.head_dim), is_verify=b.is_verify,
+                seq_lens=b.seq_lens, q_indptr=b.q_indptr, page_table=to_np(b.page_table),
+                q=to_np(b.q), k_pool=to_np(b.k_pool), v_pool=to_np(b.v_pool),
+                idx_count=b.idx_count, idx_off=b.idx_off, idx=to_np(b.idx),
+                logits_off=b.logits_off, logits_elems=b.logits_elems)
+
+
+def test_tiny_pillars_are_selected(oracle):
+    """Sanity of planting + oracle: every planted pillar of the verify request
+    is among its 13 selected positions per KV head."""
+    b = synth.make_batch(synth.TINY)
+    res = oracle.step(**_oracle_inputs(b))
+    for r in range(b.B):
+        if not b.is_verify[r]:
+            continue
+        K = b.idx_count[r]
+        for g in range(synth.TINY.num_kv_heads):
+            sel = res["idx"][b.idx_off[r] + g * K: b.idx_off[r] + (g + 1) * K]
+            assert set(b.pillar_pos[r][g].tolist()) <= set(sel.tolist())
+
+
+def test_step_equals_per_request_calls(oracle):
+    """The batched oracle routes every request's rows, logits and list
+    segments to the same places the single-request functions produce."""
+    w = synth.Workload(name="mix", batch=5, num_qo_heads=6, num_kv_heads=2, head_dim=32,
+                       dtype="bf16", spec_k=3, sparsity=Fraction(1, 10),
+                       lengths=("uniform", 20, 60), n_verify=2, seed=11)
+    b = synth.make_batch(w)
+    inp = _oracle_inputs(b)
+    res = oracle.step(**inp, nthreads=3)
+    q, kp, vp, pt = inp["q"], inp["k_pool"], inp["v_pool"], inp["page_table"]
+    for r in range(b.B):
+        L = b.seq_lens[r]
+        r0, r1 = b.q_indptr[r], b.q_indptr[r + 1]
+        if b.is_verify[r]:
+            lg, lse, o = oracle.verify_request(q[r0:r1], kp, vp, pt[r, :L], L, w.spec_k, 6, 2,
+                                               inp["sm_scale"])
+            assert np.array_equal(res["o"][r0:r1], o)
+            assert np.array_equal(res["lse"][r0:r1], lse)
+            off = b.logits_off[r]
+            assert np.array_equal(res["logits"][off:off + lg.size], lg.ravel())
+            pbar = oracle.average(lg, lse, 2, 1, w.spec_k)
+            K = b.idx_count[r]
+            for g in range(2):
+                sel = oracle.topk(pbar[g], K)
+                seg = res["idx"][b.idx_off[r] + g * K: b.idx_off[r] + (g + 1) * K]
+                assert np.array_equal(seg, sel)
+        else:
+            K = b.idx_count[r]
+            lst = inp["idx"][b.idx_off[r]: b.idx_off[r] + 2 * K].reshape(2, K)
+            o, lse = oracle.draft_request(q[r0], kp, vp, pt[r, :L], L, lst, 2, inp["sm_scale"])
+            assert np.array_equal(res["o"][r0], o)
+            assert np.array_equal(res["lse"][r0], lse)
