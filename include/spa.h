@@ -1,0 +1,160 @@
+/*
+ * spa.h -- C ABI of libspa: one unified draft/verify decode-attention step
+ * with PillarAttn critical-token selection, for AMD Instinct MI355X (gfx950).
+ *
+ * The method (pages: "SparseSpec-MLSys26" review on awesome-system-papers,
+ * section 核心方法 -> PillarAttn and "Unified batch scheduler + fused
+ * attention kernel"; marsggbo.github.io "SparseSpec" blog, sections 4.1-4.2):
+ *   - a verify request runs full causal attention for its k+1 query rows over
+ *     its whole paged context and keeps the attention logits and log-sum-exp;
+ *   - the exact scores exp(logit - LSE), averaged over the k draft rows and the
+ *     query heads of each GQA group, pick the top-K positions per KV head;
+ *   - a draft request attends only to the positions of its stored list;
+ *   - both kinds share one batch over a paged KV cache with page size 1.
+ *
+ * Conventions shared by every entry point
+ *   Ownership   The caller owns every buffer.  Device pointers (d_*) are HIP
+ *               device memory; host pointers (h_*) are ordinary host memory read
+ *               during the call only.  The library keeps one small pinned host
+ *               staging ring (allocated on first use) for the per-call work plan.
+ *   Layouts     (H_q query heads, H_kv KV heads, G = H_q / H_kv, d = head_dim,
+ *               element type per spa_layout.dtype: bf16 or fp32)
+ *               k_pool, v_pool  [num_slots][H_kv][d]; one slot holds one token.
+ *               page_table      int32 [B][page_table_stride]; entry [r][j] is the
+ *                               slot of token j of request r, valid for j < L_r
+ *                               and in [0, num_slots) (out-of-range slots are
+ *                               clamped, never dereferenced outside the pool).
+ *               q, o            [rows][H_q][d]; a verify request owns k+1
+ *                               consecutive rows (row i sits at absolute position
+ *                               L_r-(k+1)+i), a draft request one row.
+ *               lse             fp32 [rows][H_q], natural log.
+ *               logits          fp32; verify request r owns [(k+1)][H_q][L_r]
+ *                               starting at element h_logits_off[r]; entries for
+ *                               positions a row cannot see are -inf.
+ *               idx             int32; request r owns [H_kv][K_r] token positions
+ *                               (not slots) starting at element h_idx_off[r],
+ *                               ascending per KV head.
+ *   Semantics   Query head h reads KV head h / G.  Softmax scale sm_scale (0 means
+ *               1/sqrt(d)).  A list entry outside [0, L_r) is ignored; a row
+ *               whose list holds no valid entry gets O = 0 and LSE = -inf.
+ *               Top-K orders by (averaged score descending, position ascending).
+ *   Errors      Every entry point returns an spa_status.  Arguments are checked
+ *               on the host before anything is enqueued; on any non-OK return
+ *               nothing was enqueued and spa_last_error() describes why.
+ *   Streams     Work is enqueued on `stream` (a hipStream_t; NULL = default
+ *               stream) and the call returns without waiting.  Faults inside a
+ *               kernel surface at the caller's next synchronisation.
+ *   Workspace   d_ws/ws_bytes is caller-owned device scratch of at least
+ *               spa_workspace_bytes(...) bytes for the same batch; it holds the
+ *               uploaded work plan, split-K partials and averaged scores.  Calls
+ *               that share one workspace must be ordered on one stream.
+ *   Threads     Entry points may be called from several host threads.
+ *   B == 0      is a successful no-op.
+ */
+#ifndef SPA_H_
+#define SPA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SPA_ABI_VERSION 1
+
+typedef enum {
+  SPA_OK = 0,
+  SPA_ERR_INVALID_ARG = 1,         /* null pointer, bad size, bad offsets ...      */
+  SPA_ERR_UNSUPPORTED = 2,         /* head_dim, dtype or row count not built       */
+  SPA_ERR_WORKSPACE_TOO_SMALL = 3, /* ws_bytes < spa_workspace_bytes(...)          */
+  SPA_ERR_HIP = 4                  /* a HIP runtime call or launch failed          */
+} spa_status;
+
+typedef enum { SPA_BF16 = 0, SPA_F32 = 1 } spa_dtype;
+
+typedef struct {
+  int32_t num_qo_heads;      /* H_q, a multiple of num_kv_heads                     */
+  int32_t num_kv_heads;      /* H_kv                                               */
+  int32_t head_dim;          /* d: 64 or 128                                       */
+  float sm_scale;            /* softmax scale; 0 selects 1/sqrt(d)                 */
+  int32_t dtype;             /* spa_dtype of q, k_pool, v_pool and o              */
+  int64_t num_slots;         /* rows of k_pool / v_pool                            */
+  int32_t page_table_stride; /* int32 elements per page_table row (>= max L_r)    */
+} spa_layout;
+
+/* Library ABI version (SPA_ABI_VERSION of the build). */
+int32_t spa_abi_version(void);
+
+/* Message describing the last non-OK status returned on this host thread. */
+const char* spa_last_error(void);
+
+/* Workspace bytes needed by any entry point below for this batch.  h_is_verify
+ * may be NULL (all draft) and h_idx_count may be NULL for verify-only batches.
+ * Returns 0 when the arguments are invalid (spa_last_error() says why). */
+size_t spa_workspace_bytes(const spa_layout* layout, int32_t B, int32_t spec_k,
+                           const uint8_t* h_is_verify, const int32_t* h_seq_lens,
+                           const int32_t* h_idx_count);
+
+/* Full attention of B verify requests (k+1 rows each, rows r*(k+1)...), with
+ * the logits and LSE kept.  Review of SparseSpec, PillarAttn, third bullet:
+ * the verify kernel dumps attention logits and log-sum-exp on the fly.
+ * h_seq_lens[B]: L_r >= k+1.  h_logits_off[B]: element offsets, each segment
+ * (k+1)*H_q*L_r long and non-overlapping.  d_o [B(k+1)][H_q][d], d_lse
+ * [B(k+1)][H_q]. */
+int32_t spa_verify_attn(const spa_layout* layout, int32_t B, int32_t spec_k,
+                        const int32_t* h_seq_lens, const int32_t* d_page_table,
+                        const void* d_q, const void* d_k_pool, const void* d_v_pool, void* d_o,
+                        float* d_lse, float* d_logits, const int64_t* h_logits_off, void* d_ws,
+                        size_t ws_bytes, void* stream);
+
+/* PillarAttn selection for B verify requests.  Review of SparseSpec,
+ * PillarAttn, third and fourth bullets: exact scores exp(logit - LSE) are
+ * averaged over rows [avg_row_begin, avg_row_begin + avg_row_count) (the k
+ * draft rows are 1..k) and the G heads of each KV head, then the top
+ * h_topk[r] = K_r positions per KV head are written ascending to
+ * d_idx + h_idx_off[r] as [H_kv][K_r].  d_lse [B(k+1)][H_q]; logits as above. */
+int32_t spa_pillar_topk(int32_t B, int32_t spec_k, int32_t num_qo_heads, int32_t num_kv_heads,
+                        int32_t avg_row_begin, int32_t avg_row_count, const int32_t* h_seq_lens,
+                        const int32_t* h_topk, const float* d_logits,
+                        const int64_t* h_logits_off, const float* d_lse, int32_t* d_idx,
+                        const int64_t* h_idx_off, void* d_ws, size_t ws_bytes, void* stream);
+
+/* Sparse attention of B draft requests (one row each) over their stored lists.
+ * Review of SparseSpec, PillarAttn, first two bullets; blog section 4.1: a
+ * draft step attends only to the critical tokens.  h_idx_count[r] = list
+ * length n_r >= 1 per KV head, list at d_idx + h_idx_off[r] as [H_kv][n_r]. */
+int32_t spa_draft_attn(const spa_layout* layout, int32_t B, const int32_t* h_seq_lens,
+                       const int32_t* d_page_table, const int32_t* h_idx_count,
+                       const int64_t* h_idx_off, const int32_t* d_idx, const void* d_q,
+                       const void* d_k_pool, const void* d_v_pool, void* d_o, float* d_lse,
+                       void* d_ws, size_t ws_bytes, void* stream);
+
+/* One mixed batch: verify requests (h_is_verify[r] != 0) run spa_verify_attn
+ * then spa_pillar_topk semantics and overwrite their own idx segment (K_r =
+ * h_idx_count[r] entries per KV head); draft requests run spa_draft_attn over
+ * the segment they own.  All attention work of both kinds goes through one
+ * kernel launch.  Review of SparseSpec, "Unified batch scheduler + fused
+ * attention kernel": sparse and full attention share one pipeline over
+ * page-size-1 paged KV and requests of both kinds mix freely.  h_q_indptr[B+1]
+ * gives each request's first q row; counts must be k+1 (verify) or 1 (draft).
+ * h_logits_off[r] is read for verify requests only. */
+int32_t spa_unified_step(const spa_layout* layout, int32_t B, int32_t spec_k,
+                         const uint8_t* h_is_verify, const int32_t* h_seq_lens,
+                         const int32_t* h_q_indptr, const int32_t* d_page_table,
+                         const void* d_q, const void* d_k_pool, const void* d_v_pool,
+                         const int32_t* h_idx_count, const int64_t* h_idx_off, int32_t* d_idx,
+                         void* d_o, float* d_lse, float* d_logits, const int64_t* h_logits_off,
+                         int32_t avg_row_begin, int32_t avg_row_count, void* d_ws,
+                         size_t ws_bytes, void* stream);
+
+/* Process-wide split-K chunk sizes (tokens per verify work item, list entries
+ * per draft work item); 0 restores the automatic choice.  Results do not
+ * depend on them beyond floating-point summation order. */
+int32_t spa_set_split(int32_t verify_chunk_tokens, int32_t draft_chunk_entries);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPA_H_ */

@@ -1,0 +1,210 @@
+"""ctypes binding of libspa (include/spa.h): argument marshalling only.
+
+Device buffers are PyTorch tensors on the current HIP device; host metadata are
+Python sequences or numpy arrays.  Every call enqueues on the current PyTorch
+stream of the tensors' device and returns without synchronising.  The library
+must be built (``python -m sparse_self_speculative_pillarattn_amd.build``);
+there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libspa.so")
+
+SPA_OK = 0
+SPA_ERR_INVALID_ARG = 1
+SPA_ERR_UNSUPPORTED = 2
+SPA_ERR_WORKSPACE_TOO_SMALL = 3
+SPA_ERR_HIP = 4
+SPA_BF16 = 0
+SPA_F32 = 1
+
+EXPORTED = ("spa_abi_version", "spa_last_error", "spa_workspace_bytes", "spa_verify_attn",
+            "spa_pillar_topk", "spa_draft_attn", "spa_unified_step", "spa_set_split")
+
+
+class SpaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"libspa status {status}: {msg}")
+        self.status = status
+
+
+class SpaLayout(C.Structure):
+    _fields_ = [("num_qo_heads", C.c_int32), ("num_kv_heads", C.c_int32),
+                ("head_dim", C.c_int32), ("sm_scale", C.c_float), ("dtype", C.c_int32),
+                ("num_slots", C.c_int64), ("page_table_stride", C.c_int32)]
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load libspa.so; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with "
+                          "`python -m sparse_self_speculative_pillarattn_amd.build`")
+    lib = C.CDLL(path)
+    vp, i32, i64, sz = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t
+    L = C.POINTER(SpaLayout)
+    lib.spa_abi_version.restype = i32
+    lib.spa_last_error.restype = C.c_char_p
+    lib.spa_set_split.argtypes = [i32, i32]
+    lib.spa_set_split.restype = i32
+    lib.spa_workspace_bytes.argtypes = [L, i32, i32, vp, vp, vp]
+    lib.spa_workspace_bytes.restype = sz
+    lib.spa_verify_attn.argtypes = [L, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.spa_verify_attn.restype = i32
+    lib.spa_pillar_topk.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp,
+                                    sz, vp]
+    lib.spa_pillar_topk.restype = i32
+    lib.spa_draft_attn.argtypes = [L, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.spa_draft_attn.restype = i32
+    lib.spa_unified_step.argtypes = [L, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                     vp, vp, i32, i32, vp, sz, vp]
+    lib.spa_unified_step.restype = i32
+    _lib = lib
+    return lib
+
+
+def _check(rc: int):
+    if rc != SPA_OK:
+        raise SpaError(rc, load().spa_last_error().decode())
+
+
+class _Host:
+    """Keeps host arrays alive for the duration of one call."""
+
+    def __init__(self):
+        self.keep = []
+
+    def arr(self, seq, dtype):
+        if seq is None:
+            return None
+        a = np.ascontiguousarray(np.asarray(seq, dtype=dtype))
+        self.keep.append(a)
+        return a.ctypes.data_as(C.c_void_p)
+
+
+def _dptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("device buffers must be GPU tensors")
+    if not t.is_contiguous():
+        raise ValueError("device buffers must be contiguous")
+    return C.c_void_p(t.data_ptr())
+
+
+def _stream(t: torch.Tensor):
+    return C.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def layout(num_qo_heads: int, num_kv_heads: int, head_dim: int, dtype: torch.dtype,
+           num_slots: int, page_table_stride: int, sm_scale: float = 0.0) -> SpaLayout:
+    code = {torch.bfloat16: SPA_BF16, torch.float32: SPA_F32}.get(dtype)
+    if code is None:
+        raise ValueError(f"unsupported dtype {dtype}")
+    return SpaLayout(num_qo_heads, num_kv_heads, head_dim, float(sm_scale), code, int(num_slots),
+                     int(page_table_stride))
+
+
+def abi_version() -> int:
+    return load().spa_abi_version()
+
+
+def set_split(verify_chunk_tokens: int = 0, draft_chunk_entries: int = 0):
+    _check(load().spa_set_split(int(verify_chunk_tokens), int(draft_chunk_entries)))
+
+
+def workspace_bytes(lay: SpaLayout, B: int, spec_k: int, is_verify: Optional[Sequence] ,
+                    seq_lens: Sequence, idx_count: Optional[Sequence]) -> int:
+    h = _Host()
+    n = load().spa_workspace_bytes(C.byref(lay), int(B), int(spec_k), h.arr(is_verify, np.uint8),
+                                   h.arr(seq_lens, np.int32), h.arr(idx_count, np.int32))
+    if n == 0 and B > 0:
+        msg = load().spa_last_error().decode()
+        if msg:
+            raise SpaError(SPA_ERR_INVALID_ARG, msg)
+    return int(n)
+
+
+def verify_attn(lay, B, spec_k, seq_lens, page_table, q, k_pool, v_pool, o, lse, logits,
+                logits_off, ws: torch.Tensor):
+    h = _Host()
+    _check(load().spa_verify_attn(
+        C.byref(lay), int(B), int(spec_k), h.arr(seq_lens, np.int32), _dptr(page_table), _dptr(q),
+        _dptr(k_pool), _dptr(v_pool), _dptr(o), _dptr(lse), _dptr(logits),
+        h.arr(logits_off, np.int64), _dptr(ws), ws.numel() * ws.element_size(), _stream(q)))
+
+
+def pillar_topk(B, spec_k, num_qo_heads, num_kv_heads, avg_row_begin, avg_row_count, seq_lens,
+                topk, logits, logits_off, lse, idx, idx_off, ws: torch.Tensor):
+    h = _Host()
+    _check(load().spa_pillar_topk(
+        int(B), int(spec_k), int(num_qo_heads), int(num_kv_heads), int(avg_row_begin),
+        int(avg_row_count), h.arr(seq_lens, np.int32), h.arr(topk, np.int32), _dptr(logits),
+        h.arr(logits_off, np.int64), _dptr(lse), _dptr(idx), h.arr(idx_off, np.int64), _dptr(ws),
+        ws.numel() * ws.element_size(), _stream(logits)))
+
+
+def draft_attn(lay, B, seq_lens, page_table, idx_count, idx_off, idx, q, k_pool, v_pool, o, lse,
+               ws: torch.Tensor):
+    h = _Host()
+    _check(load().spa_draft_attn(
+        C.byref(lay), int(B), h.arr(seq_lens, np.int32), _dptr(page_table),
+        h.arr(idx_count, np.int32), h.arr(idx_off, np.int64), _dptr(idx), _dptr(q),
+        _dptr(k_pool), _dptr(v_pool), _dptr(o), _dptr(lse), _dptr(ws),
+        ws.numel() * ws.element_size(), _stream(q)))
+
+
+def unified_step(lay, B, spec_k, is_verify, seq_lens, q_indptr, page_table, q, k_pool, v_pool,
+                 idx_count, idx_off, idx, o, lse, logits, logits_off, ws: torch.Tensor,
+                 avg_row_begin: int = 1, avg_row_count: Optional[int] = None):
+    h = _Host()
+    avg_row_count = spec_k if avg_row_count is None else avg_row_count
+    _check(load().spa_unified_step(
+        C.byref(lay), int(B), int(spec_k), h.arr(is_verify, np.uint8), h.arr(seq_lens, np.int32),
+        h.arr(q_indptr, np.int32), _dptr(page_table), _dptr(q), _dptr(k_pool), _dptr(v_pool),
+        h.arr(idx_count, np.int32), h.arr(idx_off, np.int64), _dptr(idx), _dptr(o), _dptr(lse),
+        _dptr(logits), h.arr(logits_off, np.int64), int(avg_row_begin), int(avg_row_count),
+        _dptr(ws), ws.numel() * ws.element_size(), _stream(q)))
+
+
+# --------------------------------------------------------------------------- #
+# convenience: run one synthetic batch through the unified step
+# --------------------------------------------------------------------------- #
+class StepBuffers:
+    """Output and workspace tensors for one synthetic batch (see synth.Batch)."""
+
+    def __init__(self, batch, avg_row_begin: int = 1, avg_row_count: Optional[int] = None):
+        w = batch.w
+        dev = batch.q.device
+        self.batch = batch
+        self.lay = layout(w.num_qo_heads, w.num_kv_heads, w.head_dim, batch.q.dtype,
+                          batch.num_slots, batch.stride)
+        self.o = torch.empty_like(batch.q)
+        self.lse = torch.empty((batch.rows, w.num_qo_heads), dtype=torch.float32, device=dev)
+        self.logits = torch.empty((batch.logits_elems,), dtype=torch.float32, device=dev)
+        self.idx = batch.idx.clone()
+        self.avg_row_begin = avg_row_begin
+        self.avg_row_count = w.spec_k if avg_row_count is None else avg_row_count
+        nbytes = workspace_bytes(self.lay, batch.B, w.spec_k, batch.is_verify, batch.seq_lens,
+                                 batch.idx_count)
+        self.ws = torch.empty((max(nbytes, 256),), dtype=torch.uint8, device=dev)
+
+    def step(self):
+        b = self.batch
+        unified_step(self.lay, b.B, b.w.spec_k, b.is_verify, b.seq_lens, b.q_indptr,
+                     b.page_table, b.q, b.k_pool, b.v_pool, b.idx_count, b.idx_off, self.idx,
+                     self.o, self.lse, self.logits, [max(x, 0) for x in b.logits_off], self.ws,
+                     self.avg_row_begin, self.avg_row_count)

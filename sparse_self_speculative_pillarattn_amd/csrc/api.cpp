@@ -1,0 +1,655 @@
+// api.cpp -- host side of libspa: argument checks, work planning, plan upload
+// and kernel launches behind the C ABI of include/spa.h.
+//
+// A call turns the host metadata into a work plan (per-request descriptors,
+// attention work items, split-K merge groups, selection jobs), copies it into
+// the head of the caller's workspace through a pinned staging ring, and
+// enqueues at most four kernels: attention, merge, averaging, selection.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "spa.h"
+#include "spa_kernels.h"
+#include "spa_plan.h"
+
+using namespace spa;
+
+namespace {
+
+thread_local std::string g_err;
+std::atomic<int32_t> g_verify_chunk{0};
+std::atomic<int32_t> g_draft_chunk{0};
+
+constexpr int DEFAULT_VERIFY_CHUNK = 512;
+constexpr int DEFAULT_DRAFT_CHUNK = 1024;
+
+int32_t fail(int32_t code, const std::string& msg) {
+  g_err = msg;
+  return code;
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+struct Req {
+  int32_t L = 0;
+  bool verify = false;
+  int32_t row0 = 0;
+  int32_t nlist = 0;      // draft: entries per KV head; verify: K_r
+  int64_t logits_off = 0;
+  int64_t idx_off = 0;
+};
+
+struct Plan {
+  std::vector<ReqDesc> reqs;
+  std::vector<WorkItem> items;
+  std::vector<MergeItem> merges;
+  std::vector<TopkItem> topk;
+  std::vector<AvgItem> avg;
+  int64_t part_rows = 0;
+  int64_t pbar_elems = 0;
+  size_t off_reqs = 0, off_items = 0, off_merge = 0, off_topk = 0, off_avg = 0;
+  size_t plan_bytes = 0, off_part_o = 0, off_part_ml = 0, off_pbar = 0, total = 0;
+  int nthr = 256;
+  size_t smem = 0;
+};
+
+struct Shape {
+  int Hq = 0, Hkv = 0, G = 0, d = 0, dtype = 0, k = 0;
+  int64_t num_slots = 0;
+  int32_t stride = 0;
+  float scale = 0.f;
+};
+
+int group_template(int G) { return G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : G <= 5 ? 5 : 8; }
+
+int32_t check_layout(const spa_layout* lay, Shape* s) {
+  if (!lay) return fail(SPA_ERR_INVALID_ARG, "layout is NULL");
+  if (lay->num_qo_heads <= 0 || lay->num_kv_heads <= 0)
+    return fail(SPA_ERR_INVALID_ARG, "head counts must be positive");
+  if (lay->num_qo_heads % lay->num_kv_heads != 0)
+    return fail(SPA_ERR_INVALID_ARG, "num_qo_heads must be a multiple of num_kv_heads");
+  if (lay->num_kv_heads > 255) return fail(SPA_ERR_UNSUPPORTED, "num_kv_heads above 255");
+  if (lay->head_dim != 64 && lay->head_dim != 128)
+    return fail(SPA_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (lay->dtype != SPA_BF16 && lay->dtype != SPA_F32)
+    return fail(SPA_ERR_UNSUPPORTED, "dtype must be SPA_BF16 or SPA_F32");
+  if (lay->num_slots <= 0) return fail(SPA_ERR_INVALID_ARG, "num_slots must be positive");
+  if (lay->num_slots > 0x7fffffffLL) return fail(SPA_ERR_UNSUPPORTED, "num_slots above 2^31-1");
+  if (lay->page_table_stride <= 0)
+    return fail(SPA_ERR_INVALID_ARG, "page_table_stride must be positive");
+  if (!(lay->sm_scale >= 0.f) || std::isinf(lay->sm_scale))
+    return fail(SPA_ERR_INVALID_ARG, "sm_scale must be finite and >= 0");
+  s->Hq = lay->num_qo_heads;
+  s->Hkv = lay->num_kv_heads;
+  s->G = s->Hq / s->Hkv;
+  s->d = lay->head_dim;
+  s->dtype = lay->dtype;
+  s->num_slots = lay->num_slots;
+  s->stride = lay->page_table_stride;
+  s->scale = lay->sm_scale > 0.f ? lay->sm_scale : 1.f / std::sqrt((float)lay->head_dim);
+  return SPA_OK;
+}
+
+// Segments [off, off+len) must be non-negative and pairwise disjoint.
+int32_t check_segments(std::vector<std::pair<int64_t, int64_t>> seg, const char* what) {
+  for (auto& x : seg)
+    if (x.first < 0) return fail(SPA_ERR_INVALID_ARG, std::string(what) + ": negative offset");
+  std::sort(seg.begin(), seg.end());
+  for (size_t i = 1; i < seg.size(); ++i)
+    if (seg[i - 1].first + seg[i - 1].second > seg[i].first)
+      return fail(SPA_ERR_INVALID_ARG, std::string(what) + ": overlapping segments");
+  return SPA_OK;
+}
+
+int verify_chunk() {
+  int v = g_verify_chunk.load();
+  return v > 0 ? std::min(v, VERIFY_MAX_CHUNK) : DEFAULT_VERIFY_CHUNK;
+}
+int draft_chunk() {
+  int v = g_draft_chunk.load();
+  return v > 0 ? std::min(v, DRAFT_MAX_CHUNK) : DEFAULT_DRAFT_CHUNK;
+}
+
+// Attention (and optionally selection) plan for the requests in `rq`.
+int32_t build_plan(const Shape& s, const std::vector<Req>& rq, bool attn, bool topk,
+                   int avg_begin, int avg_count, Plan* pl) {
+  const int B = (int)rq.size();
+  const int G = s.G, Hkv = s.Hkv, D = s.d;
+  const int rows_v = s.k + 1;
+  const bool bf16 = s.dtype == SPA_BF16;
+  const int CV = verify_chunk(), CD = draft_chunk();
+  if (s.k > 255) return fail(SPA_ERR_UNSUPPORTED, "spec_k above 255");
+  pl->reqs.resize(B);
+  bool any_verify = false;
+  for (int r = 0; r < B; ++r) {
+    ReqDesc& d = pl->reqs[r];
+    d.L = rq[r].L;
+    d.row0 = rq[r].row0;
+    d.kind = rq[r].verify ? KIND_VERIFY : KIND_DRAFT;
+    d.list_len = rq[r].nlist;
+    d.off = rq[r].verify ? rq[r].logits_off : rq[r].idx_off;
+    d.nsplit = 1;
+    d.part_row0 = 0;
+    d.pad_ = 0;
+    any_verify |= rq[r].verify;
+  }
+  if (attn) {
+    // verify requests first (longest first), then drafts (longest list first):
+    // the dispatcher hands out workgroups in index order, so the big items start early
+    std::vector<int> order(B);
+    for (int r = 0; r < B; ++r) order[r] = r;
+    std::stable_sort(order.begin(), order.end(), [&](int a, int b) {
+      if (rq[a].verify != rq[b].verify) return rq[a].verify;
+      const int la = rq[a].verify ? rq[a].L : rq[a].nlist;
+      const int lb = rq[b].verify ? rq[b].L : rq[b].nlist;
+      return la > lb;
+    });
+    int64_t part_rows = 0;
+    for (int r : order) {
+      ReqDesc& d = pl->reqs[r];
+      const bool v = rq[r].verify;
+      const int span = v ? rq[r].L : rq[r].nlist;
+      const int chunk = v ? CV : CD;
+      const int ns = std::max(1, (span + chunk - 1) / chunk);
+      d.nsplit = ns;
+      const int Rr = (v ? rows_v : 1) * G;
+      if (ns > 1) {
+        d.part_row0 = part_rows;
+        part_rows += (int64_t)Hkv * ns * Rr;
+        for (int g = 0; g < Hkv; ++g) pl->merges.push_back(MergeItem{r, g});
+      }
+      const int nq = (v && !bf16) ? rows_v : 1;  // fp32 verify: one item per query row
+      for (int g = 0; g < Hkv; ++g)
+        for (int sidx = 0; sidx < ns; ++sidx)
+          for (int qi = 0; qi < nq; ++qi) {
+            WorkItem w;
+            w.r = r;
+            w.g = (uint8_t)g;
+            w.qi = (uint8_t)qi;
+            w.split = (uint16_t)sidx;
+            w.begin = sidx * chunk;
+            w.end = std::min(span, (sidx + 1) * chunk);
+            pl->items.push_back(w);
+          }
+    }
+    pl->part_rows = part_rows;
+  }
+  if (topk && any_verify) {
+    int64_t pbar = 0;
+    for (int r = 0; r < B; ++r) {
+      if (!rq[r].verify) continue;
+      for (int g = 0; g < Hkv; ++g) {
+        TopkItem t;
+        t.r = r;
+        t.g = g;
+        t.L = rq[r].L;
+        t.K = rq[r].nlist;
+        t.pbar_off = pbar;
+        t.idx_off = rq[r].idx_off + (int64_t)g * rq[r].nlist;
+        t.logits_off = rq[r].logits_off;
+        t.lse_row0 = rq[r].row0;
+        t.pad_ = 0;
+        const int ti = (int)pl->topk.size();
+        pl->topk.push_back(t);
+        for (int j0 = 0; j0 < t.L; j0 += AVG_SPAN) pl->avg.push_back(AvgItem{ti, j0});
+        pbar += rq[r].L;
+      }
+    }
+    pl->pbar_elems = pbar;
+  }
+  (void)avg_begin;
+  (void)avg_count;
+  // block shape and LDS of the attention launch
+  int nthr = 256;
+  size_t smem = 0;
+  const int GM = group_template(G);
+  bool need_valu = false, need_mfma = false;
+  for (int r = 0; r < B && attn; ++r) {
+    if (rq[r].verify && bf16) need_mfma = true;
+    else need_valu = true;
+  }
+  if (need_mfma) {
+    const int nt = (rows_v * G + 15) / 16;
+    if (nt > MAX_ROW_TILES)
+      return fail(SPA_ERR_UNSUPPORTED, "(k+1)*G above 128 rows per KV head on the MFMA path");
+    nthr = 64 * std::max(4, nt);
+    const size_t mf = (size_t)VERIFY_TILE * (D / 8) * 16 + (size_t)D * (VERIFY_TILE + 8) * 2 +
+                      (size_t)VERIFY_MAX_CHUNK * 4;
+    smem = std::max(smem, mf);
+  }
+  if (need_valu) {
+    if (G > MAX_GROUP) return fail(SPA_ERR_UNSUPPORTED, "GQA group above 8 on the gather path");
+    const int E = bf16 ? 8 : 4;
+    const int LPR = D / E;
+    const int TB = (nthr / LPR) * 4;
+    const size_t va = (size_t)DRAFT_MAX_CHUNK * 4 + (size_t)GM * TB * 4 + 3 * GM * 4 +
+                      (size_t)(nthr / 64) * GM * D * 4;
+    smem = std::max(smem, va);
+  }
+  pl->nthr = nthr;
+  pl->smem = smem;
+  // workspace layout
+  size_t o = 0;
+  pl->off_reqs = o;
+  o = align_up(o + pl->reqs.size() * sizeof(ReqDesc), 256);
+  pl->off_items = o;
+  o = align_up(o + pl->items.size() * sizeof(WorkItem), 256);
+  pl->off_merge = o;
+  o = align_up(o + pl->merges.size() * sizeof(MergeItem), 256);
+  pl->off_topk = o;
+  o = align_up(o + pl->topk.size() * sizeof(TopkItem), 256);
+  pl->off_avg = o;
+  o = align_up(o + pl->avg.size() * sizeof(AvgItem), 256);
+  pl->plan_bytes = o;
+  pl->off_part_o = o;
+  o = align_up(o + (size_t)pl->part_rows * D * 4, 256);
+  pl->off_part_ml = o;
+  o = align_up(o + (size_t)pl->part_rows * 2 * 4, 256);
+  pl->off_pbar = o;
+  o = align_up(o + (size_t)pl->pbar_elems * 4, 256);
+  pl->total = o;
+  return SPA_OK;
+}
+
+// ---- pinned staging ring for plan uploads ---------------------------------
+struct StageSlot {
+  void* host = nullptr;
+  size_t cap = 0;
+  hipEvent_t ev = nullptr;
+  bool pending = false;
+};
+constexpr int RING = 32;
+std::mutex g_ring_mu;
+StageSlot g_ring[RING];
+unsigned g_ring_next = 0;
+
+int32_t upload_plan(const Plan& pl, void* d_ws, hipStream_t st) {
+  if (pl.plan_bytes == 0) return SPA_OK;
+  std::lock_guard<std::mutex> lock(g_ring_mu);
+  StageSlot& s = g_ring[g_ring_next++ % RING];
+  hipError_t e;
+  if (s.pending) {
+    e = hipEventSynchronize(s.ev);
+    if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("staging wait: ") + hipGetErrorString(e));
+    s.pending = false;
+  }
+  if (!s.ev) {
+    e = hipEventCreateWithFlags(&s.ev, hipEventDisableTiming);
+    if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("event create: ") + hipGetErrorString(e));
+  }
+  if (s.cap < pl.plan_bytes) {
+    if (s.host) (void)hipHostFree(s.host);
+    s.host = nullptr;
+    s.cap = 0;
+    const size_t want = std::max<size_t>(pl.plan_bytes * 2, 1 << 16);
+    e = hipHostMalloc(&s.host, want, hipHostMallocDefault);
+    if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("pinned staging: ") + hipGetErrorString(e));
+    s.cap = want;
+  }
+  char* h = static_cast<char*>(s.host);
+  std::memset(h, 0, pl.plan_bytes);
+  if (!pl.reqs.empty()) std::memcpy(h + pl.off_reqs, pl.reqs.data(), pl.reqs.size() * sizeof(ReqDesc));
+  if (!pl.items.empty()) std::memcpy(h + pl.off_items, pl.items.data(), pl.items.size() * sizeof(WorkItem));
+  if (!pl.merges.empty()) std::memcpy(h + pl.off_merge, pl.merges.data(), pl.merges.size() * sizeof(MergeItem));
+  if (!pl.topk.empty()) std::memcpy(h + pl.off_topk, pl.topk.data(), pl.topk.size() * sizeof(TopkItem));
+  if (!pl.avg.empty()) std::memcpy(h + pl.off_avg, pl.avg.data(), pl.avg.size() * sizeof(AvgItem));
+  e = hipMemcpyAsync(d_ws, h, pl.plan_bytes, hipMemcpyHostToDevice, st);
+  if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("plan upload: ") + hipGetErrorString(e));
+  e = hipEventRecord(s.ev, st);
+  if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("event record: ") + hipGetErrorString(e));
+  s.pending = true;
+  return SPA_OK;
+}
+
+struct Buffers {
+  const int32_t* page_table = nullptr;
+  const void* q = nullptr;
+  const void* k_pool = nullptr;
+  const void* v_pool = nullptr;
+  const int32_t* idx_in = nullptr;
+  int32_t* idx_out = nullptr;
+  void* o = nullptr;
+  float* lse = nullptr;
+  float* logits = nullptr;
+};
+
+int32_t run(const Shape& s, const Plan& pl, const Buffers& b, bool attn, bool topk, int avg_begin,
+            int avg_count, void* d_ws, size_t ws_bytes, hipStream_t st) {
+  if (ws_bytes < pl.total)
+    return fail(SPA_ERR_WORKSPACE_TOO_SMALL,
+                "workspace of " + std::to_string(ws_bytes) + " bytes, need " + std::to_string(pl.total));
+  if (pl.total > 0 && !d_ws) return fail(SPA_ERR_INVALID_ARG, "d_ws is NULL");
+  int32_t rc = upload_plan(pl, d_ws, st);
+  if (rc) return rc;
+  char* ws = static_cast<char*>(d_ws);
+  const ReqDesc* reqs = reinterpret_cast<const ReqDesc*>(ws + pl.off_reqs);
+  float* part_o = reinterpret_cast<float*>(ws + pl.off_part_o);
+  float* part_ml = reinterpret_cast<float*>(ws + pl.off_part_ml);
+  hipError_t e;
+  if (attn && !pl.items.empty()) {
+    AttnParams p;
+    p.q = b.q;
+    p.k_pool = b.k_pool;
+    p.v_pool = b.v_pool;
+    p.page_table = b.page_table;
+    p.pt_stride = s.stride;
+    p.num_slots = s.num_slots;
+    p.idx = b.idx_in;
+    p.o = b.o;
+    p.lse = b.lse;
+    p.logits = b.logits;
+    p.reqs = reqs;
+    p.items = reinterpret_cast<const WorkItem*>(ws + pl.off_items);
+    p.part_o = part_o;
+    p.part_ml = part_ml;
+    p.Hq = s.Hq;
+    p.Hkv = s.Hkv;
+    p.G = s.G;
+    p.k = s.k;
+    p.sm_scale = s.scale;
+    e = launch_attn(p, s.dtype, s.d, (int)pl.items.size(), pl.nthr, pl.smem, st);
+    if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("attention launch: ") + hipGetErrorString(e));
+    if (!pl.merges.empty()) {
+      MergeParams mp;
+      mp.reqs = reqs;
+      mp.items = reinterpret_cast<const MergeItem*>(ws + pl.off_merge);
+      mp.part_o = part_o;
+      mp.part_ml = part_ml;
+      mp.o = b.o;
+      mp.lse = b.lse;
+      mp.Hq = s.Hq;
+      mp.G = s.G;
+      mp.k = s.k;
+      e = launch_merge(mp, s.dtype, s.d, (int)pl.merges.size(), st);
+      if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("merge launch: ") + hipGetErrorString(e));
+    }
+  }
+  if (topk && !pl.topk.empty()) {
+    AvgParams ap;
+    ap.topk = reinterpret_cast<const TopkItem*>(ws + pl.off_topk);
+    ap.avg = reinterpret_cast<const AvgItem*>(ws + pl.off_avg);
+    ap.logits = b.logits;
+    ap.lse = b.lse;
+    ap.pbar = reinterpret_cast<float*>(ws + pl.off_pbar);
+    ap.Hq = s.Hq;
+    ap.G = s.G;
+    ap.row_begin = avg_begin;
+    ap.row_count = avg_count;
+    SelectParams sp;
+    sp.topk = ap.topk;
+    sp.pbar = ap.pbar;
+    sp.idx = b.idx_out;
+    e = launch_topk(ap, (int)pl.avg.size(), sp, (int)pl.topk.size(), st);
+    if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("top-K launch: ") + hipGetErrorString(e));
+  }
+  return SPA_OK;
+}
+
+int32_t check_avg_rows(int k, int G, int begin, int count) {
+  if (begin < 0 || count < 1 || begin + count > k + 1)
+    return fail(SPA_ERR_INVALID_ARG, "averaged rows must lie in [0, k]");
+  if (count * G > MAX_AVG_TERMS)
+    return fail(SPA_ERR_UNSUPPORTED, "averaged rows times GQA group above 512");
+  return SPA_OK;
+}
+
+// Shared request checks.  verify: L >= k+1 and K in [1, L]; draft: list >= 1.
+int32_t collect(const Shape& s, int B, const uint8_t* is_verify, const int32_t* seq_lens,
+                const int32_t* q_indptr, const int32_t* counts, const int64_t* idx_off,
+                const int64_t* logits_off, bool need_logits, bool need_idx,
+                std::vector<Req>* out) {
+  out->resize(B);
+  int32_t row = q_indptr ? q_indptr[0] : 0;
+  if (row < 0) return fail(SPA_ERR_INVALID_ARG, "q_indptr[0] is negative");
+  for (int r = 0; r < B; ++r) {
+    Req& q = (*out)[r];
+    q.verify = is_verify ? is_verify[r] != 0 : false;
+    q.L = seq_lens[r];
+    if (q.L < 1) return fail(SPA_ERR_INVALID_ARG, "seq_lens[" + std::to_string(r) + "] < 1");
+    if (q.L > s.stride)
+      return fail(SPA_ERR_INVALID_ARG, "seq_lens[" + std::to_string(r) + "] exceeds page_table_stride");
+    if (q.verify && q.L < s.k + 1)
+      return fail(SPA_ERR_INVALID_ARG, "verify request " + std::to_string(r) + " shorter than k+1");
+    const int rows = q.verify ? s.k + 1 : 1;
+    if (q_indptr) {
+      if (q_indptr[r + 1] - q_indptr[r] != rows)
+        return fail(SPA_ERR_INVALID_ARG, "q_indptr row count of request " + std::to_string(r) +
+                                             " must be " + std::to_string(rows));
+      q.row0 = q_indptr[r];
+    } else {
+      q.row0 = row;
+      row += rows;
+    }
+    if (counts) {
+      q.nlist = counts[r];
+      if (q.verify && (q.nlist < 1 || q.nlist > q.L))
+        return fail(SPA_ERR_INVALID_ARG, "top-K count of request " + std::to_string(r) + " outside [1, L]");
+      if (!q.verify && q.nlist < 1)
+        return fail(SPA_ERR_INVALID_ARG, "index list of request " + std::to_string(r) + " is empty");
+    }
+    q.idx_off = idx_off ? idx_off[r] : 0;
+    q.logits_off = (logits_off && q.verify) ? logits_off[r] : 0;
+  }
+  if (need_idx) {
+    std::vector<std::pair<int64_t, int64_t>> seg;
+    for (auto& q : *out) seg.push_back({q.idx_off, (int64_t)s.Hkv * q.nlist});
+    int32_t rc = check_segments(seg, "idx offsets");
+    if (rc) return rc;
+  }
+  if (need_logits) {
+    std::vector<std::pair<int64_t, int64_t>> seg;
+    for (auto& q : *out)
+      if (q.verify) seg.push_back({q.logits_off, (int64_t)(s.k + 1) * s.Hq * q.L});
+    int32_t rc = check_segments(seg, "logits offsets");
+    if (rc) return rc;
+  }
+  return SPA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t spa_abi_version(void) { return SPA_ABI_VERSION; }
+
+const char* spa_last_error(void) { return g_err.c_str(); }
+
+int32_t spa_set_split(int32_t verify_chunk_tokens, int32_t draft_chunk_entries) {
+  if (verify_chunk_tokens < 0 || draft_chunk_entries < 0)
+    return fail(SPA_ERR_INVALID_ARG, "split sizes must be >= 0");
+  if (verify_chunk_tokens > VERIFY_MAX_CHUNK || draft_chunk_entries > DRAFT_MAX_CHUNK)
+    return fail(SPA_ERR_INVALID_ARG, "split sizes above 2048");
+  g_verify_chunk.store(verify_chunk_tokens);
+  g_draft_chunk.store(draft_chunk_entries);
+  return SPA_OK;
+}
+
+size_t spa_workspace_bytes(const spa_layout* layout, int32_t B, int32_t spec_k,
+                           const uint8_t* h_is_verify, const int32_t* h_seq_lens,
+                           const int32_t* h_idx_count) {
+  Shape s;
+  if (check_layout(layout, &s)) return 0;
+  if (B < 0) {
+    fail(SPA_ERR_INVALID_ARG, "B < 0");
+    return 0;
+  }
+  if (B == 0) return 0;
+  if (!h_seq_lens) {
+    fail(SPA_ERR_INVALID_ARG, "h_seq_lens is NULL");
+    return 0;
+  }
+  bool any_v = false;
+  for (int r = 0; r < B && h_is_verify; ++r) any_v |= h_is_verify[r] != 0;
+  if (any_v && spec_k < 1) {
+    fail(SPA_ERR_INVALID_ARG, "spec_k < 1");
+    return 0;
+  }
+  s.k = std::max(spec_k, 0);
+  std::vector<int32_t> counts(B);
+  for (int r = 0; r < B; ++r) counts[r] = h_idx_count ? h_idx_count[r] : 1;
+  std::vector<Req> rq;
+  if (collect(s, B, h_is_verify, h_seq_lens, nullptr, counts.data(), nullptr, nullptr, false,
+              false, &rq))
+    return 0;
+  Plan pl;
+  if (build_plan(s, rq, true, true, 1, std::max(1, s.k), &pl)) return 0;
+  return pl.total;
+}
+
+int32_t spa_verify_attn(const spa_layout* layout, int32_t B, int32_t spec_k,
+                        const int32_t* h_seq_lens, const int32_t* d_page_table, const void* d_q,
+                        const void* d_k_pool, const void* d_v_pool, void* d_o, float* d_lse,
+                        float* d_logits, const int64_t* h_logits_off, void* d_ws,
+                        size_t ws_bytes, void* stream) {
+  Shape s;
+  int32_t rc = check_layout(layout, &s);
+  if (rc) return rc;
+  if (B < 0) return fail(SPA_ERR_INVALID_ARG, "B < 0");
+  if (spec_k < 1) return fail(SPA_ERR_INVALID_ARG, "spec_k < 1");
+  if (B == 0) return SPA_OK;
+  if (!h_seq_lens || !d_page_table || !d_q || !d_k_pool || !d_v_pool || !d_o || !d_lse ||
+      !d_logits || !h_logits_off)
+    return fail(SPA_ERR_INVALID_ARG, "a required pointer is NULL");
+  s.k = spec_k;
+  std::vector<uint8_t> ver(B, 1);
+  std::vector<Req> rq;
+  rc = collect(s, B, ver.data(), h_seq_lens, nullptr, nullptr, nullptr, h_logits_off, true, false,
+               &rq);
+  if (rc) return rc;
+  Plan pl;
+  rc = build_plan(s, rq, true, false, 1, spec_k, &pl);
+  if (rc) return rc;
+  Buffers b;
+  b.page_table = d_page_table;
+  b.q = d_q;
+  b.k_pool = d_k_pool;
+  b.v_pool = d_v_pool;
+  b.o = d_o;
+  b.lse = d_lse;
+  b.logits = d_logits;
+  return run(s, pl, b, true, false, 1, spec_k, d_ws, ws_bytes, static_cast<hipStream_t>(stream));
+}
+
+int32_t spa_pillar_topk(int32_t B, int32_t spec_k, int32_t num_qo_heads, int32_t num_kv_heads,
+                        int32_t avg_row_begin, int32_t avg_row_count, const int32_t* h_seq_lens,
+                        const int32_t* h_topk, const float* d_logits,
+                        const int64_t* h_logits_off, const float* d_lse, int32_t* d_idx,
+                        const int64_t* h_idx_off, void* d_ws, size_t ws_bytes, void* stream) {
+  if (num_qo_heads <= 0 || num_kv_heads <= 0 || num_qo_heads % num_kv_heads != 0)
+    return fail(SPA_ERR_INVALID_ARG, "head counts must be positive with H_q % H_kv == 0");
+  if (B < 0) return fail(SPA_ERR_INVALID_ARG, "B < 0");
+  if (spec_k < 1) return fail(SPA_ERR_INVALID_ARG, "spec_k < 1");
+  Shape s;
+  s.Hq = num_qo_heads;
+  s.Hkv = num_kv_heads;
+  s.G = num_qo_heads / num_kv_heads;
+  s.d = 128;
+  s.k = spec_k;
+  s.stride = 0x7fffffff;
+  int32_t rc = check_avg_rows(spec_k, s.G, avg_row_begin, avg_row_count);
+  if (rc) return rc;
+  if (B == 0) return SPA_OK;
+  if (!h_seq_lens || !h_topk || !d_logits || !h_logits_off || !d_lse || !d_idx || !h_idx_off)
+    return fail(SPA_ERR_INVALID_ARG, "a required pointer is NULL");
+  std::vector<uint8_t> ver(B, 1);
+  std::vector<Req> rq;
+  rc = collect(s, B, ver.data(), h_seq_lens, nullptr, h_topk, h_idx_off, h_logits_off, true, true,
+               &rq);
+  if (rc) return rc;
+  Plan pl;
+  rc = build_plan(s, rq, false, true, avg_row_begin, avg_row_count, &pl);
+  if (rc) return rc;
+  Buffers b;
+  b.logits = const_cast<float*>(d_logits);
+  b.lse = const_cast<float*>(d_lse);
+  b.idx_out = d_idx;
+  return run(s, pl, b, false, true, avg_row_begin, avg_row_count, d_ws, ws_bytes,
+             static_cast<hipStream_t>(stream));
+}
+
+int32_t spa_draft_attn(const spa_layout* layout, int32_t B, const int32_t* h_seq_lens,
+                       const int32_t* d_page_table, const int32_t* h_idx_count,
+                       const int64_t* h_idx_off, const int32_t* d_idx, const void* d_q,
+                       const void* d_k_pool, const void* d_v_pool, void* d_o, float* d_lse,
+                       void* d_ws, size_t ws_bytes, void* stream) {
+  Shape s;
+  int32_t rc = check_layout(layout, &s);
+  if (rc) return rc;
+  if (B < 0) return fail(SPA_ERR_INVALID_ARG, "B < 0");
+  if (B == 0) return SPA_OK;
+  if (!h_seq_lens || !d_page_table || !h_idx_count || !h_idx_off || !d_idx || !d_q ||
+      !d_k_pool || !d_v_pool || !d_o || !d_lse)
+    return fail(SPA_ERR_INVALID_ARG, "a required pointer is NULL");
+  s.k = 0;
+  std::vector<Req> rq;
+  rc = collect(s, B, nullptr, h_seq_lens, nullptr, h_idx_count, h_idx_off, nullptr, false, true,
+               &rq);
+  if (rc) return rc;
+  Plan pl;
+  rc = build_plan(s, rq, true, false, 0, 1, &pl);
+  if (rc) return rc;
+  Buffers b;
+  b.page_table = d_page_table;
+  b.q = d_q;
+  b.k_pool = d_k_pool;
+  b.v_pool = d_v_pool;
+  b.idx_in = d_idx;
+  b.o = d_o;
+  b.lse = d_lse;
+  return run(s, pl, b, true, false, 0, 1, d_ws, ws_bytes, static_cast<hipStream_t>(stream));
+}
+
+int32_t spa_unified_step(const spa_layout* layout, int32_t B, int32_t spec_k,
+                         const uint8_t* h_is_verify, const int32_t* h_seq_lens,
+                         const int32_t* h_q_indptr, const int32_t* d_page_table,
+                         const void* d_q, const void* d_k_pool, const void* d_v_pool,
+                         const int32_t* h_idx_count, const int64_t* h_idx_off, int32_t* d_idx,
+                         void* d_o, float* d_lse, float* d_logits, const int64_t* h_logits_off,
+                         int32_t avg_row_begin, int32_t avg_row_count, void* d_ws,
+                         size_t ws_bytes, void* stream) {
+  Shape s;
+  int32_t rc = check_layout(layout, &s);
+  if (rc) return rc;
+  if (B < 0) return fail(SPA_ERR_INVALID_ARG, "B < 0");
+  if (spec_k < 1) return fail(SPA_ERR_INVALID_ARG, "spec_k < 1");
+  rc = check_avg_rows(spec_k, s.G, avg_row_begin, avg_row_count);
+  if (rc) return rc;
+  if (B == 0) return SPA_OK;
+  if (!h_is_verify || !h_seq_lens || !h_q_indptr || !d_page_table || !d_q || !d_k_pool ||
+      !d_v_pool || !h_idx_count || !h_idx_off || !d_idx || !d_o || !d_lse)
+    return fail(SPA_ERR_INVALID_ARG, "a required pointer is NULL");
+  bool any_v = false;
+  for (int r = 0; r < B; ++r) any_v |= h_is_verify[r] != 0;
+  if (any_v && (!d_logits || !h_logits_off))
+    return fail(SPA_ERR_INVALID_ARG, "verify requests need d_logits and h_logits_off");
+  s.k = spec_k;
+  std::vector<Req> rq;
+  rc = collect(s, B, h_is_verify, h_seq_lens, h_q_indptr, h_idx_count, h_idx_off, h_logits_off,
+               any_v, true, &rq);
+  if (rc) return rc;
+  Plan pl;
+  rc = build_plan(s, rq, true, true, avg_row_begin, avg_row_count, &pl);
+  if (rc) return rc;
+  Buffers b;
+  b.page_table = d_page_table;
+  b.q = d_q;
+  b.k_pool = d_k_pool;
+  b.v_pool = d_v_pool;
+  b.idx_in = d_idx;
+  b.idx_out = d_idx;
+  b.o = d_o;
+  b.lse = d_lse;
+  b.logits = d_logits;
+  return run(s, pl, b, true, true, avg_row_begin, avg_row_count, d_ws, ws_bytes,
+             static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

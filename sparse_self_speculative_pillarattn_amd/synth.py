@@ -128,6 +128,13 @@ class Batch:
     def rows(self) -> int:
         return self.q_indptr[-1]
 
+    def to(self, device) -> "Batch":
+        """A copy whose tensors live on ``device`` (host metadata is shared)."""
+        from dataclasses import replace
+        return replace(self, q=self.q.to(device), k_pool=self.k_pool.to(device),
+                       v_pool=self.v_pool.to(device), page_table=self.page_table.to(device),
+                       idx=self.idx.to(device))
+
 
 def _torch_dtype(name: str):
     return {"bf16": torch.bfloat16, "f32": torch.float32}[name]

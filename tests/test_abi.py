@@ -1,0 +1,165 @@
+"""libspa loads, exports what include/spa.h declares, and rejects bad
+arguments on the host before anything is enqueued -- CPU only (no device
+pointer is dereferenced on these paths, so fake non-null addresses stand in)."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+from sparse_self_speculative_pillarattn_amd import binding as bd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = C.c_void_p(0x1000)  # never dereferenced on the paths below
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return bd.load()
+
+
+def declared_symbols():
+    src = open(os.path.join(ROOT, "include", "spa.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(spa_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_symbols()
+    assert set(names) == set(bd.EXPORTED), names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_abi_version(lib):
+    assert lib.spa_abi_version() == 1
+
+
+def _lay(**kw):
+    d = dict(num_qo_heads=8, num_kv_heads=2, head_dim=128, sm_scale=0.0, dtype=0,
+             num_slots=4096, page_table_stride=512)
+    d.update(kw)
+    return bd.SpaLayout(**d)
+
+
+def _arr(a, dt):
+    a = np.ascontiguousarray(np.asarray(a, dtype=dt))
+    return a, a.ctypes.data_as(C.c_void_p)
+
+
+def _unified(lib, lay, B=2, k=4, ver=(1, 0), lens=(100, 50), indptr=(0, 5, 6), counts=(5, 3),
+             ioff=(0, 10), loff=(0, 0), ws_bytes=1 << 30, avg=(1, 4), null=()):
+    ver_a, ver_p = _arr(ver, np.uint8)
+    len_a, len_p = _arr(lens, np.int32)
+    ind_a, ind_p = _arr(indptr, np.int32)
+    cnt_a, cnt_p = _arr(counts, np.int32)
+    io_a, io_p = _arr(ioff, np.int64)
+    lo_a, lo_p = _arr(loff, np.int64)
+    args = dict(ver=ver_p, lens=len_p, indptr=ind_p, pt=FAKE, q=FAKE, kp=FAKE, vp=FAKE,
+                cnt=cnt_p, ioff=io_p, idx=FAKE, o=FAKE, lse=FAKE, logits=FAKE, loff=lo_p,
+                ws=FAKE)
+    for n in null:
+        args[n] = None
+    return lib.spa_unified_step(C.byref(lay), B, k, args["ver"], args["lens"], args["indptr"],
+                                args["pt"], args["q"], args["kp"], args["vp"], args["cnt"],
+                                args["ioff"], args["idx"], args["o"], args["lse"], args["logits"],
+                                args["loff"], avg[0], avg[1], args["ws"], ws_bytes, None)
+
+
+def test_valid_arguments_reach_workspace_check(lib):
+    rc = _unified(lib, _lay(), ws_bytes=0)
+    assert rc == bd.SPA_ERR_WORKSPACE_TOO_SMALL
+    assert b"workspace" in lib.spa_last_error()
+
+
+def test_empty_batch_is_a_noop(lib):
+    assert _unified(lib, _lay(), B=0, ws_bytes=0) == bd.SPA_OK
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(lay=dict(num_qo_heads=6, num_kv_heads=4)), bd.SPA_ERR_INVALID_ARG),
+    (dict(lay=dict(num_kv_heads=0)), bd.SPA_ERR_INVALID_ARG),
+    (dict(lay=dict(head_dim=96)), bd.SPA_ERR_UNSUPPORTED),
+    (dict(lay=dict(dtype=7)), bd.SPA_ERR_UNSUPPORTED),
+    (dict(lay=dict(num_slots=0)), bd.SPA_ERR_INVALID_ARG),
+    (dict(lay=dict(page_table_stride=64)), bd.SPA_ERR_INVALID_ARG),   # L exceeds stride
+    (dict(lay=dict(sm_scale=-1.0)), bd.SPA_ERR_INVALID_ARG),
+    (dict(B=-1), bd.SPA_ERR_INVALID_ARG),
+    (dict(k=0), bd.SPA_ERR_INVALID_ARG),
+    (dict(lens=(3, 50)), bd.SPA_ERR_INVALID_ARG),          # verify shorter than k+1
+    (dict(lens=(100, 0)), bd.SPA_ERR_INVALID_ARG),         # empty context
+    (dict(counts=(0, 3)), bd.SPA_ERR_INVALID_ARG),         # K_r < 1
+    (dict(counts=(101, 3)), bd.SPA_ERR_INVALID_ARG),       # K_r > L_r
+    (dict(counts=(5, 0)), bd.SPA_ERR_INVALID_ARG),         # empty draft list
+    (dict(indptr=(0, 4, 5)), bd.SPA_ERR_INVALID_ARG),      # verify must own k+1 rows
+    (dict(indptr=(0, 5, 7)), bd.SPA_ERR_INVALID_ARG),      # draft must own 1 row
+    (dict(ioff=(0, 5)), bd.SPA_ERR_INVALID_ARG),           # overlapping idx segments
+    (dict(ioff=(-2, 10)), bd.SPA_ERR_INVALID_ARG),         # negative offset
+    (dict(loff=(-1, 0)), bd.SPA_ERR_INVALID_ARG),          # negative logits offset
+    (dict(avg=(0, 6)), bd.SPA_ERR_INVALID_ARG),            # rows beyond k
+    (dict(avg=(1, 0)), bd.SPA_ERR_INVALID_ARG),
+    (dict(null=("q",)), bd.SPA_ERR_INVALID_ARG),
+    (dict(null=("ws",), ws_bytes=1 << 30), bd.SPA_ERR_INVALID_ARG),
+    (dict(null=("logits",)), bd.SPA_ERR_INVALID_ARG),
+    (dict(lay=dict(num_qo_heads=160, num_kv_heads=8), ioff=(0, 100)),
+     bd.SPA_ERR_UNSUPPORTED),  # G = 20 rows exceed the MFMA tile budget
+])
+def test_unified_step_rejects(lib, kw, code):
+    lay = _lay(**kw.pop("lay", {}))
+    assert _unified(lib, lay, **kw) == code
+    assert lib.spa_last_error()
+
+
+def test_two_verifies_need_disjoint_logits(lib):
+    rc = _unified(lib, _lay(), ver=(1, 1), indptr=(0, 5, 10), counts=(5, 3), loff=(0, 100),
+                  lens=(100, 50))
+    assert rc == bd.SPA_ERR_INVALID_ARG
+    assert b"logits" in lib.spa_last_error()
+
+
+def test_workspace_bytes_matches_call_requirement(lib):
+    lay = _lay()
+    ver = np.array([1, 0], np.uint8)
+    lens = np.array([100, 50], np.int32)
+    cnt = np.array([5, 3], np.int32)
+    need = lib.spa_workspace_bytes(C.byref(lay), 2, 4, ver.ctypes.data_as(C.c_void_p),
+                                   lens.ctypes.data_as(C.c_void_p), cnt.ctypes.data_as(C.c_void_p))
+    assert need > 0
+    assert _unified(lib, lay, ws_bytes=need - 1) == bd.SPA_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_set_split_bounds(lib):
+    assert lib.spa_set_split(-1, 0) == bd.SPA_ERR_INVALID_ARG
+    assert lib.spa_set_split(4096, 0) == bd.SPA_ERR_INVALID_ARG
+    assert lib.spa_set_split(0, 0) == bd.SPA_OK
+
+
+def test_other_entry_points_validate(lib):
+    lay = _lay()
+    lens, lp = _arr([100, 80], np.int32)
+    lo, lop = _arr([0, 4000], np.int64)
+    # verify-only: k+1 rows per request, L >= k+1
+    assert lib.spa_verify_attn(C.byref(lay), 2, 0, lp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                               lop, FAKE, 0, None) == bd.SPA_ERR_INVALID_ARG
+    assert lib.spa_verify_attn(C.byref(lay), 2, 4, lp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                               lop, FAKE, 0, None) == bd.SPA_ERR_WORKSPACE_TOO_SMALL
+    # top-K: K within [1, L], rows within [0, k]
+    kk, kp = _arr([5, 81], np.int32)
+    io, iop = _arr([0, 100], np.int64)
+    assert lib.spa_pillar_topk(2, 4, 8, 2, 1, 4, lp, kp, FAKE, lop, FAKE, FAKE, iop, FAKE, 0,
+                               None) == bd.SPA_ERR_INVALID_ARG
+    kk, kp = _arr([5, 8], np.int32)
+    assert lib.spa_pillar_topk(2, 4, 8, 2, 1, 5, lp, kp, FAKE, lop, FAKE, FAKE, iop, FAKE, 0,
+                               None) == bd.SPA_ERR_INVALID_ARG
+    assert lib.spa_pillar_topk(2, 4, 8, 3, 1, 4, lp, kp, FAKE, lop, FAKE, FAKE, iop, FAKE, 0,
+                               None) == bd.SPA_ERR_INVALID_ARG
+    assert lib.spa_pillar_topk(2, 4, 8, 2, 1, 4, lp, kp, FAKE, lop, FAKE, FAKE, iop, FAKE, 0,
+                               None) == bd.SPA_ERR_WORKSPACE_TOO_SMALL
+    # draft-only: non-empty lists, disjoint segments
+    cnt, cp = _arr([4, 0], np.int32)
+    assert lib.spa_draft_attn(C.byref(lay), 2, lp, FAKE, cp, iop, FAKE, FAKE, FAKE, FAKE, FAKE,
+                              FAKE, FAKE, 0, None) == bd.SPA_ERR_INVALID_ARG
+    cnt, cp = _arr([4, 4], np.int32)
+    assert lib.spa_draft_attn(C.byref(lay), 2, lp, FAKE, cp, iop, FAKE, FAKE, FAKE, FAKE, FAKE,
+                              FAKE, FAKE, 0, None) == bd.SPA_ERR_WORKSPACE_TOO_SMALL

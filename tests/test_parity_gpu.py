@@ -1,0 +1,229 @@
+"""HIP path against the oracle on seeded inputs -- needs an MI355X.
+
+Every case runs through the C ABI (binding -> libspa.so) and compares O, LSE,
+logits and the selected lists with the oracle element by element (tolerances in
+parity.py)."""
+from dataclasses import replace
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+from conftest import to_np, widen
+import parity
+from sparse_self_speculative_pillarattn_amd import binding as bd
+from sparse_self_speculative_pillarattn_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(autouse=True)
+def _default_split():
+    bd.set_split(0, 0)
+    yield
+    bd.set_split(0, 0)
+
+
+def run_unified(b, avg_row_begin=1, avg_row_count=None):
+    bufs = bd.StepBuffers(b, avg_row_begin, avg_row_count)
+    bufs.logits.fill_(float("nan"))
+    bufs.o.fill_(float("nan"))
+    bufs.lse.fill_(float("nan"))
+    bufs.step()
+    torch.cuda.synchronize()
+    return {"o": bufs.o, "lse": bufs.lse, "logits": bufs.logits, "idx": bufs.idx}
+
+
+def check(oracle, w, seed=0, avg_row_begin=1, avg_row_count=None, **kw):
+    b = synth.make_batch(w, seed=seed, **kw)
+    print(f"[case] {w.name} seed={seed} lens={b.seq_lens} verify={b.is_verify}", flush=True)
+    ref = oracle.step(**parity.oracle_inputs(b, avg_row_begin, avg_row_count))
+    gpu = run_unified(b.to(DEV), avg_row_begin, avg_row_count)
+    parity.compare_step(oracle, b, gpu, ref, avg_row_begin, avg_row_count)
+    return b, gpu, ref
+
+
+def test_tiny_fp32_workload(oracle):
+    check(oracle, synth.TINY)
+
+
+MIXED = [
+    # (H_q, H_kv, d, k, lengths)
+    (4, 2, 64, 4, ("uniform", 20, 300)),
+    (8, 8, 128, 1, ("uniform", 2, 200)),
+    (16, 8, 128, 8, ("uniform", 60, 700)),
+    (32, 8, 128, 8, ("uniform", 500, 1500)),
+    (40, 8, 128, 12, ("uniform", 13, 1200)),
+    (16, 2, 128, 4, ("uniform", 100, 2100)),
+    (8, 1, 64, 8, ("uniform", 9, 400)),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("shape", MIXED, ids=lambda s: f"h{s[0]}kv{s[1]}d{s[2]}k{s[3]}")
+def test_mixed_batch(oracle, shape, dtype):
+    Hq, Hkv, d, k, lengths = shape
+    w = synth.Workload(name=f"mix-{Hq}-{Hkv}-{d}-{k}-{dtype}", batch=7, num_qo_heads=Hq,
+                       num_kv_heads=Hkv, head_dim=d, dtype=dtype, spec_k=k,
+                       sparsity=Fraction(1, 20), lengths=lengths, n_verify=3, seed=21)
+    check(oracle, w)
+
+
+@pytest.mark.parametrize("L", [9, 63, 64, 65, 127, 129, 1000, 2049])
+def test_ragged_lengths(oracle, L):
+    w = synth.Workload(name=f"ragged-{L}", batch=3, num_qo_heads=32, num_kv_heads=8,
+                       head_dim=128, dtype="bf16", spec_k=8, sparsity=Fraction(1, 20),
+                       lengths=("fixed", L), n_verify=1, seed=L)
+    check(oracle, w)
+
+
+@pytest.mark.parametrize("split", [(64, 16), (2048, 2048), (320, 100)])
+def test_split_invariance(oracle, split):
+    bd.set_split(*split)
+    w = synth.Workload(name="split", batch=6, num_qo_heads=32, num_kv_heads=8, head_dim=128,
+                       dtype="bf16", spec_k=8, sparsity=Fraction(1, 5),
+                       lengths=("uniform", 900, 2600), n_verify=2, seed=5)
+    check(oracle, w)
+
+
+def test_topk_count_extremes(oracle):
+    """K = 1 and K = L per verify request."""
+    w = synth.Workload(name="kext", batch=2, num_qo_heads=8, num_kv_heads=2, head_dim=128,
+                       dtype="bf16", spec_k=4, sparsity=Fraction(1, 1), lengths=("fixed", 300),
+                       n_verify=2, seed=3)
+    b = synth.make_batch(w)
+    b.idx_count[1] = 1
+    b.idx_off[1] = b.idx_off[0] + w.num_kv_heads * b.idx_count[0]
+    ref = oracle.step(**parity.oracle_inputs(b))
+    gpu = run_unified(b.to(DEV))
+    parity.compare_step(oracle, b, gpu, ref)
+    seg = to_np(gpu["idx"])[:w.num_kv_heads * 300].reshape(w.num_kv_heads, 300)
+    assert np.array_equal(seg, np.tile(np.arange(300), (w.num_kv_heads, 1)))
+
+
+def test_averaged_rows_parameter(oracle):
+    """The averaged rows are a parameter: all k+1 rows, and rows 0..k-1."""
+    w = synth.Workload(name="avg", batch=4, num_qo_heads=16, num_kv_heads=4, head_dim=128,
+                       dtype="bf16", spec_k=6, sparsity=Fraction(1, 10),
+                       lengths=("uniform", 200, 900), n_verify=2, seed=8)
+    check(oracle, w, avg_row_begin=0, avg_row_count=7)
+    check(oracle, w, avg_row_begin=0, avg_row_count=6)
+
+
+def _draft_only(oracle, b, lists, counts):
+    """Run spa_draft_attn on B draft rows with explicit lists; compare with the oracle."""
+    w = b.w
+    Hkv = w.num_kv_heads
+    offs = np.concatenate([[0], np.cumsum([Hkv * c for c in counts])[:-1]]).astype(np.int64)
+    flat = np.concatenate([np.asarray(l, np.int32).ravel() for l in lists])
+    dq = b.q[:len(counts)].contiguous()
+    lay = bd.layout(w.num_qo_heads, Hkv, w.head_dim, b.q.dtype, b.num_slots, b.stride)
+    o = torch.full_like(dq, float("nan"), device=DEV)
+    lse = torch.full((len(counts), w.num_qo_heads), float("nan"), device=DEV)
+    nbytes = bd.workspace_bytes(lay, len(counts), 1, None, b.seq_lens[:len(counts)], counts)
+    ws = torch.empty((max(nbytes, 256),), dtype=torch.uint8, device=DEV)
+    bd.draft_attn(lay, len(counts), b.seq_lens[:len(counts)], b.page_table.to(DEV), counts, offs,
+                  torch.from_numpy(flat).to(DEV), dq.to(DEV), b.k_pool.to(DEV), b.v_pool.to(DEV),
+                  o, lse, ws)
+    torch.cuda.synchronize()
+    qn, kn, vn, ptn = to_np(dq), to_np(b.k_pool), to_np(b.v_pool), to_np(b.page_table)
+    for r, (lst, c) in enumerate(zip(lists, counts)):
+        L = b.seq_lens[r]
+        ro, rl = oracle.draft_request(np.ascontiguousarray(qn[r]), kn, vn, ptn[r, :L], L,
+                                      np.asarray(lst, np.int32).reshape(Hkv, c), Hkv,
+                                      1.0 / np.sqrt(w.head_dim))
+        parity.assert_o(to_np(o[r]), ro, w.dtype, f"draft {r} O")
+        parity.assert_lse_like(to_np(lse[r]), rl, f"draft {r} LSE")
+
+
+def test_draft_list_edge_cases(oracle):
+    """Invalid entries are ignored, duplicates count twice, an all-invalid list
+    gives O = 0 and LSE = -inf, and the full list equals dense attention."""
+    w = synth.Workload(name="edge", batch=5, num_qo_heads=8, num_kv_heads=2, head_dim=128,
+                       dtype="bf16", spec_k=4, sparsity=Fraction(1, 20),
+                       lengths=("fixed", 400), n_verify=0, seed=4)
+    b = synth.make_batch(w, is_verify=[False] * 5)
+    rng = np.random.default_rng(0)
+    lists, counts = [], []
+    base = np.sort(rng.choice(400, 30, replace=False))
+    lists.append(np.stack([np.concatenate([base, [400, -1, 1 << 30, -7]])] * 2)); counts.append(34)
+    lists.append(np.stack([np.array([5, 5, 9, 9, 9])] * 2)); counts.append(5)
+    lists.append(np.stack([np.array([400, -1, 4000])] * 2)); counts.append(3)
+    lists.append(np.stack([np.arange(400)] * 2)); counts.append(400)
+    lists.append(np.stack([rng.permutation(400)[:50], rng.permutation(400)[:50]])); counts.append(50)
+    _draft_only(oracle, b, lists, counts)
+
+
+def test_sequential_entry_points_match_unified(oracle):
+    """spa_verify_attn + spa_pillar_topk + spa_draft_attn on the same batch give
+    what spa_unified_step gives."""
+    w = synth.Workload(name="seq", batch=6, num_qo_heads=32, num_kv_heads=8, head_dim=128,
+                       dtype="bf16", spec_k=8, sparsity=Fraction(1, 20),
+                       lengths=("uniform", 300, 1800), n_verify=2, seed=9)
+    b = synth.make_batch(w)
+    bd_ = b.to(DEV)
+    uni = run_unified(bd_)
+    ver = [r for r in range(b.B) if b.is_verify[r]]
+    dra = [r for r in range(b.B) if not b.is_verify[r]]
+    k, Hq, Hkv, d = w.spec_k, w.num_qo_heads, w.num_kv_heads, w.head_dim
+    lay = bd.layout(Hq, Hkv, d, b.q.dtype, b.num_slots, b.stride)
+    # verify-only batch
+    qv = torch.cat([bd_.q[b.q_indptr[r]:b.q_indptr[r + 1]] for r in ver]).contiguous()
+    ptv = torch.stack([bd_.page_table[r] for r in ver]).contiguous()
+    lv = [b.seq_lens[r] for r in ver]
+    loff = np.concatenate([[0], np.cumsum([(k + 1) * Hq * L for L in lv])[:-1]]).astype(np.int64)
+    ov = torch.empty_like(qv)
+    lsev = torch.empty((qv.shape[0], Hq), device=DEV)
+    lgv = torch.empty((int(sum((k + 1) * Hq * L for L in lv)),), device=DEV)
+    nb = bd.workspace_bytes(lay, len(ver), k, [1] * len(ver), lv, [b.idx_count[r] for r in ver])
+    ws = torch.empty((nb,), dtype=torch.uint8, device=DEV)
+    bd.verify_attn(lay, len(ver), k, lv, ptv, qv, bd_.k_pool, bd_.v_pool, ov, lsev, lgv, loff, ws)
+    Kv = [b.idx_count[r] for r in ver]
+    ioff = np.concatenate([[0], np.cumsum([Hkv * K for K in Kv])[:-1]]).astype(np.int64)
+    idxv = torch.zeros((int(sum(Hkv * K for K in Kv)),), dtype=torch.int32, device=DEV)
+    bd.pillar_topk(len(ver), k, Hq, Hkv, 1, k, lv, Kv, lgv, loff, lsev, idxv, ioff, ws)
+    # draft-only batch
+    qd = torch.stack([bd_.q[b.q_indptr[r]] for r in dra]).contiguous()
+    ptd = torch.stack([bd_.page_table[r] for r in dra]).contiguous()
+    ld = [b.seq_lens[r] for r in dra]
+    Kd = [b.idx_count[r] for r in dra]
+    doff = np.concatenate([[0], np.cumsum([Hkv * K for K in Kd])[:-1]]).astype(np.int64)
+    idxd = torch.cat([bd_.idx[b.idx_off[r]:b.idx_off[r] + Hkv * b.idx_count[r]] for r in dra])
+    od = torch.empty_like(qd)
+    lsed = torch.empty((len(dra), Hq), device=DEV)
+    bd.draft_attn(lay, len(dra), ld, ptd, Kd, doff, idxd.contiguous(), qd, bd_.k_pool,
+                  bd_.v_pool, od, lsed, ws)
+    torch.cuda.synchronize()
+    uo, ul, ui = to_np(uni["o"]), to_np(uni["lse"]), to_np(uni["idx"])
+    row = 0
+    for j, r in enumerate(ver):
+        a, z = b.q_indptr[r], b.q_indptr[r + 1]
+        assert np.array_equal(to_np(ov[row:row + k + 1]), uo[a:z])
+        assert np.array_equal(to_np(lsev[row:row + k + 1]), ul[a:z])
+        row += k + 1
+        assert np.array_equal(to_np(idxv)[ioff[j]:ioff[j] + Hkv * Kv[j]],
+                              ui[b.idx_off[r]:b.idx_off[r] + Hkv * Kv[j]])
+    for j, r in enumerate(dra):
+        assert np.array_equal(to_np(od[j]), uo[b.q_indptr[r]])
+        assert np.array_equal(to_np(lsed[j]), ul[b.q_indptr[r]])
+
+
+def test_chained_verify_then_draft(oracle):
+    """A verify step's selected lists feed the next step, where the same
+    requests draft over them."""
+    w = synth.Workload(name="chain", batch=3, num_qo_heads=32, num_kv_heads=8, head_dim=128,
+                       dtype="bf16", spec_k=8, sparsity=Fraction(1, 20),
+                       lengths=("uniform", 1000, 3000), n_verify=3, seed=12)
+    b, gpu, ref = check(oracle, w)
+    # next step: every request drafts with the list its verify just produced
+    b2 = synth.make_batch(replace(w, n_verify=0, seed=13), is_verify=[False] * 3,
+                          seq_lens=b.seq_lens)
+    b2 = replace(b2, k_pool=b.k_pool, v_pool=b.v_pool, page_table=b.page_table,
+                 idx=gpu["idx"].cpu(), idx_count=b.idx_count, idx_off=b.idx_off,
+                 num_slots=b.num_slots)
+    ref2 = oracle.step(**parity.oracle_inputs(b2))
+    gpu2 = run_unified(b2.to(DEV))
+    parity.compare_step(oracle, b2, gpu2, ref2)
