@@ -1,0 +1,309 @@
+"""Throughput of the unified draft/verify decode-attention step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload qwen3-8b-attn-B128-L8192]
+
+One step = one spa_unified_step call over the whole synthetic batch: verify
+attention with the logits/LSE dump, draft attention over the stored index
+lists, the split-K merge, score averaging and per-KV-head top-K.  Inputs are
+generated on the GPU and stay resident in HBM; the timed region covers
+exactly --steps steps between two device synchronisations.
+
+Prints one JSON line with steps/s (value), attended KV tokens/s, algorithmic
+HBM GB/s against the 8 TB/s peak, the dominant kernel's roofline and the
+oracle's time on this machine's host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from sparse_self_speculative_pillarattn_amd import binding as bd  # noqa: E402
+from sparse_self_speculative_pillarattn_amd import synth  # noqa: E402
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "mixed draft/verify attn steps/s; attended KV tok/s; HBM GB/s vs 8 TB/s peak"
+CSRC = os.path.join(ROOT, "sparse_self_speculative_pillarattn_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+# --------------------------------------------------------------------------- #
+# algorithmic bytes
+# --------------------------------------------------------------------------- #
+def algorithmic_bytes(b) -> dict:
+    """Bytes the method must move per step (each byte once), by kernel.
+
+    verify request r (L tokens, k+1 rows):  K+V rows of every position
+        L*H_kv*d*2e, page-table entries L*4, Q and O (k+1)*H_q*d*e each,
+        LSE (k+1)*H_q*4, logits written (k+1)*H_q*L*4; top-K then reads the k
+        averaged rows' logits k*H_q*L*4 and writes H_kv*K*4.
+    draft request r (K list entries per KV head): K*H_kv*(2*d*e + 4 + 4) for the
+        gathered K+V rows, list entries and page-table entries, plus Q, O, LSE.
+    """
+    w = b.w
+    e = 2 if w.dtype == "bf16" else 4
+    Hq, Hkv, d, k = w.num_qo_heads, w.num_kv_heads, w.head_dim, w.spec_k
+    out = dict(kv_verify=0, kv_draft=0, index=0, qo=0, logits_write=0, logits_read=0, topk_out=0)
+    tokens = 0
+    for r in range(b.B):
+        if b.is_verify[r]:
+            L = b.seq_lens[r]
+            out["kv_verify"] += L * Hkv * d * 2 * e
+            out["index"] += L * 4
+            out["qo"] += (k + 1) * Hq * (2 * d * e + 4)
+            out["logits_write"] += (k + 1) * Hq * L * 4
+            out["logits_read"] += k * Hq * L * 4
+            out["topk_out"] += Hkv * b.idx_count[r] * 4
+            tokens += L
+        else:
+            K = b.idx_count[r]
+            out["kv_draft"] += K * Hkv * d * 2 * e
+            out["index"] += K * Hkv * 8
+            out["qo"] += Hq * (2 * d * e + 4)
+            tokens += K
+    out["bytes_min"] = (out["kv_verify"] + out["kv_draft"] + out["index"] + out["qo"] +
+                        out["topk_out"])
+    out["bytes_method"] = out["bytes_min"] + out["logits_write"] + out["logits_read"]
+    # what the attention launch itself must move: everything but the top-K stage
+    out["attn_launch"] = (out["kv_verify"] + out["kv_draft"] + out["index"] + out["qo"] +
+                          out["logits_write"])
+    out["attended_tokens"] = tokens
+    return out
+
+
+# --------------------------------------------------------------------------- #
+# counter-based traffic, valid only for the kernel source it was taken on
+# --------------------------------------------------------------------------- #
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".h", ".cpp")):
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload: str):
+    """HBM bytes per attention launch from a committed counter summary, or None
+    when none exists for this workload or the kernels changed since."""
+    path = os.path.join(PROFILES, f"attn_kernel_{workload}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    src = re.search(r"source_sha256:\s*([0-9a-f]+)", text)
+    val = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not src or not val or src.group(1) != kernel_source_hash():
+        return None
+    return float(val.group(1))
+
+
+# --------------------------------------------------------------------------- #
+# CPU baseline: the oracle on this machine's host cores
+# --------------------------------------------------------------------------- #
+def compact_for_oracle(b):
+    """Host copies of exactly what the requests read: the pool rows their page
+    tables reference, re-laid-out in page-table order (results do not depend on
+    where a slot lives)."""
+    lens = b.seq_lens
+    stride = max(lens)
+    flat = torch.cat([b.page_table[r, :lens[r]].long() for r in range(b.B)])
+    kp = b.k_pool.index_select(0, flat).cpu()
+    vp = b.v_pool.index_select(0, flat).cpu()
+    pt = np.zeros((b.B, stride), np.int32)
+    off = 0
+    for r in range(b.B):
+        pt[r, :lens[r]] = np.arange(off, off + lens[r], dtype=np.int32)
+        off += lens[r]
+
+    def host(t):
+        t = t.contiguous()
+        if t.dtype == torch.bfloat16:
+            return t.view(torch.int16).numpy().view(np.uint16)
+        return t.numpy()
+
+    return dict(k=b.w.spec_k, Hq=b.w.num_qo_heads, Hkv=b.w.num_kv_heads,
+                sm_scale=1.0 / np.sqrt(b.w.head_dim), is_verify=b.is_verify, seq_lens=lens,
+                q_indptr=b.q_indptr, page_table=pt, q=host(b.q.cpu()), k_pool=host(kp),
+                v_pool=host(vp), idx_count=b.idx_count, idx_off=b.idx_off,
+                idx=host(b.idx.cpu()), logits_off=b.logits_off, logits_elems=b.logits_elems)
+
+
+def cpu_baseline(b, repeats: int) -> dict:
+    from oracle import Oracle  # the oracle is only ever used for this baseline leg
+    orc = Oracle()
+    inp = compact_for_oracle(b)
+    cores = len(os.sched_getaffinity(0))
+    times = []
+    for _ in range(repeats):
+        t0 = time.perf_counter()
+        orc.step(**inp, nthreads=cores)
+        times.append(time.perf_counter() - t0)
+    t = float(np.median(times))
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"value": 1.0 / t, "unit": "steps/s", "cores": cores, "kind": "oracle",
+            "sample": f"the whole step ({b.B} requests), median of {repeats} runs, "
+                      f"{t:.2f} s each; fp64 C oracle, one thread per request",
+            "seconds_per_step": t, "cpu": cpu_model}
+
+
+# --------------------------------------------------------------------------- #
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=synth.QWEN3_8B.name, choices=sorted(synth.WORKLOADS))
+    ap.add_argument("--cold-steps", type=int, default=20,
+                    help="steps timed one by one after a 512 MB cache-flushing write")
+    ap.add_argument("--cpu-repeats", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    bd.load()  # fails loudly when libspa.so is missing
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = synth.WORKLOADS[args.workload]
+    print(f"[bench] generating {w.name} on {dev}", file=sys.stderr, flush=True)
+    b = synth.make_batch(w, device=dev)
+    bufs = bd.StepBuffers(b)
+    alg = algorithmic_bytes(b)
+    torch.cuda.synchronize()
+
+    # warm-up
+    for _ in range(args.warmup):
+        bufs.step()
+    torch.cuda.synchronize()
+
+    # timed region: K steps back to back; the attention launch is bracketed by
+    # HIP events recorded on its own stream
+    bd.profile_reset()
+    bd.profile_enable(1 << bd.PROF_ATTN)
+    t_ev0 = torch.cuda.Event(enable_timing=True)
+    t_ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_ev0.record()
+    for _ in range(args.steps):
+        bufs.step()
+    t_ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    bd.profile_enable(0)
+    n_attn, ms_attn = bd.profile_read(bd.PROF_ATTN)
+    ms_total = t_ev0.elapsed_time(t_ev1)
+    ms_step = ms_total / args.steps
+    print(f"[bench] timed {args.steps} steps: {ms_step * 1e3:.1f} us/step "
+          f"(host wall {wall * 1e6 / args.steps:.1f} us/step)", file=sys.stderr, flush=True)
+
+    # per-kernel breakdown (separate pass, every kernel bracketed)
+    bd.profile_reset()
+    bd.profile_enable(0b11111)
+    for _ in range(10):
+        bufs.step()
+    torch.cuda.synchronize()
+    bd.profile_enable(0)
+    breakdown = {}
+    for i, name in enumerate(bd.PROF_NAMES):
+        n, ms = bd.profile_read(i)
+        if n:
+            breakdown[name] = round(ms / n * 1e3, 2)
+
+    # cold steps: a 512 MB write between steps evicts the 256 MB Infinity Cache
+    cold = None
+    if args.cold_steps > 0:
+        scratch = torch.empty((512 << 20,), dtype=torch.uint8, device=dev)
+        times = []
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        for i in range(args.cold_steps):
+            scratch.fill_(i & 0xFF)
+            e0.record()
+            bufs.step()
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) * 1e3)
+        del scratch
+        times = np.array(times)
+        cold = {"us_median": round(float(np.median(times)), 1),
+                "us_p10": round(float(np.percentile(times, 10)), 1),
+                "us_p90": round(float(np.percentile(times, 90)), 1),
+                "hbm_gbps_method": round(alg["bytes_method"] / (np.median(times) * 1e-6) / 1e9, 1)}
+
+    steps_per_s = 1e3 / ms_step
+    gbps_method = alg["bytes_method"] / (ms_step * 1e-3) / 1e9
+    gbps_min = alg["bytes_min"] / (ms_step * 1e-3) / 1e9
+    attn_us = ms_attn / max(n_attn, 1) * 1e3
+    attn_gbps = alg["attn_launch"] / (attn_us * 1e-6) / 1e9
+    traffic = recorded_traffic(w.name)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the oracle on host cores", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(b, args.cpu_repeats)
+
+    nv = sum(b.is_verify)
+    line = {
+        "metric": METRIC,
+        "value": round(steps_per_s, 2),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": b.B, "n_verify": nv, "n_draft": b.B - nv,
+                   "seq_lens": "fixed" if len(set(b.seq_lens)) == 1 else "drawn",
+                   "mean_seq_len": round(float(np.mean(b.seq_lens)), 1),
+                   "num_qo_heads": w.num_qo_heads, "num_kv_heads": w.num_kv_heads,
+                   "head_dim": w.head_dim, "spec_k": w.spec_k,
+                   "sparsity": f"{w.sparsity.numerator}/{w.sparsity.denominator}",
+                   "page_size": 1, "pool_slots": b.num_slots},
+        "attended_kv_tokens_per_s": round(alg["attended_tokens"] * steps_per_s, 1),
+        "hbm_gbps_method": round(gbps_method, 1),
+        "hbm_frac_method": round(gbps_method / HBM_PEAK_GBPS, 4),
+        "hbm_gbps_min": round(gbps_min, 1),
+        "bytes_method_per_step": alg["bytes_method"],
+        "bytes_min_per_step": alg["bytes_min"],
+        "kernel_us": breakdown,
+        "cold": cold,
+        "roofline": {"bound": "hbm", "kernel": "attn_kernel", "achieved": round(attn_gbps, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(attn_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                     "algorithmic_bytes_per_launch": alg["attn_launch"],
+                     "launch_us": round(attn_us, 2), "launches": n_attn},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -153,6 +153,20 @@ int32_t spa_unified_step(const spa_layout* layout, int32_t B, int32_t spec_k,
  * depend on them beyond floating-point summation order. */
 int32_t spa_set_split(int32_t verify_chunk_tokens, int32_t draft_chunk_entries);
 
+/* Per-launch timing.  With a nonzero kernel mask, every later launch of a
+ * selected kernel is bracketed by a pair of HIP events recorded on the launch
+ * stream (bit 0 plan upload, bit 1 attention, bit 2 split-K merge, bit 3 score
+ * averaging, bit 4 top-K selection); 0 turns it off.  Returns SPA_OK. */
+int32_t spa_profile_enable(int32_t kernel_mask);
+
+/* Waits for the recorded launches of kernel `which` (bit index as above),
+ * adds their durations to the running totals and returns them: number of
+ * launches and summed milliseconds since the last spa_profile_reset(). */
+int32_t spa_profile_read(int32_t which, int64_t* count, double* total_ms);
+
+/* Drops the running totals and any launches not yet read. */
+int32_t spa_profile_reset(void);
+
 #ifdef __cplusplus
 }
 #endif

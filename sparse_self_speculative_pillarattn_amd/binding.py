@@ -27,7 +27,12 @@ SPA_BF16 = 0
 SPA_F32 = 1
 
 EXPORTED = ("spa_abi_version", "spa_last_error", "spa_workspace_bytes", "spa_verify_attn",
-            "spa_pillar_topk", "spa_draft_attn", "spa_unified_step", "spa_set_split")
+            "spa_pillar_topk", "spa_draft_attn", "spa_unified_step", "spa_set_split",
+            "spa_profile_enable", "spa_profile_read", "spa_profile_reset")
+
+# kernel indices of the per-launch timer
+PROF_UPLOAD, PROF_ATTN, PROF_MERGE, PROF_AVG, PROF_SELECT = range(5)
+PROF_NAMES = ("plan_upload", "attn", "merge", "avg", "select")
 
 
 class SpaError(RuntimeError):
@@ -72,6 +77,11 @@ def load(path: str = LIB_PATH):
     lib.spa_unified_step.argtypes = [L, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                      vp, vp, i32, i32, vp, sz, vp]
     lib.spa_unified_step.restype = i32
+    lib.spa_profile_enable.argtypes = [i32]
+    lib.spa_profile_enable.restype = i32
+    lib.spa_profile_read.argtypes = [i32, C.POINTER(C.c_int64), C.POINTER(C.c_double)]
+    lib.spa_profile_read.restype = i32
+    lib.spa_profile_reset.restype = i32
     _lib = lib
     return lib
 
@@ -124,6 +134,22 @@ def abi_version() -> int:
 
 def set_split(verify_chunk_tokens: int = 0, draft_chunk_entries: int = 0):
     _check(load().spa_set_split(int(verify_chunk_tokens), int(draft_chunk_entries)))
+
+
+def profile_enable(mask: int):
+    _check(load().spa_profile_enable(int(mask)))
+
+
+def profile_reset():
+    _check(load().spa_profile_reset())
+
+
+def profile_read(which: int):
+    """(launch count, summed milliseconds) of kernel ``which`` since the last reset."""
+    n = C.c_int64(0)
+    ms = C.c_double(0.0)
+    _check(load().spa_profile_read(int(which), C.byref(n), C.byref(ms)))
+    return int(n.value), float(ms.value)
 
 
 def workspace_bytes(lay: SpaLayout, B: int, spec_k: int, is_verify: Optional[Sequence] ,

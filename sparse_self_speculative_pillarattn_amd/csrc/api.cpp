@@ -259,6 +259,54 @@ int32_t build_plan(const Shape& s, const std::vector<Req>& rq, bool attn, bool t
   return SPA_OK;
 }
 
+// ---- opt-in per-launch timing ------------------------------------------------
+enum { PROF_UPLOAD = 0, PROF_ATTN = 1, PROF_MERGE = 2, PROF_AVG = 3, PROF_SELECT = 4, PROF_N = 5 };
+std::mutex g_prof_mu;
+std::atomic<int32_t> g_prof_mask{0};
+struct ProfPending {
+  int which;
+  hipEvent_t a, b;
+};
+std::vector<ProfPending> g_prof_pending;
+std::vector<hipEvent_t> g_prof_free;
+int64_t g_prof_count[PROF_N] = {0};
+double g_prof_ms[PROF_N] = {0};
+
+hipEvent_t prof_event() {
+  if (!g_prof_free.empty()) {
+    hipEvent_t e = g_prof_free.back();
+    g_prof_free.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Brackets one launch; begin() before, end() after.  No-ops when unselected.
+struct ProfScope {
+  int which;
+  hipStream_t st;
+  hipEvent_t a = nullptr;
+  ProfScope(int w, hipStream_t s) : which(w), st(s) {
+    if (!((g_prof_mask.load() >> which) & 1)) return;
+    std::lock_guard<std::mutex> lock(g_prof_mu);
+    a = prof_event();
+    if (a && hipEventRecord(a, st) != hipSuccess) a = nullptr;
+  }
+  ~ProfScope() {
+    if (!a) return;
+    std::lock_guard<std::mutex> lock(g_prof_mu);
+    hipEvent_t b = prof_event();
+    if (b && hipEventRecord(b, st) == hipSuccess) {
+      g_prof_pending.push_back(ProfPending{which, a, b});
+    } else {
+      g_prof_free.push_back(a);
+      if (b) g_prof_free.push_back(b);
+    }
+  }
+};
+
 // ---- pinned staging ring for plan uploads ---------------------------------
 struct StageSlot {
   void* host = nullptr;
@@ -327,7 +375,11 @@ int32_t run(const Shape& s, const Plan& pl, const Buffers& b, bool attn, bool to
     return fail(SPA_ERR_WORKSPACE_TOO_SMALL,
                 "workspace of " + std::to_string(ws_bytes) + " bytes, need " + std::to_string(pl.total));
   if (pl.total > 0 && !d_ws) return fail(SPA_ERR_INVALID_ARG, "d_ws is NULL");
-  int32_t rc = upload_plan(pl, d_ws, st);
+  int32_t rc;
+  {
+    ProfScope ps(PROF_UPLOAD, st);
+    rc = upload_plan(pl, d_ws, st);
+  }
   if (rc) return rc;
   char* ws = static_cast<char*>(d_ws);
   const ReqDesc* reqs = reinterpret_cast<const ReqDesc*>(ws + pl.off_reqs);
@@ -355,7 +407,10 @@ int32_t run(const Shape& s, const Plan& pl, const Buffers& b, bool attn, bool to
     p.G = s.G;
     p.k = s.k;
     p.sm_scale = s.scale;
-    e = launch_attn(p, s.dtype, s.d, (int)pl.items.size(), pl.nthr, pl.smem, st);
+    {
+      ProfScope ps(PROF_ATTN, st);
+      e = launch_attn(p, s.dtype, s.d, (int)pl.items.size(), pl.nthr, pl.smem, st);
+    }
     if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("attention launch: ") + hipGetErrorString(e));
     if (!pl.merges.empty()) {
       MergeParams mp;
@@ -368,7 +423,10 @@ int32_t run(const Shape& s, const Plan& pl, const Buffers& b, bool attn, bool to
       mp.Hq = s.Hq;
       mp.G = s.G;
       mp.k = s.k;
-      e = launch_merge(mp, s.dtype, s.d, (int)pl.merges.size(), st);
+      {
+        ProfScope ps(PROF_MERGE, st);
+        e = launch_merge(mp, s.dtype, s.d, (int)pl.merges.size(), st);
+      }
       if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("merge launch: ") + hipGetErrorString(e));
     }
   }
@@ -387,7 +445,15 @@ int32_t run(const Shape& s, const Plan& pl, const Buffers& b, bool attn, bool to
     sp.topk = ap.topk;
     sp.pbar = ap.pbar;
     sp.idx = b.idx_out;
-    e = launch_topk(ap, (int)pl.avg.size(), sp, (int)pl.topk.size(), st);
+    {
+      ProfScope ps(PROF_AVG, st);
+      e = launch_avg(ap, (int)pl.avg.size(), st);
+    }
+    if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("averaging launch: ") + hipGetErrorString(e));
+    {
+      ProfScope ps(PROF_SELECT, st);
+      e = launch_select(sp, (int)pl.topk.size(), st);
+    }
     if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("top-K launch: ") + hipGetErrorString(e));
   }
   return SPA_OK;
@@ -457,6 +523,53 @@ int32_t collect(const Shape& s, int B, const uint8_t* is_verify, const int32_t* 
 }  // namespace
 
 extern "C" {
+
+int32_t spa_profile_enable(int32_t kernel_mask) {
+  g_prof_mask.store(kernel_mask & ((1 << PROF_N) - 1));
+  return SPA_OK;
+}
+
+int32_t spa_profile_read(int32_t which, int64_t* count, double* total_ms) {
+  if (which < 0 || which >= PROF_N) return fail(SPA_ERR_INVALID_ARG, "unknown kernel index");
+  std::lock_guard<std::mutex> lock(g_prof_mu);
+  std::vector<ProfPending> keep;
+  for (auto& pp : g_prof_pending) {
+    if (pp.which != which) {
+      keep.push_back(pp);
+      continue;
+    }
+    hipError_t e = hipEventSynchronize(pp.b);
+    float ms = 0.f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, pp.a, pp.b);
+    if (e != hipSuccess) {
+      g_prof_pending.swap(keep);
+      return fail(SPA_ERR_HIP, std::string("profile read: ") + hipGetErrorString(e));
+    }
+    g_prof_count[which] += 1;
+    g_prof_ms[which] += ms;
+    g_prof_free.push_back(pp.a);
+    g_prof_free.push_back(pp.b);
+  }
+  g_prof_pending.swap(keep);
+  if (count) *count = g_prof_count[which];
+  if (total_ms) *total_ms = g_prof_ms[which];
+  return SPA_OK;
+}
+
+int32_t spa_profile_reset(void) {
+  std::lock_guard<std::mutex> lock(g_prof_mu);
+  for (auto& pp : g_prof_pending) {
+    (void)hipEventSynchronize(pp.b);
+    g_prof_free.push_back(pp.a);
+    g_prof_free.push_back(pp.b);
+  }
+  g_prof_pending.clear();
+  for (int i = 0; i < PROF_N; ++i) {
+    g_prof_count[i] = 0;
+    g_prof_ms[i] = 0;
+  }
+  return SPA_OK;
+}
 
 int32_t spa_abi_version(void) { return SPA_ABI_VERSION; }
 

@@ -718,12 +718,14 @@ hipError_t launch_merge(const MergeParams& p, int dtype, int head_dim, int nitem
   return hipGetLastError();
 }
 
-hipError_t launch_topk(const AvgParams& ap, int navg, const SelectParams& sp, int ntopk,
-                       hipStream_t st) {
-  if (ntopk == 0) return hipSuccess;
+hipError_t launch_avg(const AvgParams& ap, int navg, hipStream_t st) {
+  if (navg == 0) return hipSuccess;
   hipLaunchKernelGGL(avg_kernel, dim3(navg), dim3(256), 0, st, ap);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  return hipGetLastError();
+}
+
+hipError_t launch_select(const SelectParams& sp, int ntopk, hipStream_t st) {
+  if (ntopk == 0) return hipSuccess;
   hipLaunchKernelGGL(select_kernel, dim3(ntopk), dim3(1024), 0, st, sp);
   return hipGetLastError();
 }

@@ -57,7 +57,7 @@ hipError_t launch_attn(const AttnParams& p, int dtype, int head_dim, int nitems,
                        size_t smem, hipStream_t st);
 hipError_t launch_merge(const MergeParams& p, int dtype, int head_dim, int nitems,
                         hipStream_t st);
-hipError_t launch_topk(const AvgParams& ap, int navg, const SelectParams& sp, int ntopk,
-                       hipStream_t st);
+hipError_t launch_avg(const AvgParams& ap, int navg, hipStream_t st);
+hipError_t launch_select(const SelectParams& sp, int ntopk, hipStream_t st);
 
 }  // namespace spa
