@@ -222,7 +222,7 @@ def main():
 
     # per-kernel breakdown (separate pass, every kernel bracketed)
     bd.profile_reset()
-    bd.profile_enable(0b11111)
+    bd.profile_enable((1 << len(bd.PROF_NAMES)) - 1)
     for _ in range(10):
         bufs.step()
     torch.cuda.synchronize()

@@ -15,8 +15,9 @@
  * Conventions shared by every entry point
  *   Ownership   The caller owns every buffer.  Device pointers (d_*) are HIP
  *               device memory; host pointers (h_*) are ordinary host memory read
- *               during the call only.  The library keeps one small pinned host
- *               staging ring (allocated on first use) for the per-call work plan.
+ *               during the call only.  The library keeps a small ring of pinned
+ *               host buffers (allocated on first use, grown on demand) holding
+ *               each call's work plan, which the kernels read in place.
  *   Layouts     (H_q query heads, H_kv KV heads, G = H_q / H_kv, d = head_dim,
  *               element type per spa_layout.dtype: bf16 or fp32)
  *               k_pool, v_pool  [num_slots][H_kv][d]; one slot holds one token.
@@ -45,9 +46,10 @@
  *               stream) and the call returns without waiting.  Faults inside a
  *               kernel surface at the caller's next synchronisation.
  *   Workspace   d_ws/ws_bytes is caller-owned device scratch of at least
- *               spa_workspace_bytes(...) bytes for the same batch; it holds the
- *               uploaded work plan, split-K partials and averaged scores.  Calls
- *               that share one workspace must be ordered on one stream.
+ *               spa_workspace_bytes(...) bytes for the same batch; it holds
+ *               split-K partials and averaged scores.  Its contents on entry do
+ *               not matter and need no initialisation.  Calls that share one
+ *               workspace must be ordered on one stream.
  *   Threads     Entry points may be called from several host threads.
  *   B == 0      is a successful no-op.
  */
@@ -155,8 +157,10 @@ int32_t spa_set_split(int32_t verify_chunk_tokens, int32_t draft_chunk_entries);
 
 /* Per-launch timing.  With a nonzero kernel mask, every later launch of a
  * selected kernel is bracketed by a pair of HIP events recorded on the launch
- * stream (bit 0 plan upload, bit 1 attention, bit 2 split-K merge, bit 3 score
- * averaging, bit 4 top-K selection); 0 turns it off.  Returns SPA_OK. */
+ * stream (bit 0: the attention launch; bit 1: the post-pass launch holding the
+ * split-K merges and score averaging; bit 2: the top-K selection launch); 0
+ * turns it off.
+ * Returns SPA_OK. */
 int32_t spa_profile_enable(int32_t kernel_mask);
 
 /* Waits for the recorded launches of kernel `which` (bit index as above),

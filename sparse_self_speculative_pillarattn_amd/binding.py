@@ -31,8 +31,8 @@ EXPORTED = ("spa_abi_version", "spa_last_error", "spa_workspace_bytes", "spa_ver
             "spa_profile_enable", "spa_profile_read", "spa_profile_reset")
 
 # kernel indices of the per-launch timer
-PROF_UPLOAD, PROF_ATTN, PROF_MERGE, PROF_AVG, PROF_SELECT = range(5)
-PROF_NAMES = ("plan_upload", "attn", "merge", "avg", "select")
+PROF_ATTN, PROF_POST, PROF_SELECT = range(3)
+PROF_NAMES = ("attn", "post", "select")
 
 
 class SpaError(RuntimeError):
@@ -206,6 +206,11 @@ def unified_step(lay, B, spec_k, is_verify, seq_lens, q_indptr, page_table, q, k
         _dptr(ws), ws.numel() * ws.element_size(), _stream(q)))
 
 
+def workspace(nbytes: int, device) -> torch.Tensor:
+    """A workspace of at least ``nbytes`` (its contents on entry do not matter)."""
+    return torch.empty((max(int(nbytes), 256),), dtype=torch.uint8, device=device)
+
+
 # --------------------------------------------------------------------------- #
 # convenience: run one synthetic batch through the unified step
 # --------------------------------------------------------------------------- #
@@ -226,7 +231,7 @@ class StepBuffers:
         self.avg_row_count = w.spec_k if avg_row_count is None else avg_row_count
         nbytes = workspace_bytes(self.lay, batch.B, w.spec_k, batch.is_verify, batch.seq_lens,
                                  batch.idx_count)
-        self.ws = torch.empty((max(nbytes, 256),), dtype=torch.uint8, device=dev)
+        self.ws = workspace(nbytes, dev)
 
     def step(self):
         b = self.batch

@@ -1,10 +1,13 @@
-// api.cpp -- host side of libspa: argument checks, work planning, plan upload
-// and kernel launches behind the C ABI of include/spa.h.
+// api.cpp -- host side of libspa: argument checks, work planning and kernel
+// launches behind the C ABI of include/spa.h.
 //
-// A call turns the host metadata into a work plan (per-request descriptors,
-// attention work items, split-K merge groups, selection jobs), copies it into
-// the head of the caller's workspace through a pinned staging ring, and
-// enqueues at most four kernels: attention, merge, averaging, selection.
+// A call turns the host metadata into a work plan -- one record per workgroup
+// -- written into a slot of a pinned host ring that the kernels read in place
+// (no copy is enqueued).  Items of one (request, KV head) stay on one XCD:
+// workgroup i of a launch runs on XCD i % 8, so the attention plan interleaves
+// eight per-XCD queues balanced by bytes.  A call enqueues at most two
+// launches: the attention of every request, then the post-pass (split-K
+// merges, score averaging and top-K selection).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -30,6 +33,7 @@ std::atomic<int32_t> g_draft_chunk{0};
 
 constexpr int DEFAULT_VERIFY_CHUNK = 512;
 constexpr int DEFAULT_DRAFT_CHUNK = 1024;
+constexpr int NUM_XCD = 8;
 
 int32_t fail(int32_t code, const std::string& msg) {
   g_err = msg;
@@ -42,23 +46,9 @@ struct Req {
   int32_t L = 0;
   bool verify = false;
   int32_t row0 = 0;
-  int32_t nlist = 0;      // draft: entries per KV head; verify: K_r
+  int32_t nlist = 0;  // draft: entries per KV head; verify: K_r
   int64_t logits_off = 0;
   int64_t idx_off = 0;
-};
-
-struct Plan {
-  std::vector<ReqDesc> reqs;
-  std::vector<WorkItem> items;
-  std::vector<MergeItem> merges;
-  std::vector<TopkItem> topk;
-  std::vector<AvgItem> avg;
-  int64_t part_rows = 0;
-  int64_t pbar_elems = 0;
-  size_t off_reqs = 0, off_items = 0, off_merge = 0, off_topk = 0, off_avg = 0;
-  size_t plan_bytes = 0, off_part_o = 0, off_part_ml = 0, off_pbar = 0, total = 0;
-  int nthr = 256;
-  size_t smem = 0;
 };
 
 struct Shape {
@@ -68,7 +58,19 @@ struct Shape {
   float scale = 0.f;
 };
 
-int group_template(int G) { return G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : G <= 5 ? 5 : 8; }
+struct Plan {
+  std::vector<Item> items;      // attention launch: interleaved per-XCD queues, NOP-padded
+  std::vector<PostItem> post;   // post-pass launch
+  std::vector<PostItem> sel;    // selection launch: one record per verify (r, g)
+  int64_t part_rows = 0;
+  int64_t pbar_elems = 0;
+  // pinned plan layout
+  size_t h_items = 0, h_post = 0, h_sel = 0, h_bytes = 0;
+  // workspace layout
+  size_t off_part_o = 0, off_part_ml = 0, off_pbar = 0, total = 0;
+  int nthr = 256;
+  size_t smem = 0;
+};
 
 int32_t check_layout(const spa_layout* lay, Shape* s) {
   if (!lay) return fail(SPA_ERR_INVALID_ARG, "layout is NULL");
@@ -118,149 +120,184 @@ int draft_chunk() {
   return v > 0 ? std::min(v, DRAFT_MAX_CHUNK) : DEFAULT_DRAFT_CHUNK;
 }
 
-// Attention (and optionally selection) plan for the requests in `rq`.
-int32_t build_plan(const Shape& s, const std::vector<Req>& rq, bool attn, bool topk,
-                   int avg_begin, int avg_count, Plan* pl) {
+// Work items of one (request, KV head) before they are laid out.
+struct Group {
+  std::vector<Item> items;
+  double bytes = 0;  // estimated HBM bytes, for the XCD balance
+};
+
+// Attention plan (attn) and/or PillarAttn selection plan (topk) for `rq`.
+int32_t build_plan(const Shape& s, const std::vector<Req>& rq, bool attn, bool topk, Plan* pl) {
   const int B = (int)rq.size();
   const int G = s.G, Hkv = s.Hkv, D = s.d;
   const int rows_v = s.k + 1;
   const bool bf16 = s.dtype == SPA_BF16;
+  const int esz = bf16 ? 2 : 4;
   const int CV = verify_chunk(), CD = draft_chunk();
   if (s.k > 255) return fail(SPA_ERR_UNSUPPORTED, "spec_k above 255");
-  pl->reqs.resize(B);
-  bool any_verify = false;
-  for (int r = 0; r < B; ++r) {
-    ReqDesc& d = pl->reqs[r];
-    d.L = rq[r].L;
-    d.row0 = rq[r].row0;
-    d.kind = rq[r].verify ? KIND_VERIFY : KIND_DRAFT;
-    d.list_len = rq[r].nlist;
-    d.off = rq[r].verify ? rq[r].logits_off : rq[r].idx_off;
-    d.nsplit = 1;
-    d.part_row0 = 0;
-    d.pad_ = 0;
-    any_verify |= rq[r].verify;
-  }
+
+  bool any_verify = false, any_draft = false;
+  for (auto& q : rq) (q.verify ? any_verify : any_draft) = true;
+
+  // split-K chunking per request
+  std::vector<int> nchunk(B, 1);
+  std::vector<int64_t> part0(B * (size_t)Hkv, 0);
+  int64_t part_rows = 0;
+  std::vector<PostItem> merges;
   if (attn) {
-    // verify requests first (longest first), then drafts (longest list first):
-    // the dispatcher hands out workgroups in index order, so the big items start early
-    std::vector<int> order(B);
-    for (int r = 0; r < B; ++r) order[r] = r;
-    std::stable_sort(order.begin(), order.end(), [&](int a, int b) {
-      if (rq[a].verify != rq[b].verify) return rq[a].verify;
-      const int la = rq[a].verify ? rq[a].L : rq[a].nlist;
-      const int lb = rq[b].verify ? rq[b].L : rq[b].nlist;
-      return la > lb;
-    });
-    int64_t part_rows = 0;
-    for (int r : order) {
-      ReqDesc& d = pl->reqs[r];
-      const bool v = rq[r].verify;
-      const int span = v ? rq[r].L : rq[r].nlist;
-      const int chunk = v ? CV : CD;
-      const int ns = std::max(1, (span + chunk - 1) / chunk);
-      d.nsplit = ns;
-      const int Rr = (v ? rows_v : 1) * G;
-      if (ns > 1) {
-        d.part_row0 = part_rows;
-        part_rows += (int64_t)Hkv * ns * Rr;
-        for (int g = 0; g < Hkv; ++g) pl->merges.push_back(MergeItem{r, g});
-      }
-      const int nq = (v && !bf16) ? rows_v : 1;  // fp32 verify: one item per query row
-      for (int g = 0; g < Hkv; ++g)
-        for (int sidx = 0; sidx < ns; ++sidx)
-          for (int qi = 0; qi < nq; ++qi) {
-            WorkItem w;
-            w.r = r;
-            w.g = (uint8_t)g;
-            w.qi = (uint8_t)qi;
-            w.split = (uint16_t)sidx;
-            w.begin = sidx * chunk;
-            w.end = std::min(span, (sidx + 1) * chunk);
-            pl->items.push_back(w);
-          }
-    }
-    pl->part_rows = part_rows;
-  }
-  if (topk && any_verify) {
-    int64_t pbar = 0;
+    std::vector<Group> groups;
     for (int r = 0; r < B; ++r) {
-      if (!rq[r].verify) continue;
+      const Req& q = rq[r];
+      const bool v = q.verify;
+      const int span = v ? q.L : q.nlist;
+      const int chunk = v ? CV : CD;
+      const int nc = std::max(1, (span + chunk - 1) / chunk);
+      if (nc > MAX_MERGE_CHUNKS) return fail(SPA_ERR_UNSUPPORTED, "more than 512 split-K chunks");
+      nchunk[r] = nc;
+      const int nq = (v && !bf16) ? rows_v : 1;  // fp32 verify: one item per query row
+      const int Rr = (v ? rows_v : 1) * G;
       for (int g = 0; g < Hkv; ++g) {
-        TopkItem t;
-        t.r = r;
-        t.g = g;
-        t.L = rq[r].L;
-        t.K = rq[r].nlist;
-        t.pbar_off = pbar;
-        t.idx_off = rq[r].idx_off + (int64_t)g * rq[r].nlist;
-        t.logits_off = rq[r].logits_off;
-        t.lse_row0 = rq[r].row0;
-        t.pad_ = 0;
-        const int ti = (int)pl->topk.size();
-        pl->topk.push_back(t);
-        for (int j0 = 0; j0 < t.L; j0 += AVG_SPAN) pl->avg.push_back(AvgItem{ti, j0});
-        pbar += rq[r].L;
+        Group grp;
+        Item base;
+        std::memset(&base, 0, sizeof base);
+        base.kind = v ? KIND_VERIFY : KIND_DRAFT;
+        base.r = r;
+        base.g = g;
+        base.L = q.L;
+        base.row0 = q.row0;
+        base.nchunk = nc;
+        base.list_len = q.nlist;
+        base.off = v ? q.logits_off : q.idx_off + (int64_t)g * q.nlist;
+        if (nc > 1) {
+          base.part_row0 = part_rows;
+          part0[(size_t)r * Hkv + g] = part_rows;
+          part_rows += (int64_t)nc * Rr;
+          PostItem m;
+          std::memset(&m, 0, sizeof m);
+          m.kind = POST_MERGE;
+          m.r = r;
+          m.g = g;
+          m.rows_q = v ? rows_v : 1;
+          m.L = q.L;
+          m.row0 = q.row0;
+          m.nchunk = nc;
+          m.part_row0 = base.part_row0;
+          merges.push_back(m);
+        }
+        for (int c = 0; c < nc; ++c)
+          for (int qi = 0; qi < nq; ++qi) {
+            Item it = base;
+            it.qi = qi;
+            it.split = c;
+            it.begin = c * chunk;
+            it.end = std::min(span, (c + 1) * chunk);
+            grp.items.push_back(it);
+          }
+        grp.bytes = v ? (double)q.L * (2.0 * D * esz + 4 + 4.0 * rows_v * G)
+                      : (double)q.nlist * (2.0 * D * esz + 8);
+        groups.push_back(std::move(grp));
       }
     }
-    pl->pbar_elems = pbar;
+    // longest-processing-time assignment of groups to the XCD queues
+    std::vector<int> order(groups.size());
+    for (size_t i = 0; i < order.size(); ++i) order[i] = (int)i;
+    std::stable_sort(order.begin(), order.end(),
+                     [&](int a, int b) { return groups[a].bytes > groups[b].bytes; });
+    std::vector<std::vector<Item>> queue(NUM_XCD);
+    double load[NUM_XCD] = {0};
+    for (int gi : order) {
+      int x = 0;
+      for (int y = 1; y < NUM_XCD; ++y)
+        if (load[y] < load[x]) x = y;
+      load[x] += groups[gi].bytes;
+      for (auto& it : groups[gi].items) queue[x].push_back(it);
+    }
+    size_t maxlen = 0;
+    for (auto& qx : queue) maxlen = std::max(maxlen, qx.size());
+    Item nop;
+    std::memset(&nop, 0, sizeof nop);
+    nop.kind = KIND_NOP;
+    pl->items.reserve(maxlen * NUM_XCD);
+    for (size_t i = 0; i < maxlen; ++i)
+      for (int x = 0; x < NUM_XCD; ++x) pl->items.push_back(i < queue[x].size() ? queue[x][i] : nop);
   }
-  (void)avg_begin;
-  (void)avg_count;
+  // post-pass: averaging chunks of every verify (r, g), then the merges
+  int64_t pbar = 0;
+  if (topk && any_verify) {
+    for (int r = 0; r < B; ++r) {
+      const Req& q = rq[r];
+      if (!q.verify) continue;
+      const int nparts = (q.L + AVG_SPAN - 1) / AVG_SPAN;
+      for (int g = 0; g < Hkv; ++g) {
+        for (int pidx = 0; pidx < nparts; ++pidx) {
+          PostItem a;
+          std::memset(&a, 0, sizeof a);
+          a.kind = POST_AVG;
+          a.r = r;
+          a.g = g;
+          a.rows_q = rows_v;
+          a.L = q.L;
+          a.row0 = q.row0;
+          a.nchunk = attn ? nchunk[r] : 1;
+          a.part_row0 = attn ? part0[(size_t)r * Hkv + g] : 0;
+          a.j0 = pidx * AVG_SPAN;
+          a.j1 = std::min(q.L, (pidx + 1) * AVG_SPAN);
+          a.K = q.nlist;
+          a.logits_off = q.logits_off;
+          a.idx_off = q.idx_off + (int64_t)g * q.nlist;
+          a.pbar_off = pbar;
+          pl->post.push_back(a);
+          if (pidx == 0) pl->sel.push_back(a);
+        }
+        pbar += (q.L + 3) / 4 * 4;  // rows start 16-byte aligned
+      }
+    }
+  }
+  for (auto& m : merges) pl->post.push_back(m);
+  pl->part_rows = part_rows;
+  pl->pbar_elems = pbar;
+
   // block shape and LDS of the attention launch
-  int nthr = 256;
-  size_t smem = 0;
-  const int GM = group_template(G);
-  bool need_valu = false, need_mfma = false;
-  for (int r = 0; r < B && attn; ++r) {
-    if (rq[r].verify && bf16) need_mfma = true;
-    else need_valu = true;
+  bool need_mfma = false, need_valu = false;
+  if (attn) {
+    need_mfma = any_verify && bf16;
+    need_valu = any_draft || (any_verify && !bf16);
   }
+  int nthr = 256;
   if (need_mfma) {
     const int nt = (rows_v * G + 15) / 16;
     if (nt > MAX_ROW_TILES)
       return fail(SPA_ERR_UNSUPPORTED, "(k+1)*G above 128 rows per KV head on the MFMA path");
     nthr = 64 * std::max(4, nt);
-    const size_t mf = (size_t)VERIFY_TILE * (D / 8) * 16 + (size_t)D * (VERIFY_TILE + 8) * 2 +
-                      (size_t)VERIFY_MAX_CHUNK * 4;
-    smem = std::max(smem, mf);
   }
-  if (need_valu) {
-    if (G > MAX_GROUP) return fail(SPA_ERR_UNSUPPORTED, "GQA group above 8 on the gather path");
-    const int E = bf16 ? 8 : 4;
-    const int LPR = D / E;
-    const int TB = (nthr / LPR) * 4;
-    const size_t va = (size_t)DRAFT_MAX_CHUNK * 4 + (size_t)GM * TB * 4 + 3 * GM * 4 +
-                      (size_t)(nthr / 64) * GM * D * 4;
-    smem = std::max(smem, va);
-  }
+  if (need_valu && G > MAX_GROUP)
+    return fail(SPA_ERR_UNSUPPORTED, "GQA group above 8 on the gather path");
   pl->nthr = nthr;
-  pl->smem = smem;
+  pl->smem = attn ? attn_smem_bytes(s.dtype, D, G, nthr, need_mfma, need_valu) : 0;
+
+  // pinned plan layout
+  size_t h = 0;
+  pl->h_items = h;
+  h = align_up(h + pl->items.size() * sizeof(Item), 256);
+  pl->h_post = h;
+  h = align_up(h + pl->post.size() * sizeof(PostItem), 256);
+  pl->h_sel = h;
+  h = align_up(h + pl->sel.size() * sizeof(PostItem), 256);
+  pl->h_bytes = h;
   // workspace layout
   size_t o = 0;
-  pl->off_reqs = o;
-  o = align_up(o + pl->reqs.size() * sizeof(ReqDesc), 256);
-  pl->off_items = o;
-  o = align_up(o + pl->items.size() * sizeof(WorkItem), 256);
-  pl->off_merge = o;
-  o = align_up(o + pl->merges.size() * sizeof(MergeItem), 256);
-  pl->off_topk = o;
-  o = align_up(o + pl->topk.size() * sizeof(TopkItem), 256);
-  pl->off_avg = o;
-  o = align_up(o + pl->avg.size() * sizeof(AvgItem), 256);
-  pl->plan_bytes = o;
   pl->off_part_o = o;
-  o = align_up(o + (size_t)pl->part_rows * D * 4, 256);
+  o = align_up(o + (size_t)part_rows * D * 4, 256);
   pl->off_part_ml = o;
-  o = align_up(o + (size_t)pl->part_rows * 2 * 4, 256);
+  o = align_up(o + (size_t)part_rows * 2 * 4, 256);
   pl->off_pbar = o;
-  o = align_up(o + (size_t)pl->pbar_elems * 4, 256);
+  o = align_up(o + (size_t)pbar * 4, 256);
   pl->total = o;
   return SPA_OK;
 }
 
 // ---- opt-in per-launch timing ------------------------------------------------
-enum { PROF_UPLOAD = 0, PROF_ATTN = 1, PROF_MERGE = 2, PROF_AVG = 3, PROF_SELECT = 4, PROF_N = 5 };
+enum { PROF_ATTN = 0, PROF_POST = 1, PROF_SELECT = 2, PROF_N = 3 };
 std::mutex g_prof_mu;
 std::atomic<int32_t> g_prof_mask{0};
 struct ProfPending {
@@ -283,7 +320,7 @@ hipEvent_t prof_event() {
   return e;
 }
 
-// Brackets one launch; begin() before, end() after.  No-ops when unselected.
+// Brackets one launch with a pair of events when the kernel is selected.
 struct ProfScope {
   int which;
   hipStream_t st;
@@ -307,53 +344,53 @@ struct ProfScope {
   }
 };
 
-// ---- pinned staging ring for plan uploads ---------------------------------
-struct StageSlot {
+// ---- pinned plan ring ----------------------------------------------------------
+// A slot holds one call's plan until the call's last kernel has finished; a
+// slot is reused only after the event recorded behind that kernel completes.
+struct PlanSlot {
   void* host = nullptr;
+  void* dev = nullptr;
   size_t cap = 0;
   hipEvent_t ev = nullptr;
   bool pending = false;
 };
-constexpr int RING = 32;
+constexpr int RING = 64;
 std::mutex g_ring_mu;
-StageSlot g_ring[RING];
+PlanSlot g_ring[RING];
 unsigned g_ring_next = 0;
 
-int32_t upload_plan(const Plan& pl, void* d_ws, hipStream_t st) {
-  if (pl.plan_bytes == 0) return SPA_OK;
-  std::lock_guard<std::mutex> lock(g_ring_mu);
-  StageSlot& s = g_ring[g_ring_next++ % RING];
+int32_t acquire_slot(const Plan& pl, PlanSlot** out) {
+  PlanSlot& s = g_ring[g_ring_next++ % RING];
   hipError_t e;
   if (s.pending) {
     e = hipEventSynchronize(s.ev);
-    if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("staging wait: ") + hipGetErrorString(e));
+    if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("plan slot wait: ") + hipGetErrorString(e));
     s.pending = false;
   }
   if (!s.ev) {
     e = hipEventCreateWithFlags(&s.ev, hipEventDisableTiming);
     if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("event create: ") + hipGetErrorString(e));
   }
-  if (s.cap < pl.plan_bytes) {
+  if (s.cap < pl.h_bytes) {
     if (s.host) (void)hipHostFree(s.host);
-    s.host = nullptr;
+    s.host = s.dev = nullptr;
     s.cap = 0;
-    const size_t want = std::max<size_t>(pl.plan_bytes * 2, 1 << 16);
-    e = hipHostMalloc(&s.host, want, hipHostMallocDefault);
-    if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("pinned staging: ") + hipGetErrorString(e));
+    const size_t want = std::max<size_t>(pl.h_bytes * 2, 1 << 16);
+    e = hipHostMalloc(&s.host, want, hipHostMallocMapped | hipHostMallocPortable);
+    if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("pinned plan: ") + hipGetErrorString(e));
+    e = hipHostGetDevicePointer(&s.dev, s.host, 0);
+    if (e != hipSuccess) {
+      (void)hipHostFree(s.host);
+      s.host = nullptr;
+      return fail(SPA_ERR_HIP, std::string("pinned plan mapping: ") + hipGetErrorString(e));
+    }
     s.cap = want;
   }
   char* h = static_cast<char*>(s.host);
-  std::memset(h, 0, pl.plan_bytes);
-  if (!pl.reqs.empty()) std::memcpy(h + pl.off_reqs, pl.reqs.data(), pl.reqs.size() * sizeof(ReqDesc));
-  if (!pl.items.empty()) std::memcpy(h + pl.off_items, pl.items.data(), pl.items.size() * sizeof(WorkItem));
-  if (!pl.merges.empty()) std::memcpy(h + pl.off_merge, pl.merges.data(), pl.merges.size() * sizeof(MergeItem));
-  if (!pl.topk.empty()) std::memcpy(h + pl.off_topk, pl.topk.data(), pl.topk.size() * sizeof(TopkItem));
-  if (!pl.avg.empty()) std::memcpy(h + pl.off_avg, pl.avg.data(), pl.avg.size() * sizeof(AvgItem));
-  e = hipMemcpyAsync(d_ws, h, pl.plan_bytes, hipMemcpyHostToDevice, st);
-  if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("plan upload: ") + hipGetErrorString(e));
-  e = hipEventRecord(s.ev, st);
-  if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("event record: ") + hipGetErrorString(e));
-  s.pending = true;
+  if (!pl.items.empty()) std::memcpy(h + pl.h_items, pl.items.data(), pl.items.size() * sizeof(Item));
+  if (!pl.post.empty()) std::memcpy(h + pl.h_post, pl.post.data(), pl.post.size() * sizeof(PostItem));
+  if (!pl.sel.empty()) std::memcpy(h + pl.h_sel, pl.sel.data(), pl.sel.size() * sizeof(PostItem));
+  *out = &s;
   return SPA_OK;
 }
 
@@ -369,37 +406,35 @@ struct Buffers {
   float* logits = nullptr;
 };
 
-int32_t run(const Shape& s, const Plan& pl, const Buffers& b, bool attn, bool topk, int avg_begin,
-            int avg_count, void* d_ws, size_t ws_bytes, hipStream_t st) {
+int32_t run(const Shape& s, const Plan& pl, const Buffers& b, int avg_begin, int avg_count,
+            void* d_ws, size_t ws_bytes, hipStream_t st) {
   if (ws_bytes < pl.total)
     return fail(SPA_ERR_WORKSPACE_TOO_SMALL,
                 "workspace of " + std::to_string(ws_bytes) + " bytes, need " + std::to_string(pl.total));
   if (pl.total > 0 && !d_ws) return fail(SPA_ERR_INVALID_ARG, "d_ws is NULL");
-  int32_t rc;
-  {
-    ProfScope ps(PROF_UPLOAD, st);
-    rc = upload_plan(pl, d_ws, st);
-  }
+  if (pl.items.empty() && pl.post.empty()) return SPA_OK;
+  std::lock_guard<std::mutex> lock(g_ring_mu);
+  PlanSlot* slot = nullptr;
+  int32_t rc = acquire_slot(pl, &slot);
   if (rc) return rc;
+  const char* plan = static_cast<const char*>(slot->dev);
   char* ws = static_cast<char*>(d_ws);
-  const ReqDesc* reqs = reinterpret_cast<const ReqDesc*>(ws + pl.off_reqs);
   float* part_o = reinterpret_cast<float*>(ws + pl.off_part_o);
   float* part_ml = reinterpret_cast<float*>(ws + pl.off_part_ml);
   hipError_t e;
-  if (attn && !pl.items.empty()) {
+  if (!pl.items.empty()) {
     AttnParams p;
+    p.items = reinterpret_cast<const Item*>(plan + pl.h_items);
     p.q = b.q;
     p.k_pool = b.k_pool;
     p.v_pool = b.v_pool;
     p.page_table = b.page_table;
     p.pt_stride = s.stride;
     p.num_slots = s.num_slots;
-    p.idx = b.idx_in;
+    p.idx_in = b.idx_in;
     p.o = b.o;
     p.lse = b.lse;
     p.logits = b.logits;
-    p.reqs = reqs;
-    p.items = reinterpret_cast<const WorkItem*>(ws + pl.off_items);
     p.part_o = part_o;
     p.part_ml = part_ml;
     p.Hq = s.Hq;
@@ -412,50 +447,40 @@ int32_t run(const Shape& s, const Plan& pl, const Buffers& b, bool attn, bool to
       e = launch_attn(p, s.dtype, s.d, (int)pl.items.size(), pl.nthr, pl.smem, st);
     }
     if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("attention launch: ") + hipGetErrorString(e));
-    if (!pl.merges.empty()) {
-      MergeParams mp;
-      mp.reqs = reqs;
-      mp.items = reinterpret_cast<const MergeItem*>(ws + pl.off_merge);
-      mp.part_o = part_o;
-      mp.part_ml = part_ml;
-      mp.o = b.o;
-      mp.lse = b.lse;
-      mp.Hq = s.Hq;
-      mp.G = s.G;
-      mp.k = s.k;
-      {
-        ProfScope ps(PROF_MERGE, st);
-        e = launch_merge(mp, s.dtype, s.d, (int)pl.merges.size(), st);
-      }
-      if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("merge launch: ") + hipGetErrorString(e));
-    }
   }
-  if (topk && !pl.topk.empty()) {
-    AvgParams ap;
-    ap.topk = reinterpret_cast<const TopkItem*>(ws + pl.off_topk);
-    ap.avg = reinterpret_cast<const AvgItem*>(ws + pl.off_avg);
-    ap.logits = b.logits;
-    ap.lse = b.lse;
-    ap.pbar = reinterpret_cast<float*>(ws + pl.off_pbar);
-    ap.Hq = s.Hq;
-    ap.G = s.G;
-    ap.row_begin = avg_begin;
-    ap.row_count = avg_count;
-    SelectParams sp;
-    sp.topk = ap.topk;
-    sp.pbar = ap.pbar;
-    sp.idx = b.idx_out;
+  if (!pl.post.empty()) {
+    PostParams pp;
+    pp.items = reinterpret_cast<const PostItem*>(plan + pl.h_post);
+    pp.part_o = part_o;
+    pp.part_ml = part_ml;
+    pp.o = b.o;
+    pp.lse = b.lse;
+    pp.logits = b.logits;
+    pp.pbar = reinterpret_cast<float*>(ws + pl.off_pbar);
+    pp.Hq = s.Hq;
+    pp.G = s.G;
+    pp.avg_row_begin = avg_begin;
+    pp.avg_row_count = avg_count;
     {
-      ProfScope ps(PROF_AVG, st);
-      e = launch_avg(ap, (int)pl.avg.size(), st);
+      ProfScope ps(PROF_POST, st);
+      e = launch_post(pp, s.dtype, s.d, (int)pl.post.size(), st);
     }
-    if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("averaging launch: ") + hipGetErrorString(e));
+    if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("post-pass launch: ") + hipGetErrorString(e));
+  }
+  if (!pl.sel.empty()) {
+    SelectParams sp;
+    sp.items = reinterpret_cast<const PostItem*>(plan + pl.h_sel);
+    sp.pbar = reinterpret_cast<const float*>(ws + pl.off_pbar);
+    sp.idx_out = b.idx_out;
     {
       ProfScope ps(PROF_SELECT, st);
-      e = launch_select(sp, (int)pl.topk.size(), st);
+      e = launch_select(sp, (int)pl.sel.size(), st);
     }
-    if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("top-K launch: ") + hipGetErrorString(e));
+    if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("selection launch: ") + hipGetErrorString(e));
   }
+  e = hipEventRecord(slot->ev, st);
+  if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("event record: ") + hipGetErrorString(e));
+  slot->pending = true;
   return SPA_OK;
 }
 
@@ -612,8 +637,9 @@ size_t spa_workspace_bytes(const spa_layout* layout, int32_t B, int32_t spec_k,
   if (collect(s, B, h_is_verify, h_seq_lens, nullptr, counts.data(), nullptr, nullptr, false,
               false, &rq))
     return 0;
+  // the unified step needs the most: attention plus selection
   Plan pl;
-  if (build_plan(s, rq, true, true, 1, std::max(1, s.k), &pl)) return 0;
+  if (build_plan(s, rq, true, true, &pl)) return 0;
   return pl.total;
 }
 
@@ -638,7 +664,7 @@ int32_t spa_verify_attn(const spa_layout* layout, int32_t B, int32_t spec_k,
                &rq);
   if (rc) return rc;
   Plan pl;
-  rc = build_plan(s, rq, true, false, 1, spec_k, &pl);
+  rc = build_plan(s, rq, true, false, &pl);
   if (rc) return rc;
   Buffers b;
   b.page_table = d_page_table;
@@ -648,7 +674,7 @@ int32_t spa_verify_attn(const spa_layout* layout, int32_t B, int32_t spec_k,
   b.o = d_o;
   b.lse = d_lse;
   b.logits = d_logits;
-  return run(s, pl, b, true, false, 1, spec_k, d_ws, ws_bytes, static_cast<hipStream_t>(stream));
+  return run(s, pl, b, 1, spec_k, d_ws, ws_bytes, static_cast<hipStream_t>(stream));
 }
 
 int32_t spa_pillar_topk(int32_t B, int32_t spec_k, int32_t num_qo_heads, int32_t num_kv_heads,
@@ -678,13 +704,13 @@ int32_t spa_pillar_topk(int32_t B, int32_t spec_k, int32_t num_qo_heads, int32_t
                &rq);
   if (rc) return rc;
   Plan pl;
-  rc = build_plan(s, rq, false, true, avg_row_begin, avg_row_count, &pl);
+  rc = build_plan(s, rq, false, true, &pl);
   if (rc) return rc;
   Buffers b;
   b.logits = const_cast<float*>(d_logits);
   b.lse = const_cast<float*>(d_lse);
   b.idx_out = d_idx;
-  return run(s, pl, b, false, true, avg_row_begin, avg_row_count, d_ws, ws_bytes,
+  return run(s, pl, b, avg_row_begin, avg_row_count, d_ws, ws_bytes,
              static_cast<hipStream_t>(stream));
 }
 
@@ -707,7 +733,7 @@ int32_t spa_draft_attn(const spa_layout* layout, int32_t B, const int32_t* h_seq
                &rq);
   if (rc) return rc;
   Plan pl;
-  rc = build_plan(s, rq, true, false, 0, 1, &pl);
+  rc = build_plan(s, rq, true, false, &pl);
   if (rc) return rc;
   Buffers b;
   b.page_table = d_page_table;
@@ -717,7 +743,7 @@ int32_t spa_draft_attn(const spa_layout* layout, int32_t B, const int32_t* h_seq
   b.idx_in = d_idx;
   b.o = d_o;
   b.lse = d_lse;
-  return run(s, pl, b, true, false, 0, 1, d_ws, ws_bytes, static_cast<hipStream_t>(stream));
+  return run(s, pl, b, 0, 1, d_ws, ws_bytes, static_cast<hipStream_t>(stream));
 }
 
 int32_t spa_unified_step(const spa_layout* layout, int32_t B, int32_t spec_k,
@@ -749,7 +775,7 @@ int32_t spa_unified_step(const spa_layout* layout, int32_t B, int32_t spec_k,
                any_v, true, &rq);
   if (rc) return rc;
   Plan pl;
-  rc = build_plan(s, rq, true, true, avg_row_begin, avg_row_count, &pl);
+  rc = build_plan(s, rq, true, true, &pl);
   if (rc) return rc;
   Buffers b;
   b.page_table = d_page_table;
@@ -761,7 +787,7 @@ int32_t spa_unified_step(const spa_layout* layout, int32_t B, int32_t spec_k,
   b.o = d_o;
   b.lse = d_lse;
   b.logits = d_logits;
-  return run(s, pl, b, true, true, avg_row_begin, avg_row_count, d_ws, ws_bytes,
+  return run(s, pl, b, avg_row_begin, avg_row_count, d_ws, ws_bytes,
              static_cast<hipStream_t>(stream));
 }
 

@@ -1,22 +1,23 @@
 // kernels.hip -- device code of libspa for gfx950 (CDNA4).
 //
-// attn_kernel   one work item per workgroup: a verify item (request r, KV head g,
-//               token chunk) runs the MFMA tile below; a draft item (r, g, chunk of
-//               its index list) runs the VALU gather tile.  Both kinds go through
-//               the same launch ("Unified batch scheduler + fused attention
-//               kernel", SparseSpec review).
-// merge_kernel  split-K partials (O, m, l) of one (request, KV head) -> O, LSE.
-// avg_kernel    exact scores exp(logit - LSE) averaged over the draft rows and
-//               the GQA group (SparseSpec review, PillarAttn, third bullet).
-// select_kernel per (verify request, KV head) top-K of the averaged scores by an
-//               MSB-first radix select on the fp32 bit patterns, then an ordered
-//               compaction so the list comes out ascending (PillarAttn, fourth
-//               bullet).
+// attn_kernel   one launch for all attention work of a batch.  Each workgroup
+//               takes one plan item: a verify item (request r, KV head g, a chunk
+//               of positions) runs the MFMA tile, a draft item (r, g, a chunk of
+//               its index list) runs the VALU gather tile.  Both kinds share the
+//               launch ("Unified batch scheduler + fused attention kernel",
+//               SparseSpec review).  Outputs are final when (r, g) is one chunk,
+//               split-K partials otherwise.  No workgroup waits for another.
+// post_kernel   the PillarAttn post-pass: split-K merges, and the exact scores
+//               exp(logit - LSE) averaged over the draft rows and the GQA group
+//               in position chunks; the last chunk of a verify (r, g) selects its
+//               top-K by a radix select (PillarAttn, SparseSpec review).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "spa_plan.h"
+#include <algorithm>
+
 #include "spa_kernels.h"
+#include "spa_plan.h"
 
 namespace spa {
 
@@ -26,7 +27,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr float LOG2E = 1.4426950408889634f;
 #define NEG_INF (-__builtin_inff())
 
-__device__ __forceinline__ float bf2f(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 __device__ __forceinline__ uint32_t f2bf(float f) {
   __bf16 h = (__bf16)f;  // round to nearest even
   return (uint32_t)__builtin_bit_cast(uint16_t, h);
@@ -37,11 +37,10 @@ __device__ __forceinline__ int64_t clamp_slot(int32_t s, int64_t n) {
   return s < 0 ? 0 : (s >= n ? n - 1 : (int64_t)s);
 }
 
-// 16-byte piece -> floats
 template <typename T>
 struct Piece;
 template <>
-struct Piece<uint16_t> {  // bf16
+struct Piece<uint16_t> {  // bf16: 8 elements per 16 bytes
   static constexpr int E = 8;
   __device__ static void unpack(const uint4& v, float* f) {
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
@@ -74,28 +73,156 @@ __device__ __forceinline__ void store_out<float>(float* dst, float v) {
   *dst = v;
 }
 
-// LDS chunk swizzle of the K tile: spreads the 16 rows an MFMA operand read
-// touches over all banks.
+// LDS chunk swizzle of the K tile: the 16 rows one MFMA operand read touches
+// land on distinct bank groups.
 template <int NCH>
 __device__ __forceinline__ int kswz(int tau) {
   return ((tau & 3) | (((tau >> 3) & 3) << 2)) & (NCH - 1);
 }
 
-// --------------------------------------------------------------------------
-// Verify tile on MFMA (bf16).  Rows rho = i*G + hh (query row i, head hh of the
-// group) are split into 16-row tiles, one per wave.  Per 64-token tile:
-//   S^T = K * Q^T      (16x16x32 MFMA, A = K rows from LDS, B = Q^T in registers)
-//   logits stored, online softmax in registers,
-//   O^T += V^T * P^T   (A = V^T from the transposed LDS tile, B = P^T, which is
-//                       the S^T accumulator layout repacked to bf16 in place).
-// Token order inside a tile is permuted so that the S^T accumulator of two
-// 16-token MFMA tiles is exactly the P^T operand of one 32-token PV step and
-// every lane owns 4 consecutive positions (vector logits stores).
-// --------------------------------------------------------------------------
+// DPP lane exchanges inside a row of 16 lanes (no LDS traffic).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+constexpr int DPP_XOR1 = 0xB1;         // quad_perm [1,0,3,2]
+constexpr int DPP_XOR2 = 0x4E;         // quad_perm [2,3,0,1]
+constexpr int DPP_HALF_MIRROR = 0x141; // lane i <-> 7-i within each half row
+constexpr int DPP_MIRROR = 0x140;      // lane i <-> 15-i within each row
+
+// Sum over groups of N consecutive lanes (N = 1, 2, 4, 8, 16, 32, 64); every
+// lane of a group receives the group's sum.
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (N >= 2) v += dpp<DPP_XOR1>(v);
+  if constexpr (N >= 4) v += dpp<DPP_XOR2>(v);
+  if constexpr (N >= 8) v += dpp<DPP_HALF_MIRROR>(v);
+  if constexpr (N >= 16) v += dpp<DPP_MIRROR>(v);
+  if constexpr (N >= 32) v += __shfl_xor(v, 16);
+  if constexpr (N >= 64) v += __shfl_xor(v, 32);
+  return v;
+}
+
+// ==========================================================================
+// Verify tile on MFMA (bf16)
+//
+// Rows rho = i*G + hh (query row i, head hh of the group) form 16-row tiles,
+// one per wave.  Per 64-token tile:
+//   S^T = K Q^T       16x16x32 MFMA; A = K rows from LDS, B = Q^T in registers
+//   logits stored; online softmax in registers (two lane shuffles per row)
+//   O^T += V^T P^T    A = V^T from the transposed LDS tile; B = P^T is the S^T
+//                     accumulator repacked to bf16 in place.
+// Tokens inside a tile are permuted so that two 16-token S^T accumulators are
+// exactly the P^T operand of one 32-token PV step and every lane owns four
+// consecutive positions.  Two tiles of K/V rows are in flight in registers
+// while a third is computed from LDS.
+// ==========================================================================
 template <int D>
-__device__ void verify_tile_mfma(const AttnParams& p, const WorkItem& it, const ReqDesc& rq,
-                                 char* smem) {
-  constexpr int NCH = D / 8;   // 16-byte chunks per row
+constexpr size_t mfma_smem_bytes() {
+  return (size_t)VERIFY_TILE * (D / 8) * 16 + (size_t)D * (VERIFY_TILE + 8) * 2 +
+         (size_t)VERIFY_MAX_CHUNK * 4;
+}
+
+// Registers holding one 64-token K/V tile on its way to LDS: up to four K
+// pieces and four V pieces (16 bytes each) per thread.
+struct KVRegs {
+  uint4 k0, k1, k2, k3, v0, v1, v2, v3;
+};
+
+template <int D>
+struct VerifyTileCtx {
+  uint4* Ks;
+  uint16_t* Vt;
+  const int32_t* slots;
+  const uint16_t* kpool;
+  const uint16_t* vpool;
+  int tid, nthr, jb, je, g, Hkv;
+};
+
+template <int D>
+__device__ __forceinline__ uint4 fetch_k(const VerifyTileCtx<D>& c, int t0, int i) {
+  constexpr int NCH = D / 8;
+  const int pc = min(c.tid + i * c.nthr, VERIFY_TILE * NCH - 1);
+  const int tau = pc / NCH, ch = pc % NCH;
+  const int64_t slot = c.slots[min(t0 - c.jb + tau, c.je - 1 - c.jb)];
+  return *reinterpret_cast<const uint4*>(c.kpool + (slot * c.Hkv + c.g) * D + 8 * ch);
+}
+
+template <int D>
+__device__ __forceinline__ uint4 fetch_v(const VerifyTileCtx<D>& c, int t0, int i) {
+  constexpr int NCH = D / 8;
+  constexpr int VUNITS = (VERIFY_TILE / 4) * NCH;
+  const int u = min(c.tid, VUNITS - 1);
+  const int tg = u / NCH, ch = u % NCH;
+  const int64_t slot = c.slots[min(t0 - c.jb + 4 * tg + i, c.je - 1 - c.jb)];
+  return *reinterpret_cast<const uint4*>(c.vpool + (slot * c.Hkv + c.g) * D + 8 * ch);
+}
+
+template <int D>
+__device__ __forceinline__ void fetch_tile(const VerifyTileCtx<D>& c, KVRegs& r, int t0) {
+  constexpr int KP = VERIFY_TILE * (D / 8) / 256;
+  r.k0 = fetch_k<D>(c, t0, 0);
+  r.k1 = fetch_k<D>(c, t0, 1);
+  if constexpr (KP > 2) {
+    r.k2 = fetch_k<D>(c, t0, 2);
+    r.k3 = fetch_k<D>(c, t0, 3);
+  }
+  r.v0 = fetch_v<D>(c, t0, 0);
+  r.v1 = fetch_v<D>(c, t0, 1);
+  r.v2 = fetch_v<D>(c, t0, 2);
+  r.v3 = fetch_v<D>(c, t0, 3);
+}
+
+template <int D>
+__device__ __forceinline__ void stage_k(const VerifyTileCtx<D>& c, const uint4& v, int nt, int i) {
+  constexpr int NCH = D / 8;
+  const int pc = c.tid + i * c.nthr;
+  if (pc < VERIFY_TILE * NCH) {
+    const int tau = pc / NCH, ch = pc % NCH;
+    c.Ks[tau * NCH + (ch ^ kswz<NCH>(tau))] = tau < nt ? v : make_uint4(0u, 0u, 0u, 0u);
+  }
+}
+
+__device__ __forceinline__ uint32_t half16(uint32_t w, int hi) { return hi ? (w >> 16) : (w & 0xffffu); }
+
+// V tile transposed into LDS: thread (token group tg, chunk ch) holds four
+// consecutive tokens' 8 elements; element e of the four tokens becomes one
+// 8-byte row segment Vt[8 ch + e][4 tg .. 4 tg + 3].
+template <int D>
+__device__ __forceinline__ void stage_tile(const VerifyTileCtx<D>& c, const KVRegs& r, int t0) {
+  constexpr int NCH = D / 8;
+  constexpr int KP = VERIFY_TILE * NCH / 256;
+  constexpr int VTS = VERIFY_TILE + 8;
+  constexpr int VUNITS = (VERIFY_TILE / 4) * NCH;
+  const int nt = min(VERIFY_TILE, c.je - t0);
+  stage_k<D>(c, r.k0, nt, 0);
+  stage_k<D>(c, r.k1, nt, 1);
+  if constexpr (KP > 2) {
+    stage_k<D>(c, r.k2, nt, 2);
+    stage_k<D>(c, r.k3, nt, 3);
+  }
+  if (c.tid < VUNITS) {
+    const int tg = c.tid / NCH, ch = c.tid % NCH;
+    const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+    const uint4 a = (4 * tg + 0 < nt) ? r.v0 : z;
+    const uint4 b = (4 * tg + 1 < nt) ? r.v1 : z;
+    const uint4 d = (4 * tg + 2 < nt) ? r.v2 : z;
+    const uint4 e4 = (4 * tg + 3 < nt) ? r.v3 : z;
+    const uint32_t wa[4] = {a.x, a.y, a.z, a.w}, wb[4] = {b.x, b.y, b.z, b.w};
+    const uint32_t wd[4] = {d.x, d.y, d.z, d.w}, we[4] = {e4.x, e4.y, e4.z, e4.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int w = e >> 1, hi = e & 1;
+      *reinterpret_cast<uint2*>(c.Vt + (8 * ch + e) * VTS + 4 * tg) =
+          make_uint2(half16(wa[w], hi) | (half16(wb[w], hi) << 16),
+                     half16(wd[w], hi) | (half16(we[w], hi) << 16));
+    }
+  }
+}
+
+template <int D>
+__device__ void verify_tile_mfma(const AttnParams& p, const Item& it, char* smem) {
+  constexpr int NCH = D / 8;   // 16-byte chunks per K/V row
   constexpr int KS = D / 32;   // k-steps of S^T = K Q^T
   constexpr int DT = D / 16;   // d tiles of O^T
   constexpr int TT = VERIFY_TILE;
@@ -106,7 +233,7 @@ __device__ void verify_tile_mfma(const AttnParams& p, const WorkItem& it, const 
   const int rows_q = p.k + 1;
   const int R = rows_q * G;
   const int g = it.g;
-  const int L = rq.L;
+  const int L = it.L;
   const int jb = it.begin, je = it.end;
 
   uint4* Ks = reinterpret_cast<uint4*>(smem);
@@ -127,7 +254,7 @@ __device__ void verify_tile_mfma(const AttnParams& p, const WorkItem& it, const 
   bf16x8 qop[KS];
   {
     const uint16_t* qrow =
-        reinterpret_cast<const uint16_t*>(p.q) + ((int64_t)(rq.row0 + qi) * Hq + h) * D;
+        reinterpret_cast<const uint16_t*>(p.q) + ((int64_t)(it.row0 + qi) * Hq + h) * D;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       uint4 v = make_uint4(0u, 0u, 0u, 0u);
@@ -135,56 +262,25 @@ __device__ void verify_tile_mfma(const AttnParams& p, const WorkItem& it, const 
       qop[s] = __builtin_bit_cast(bf16x8, v);
     }
   }
+  const uint16_t* kpool = reinterpret_cast<const uint16_t*>(p.k_pool);
+  const uint16_t* vpool = reinterpret_cast<const uint16_t*>(p.v_pool);
+  __syncthreads();  // slots visible
 
+  // Loads are unconditional (a token past the chunk end re-reads the chunk's
+  // last row) so that no branch separates them and several tiles stay in
+  // flight; validity is applied when the registers are staged into LDS.
+  const VerifyTileCtx<D> ctx{Ks, Vt, slots, kpool, vpool, tid, nthr, jb, je, g, Hkv};
   float m_run = NEG_INF, l_run = 0.f;
   f32x4 oacc[DT];
 #pragma unroll
   for (int i = 0; i < DT; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int last_vis = L - rows_q + qi;
-  float* lrow = p.logits + rq.off + ((int64_t)qi * Hq + h) * L;
+  float* lrow = p.logits + it.off + ((int64_t)qi * Hq + h) * L;
   const float sc = p.sm_scale;
-  const uint16_t* kpool = reinterpret_cast<const uint16_t*>(p.k_pool);
-  const uint16_t* vpool = reinterpret_cast<const uint16_t*>(p.v_pool);
+  const bool rows_aligned = ((it.off | (int64_t)L) & 3) == 0;  // every logits row 16-byte aligned
 
-  for (int t0 = jb; t0 < je; t0 += TT) {
-    const int nt = min(TT, je - t0);
-    __syncthreads();  // slots ready / previous tile consumed
-    for (int pc = tid; pc < TT * NCH; pc += nthr) {
-      const int tau = pc / NCH, c = pc % NCH;
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (tau < nt) {
-        const int64_t slot = slots[t0 - jb + tau];
-        v = *reinterpret_cast<const uint4*>(kpool + (slot * Hkv + g) * D + 8 * c);
-      }
-      Ks[tau * NCH + (c ^ kswz<NCH>(tau))] = v;
-    }
-    for (int u = tid; u < (TT / 4) * NCH; u += nthr) {
-      const int tg = u / NCH, c = u % NCH;
-      uint32_t w[4][4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int tau = 4 * tg + i;
-        uint4 v = make_uint4(0u, 0u, 0u, 0u);
-        if (tau < nt) {
-          const int64_t slot = slots[t0 - jb + tau];
-          v = *reinterpret_cast<const uint4*>(vpool + (slot * Hkv + g) * D + 8 * c);
-        }
-        w[i][0] = v.x; w[i][1] = v.y; w[i][2] = v.z; w[i][3] = v.w;
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int sh = 16 * (e & 1);
-        const uint32_t a0 = (w[0][e >> 1] >> sh) & 0xffffu;
-        const uint32_t a1 = (w[1][e >> 1] >> sh) & 0xffffu;
-        const uint32_t a2 = (w[2][e >> 1] >> sh) & 0xffffu;
-        const uint32_t a3 = (w[3][e >> 1] >> sh) & 0xffffu;
-        *reinterpret_cast<uint2*>(Vt + (8 * c + e) * VTS + 4 * tg) =
-            make_uint2(a0 | (a1 << 16), a2 | (a3 << 16));
-      }
-    }
-    __syncthreads();
-    if (!wave_active) continue;
-
+  auto compute = [&](int t0) {
+    if (!wave_active) return;
     f32x4 sacc[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
@@ -198,7 +294,6 @@ __device__ void verify_tile_mfma(const AttnParams& p, const WorkItem& it, const 
                                                           sacc[t], 0, 0, 0);
       }
     }
-
     float v[4][4];
     float mx = NEG_INF;
 #pragma unroll
@@ -217,7 +312,7 @@ __device__ void verify_tile_mfma(const AttnParams& p, const WorkItem& it, const 
       for (int t = 0; t < 4; ++t) {
         const int tb = t0 + 32 * (t >> 1) + 8 * q4 + 4 * (t & 1);
         float* dst = lrow + tb;
-        if (tb + 4 <= je && ((reinterpret_cast<uintptr_t>(dst) & 15) == 0)) {
+        if (rows_aligned && tb + 4 <= je) {
           *reinterpret_cast<float4*>(dst) = make_float4(v[t][0], v[t][1], v[t][2], v[t][3]);
         } else {
 #pragma unroll
@@ -266,15 +361,32 @@ __device__ void verify_tile_mfma(const AttnParams& p, const WorkItem& it, const 
                                                            oacc[dd], 0, 0, 0);
       }
     }
+  };
+
+  KVRegs A, B;
+  fetch_tile(ctx, A, jb);
+  if (jb + TT < je) fetch_tile(ctx, B, jb + TT);
+  for (int t0 = jb; t0 < je; t0 += 2 * TT) {
+    if (t0 != jb) __syncthreads();  // previous tile consumed
+    stage_tile(ctx, A, t0);
+    __syncthreads();
+    if (t0 + 2 * TT < je) fetch_tile(ctx, A, t0 + 2 * TT);
+    compute(t0);
+    if (t0 + TT >= je) break;
+    __syncthreads();
+    stage_tile(ctx, B, t0 + TT);
+    __syncthreads();
+    if (t0 + 3 * TT < je) fetch_tile(ctx, B, t0 + 3 * TT);
+    compute(t0 + TT);
   }
 
   if (!wave_active) return;
   float l_tot = l_run + __shfl_xor(l_run, 16);
   l_tot += __shfl_xor(l_tot, 32);
   if (!row_ok) return;
-  if (rq.nsplit == 1) {
+  if (it.nchunk == 1) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    uint16_t* orow = reinterpret_cast<uint16_t*>(p.o) + ((int64_t)(rq.row0 + qi) * Hq + h) * D;
+    uint16_t* orow = reinterpret_cast<uint16_t*>(p.o) + ((int64_t)(it.row0 + qi) * Hq + h) * D;
 #pragma unroll
     for (int dd = 0; dd < DT; ++dd) {
       const uint32_t b0 = f2bf(oacc[dd][0] * inv), b1 = f2bf(oacc[dd][1] * inv);
@@ -282,9 +394,9 @@ __device__ void verify_tile_mfma(const AttnParams& p, const WorkItem& it, const 
       *reinterpret_cast<uint2*>(orow + 16 * dd + 4 * q4) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
     }
     if (q4 == 0)
-      p.lse[(int64_t)(rq.row0 + qi) * Hq + h] = l_tot > 0.f ? m_run + logf(l_tot) : NEG_INF;
+      p.lse[(int64_t)(it.row0 + qi) * Hq + h] = l_tot > 0.f ? m_run + logf(l_tot) : NEG_INF;
   } else {
-    const int64_t pr = rq.part_row0 + (int64_t)(g * rq.nsplit + it.split) * R + rho;
+    const int64_t pr = it.part_row0 + (int64_t)it.split * R + rho;
     float* po = p.part_o + pr * D;
 #pragma unroll
     for (int dd = 0; dd < DT; ++dd)
@@ -297,18 +409,18 @@ __device__ void verify_tile_mfma(const AttnParams& p, const WorkItem& it, const 
   }
 }
 
-// --------------------------------------------------------------------------
-// VALU gather tile: the GQA group's G query heads of one query row attend to a
-// set of positions -- a draft row's index-list entries [begin, end), or (fp32
-// verify) the contiguous positions [begin, end) with a causal limit.  Each K/V
-// row is read as 16-byte pieces by LPR consecutive lanes, partial dot products
-// are reduced with lane shuffles, the softmax statistics of each block go
-// through LDS, and P*V accumulates per lane before a final cross-wave sum.
-// --------------------------------------------------------------------------
+// ==========================================================================
+// VALU gather tile: the G query heads of one query row attend to a set of
+// positions -- a draft row's list entries [begin, end), or (fp32 verify) the
+// positions [begin, end) under a causal limit.  LPR consecutive lanes read one
+// K/V row as 16-byte pieces; partial dot products are reduced with lane
+// shuffles; each block's softmax statistics go through LDS; P*V accumulates per
+// lane and is summed across waves at the end.  Two blocks of rows are in flight
+// in registers while a third is processed.
+// ==========================================================================
 template <int D, typename T, int GM>
-__device__ void gather_tile_valu(const AttnParams& p, const WorkItem& it, const ReqDesc& rq,
-                                 char* smem, bool is_list, int qi, int last_vis, float* lrow,
-                                 int rho0, int Rr) {
+__device__ void gather_tile_valu(const AttnParams& p, const Item& it, char* smem, bool is_list,
+                                 int qi, int last_vis, float* lrow, int rho0, int Rr) {
   constexpr int E = Piece<T>::E;   // elements per 16-byte piece
   constexpr int LPR = D / E;       // lanes per K/V row
   constexpr int TPT = 4;           // rows per thread per block
@@ -318,7 +430,7 @@ __device__ void gather_tile_valu(const AttnParams& p, const WorkItem& it, const 
   const int c = tid % LPR, tl = tid / LPR, NTL = nthr / LPR;
   const int TB = NTL * TPT;
   const int nent = it.end - it.begin;
-  const int L = rq.L;
+  const int L = it.L;
 
   int32_t* slots = reinterpret_cast<int32_t*>(smem);
   float* scs = reinterpret_cast<float*>(slots + DRAFT_MAX_CHUNK);  // [GM][TB]
@@ -326,7 +438,7 @@ __device__ void gather_tile_valu(const AttnParams& p, const WorkItem& it, const 
   float* red = st + 3 * GM;                                          // [nwaves][GM][D]
 
   const int32_t* ptr = p.page_table + (int64_t)it.r * p.pt_stride;
-  const int32_t* list = is_list ? p.idx + rq.off + (int64_t)g * rq.list_len : nullptr;
+  const int32_t* list = is_list ? p.idx_in + it.off : nullptr;
   for (int t = tid; t < nent; t += nthr) {
     const int pos = is_list ? list[it.begin + t] : it.begin + t;
     int32_t s = -1;
@@ -339,7 +451,7 @@ __device__ void gather_tile_valu(const AttnParams& p, const WorkItem& it, const 
   }
 
   float qv[GM][E];
-  const T* qbase = reinterpret_cast<const T*>(p.q) + ((int64_t)(rq.row0 + qi) * Hq + g * G) * D;
+  const T* qbase = reinterpret_cast<const T*>(p.q) + ((int64_t)(it.row0 + qi) * Hq + g * G) * D;
 #pragma unroll
   for (int hh = 0; hh < GM; ++hh) {
     uint4 v = make_uint4(0u, 0u, 0u, 0u);
@@ -357,21 +469,21 @@ __device__ void gather_tile_valu(const AttnParams& p, const WorkItem& it, const 
   const float sc = p.sm_scale;
   __syncthreads();
 
-  for (int b0 = 0; b0 < nent; b0 += TB) {
-    int32_t sl[TPT];
-    uint4 kr[TPT], vr[TPT];
+  // Unconditional loads (an invalid entry reads pool row 0) keep the blocks in
+  // flight; invalid entries are masked when the block is processed.
+  auto fetch = [&](int b0, int32_t (&s_)[TPT], uint4 (&k_)[TPT], uint4 (&v_)[TPT]) {
 #pragma unroll
     for (int i = 0; i < TPT; ++i) {
       const int t = b0 + tl + NTL * i;
-      sl[i] = (t < nent) ? slots[t] : -1;
-      kr[i] = make_uint4(0u, 0u, 0u, 0u);
-      vr[i] = make_uint4(0u, 0u, 0u, 0u);
-      if (sl[i] >= 0) {
-        const int64_t off = ((int64_t)sl[i] * Hkv + g) * D + c * E;
-        kr[i] = *reinterpret_cast<const uint4*>(kpool + off);
-        vr[i] = *reinterpret_cast<const uint4*>(vpool + off);
-      }
+      const int32_t sv = slots[min(t, nent - 1)];
+      s_[i] = (t < nent) ? sv : -1;
+      const int64_t off = ((int64_t)max(sv, 0) * Hkv + g) * D + c * E;
+      k_[i] = *reinterpret_cast<const uint4*>(kpool + off);
+      v_[i] = *reinterpret_cast<const uint4*>(vpool + off);
     }
+  };
+  auto process = [&](int b0, const int32_t (&sl)[TPT], const uint4 (&kr)[TPT],
+                     const uint4 (&vr)[TPT]) {
 #pragma unroll
     for (int i = 0; i < TPT; ++i) {
       float kf[E];
@@ -382,9 +494,7 @@ __device__ void gather_tile_valu(const AttnParams& p, const WorkItem& it, const 
         float a = 0.f;
 #pragma unroll
         for (int e = 0; e < E; ++e) a = fmaf(qv[hh][e], kf[e], a);
-#pragma unroll
-        for (int off = LPR / 2; off > 0; off >>= 1) a += __shfl_xor(a, off);
-        dot[hh] = a;
+        dot[hh] = group_sum<LPR>(a);
       }
       const int u = tl + NTL * i;
       if (c == 0) {
@@ -451,7 +561,19 @@ __device__ void gather_tile_valu(const AttnParams& p, const WorkItem& it, const 
         }
       }
     }
-    __syncthreads();
+    __syncthreads();  // scs and st reused by the next block
+  };
+
+  int32_t sA[TPT], sB[TPT];
+  uint4 kA[TPT], vA[TPT], kB[TPT], vB[TPT];
+  fetch(0, sA, kA, vA);
+  if (TB < nent) fetch(TB, sB, kB, vB);
+  for (int b0 = 0; b0 < nent; b0 += 2 * TB) {
+    process(b0, sA, kA, vA);
+    if (b0 + 2 * TB < nent) fetch(b0 + 2 * TB, sA, kA, vA);
+    if (b0 + TB >= nent) break;
+    process(b0 + TB, sB, kB, vB);
+    if (b0 + 3 * TB < nent) fetch(b0 + 3 * TB, sB, kB, vB);
   }
 
   // lanes of one wave that share c hold partial sums of the same output slice
@@ -475,12 +597,12 @@ __device__ void gather_tile_valu(const AttnParams& p, const WorkItem& it, const 
     for (int w = 0; w < nwaves; ++w) acc += red[(w * GM + hh) * D + d];
     const float m = st[hh], l = st[GM + hh];
     const int h = g * G + hh;
-    if (rq.nsplit == 1) {
-      const int64_t orow = (int64_t)(rq.row0 + qi) * Hq + h;
+    if (it.nchunk == 1) {
+      const int64_t orow = (int64_t)(it.row0 + qi) * Hq + h;
       store_out<T>(reinterpret_cast<T*>(p.o) + orow * D + d, l > 0.f ? acc / l : 0.f);
       if (d == 0) p.lse[orow] = l > 0.f ? m + logf(l) : NEG_INF;
     } else {
-      const int64_t pr = rq.part_row0 + (int64_t)(g * rq.nsplit + it.split) * Rr + rho0 + hh;
+      const int64_t pr = it.part_row0 + (int64_t)it.split * Rr + rho0 + hh;
       p.part_o[pr * D + d] = acc;
       if (d == 0) {
         p.part_ml[2 * pr] = m;
@@ -493,116 +615,153 @@ __device__ void gather_tile_valu(const AttnParams& p, const WorkItem& it, const 
 template <int D, typename T, int GM>
 __global__ void __launch_bounds__(512) attn_kernel(AttnParams p) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  const WorkItem it = p.items[blockIdx.x];
-  const ReqDesc rq = p.reqs[it.r];
-  if (rq.kind == KIND_VERIFY) {
+  const Item it = p.items[blockIdx.x];
+  if (it.kind == KIND_NOP) return;
+  if (it.kind == KIND_VERIFY) {
     if constexpr (sizeof(T) == 2) {
-      verify_tile_mfma<D>(p, it, rq, smem);
+      verify_tile_mfma<D>(p, it, smem);
     } else {
       const int qi = it.qi;
-      const int last_vis = rq.L - (p.k + 1) + qi;
-      float* lrow = p.logits + rq.off + ((int64_t)qi * p.Hq + it.g * p.G) * rq.L;
-      gather_tile_valu<D, T, GM>(p, it, rq, smem, false, qi, last_vis, lrow, qi * p.G,
+      const int last_vis = it.L - (p.k + 1) + qi;
+      float* lrow = p.logits + it.off + ((int64_t)qi * p.Hq + it.g * p.G) * it.L;
+      gather_tile_valu<D, T, GM>(p, it, smem, false, qi, last_vis, lrow, qi * p.G,
                                  (p.k + 1) * p.G);
     }
   } else {
-    gather_tile_valu<D, T, GM>(p, it, rq, smem, true, 0, 0x7fffffff, nullptr, 0, p.G);
+    gather_tile_valu<D, T, GM>(p, it, smem, true, 0, 0x7fffffff, nullptr, 0, p.G);
   }
 }
 
-// --------------------------------------------------------------------------
-// split-K merge: m* = max_s m_s, l* = sum_s l_s e^{m_s - m*},
+// ==========================================================================
+// PillarAttn post-pass
+// ==========================================================================
+// split-K merge of one (r, g): m* = max_s m_s, l* = sum_s l_s e^{m_s - m*},
 // O = sum_s e^{m_s - m*} O_s / l*, LSE = m* + ln l*.
-// --------------------------------------------------------------------------
 template <int D, typename T>
-__global__ void __launch_bounds__(256) merge_kernel(MergeParams mp) {
-  const MergeItem mi = mp.items[blockIdx.x];
-  const ReqDesc rq = mp.reqs[mi.r];
-  const int G = mp.G;
-  const int rows_q = rq.kind == KIND_VERIFY ? mp.k + 1 : 1;
-  const int R = rows_q * G;
-  const int ns = rq.nsplit;
-  const int64_t base = rq.part_row0 + (int64_t)mi.g * ns * R;
-  for (int x = threadIdx.x; x < R * D; x += blockDim.x) {
-    const int rho = x / D, d = x % D;
+__device__ void merge_group(const PostParams& p, const PostItem& it) {
+  const int G = p.G;
+  const int R = it.rows_q * G;
+  const int ns = it.nchunk;
+  constexpr int D4 = D / 4;
+  for (int x = threadIdx.x; x < R * D4; x += blockDim.x) {
+    const int rho = x / D4, d4 = x % D4;
     float mstar = NEG_INF;
-    for (int s = 0; s < ns; ++s) mstar = fmaxf(mstar, mp.part_ml[2 * (base + (int64_t)s * R + rho)]);
-    float lsum = 0.f, acc = 0.f;
+    for (int s = 0; s < ns; ++s)
+      mstar = fmaxf(mstar, p.part_ml[2 * (it.part_row0 + (int64_t)s * R + rho)]);
+    float lsum = 0.f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     if (mstar != NEG_INF) {
       for (int s = 0; s < ns; ++s) {
-        const int64_t pr = base + (int64_t)s * R + rho;
-        const float m = mp.part_ml[2 * pr], l = mp.part_ml[2 * pr + 1];
+        const int64_t pr = it.part_row0 + (int64_t)s * R + rho;
+        const float m = p.part_ml[2 * pr], l = p.part_ml[2 * pr + 1];
         const float w = (m == NEG_INF) ? 0.f : fast_exp2((m - mstar) * LOG2E);
+        const float4 o = *reinterpret_cast<const float4*>(p.part_o + pr * D + 4 * d4);
         lsum = fmaf(w, l, lsum);
-        acc = fmaf(w, mp.part_o[pr * D + d], acc);
+        acc.x = fmaf(w, o.x, acc.x);
+        acc.y = fmaf(w, o.y, acc.y);
+        acc.z = fmaf(w, o.z, acc.z);
+        acc.w = fmaf(w, o.w, acc.w);
       }
     }
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
     const int qi = rho / G, hh = rho % G;
-    const int64_t orow = (int64_t)(rq.row0 + qi) * mp.Hq + mi.g * G + hh;
-    store_out<T>(reinterpret_cast<T*>(mp.o) + orow * D + d, lsum > 0.f ? acc / lsum : 0.f);
-    if (d == 0) mp.lse[orow] = lsum > 0.f ? mstar + logf(lsum) : NEG_INF;
+    const int64_t orow = (int64_t)(it.row0 + qi) * p.Hq + it.g * G + hh;
+    T* dst = reinterpret_cast<T*>(p.o) + orow * D + 4 * d4;
+    store_out<T>(dst + 0, acc.x * inv);
+    store_out<T>(dst + 1, acc.y * inv);
+    store_out<T>(dst + 2, acc.z * inv);
+    store_out<T>(dst + 3, acc.w * inv);
+    if (d4 == 0) p.lse[orow] = lsum > 0.f ? mstar + logf(lsum) : NEG_INF;
   }
 }
 
-// --------------------------------------------------------------------------
-// averaged exact scores: pbar[j] = 1/(n G) sum_i sum_hh exp(logit - LSE)
-// --------------------------------------------------------------------------
-__global__ void __launch_bounds__(256) avg_kernel(AvgParams ap) {
-  __shared__ float lse_s[MAX_AVG_TERMS];
-  const AvgItem ai = ap.avg[blockIdx.x];
-  const TopkItem ti = ap.topk[ai.t];
-  const int G = ap.G, Hq = ap.Hq, n = ap.row_count, a = ap.row_begin;
-  const int terms = n * G;
-  const int L = ti.L;
-  for (int x = threadIdx.x; x < terms; x += blockDim.x) {
-    const int i = a + x / G, hh = x % G;
-    lse_s[x] = ap.lse[(int64_t)(ti.lse_row0 + i) * Hq + ti.g * G + hh];
+// Block-wide exclusive prefix of per-thread counts (wave scan + per-wave
+// totals in LDS).  Returns the prefix; *total receives the block sum.
+__device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* wsum, uint32_t* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
+  uint32_t incl = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t y = __shfl_up(incl, off);
+    if (lane >= off) incl += y;
   }
+  if (lane == 63) wsum[wave] = incl;
   __syncthreads();
-  const float inv = 1.f / (float)terms;
-  const float* lg = ap.logits + ti.logits_off;
-  const int jend = min(ai.j0 + AVG_SPAN, L);
-  for (int j = ai.j0 + threadIdx.x; j < jend; j += blockDim.x) {
-    float s = 0.f;
-    for (int x = 0; x < terms; ++x) {
-      const int i = a + x / G, hh = x % G;
-      const float l = lg[((int64_t)i * Hq + ti.g * G + hh) * L + j];
-      s += (l == NEG_INF) ? 0.f : expf(l - lse_s[x]);
-    }
-    ap.pbar[ti.pbar_off + j] = s * inv;
+  uint32_t before = 0, all = 0;
+  for (int w = 0; w < nwaves; ++w) {
+    const uint32_t s = wsum[w];
+    if (w < wave) before += s;
+    all += s;
   }
+  __syncthreads();  // wsum reusable
+  *total = all;
+  return before + incl - v;
 }
 
-// --------------------------------------------------------------------------
-// top-K by MSB-first radix select over the fp32 bit patterns (scores are >= 0,
-// so the unsigned order of the bits is the numeric order), then an ordered
-// compaction: every position above the threshold, plus the lowest positions
-// equal to it, written ascending.
-// --------------------------------------------------------------------------
-__global__ void __launch_bounds__(1024) select_kernel(SelectParams sp) {
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t s_prefix, s_rem;
-  __shared__ uint32_t cnt_eq[16], cnt_take[16];
-  __shared__ uint32_t s_base_eq, s_base_take;
-  const TopkItem ti = sp.topk[blockIdx.x];
-  const uint32_t* keys = reinterpret_cast<const uint32_t*>(sp.pbar + ti.pbar_off);
-  const int L = ti.L, K = ti.K;
+// Top-K of L non-negative fp32 scores (their bit patterns order like the
+// values).  MSB-first radix select, 8 bits per pass, finds the K-th largest
+// value tau and how many positions equal to it are kept; the compaction then
+// writes every position above tau and the lowest positions equal to tau,
+// ascending.  Thread t owns the KPT consecutive positions c0 + KPT t + [0, KPT)
+// of each chunk of KPT*nthr positions; keys stay in registers when L fits one
+// chunk and are re-read chunk by chunk otherwise.  Each wave counts into its
+// own histogram so that atomics only contend inside a wave.
+// LDS: 276 + 256 * waves words.
+template <int KPT>
+__device__ void select_topk(const float* scores, int L, int K, int32_t* out, char* smem) {
+  static_assert(KPT % 4 == 0, "keys are loaded four at a time");
+  uint32_t* hist = reinterpret_cast<uint32_t*>(smem);  // [256] block histogram
+  uint32_t* sv = hist + 256;                           // prefix, rem
+  uint32_t* wsum = sv + 4;                             // [16]
+  uint32_t* whist = wsum + 16;                         // [nwaves][256] per-wave histograms
+  const uint32_t* keys = reinterpret_cast<const uint32_t*>(scores);
   const int tid = threadIdx.x, nthr = blockDim.x, lane = tid & 63, wave = tid >> 6;
-  const int nwaves = nthr >> 6;
+  const int span = KPT * nthr;
+  const bool resident = L <= span;
+  const bool vec = (reinterpret_cast<uintptr_t>(scores) & 15) == 0;
+  uint32_t key[KPT];
+  auto load = [&](int c0) {
+    const int j0 = c0 + KPT * tid;
+#pragma unroll
+    for (int m = 0; m < KPT; m += 4) {
+      const int j = j0 + m;
+      if (vec && j + 4 <= L) {
+        const uint4 v = *reinterpret_cast<const uint4*>(keys + j);
+        key[m] = v.x;
+        key[m + 1] = v.y;
+        key[m + 2] = v.z;
+        key[m + 3] = v.w;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) key[m + e] = (j + e < L) ? keys[j + e] : 0u;
+      }
+    }
+  };
+  if (resident) load(0);
+  __syncthreads();
   if (tid == 0) {
-    s_prefix = 0u;
-    s_rem = (uint32_t)K;
-    s_base_eq = 0u;
-    s_base_take = 0u;
+    sv[0] = 0u;
+    sv[1] = (uint32_t)K;
   }
+  const int nwaves = nthr >> 6;
+  uint32_t* my_hist = whist + 256 * wave;
   uint32_t mask = 0u;
   for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int b = tid; b < 256; b += nthr) hist[b] = 0u;
+    for (int b = tid; b < 256 * nwaves; b += nthr) whist[b] = 0u;
     __syncthreads();
-    const uint32_t prefix = s_prefix;
-    for (int j = tid; j < L; j += nthr) {
-      const uint32_t key = keys[j];
-      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+    const uint32_t prefix = sv[0];
+    for (int c0 = 0; c0 < L; c0 += span) {
+      if (!resident) load(c0);
+      const int j0 = c0 + KPT * tid;
+#pragma unroll
+      for (int m = 0; m < KPT; ++m)
+        if (j0 + m < L && (key[m] & mask) == prefix) atomicAdd(&my_hist[(key[m] >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    for (int b = tid; b < 256; b += nthr) {
+      uint32_t sum = 0u;
+      for (int w = 0; w < nwaves; ++w) sum += whist[256 * w + b];
+      hist[b] = sum;
     }
     __syncthreads();
     if (wave == 0) {
@@ -619,14 +778,14 @@ __global__ void __launch_bounds__(1024) select_kernel(SelectParams sp) {
         if (lane >= off) incl += y;
       }
       const uint32_t excl = incl - sum;
-      const uint32_t rem = s_rem;
+      const uint32_t rem = sv[1];
       if (excl < rem && incl >= rem) {
         uint32_t acc = excl;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           if (acc + cnt[i] >= rem) {
-            s_prefix = prefix | ((uint32_t)(255 - 4 * lane - i) << shift);
-            s_rem = rem - acc;
+            sv[0] = prefix | ((uint32_t)(255 - 4 * lane - i) << shift);
+            sv[1] = rem - acc;
             break;
           }
           acc += cnt[i];
@@ -636,51 +795,163 @@ __global__ void __launch_bounds__(1024) select_kernel(SelectParams sp) {
     mask |= 255u << shift;
     __syncthreads();
   }
-  const uint32_t tau = s_prefix, rem = s_rem;
-  int32_t* out = sp.idx + ti.idx_off;
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int c0 = 0; c0 < L; c0 += nthr) {
-    const int j = c0 + tid;
-    const uint32_t key = j < L ? keys[j] : 0u;
-    const bool gt = j < L && key > tau;
-    const bool eq = j < L && key == tau;
-    const uint64_t beq = __ballot(eq);
-    if (lane == 0) cnt_eq[wave] = (uint32_t)__popcll(beq);
-    __syncthreads();
-    uint32_t eq_rank = s_base_eq + (uint32_t)__popcll(beq & lt_mask);
-    for (int w = 0; w < wave; ++w) eq_rank += cnt_eq[w];
-    const bool take = gt || (eq && eq_rank < rem);
-    const uint64_t btk = __ballot(take);
-    if (lane == 0) cnt_take[wave] = (uint32_t)__popcll(btk);
-    __syncthreads();
-    uint32_t pos = s_base_take + (uint32_t)__popcll(btk & lt_mask);
-    for (int w = 0; w < wave; ++w) pos += cnt_take[w];
-    if (take && pos < (uint32_t)K) out[pos] = j;
-    __syncthreads();
-    if (tid == 0) {
-      uint32_t te = 0u, tt = 0u;
-      for (int w = 0; w < nwaves; ++w) {
-        te += cnt_eq[w];
-        tt += cnt_take[w];
-      }
-      s_base_eq += te;
-      s_base_take += tt;
+  const uint32_t tau = sv[0], rem = sv[1];
+  uint32_t base_eq = 0, base_take = 0;
+  for (int c0 = 0; c0 < L; c0 += span) {
+    if (!resident) load(c0);
+    const int j0 = c0 + KPT * tid;
+    uint32_t n_gt = 0, n_eq = 0;
+#pragma unroll
+    for (int m = 0; m < KPT; ++m) {
+      const bool ok = j0 + m < L;
+      n_gt += (ok && key[m] > tau) ? 1u : 0u;
+      n_eq += (ok && key[m] == tau) ? 1u : 0u;
     }
-    __syncthreads();
+    uint32_t tot_eq, tot_take;
+    const uint32_t eq_before = base_eq + block_exclusive_scan(n_eq, wsum, &tot_eq);
+    // equal keys are kept in position order until rem of them are taken
+    const uint32_t eq_keep = eq_before >= rem ? 0u : min(n_eq, rem - eq_before);
+    uint32_t pos = base_take + block_exclusive_scan(n_gt + eq_keep, wsum, &tot_take);
+    uint32_t eq_seen = 0;
+#pragma unroll
+    for (int m = 0; m < KPT; ++m) {
+      const bool ok = j0 + m < L;
+      bool take = ok && key[m] > tau;
+      if (ok && key[m] == tau) {
+        take = eq_seen < eq_keep;
+        ++eq_seen;
+      }
+      if (take && pos < (uint32_t)K) out[pos++] = j0 + m;
+    }
+    base_eq += tot_eq;
+    base_take += tot_take;
   }
 }
 
-// --------------------------------------------------------------------------
-// launchers
-// --------------------------------------------------------------------------
+template <int D, typename T>
+__global__ void __launch_bounds__(256) post_kernel(PostParams p) {
+  __shared__ float lse2_s[MAX_AVG_TERMS];
+  __shared__ int64_t rowoff_s[MAX_AVG_TERMS];
+  const PostItem it = p.items[blockIdx.x];
+  if (it.kind == POST_NOP) return;
+  if (it.kind == POST_MERGE) {
+    merge_group<D, T>(p, it);
+    return;
+  }
+  // POST_AVG: LSE of the averaged rows (one thread per (row, head)), then
+  // their exact scores averaged over positions [j0, j1)
+  const int tid = threadIdx.x, nthr = blockDim.x;
+  const int G = p.G, Hq = p.Hq, a = p.avg_row_begin, n = p.avg_row_count;
+  const int terms = n * G;
+  const int R = it.rows_q * G;
+  const int L = it.L;
+  for (int x = tid; x < terms; x += nthr) {
+    const int i = a + x / G, hh = x % G;
+    const int rho = i * G + hh;
+    float lse;
+    if (it.nchunk == 1) {
+      lse = p.lse[(int64_t)(it.row0 + i) * Hq + it.g * G + hh];
+    } else {
+      // one pass: running max with the sum rescaled as it grows
+      float mstar = NEG_INF, lsum = 0.f;
+      for (int s0 = 0; s0 < it.nchunk; s0 += 8) {
+        float mm[8], ll[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int s = min(s0 + u, it.nchunk - 1);
+          const int64_t pr = it.part_row0 + (int64_t)s * R + rho;
+          mm[u] = p.part_ml[2 * pr];
+          ll[u] = p.part_ml[2 * pr + 1];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          if (s0 + u >= it.nchunk || mm[u] == NEG_INF) continue;
+          if (mm[u] > mstar) {
+            lsum = (mstar == NEG_INF) ? 0.f : lsum * fast_exp2((mstar - mm[u]) * LOG2E);
+            mstar = mm[u];
+          }
+          lsum = fmaf(ll[u], fast_exp2((mm[u] - mstar) * LOG2E), lsum);
+        }
+      }
+      lse = lsum > 0.f ? mstar + logf(lsum) : NEG_INF;
+    }
+    lse2_s[x] = lse * LOG2E;
+    rowoff_s[x] = ((int64_t)i * Hq + it.g * G + hh) * L;
+  }
+  __syncthreads();
+  const float* lg = p.logits + it.logits_off;
+  float* pbar = p.pbar + it.pbar_off;
+  const float inv = 1.f / (float)terms;
+  const bool vec = ((it.logits_off | (int64_t)L) & 3) == 0;
+  for (int j4 = it.j0 + 4 * tid; j4 < it.j1; j4 += 4 * nthr) {
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    if (vec && j4 + 4 <= it.j1) {
+#pragma unroll 16
+      for (int x = 0; x < terms; ++x) {
+        const float4 v = *reinterpret_cast<const float4*>(lg + rowoff_s[x] + j4);
+        const float l2 = lse2_s[x];
+        const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          acc[e] += (vv[e] == NEG_INF || l2 == NEG_INF) ? 0.f : fast_exp2(fmaf(vv[e], LOG2E, -l2));
+      }
+      *reinterpret_cast<float4*>(pbar + j4) =
+          make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+    } else {
+      for (int e = 0; e < 4; ++e) {
+        const int j = j4 + e;
+        if (j >= it.j1) break;
+        float s = 0.f;
+        for (int x = 0; x < terms; ++x) {
+          const float v = lg[rowoff_s[x] + j];
+          const float l2 = lse2_s[x];
+          s += (v == NEG_INF || l2 == NEG_INF) ? 0.f : fast_exp2(fmaf(v, LOG2E, -l2));
+        }
+        pbar[j] = s * inv;
+      }
+    }
+  }
+}
+
+// Selection launch: one workgroup per verify (request, KV head).
+constexpr int SELECT_THREADS = 1024;
+constexpr int SELECT_KPT = 8;  // keys per thread kept in registers (8192 at 1024 threads)
+
+__global__ void __launch_bounds__(SELECT_THREADS) select_kernel(SelectParams sp) {
+  __shared__ __attribute__((aligned(16))) char smem[(276 + 256 * (SELECT_THREADS / 64)) * 4];
+  const PostItem it = sp.items[blockIdx.x];
+  select_topk<SELECT_KPT>(sp.pbar + it.pbar_off, it.L, it.K, sp.idx_out + it.idx_off, smem);
+}
+
+// ==========================================================================
+// host-side shapes and launchers
+// ==========================================================================
+static int group_template(int G) { return G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : G <= 5 ? 5 : 8; }
+
+size_t attn_smem_bytes(int dtype, int head_dim, int G, int nthr, bool mfma_verify, bool valu) {
+  size_t s = 16;
+  if (mfma_verify)
+    s = std::max(s, head_dim == 128 ? mfma_smem_bytes<128>() : mfma_smem_bytes<64>());
+  if (valu) {
+    const int GM = group_template(G);
+    const int E = dtype == 0 ? 8 : 4;
+    const int LPR = head_dim / E;
+    const int TB = (nthr / LPR) * 4;
+    const size_t v = (size_t)DRAFT_MAX_CHUNK * 4 + (size_t)GM * TB * 4 + 3 * GM * 4 +
+                     (size_t)(nthr / 64) * GM * head_dim * 4;
+    s = std::max(s, v);
+  }
+  return s;
+}
+
 template <int D, typename T>
 static hipError_t launch_attn_g(const AttnParams& p, int nitems, int nthr, size_t smem,
                                 hipStream_t st) {
   const int G = p.G;
-#define SPA_ATTN(GMV)                                                                       \
-  do {                                                                                      \
-    hipLaunchKernelGGL((attn_kernel<D, T, GMV>), dim3(nitems), dim3(nthr), smem, st, p);    \
-    return hipGetLastError();                                                               \
+#define SPA_ATTN(GMV)                                                                    \
+  do {                                                                                   \
+    hipLaunchKernelGGL((attn_kernel<D, T, GMV>), dim3(nitems), dim3(nthr), smem, st, p); \
+    return hipGetLastError();                                                            \
   } while (0)
   if (G <= 1) SPA_ATTN(1);
   if (G <= 2) SPA_ATTN(2);
@@ -701,32 +972,25 @@ hipError_t launch_attn(const AttnParams& p, int dtype, int head_dim, int nitems,
   return launch_attn_g<64, float>(p, nitems, nthr, smem, st);
 }
 
-hipError_t launch_merge(const MergeParams& p, int dtype, int head_dim, int nitems,
-                        hipStream_t st) {
+hipError_t launch_select(const SelectParams& sp, int nitems, hipStream_t st) {
+  if (nitems == 0) return hipSuccess;
+  hipLaunchKernelGGL(select_kernel, dim3(nitems), dim3(SELECT_THREADS), 0, st, sp);
+  return hipGetLastError();
+}
+
+hipError_t launch_post(const PostParams& p, int dtype, int head_dim, int nitems, hipStream_t st) {
   if (nitems == 0) return hipSuccess;
   if (dtype == 0) {
     if (head_dim == 128)
-      hipLaunchKernelGGL((merge_kernel<128, uint16_t>), dim3(nitems), dim3(256), 0, st, p);
+      hipLaunchKernelGGL((post_kernel<128, uint16_t>), dim3(nitems), dim3(256), 0, st, p);
     else
-      hipLaunchKernelGGL((merge_kernel<64, uint16_t>), dim3(nitems), dim3(256), 0, st, p);
+      hipLaunchKernelGGL((post_kernel<64, uint16_t>), dim3(nitems), dim3(256), 0, st, p);
   } else {
     if (head_dim == 128)
-      hipLaunchKernelGGL((merge_kernel<128, float>), dim3(nitems), dim3(256), 0, st, p);
+      hipLaunchKernelGGL((post_kernel<128, float>), dim3(nitems), dim3(256), 0, st, p);
     else
-      hipLaunchKernelGGL((merge_kernel<64, float>), dim3(nitems), dim3(256), 0, st, p);
+      hipLaunchKernelGGL((post_kernel<64, float>), dim3(nitems), dim3(256), 0, st, p);
   }
-  return hipGetLastError();
-}
-
-hipError_t launch_avg(const AvgParams& ap, int navg, hipStream_t st) {
-  if (navg == 0) return hipSuccess;
-  hipLaunchKernelGGL(avg_kernel, dim3(navg), dim3(256), 0, st, ap);
-  return hipGetLastError();
-}
-
-hipError_t launch_select(const SelectParams& sp, int ntopk, hipStream_t st) {
-  if (ntopk == 0) return hipSuccess;
-  hipLaunchKernelGGL(select_kernel, dim3(ntopk), dim3(1024), 0, st, sp);
   return hipGetLastError();
 }
 

@@ -7,57 +7,49 @@
 
 namespace spa {
 
-constexpr int MAX_AVG_TERMS = 512;  // averaged (row, head) pairs per KV head
-
 struct AttnParams {
+  const Item* items;  // pinned host plan, read in place
   const void* q;
   const void* k_pool;
   const void* v_pool;
   const int32_t* page_table;
   int64_t pt_stride;
   int64_t num_slots;
-  const int32_t* idx;
+  const int32_t* idx_in;  // draft lists
   void* o;
   float* lse;
   float* logits;
-  const ReqDesc* reqs;
-  const WorkItem* items;
   float* part_o;
   float* part_ml;
   int32_t Hq, Hkv, G, k;
   float sm_scale;
 };
 
-struct MergeParams {
-  const ReqDesc* reqs;
-  const MergeItem* items;
+struct PostParams {
+  const PostItem* items;  // pinned host plan, read in place
   const float* part_o;
   const float* part_ml;
   void* o;
   float* lse;
-  int32_t Hq, G, k;
-};
-
-struct AvgParams {
-  const TopkItem* topk;
-  const AvgItem* avg;
   const float* logits;
-  const float* lse;
   float* pbar;
-  int32_t Hq, G, row_begin, row_count;
+  int32_t Hq, G;
+  int32_t avg_row_begin, avg_row_count;
 };
 
 struct SelectParams {
-  const TopkItem* topk;
+  const PostItem* items;  // one POST_AVG record of each selected (r, g)
   const float* pbar;
-  int32_t* idx;
+  int32_t* idx_out;
 };
+
+// LDS bytes the attention kernel needs for a launch shape.
+size_t attn_smem_bytes(int dtype, int head_dim, int G, int nthr, bool mfma_verify, bool valu);
+size_t post_smem_bytes();
 
 hipError_t launch_attn(const AttnParams& p, int dtype, int head_dim, int nitems, int nthr,
                        size_t smem, hipStream_t st);
-hipError_t launch_merge(const MergeParams& p, int dtype, int head_dim, int nitems,
-                        hipStream_t st);
-hipError_t launch_avg(const AvgParams& ap, int navg, hipStream_t st);
-hipError_t launch_select(const SelectParams& sp, int ntopk, hipStream_t st);
+hipError_t launch_post(const PostParams& p, int dtype, int head_dim, int nitems, hipStream_t st);
+hipError_t launch_select(const SelectParams& sp, int nitems, hipStream_t st);
 
 }  // namespace spa

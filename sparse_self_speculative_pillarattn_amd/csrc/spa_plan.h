@@ -1,66 +1,69 @@
-// spa_plan.h -- work-plan records written by the host planner into the
-// caller's workspace and read by the kernels.  Internal to libspa.
+// spa_plan.h -- work-plan records shared by the host planner and the kernels.
+// Internal to libspa.  The plan lives in pinned host memory and the kernels
+// read it in place; one record per workgroup.
 #pragma once
 #include <stdint.h>
 
 namespace spa {
 
-enum : int32_t { KIND_DRAFT = 0, KIND_VERIFY = 1 };
-
-// One request of the batch (32 bytes).
-struct ReqDesc {
-  int32_t L;          // tokens in context (includes the k+1 verify tokens)
-  int32_t row0;       // first q / o / lse row
-  int32_t kind;       // KIND_DRAFT or KIND_VERIFY
-  int32_t nsplit;     // work items per KV head (1 = outputs written directly)
-  int64_t part_row0;  // first split-K partial row (rows of d floats) of this request
-  int64_t off;        // verify: logits element offset; draft: idx element offset
-  int32_t list_len;   // draft: list entries per KV head; verify: K_r to select
-  int32_t pad_;
+// ---- attention launch ------------------------------------------------------
+enum : int32_t {
+  KIND_NOP = 0,     // padding item (keeps the XCD interleave aligned); exits at once
+  KIND_VERIFY = 1,  // full attention of the verify rows over positions [begin, end)
+  KIND_DRAFT = 2,   // sparse attention of one draft row over list entries [begin, end)
 };
 
-// One attention work item (16 bytes): KV head g of request r over
-// positions [begin, end) (verify) or list entries [begin, end) (draft).
-// qi selects the single query row of an fp32 verify item (VALU path).
-struct WorkItem {
+// One attention work item (64 bytes): KV head g of request r.
+struct Item {
+  int32_t kind;
   int32_t r;
-  uint8_t g;
-  uint8_t qi;
-  uint16_t split;
-  int32_t begin;
+  int32_t g;
+  int32_t qi;         // fp32 verify items: the single query row handled
+  int32_t begin;      // positions (verify) or list entries (draft)
   int32_t end;
-};
-
-// One split-K merge group: request r, KV head g (8 bytes).
-struct MergeItem {
-  int32_t r;
-  int32_t g;
-};
-
-// One verify request's selection job for one KV head (48 bytes).
-struct TopkItem {
-  int32_t r;
-  int32_t g;
-  int32_t L;
-  int32_t K;
-  int64_t pbar_off;    // element offset of this (r, g) row of averaged scores
-  int64_t idx_off;     // element offset of the [K] output list
-  int64_t logits_off;  // element offset of the request's [(k+1)][H_q][L] logits
-  int32_t lse_row0;    // first lse row of the request
+  int32_t L;          // context length of request r
+  int32_t row0;       // first q / o / lse row of request r
+  int32_t nchunk;     // split-K chunks of (r, g); 1 = outputs written directly
+  int32_t split;      // chunk index of this item within (r, g)
+  int32_t list_len;   // draft: entries per KV head
   int32_t pad_;
+  int64_t off;        // verify: logits element offset of request r; draft: list offset of (r, g)
+  int64_t part_row0;  // first split-K partial row of (r, g)
 };
 
-// One averaging block: TopkItem t, positions [j0, j0 + AVG_SPAN).
-struct AvgItem {
-  int32_t t;
-  int32_t j0;
+// ---- PillarAttn post-pass launch -------------------------------------------
+enum : int32_t {
+  POST_NOP = 0,
+  POST_MERGE = 1,  // merge the split-K partials of (r, g) into O and LSE
+  POST_AVG = 2,    // averaged exact scores of positions [j0, j1) of verify (r, g)
 };
 
-constexpr int AVG_SPAN = 1024;     // positions per averaging block
-constexpr int VERIFY_TILE = 64;    // tokens per LDS tile of the MFMA verify path
+// One post-pass item (72 bytes).  The selection launch reads the same record,
+// one per verify (r, g).
+struct PostItem {
+  int32_t kind;
+  int32_t r;
+  int32_t g;
+  int32_t rows_q;      // query rows of request r (k+1 verify, 1 draft)
+  int32_t L;
+  int32_t row0;        // first q / o / lse row of request r
+  int32_t nchunk;      // split-K partials per row (1 = the LSE array is already final)
+  int32_t j0, j1;      // POST_AVG: positions
+  int32_t K;           // positions to select
+  int32_t pad_;
+  int64_t part_row0;   // first split-K partial row of (r, g)
+  int64_t logits_off;  // POST_AVG: logits element offset of request r
+  int64_t idx_off;     // POST_AVG: element offset of the (r, g) output list
+  int64_t pbar_off;    // POST_AVG: element offset of the (r, g) averaged scores
+};
+
+constexpr int AVG_SPAN = 1024;         // positions per averaging item
+constexpr int VERIFY_TILE = 64;        // tokens per LDS tile of the MFMA verify path
 constexpr int VERIFY_MAX_CHUNK = 2048;
 constexpr int DRAFT_MAX_CHUNK = 2048;
-constexpr int MAX_GROUP = 8;       // query heads per KV head handled by the VALU path
-constexpr int MAX_ROW_TILES = 8;   // 16-row MFMA tiles (one wave each, 512 threads max)
+constexpr int MAX_GROUP = 8;           // query heads per KV head on the VALU path
+constexpr int MAX_ROW_TILES = 8;       // 16-row MFMA tiles (one wave each, 512 threads max)
+constexpr int MAX_AVG_TERMS = 512;     // averaged (row, head) pairs per KV head
+constexpr int MAX_MERGE_CHUNKS = 512;  // split-K chunks per (r, g)
 
 }  // namespace spa

@@ -136,17 +136,18 @@ def test_set_split_bounds(lib):
 
 
 def test_other_entry_points_validate(lib):
-    lay = _lay()
-    lens, lp = _arr([100, 80], np.int32)
-    lo, lop = _arr([0, 4000], np.int64)
+    lay = _lay(page_table_stride=2048)
+    # lengths above one work chunk, so that every call below needs workspace
+    lens, lp = _arr([1000, 800], np.int32)
+    lo, lop = _arr([0, 5 * 8 * 1000], np.int64)
     # verify-only: k+1 rows per request, L >= k+1
     assert lib.spa_verify_attn(C.byref(lay), 2, 0, lp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                                lop, FAKE, 0, None) == bd.SPA_ERR_INVALID_ARG
     assert lib.spa_verify_attn(C.byref(lay), 2, 4, lp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                                lop, FAKE, 0, None) == bd.SPA_ERR_WORKSPACE_TOO_SMALL
     # top-K: K within [1, L], rows within [0, k]
-    kk, kp = _arr([5, 81], np.int32)
-    io, iop = _arr([0, 100], np.int64)
+    kk, kp = _arr([5, 801], np.int32)
+    io, iop = _arr([0, 4000], np.int64)
     assert lib.spa_pillar_topk(2, 4, 8, 2, 1, 4, lp, kp, FAKE, lop, FAKE, FAKE, iop, FAKE, 0,
                                None) == bd.SPA_ERR_INVALID_ARG
     kk, kp = _arr([5, 8], np.int32)
@@ -160,6 +161,7 @@ def test_other_entry_points_validate(lib):
     cnt, cp = _arr([4, 0], np.int32)
     assert lib.spa_draft_attn(C.byref(lay), 2, lp, FAKE, cp, iop, FAKE, FAKE, FAKE, FAKE, FAKE,
                               FAKE, FAKE, 0, None) == bd.SPA_ERR_INVALID_ARG
-    cnt, cp = _arr([4, 4], np.int32)
+    cnt, cp = _arr([1500, 4], np.int32)
+    io, iop = _arr([0, 4000], np.int64)
     assert lib.spa_draft_attn(C.byref(lay), 2, lp, FAKE, cp, iop, FAKE, FAKE, FAKE, FAKE, FAKE,
                               FAKE, FAKE, 0, None) == bd.SPA_ERR_WORKSPACE_TOO_SMALL

@@ -124,7 +124,7 @@ def _draft_only(oracle, b, lists, counts):
     o = torch.full_like(dq, float("nan"), device=DEV)
     lse = torch.full((len(counts), w.num_qo_heads), float("nan"), device=DEV)
     nbytes = bd.workspace_bytes(lay, len(counts), 1, None, b.seq_lens[:len(counts)], counts)
-    ws = torch.empty((max(nbytes, 256),), dtype=torch.uint8, device=DEV)
+    ws = bd.workspace(nbytes, DEV)
     bd.draft_attn(lay, len(counts), b.seq_lens[:len(counts)], b.page_table.to(DEV), counts, offs,
                   torch.from_numpy(flat).to(DEV), dq.to(DEV), b.k_pool.to(DEV), b.v_pool.to(DEV),
                   o, lse, ws)
@@ -179,7 +179,7 @@ def test_sequential_entry_points_match_unified(oracle):
     lsev = torch.empty((qv.shape[0], Hq), device=DEV)
     lgv = torch.empty((int(sum((k + 1) * Hq * L for L in lv)),), device=DEV)
     nb = bd.workspace_bytes(lay, len(ver), k, [1] * len(ver), lv, [b.idx_count[r] for r in ver])
-    ws = torch.empty((nb,), dtype=torch.uint8, device=DEV)
+    ws = bd.workspace(nb, DEV)
     bd.verify_attn(lay, len(ver), k, lv, ptv, qv, bd_.k_pool, bd_.v_pool, ov, lsev, lgv, loff, ws)
     Kv = [b.idx_count[r] for r in ver]
     ioff = np.concatenate([[0], np.cumsum([Hkv * K for K in Kv])[:-1]]).astype(np.int64)
@@ -227,3 +227,31 @@ def test_chained_verify_then_draft(oracle):
     ref2 = oracle.step(**parity.oracle_inputs(b2))
     gpu2 = run_unified(b2.to(DEV))
     parity.compare_step(oracle, b2, gpu2, ref2)
+
+
+def test_workspace_reuse_across_batches(oracle):
+    """One workspace serves differently shaped batches back to back; it is
+    poisoned with NaN bytes before each call, so a read of anything a call did
+    not write itself shows up in the outputs."""
+    shapes = [(5, ("uniform", 600, 2500), 2, 3), (3, ("uniform", 100, 1300), 1, 4),
+              (6, ("uniform", 1500, 3000), 3, 5)]
+    batches = []
+    for B, lengths, nv, seed in shapes:
+        w = synth.Workload(name=f"reuse{seed}", batch=B, num_qo_heads=32, num_kv_heads=8,
+                           head_dim=128, dtype="bf16", spec_k=8, sparsity=Fraction(1, 20),
+                           lengths=lengths, n_verify=nv, seed=seed)
+        batches.append(synth.make_batch(w))
+    need = 0
+    for b in batches:
+        lay = bd.layout(32, 8, 128, b.q.dtype, b.num_slots, b.stride)
+        need = max(need, bd.workspace_bytes(lay, b.B, 8, b.is_verify, b.seq_lens, b.idx_count))
+    ws = bd.workspace(need, DEV)
+    for b in batches:
+        ws.fill_(0xFF)
+        bufs = bd.StepBuffers(b.to(DEV))
+        bufs.ws = ws
+        bufs.step()
+        torch.cuda.synchronize()
+        ref = oracle.step(**parity.oracle_inputs(b))
+        parity.compare_step(oracle, b, {"o": bufs.o, "lse": bufs.lse, "logits": bufs.logits,
+                                        "idx": bufs.idx}, ref)
