@@ -100,9 +100,12 @@ class _Host:
     def arr(self, seq, dtype):
         if seq is None:
             return None
-        a = np.ascontiguousarray(np.asarray(seq, dtype=dtype))
+        if isinstance(seq, np.ndarray) and seq.dtype == dtype and seq.flags.c_contiguous:
+            a = seq
+        else:
+            a = np.ascontiguousarray(np.asarray(seq, dtype=dtype))
         self.keep.append(a)
-        return a.ctypes.data_as(C.c_void_p)
+        return C.c_void_p(a.ctypes.data)
 
 
 def _dptr(t: Optional[torch.Tensor]):
@@ -232,10 +235,17 @@ class StepBuffers:
         nbytes = workspace_bytes(self.lay, batch.B, w.spec_k, batch.is_verify, batch.seq_lens,
                                  batch.idx_count)
         self.ws = workspace(nbytes, dev)
+        # host metadata typed once, so a step only marshals pointers
+        self.h_is_verify = np.ascontiguousarray(batch.is_verify, dtype=np.uint8)
+        self.h_seq_lens = np.ascontiguousarray(batch.seq_lens, dtype=np.int32)
+        self.h_q_indptr = np.ascontiguousarray(batch.q_indptr, dtype=np.int32)
+        self.h_idx_count = np.ascontiguousarray(batch.idx_count, dtype=np.int32)
+        self.h_idx_off = np.ascontiguousarray(batch.idx_off, dtype=np.int64)
+        self.h_logits_off = np.ascontiguousarray(np.maximum(batch.logits_off, 0), dtype=np.int64)
 
     def step(self):
         b = self.batch
-        unified_step(self.lay, b.B, b.w.spec_k, b.is_verify, b.seq_lens, b.q_indptr,
-                     b.page_table, b.q, b.k_pool, b.v_pool, b.idx_count, b.idx_off, self.idx,
-                     self.o, self.lse, self.logits, [max(x, 0) for x in b.logits_off], self.ws,
-                     self.avg_row_begin, self.avg_row_count)
+        unified_step(self.lay, b.B, b.w.spec_k, self.h_is_verify, self.h_seq_lens,
+                     self.h_q_indptr, b.page_table, b.q, b.k_pool, b.v_pool, self.h_idx_count,
+                     self.h_idx_off, self.idx, self.o, self.lse, self.logits, self.h_logits_off,
+                     self.ws, self.avg_row_begin, self.avg_row_count)

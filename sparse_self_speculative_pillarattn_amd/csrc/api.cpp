@@ -5,9 +5,9 @@
 // -- written into a slot of a pinned host ring that the kernels read in place
 // (no copy is enqueued).  Items of one (request, KV head) stay on one XCD:
 // workgroup i of a launch runs on XCD i % 8, so the attention plan interleaves
-// eight per-XCD queues balanced by bytes.  A call enqueues at most two
-// launches: the attention of every request, then the post-pass (split-K
-// merges, score averaging and top-K selection).
+// eight per-XCD queues balanced by bytes.  A call enqueues at most three
+// launches: the attention of every request, the post-pass (split-K merges and
+// score averaging), then the top-K selection.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -58,10 +58,18 @@ struct Shape {
   float scale = 0.f;
 };
 
+// A call's work plan.  plan_size() fixes every count, offset and the XCD of
+// each (request, KV head); plan_write() then writes the records straight into
+// the pinned slot, so the host touches each record once.
 struct Plan {
-  std::vector<Item> items;      // attention launch: interleaved per-XCD queues, NOP-padded
-  std::vector<PostItem> post;   // post-pass launch
-  std::vector<PostItem> sel;    // selection launch: one record per verify (r, g)
+  bool attn = false, topk = false;
+  std::vector<int32_t> order;   // requests by estimated bytes, descending
+  std::vector<uint8_t> xcd;     // XCD queue of (r, g)
+  std::vector<int32_t> nchunk;  // split-K chunks of request r
+  std::vector<int64_t> part0;   // first split-K partial row of (r, 0); heads follow
+  int qlen[8] = {0};            // items per XCD queue
+  int n_items = 0;              // attention records, NOP padding included
+  int n_merge = 0, n_avg = 0, n_sel = 0;
   int64_t part_rows = 0;
   int64_t pbar_elems = 0;
   // pinned plan layout
@@ -120,14 +128,12 @@ int draft_chunk() {
   return v > 0 ? std::min(v, DRAFT_MAX_CHUNK) : DEFAULT_DRAFT_CHUNK;
 }
 
-// Work items of one (request, KV head) before they are laid out.
-struct Group {
-  std::vector<Item> items;
-  double bytes = 0;  // estimated HBM bytes, for the XCD balance
-};
+int avg_parts(int L) { return (L + AVG_SPAN - 1) / AVG_SPAN; }
+int64_t pbar_row(int L) { return (L + 3) / 4 * 4; }  // rows start 16-byte aligned
 
-// Attention plan (attn) and/or PillarAttn selection plan (topk) for `rq`.
-int32_t build_plan(const Shape& s, const std::vector<Req>& rq, bool attn, bool topk, Plan* pl) {
+// Counts, offsets and the XCD balance of the attention (attn) and/or PillarAttn
+// selection (topk) plan for `rq`.
+int32_t plan_size(const Shape& s, const std::vector<Req>& rq, bool attn, bool topk, Plan* pl) {
   const int B = (int)rq.size();
   const int G = s.G, Hkv = s.Hkv, D = s.d;
   const int rows_v = s.k + 1;
@@ -135,125 +141,64 @@ int32_t build_plan(const Shape& s, const std::vector<Req>& rq, bool attn, bool t
   const int esz = bf16 ? 2 : 4;
   const int CV = verify_chunk(), CD = draft_chunk();
   if (s.k > 255) return fail(SPA_ERR_UNSUPPORTED, "spec_k above 255");
+  pl->attn = attn;
+  pl->topk = topk;
 
   bool any_verify = false, any_draft = false;
   for (auto& q : rq) (q.verify ? any_verify : any_draft) = true;
 
-  // split-K chunking per request
-  std::vector<int> nchunk(B, 1);
-  std::vector<int64_t> part0(B * (size_t)Hkv, 0);
+  pl->nchunk.assign(B, 1);
+  pl->part0.assign(B, 0);
   int64_t part_rows = 0;
-  std::vector<PostItem> merges;
   if (attn) {
-    std::vector<Group> groups;
+    std::vector<double> bytes(B);
+    std::vector<int> nitems(B);
     for (int r = 0; r < B; ++r) {
       const Req& q = rq[r];
       const bool v = q.verify;
       const int span = v ? q.L : q.nlist;
       const int chunk = v ? CV : CD;
       const int nc = std::max(1, (span + chunk - 1) / chunk);
-      if (nc > MAX_MERGE_CHUNKS) return fail(SPA_ERR_UNSUPPORTED, "more than 512 split-K chunks");
-      nchunk[r] = nc;
-      const int nq = (v && !bf16) ? rows_v : 1;  // fp32 verify: one item per query row
-      const int Rr = (v ? rows_v : 1) * G;
-      for (int g = 0; g < Hkv; ++g) {
-        Group grp;
-        Item base;
-        std::memset(&base, 0, sizeof base);
-        base.kind = v ? KIND_VERIFY : KIND_DRAFT;
-        base.r = r;
-        base.g = g;
-        base.L = q.L;
-        base.row0 = q.row0;
-        base.nchunk = nc;
-        base.list_len = q.nlist;
-        base.off = v ? q.logits_off : q.idx_off + (int64_t)g * q.nlist;
-        if (nc > 1) {
-          base.part_row0 = part_rows;
-          part0[(size_t)r * Hkv + g] = part_rows;
-          part_rows += (int64_t)nc * Rr;
-          PostItem m;
-          std::memset(&m, 0, sizeof m);
-          m.kind = POST_MERGE;
-          m.r = r;
-          m.g = g;
-          m.rows_q = v ? rows_v : 1;
-          m.L = q.L;
-          m.row0 = q.row0;
-          m.nchunk = nc;
-          m.part_row0 = base.part_row0;
-          merges.push_back(m);
-        }
-        for (int c = 0; c < nc; ++c)
-          for (int qi = 0; qi < nq; ++qi) {
-            Item it = base;
-            it.qi = qi;
-            it.split = c;
-            it.begin = c * chunk;
-            it.end = std::min(span, (c + 1) * chunk);
-            grp.items.push_back(it);
-          }
-        grp.bytes = v ? (double)q.L * (2.0 * D * esz + 4 + 4.0 * rows_v * G)
-                      : (double)q.nlist * (2.0 * D * esz + 8);
-        groups.push_back(std::move(grp));
+      if (nc > MAX_MERGE_CHUNKS) return fail(SPA_ERR_UNSUPPORTED, "more than 256 split-K chunks per request");
+      pl->nchunk[r] = nc;
+      nitems[r] = nc * ((v && !bf16) ? rows_v : 1);  // fp32 verify: one item per query row
+      if (nc > 1) {
+        pl->part0[r] = part_rows;
+        part_rows += (int64_t)Hkv * nc * (v ? rows_v : 1) * G;
+        pl->n_merge += Hkv * ((((v ? rows_v : 1) * G) + MERGE_ROWS - 1) / MERGE_ROWS);
       }
+      bytes[r] = v ? (double)q.L * (2.0 * D * esz + 4 + 4.0 * rows_v * G)
+                   : (double)q.nlist * (2.0 * D * esz + 8);
     }
-    // longest-processing-time assignment of groups to the XCD queues
-    std::vector<int> order(groups.size());
-    for (size_t i = 0; i < order.size(); ++i) order[i] = (int)i;
-    std::stable_sort(order.begin(), order.end(),
-                     [&](int a, int b) { return groups[a].bytes > groups[b].bytes; });
-    std::vector<std::vector<Item>> queue(NUM_XCD);
+    // longest-processing-time assignment of (r, g) to the XCD queues; all heads
+    // of a request weigh the same, so sorting the requests suffices
+    pl->order.resize(B);
+    for (int r = 0; r < B; ++r) pl->order[r] = r;
+    std::stable_sort(pl->order.begin(), pl->order.end(),
+                     [&](int a, int b) { return bytes[a] > bytes[b]; });
+    pl->xcd.resize((size_t)B * Hkv);
     double load[NUM_XCD] = {0};
-    for (int gi : order) {
-      int x = 0;
-      for (int y = 1; y < NUM_XCD; ++y)
-        if (load[y] < load[x]) x = y;
-      load[x] += groups[gi].bytes;
-      for (auto& it : groups[gi].items) queue[x].push_back(it);
-    }
-    size_t maxlen = 0;
-    for (auto& qx : queue) maxlen = std::max(maxlen, qx.size());
-    Item nop;
-    std::memset(&nop, 0, sizeof nop);
-    nop.kind = KIND_NOP;
-    pl->items.reserve(maxlen * NUM_XCD);
-    for (size_t i = 0; i < maxlen; ++i)
-      for (int x = 0; x < NUM_XCD; ++x) pl->items.push_back(i < queue[x].size() ? queue[x][i] : nop);
-  }
-  // post-pass: averaging chunks of every verify (r, g), then the merges
-  int64_t pbar = 0;
-  if (topk && any_verify) {
-    for (int r = 0; r < B; ++r) {
-      const Req& q = rq[r];
-      if (!q.verify) continue;
-      const int nparts = (q.L + AVG_SPAN - 1) / AVG_SPAN;
+    for (int r : pl->order)
       for (int g = 0; g < Hkv; ++g) {
-        for (int pidx = 0; pidx < nparts; ++pidx) {
-          PostItem a;
-          std::memset(&a, 0, sizeof a);
-          a.kind = POST_AVG;
-          a.r = r;
-          a.g = g;
-          a.rows_q = rows_v;
-          a.L = q.L;
-          a.row0 = q.row0;
-          a.nchunk = attn ? nchunk[r] : 1;
-          a.part_row0 = attn ? part0[(size_t)r * Hkv + g] : 0;
-          a.j0 = pidx * AVG_SPAN;
-          a.j1 = std::min(q.L, (pidx + 1) * AVG_SPAN);
-          a.K = q.nlist;
-          a.logits_off = q.logits_off;
-          a.idx_off = q.idx_off + (int64_t)g * q.nlist;
-          a.pbar_off = pbar;
-          pl->post.push_back(a);
-          if (pidx == 0) pl->sel.push_back(a);
-        }
-        pbar += (q.L + 3) / 4 * 4;  // rows start 16-byte aligned
+        int x = 0;
+        for (int y = 1; y < NUM_XCD; ++y)
+          if (load[y] < load[x]) x = y;
+        load[x] += bytes[r];
+        pl->qlen[x] += nitems[r];
+        pl->xcd[(size_t)r * Hkv + g] = (uint8_t)x;
       }
-    }
+    int maxlen = 0;
+    for (int x = 0; x < NUM_XCD; ++x) maxlen = std::max(maxlen, pl->qlen[x]);
+    pl->n_items = maxlen * NUM_XCD;
   }
-  for (auto& m : merges) pl->post.push_back(m);
+  int64_t pbar = 0;
+  if (topk)
+    for (auto& q : rq)
+      if (q.verify) {
+        pl->n_avg += Hkv * avg_parts(q.L);
+        pl->n_sel += Hkv;
+        pbar += Hkv * pbar_row(q.L);
+      }
   pl->part_rows = part_rows;
   pl->pbar_elems = pbar;
 
@@ -278,11 +223,11 @@ int32_t build_plan(const Shape& s, const std::vector<Req>& rq, bool attn, bool t
   // pinned plan layout
   size_t h = 0;
   pl->h_items = h;
-  h = align_up(h + pl->items.size() * sizeof(Item), 256);
+  h = align_up(h + (size_t)pl->n_items * sizeof(Item), 256);
   pl->h_post = h;
-  h = align_up(h + pl->post.size() * sizeof(PostItem), 256);
+  h = align_up(h + (size_t)(pl->n_avg + pl->n_merge) * sizeof(PostItem), 256);
   pl->h_sel = h;
-  h = align_up(h + pl->sel.size() * sizeof(PostItem), 256);
+  h = align_up(h + (size_t)pl->n_sel * sizeof(PostItem), 256);
   pl->h_bytes = h;
   // workspace layout
   size_t o = 0;
@@ -294,6 +239,117 @@ int32_t build_plan(const Shape& s, const std::vector<Req>& rq, bool attn, bool t
   o = align_up(o + (size_t)pbar * 4, 256);
   pl->total = o;
   return SPA_OK;
+}
+
+// Writes the records of a sized plan into the pinned slot at `h`.
+void plan_write(const Shape& s, const std::vector<Req>& rq, const Plan& pl, char* h) {
+  const int B = (int)rq.size();
+  const int G = s.G, Hkv = s.Hkv;
+  const int rows_v = s.k + 1;
+  const bool bf16 = s.dtype == SPA_BF16;
+  const int CV = verify_chunk(), CD = draft_chunk();
+  if (pl.attn) {
+    Item* items = reinterpret_cast<Item*>(h + pl.h_items);
+    int cur[NUM_XCD] = {0};
+    for (int r : pl.order) {
+      const Req& q = rq[r];
+      const bool v = q.verify;
+      const int span = v ? q.L : q.nlist;
+      const int chunk = v ? CV : CD;
+      const int nc = pl.nchunk[r];
+      const int nq = (v && !bf16) ? rows_v : 1;
+      const int64_t head_rows = (int64_t)nc * (v ? rows_v : 1) * G;
+      for (int g = 0; g < Hkv; ++g) {
+        const int x = pl.xcd[(size_t)r * Hkv + g];
+        Item it;
+        std::memset(&it, 0, sizeof it);
+        it.kind = v ? KIND_VERIFY : KIND_DRAFT;
+        it.r = r;
+        it.g = g;
+        it.L = q.L;
+        it.row0 = q.row0;
+        it.nchunk = nc;
+        it.list_len = q.nlist;
+        it.off = v ? q.logits_off : q.idx_off + (int64_t)g * q.nlist;
+        it.part_row0 = nc > 1 ? pl.part0[r] + g * head_rows : 0;
+        for (int c = 0; c < nc; ++c)
+          for (int qi = 0; qi < nq; ++qi) {
+            it.qi = qi;
+            it.split = c;
+            it.begin = c * chunk;
+            it.end = std::min(span, (c + 1) * chunk);
+            items[(size_t)cur[x]++ * NUM_XCD + x] = it;
+          }
+      }
+    }
+    Item nop;
+    std::memset(&nop, 0, sizeof nop);
+    nop.kind = KIND_NOP;
+    const int maxlen = pl.n_items / NUM_XCD;
+    for (int x = 0; x < NUM_XCD; ++x)
+      for (int i = cur[x]; i < maxlen; ++i) items[(size_t)i * NUM_XCD + x] = nop;
+  }
+  // post-pass: averaging chunks of every verify (r, g), then the merges
+  PostItem* post = reinterpret_cast<PostItem*>(h + pl.h_post);
+  PostItem* sel = reinterpret_cast<PostItem*>(h + pl.h_sel);
+  int np = 0, ns = 0;
+  if (pl.topk) {
+    int64_t pbar = 0;
+    for (int r = 0; r < B; ++r) {
+      const Req& q = rq[r];
+      if (!q.verify) continue;
+      const int nparts = avg_parts(q.L);
+      const int nc = pl.attn ? pl.nchunk[r] : 1;
+      const int64_t head_rows = (int64_t)nc * rows_v * G;
+      for (int g = 0; g < Hkv; ++g) {
+        PostItem a;
+        std::memset(&a, 0, sizeof a);
+        a.kind = POST_AVG;
+        a.r = r;
+        a.g = g;
+        a.rows_q = rows_v;
+        a.L = q.L;
+        a.row0 = q.row0;
+        a.nchunk = nc;
+        a.part_row0 = nc > 1 ? pl.part0[r] + g * head_rows : 0;
+        a.K = q.nlist;
+        a.logits_off = q.logits_off;
+        a.idx_off = q.idx_off + (int64_t)g * q.nlist;
+        a.pbar_off = pbar;
+        sel[ns++] = a;
+        for (int pidx = 0; pidx < nparts; ++pidx) {
+          a.j0 = pidx * AVG_SPAN;
+          a.j1 = std::min(q.L, (pidx + 1) * AVG_SPAN);
+          post[np++] = a;
+        }
+        pbar += pbar_row(q.L);
+      }
+    }
+  }
+  if (pl.attn)
+    for (int r = 0; r < B; ++r) {
+      const int nc = pl.nchunk[r];
+      if (nc == 1) continue;
+      const Req& q = rq[r];
+      const int rq_rows = q.verify ? rows_v : 1;
+      for (int g = 0; g < Hkv; ++g) {
+        PostItem m;
+        std::memset(&m, 0, sizeof m);
+        m.kind = POST_MERGE;
+        m.r = r;
+        m.g = g;
+        m.rows_q = rq_rows;
+        m.L = q.L;
+        m.row0 = q.row0;
+        m.nchunk = nc;
+        m.part_row0 = pl.part0[r] + g * (int64_t)nc * rq_rows * G;
+        for (int j = 0; j < rq_rows * G; j += MERGE_ROWS) {
+          m.j0 = j;
+          m.j1 = std::min(rq_rows * G, j + MERGE_ROWS);
+          post[np++] = m;
+        }
+      }
+    }
 }
 
 // ---- opt-in per-launch timing ------------------------------------------------
@@ -386,10 +442,6 @@ int32_t acquire_slot(const Plan& pl, PlanSlot** out) {
     }
     s.cap = want;
   }
-  char* h = static_cast<char*>(s.host);
-  if (!pl.items.empty()) std::memcpy(h + pl.h_items, pl.items.data(), pl.items.size() * sizeof(Item));
-  if (!pl.post.empty()) std::memcpy(h + pl.h_post, pl.post.data(), pl.post.size() * sizeof(PostItem));
-  if (!pl.sel.empty()) std::memcpy(h + pl.h_sel, pl.sel.data(), pl.sel.size() * sizeof(PostItem));
   *out = &s;
   return SPA_OK;
 }
@@ -406,23 +458,25 @@ struct Buffers {
   float* logits = nullptr;
 };
 
-int32_t run(const Shape& s, const Plan& pl, const Buffers& b, int avg_begin, int avg_count,
-            void* d_ws, size_t ws_bytes, hipStream_t st) {
+int32_t run(const Shape& s, const std::vector<Req>& rq, const Plan& pl, const Buffers& b,
+            int avg_begin, int avg_count, void* d_ws, size_t ws_bytes, hipStream_t st) {
   if (ws_bytes < pl.total)
     return fail(SPA_ERR_WORKSPACE_TOO_SMALL,
                 "workspace of " + std::to_string(ws_bytes) + " bytes, need " + std::to_string(pl.total));
   if (pl.total > 0 && !d_ws) return fail(SPA_ERR_INVALID_ARG, "d_ws is NULL");
-  if (pl.items.empty() && pl.post.empty()) return SPA_OK;
+  const int n_post = pl.n_avg + pl.n_merge;
+  if (pl.n_items == 0 && n_post == 0 && pl.n_sel == 0) return SPA_OK;
   std::lock_guard<std::mutex> lock(g_ring_mu);
   PlanSlot* slot = nullptr;
   int32_t rc = acquire_slot(pl, &slot);
   if (rc) return rc;
+  plan_write(s, rq, pl, static_cast<char*>(slot->host));
   const char* plan = static_cast<const char*>(slot->dev);
   char* ws = static_cast<char*>(d_ws);
   float* part_o = reinterpret_cast<float*>(ws + pl.off_part_o);
   float* part_ml = reinterpret_cast<float*>(ws + pl.off_part_ml);
   hipError_t e;
-  if (!pl.items.empty()) {
+  if (pl.n_items > 0) {
     AttnParams p;
     p.items = reinterpret_cast<const Item*>(plan + pl.h_items);
     p.q = b.q;
@@ -444,11 +498,11 @@ int32_t run(const Shape& s, const Plan& pl, const Buffers& b, int avg_begin, int
     p.sm_scale = s.scale;
     {
       ProfScope ps(PROF_ATTN, st);
-      e = launch_attn(p, s.dtype, s.d, (int)pl.items.size(), pl.nthr, pl.smem, st);
+      e = launch_attn(p, s.dtype, s.d, pl.n_items, pl.nthr, pl.smem, st);
     }
     if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("attention launch: ") + hipGetErrorString(e));
   }
-  if (!pl.post.empty()) {
+  if (n_post > 0) {
     PostParams pp;
     pp.items = reinterpret_cast<const PostItem*>(plan + pl.h_post);
     pp.part_o = part_o;
@@ -463,18 +517,18 @@ int32_t run(const Shape& s, const Plan& pl, const Buffers& b, int avg_begin, int
     pp.avg_row_count = avg_count;
     {
       ProfScope ps(PROF_POST, st);
-      e = launch_post(pp, s.dtype, s.d, (int)pl.post.size(), st);
+      e = launch_post(pp, s.dtype, s.d, n_post, st);
     }
     if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("post-pass launch: ") + hipGetErrorString(e));
   }
-  if (!pl.sel.empty()) {
+  if (pl.n_sel > 0) {
     SelectParams sp;
     sp.items = reinterpret_cast<const PostItem*>(plan + pl.h_sel);
     sp.pbar = reinterpret_cast<const float*>(ws + pl.off_pbar);
     sp.idx_out = b.idx_out;
     {
       ProfScope ps(PROF_SELECT, st);
-      e = launch_select(sp, (int)pl.sel.size(), st);
+      e = launch_select(sp, pl.n_sel, st);
     }
     if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("selection launch: ") + hipGetErrorString(e));
   }
@@ -639,7 +693,7 @@ size_t spa_workspace_bytes(const spa_layout* layout, int32_t B, int32_t spec_k,
     return 0;
   // the unified step needs the most: attention plus selection
   Plan pl;
-  if (build_plan(s, rq, true, true, &pl)) return 0;
+  if (plan_size(s, rq, true, true, &pl)) return 0;
   return pl.total;
 }
 
@@ -664,7 +718,7 @@ int32_t spa_verify_attn(const spa_layout* layout, int32_t B, int32_t spec_k,
                &rq);
   if (rc) return rc;
   Plan pl;
-  rc = build_plan(s, rq, true, false, &pl);
+  rc = plan_size(s, rq, true, false, &pl);
   if (rc) return rc;
   Buffers b;
   b.page_table = d_page_table;
@@ -674,7 +728,7 @@ int32_t spa_verify_attn(const spa_layout* layout, int32_t B, int32_t spec_k,
   b.o = d_o;
   b.lse = d_lse;
   b.logits = d_logits;
-  return run(s, pl, b, 1, spec_k, d_ws, ws_bytes, static_cast<hipStream_t>(stream));
+  return run(s, rq, pl, b, 1, spec_k, d_ws, ws_bytes, static_cast<hipStream_t>(stream));
 }
 
 int32_t spa_pillar_topk(int32_t B, int32_t spec_k, int32_t num_qo_heads, int32_t num_kv_heads,
@@ -704,13 +758,13 @@ int32_t spa_pillar_topk(int32_t B, int32_t spec_k, int32_t num_qo_heads, int32_t
                &rq);
   if (rc) return rc;
   Plan pl;
-  rc = build_plan(s, rq, false, true, &pl);
+  rc = plan_size(s, rq, false, true, &pl);
   if (rc) return rc;
   Buffers b;
   b.logits = const_cast<float*>(d_logits);
   b.lse = const_cast<float*>(d_lse);
   b.idx_out = d_idx;
-  return run(s, pl, b, avg_row_begin, avg_row_count, d_ws, ws_bytes,
+  return run(s, rq, pl, b, avg_row_begin, avg_row_count, d_ws, ws_bytes,
              static_cast<hipStream_t>(stream));
 }
 
@@ -733,7 +787,7 @@ int32_t spa_draft_attn(const spa_layout* layout, int32_t B, const int32_t* h_seq
                &rq);
   if (rc) return rc;
   Plan pl;
-  rc = build_plan(s, rq, true, false, &pl);
+  rc = plan_size(s, rq, true, false, &pl);
   if (rc) return rc;
   Buffers b;
   b.page_table = d_page_table;
@@ -743,7 +797,7 @@ int32_t spa_draft_attn(const spa_layout* layout, int32_t B, const int32_t* h_seq
   b.idx_in = d_idx;
   b.o = d_o;
   b.lse = d_lse;
-  return run(s, pl, b, 0, 1, d_ws, ws_bytes, static_cast<hipStream_t>(stream));
+  return run(s, rq, pl, b, 0, 1, d_ws, ws_bytes, static_cast<hipStream_t>(stream));
 }
 
 int32_t spa_unified_step(const spa_layout* layout, int32_t B, int32_t spec_k,
@@ -775,7 +829,7 @@ int32_t spa_unified_step(const spa_layout* layout, int32_t B, int32_t spec_k,
                any_v, true, &rq);
   if (rc) return rc;
   Plan pl;
-  rc = build_plan(s, rq, true, true, &pl);
+  rc = plan_size(s, rq, true, true, &pl);
   if (rc) return rc;
   Buffers b;
   b.page_table = d_page_table;
@@ -787,7 +841,7 @@ int32_t spa_unified_step(const spa_layout* layout, int32_t B, int32_t spec_k,
   b.o = d_o;
   b.lse = d_lse;
   b.logits = d_logits;
-  return run(s, pl, b, avg_row_begin, avg_row_count, d_ws, ws_bytes,
+  return run(s, rq, pl, b, avg_row_begin, avg_row_count, d_ws, ws_bytes,
              static_cast<hipStream_t>(stream));
 }
 

@@ -635,44 +635,82 @@ __global__ void __launch_bounds__(512) attn_kernel(AttnParams p) {
 // ==========================================================================
 // PillarAttn post-pass
 // ==========================================================================
-// split-K merge of one (r, g): m* = max_s m_s, l* = sum_s l_s e^{m_s - m*},
-// O = sum_s e^{m_s - m*} O_s / l*, LSE = m* + ln l*.
+// split-K merge of rows [j0, j1) of one (r, g): m* = max_s m_s,
+// l* = sum_s l_s e^{m_s - m*}, O = sum_s e^{m_s - m*} O_s / l*, LSE = m* + ln l*.
+// The (m, l) pairs of every chunk are staged in LDS, one wave per row turns
+// them into weights in place (lane s % 64 alone touches pair s), and each
+// thread then owns one (row, 4 dims) column of O.
 template <int D, typename T>
-__device__ void merge_group(const PostParams& p, const PostItem& it) {
+__device__ void merge_rows(const PostParams& p, const PostItem& it, char* smem) {
+  constexpr int D4 = D / 4;
+  static_assert(MERGE_ROWS * D4 <= 256, "one O column per thread");
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nwaves = blockDim.x >> 6;
   const int G = p.G;
   const int R = it.rows_q * G;
   const int ns = it.nchunk;
-  constexpr int D4 = D / 4;
-  for (int x = threadIdx.x; x < R * D4; x += blockDim.x) {
-    const int rho = x / D4, d4 = x % D4;
-    float mstar = NEG_INF;
-    for (int s = 0; s < ns; ++s)
-      mstar = fmaxf(mstar, p.part_ml[2 * (it.part_row0 + (int64_t)s * R + rho)]);
-    float lsum = 0.f;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (mstar != NEG_INF) {
-      for (int s = 0; s < ns; ++s) {
-        const int64_t pr = it.part_row0 + (int64_t)s * R + rho;
-        const float m = p.part_ml[2 * pr], l = p.part_ml[2 * pr + 1];
-        const float w = (m == NEG_INF) ? 0.f : fast_exp2((m - mstar) * LOG2E);
-        const float4 o = *reinterpret_cast<const float4*>(p.part_o + pr * D + 4 * d4);
-        lsum = fmaf(w, l, lsum);
-        acc.x = fmaf(w, o.x, acc.x);
-        acc.y = fmaf(w, o.y, acc.y);
-        acc.z = fmaf(w, o.z, acc.z);
-        acc.w = fmaf(w, o.w, acc.w);
-      }
-    }
-    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-    const int qi = rho / G, hh = rho % G;
-    const int64_t orow = (int64_t)(it.row0 + qi) * p.Hq + it.g * G + hh;
-    T* dst = reinterpret_cast<T*>(p.o) + orow * D + 4 * d4;
-    store_out<T>(dst + 0, acc.x * inv);
-    store_out<T>(dst + 1, acc.y * inv);
-    store_out<T>(dst + 2, acc.z * inv);
-    store_out<T>(dst + 3, acc.w * inv);
-    if (d4 == 0) p.lse[orow] = lsum > 0.f ? mstar + logf(lsum) : NEG_INF;
+  const int rho0 = it.j0, nr = it.j1 - it.j0;
+  float* w_s = reinterpret_cast<float*>(smem);  // [MERGE_ROWS][ns] (m, l) pairs
+  const float2* ml = reinterpret_cast<const float2*>(p.part_ml);
+  for (int x = tid; x < nr * ns; x += blockDim.x) {
+    const int rr = x / ns, sidx = x % ns;
+    const float2 v = ml[it.part_row0 + (int64_t)sidx * R + rho0 + rr];
+    w_s[2 * x] = v.x;
+    w_s[2 * x + 1] = v.y;
   }
+  __syncthreads();
+  for (int rr = wave; rr < nr; rr += nwaves) {
+    float* pr = w_s + 2 * rr * ns;
+    float mx = NEG_INF;
+    for (int sidx = lane; sidx < ns; sidx += 64) mx = fmaxf(mx, pr[2 * sidx]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    float ls = 0.f;
+    if (mx != NEG_INF)
+      for (int sidx = lane; sidx < ns; sidx += 64) {
+        const float m = pr[2 * sidx];
+        if (m != NEG_INF) ls = fmaf(pr[2 * sidx + 1], fast_exp2((m - mx) * LOG2E), ls);
+      }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) ls += __shfl_xor(ls, off);
+    const float inv = ls > 0.f ? 1.f / ls : 0.f;
+    for (int sidx = lane; sidx < ns; sidx += 64) {
+      const float m = pr[2 * sidx];
+      pr[2 * sidx] = (m == NEG_INF || inv == 0.f) ? 0.f : fast_exp2((m - mx) * LOG2E) * inv;
+    }
+    if (lane == 0) {
+      const int rho = rho0 + rr, qi = rho / G, hh = rho % G;
+      p.lse[(int64_t)(it.row0 + qi) * p.Hq + it.g * G + hh] = ls > 0.f ? mx + logf(ls) : NEG_INF;
+    }
+  }
+  __syncthreads();
+  if (tid >= nr * D4) return;
+  const int rr = tid / D4, d4 = tid % D4;
+  const int rho = rho0 + rr;
+  const float* src = p.part_o + (it.part_row0 + rho) * D + 4 * d4;
+  const int64_t sstride = (int64_t)R * D;
+  const float* w = w_s + 2 * rr * ns;  // weight of chunk s at w[2 s]
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s0 = 0; s0 < ns; s0 += 8) {
+    float4 o[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      o[u] = *reinterpret_cast<const float4*>(src + min(s0 + u, ns - 1) * sstride);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float wu = (s0 + u < ns) ? w[2 * (s0 + u)] : 0.f;
+      acc.x = fmaf(wu, o[u].x, acc.x);
+      acc.y = fmaf(wu, o[u].y, acc.y);
+      acc.z = fmaf(wu, o[u].z, acc.z);
+      acc.w = fmaf(wu, o[u].w, acc.w);
+    }
+  }
+  const int qi = rho / G, hh = rho % G;
+  const int64_t orow = (int64_t)(it.row0 + qi) * p.Hq + it.g * G + hh;
+  T* dst = reinterpret_cast<T*>(p.o) + orow * D + 4 * d4;
+  store_out<T>(dst + 0, acc.x);
+  store_out<T>(dst + 1, acc.y);
+  store_out<T>(dst + 2, acc.z);
+  store_out<T>(dst + 3, acc.w);
 }
 
 // Block-wide exclusive prefix of per-thread counts (wave scan + per-wave
@@ -830,12 +868,18 @@ __device__ void select_topk(const float* scores, int L, int K, int32_t* out, cha
 
 template <int D, typename T>
 __global__ void __launch_bounds__(256) post_kernel(PostParams p) {
-  __shared__ float lse2_s[MAX_AVG_TERMS];
-  __shared__ int64_t rowoff_s[MAX_AVG_TERMS];
+  // merge: (m, l) pairs then weights of MERGE_ROWS rows; averaging: LSE and
+  // logits row offsets of the averaged terms
+  constexpr int SMEM = 2 * MERGE_ROWS * MAX_MERGE_CHUNKS * 4 > MAX_AVG_TERMS * 12
+                           ? 2 * MERGE_ROWS * MAX_MERGE_CHUNKS * 4
+                           : MAX_AVG_TERMS * 12;
+  __shared__ __attribute__((aligned(16))) char smem[SMEM];
+  float* lse2_s = reinterpret_cast<float*>(smem);
+  int64_t* rowoff_s = reinterpret_cast<int64_t*>(smem + MAX_AVG_TERMS * 4);
   const PostItem it = p.items[blockIdx.x];
   if (it.kind == POST_NOP) return;
   if (it.kind == POST_MERGE) {
-    merge_group<D, T>(p, it);
+    merge_rows<D, T>(p, it, smem);
     return;
   }
   // POST_AVG: LSE of the averaged rows (one thread per (row, head)), then

@@ -34,7 +34,7 @@ struct Item {
 // ---- PillarAttn post-pass launch -------------------------------------------
 enum : int32_t {
   POST_NOP = 0,
-  POST_MERGE = 1,  // merge the split-K partials of (r, g) into O and LSE
+  POST_MERGE = 1,  // merge the split-K partials of rows [j0, j1) of (r, g) into O and LSE
   POST_AVG = 2,    // averaged exact scores of positions [j0, j1) of verify (r, g)
 };
 
@@ -48,7 +48,7 @@ struct PostItem {
   int32_t L;
   int32_t row0;        // first q / o / lse row of request r
   int32_t nchunk;      // split-K partials per row (1 = the LSE array is already final)
-  int32_t j0, j1;      // POST_AVG: positions
+  int32_t j0, j1;      // POST_AVG: positions; POST_MERGE: rows i*G + h of (r, g)
   int32_t K;           // positions to select
   int32_t pad_;
   int64_t part_row0;   // first split-K partial row of (r, g)
@@ -64,6 +64,7 @@ constexpr int DRAFT_MAX_CHUNK = 2048;
 constexpr int MAX_GROUP = 8;           // query heads per KV head on the VALU path
 constexpr int MAX_ROW_TILES = 8;       // 16-row MFMA tiles (one wave each, 512 threads max)
 constexpr int MAX_AVG_TERMS = 512;     // averaged (row, head) pairs per KV head
-constexpr int MAX_MERGE_CHUNKS = 512;  // split-K chunks per (r, g)
+constexpr int MAX_MERGE_CHUNKS = 256;  // split-K chunks per (r, g)
+constexpr int MERGE_ROWS = 8;          // rows per merge item
 
 }  // namespace spa

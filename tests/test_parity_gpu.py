@@ -80,7 +80,7 @@ def test_ragged_lengths(oracle, L):
     check(oracle, w)
 
 
-@pytest.mark.parametrize("split", [(64, 16), (2048, 2048), (320, 100)])
+@pytest.mark.parametrize("split", [(64, 16), (2048, 2048), (320, 100), (40, 7)])
 def test_split_invariance(oracle, split):
     bd.set_split(*split)
     w = synth.Workload(name="split", batch=6, num_qo_heads=32, num_kv_heads=8, head_dim=128,
