@@ -212,8 +212,8 @@ int32_t plan_size(const Shape& s, const std::vector<Req>& rq, bool attn, bool to
   if (need_mfma) {
     const int nt = (rows_v * G + 15) / 16;
     if (nt > MAX_ROW_TILES)
-      return fail(SPA_ERR_UNSUPPORTED, "(k+1)*G above 128 rows per KV head on the MFMA path");
-    nthr = 64 * std::max(4, nt);
+      return fail(SPA_ERR_UNSUPPORTED, "(k+1)*G above 112 rows per KV head on the MFMA path");
+    nthr = 64 * std::max(4, nt + 1);  // one consumer wave per row tile, one producer wave
   }
   if (need_valu && G > MAX_GROUP)
     return fail(SPA_ERR_UNSUPPORTED, "GQA group above 8 on the gather path");

@@ -104,144 +104,137 @@ __device__ __forceinline__ float group_sum(float v) {
 }
 
 // ==========================================================================
-// Verify tile on MFMA (bf16)
+// Verify tile on MFMA (bf16), wave-specialised
 //
-// Rows rho = i*G + hh (query row i, head hh of the group) form 16-row tiles,
-// one per wave.  Per 64-token tile:
-//   S^T = K Q^T       16x16x32 MFMA; A = K rows from LDS, B = Q^T in registers
-//   logits stored; online softmax in registers (two lane shuffles per row)
-//   O^T += V^T P^T    A = V^T from the transposed LDS tile; B = P^T is the S^T
-//                     accumulator repacked to bf16 in place.
-// Tokens inside a tile are permuted so that two 16-token S^T accumulators are
-// exactly the P^T operand of one 32-token PV step and every lane owns four
-// consecutive positions.  Two tiles of K/V rows are in flight in registers
-// while a third is computed from LDS.
+// The last wave of the block is the producer: it streams the K and V rows of
+// 32-token tiles from the paged pool straight into a ring of LDS stages with
+// global->LDS loads.  It issues loads only, so it can wait for one tile while
+// the next ones are still in flight.  The other waves are consumers, one per
+// 16-row tile of rows rho = i*G + hh (query row i, head hh of the group):
+//   S^T = K Q^T      16x16x32 MFMA over tokens 16t..16t+15 of the tile (t = 0, 1);
+//                    A = K rows from LDS, B = Q^T in registers.  Lane (n, q)
+//                    holds row n's scores of tokens 16t + 4q .. 16t + 4q + 3.
+//   logits stored (each store writes 64 contiguous bytes per row); online
+//   softmax in registers (two lane shuffles per row)
+//   O^T += V^T P^T   B = P^T is the two S^T accumulators in bf16: contraction
+//                    index 8q + j is token 4q + j (j < 4) or 16 + 4q + j - 4;
+//                    A = V^T of the same tokens, read from the row-major V
+//                    stage with the LDS transpose read.
+// Consumers only read LDS, run MFMA and store.  One barrier per tile hands a
+// stage from the producer to the consumers and, a tile later, back.
 // ==========================================================================
+constexpr int DMA_TT = 32;     // tokens per stage
+constexpr int DMA_STAGES = 4;  // LDS stages; DMA_STAGES - 1 tiles in flight
+
 template <int D>
-constexpr size_t mfma_smem_bytes() {
-  return (size_t)VERIFY_TILE * (D / 8) * 16 + (size_t)D * (VERIFY_TILE + 8) * 2 +
-         (size_t)VERIFY_MAX_CHUNK * 4;
+constexpr size_t dma_smem_bytes() {  // the stage ring; the chunk's slots follow it
+  return (size_t)DMA_STAGES * 2 * DMA_TT * D * 2;
 }
 
-// Registers holding one 64-token K/V tile on its way to LDS: up to four K
-// pieces and four V pieces (16 bytes each) per thread.
-struct KVRegs {
-  uint4 k0, k1, k2, k3, v0, v1, v2, v3;
-};
-
-template <int D>
-struct VerifyTileCtx {
-  uint4* Ks;
-  uint16_t* Vt;
-  const int32_t* slots;
-  const uint16_t* kpool;
-  const uint16_t* vpool;
-  int tid, nthr, jb, je, g, Hkv;
-};
-
-template <int D>
-__device__ __forceinline__ uint4 fetch_k(const VerifyTileCtx<D>& c, int t0, int i) {
-  constexpr int NCH = D / 8;
-  const int pc = min(c.tid + i * c.nthr, VERIFY_TILE * NCH - 1);
-  const int tau = pc / NCH, ch = pc % NCH;
-  const int64_t slot = c.slots[min(t0 - c.jb + tau, c.je - 1 - c.jb)];
-  return *reinterpret_cast<const uint4*>(c.kpool + (slot * c.Hkv + c.g) * D + 8 * ch);
+// LDS chunk swizzles of a stage.  K: the 16 consecutive rows one MFMA operand
+// read touches land on distinct bank groups.  V: the eight rows (two 16-byte
+// chunks each) of every half-wave transpose read land on distinct bank groups.
+template <int NCH>
+__device__ __forceinline__ int kswz_t(int tau) {
+  return tau & (NCH - 1);
+}
+template <int NCH>
+__device__ __forceinline__ int vswz(int tau) {
+  return (2 * (tau & 7)) & (NCH - 1);
 }
 
-template <int D>
-__device__ __forceinline__ uint4 fetch_v(const VerifyTileCtx<D>& c, int t0, int i) {
-  constexpr int NCH = D / 8;
-  constexpr int VUNITS = (VERIFY_TILE / 4) * NCH;
-  const int u = min(c.tid, VUNITS - 1);
-  const int tg = u / NCH, ch = u % NCH;
-  const int64_t slot = c.slots[min(t0 - c.jb + 4 * tg + i, c.je - 1 - c.jb)];
-  return *reinterpret_cast<const uint4*>(c.vpool + (slot * c.Hkv + c.g) * D + 8 * ch);
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+// Wait until at most N vector-memory loads of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// 16 bytes per lane from global memory to LDS: lane l's piece lands at
+// dst + 16 l (dst is wave-uniform).
+__device__ __forceinline__ void load_lds16(const void* src, char* dst) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)dst, 16, 0, 0);
 }
 
 template <int D>
-__device__ __forceinline__ void fetch_tile(const VerifyTileCtx<D>& c, KVRegs& r, int t0) {
-  constexpr int KP = VERIFY_TILE * (D / 8) / 256;
-  r.k0 = fetch_k<D>(c, t0, 0);
-  r.k1 = fetch_k<D>(c, t0, 1);
-  if constexpr (KP > 2) {
-    r.k2 = fetch_k<D>(c, t0, 2);
-    r.k3 = fetch_k<D>(c, t0, 3);
-  }
-  r.v0 = fetch_v<D>(c, t0, 0);
-  r.v1 = fetch_v<D>(c, t0, 1);
-  r.v2 = fetch_v<D>(c, t0, 2);
-  r.v3 = fetch_v<D>(c, t0, 3);
-}
-
-template <int D>
-__device__ __forceinline__ void stage_k(const VerifyTileCtx<D>& c, const uint4& v, int nt, int i) {
-  constexpr int NCH = D / 8;
-  const int pc = c.tid + i * c.nthr;
-  if (pc < VERIFY_TILE * NCH) {
-    const int tau = pc / NCH, ch = pc % NCH;
-    c.Ks[tau * NCH + (ch ^ kswz<NCH>(tau))] = tau < nt ? v : make_uint4(0u, 0u, 0u, 0u);
-  }
-}
-
-__device__ __forceinline__ uint32_t half16(uint32_t w, int hi) { return hi ? (w >> 16) : (w & 0xffffu); }
-
-// V tile transposed into LDS: thread (token group tg, chunk ch) holds four
-// consecutive tokens' 8 elements; element e of the four tokens becomes one
-// 8-byte row segment Vt[8 ch + e][4 tg .. 4 tg + 3].
-template <int D>
-__device__ __forceinline__ void stage_tile(const VerifyTileCtx<D>& c, const KVRegs& r, int t0) {
-  constexpr int NCH = D / 8;
-  constexpr int KP = VERIFY_TILE * NCH / 256;
-  constexpr int VTS = VERIFY_TILE + 8;
-  constexpr int VUNITS = (VERIFY_TILE / 4) * NCH;
-  const int nt = min(VERIFY_TILE, c.je - t0);
-  stage_k<D>(c, r.k0, nt, 0);
-  stage_k<D>(c, r.k1, nt, 1);
-  if constexpr (KP > 2) {
-    stage_k<D>(c, r.k2, nt, 2);
-    stage_k<D>(c, r.k3, nt, 3);
-  }
-  if (c.tid < VUNITS) {
-    const int tg = c.tid / NCH, ch = c.tid % NCH;
-    const uint4 z = make_uint4(0u, 0u, 0u, 0u);
-    const uint4 a = (4 * tg + 0 < nt) ? r.v0 : z;
-    const uint4 b = (4 * tg + 1 < nt) ? r.v1 : z;
-    const uint4 d = (4 * tg + 2 < nt) ? r.v2 : z;
-    const uint4 e4 = (4 * tg + 3 < nt) ? r.v3 : z;
-    const uint32_t wa[4] = {a.x, a.y, a.z, a.w}, wb[4] = {b.x, b.y, b.z, b.w};
-    const uint32_t wd[4] = {d.x, d.y, d.z, d.w}, we[4] = {e4.x, e4.y, e4.z, e4.w};
+__device__ __forceinline__ void issue_kv_tile(char* stage, const int32_t* slots, const uint16_t* kp,
+                                              const uint16_t* vp, int64_t rs, int lane) {
+  constexpr int NCH = D / 8;         // 16-byte chunks per row
+  constexpr int RPI = 64 / NCH;      // rows per load instruction
+  constexpr int NI = DMA_TT / RPI;   // load instructions per tensor and tile
+  constexpr int STAGE = DMA_TT * D * 2;
+  const int sub = lane / NCH, pc = lane % NCH;
+  int sl[NI];  // all slot reads first: a later LDS read may not pass an LDS-writing load
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int w = e >> 1, hi = e & 1;
-      *reinterpret_cast<uint2*>(c.Vt + (8 * ch + e) * VTS + 4 * tg) =
-          make_uint2(half16(wa[w], hi) | (half16(wb[w], hi) << 16),
-                     half16(wd[w], hi) | (half16(we[w], hi) << 16));
-    }
+  for (int j = 0; j < NI; ++j) sl[j] = slots[RPI * j + sub];
+#pragma unroll
+  for (int j = 0; j < NI; ++j) {
+    const int tau = RPI * j + sub;
+    const int64_t row = (int64_t)sl[j] * rs;
+    load_lds16(kp + row + 8 * (pc ^ kswz_t<NCH>(tau)), stage + 1024 * j);
+    load_lds16(vp + row + 8 * (pc ^ vswz<NCH>(tau)), stage + STAGE + 1024 * j);
+  }
+}
+
+// Producer side of the per-tile barrier: wait until the awaited tile has
+// landed in LDS, `after` tiles having been issued behind it, then meet the
+// consumers.  A bare s_barrier: __syncthreads() would add a workgroup release
+// fence, which drains every outstanding global->LDS load, not just this tile.
+template <int PER_TILE>
+__device__ __forceinline__ void producer_barrier(int after) {
+  if (after >= 2)
+    wait_vmcnt<2 * PER_TILE>();
+  else if (after == 1)
+    wait_vmcnt<PER_TILE>();
+  else
+    wait_vmcnt<0>();
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+}
+
+// The chunk's slots are in LDS (slots[j - begin], tokens past the chunk end
+// padded with its last slot) before the producer starts.  It issues only
+// global->LDS loads, so partial vmcnt waits track its tiles exactly.
+template <int D>
+__device__ void verify_producer(const AttnParams& p, const Item& it, char* smem,
+                                const int32_t* slots, int lane) {
+  constexpr int NCH = D / 8;
+  constexpr int PER_TILE = 2 * (DMA_TT * NCH / 64);  // load instructions per tile
+  constexpr int STAGE2 = 2 * DMA_TT * D * 2;
+  static_assert(DMA_STAGES == 4, "the waits below assume two tiles behind the awaited one");
+  const int n = (it.end - it.begin + DMA_TT - 1) / DMA_TT;
+  const uint16_t* kp = reinterpret_cast<const uint16_t*>(p.k_pool) + it.g * D;
+  const uint16_t* vp = reinterpret_cast<const uint16_t*>(p.v_pool) + it.g * D;
+  const int64_t rs = (int64_t)p.Hkv * D;
+  for (int i = 0; i < min(n, DMA_STAGES - 1); ++i)
+    issue_kv_tile<D>(smem + i * STAGE2, slots + i * DMA_TT, kp, vp, rs, lane);
+  producer_barrier<PER_TILE>(min(n, DMA_STAGES - 1) - 1);  // tile 0 ready
+  for (int i = 0; i + 1 < n; ++i) {
+    const int t = i + DMA_STAGES - 1;  // into the stage tile i-1 used
+    if (t < n)
+      issue_kv_tile<D>(smem + (t % DMA_STAGES) * STAGE2, slots + t * DMA_TT, kp, vp, rs, lane);
+    producer_barrier<PER_TILE>(min(n - 1, t) - (i + 1));  // tile i+1 ready
   }
 }
 
 template <int D>
-__device__ void verify_tile_mfma(const AttnParams& p, const Item& it, char* smem) {
+__device__ void verify_consumer(const AttnParams& p, const Item& it, const char* smem, int wave,
+                                int lane) {
   constexpr int NCH = D / 8;   // 16-byte chunks per K/V row
   constexpr int KS = D / 32;   // k-steps of S^T = K Q^T
   constexpr int DT = D / 16;   // d tiles of O^T
-  constexpr int TT = VERIFY_TILE;
-  constexpr int VTS = TT + 8;  // bf16 elements per transposed V row
-  const int tid = threadIdx.x, nthr = blockDim.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int G = p.G, Hq = p.Hq, Hkv = p.Hkv;
+  constexpr int STAGE = DMA_TT * D * 2;
+  const int G = p.G, Hq = p.Hq;
   const int rows_q = p.k + 1;
   const int R = rows_q * G;
-  const int g = it.g;
   const int L = it.L;
   const int jb = it.begin, je = it.end;
-
-  uint4* Ks = reinterpret_cast<uint4*>(smem);
-  uint16_t* Vt = reinterpret_cast<uint16_t*>(smem + TT * NCH * 16);
-  int32_t* slots = reinterpret_cast<int32_t*>(smem + TT * NCH * 16 + D * VTS * 2);
-
-  const int32_t* ptr = p.page_table + (int64_t)it.r * p.pt_stride;
-  for (int j = jb + tid; j < je; j += nthr) slots[j - jb] = (int32_t)clamp_slot(ptr[j], p.num_slots);
+  const int n_tiles = (je - jb + DMA_TT - 1) / DMA_TT;
 
   const int n = lane & 15, q4 = lane >> 4;
   const int rho = wave * 16 + n;
@@ -249,7 +242,7 @@ __device__ void verify_tile_mfma(const AttnParams& p, const Item& it, char* smem
   const bool row_ok = rho < R;
   const int qi = row_ok ? rho / G : 0;
   const int hh = row_ok ? rho % G : 0;
-  const int h = g * G + hh;
+  const int h = it.g * G + hh;
 
   bf16x8 qop[KS];
   {
@@ -262,14 +255,6 @@ __device__ void verify_tile_mfma(const AttnParams& p, const Item& it, char* smem
       qop[s] = __builtin_bit_cast(bf16x8, v);
     }
   }
-  const uint16_t* kpool = reinterpret_cast<const uint16_t*>(p.k_pool);
-  const uint16_t* vpool = reinterpret_cast<const uint16_t*>(p.v_pool);
-  __syncthreads();  // slots visible
-
-  // Loads are unconditional (a token past the chunk end re-reads the chunk's
-  // last row) so that no branch separates them and several tiles stay in
-  // flight; validity is applied when the registers are staged into LDS.
-  const VerifyTileCtx<D> ctx{Ks, Vt, slots, kpool, vpool, tid, nthr, jb, je, g, Hkv};
   float m_run = NEG_INF, l_run = 0.f;
   f32x4 oacc[DT];
 #pragma unroll
@@ -279,105 +264,121 @@ __device__ void verify_tile_mfma(const AttnParams& p, const Item& it, char* smem
   const float sc = p.sm_scale;
   const bool rows_aligned = ((it.off | (int64_t)L) & 3) == 0;  // every logits row 16-byte aligned
 
-  auto compute = [&](int t0) {
-    if (!wave_active) return;
-    f32x4 sacc[4];
+  // Transpose-read source rows of this lane: tokens 4 q + n / 4 and 16 more.
+  // The lane supplies dims 4 (n % 4) .. + 3 of its 16-dim block.
+  const int vrow0 = 4 * q4 + (n >> 2), vrow1 = vrow0 + 16;
+  const int vcol = (n & 3);
+  // causal limit of the earliest row of the request: every row sees a token
+  // at or below it
+  const int vis_all = L - rows_q;
+
+  for (int i = 0; i < n_tiles; ++i) {
+    __syncthreads();  // tile i ready (and tile i-1 released)
+    if (!wave_active) continue;
+    const int t0 = jb + i * DMA_TT;
+    const char* Ks = smem + (i % DMA_STAGES) * 2 * STAGE;
+    const char* Vs = Ks + STAGE;
+    f32x4 sacc[2];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    for (int t = 0; t < 2; ++t) {
       sacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const int tau = 32 * (t >> 1) + 8 * (n >> 2) + 4 * (t & 1) + (n & 3);
+      const int tau = 16 * t + n;
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
         const int c = 4 * s + q4;
-        const uint4 kv = Ks[tau * NCH + (c ^ kswz<NCH>(tau))];
+        const uint4 kv =
+            *reinterpret_cast<const uint4*>(Ks + tau * NCH * 16 + 16 * (c ^ kswz_t<NCH>(tau)));
         sacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kv), qop[s],
                                                           sacc[t], 0, 0, 0);
       }
     }
-    float v[4][4];
+    // full tile: every token inside the chunk and visible to every row
+    const bool full = t0 + DMA_TT <= je && t0 + DMA_TT - 1 <= vis_all;
+    float v[2][4];
     float mx = NEG_INF;
+    if (full) {
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int tok = t0 + 32 * (t >> 1) + 8 * q4 + 4 * (t & 1) + i;
-        float x = sacc[t][i] * sc;
-        if (tok >= je || tok > last_vis) x = NEG_INF;
-        v[t][i] = x;
-        mx = fmaxf(mx, x);
+        for (int e = 0; e < 4; ++e) {
+          v[t][e] = sacc[t][e] * sc;
+          mx = fmaxf(mx, v[t][e]);
+        }
+      if (row_ok && rows_aligned) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+          *reinterpret_cast<float4*>(lrow + t0 + 16 * t + 4 * q4) =
+              make_float4(v[t][0], v[t][1], v[t][2], v[t][3]);
+      } else if (row_ok) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) lrow[t0 + 16 * t + 4 * q4 + e] = v[t][e];
       }
-    }
-    if (row_ok) {
+    } else {
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int tb = t0 + 32 * (t >> 1) + 8 * q4 + 4 * (t & 1);
-        float* dst = lrow + tb;
-        if (rows_aligned && tb + 4 <= je) {
-          *reinterpret_cast<float4*>(dst) = make_float4(v[t][0], v[t][1], v[t][2], v[t][3]);
-        } else {
+      for (int t = 0; t < 2; ++t) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (tb + i < je) dst[i] = v[t][i];
+        for (int e = 0; e < 4; ++e) {
+          const int tok = t0 + 16 * t + 4 * q4 + e;
+          float x = sacc[t][e] * sc;
+          if (tok >= je || tok > last_vis) x = NEG_INF;
+          v[t][e] = x;
+          mx = fmaxf(mx, x);
+        }
+      }
+      if (row_ok) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int tb = t0 + 16 * t + 4 * q4;
+          float* dst = lrow + tb;
+          if (rows_aligned && tb + 4 <= je) {
+            *reinterpret_cast<float4*>(dst) = make_float4(v[t][0], v[t][1], v[t][2], v[t][3]);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (tb + e < je) dst[e] = v[t][e];
+          }
         }
       }
     }
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float m_new = fmaxf(m_run, mx);
-    float alpha = 1.f, base = 0.f;
-    if (m_new != NEG_INF) {
-      alpha = fast_exp2((m_run - m_new) * LOG2E);
-      base = m_new * LOG2E;
+    // the accumulators are rescaled only when some row's maximum grew
+    if (__any(m_new > m_run)) {
+      const float alpha = (m_new == NEG_INF) ? 1.f : fast_exp2((m_run - m_new) * LOG2E);
+      l_run *= alpha;
+#pragma unroll
+      for (int dd = 0; dd < DT; ++dd) oacc[dd] *= alpha;
+      m_run = m_new;
     }
+    const float base = (m_run == NEG_INF) ? 0.f : m_run * LOG2E;
     float psum = 0.f;
-    float pf[4][4];
+    bf16x8 pb;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    for (int t = 0; t < 2; ++t) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float x = v[t][i];
-        const float e = (x == NEG_INF) ? 0.f : fast_exp2(fmaf(x, LOG2E, -base));
-        pf[t][i] = e;
-        psum += e;
+      for (int e = 0; e < 4; ++e) {
+        const float x = v[t][e];
+        const float ex = (full || x != NEG_INF) ? fast_exp2(fmaf(x, LOG2E, -base)) : 0.f;
+        pb[4 * t + e] = (__bf16)ex;
+        psum += ex;
       }
     }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
+    l_run += psum;
 #pragma unroll
-    for (int dd = 0; dd < DT; ++dd) oacc[dd] *= alpha;
-#pragma unroll
-    for (int kap = 0; kap < 2; ++kap) {
-      bf16x8 pb;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        pb[i] = (__bf16)pf[2 * kap][i];
-        pb[4 + i] = (__bf16)pf[2 * kap + 1][i];
-      }
-#pragma unroll
-      for (int dd = 0; dd < DT; ++dd) {
-        const uint4 vv =
-            *reinterpret_cast<const uint4*>(Vt + (16 * dd + n) * VTS + 32 * kap + 8 * q4);
-        oacc[dd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vv), pb,
-                                                           oacc[dd], 0, 0, 0);
-      }
+    for (int dd = 0; dd < DT; ++dd) {
+      const int c = 2 * dd + (vcol >> 1);
+      const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_v4i16*)(Vs + vrow0 * NCH * 16 + 16 * (c ^ vswz<NCH>(vrow0)) + 8 * (vcol & 1)));
+      const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_v4i16*)(Vs + vrow1 * NCH * 16 + 16 * (c ^ vswz<NCH>(vrow1)) + 8 * (vcol & 1)));
+      const bf16x8 va = __builtin_bit_cast(
+          bf16x8, (short __attribute__((ext_vector_type(8)))){lo[0], lo[1], lo[2], lo[3], hi[0],
+                                                              hi[1], hi[2], hi[3]});
+      oacc[dd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, oacc[dd], 0, 0, 0);
     }
-  };
-
-  KVRegs A, B;
-  fetch_tile(ctx, A, jb);
-  if (jb + TT < je) fetch_tile(ctx, B, jb + TT);
-  for (int t0 = jb; t0 < je; t0 += 2 * TT) {
-    if (t0 != jb) __syncthreads();  // previous tile consumed
-    stage_tile(ctx, A, t0);
-    __syncthreads();
-    if (t0 + 2 * TT < je) fetch_tile(ctx, A, t0 + 2 * TT);
-    compute(t0);
-    if (t0 + TT >= je) break;
-    __syncthreads();
-    stage_tile(ctx, B, t0 + TT);
-    __syncthreads();
-    if (t0 + 3 * TT < je) fetch_tile(ctx, B, t0 + 3 * TT);
-    compute(t0 + TT);
   }
 
   if (!wave_active) return;
@@ -407,6 +408,23 @@ __device__ void verify_tile_mfma(const AttnParams& p, const Item& it, char* smem
       p.part_ml[2 * pr + 1] = l_tot;
     }
   }
+}
+
+template <int D>
+__device__ void verify_tile_mfma(const AttnParams& p, const Item& it, char* smem) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // slots of the chunk, padded to whole tiles
+  int32_t* slots = reinterpret_cast<int32_t*>(smem + dma_smem_bytes<D>());
+  const int jb = it.begin, je = it.end;
+  const int padded = (je - jb + DMA_TT - 1) / DMA_TT * DMA_TT;
+  const int32_t* pt = p.page_table + (int64_t)it.r * p.pt_stride;
+  for (int j = tid; j < padded; j += blockDim.x)
+    slots[j] = (int32_t)clamp_slot(pt[min(jb + j, je - 1)], p.num_slots);
+  __syncthreads();
+  if (wave == (int)(blockDim.x >> 6) - 1)
+    verify_producer<D>(p, it, smem, slots, lane);
+  else
+    verify_consumer<D>(p, it, smem, wave, lane);
 }
 
 // ==========================================================================
@@ -975,7 +993,8 @@ static int group_template(int G) { return G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 :
 size_t attn_smem_bytes(int dtype, int head_dim, int G, int nthr, bool mfma_verify, bool valu) {
   size_t s = 16;
   if (mfma_verify)
-    s = std::max(s, head_dim == 128 ? mfma_smem_bytes<128>() : mfma_smem_bytes<64>());
+    s = std::max(s, (head_dim == 128 ? dma_smem_bytes<128>() : dma_smem_bytes<64>()) +
+                        (size_t)VERIFY_MAX_CHUNK * 4);
   if (valu) {
     const int GM = group_template(G);
     const int E = dtype == 0 ? 8 : 4;

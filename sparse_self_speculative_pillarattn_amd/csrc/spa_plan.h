@@ -58,11 +58,10 @@ struct PostItem {
 };
 
 constexpr int AVG_SPAN = 1024;         // positions per averaging item
-constexpr int VERIFY_TILE = 64;        // tokens per LDS tile of the MFMA verify path
 constexpr int VERIFY_MAX_CHUNK = 2048;
 constexpr int DRAFT_MAX_CHUNK = 2048;
 constexpr int MAX_GROUP = 8;           // query heads per KV head on the VALU path
-constexpr int MAX_ROW_TILES = 8;       // 16-row MFMA tiles (one wave each, 512 threads max)
+constexpr int MAX_ROW_TILES = 7;       // 16-row MFMA tiles (one wave each + a producer, 512 threads max)
 constexpr int MAX_AVG_TERMS = 512;     // averaged (row, head) pairs per KV head
 constexpr int MAX_MERGE_CHUNKS = 256;  // split-K chunks per (r, g)
 constexpr int MERGE_ROWS = 8;          // rows per merge item
