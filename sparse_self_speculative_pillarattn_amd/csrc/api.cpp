@@ -203,20 +203,21 @@ int32_t plan_size(const Shape& s, const std::vector<Req>& rq, bool attn, bool to
   pl->pbar_elems = pbar;
 
   // block shape and LDS of the attention launch
+  // bf16: every item on the MFMA path; fp32: every item on the VALU path
   bool need_mfma = false, need_valu = false;
   if (attn) {
-    need_mfma = any_verify && bf16;
-    need_valu = any_draft || (any_verify && !bf16);
+    need_mfma = bf16;
+    need_valu = !bf16;
   }
   int nthr = 256;
   if (need_mfma) {
-    const int nt = (rows_v * G + 15) / 16;
+    const int nt = ((any_verify ? rows_v : 1) * G + 15) / 16;
     if (nt > MAX_ROW_TILES)
       return fail(SPA_ERR_UNSUPPORTED, "(k+1)*G above 112 rows per KV head on the MFMA path");
     nthr = 64 * std::max(4, nt + 1);  // one consumer wave per row tile, one producer wave
   }
   if (need_valu && G > MAX_GROUP)
-    return fail(SPA_ERR_UNSUPPORTED, "GQA group above 8 on the gather path");
+    return fail(SPA_ERR_UNSUPPORTED, "GQA group above 8 on the fp32 path");
   pl->nthr = nthr;
   pl->smem = attn ? attn_smem_bytes(s.dtype, D, G, nthr, need_mfma, need_valu) : 0;
 

@@ -174,7 +174,7 @@ __device__ __forceinline__ void issue_kv_tile(char* stage, const int32_t* slots,
 #pragma unroll
   for (int j = 0; j < NI; ++j) {
     const int tau = RPI * j + sub;
-    const int64_t row = (int64_t)sl[j] * rs;
+    const int64_t row = (int64_t)max(sl[j], 0) * rs;  // a masked entry reads row 0
     load_lds16(kp + row + 8 * (pc ^ kswz_t<NCH>(tau)), stage + 1024 * j);
     load_lds16(vp + row + 8 * (pc ^ vswz<NCH>(tau)), stage + STAGE + 1024 * j);
   }
@@ -197,11 +197,11 @@ __device__ __forceinline__ void producer_barrier(int after) {
   __asm__ volatile("" ::: "memory");
 }
 
-// The chunk's slots are in LDS (slots[j - begin], tokens past the chunk end
-// padded with its last slot) before the producer starts.  It issues only
+// The chunk's slots are in LDS (slots[j], -1 for an entry that is masked)
+// before the producer starts.  It issues only
 // global->LDS loads, so partial vmcnt waits track its tiles exactly.
 template <int D>
-__device__ void verify_producer(const AttnParams& p, const Item& it, char* smem,
+__device__ void dma_producer(const AttnParams& p, const Item& it, char* smem,
                                 const int32_t* slots, int lane) {
   constexpr int NCH = D / 8;
   constexpr int PER_TILE = 2 * (DMA_TT * NCH / 64);  // load instructions per tile
@@ -223,14 +223,14 @@ __device__ void verify_producer(const AttnParams& p, const Item& it, char* smem,
 }
 
 template <int D>
-__device__ void verify_consumer(const AttnParams& p, const Item& it, const char* smem, int wave,
-                                int lane) {
+__device__ void dma_consumer(const AttnParams& p, const Item& it, const char* smem,
+                             const int32_t* slots, bool is_list, int wave, int lane) {
   constexpr int NCH = D / 8;   // 16-byte chunks per K/V row
   constexpr int KS = D / 32;   // k-steps of S^T = K Q^T
   constexpr int DT = D / 16;   // d tiles of O^T
   constexpr int STAGE = DMA_TT * D * 2;
   const int G = p.G, Hq = p.Hq;
-  const int rows_q = p.k + 1;
+  const int rows_q = is_list ? 1 : p.k + 1;
   const int R = rows_q * G;
   const int L = it.L;
   const int jb = it.begin, je = it.end;
@@ -259,8 +259,8 @@ __device__ void verify_consumer(const AttnParams& p, const Item& it, const char*
   f32x4 oacc[DT];
 #pragma unroll
   for (int i = 0; i < DT; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int last_vis = L - rows_q + qi;
-  float* lrow = p.logits + it.off + ((int64_t)qi * Hq + h) * L;
+  const int last_vis = is_list ? 0x7fffffff : L - rows_q + qi;
+  float* lrow = is_list ? nullptr : p.logits + it.off + ((int64_t)qi * Hq + h) * L;
   const float sc = p.sm_scale;
   const bool rows_aligned = ((it.off | (int64_t)L) & 3) == 0;  // every logits row 16-byte aligned
 
@@ -292,8 +292,9 @@ __device__ void verify_consumer(const AttnParams& p, const Item& it, const char*
                                                           sacc[t], 0, 0, 0);
       }
     }
-    // full tile: every token inside the chunk and visible to every row
-    const bool full = t0 + DMA_TT <= je && t0 + DMA_TT - 1 <= vis_all;
+    // full tile: every token inside the chunk and visible to every row (a
+    // list tile is masked by the slots staged for it)
+    const bool full = !is_list && t0 + DMA_TT <= je && t0 + DMA_TT - 1 <= vis_all;
     float v[2][4];
     float mx = NEG_INF;
     if (full) {
@@ -316,18 +317,35 @@ __device__ void verify_consumer(const AttnParams& p, const Item& it, const char*
           for (int e = 0; e < 4; ++e) lrow[t0 + 16 * t + 4 * q4 + e] = v[t][e];
       }
     } else {
+      int ok[2][4];
+      if (is_list) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int4 sv = *reinterpret_cast<const int4*>(slots + i * DMA_TT + 16 * t + 4 * q4);
+          ok[t][0] = sv.x >= 0;
+          ok[t][1] = sv.y >= 0;
+          ok[t][2] = sv.z >= 0;
+          ok[t][3] = sv.w >= 0;
+        }
+      } else {
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int tok = t0 + 16 * t + 4 * q4 + e;
+            ok[t][e] = tok < je && tok <= last_vis;
+          }
+      }
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int tok = t0 + 16 * t + 4 * q4 + e;
-          float x = sacc[t][e] * sc;
-          if (tok >= je || tok > last_vis) x = NEG_INF;
+          const float x = ok[t][e] ? sacc[t][e] * sc : NEG_INF;
           v[t][e] = x;
           mx = fmaxf(mx, x);
         }
       }
-      if (row_ok) {
+      if (row_ok && !is_list) {
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           const int tb = t0 + 16 * t + 4 * q4;
@@ -410,21 +428,36 @@ __device__ void verify_consumer(const AttnParams& p, const Item& it, const char*
   }
 }
 
+// One attention item on the MFMA path: a verify chunk (positions [begin, end)
+// under the causal limit, logits dumped) or a draft chunk (list entries
+// [begin, end); an entry outside [0, L) is masked).
 template <int D>
-__device__ void verify_tile_mfma(const AttnParams& p, const Item& it, char* smem) {
+__device__ void attn_tile_dma(const AttnParams& p, const Item& it, char* smem, bool is_list) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // slots of the chunk, padded to whole tiles
+  // slots of the chunk, padded to whole tiles; -1 marks a masked entry
   int32_t* slots = reinterpret_cast<int32_t*>(smem + dma_smem_bytes<D>());
   const int jb = it.begin, je = it.end;
   const int padded = (je - jb + DMA_TT - 1) / DMA_TT * DMA_TT;
   const int32_t* pt = p.page_table + (int64_t)it.r * p.pt_stride;
-  for (int j = tid; j < padded; j += blockDim.x)
-    slots[j] = (int32_t)clamp_slot(pt[min(jb + j, je - 1)], p.num_slots);
+  if (is_list) {
+    const int32_t* list = p.idx_in + it.off;
+    for (int j = tid; j < padded; j += blockDim.x) {
+      int32_t sl = -1;
+      if (jb + j < je) {
+        const int pos = list[jb + j];
+        if (pos >= 0 && pos < it.L) sl = (int32_t)clamp_slot(pt[pos], p.num_slots);
+      }
+      slots[j] = sl;
+    }
+  } else {
+    for (int j = tid; j < padded; j += blockDim.x)
+      slots[j] = (int32_t)clamp_slot(pt[min(jb + j, je - 1)], p.num_slots);
+  }
   __syncthreads();
   if (wave == (int)(blockDim.x >> 6) - 1)
-    verify_producer<D>(p, it, smem, slots, lane);
+    dma_producer<D>(p, it, smem, slots, lane);
   else
-    verify_consumer<D>(p, it, smem, wave, lane);
+    dma_consumer<D>(p, it, smem, slots, is_list, wave, lane);
 }
 
 // ==========================================================================
@@ -635,16 +668,13 @@ __global__ void __launch_bounds__(512) attn_kernel(AttnParams p) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const Item it = p.items[blockIdx.x];
   if (it.kind == KIND_NOP) return;
-  if (it.kind == KIND_VERIFY) {
-    if constexpr (sizeof(T) == 2) {
-      verify_tile_mfma<D>(p, it, smem);
-    } else {
-      const int qi = it.qi;
-      const int last_vis = it.L - (p.k + 1) + qi;
-      float* lrow = p.logits + it.off + ((int64_t)qi * p.Hq + it.g * p.G) * it.L;
-      gather_tile_valu<D, T, GM>(p, it, smem, false, qi, last_vis, lrow, qi * p.G,
-                                 (p.k + 1) * p.G);
-    }
+  if constexpr (sizeof(T) == 2) {
+    attn_tile_dma<D>(p, it, smem, it.kind == KIND_DRAFT);
+  } else if (it.kind == KIND_VERIFY) {
+    const int qi = it.qi;
+    const int last_vis = it.L - (p.k + 1) + qi;
+    float* lrow = p.logits + it.off + ((int64_t)qi * p.Hq + it.g * p.G) * it.L;
+    gather_tile_valu<D, T, GM>(p, it, smem, false, qi, last_vis, lrow, qi * p.G, (p.k + 1) * p.G);
   } else {
     gather_tile_valu<D, T, GM>(p, it, smem, true, 0, 0x7fffffff, nullptr, 0, p.G);
   }

@@ -102,8 +102,8 @@ def test_empty_batch_is_a_noop(lib):
     (dict(null=("q",)), bd.SPA_ERR_INVALID_ARG),
     (dict(null=("ws",), ws_bytes=1 << 30), bd.SPA_ERR_INVALID_ARG),
     (dict(null=("logits",)), bd.SPA_ERR_INVALID_ARG),
-    (dict(lay=dict(num_qo_heads=160, num_kv_heads=8), ioff=(0, 100)),
-     bd.SPA_ERR_UNSUPPORTED),  # G = 20 rows exceed the MFMA tile budget
+    (dict(lay=dict(num_qo_heads=192, num_kv_heads=8), ioff=(0, 100)),
+     bd.SPA_ERR_UNSUPPORTED),  # (k+1) G = 120 rows exceed the 112-row MFMA budget
 ])
 def test_unified_step_rejects(lib, kw, code):
     lay = _lay(**kw.pop("lay", {}))

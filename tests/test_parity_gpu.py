@@ -72,6 +72,20 @@ def test_mixed_batch(oracle, shape, dtype):
     check(oracle, w)
 
 
+@pytest.mark.parametrize("shape", [(32, 2, 128, 6, ("uniform", 7, 900)),
+                                   (64, 4, 128, 3, ("uniform", 40, 1300)),
+                                   (16, 1, 64, 2, ("uniform", 3, 500))],
+                         ids=lambda s: f"h{s[0]}kv{s[1]}d{s[2]}k{s[3]}")
+def test_large_group_bf16(oracle, shape):
+    """GQA groups above 8 (bf16 only): draft rows of G = 16 heads, and the
+    largest verify row count, (k+1) G = 112, i.e. seven MFMA row tiles."""
+    Hq, Hkv, d, k, lengths = shape
+    w = synth.Workload(name=f"bigg-{Hq}-{Hkv}-{d}-{k}", batch=6, num_qo_heads=Hq,
+                       num_kv_heads=Hkv, head_dim=d, dtype="bf16", spec_k=k,
+                       sparsity=Fraction(1, 10), lengths=lengths, n_verify=2, seed=31)
+    check(oracle, w)
+
+
 @pytest.mark.parametrize("L", [9, 63, 64, 65, 127, 129, 1000, 2049])
 def test_ragged_lengths(oracle, L):
     w = synth.Workload(name=f"ragged-{L}", batch=3, num_qo_heads=32, num_kv_heads=8,
