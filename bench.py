@@ -173,7 +173,8 @@ def main():
     ap.add_argument("--workload", default=synth.QWEN3_8B.name, choices=sorted(synth.WORKLOADS))
     ap.add_argument("--cold-steps", type=int, default=20,
                     help="steps timed one by one after a 512 MB cache-flushing write")
-    ap.add_argument("--cpu-repeats", type=int, default=3)
+    ap.add_argument("--cpu-repeats", type=int, default=15,
+                    help="oracle runs of the whole step (about 0.8 s each on 16 EPYC cores)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
 

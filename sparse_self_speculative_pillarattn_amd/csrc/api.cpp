@@ -31,7 +31,7 @@ thread_local std::string g_err;
 std::atomic<int32_t> g_verify_chunk{0};
 std::atomic<int32_t> g_draft_chunk{0};
 
-constexpr int DEFAULT_VERIFY_CHUNK = 512;
+constexpr int DEFAULT_VERIFY_CHUNK = 2048;  // fewer split-K partials; drafts fill the XCD queues
 constexpr int DEFAULT_DRAFT_CHUNK = 1024;
 constexpr int NUM_XCD = 8;
 
@@ -219,7 +219,9 @@ int32_t plan_size(const Shape& s, const std::vector<Req>& rq, bool attn, bool to
   if (need_valu && G > MAX_GROUP)
     return fail(SPA_ERR_UNSUPPORTED, "GQA group above 8 on the fp32 path");
   pl->nthr = nthr;
-  pl->smem = attn ? attn_smem_bytes(s.dtype, D, G, nthr, need_mfma, need_valu) : 0;
+  int max_chunk = 1;  // longest item: positions (verify) or list entries (draft)
+  for (auto& q : rq) max_chunk = std::max(max_chunk, std::min(q.verify ? q.L : q.nlist, q.verify ? CV : CD));
+  pl->smem = attn ? attn_smem_bytes(s.dtype, D, G, nthr, need_mfma, need_valu, max_chunk) : 0;
 
   // pinned plan layout
   size_t h = 0;

@@ -206,7 +206,7 @@ __device__ void dma_producer(const AttnParams& p, const Item& it, char* smem,
   constexpr int NCH = D / 8;
   constexpr int PER_TILE = 2 * (DMA_TT * NCH / 64);  // load instructions per tile
   constexpr int STAGE2 = 2 * DMA_TT * D * 2;
-  static_assert(DMA_STAGES == 4, "the waits below assume two tiles behind the awaited one");
+  static_assert(DMA_STAGES == 3 || DMA_STAGES == 4, "the waits below allow at most two tiles behind");
   const int n = (it.end - it.begin + DMA_TT - 1) / DMA_TT;
   const uint16_t* kp = reinterpret_cast<const uint16_t*>(p.k_pool) + it.g * D;
   const uint16_t* vp = reinterpret_cast<const uint16_t*>(p.v_pool) + it.g * D;
@@ -1020,11 +1020,12 @@ __global__ void __launch_bounds__(SELECT_THREADS) select_kernel(SelectParams sp)
 // ==========================================================================
 static int group_template(int G) { return G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : G <= 5 ? 5 : 8; }
 
-size_t attn_smem_bytes(int dtype, int head_dim, int G, int nthr, bool mfma_verify, bool valu) {
+size_t attn_smem_bytes(int dtype, int head_dim, int G, int nthr, bool mfma, bool valu,
+                       int max_chunk) {
   size_t s = 16;
-  if (mfma_verify)
+  if (mfma)  // stage ring, then the slots of the longest chunk padded to whole tiles
     s = std::max(s, (head_dim == 128 ? dma_smem_bytes<128>() : dma_smem_bytes<64>()) +
-                        (size_t)VERIFY_MAX_CHUNK * 4);
+                        (size_t)(max_chunk + DMA_TT - 1) / DMA_TT * DMA_TT * 4);
   if (valu) {
     const int GM = group_template(G);
     const int E = dtype == 0 ? 8 : 4;

@@ -44,7 +44,8 @@ struct SelectParams {
 };
 
 // LDS bytes the attention kernel needs for a launch shape.
-size_t attn_smem_bytes(int dtype, int head_dim, int G, int nthr, bool mfma_verify, bool valu);
+size_t attn_smem_bytes(int dtype, int head_dim, int G, int nthr, bool mfma, bool valu,
+                       int max_chunk);
 size_t post_smem_bytes();
 
 hipError_t launch_attn(const AttnParams& p, int dtype, int head_dim, int nitems, int nthr,

@@ -135,7 +135,15 @@ def test_set_split_bounds(lib):
     assert lib.spa_set_split(0, 0) == bd.SPA_OK
 
 
-def test_other_entry_points_validate(lib):
+@pytest.fixture
+def small_split(lib):
+    """Work chunks of 512 positions / 256 list entries for the test's duration."""
+    assert lib.spa_set_split(512, 256) == bd.SPA_OK
+    yield
+    assert lib.spa_set_split(0, 0) == bd.SPA_OK
+
+
+def test_other_entry_points_validate(lib, small_split):
     lay = _lay(page_table_stride=2048)
     # lengths above one work chunk, so that every call below needs workspace
     lens, lp = _arr([1000, 800], np.int32)
