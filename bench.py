@@ -176,6 +176,9 @@ def main():
     ap.add_argument("--cpu-repeats", type=int, default=15,
                     help="oracle runs of the whole step (about 0.8 s each on 16 EPYC cores)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run 5 plain device copies of MIB MiB (reference for the HBM "
+                         "byte counters) and exit")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -185,9 +188,19 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
-    bd.load()  # fails loudly when libspa.so is missing
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones((n,), dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            dst.copy_(src)  # reads n bytes, writes n bytes
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n, "copies": 5}))
+        return
+    bd.load()  # fails loudly when libspa.so is missing
     w = synth.WORKLOADS[args.workload]
     print(f"[bench] generating {w.name} on {dev}", file=sys.stderr, flush=True)
     b = synth.make_batch(w, device=dev)
