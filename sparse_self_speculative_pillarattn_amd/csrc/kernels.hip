@@ -761,16 +761,28 @@ __device__ void merge_rows(const PostParams& p, const PostItem& it, char* smem) 
   store_out<T>(dst + 3, acc.w);
 }
 
-// Block-wide exclusive prefix of per-thread counts (wave scan + per-wave
+// Inclusive prefix sum over the 64 lanes of a wave with DPP only: row_shr
+// 1, 2, 4, 8 scans each row of 16 lanes; row_bcast:15 then row_bcast:31 carry
+// the row totals into the later rows.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_rows(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWS, 0xf, false);
+}
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+  v += dpp_rows<0x111, 0xf>(v);  // row_shr:1
+  v += dpp_rows<0x112, 0xf>(v);  // row_shr:2
+  v += dpp_rows<0x114, 0xf>(v);  // row_shr:4
+  v += dpp_rows<0x118, 0xf>(v);  // row_shr:8
+  v += dpp_rows<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
+  v += dpp_rows<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
+  return v;
+}
+
+// Block-wide exclusive prefix of per-thread counts (DPP wave scan + per-wave
 // totals in LDS).  Returns the prefix; *total receives the block sum.
 __device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* wsum, uint32_t* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
-  uint32_t incl = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t y = __shfl_up(incl, off);
-    if (lane >= off) incl += y;
-  }
+  const uint32_t incl = wave_incl_scan(v);
   if (lane == 63) wsum[wave] = incl;
   __syncthreads();
   uint32_t before = 0, all = 0;
@@ -784,24 +796,59 @@ __device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* wsum, uint32_t* t
   return before + incl - v;
 }
 
+// Sum, AND and OR over each row of 16 lanes (DPP, no LDS); every lane of the
+// row receives the result.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dppu(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xf, 0xf, false);
+}
+__device__ __forceinline__ uint32_t row_sum_u32(uint32_t v) {
+  v += dppu<DPP_XOR1>(v);
+  v += dppu<DPP_XOR2>(v);
+  v += dppu<DPP_HALF_MIRROR>(v);
+  v += dppu<DPP_MIRROR>(v);
+  return v;
+}
+__device__ __forceinline__ uint32_t row_and_u32(uint32_t v) {
+  v &= dppu<DPP_XOR1>(v);
+  v &= dppu<DPP_XOR2>(v);
+  v &= dppu<DPP_HALF_MIRROR>(v);
+  v &= dppu<DPP_MIRROR>(v);
+  return v;
+}
+__device__ __forceinline__ uint32_t row_or_u32(uint32_t v) {
+  v |= dppu<DPP_XOR1>(v);
+  v |= dppu<DPP_XOR2>(v);
+  v |= dppu<DPP_HALF_MIRROR>(v);
+  v |= dppu<DPP_MIRROR>(v);
+  return v;
+}
+
+constexpr int SELECT_FINISH = 64;  // candidates ranked directly by one wave
+
 // Top-K of L non-negative fp32 scores (their bit patterns order like the
-// values).  MSB-first radix select, 8 bits per pass, finds the K-th largest
+// values).  MSB-first radix select with 4-bit digits finds the K-th largest
 // value tau and how many positions equal to it are kept; the compaction then
 // writes every position above tau and the lowest positions equal to tau,
 // ascending.  Thread t owns the KPT consecutive positions c0 + KPT t + [0, KPT)
 // of each chunk of KPT*nthr positions; keys stay in registers when L fits one
-// chunk and are re-read chunk by chunk otherwise.  Each wave counts into its
-// own histogram so that atomics only contend inside a wave.
-// LDS: 276 + 256 * waves words.
+// chunk and are re-read chunk by chunk otherwise.
+//   - The digits every key shares (block-wide AND/OR) are skipped.
+//   - A pass counts without atomics: 4-bit counters packed in two registers
+//     per thread (KPT <= 8 per chunk), widened to bytes and summed over rows
+//     of 16 lanes with DPP (<= 128 per byte), then to 32 bits per digit.
+//   - Once the bucket holding the K-th key has at most 64 keys, they are
+//     gathered into LDS and one wave ranks them directly.
 template <int KPT>
 __device__ void select_topk(const float* scores, int L, int K, int32_t* out, char* smem) {
-  static_assert(KPT % 4 == 0, "keys are loaded four at a time");
-  uint32_t* hist = reinterpret_cast<uint32_t*>(smem);  // [256] block histogram
-  uint32_t* sv = hist + 256;                           // prefix, rem
-  uint32_t* wsum = sv + 4;                             // [16]
-  uint32_t* whist = wsum + 16;                         // [nwaves][256] per-wave histograms
+  static_assert(KPT % 4 == 0 && KPT <= 8, "keys are loaded four at a time; nibble counters");
+  uint32_t* sv = reinterpret_cast<uint32_t*>(smem);  // prefix, rem, bucket count, and/or
+  uint32_t* wsum = sv + 8;                           // [16] block scans
+  uint32_t* tab = wsum + 16;                         // [waves * 4 rows][16 digits]
+  uint32_t* ckey = tab + 16 * 64;                    // [SELECT_FINISH] candidate keys
   const uint32_t* keys = reinterpret_cast<const uint32_t*>(scores);
   const int tid = threadIdx.x, nthr = blockDim.x, lane = tid & 63, wave = tid >> 6;
+  const int nrows = (nthr >> 6) * 4;
   const int span = KPT * nthr;
   const bool resident = L <= span;
   const bool vec = (reinterpret_cast<uintptr_t>(scores) & 15) == 0;
@@ -824,65 +871,144 @@ __device__ void select_topk(const float* scores, int L, int K, int32_t* out, cha
     }
   };
   if (resident) load(0);
-  __syncthreads();
+  // bits shared by every key: AND and OR over the block
   if (tid == 0) {
-    sv[0] = 0u;
-    sv[1] = (uint32_t)K;
+    sv[4] = 0xffffffffu;
+    sv[5] = 0u;
   }
-  const int nwaves = nthr >> 6;
-  uint32_t* my_hist = whist + 256 * wave;
-  uint32_t mask = 0u;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int b = tid; b < 256 * nwaves; b += nthr) whist[b] = 0u;
-    __syncthreads();
-    const uint32_t prefix = sv[0];
+  __syncthreads();
+  {
+    uint32_t va = 0xffffffffu, vo = 0u;
     for (int c0 = 0; c0 < L; c0 += span) {
       if (!resident) load(c0);
       const int j0 = c0 + KPT * tid;
 #pragma unroll
       for (int m = 0; m < KPT; ++m)
-        if (j0 + m < L && (key[m] & mask) == prefix) atomicAdd(&my_hist[(key[m] >> shift) & 255u], 1u);
+        if (j0 + m < L) {
+          va &= key[m];
+          vo |= key[m];
+        }
     }
-    __syncthreads();
-    for (int b = tid; b < 256; b += nthr) {
-      uint32_t sum = 0u;
-      for (int w = 0; w < nwaves; ++w) sum += whist[256 * w + b];
-      hist[b] = sum;
+    va = row_and_u32(va);
+    vo = row_or_u32(vo);
+    if ((lane & 15) == 0) {
+      atomicAnd(&sv[4], va);
+      atomicOr(&sv[5], vo);
+    }
+  }
+  if (tid == 0) {
+    sv[0] = 0u;
+    sv[1] = (uint32_t)K;
+  }
+  __syncthreads();
+  const uint32_t diff = sv[4] ^ sv[5];
+  int shift = diff == 0u ? 0 : (31 - __builtin_clz(diff)) / 4 * 4;  // top differing digit
+  uint32_t mask = shift >= 28 ? 0u : 0xffffffffu << (shift + 4);
+  if (tid == 0) sv[0] = sv[4] & mask;  // the shared leading digits
+  __syncthreads();
+  bool finish = false;
+  for (; shift >= 0; shift -= 4) {
+    const uint32_t prefix = sv[0];
+    uint32_t acc[16];  // per row of 16 lanes
+#pragma unroll
+    for (int d = 0; d < 16; ++d) acc[d] = 0u;
+    for (int c0 = 0; c0 < L; c0 += span) {
+      if (!resident) load(c0);
+      const int j0 = c0 + KPT * tid;
+      // Positions past L hold key 0, the smallest value, and come after every
+      // real position in the tie order, so counting them never moves the
+      // K-th largest real key (K <= L); the compaction skips them.
+      uint32_t lo = 0u, hi = 0u;  // nibble counters of digits 0..7 and 8..15
+#pragma unroll
+      for (int m = 0; m < KPT; ++m) {
+        const bool inb = (key[m] & mask) == prefix;
+        const uint32_t d = (key[m] >> shift) & 15u;
+        const uint32_t inc = inb ? (1u << (4u * (d & 7u))) : 0u;
+        if (d < 8u)
+          lo += inc;
+        else
+          hi += inc;
+      }
+      // bytes of w: digits (0,2,4,6), (1,3,5,7), (8,10,12,14), (9,11,13,15)
+      const uint32_t w[4] = {row_sum_u32(lo & 0x0f0f0f0fu), row_sum_u32((lo >> 4) & 0x0f0f0f0fu),
+                             row_sum_u32(hi & 0x0f0f0f0fu), row_sum_u32((hi >> 4) & 0x0f0f0f0fu)};
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[8 * (q >> 1) + 2 * e + (q & 1)] += (w[q] >> (8 * e)) & 255u;
+    }
+    if ((lane & 15) == 0) {
+      uint32_t* row = tab + 16 * (wave * 4 + (lane >> 4));
+#pragma unroll
+      for (int d = 0; d < 16; d += 4)
+        *reinterpret_cast<uint4*>(row + d) = make_uint4(acc[d], acc[d + 1], acc[d + 2], acc[d + 3]);
     }
     __syncthreads();
     if (wave == 0) {
-      uint32_t cnt[4], sum = 0u;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        cnt[i] = hist[255 - 4 * lane - i];
-        sum += cnt[i];
-      }
-      uint32_t incl = sum;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t y = __shfl_up(incl, off);
-        if (lane >= off) incl += y;
-      }
-      const uint32_t excl = incl - sum;
+      // lane l: digit dl = 15 - (l & 15) over rows (l >> 4) + 4 i
+      const int dl = 15 - (lane & 15);
+      uint32_t cnt = 0u;
+#pragma unroll 4
+      for (int r = lane >> 4; r < nrows; r += 4) cnt += tab[16 * r + dl];
+      cnt += __shfl_xor(cnt, 16);
+      cnt += __shfl_xor(cnt, 32);
+      uint32_t incl = cnt;  // inclusive scan inside each row of 16 lanes
+      incl += dpp_rows<0x111, 0xf>(incl);
+      incl += dpp_rows<0x112, 0xf>(incl);
+      incl += dpp_rows<0x114, 0xf>(incl);
+      incl += dpp_rows<0x118, 0xf>(incl);
       const uint32_t rem = sv[1];
-      if (excl < rem && incl >= rem) {
-        uint32_t acc = excl;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if (acc + cnt[i] >= rem) {
-            sv[0] = prefix | ((uint32_t)(255 - 4 * lane - i) << shift);
-            sv[1] = rem - acc;
-            break;
-          }
-          acc += cnt[i];
-        }
+      const uint32_t excl = incl - cnt;
+      if (lane < 16 && excl < rem && incl >= rem) {
+        sv[0] = prefix | ((uint32_t)dl << shift);
+        sv[1] = rem - excl;
+        sv[2] = cnt;
       }
     }
-    mask |= 255u << shift;
+    mask |= 15u << shift;
+    __syncthreads();
+    if (sv[2] <= (uint32_t)SELECT_FINISH && shift > 0) {
+      finish = true;
+      break;
+    }
+  }
+  if (finish) {
+    // gather the keys of the chosen bucket and rank them in one wave
+    const uint32_t prefix = sv[0];
+    uint32_t base = 0u;
+    for (int c0 = 0; c0 < L; c0 += span) {
+      if (!resident) load(c0);
+      const int j0 = c0 + KPT * tid;
+      uint32_t n = 0u;
+#pragma unroll
+      for (int m = 0; m < KPT; ++m) n += (j0 + m < L && (key[m] & mask) == prefix) ? 1u : 0u;
+      uint32_t tot;
+      uint32_t pos = base + block_exclusive_scan(n, wsum, &tot);
+#pragma unroll
+      for (int m = 0; m < KPT; ++m)
+        if (j0 + m < L && (key[m] & mask) == prefix) ckey[pos++] = key[m];
+      base += tot;
+    }
+    __syncthreads();
+    if (wave == 0) {
+      const int nc = (int)sv[2];
+      const uint32_t rem = sv[1];
+      const uint32_t mine = lane < nc ? ckey[lane] : 0u;
+      uint32_t gt = 0u, eq = 0u;
+      for (int j = 0; j < nc; ++j) {  // candidate j broadcast from its lane
+        const uint32_t o = (uint32_t)__builtin_amdgcn_readlane((int)mine, j);
+        gt += o > mine ? 1u : 0u;
+        eq += o == mine ? 1u : 0u;
+      }
+      if (lane < nc && gt < rem && gt + eq >= rem) {
+        sv[0] = mine;
+        sv[1] = rem - gt;
+      }
+    }
     __syncthreads();
   }
   const uint32_t tau = sv[0], rem = sv[1];
-  uint32_t base_eq = 0, base_take = 0;
+  uint32_t base_eq = 0, base_gt = 0;
   for (int c0 = 0; c0 < L; c0 += span) {
     if (!resident) load(c0);
     const int j0 = c0 + KPT * tid;
@@ -893,11 +1019,14 @@ __device__ void select_topk(const float* scores, int L, int K, int32_t* out, cha
       n_gt += (ok && key[m] > tau) ? 1u : 0u;
       n_eq += (ok && key[m] == tau) ? 1u : 0u;
     }
-    uint32_t tot_eq, tot_take;
-    const uint32_t eq_before = base_eq + block_exclusive_scan(n_eq, wsum, &tot_eq);
+    // one scan of both counts (each below 2^16 within a chunk)
+    uint32_t tot;
+    const uint32_t pre = block_exclusive_scan(n_gt | (n_eq << 16), wsum, &tot);
+    const uint32_t gt_before = base_gt + (pre & 0xffffu);
+    const uint32_t eq_before = base_eq + (pre >> 16);
     // equal keys are kept in position order until rem of them are taken
     const uint32_t eq_keep = eq_before >= rem ? 0u : min(n_eq, rem - eq_before);
-    uint32_t pos = base_take + block_exclusive_scan(n_gt + eq_keep, wsum, &tot_take);
+    uint32_t pos = gt_before + min(eq_before, rem);
     uint32_t eq_seen = 0;
 #pragma unroll
     for (int m = 0; m < KPT; ++m) {
@@ -909,8 +1038,8 @@ __device__ void select_topk(const float* scores, int L, int K, int32_t* out, cha
       }
       if (take && pos < (uint32_t)K) out[pos++] = j0 + m;
     }
-    base_eq += tot_eq;
-    base_take += tot_take;
+    base_gt += tot & 0xffffu;
+    base_eq += tot >> 16;
   }
 }
 
@@ -1010,7 +1139,7 @@ constexpr int SELECT_THREADS = 1024;
 constexpr int SELECT_KPT = 8;  // keys per thread kept in registers (8192 at 1024 threads)
 
 __global__ void __launch_bounds__(SELECT_THREADS) select_kernel(SelectParams sp) {
-  __shared__ __attribute__((aligned(16))) char smem[(276 + 256 * (SELECT_THREADS / 64)) * 4];
+  __shared__ __attribute__((aligned(16))) char smem[(24 + 16 * 64 + SELECT_FINISH) * 4];
   const PostItem it = sp.items[blockIdx.x];
   select_topk<SELECT_KPT>(sp.pbar + it.pbar_off, it.L, it.K, sp.idx_out + it.idx_off, smem);
 }
