@@ -67,6 +67,7 @@ struct Plan {
   std::vector<uint8_t> xcd;     // XCD queue of (r, g)
   std::vector<int32_t> nchunk;  // split-K chunks of request r
   std::vector<int64_t> part0;   // first split-K partial row of (r, 0); heads follow
+  int max_nchunk = 1;           // most split-K chunks of any merged request
   int qlen[8] = {0};            // items per XCD queue
   int n_items = 0;              // attention records, NOP padding included
   int n_merge = 0, n_avg = 0, n_sel = 0;
@@ -161,6 +162,7 @@ int32_t plan_size(const Shape& s, const std::vector<Req>& rq, bool attn, bool to
       const int nc = std::max(1, (span + chunk - 1) / chunk);
       if (nc > MAX_MERGE_CHUNKS) return fail(SPA_ERR_UNSUPPORTED, "more than 256 split-K chunks per request");
       pl->nchunk[r] = nc;
+      if (nc > 1) pl->max_nchunk = std::max(pl->max_nchunk, nc);
       nitems[r] = nc * ((v && !bf16) ? rows_v : 1);  // fp32 verify: one item per query row
       if (nc > 1) {
         pl->part0[r] = part_rows;
@@ -292,7 +294,8 @@ void plan_write(const Shape& s, const std::vector<Req>& rq, const Plan& pl, char
     for (int x = 0; x < NUM_XCD; ++x)
       for (int i = cur[x]; i < maxlen; ++i) items[(size_t)i * NUM_XCD + x] = nop;
   }
-  // post-pass: averaging chunks of every verify (r, g), then the merges
+  // post-pass: the averaging chunks of every verify (r, g), then the split-K
+  // merges (measured faster than the reverse order)
   PostItem* post = reinterpret_cast<PostItem*>(h + pl.h_post);
   PostItem* sel = reinterpret_cast<PostItem*>(h + pl.h_sel);
   int np = 0, ns = 0;
@@ -520,7 +523,8 @@ int32_t run(const Shape& s, const std::vector<Req>& rq, const Plan& pl, const Bu
     pp.avg_row_count = avg_count;
     {
       ProfScope ps(PROF_POST, st);
-      e = launch_post(pp, s.dtype, s.d, n_post, st);
+      e = launch_post(pp, s.dtype, s.d, n_post,
+                      post_smem_bytes(pl.n_avg ? avg_count * s.G : 0, pl.max_nchunk), st);
     }
     if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("post-pass launch: ") + hipGetErrorString(e));
   }

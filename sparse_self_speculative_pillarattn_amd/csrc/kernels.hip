@@ -1043,16 +1043,16 @@ __device__ void select_topk(const float* scores, int L, int K, int32_t* out, cha
   }
 }
 
+constexpr int POST_THREADS = 256;
+static_assert(AVG_SPAN == 4 * POST_THREADS, "an averaging thread owns four positions");
+
 template <int D, typename T>
-__global__ void __launch_bounds__(256) post_kernel(PostParams p) {
+__global__ void __launch_bounds__(POST_THREADS) post_kernel(PostParams p) {
   // merge: (m, l) pairs then weights of MERGE_ROWS rows; averaging: LSE and
   // logits row offsets of the averaged terms
-  constexpr int SMEM = 2 * MERGE_ROWS * MAX_MERGE_CHUNKS * 4 > MAX_AVG_TERMS * 12
-                           ? 2 * MERGE_ROWS * MAX_MERGE_CHUNKS * 4
-                           : MAX_AVG_TERMS * 12;
-  __shared__ __attribute__((aligned(16))) char smem[SMEM];
-  float* lse2_s = reinterpret_cast<float*>(smem);
-  int64_t* rowoff_s = reinterpret_cast<int64_t*>(smem + MAX_AVG_TERMS * 4);
+  // dynamic LDS (post_smem_bytes): the (m, l) pairs of MERGE_ROWS rows, or the
+  // LSE and logits row offset of every averaged term
+  extern __shared__ __attribute__((aligned(16))) char smem[];
   const PostItem it = p.items[blockIdx.x];
   if (it.kind == POST_NOP) return;
   if (it.kind == POST_MERGE) {
@@ -1060,13 +1060,16 @@ __global__ void __launch_bounds__(256) post_kernel(PostParams p) {
     return;
   }
   // POST_AVG: LSE of the averaged rows (one thread per (row, head)), then
-  // their exact scores averaged over positions [j0, j1)
-  const int tid = threadIdx.x, nthr = blockDim.x;
+  // their exact scores averaged over positions [j0, j1); each thread owns four
+  // consecutive positions (AVG_SPAN = 4 * blockDim.x)
+  const int tid = threadIdx.x;
   const int G = p.G, Hq = p.Hq, a = p.avg_row_begin, n = p.avg_row_count;
   const int terms = n * G;
   const int R = it.rows_q * G;
   const int L = it.L;
-  for (int x = tid; x < terms; x += nthr) {
+  float* lse2_s = reinterpret_cast<float*>(smem);
+  int64_t* rowoff_s = reinterpret_cast<int64_t*>(smem + (terms * 4 + 7) / 8 * 8);
+  for (int x = tid; x < terms; x += blockDim.x) {
     const int i = a + x / G, hh = x % G;
     const int rho = i * G + hh;
     float lse;
@@ -1103,33 +1106,31 @@ __global__ void __launch_bounds__(256) post_kernel(PostParams p) {
   const float* lg = p.logits + it.logits_off;
   float* pbar = p.pbar + it.pbar_off;
   const float inv = 1.f / (float)terms;
-  const bool vec = ((it.logits_off | (int64_t)L) & 3) == 0;
-  for (int j4 = it.j0 + 4 * tid; j4 < it.j1; j4 += 4 * nthr) {
+  const int j4 = it.j0 + 4 * tid;
+  if (j4 >= it.j1) return;
+  if (((it.logits_off | (int64_t)L) & 3) == 0 && j4 + 4 <= it.j1) {
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    if (vec && j4 + 4 <= it.j1) {
 #pragma unroll 16
-      for (int x = 0; x < terms; ++x) {
-        const float4 v = *reinterpret_cast<const float4*>(lg + rowoff_s[x] + j4);
-        const float l2 = lse2_s[x];
-        const float vv[4] = {v.x, v.y, v.z, v.w};
+    for (int x = 0; x < terms; ++x) {
+      const float4 v = *reinterpret_cast<const float4*>(lg + rowoff_s[x] + j4);
+      const float l2 = lse2_s[x];
+      const float vv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          acc[e] += (vv[e] == NEG_INF || l2 == NEG_INF) ? 0.f : fast_exp2(fmaf(vv[e], LOG2E, -l2));
+      for (int e = 0; e < 4; ++e)
+        acc[e] += (vv[e] == NEG_INF || l2 == NEG_INF) ? 0.f : fast_exp2(fmaf(vv[e], LOG2E, -l2));
+    }
+    *reinterpret_cast<float4*>(pbar + j4) =
+        make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+  } else {
+    for (int e = 0; e < 4 && j4 + e < it.j1; ++e) {
+      const int j = j4 + e;
+      float sacc = 0.f;
+      for (int x = 0; x < terms; ++x) {
+        const float v = lg[rowoff_s[x] + j];
+        const float l2 = lse2_s[x];
+        sacc += (v == NEG_INF || l2 == NEG_INF) ? 0.f : fast_exp2(fmaf(v, LOG2E, -l2));
       }
-      *reinterpret_cast<float4*>(pbar + j4) =
-          make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
-    } else {
-      for (int e = 0; e < 4; ++e) {
-        const int j = j4 + e;
-        if (j >= it.j1) break;
-        float s = 0.f;
-        for (int x = 0; x < terms; ++x) {
-          const float v = lg[rowoff_s[x] + j];
-          const float l2 = lse2_s[x];
-          s += (v == NEG_INF || l2 == NEG_INF) ? 0.f : fast_exp2(fmaf(v, LOG2E, -l2));
-        }
-        pbar[j] = s * inv;
-      }
+      pbar[j] = sacc * inv;
     }
   }
 }
@@ -1201,18 +1202,25 @@ hipError_t launch_select(const SelectParams& sp, int nitems, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_post(const PostParams& p, int dtype, int head_dim, int nitems, hipStream_t st) {
+size_t post_smem_bytes(int avg_terms, int max_nchunk) {
+  const size_t avg = (size_t)(avg_terms * 4 + 7) / 8 * 8 + (size_t)avg_terms * 8;
+  const size_t merge = (size_t)2 * MERGE_ROWS * max_nchunk * 4;
+  return std::max<size_t>(16, std::max(avg, merge));
+}
+
+hipError_t launch_post(const PostParams& p, int dtype, int head_dim, int nitems, size_t smem,
+                       hipStream_t st) {
   if (nitems == 0) return hipSuccess;
   if (dtype == 0) {
     if (head_dim == 128)
-      hipLaunchKernelGGL((post_kernel<128, uint16_t>), dim3(nitems), dim3(256), 0, st, p);
+      hipLaunchKernelGGL((post_kernel<128, uint16_t>), dim3(nitems), dim3(POST_THREADS), smem, st, p);
     else
-      hipLaunchKernelGGL((post_kernel<64, uint16_t>), dim3(nitems), dim3(256), 0, st, p);
+      hipLaunchKernelGGL((post_kernel<64, uint16_t>), dim3(nitems), dim3(POST_THREADS), smem, st, p);
   } else {
     if (head_dim == 128)
-      hipLaunchKernelGGL((post_kernel<128, float>), dim3(nitems), dim3(256), 0, st, p);
+      hipLaunchKernelGGL((post_kernel<128, float>), dim3(nitems), dim3(POST_THREADS), smem, st, p);
     else
-      hipLaunchKernelGGL((post_kernel<64, float>), dim3(nitems), dim3(256), 0, st, p);
+      hipLaunchKernelGGL((post_kernel<64, float>), dim3(nitems), dim3(POST_THREADS), smem, st, p);
   }
   return hipGetLastError();
 }

@@ -46,11 +46,12 @@ struct SelectParams {
 // LDS bytes the attention kernel needs for a launch shape.
 size_t attn_smem_bytes(int dtype, int head_dim, int G, int nthr, bool mfma, bool valu,
                        int max_chunk);
-size_t post_smem_bytes();
+size_t post_smem_bytes(int avg_terms, int max_nchunk);
 
 hipError_t launch_attn(const AttnParams& p, int dtype, int head_dim, int nitems, int nthr,
                        size_t smem, hipStream_t st);
-hipError_t launch_post(const PostParams& p, int dtype, int head_dim, int nitems, hipStream_t st);
+hipError_t launch_post(const PostParams& p, int dtype, int head_dim, int nitems, size_t smem,
+                       hipStream_t st);
 hipError_t launch_select(const SelectParams& sp, int nitems, hipStream_t st);
 
 }  // namespace spa
