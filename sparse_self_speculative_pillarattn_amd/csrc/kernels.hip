@@ -127,9 +127,13 @@ constexpr int DMA_TT = 32;     // tokens per stage
 constexpr int DMA_STAGES = 4;  // LDS stages; DMA_STAGES - 1 tiles in flight
 
 template <int D>
-constexpr size_t dma_smem_bytes() {  // the stage ring; the chunk's slots follow it
+constexpr size_t dma_smem_bytes() {  // the stage ring; logits staging and slots follow it
   return (size_t)DMA_STAGES * 2 * DMA_TT * D * 2;
 }
+// Logits staging of one consumer wave: 16 rows of a tile, padded so that the
+// column-major writes and the row-major reads are both free of bank conflicts.
+constexpr int LSTG = DMA_TT + 4;  // floats per staged row
+constexpr size_t logit_stage_bytes(int consumer_waves) { return (size_t)consumer_waves * 16 * LSTG * 4; }
 
 // LDS chunk swizzles of a stage.  K: the 16 consecutive rows one MFMA operand
 // read touches land on distinct bank groups.  V: the eight rows (two 16-byte
@@ -160,21 +164,32 @@ __device__ __forceinline__ void load_lds16(const void* src, char* dst) {
   __builtin_amdgcn_global_load_lds(src, (lds_void*)dst, 16, 0, 0);
 }
 
+// Slots of one tile as the producer's lanes use them: lane l loads rows
+// RPI j + l / NCH of the tile.
 template <int D>
-__device__ __forceinline__ void issue_kv_tile(char* stage, const int32_t* slots, const uint16_t* kp,
+struct TileSlots {
+  int v[DMA_TT * (D / 8) / 64];
+};
+
+template <int D>
+__device__ __forceinline__ void read_tile_slots(TileSlots<D>& s, const int32_t* slots, int lane) {
+  constexpr int RPI = 64 / (D / 8);
+#pragma unroll
+  for (int j = 0; j < DMA_TT / RPI; ++j) s.v[j] = slots[RPI * j + lane / (D / 8)];
+}
+
+template <int D>
+__device__ __forceinline__ void issue_kv_tile(char* stage, const TileSlots<D>& s, const uint16_t* kp,
                                               const uint16_t* vp, int64_t rs, int lane) {
   constexpr int NCH = D / 8;         // 16-byte chunks per row
   constexpr int RPI = 64 / NCH;      // rows per load instruction
   constexpr int NI = DMA_TT / RPI;   // load instructions per tensor and tile
   constexpr int STAGE = DMA_TT * D * 2;
   const int sub = lane / NCH, pc = lane % NCH;
-  int sl[NI];  // all slot reads first: a later LDS read may not pass an LDS-writing load
-#pragma unroll
-  for (int j = 0; j < NI; ++j) sl[j] = slots[RPI * j + sub];
 #pragma unroll
   for (int j = 0; j < NI; ++j) {
     const int tau = RPI * j + sub;
-    const int64_t row = (int64_t)max(sl[j], 0) * rs;  // a masked entry reads row 0
+    const int64_t row = (int64_t)max(s.v[j], 0) * rs;  // a masked entry reads row 0
     load_lds16(kp + row + 8 * (pc ^ kswz_t<NCH>(tau)), stage + 1024 * j);
     load_lds16(vp + row + 8 * (pc ^ vswz<NCH>(tau)), stage + STAGE + 1024 * j);
   }
@@ -211,19 +226,28 @@ __device__ void dma_producer(const AttnParams& p, const Item& it, char* smem,
   const uint16_t* kp = reinterpret_cast<const uint16_t*>(p.k_pool) + it.g * D;
   const uint16_t* vp = reinterpret_cast<const uint16_t*>(p.v_pool) + it.g * D;
   const int64_t rs = (int64_t)p.Hkv * D;
-  for (int i = 0; i < min(n, DMA_STAGES - 1); ++i)
-    issue_kv_tile<D>(smem + i * STAGE2, slots + i * DMA_TT, kp, vp, rs, lane);
+  // The slots of the next tile are read from LDS right after a tile is issued,
+  // so that their latency (LDS is busy with the consumers' operand reads)
+  // passes while the producer waits, not on the issue path.
+  TileSlots<D> ts;
+  read_tile_slots<D>(ts, slots, lane);
+  for (int i = 0; i < min(n, DMA_STAGES - 1); ++i) {
+    issue_kv_tile<D>(smem + i * STAGE2, ts, kp, vp, rs, lane);
+    if (i + 1 < n) read_tile_slots<D>(ts, slots + (i + 1) * DMA_TT, lane);
+  }
   producer_barrier<PER_TILE>(min(n, DMA_STAGES - 1) - 1);  // tile 0 ready
   for (int i = 0; i + 1 < n; ++i) {
     const int t = i + DMA_STAGES - 1;  // into the stage tile i-1 used
-    if (t < n)
-      issue_kv_tile<D>(smem + (t % DMA_STAGES) * STAGE2, slots + t * DMA_TT, kp, vp, rs, lane);
+    if (t < n) {
+      issue_kv_tile<D>(smem + (t % DMA_STAGES) * STAGE2, ts, kp, vp, rs, lane);
+      if (t + 1 < n) read_tile_slots<D>(ts, slots + (t + 1) * DMA_TT, lane);
+    }
     producer_barrier<PER_TILE>(min(n - 1, t) - (i + 1));  // tile i+1 ready
   }
 }
 
 template <int D>
-__device__ void dma_consumer(const AttnParams& p, const Item& it, const char* smem,
+__device__ void dma_consumer(const AttnParams& p, const Item& it, char* smem,
                              const int32_t* slots, bool is_list, int wave, int lane) {
   constexpr int NCH = D / 8;   // 16-byte chunks per K/V row
   constexpr int KS = D / 32;   // k-steps of S^T = K Q^T
@@ -263,6 +287,17 @@ __device__ void dma_consumer(const AttnParams& p, const Item& it, const char* sm
   float* lrow = is_list ? nullptr : p.logits + it.off + ((int64_t)qi * Hq + h) * L;
   const float sc = p.sm_scale;
   const bool rows_aligned = ((it.off | (int64_t)L) & 3) == 0;  // every logits row 16-byte aligned
+  // Full aligned tiles go out through this wave's LDS staging: 8 lanes then
+  // write 128 contiguous bytes of one row (rows rA and rA + 8 of the wave).
+  float* stg = reinterpret_cast<float*>(smem + dma_smem_bytes<D>()) + wave * 16 * LSTG;
+  const int rA = lane >> 3, cA = 4 * (lane & 7);
+  float* lA = nullptr;
+  float* lB = nullptr;
+  if (!is_list) {
+    const int rho_a = wave * 16 + rA, rho_b = rho_a + 8;
+    if (rho_a < R) lA = p.logits + it.off + ((int64_t)(rho_a / G) * Hq + it.g * G + rho_a % G) * L;
+    if (rho_b < R) lB = p.logits + it.off + ((int64_t)(rho_b / G) * Hq + it.g * G + rho_b % G) * L;
+  }
 
   // Transpose-read source rows of this lane: tokens 4 q + n / 4 and 16 more.
   // The lane supplies dims 4 (n % 4) .. + 3 of its 16-dim block.
@@ -305,11 +340,17 @@ __device__ void dma_consumer(const AttnParams& p, const Item& it, const char* sm
           v[t][e] = sacc[t][e] * sc;
           mx = fmaxf(mx, v[t][e]);
         }
-      if (row_ok && rows_aligned) {
+      if (rows_aligned) {
+        // lane (n, q) holds row n's tokens 16 t + 4 q .. + 3; a wave's LDS
+        // accesses complete in order, so the read-back needs no barrier
 #pragma unroll
         for (int t = 0; t < 2; ++t)
-          *reinterpret_cast<float4*>(lrow + t0 + 16 * t + 4 * q4) =
+          *reinterpret_cast<float4*>(stg + n * LSTG + 16 * t + 4 * q4) =
               make_float4(v[t][0], v[t][1], v[t][2], v[t][3]);
+        const float4 va = *reinterpret_cast<const float4*>(stg + rA * LSTG + cA);
+        const float4 vb = *reinterpret_cast<const float4*>(stg + (rA + 8) * LSTG + cA);
+        if (lA) *reinterpret_cast<float4*>(lA + t0 + cA) = va;
+        if (lB) *reinterpret_cast<float4*>(lB + t0 + cA) = vb;
       } else if (row_ok) {
 #pragma unroll
         for (int t = 0; t < 2; ++t)
@@ -435,7 +476,8 @@ template <int D>
 __device__ void attn_tile_dma(const AttnParams& p, const Item& it, char* smem, bool is_list) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // slots of the chunk, padded to whole tiles; -1 marks a masked entry
-  int32_t* slots = reinterpret_cast<int32_t*>(smem + dma_smem_bytes<D>());
+  int32_t* slots = reinterpret_cast<int32_t*>(smem + dma_smem_bytes<D>() +
+                                              logit_stage_bytes((int)(blockDim.x >> 6) - 1));
   const int jb = it.begin, je = it.end;
   const int padded = (je - jb + DMA_TT - 1) / DMA_TT * DMA_TT;
   const int32_t* pt = p.page_table + (int64_t)it.r * p.pt_stride;
@@ -1153,8 +1195,9 @@ static int group_template(int G) { return G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 :
 size_t attn_smem_bytes(int dtype, int head_dim, int G, int nthr, bool mfma, bool valu,
                        int max_chunk) {
   size_t s = 16;
-  if (mfma)  // stage ring, then the slots of the longest chunk padded to whole tiles
+  if (mfma)  // stage ring, logits staging, the slots of the longest chunk padded to whole tiles
     s = std::max(s, (head_dim == 128 ? dma_smem_bytes<128>() : dma_smem_bytes<64>()) +
+                        logit_stage_bytes(nthr / 64 - 1) +
                         (size_t)(max_chunk + DMA_TT - 1) / DMA_TT * DMA_TT * 4);
   if (valu) {
     const int GM = group_template(G);
