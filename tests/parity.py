@@ -115,3 +115,74 @@ def compare_step(orc, b, gpu, ref, avg_row_begin=1, avg_row_count=None, check_lo
         for g in range(w.num_kv_heads):
             sel = idx[b.idx_off[r] + g * K: b.idx_off[r] + (g + 1) * K]
             assert_topk(sel, pbar[g], K, f"top-K req {r} head {g}")
+
+
+def request_inputs(b, r):
+    """Host copies of what request r reads: its q rows and the K/V pool rows of
+    its L positions, re-laid-out in position order (so its page table becomes
+    0..L-1; results do not depend on where a slot lives)."""
+    L = b.seq_lens[r]
+    slots = b.page_table[r, :L].long()
+    kp = to_np(b.k_pool.index_select(0, slots))
+    vp = to_np(b.v_pool.index_select(0, slots))
+    rows = slice(b.q_indptr[r], b.q_indptr[r + 1])
+    return to_np(b.q[rows]), kp, vp, np.arange(L, dtype=np.int32)
+
+
+def compare_sampled(orc, b, gpu, verify_reqs, draft_reqs):
+    """Full-size check of chosen requests against the oracle, one request at a
+    time: verify O, LSE, every dumped logit and the per-KV-head top-K; draft O
+    and LSE.  gpu: dict of tensors (o, lse, logits, idx) after the step."""
+    w = b.w
+    k, Hq, Hkv, d = w.spec_k, w.num_qo_heads, w.num_kv_heads, w.head_dim
+    sm = 1.0 / np.sqrt(d)
+    for r in verify_reqs:
+        assert b.is_verify[r]
+        L = b.seq_lens[r]
+        q, kp, vp, ptr = request_inputs(b, r)
+        lg, lse, o = orc.verify_request(q, kp, vp, ptr, L, k, Hq, Hkv, sm)
+        rows = slice(b.q_indptr[r], b.q_indptr[r + 1])
+        assert_o(to_np(gpu["o"][rows]), o, w.dtype, f"O req {r}")
+        assert_lse_like(to_np(gpu["lse"][rows]), lse, f"LSE req {r}")
+        off, n = b.logits_off[r], (k + 1) * Hq * L
+        assert_lse_like(to_np(gpu["logits"][off:off + n]), lg.reshape(-1), f"logits req {r}")
+        pbar = orc.average(lg, lse, Hkv, 1, k)
+        K = b.idx_count[r]
+        idx = to_np(gpu["idx"][b.idx_off[r]:b.idx_off[r] + Hkv * K]).reshape(Hkv, K)
+        for g in range(Hkv):
+            assert_topk(idx[g], pbar[g], K, f"top-K req {r} head {g}")
+    for r in draft_reqs:
+        assert not b.is_verify[r]
+        L, K = b.seq_lens[r], b.idx_count[r]
+        q, kp, vp, ptr = request_inputs(b, r)
+        lst = to_np(b.idx[b.idx_off[r]:b.idx_off[r] + Hkv * K]).reshape(Hkv, K)
+        o, lse = orc.draft_request(q[0], kp, vp, ptr, L, lst, Hkv, sm)
+        row = b.q_indptr[r]
+        assert_o(to_np(gpu["o"][row]), o, w.dtype, f"O draft {r}")
+        assert_lse_like(to_np(gpu["lse"][row]), lse, f"LSE draft {r}")
+
+
+def check_whole_batch_properties(b, gpu):
+    """Properties that hold at any size, for every request: finite LSE and O,
+    each verify row's causally hidden logits exactly -inf, and every top-K list
+    K distinct in-range positions, ascending."""
+    w = b.w
+    k, Hq, Hkv = w.spec_k, w.num_qo_heads, w.num_kv_heads
+    lse = to_np(gpu["lse"])
+    assert np.isfinite(lse).all(), "non-finite LSE"
+    o = gpu["o"].float()
+    assert bool(torch.isfinite(o).all()), "non-finite O"
+    idx = to_np(gpu["idx"])
+    logits = gpu["logits"]
+    for r in range(b.B):
+        if not b.is_verify[r]:
+            continue
+        L, K = b.seq_lens[r], b.idx_count[r]
+        lst = idx[b.idx_off[r]:b.idx_off[r] + Hkv * K].reshape(Hkv, K)
+        assert (np.diff(lst, axis=1) > 0).all(), f"top-K req {r} not strictly ascending"
+        assert lst.min() >= 0 and lst.max() < L, f"top-K req {r} out of range"
+        lg = logits[b.logits_off[r]:b.logits_off[r] + (k + 1) * Hq * L].view(k + 1, Hq, L)
+        for i in range(k):  # row i hides the last k - i positions
+            tail = lg[i, :, L - k + i:]
+            assert bool(torch.isneginf(tail).all()), f"req {r} row {i}: hidden logits not -inf"
+            assert bool(torch.isfinite(lg[i, :, :L - k + i]).all()), f"req {r} row {i}: non-finite logits"

@@ -269,3 +269,30 @@ def test_workspace_reuse_across_batches(oracle):
         ref = oracle.step(**parity.oracle_inputs(b))
         parity.compare_step(oracle, b, {"o": bufs.o, "lse": bufs.lse, "logits": bufs.logits,
                                         "idx": bufs.idx}, ref)
+
+
+FULL = [synth.QWEN3_1_7B.name, synth.QWEN3_8B.name, synth.QWEN3_14B.name, synth.LONG_CTX.name]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled(oracle, name):
+    """Each workload at its full size, in the configuration the benchmark times
+    (one unified step, default work split): sampled requests against the oracle
+    one by one (shortest and longest verify request, three drafts), plus
+    size-independent properties over the whole batch."""
+    w = synth.WORKLOADS[name]
+    print(f"[full-size] {name}", flush=True)
+    b = synth.make_batch(w, device=DEV)
+    bufs = bd.StepBuffers(b)
+    bufs.step()
+    torch.cuda.synchronize()
+    gpu = {"o": bufs.o, "lse": bufs.lse, "logits": bufs.logits, "idx": bufs.idx}
+    ver = [r for r in range(b.B) if b.is_verify[r]]
+    dra = [r for r in range(b.B) if not b.is_verify[r]]
+    ver_by_len = sorted(ver, key=lambda r: b.seq_lens[r])
+    vsample = [ver_by_len[0]] if b.seq_lens[ver_by_len[-1]] > 40000 else sorted({ver_by_len[0], ver_by_len[-1]})
+    dsample = sorted({dra[0], dra[len(dra) // 2], dra[-1]})
+    parity.check_whole_batch_properties(b, gpu)
+    parity.compare_sampled(oracle, b, gpu, vsample, dsample)
+    del bufs, gpu, b
+    torch.cuda.empty_cache()
