@@ -165,6 +165,102 @@ def cpu_baseline(b, repeats: int) -> dict:
 
 
 # --------------------------------------------------------------------------- #
+# extra measurements (not part of the one-line result)
+# --------------------------------------------------------------------------- #
+def _time_steps(fn, steps: int, warmup: int) -> float:
+    """Mean microseconds per call of ``fn`` over ``steps`` back-to-back calls."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps * 1e3
+
+
+def sparsity_sweep(w, dev, steps: int, warmup: int):
+    """Draft-only batches (every request a draft, the workload's shapes) at a
+    range of sparsities: per-step time should fall close to proportionally to s."""
+    from dataclasses import replace
+    from fractions import Fraction
+    L = w.lengths[1] if w.lengths[0] == "fixed" else 8192
+    rows = []
+    for s in (Fraction(1, 100), Fraction(1, 50), Fraction(1, 20), Fraction(1, 10), Fraction(1, 5),
+              Fraction(1, 2), Fraction(1, 1)):
+        ws = replace(w, sparsity=s, name=f"{w.name}-draft-only-s{float(s)}")
+        b = synth.uniform_batch(ws, w.batch, L, [0] * w.batch, device=dev, seed=w.seed)
+        bufs = bd.StepBuffers(b)
+        us = _time_steps(bufs.step, steps, warmup)
+        bd.profile_reset()
+        bd.profile_enable((1 << len(bd.PROF_NAMES)) - 1)
+        for _ in range(5):
+            bufs.step()
+        torch.cuda.synchronize()
+        bd.profile_enable(0)
+        kern = {}
+        for i, nm in enumerate(bd.PROF_NAMES):
+            n, ms = bd.profile_read(i)
+            if n:
+                kern[nm] = round(ms / n * 1e3, 1)
+        alg = algorithmic_bytes(b)
+        rows.append({"s": float(s), "K": b.idx_count[0], "us_per_step": round(us, 1), "kernel_us": kern,
+                     "bytes_min": alg["bytes_min"],
+                     "hbm_gbps_min": round(alg["bytes_min"] / (us * 1e-6) / 1e9, 1)})
+        del bufs, b
+        torch.cuda.empty_cache()
+    t1 = rows[-1]["us_per_step"]
+    for r in rows:
+        r["t_over_t1"] = round(r["us_per_step"] / t1, 4)
+    print(json.dumps({"sparsity_sweep": w.name, "batch": w.batch, "L": L, "rows": rows}))
+
+
+def unified_vs_sequential(w, dev, steps: int, warmup: int):
+    """The unified step against the three entry points called one after the
+    other on the same batch (verify attention, PillarAttn top-K, draft attention)."""
+    b = synth.make_batch(w, device=dev)
+    bufs = bd.StepBuffers(b)
+    k, Hq, Hkv, d = w.spec_k, w.num_qo_heads, w.num_kv_heads, w.head_dim
+    lay = bufs.lay
+    ver = [r for r in range(b.B) if b.is_verify[r]]
+    dra = [r for r in range(b.B) if not b.is_verify[r]]
+    qv = torch.cat([b.q[b.q_indptr[r]:b.q_indptr[r + 1]] for r in ver]).contiguous()
+    ptv = torch.stack([b.page_table[r] for r in ver]).contiguous()
+    lv = [b.seq_lens[r] for r in ver]
+    loff = np.concatenate([[0], np.cumsum([(k + 1) * Hq * L for L in lv])[:-1]]).astype(np.int64)
+    ov = torch.empty_like(qv)
+    lsev = torch.empty((qv.shape[0], Hq), device=dev)
+    lgv = torch.empty((int(sum((k + 1) * Hq * L for L in lv)),), device=dev)
+    Kv = [b.idx_count[r] for r in ver]
+    ioff = np.concatenate([[0], np.cumsum([Hkv * K for K in Kv])[:-1]]).astype(np.int64)
+    idxv = torch.zeros((int(sum(Hkv * K for K in Kv)),), dtype=torch.int32, device=dev)
+    qd = torch.stack([b.q[b.q_indptr[r]] for r in dra]).contiguous()
+    ptd = torch.stack([b.page_table[r] for r in dra]).contiguous()
+    ld = [b.seq_lens[r] for r in dra]
+    Kd = [b.idx_count[r] for r in dra]
+    doff = np.concatenate([[0], np.cumsum([Hkv * K for K in Kd])[:-1]]).astype(np.int64)
+    idxd = torch.cat([b.idx[b.idx_off[r]:b.idx_off[r] + Hkv * b.idx_count[r]] for r in dra])
+    od = torch.empty_like(qd)
+    lsed = torch.empty((len(dra), Hq), device=dev)
+    ws = bd.workspace(max(bd.workspace_bytes(lay, len(ver), k, [1] * len(ver), lv, Kv),
+                          bd.workspace_bytes(lay, len(dra), 1, None, ld, Kd)), dev)
+
+    def sequential():
+        bd.verify_attn(lay, len(ver), k, lv, ptv, qv, b.k_pool, b.v_pool, ov, lsev, lgv, loff, ws)
+        bd.pillar_topk(len(ver), k, Hq, Hkv, 1, k, lv, Kv, lgv, loff, lsev, idxv, ioff, ws)
+        bd.draft_attn(lay, len(dra), ld, ptd, Kd, doff, idxd.contiguous(), qd, b.k_pool, b.v_pool,
+                      od, lsed, ws)
+
+    uni = _time_steps(bufs.step, steps, warmup)
+    seq = _time_steps(sequential, steps, warmup)
+    print(json.dumps({"unified_vs_sequential": w.name, "unified_us": round(uni, 1),
+                      "sequential_us": round(seq, 1), "speedup": round(seq / uni, 3)}))
+
+
+# --------------------------------------------------------------------------- #
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -176,6 +272,10 @@ def main():
     ap.add_argument("--cpu-repeats", type=int, default=15,
                     help="oracle runs of the whole step (about 0.8 s each on 16 EPYC cores)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sparsity-sweep", action="store_true",
+                    help="only run the draft-only sparsity sweep and print its JSON line")
+    ap.add_argument("--unified-vs-sequential", action="store_true",
+                    help="only compare the unified step with the three entry points in sequence")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 5 plain device copies of MIB MiB (reference for the HBM "
                          "byte counters) and exit")
@@ -202,6 +302,12 @@ def main():
         return
     bd.load()  # fails loudly when libspa.so is missing
     w = synth.WORKLOADS[args.workload]
+    if args.sparsity_sweep:
+        sparsity_sweep(w, dev, args.steps, args.warmup)
+        return
+    if args.unified_vs_sequential:
+        unified_vs_sequential(w, dev, args.steps, args.warmup)
+        return
     print(f"[bench] generating {w.name} on {dev}", file=sys.stderr, flush=True)
     b = synth.make_batch(w, device=dev)
     bufs = bd.StepBuffers(b)

@@ -407,23 +407,63 @@ struct ProfScope {
 };
 
 // ---- pinned plan ring ----------------------------------------------------------
-// A slot holds one call's plan until the call's last kernel has finished; a
-// slot is reused only after the event recorded behind that kernel completes.
+// RING slots carved from one pinned, device-mapped arena.  A slot holds one
+// call's plan until the call's last kernel has finished; it is reused only
+// after the event recorded behind that kernel completes.  When a plan outgrows
+// the slots, every pending slot is waited for and the arena is reallocated
+// once for all of them, so pinned allocation happens only when plans grow.
 struct PlanSlot {
-  void* host = nullptr;
-  void* dev = nullptr;
-  size_t cap = 0;
+  char* host = nullptr;
+  char* dev = nullptr;
   hipEvent_t ev = nullptr;
   bool pending = false;
 };
-constexpr int RING = 64;
+constexpr int RING = 16;
 std::mutex g_ring_mu;
 PlanSlot g_ring[RING];
+char* g_arena_host = nullptr;
+char* g_arena_dev = nullptr;
+size_t g_slot_cap = 0;
 unsigned g_ring_next = 0;
 
-int32_t acquire_slot(const Plan& pl, PlanSlot** out) {
-  PlanSlot& s = g_ring[g_ring_next++ % RING];
+int32_t grow_arena(size_t need) {
   hipError_t e;
+  for (auto& s : g_ring)
+    if (s.pending) {
+      e = hipEventSynchronize(s.ev);
+      if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("plan slot wait: ") + hipGetErrorString(e));
+      s.pending = false;
+    }
+  if (g_arena_host) (void)hipHostFree(g_arena_host);
+  g_arena_host = g_arena_dev = nullptr;
+  g_slot_cap = 0;
+  const size_t cap = align_up(std::max<size_t>(need * 2, 256 << 10), 4096);
+  void* h = nullptr;
+  e = hipHostMalloc(&h, cap * RING, hipHostMallocMapped | hipHostMallocPortable);
+  if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("pinned plan: ") + hipGetErrorString(e));
+  void* d = nullptr;
+  e = hipHostGetDevicePointer(&d, h, 0);
+  if (e != hipSuccess) {
+    (void)hipHostFree(h);
+    return fail(SPA_ERR_HIP, std::string("pinned plan mapping: ") + hipGetErrorString(e));
+  }
+  g_arena_host = static_cast<char*>(h);
+  g_arena_dev = static_cast<char*>(d);
+  g_slot_cap = cap;
+  for (int i = 0; i < RING; ++i) {
+    g_ring[i].host = g_arena_host + (size_t)i * cap;
+    g_ring[i].dev = g_arena_dev + (size_t)i * cap;
+  }
+  return SPA_OK;
+}
+
+int32_t acquire_slot(const Plan& pl, PlanSlot** out) {
+  hipError_t e;
+  if (g_slot_cap < pl.h_bytes) {
+    const int32_t rc = grow_arena(pl.h_bytes);
+    if (rc) return rc;
+  }
+  PlanSlot& s = g_ring[g_ring_next++ % RING];
   if (s.pending) {
     e = hipEventSynchronize(s.ev);
     if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("plan slot wait: ") + hipGetErrorString(e));
@@ -432,21 +472,6 @@ int32_t acquire_slot(const Plan& pl, PlanSlot** out) {
   if (!s.ev) {
     e = hipEventCreateWithFlags(&s.ev, hipEventDisableTiming);
     if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("event create: ") + hipGetErrorString(e));
-  }
-  if (s.cap < pl.h_bytes) {
-    if (s.host) (void)hipHostFree(s.host);
-    s.host = s.dev = nullptr;
-    s.cap = 0;
-    const size_t want = std::max<size_t>(pl.h_bytes * 2, 1 << 16);
-    e = hipHostMalloc(&s.host, want, hipHostMallocMapped | hipHostMallocPortable);
-    if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("pinned plan: ") + hipGetErrorString(e));
-    e = hipHostGetDevicePointer(&s.dev, s.host, 0);
-    if (e != hipSuccess) {
-      (void)hipHostFree(s.host);
-      s.host = nullptr;
-      return fail(SPA_ERR_HIP, std::string("pinned plan mapping: ") + hipGetErrorString(e));
-    }
-    s.cap = want;
   }
   *out = &s;
   return SPA_OK;
