@@ -150,6 +150,16 @@ int32_t spa_unified_step(const spa_layout* layout, int32_t B, int32_t spec_k,
                          int32_t avg_row_begin, int32_t avg_row_count, void* d_ws,
                          size_t ws_bytes, void* stream);
 
+/* Process-wide switch for spa_unified_step on a batch holding both verify
+ * and draft requests (default 0): 1 runs its draft attention as a second
+ * launch on a library-owned stream (default priority, one per device) that is
+ * forked from `stream` after the work already queued there and joined back
+ * before the call's last operation, so the call as a whole stays ordered on
+ * `stream` while the verify attention, score averaging and top-K overlap the
+ * draft attention; 0 runs all attention items in one launch.  Results do not
+ * depend on it.  Returns SPA_OK. */
+int32_t spa_set_overlap(int32_t enable);
+
 /* Process-wide split-K chunk sizes (tokens per verify work item, list entries
  * per draft work item); 0 restores the automatic choice.  Results do not
  * depend on them beyond floating-point summation order. */
@@ -157,9 +167,12 @@ int32_t spa_set_split(int32_t verify_chunk_tokens, int32_t draft_chunk_entries);
 
 /* Per-launch timing.  With a nonzero kernel mask, every later launch of a
  * selected kernel is bracketed by a pair of HIP events recorded on the launch
- * stream (bit 0: the attention launch; bit 1: the post-pass launch holding the
- * split-K merges and score averaging; bit 2: the top-K selection launch); 0
- * turns it off.
+ * stream (bit 0: the attention launch, or with overlap the verify attention
+ * launch; bit 1: the post-pass launch holding the split-K merges and score
+ * averaging; bit 2: the top-K selection launch; bit 3: the draft attention
+ * launch of an overlapped unified step; bit 4: all attention of a call, from
+ * the start of its first attention launch to the end of its last, over both
+ * streams when overlapped); 0 turns it off.
  * Returns SPA_OK. */
 int32_t spa_profile_enable(int32_t kernel_mask);
 

@@ -27,12 +27,12 @@ SPA_BF16 = 0
 SPA_F32 = 1
 
 EXPORTED = ("spa_abi_version", "spa_last_error", "spa_workspace_bytes", "spa_verify_attn",
-            "spa_pillar_topk", "spa_draft_attn", "spa_unified_step", "spa_set_split",
+            "spa_pillar_topk", "spa_draft_attn", "spa_unified_step", "spa_set_split", "spa_set_overlap",
             "spa_profile_enable", "spa_profile_read", "spa_profile_reset")
 
 # kernel indices of the per-launch timer
-PROF_ATTN, PROF_POST, PROF_SELECT = range(3)
-PROF_NAMES = ("attn", "post", "select")
+PROF_ATTN, PROF_POST, PROF_SELECT, PROF_ATTN_DRAFT, PROF_ATTN_SPAN = range(5)
+PROF_NAMES = ("attn", "post", "select", "attn_draft", "attn_span")
 
 
 class SpaError(RuntimeError):
@@ -65,6 +65,8 @@ def load(path: str = LIB_PATH):
     lib.spa_last_error.restype = C.c_char_p
     lib.spa_set_split.argtypes = [i32, i32]
     lib.spa_set_split.restype = i32
+    lib.spa_set_overlap.argtypes = [i32]
+    lib.spa_set_overlap.restype = i32
     lib.spa_workspace_bytes.argtypes = [L, i32, i32, vp, vp, vp]
     lib.spa_workspace_bytes.restype = sz
     lib.spa_verify_attn.argtypes = [L, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -133,6 +135,11 @@ def layout(num_qo_heads: int, num_kv_heads: int, head_dim: int, dtype: torch.dty
 
 def abi_version() -> int:
     return load().spa_abi_version()
+
+
+def set_overlap(enable: bool):
+    """Run the draft attention of a mixed unified step on a side stream (default off)."""
+    _check(load().spa_set_overlap(1 if enable else 0))
 
 
 def set_split(verify_chunk_tokens: int = 0, draft_chunk_entries: int = 0):

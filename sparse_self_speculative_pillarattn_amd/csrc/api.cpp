@@ -30,6 +30,7 @@ namespace {
 thread_local std::string g_err;
 std::atomic<int32_t> g_verify_chunk{0};
 std::atomic<int32_t> g_draft_chunk{0};
+std::atomic<int32_t> g_overlap{0};
 
 constexpr int DEFAULT_VERIFY_CHUNK = 2048;  // fewer split-K partials; drafts fill the XCD queues
 constexpr int DEFAULT_DRAFT_CHUNK = 1024;
@@ -70,11 +71,18 @@ struct Plan {
   int max_nchunk = 1;           // most split-K chunks of any merged request
   int qlen[8] = {0};            // items per XCD queue
   int n_items = 0;              // attention records, NOP padding included
+  // split: a mixed batch runs its draft items in a second attention launch on
+  // a side stream, concurrently with verify attention, merge, averaging and
+  // top-K on the caller's stream
+  bool split = false;
+  int qlen_d[8] = {0};
+  int n_items_d = 0;            // draft launch records, NOP padding included
+  int n_merge_d = 0;            // draft merges, run after the join
   int n_merge = 0, n_avg = 0, n_sel = 0;
   int64_t part_rows = 0;
   int64_t pbar_elems = 0;
   // pinned plan layout
-  size_t h_items = 0, h_post = 0, h_sel = 0, h_bytes = 0;
+  size_t h_items = 0, h_items_d = 0, h_post = 0, h_post_d = 0, h_sel = 0, h_bytes = 0;
   // workspace layout
   size_t off_part_o = 0, off_part_ml = 0, off_pbar = 0, total = 0;
   int nthr = 256;
@@ -147,6 +155,7 @@ int32_t plan_size(const Shape& s, const std::vector<Req>& rq, bool attn, bool to
 
   bool any_verify = false, any_draft = false;
   for (auto& q : rq) (q.verify ? any_verify : any_draft) = true;
+  pl->split = attn && topk && any_verify && any_draft && g_overlap.load() != 0;
 
   pl->nchunk.assign(B, 1);
   pl->part0.assign(B, 0);
@@ -167,7 +176,11 @@ int32_t plan_size(const Shape& s, const std::vector<Req>& rq, bool attn, bool to
       if (nc > 1) {
         pl->part0[r] = part_rows;
         part_rows += (int64_t)Hkv * nc * (v ? rows_v : 1) * G;
-        pl->n_merge += Hkv * ((((v ? rows_v : 1) * G) + MERGE_ROWS - 1) / MERGE_ROWS);
+        const int nm = Hkv * ((((v ? rows_v : 1) * G) + MERGE_ROWS - 1) / MERGE_ROWS);
+        if (pl->split && !v)
+          pl->n_merge_d += nm;
+        else
+          pl->n_merge += nm;
       }
       bytes[r] = v ? (double)q.L * (2.0 * D * esz + 4 + 4.0 * rows_v * G)
                    : (double)q.nlist * (2.0 * D * esz + 8);
@@ -179,19 +192,27 @@ int32_t plan_size(const Shape& s, const std::vector<Req>& rq, bool attn, bool to
     std::stable_sort(pl->order.begin(), pl->order.end(),
                      [&](int a, int b) { return bytes[a] > bytes[b]; });
     pl->xcd.resize((size_t)B * Hkv);
-    double load[NUM_XCD] = {0};
-    for (int r : pl->order)
+    double load[NUM_XCD] = {0}, load_d[NUM_XCD] = {0};
+    for (int r : pl->order) {
+      const bool own = pl->split && !rq[r].verify;  // the draft launch's queues
+      double* ld = own ? load_d : load;
+      int* ql = own ? pl->qlen_d : pl->qlen;
       for (int g = 0; g < Hkv; ++g) {
         int x = 0;
         for (int y = 1; y < NUM_XCD; ++y)
-          if (load[y] < load[x]) x = y;
-        load[x] += bytes[r];
-        pl->qlen[x] += nitems[r];
+          if (ld[y] < ld[x]) x = y;
+        ld[x] += bytes[r];
+        ql[x] += nitems[r];
         pl->xcd[(size_t)r * Hkv + g] = (uint8_t)x;
       }
-    int maxlen = 0;
-    for (int x = 0; x < NUM_XCD; ++x) maxlen = std::max(maxlen, pl->qlen[x]);
+    }
+    int maxlen = 0, maxlen_d = 0;
+    for (int x = 0; x < NUM_XCD; ++x) {
+      maxlen = std::max(maxlen, pl->qlen[x]);
+      maxlen_d = std::max(maxlen_d, pl->qlen_d[x]);
+    }
     pl->n_items = maxlen * NUM_XCD;
+    pl->n_items_d = maxlen_d * NUM_XCD;
   }
   int64_t pbar = 0;
   if (topk)
@@ -229,8 +250,12 @@ int32_t plan_size(const Shape& s, const std::vector<Req>& rq, bool attn, bool to
   size_t h = 0;
   pl->h_items = h;
   h = align_up(h + (size_t)pl->n_items * sizeof(Item), 256);
+  pl->h_items_d = h;
+  h = align_up(h + (size_t)pl->n_items_d * sizeof(Item), 256);
   pl->h_post = h;
   h = align_up(h + (size_t)(pl->n_avg + pl->n_merge) * sizeof(PostItem), 256);
+  pl->h_post_d = h;
+  h = align_up(h + (size_t)pl->n_merge_d * sizeof(PostItem), 256);
   pl->h_sel = h;
   h = align_up(h + (size_t)pl->n_sel * sizeof(PostItem), 256);
   pl->h_bytes = h;
@@ -254,8 +279,9 @@ void plan_write(const Shape& s, const std::vector<Req>& rq, const Plan& pl, char
   const bool bf16 = s.dtype == SPA_BF16;
   const int CV = verify_chunk(), CD = draft_chunk();
   if (pl.attn) {
-    Item* items = reinterpret_cast<Item*>(h + pl.h_items);
-    int cur[NUM_XCD] = {0};
+    Item* items_v = reinterpret_cast<Item*>(h + pl.h_items);
+    Item* items_d = reinterpret_cast<Item*>(h + pl.h_items_d);
+    int cur_v[NUM_XCD] = {0}, cur_dr[NUM_XCD] = {0};
     for (int r : pl.order) {
       const Req& q = rq[r];
       const bool v = q.verify;
@@ -264,6 +290,8 @@ void plan_write(const Shape& s, const std::vector<Req>& rq, const Plan& pl, char
       const int nc = pl.nchunk[r];
       const int nq = (v && !bf16) ? rows_v : 1;
       const int64_t head_rows = (int64_t)nc * (v ? rows_v : 1) * G;
+      Item* items = (pl.split && !v) ? items_d : items_v;
+      int* cur = (pl.split && !v) ? cur_dr : cur_v;
       for (int g = 0; g < Hkv; ++g) {
         const int x = pl.xcd[(size_t)r * Hkv + g];
         Item it;
@@ -290,15 +318,18 @@ void plan_write(const Shape& s, const std::vector<Req>& rq, const Plan& pl, char
     Item nop;
     std::memset(&nop, 0, sizeof nop);
     nop.kind = KIND_NOP;
-    const int maxlen = pl.n_items / NUM_XCD;
-    for (int x = 0; x < NUM_XCD; ++x)
-      for (int i = cur[x]; i < maxlen; ++i) items[(size_t)i * NUM_XCD + x] = nop;
+    const int maxlen = pl.n_items / NUM_XCD, maxlen_d = pl.n_items_d / NUM_XCD;
+    for (int x = 0; x < NUM_XCD; ++x) {
+      for (int i = cur_v[x]; i < maxlen; ++i) items_v[(size_t)i * NUM_XCD + x] = nop;
+      for (int i = cur_dr[x]; i < maxlen_d; ++i) items_d[(size_t)i * NUM_XCD + x] = nop;
+    }
   }
   // post-pass: the averaging chunks of every verify (r, g), then the split-K
   // merges (measured faster than the reverse order)
   PostItem* post = reinterpret_cast<PostItem*>(h + pl.h_post);
+  PostItem* post_d = reinterpret_cast<PostItem*>(h + pl.h_post_d);
   PostItem* sel = reinterpret_cast<PostItem*>(h + pl.h_sel);
-  int np = 0, ns = 0;
+  int np = 0, ns = 0, npd = 0;
   if (pl.topk) {
     int64_t pbar = 0;
     for (int r = 0; r < B; ++r) {
@@ -352,19 +383,30 @@ void plan_write(const Shape& s, const std::vector<Req>& rq, const Plan& pl, char
         for (int j = 0; j < rq_rows * G; j += MERGE_ROWS) {
           m.j0 = j;
           m.j1 = std::min(rq_rows * G, j + MERGE_ROWS);
-          post[np++] = m;
+          if (pl.split && !q.verify)
+            post_d[npd++] = m;
+          else
+            post[np++] = m;
         }
       }
     }
 }
 
 // ---- opt-in per-launch timing ------------------------------------------------
-enum { PROF_ATTN = 0, PROF_POST = 1, PROF_SELECT = 2, PROF_N = 3 };
+enum {
+  PROF_ATTN = 0,        // the attention launch (with overlap: the verify attention launch)
+  PROF_POST = 1,
+  PROF_SELECT = 2,
+  PROF_ATTN_DRAFT = 3,  // the draft attention launch of an overlapped unified step
+  PROF_ATTN_SPAN = 4,   // all attention of a call: first launch start to last launch end
+  PROF_N = 5
+};
 std::mutex g_prof_mu;
 std::atomic<int32_t> g_prof_mask{0};
 struct ProfPending {
   int which;
   hipEvent_t a, b;
+  hipEvent_t c = nullptr;  // a second end event (span over two streams), or null
 };
 std::vector<ProfPending> g_prof_pending;
 std::vector<hipEvent_t> g_prof_free;
@@ -402,6 +444,36 @@ struct ProfScope {
     } else {
       g_prof_free.push_back(a);
       if (b) g_prof_free.push_back(b);
+    }
+  }
+};
+
+// Span of all attention of one call: a start event on the caller's stream and
+// an end event behind each attention launch (one or two streams).
+struct ProfSpan {
+  hipEvent_t a = nullptr, b = nullptr, c = nullptr;
+  bool on = false;
+  void start(hipStream_t st) {
+    if (!((g_prof_mask.load() >> PROF_ATTN_SPAN) & 1)) return;
+    std::lock_guard<std::mutex> lock(g_prof_mu);
+    a = prof_event();
+    on = a && hipEventRecord(a, st) == hipSuccess;
+  }
+  void end(hipStream_t st, bool second) {
+    if (!on) return;
+    std::lock_guard<std::mutex> lock(g_prof_mu);
+    hipEvent_t e = prof_event();
+    if (e && hipEventRecord(e, st) != hipSuccess) e = nullptr;
+    (second ? c : b) = e;
+  }
+  void finish() {
+    if (!on) return;
+    std::lock_guard<std::mutex> lock(g_prof_mu);
+    if (b) {
+      g_prof_pending.push_back(ProfPending{PROF_ATTN_SPAN, a, b, c});
+    } else {
+      g_prof_free.push_back(a);
+      if (c) g_prof_free.push_back(c);
     }
   }
 };
@@ -477,6 +549,31 @@ int32_t acquire_slot(const Plan& pl, PlanSlot** out) {
   return SPA_OK;
 }
 
+// ---- side stream of the split attention launch --------------------------------
+// One per device, default priority; forked from and joined back to the
+// caller's stream with events, so the call stays ordered on that stream.
+struct Side {
+  hipStream_t stream = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+std::vector<Side> g_side;
+
+int32_t side_stream(Side** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("get device: ") + hipGetErrorString(e));
+  if ((int)g_side.size() <= dev) g_side.resize(dev + 1);
+  Side& sd = g_side[dev];
+  if (!sd.stream) {
+    e = hipStreamCreateWithFlags(&sd.stream, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&sd.fork, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&sd.join, hipEventDisableTiming);
+    if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("side stream: ") + hipGetErrorString(e));
+  }
+  *out = &sd;
+  return SPA_OK;
+}
+
 struct Buffers {
   const int32_t* page_table = nullptr;
   const void* q = nullptr;
@@ -496,7 +593,7 @@ int32_t run(const Shape& s, const std::vector<Req>& rq, const Plan& pl, const Bu
                 "workspace of " + std::to_string(ws_bytes) + " bytes, need " + std::to_string(pl.total));
   if (pl.total > 0 && !d_ws) return fail(SPA_ERR_INVALID_ARG, "d_ws is NULL");
   const int n_post = pl.n_avg + pl.n_merge;
-  if (pl.n_items == 0 && n_post == 0 && pl.n_sel == 0) return SPA_OK;
+  if (pl.n_items == 0 && pl.n_items_d == 0 && n_post == 0 && pl.n_sel == 0) return SPA_OK;
   std::lock_guard<std::mutex> lock(g_ring_mu);
   PlanSlot* slot = nullptr;
   int32_t rc = acquire_slot(pl, &slot);
@@ -507,7 +604,12 @@ int32_t run(const Shape& s, const std::vector<Req>& rq, const Plan& pl, const Bu
   float* part_o = reinterpret_cast<float*>(ws + pl.off_part_o);
   float* part_ml = reinterpret_cast<float*>(ws + pl.off_part_ml);
   hipError_t e;
-  if (pl.n_items > 0) {
+  Side* side = nullptr;
+  if (pl.split) {
+    rc = side_stream(&side);
+    if (rc) return rc;
+  }
+  if (pl.n_items > 0 || pl.n_items_d > 0) {
     AttnParams p;
     p.items = reinterpret_cast<const Item*>(plan + pl.h_items);
     p.q = b.q;
@@ -527,11 +629,36 @@ int32_t run(const Shape& s, const std::vector<Req>& rq, const Plan& pl, const Bu
     p.G = s.G;
     p.k = s.k;
     p.sm_scale = s.scale;
-    {
+    ProfSpan span;
+    span.start(st);
+    if (pl.split) {
+      // the fork point: everything already on `st`, but not the verify attention
+      e = hipEventRecord(side->fork, st);
+      if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("fork: ") + hipGetErrorString(e));
+    }
+    // verify (or all) attention first, so that its long items reach the CUs
+    // before the draft launch's
+    if (pl.n_items > 0) {
       ProfScope ps(PROF_ATTN, st);
-      e = launch_attn(p, s.dtype, s.d, pl.n_items, pl.nthr, pl.smem, st);
+      e = launch_attn(p, s.dtype, s.d, pl.n_items, pl.nthr, pl.smem, false, st);
     }
     if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("attention launch: ") + hipGetErrorString(e));
+    span.end(st, false);
+    if (pl.split) {
+      e = hipStreamWaitEvent(side->stream, side->fork, 0);
+      if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("fork wait: ") + hipGetErrorString(e));
+      AttnParams pd = p;
+      pd.items = reinterpret_cast<const Item*>(plan + pl.h_items_d);
+      {
+        ProfScope ps(PROF_ATTN_DRAFT, side->stream);
+        e = launch_attn(pd, s.dtype, s.d, pl.n_items_d, pl.nthr, pl.smem, true, side->stream);
+      }
+      if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("draft attention launch: ") + hipGetErrorString(e));
+      span.end(side->stream, true);
+      e = hipEventRecord(side->join, side->stream);
+      if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("join record: ") + hipGetErrorString(e));
+    }
+    span.finish();
   }
   if (n_post > 0) {
     PostParams pp;
@@ -563,6 +690,29 @@ int32_t run(const Shape& s, const std::vector<Req>& rq, const Plan& pl, const Bu
       e = launch_select(sp, pl.n_sel, st);
     }
     if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("selection launch: ") + hipGetErrorString(e));
+  }
+  if (pl.split) {
+    e = hipStreamWaitEvent(st, side->join, 0);
+    if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("join: ") + hipGetErrorString(e));
+    if (pl.n_merge_d > 0) {  // merges of drafts split into several chunks
+      PostParams pp;
+      pp.items = reinterpret_cast<const PostItem*>(plan + pl.h_post_d);
+      pp.part_o = part_o;
+      pp.part_ml = part_ml;
+      pp.o = b.o;
+      pp.lse = b.lse;
+      pp.logits = b.logits;
+      pp.pbar = nullptr;
+      pp.Hq = s.Hq;
+      pp.G = s.G;
+      pp.avg_row_begin = avg_begin;
+      pp.avg_row_count = avg_count;
+      {
+        ProfScope ps(PROF_POST, st);
+        e = launch_post(pp, s.dtype, s.d, pl.n_merge_d, post_smem_bytes(0, pl.max_nchunk), st);
+      }
+      if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("draft merge launch: ") + hipGetErrorString(e));
+    }
   }
   e = hipEventRecord(slot->ev, st);
   if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("event record: ") + hipGetErrorString(e));
@@ -652,6 +802,12 @@ int32_t spa_profile_read(int32_t which, int64_t* count, double* total_ms) {
     hipError_t e = hipEventSynchronize(pp.b);
     float ms = 0.f;
     if (e == hipSuccess) e = hipEventElapsedTime(&ms, pp.a, pp.b);
+    if (e == hipSuccess && pp.c) {
+      float ms2 = 0.f;
+      e = hipEventSynchronize(pp.c);
+      if (e == hipSuccess) e = hipEventElapsedTime(&ms2, pp.a, pp.c);
+      ms = std::max(ms, ms2);
+    }
     if (e != hipSuccess) {
       g_prof_pending.swap(keep);
       return fail(SPA_ERR_HIP, std::string("profile read: ") + hipGetErrorString(e));
@@ -660,6 +816,7 @@ int32_t spa_profile_read(int32_t which, int64_t* count, double* total_ms) {
     g_prof_ms[which] += ms;
     g_prof_free.push_back(pp.a);
     g_prof_free.push_back(pp.b);
+    if (pp.c) g_prof_free.push_back(pp.c);
   }
   g_prof_pending.swap(keep);
   if (count) *count = g_prof_count[which];
@@ -671,8 +828,10 @@ int32_t spa_profile_reset(void) {
   std::lock_guard<std::mutex> lock(g_prof_mu);
   for (auto& pp : g_prof_pending) {
     (void)hipEventSynchronize(pp.b);
+    if (pp.c) (void)hipEventSynchronize(pp.c);
     g_prof_free.push_back(pp.a);
     g_prof_free.push_back(pp.b);
+    if (pp.c) g_prof_free.push_back(pp.c);
   }
   g_prof_pending.clear();
   for (int i = 0; i < PROF_N; ++i) {
@@ -685,6 +844,11 @@ int32_t spa_profile_reset(void) {
 int32_t spa_abi_version(void) { return SPA_ABI_VERSION; }
 
 const char* spa_last_error(void) { return g_err.c_str(); }
+
+int32_t spa_set_overlap(int32_t enable) {
+  g_overlap.store(enable != 0);
+  return SPA_OK;
+}
 
 int32_t spa_set_split(int32_t verify_chunk_tokens, int32_t draft_chunk_entries) {
   if (verify_chunk_tokens < 0 || draft_chunk_entries < 0)

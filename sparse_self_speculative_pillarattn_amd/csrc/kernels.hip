@@ -706,8 +706,7 @@ __device__ void gather_tile_valu(const AttnParams& p, const Item& it, char* smem
 }
 
 template <int D, typename T, int GM>
-__global__ void __launch_bounds__(512) attn_kernel(AttnParams p) {
-  extern __shared__ __attribute__((aligned(16))) char smem[];
+__device__ __forceinline__ void attn_body(const AttnParams& p, char* smem) {
   const Item it = p.items[blockIdx.x];
   if (it.kind == KIND_NOP) return;
   if constexpr (sizeof(T) == 2) {
@@ -720,6 +719,22 @@ __global__ void __launch_bounds__(512) attn_kernel(AttnParams p) {
   } else {
     gather_tile_valu<D, T, GM>(p, it, smem, true, 0, 0x7fffffff, nullptr, 0, p.G);
   }
+}
+
+// All attention items of a call (or, for a mixed batch with overlap, its
+// verify items).
+template <int D, typename T, int GM>
+__global__ void __launch_bounds__(512) attn_kernel(AttnParams p) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  attn_body<D, T, GM>(p, smem);
+}
+
+// The draft items of a mixed batch, launched on the side stream (same work
+// per item; a separate symbol so that profiles tell the two launches apart).
+template <int D, typename T, int GM>
+__global__ void __launch_bounds__(512) attn_kernel_draft(AttnParams p) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  attn_body<D, T, GM>(p, smem);
 }
 
 // ==========================================================================
@@ -1212,31 +1227,38 @@ size_t attn_smem_bytes(int dtype, int head_dim, int G, int nthr, bool mfma, bool
 }
 
 template <int D, typename T>
-static hipError_t launch_attn_g(const AttnParams& p, int nitems, int nthr, size_t smem,
+static hipError_t launch_attn_g(const AttnParams& p, int nitems, int nthr, size_t smem, bool draft,
                                 hipStream_t st) {
   const int G = p.G;
-#define SPA_ATTN(GMV)                                                                    \
-  do {                                                                                   \
-    hipLaunchKernelGGL((attn_kernel<D, T, GMV>), dim3(nitems), dim3(nthr), smem, st, p); \
-    return hipGetLastError();                                                            \
+#define SPA_ATTN(GMV)                                                                           \
+  do {                                                                                          \
+    if (draft)                                                                                  \
+      hipLaunchKernelGGL((attn_kernel_draft<D, T, GMV>), dim3(nitems), dim3(nthr), smem, st, p); \
+    else                                                                                        \
+      hipLaunchKernelGGL((attn_kernel<D, T, GMV>), dim3(nitems), dim3(nthr), smem, st, p);       \
+    return hipGetLastError();                                                                   \
   } while (0)
-  if (G <= 1) SPA_ATTN(1);
-  if (G <= 2) SPA_ATTN(2);
-  if (G <= 4) SPA_ATTN(4);
-  if (G <= 5) SPA_ATTN(5);
-  SPA_ATTN(8);
+  if constexpr (sizeof(T) == 2) {
+    SPA_ATTN(1);  // the MFMA path does not depend on the group template
+  } else {
+    if (G <= 1) SPA_ATTN(1);
+    if (G <= 2) SPA_ATTN(2);
+    if (G <= 4) SPA_ATTN(4);
+    if (G <= 5) SPA_ATTN(5);
+    SPA_ATTN(8);
+  }
 #undef SPA_ATTN
 }
 
 hipError_t launch_attn(const AttnParams& p, int dtype, int head_dim, int nitems, int nthr,
-                       size_t smem, hipStream_t st) {
+                       size_t smem, bool draft, hipStream_t st) {
   if (nitems == 0) return hipSuccess;
   if (dtype == 0) {
-    if (head_dim == 128) return launch_attn_g<128, uint16_t>(p, nitems, nthr, smem, st);
-    return launch_attn_g<64, uint16_t>(p, nitems, nthr, smem, st);
+    if (head_dim == 128) return launch_attn_g<128, uint16_t>(p, nitems, nthr, smem, draft, st);
+    return launch_attn_g<64, uint16_t>(p, nitems, nthr, smem, draft, st);
   }
-  if (head_dim == 128) return launch_attn_g<128, float>(p, nitems, nthr, smem, st);
-  return launch_attn_g<64, float>(p, nitems, nthr, smem, st);
+  if (head_dim == 128) return launch_attn_g<128, float>(p, nitems, nthr, smem, draft, st);
+  return launch_attn_g<64, float>(p, nitems, nthr, smem, draft, st);
 }
 
 hipError_t launch_select(const SelectParams& sp, int nitems, hipStream_t st) {

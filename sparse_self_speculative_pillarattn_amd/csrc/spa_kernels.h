@@ -49,7 +49,7 @@ size_t attn_smem_bytes(int dtype, int head_dim, int G, int nthr, bool mfma, bool
 size_t post_smem_bytes(int avg_terms, int max_nchunk);
 
 hipError_t launch_attn(const AttnParams& p, int dtype, int head_dim, int nitems, int nthr,
-                       size_t smem, hipStream_t st);
+                       size_t smem, bool draft, hipStream_t st);
 hipError_t launch_post(const PostParams& p, int dtype, int head_dim, int nitems, size_t smem,
                        hipStream_t st);
 hipError_t launch_select(const SelectParams& sp, int nitems, hipStream_t st);

@@ -94,6 +94,20 @@ def test_ragged_lengths(oracle, L):
     check(oracle, w)
 
 
+@pytest.mark.parametrize("overlap", [True, False])
+def test_overlap_switch(oracle, overlap):
+    """The unified step with the draft attention on the side stream and in one
+    launch with the verify attention: same results."""
+    bd.set_overlap(overlap)
+    try:
+        w = synth.Workload(name=f"ovl{int(overlap)}", batch=9, num_qo_heads=32, num_kv_heads=8,
+                           head_dim=128, dtype="bf16", spec_k=8, sparsity=Fraction(1, 4),
+                           lengths=("uniform", 300, 5000), n_verify=3, seed=41)
+        check(oracle, w)
+    finally:
+        bd.set_overlap(False)
+
+
 @pytest.mark.parametrize("split", [(64, 16), (2048, 2048), (320, 100), (40, 7)])
 def test_split_invariance(oracle, split):
     bd.set_split(*split)
