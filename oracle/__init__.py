@@ -48,6 +48,9 @@ def _load(mutant: int = 0):
                                 vp, vp, vp, _i32p, _i64p, _i32p, _f64p, _f64p, _f64p, _i64p,
                                 vp, C.c_int]
     lib.oracle_step.restype = C.c_int
+    lib.oracle_recall_index.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int, _i32p, C.c_int,
+                                        _i32p]
+    lib.oracle_recall_index.restype = C.c_int
     lib.oracle_mutant_id.restype = C.c_int
     _LIBS[mutant] = lib
     return lib
@@ -119,6 +122,17 @@ class Oracle:
                                       np.ascontiguousarray(pt_row, np.int32), idx.shape[1], idx,
                                       o, lse)
         return o, lse
+
+    def recall_index(self, L, n_sink, n_recent, stored, cap):
+        """stored [n] positions of one KV head -> (out [cap], u): the ascending
+        union of sinks, valid stored positions and recent positions, then -1."""
+        stored = np.ascontiguousarray(stored, np.int32).reshape(-1)
+        out = np.empty((max(int(cap), 1),), np.int32)
+        u = self.lib.oracle_recall_index(int(L), int(n_sink), int(n_recent), stored.shape[0],
+                                         stored, int(cap), out)
+        if u < 0:
+            raise ValueError(f"oracle_recall_index failed ({u})")
+        return out[:int(cap)], u
 
     # -- whole batch --------------------------------------------------------------
     def step(self, *, k, Hq, Hkv, sm_scale, is_verify, seq_lens, q_indptr, page_table, q,

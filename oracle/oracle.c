@@ -23,6 +23,11 @@
  *   oracle_step            the whole unified batch: verify requests run the
  *                          first three, draft requests the last (review,
  *                          "Unified batch scheduler + fused attention kernel").
+ *   oracle_recall_index    the recallable per-head index of a draft step: sink
+ *                          tokens, the stored important positions and the
+ *                          recent tokens (arxiv.org 2607.27735 as rendered on
+ *                          bittide.aicompass.dev, "全局的稀疏一瞥", section 方法,
+ *                          Figure 3 caption).
  *
  * Readings where the pages are silent (each is exercised by a test):
  *   - softmax scale is a parameter (callers use 1/sqrt(d));
@@ -35,7 +40,11 @@
  *   - top-K orders by (score descending, position ascending) and returns the
  *     chosen positions ascending;
  *   - a draft list entry outside [0, L) is ignored; if none remains, O = 0 and
- *     LSE = -inf; duplicate entries are attended as many times as listed.
+ *     LSE = -inf; duplicate entries are attended as many times as listed;
+ *   - the recallable index is a set: sinks are positions [0, n_sink), recent
+ *     tokens are the last n_recent positions [L - n_recent, L) of the draft's
+ *     current length L (so they include the tokens the draft itself appended),
+ *     and each position appears once; the pages give neither count.
  *
  * Arithmetic is fp64; bf16 inputs are widened exactly.
  *
@@ -341,6 +350,39 @@ int oracle_step(int B, int k, int Hq, int Hkv, int d, double sm_scale, int dtype
   free(th);
   pthread_mutex_destroy(&a.lock);
   return a.status;
+}
+
+/* ---- recallable sparse index of one KV head --------------------------------
+ * Position j in [0, L) belongs to the index when it is a sink (j < n_sink), a
+ * recent token (j >= L - n_recent), or an entry of the stored list `in`
+ * (entries outside [0, L) name no position).  Members go to out[0..u)
+ * ascending; out[u..cap) is filled with -1, an entry that draft attention
+ * ignores.  Returns u, or -1 when u > cap.
+ */
+int oracle_recall_index(int L, int n_sink, int n_recent, int n_in, const int32_t* in, int cap,
+                        int32_t* out) {
+  unsigned char* member = (unsigned char*)calloc((size_t)(L > 0 ? L : 1), 1);
+  if (!member) return -2;
+  for (int j = 0; j < L; ++j) {
+    int sink = MUT(15) ? (j <= n_sink) : (j < n_sink);
+    int recent = MUT(13) ? (j >= L - n_recent - 1 && j < L - 1) : (j >= L - n_recent);
+    if (sink || recent) member[j] = 1;
+  }
+  for (int t = 0; t < n_in; ++t) {
+    int32_t p = in[t];
+    if (MUT(14) && p >= L) p = L - 1;
+    if (p >= 0 && p < L) member[p] = 1;
+  }
+  int u = 0;
+  for (int j = 0; j < L; ++j) {
+    if (!member[j]) continue;
+    if (u < cap) out[u] = j;
+    ++u;
+  }
+  free(member);
+  if (u > cap) return -1;
+  for (int t = u; t < cap; ++t) out[t] = MUT(16) ? 0 : -1;
+  return u;
 }
 
 int oracle_mutant_id(void) { return ORACLE_MUTANT; }

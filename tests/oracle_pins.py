@@ -288,7 +288,65 @@ def pin_bf16_widening(orc):
         _close(a, b, 0.0, "bf16 widening")
 
 
+# --------------------------------------------------------------------------- #
+# recallable index (sinks + stored important positions + recent tokens)
+# --------------------------------------------------------------------------- #
+def pin_recall_special_cases(orc):
+    """No sinks and no window return the stored list itself; sinks or a window
+    covering the whole context return every position; padding is -1."""
+    got, u = orc.recall_index(40, 0, 0, [2, 5, 17, 39], 6)
+    assert u == 4 and list(got) == [2, 5, 17, 39, -1, -1], (u, got)
+    for S, W in ((40, 0), (0, 40), (25, 15), (100, 3)):
+        got, u = orc.recall_index(40, S, W, [7, 7, 60, -3], 40)
+        assert u == 40 and list(got) == list(range(40)), (S, W, u)
+    got, u = orc.recall_index(1, 0, 0, [], 1)
+    assert u == 0 and list(got) == [-1]
+    # stored entries past the context or negative name no position
+    got, u = orc.recall_index(30, 2, 0, [5, 30, 33, -1, 5], 8)
+    assert u == 3 and list(got) == [0, 1, 5, -1, -1, -1, -1, -1], (u, got)
+
+
+def pin_recall_newest_tokens(orc):
+    """A window of w keeps exactly the last w positions, so the newest token a
+    draft appended (position L-1) is always recalled when w >= 1."""
+    for L in (1, 2, 9, 33):
+        for w in (1, 3, 8):
+            got, u = orc.recall_index(L, 0, w, [], L)
+            assert list(got[:u]) == list(range(max(0, L - w), L)), (L, w, got)
+
+
+def pin_recall_set_properties(orc):
+    """Random stored lists (with duplicates and out-of-range entries): the
+    output is strictly ascending, holds every sink, every recent position and
+    every valid stored entry, nothing else, and its size matches the count of
+    the union worked out from interval lengths."""
+    rng = np.random.default_rng(11)
+    for trial in range(60):
+        L = int(rng.integers(1, 300))
+        S = int(rng.integers(0, 12))
+        W = int(rng.integers(0, 20))
+        n = int(rng.integers(0, 40))
+        stored = rng.integers(-4, L + 6, size=n).astype(np.int32)
+        cap = L + 2
+        got, u = orc.recall_index(L, S, W, stored, cap)
+        body = np.asarray(got[:u], np.int64)
+        assert np.all(got[u:] == -1), "padding"
+        assert np.all(np.diff(body) > 0), "not strictly ascending"
+        assert body.size == 0 or (body[0] >= 0 and body[-1] < L), "out of range"
+        s_end = min(S, L)
+        r_begin = max(s_end, L - W)
+        valid = {int(p) for p in stored if 0 <= p < L}
+        want_count = s_end + (L - r_begin) + sum(1 for p in valid if s_end <= p < r_begin)
+        assert u == want_count, (trial, u, want_count)
+        members = set(body.tolist())
+        assert set(range(s_end)) <= members and set(range(r_begin, L)) <= members
+        assert valid <= members
+        for p in members:
+            assert p < S or p >= L - W or p in valid, (trial, p)
+
+
 ALL_PINS = [pin_verify_vs_sdpa, pin_uniform_keys, pin_one_and_two_keys, pin_dump_consistency,
             pin_average, pin_topk_bruteforce, pin_topk_vs_torch, pin_topk_special,
             pin_draft_full_list, pin_draft_invariances, pin_draft_matches_last_verify_row,
-            pin_bf16_widening]
+            pin_bf16_widening, pin_recall_special_cases, pin_recall_newest_tokens,
+            pin_recall_set_properties]

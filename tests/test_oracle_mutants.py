@@ -17,6 +17,10 @@ MUTANTS = {
     10: "invalid draft positions clamped instead of ignored",
     11: "V gathered by position instead of slot",
     12: "pool layout read as [slots][d][H_kv]",
+    13: "recent window shifted back one position (newest token dropped)",
+    14: "stored positions past the context clamped to the last position",
+    15: "one sink too many",
+    16: "recallable index padded with position 0 instead of -1",
 }
 
 
