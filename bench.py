@@ -267,6 +267,66 @@ def unified_vs_sequential(w, dev, steps: int, warmup: int):
                       "sequential_us": round(seq, 1), "speedup": round(seq / uni, 3)}))
 
 
+def recall_measure(w, dev, steps: int, warmup: int, n_sink: int, n_recent: int):
+    """The recallable index on the workload's drafts: the index launch alone,
+    and the unified step whose drafts read recalled lists (index launch + step)
+    against the same step over the stored lists."""
+    from dataclasses import replace
+    b = synth.make_batch(w, device=dev)
+    Hkv = w.num_kv_heads
+    dra = [r for r in range(b.B) if not b.is_verify[r]]
+    cnt = [bd.recall_length(b.seq_lens[r], b.idx_count[r], n_sink, n_recent) for r in dra]
+    new_off, new_cnt = list(b.idx_off), list(b.idx_count)
+    cur = b.idx_elems
+    for r, c in zip(dra, cnt):
+        new_off[r], new_cnt[r] = cur, c
+        cur += Hkv * c
+    idx = torch.cat([b.idx, torch.zeros((cur - b.idx_elems,), dtype=torch.int32, device=dev)])
+    b2 = replace(b, idx=idx, idx_off=new_off, idx_count=new_cnt, idx_elems=cur)
+    plain = bd.StepBuffers(b)
+    recalled = bd.StepBuffers(b2)
+    lens_d = np.asarray([b.seq_lens[r] for r in dra], np.int32)
+    inc_d = np.asarray([b.idx_count[r] for r in dra], np.int32)
+    inoff_d = np.asarray([b.idx_off[r] for r in dra], np.int64)
+    outc_d = np.asarray(cnt, np.int32)
+    outoff_d = np.asarray([new_off[r] for r in dra], np.int64)
+
+    def recall():  # stored lists and recalled lists live in the step's own idx buffer
+        bd.recall_index(len(dra), Hkv, lens_d, n_sink, n_recent, inc_d, inoff_d, recalled.idx,
+                        outc_d, outoff_d, recalled.idx)
+
+    def step_with_recall():
+        recall()
+        recalled.step()
+
+    t_plain = _time_steps(plain.step, steps, warmup)
+    t_recall = _time_steps(recall, steps, warmup)
+    t_both = _time_steps(step_with_recall, steps, warmup)
+    bd.profile_reset()
+    bd.profile_enable((1 << len(bd.PROF_NAMES)) - 1)
+    for _ in range(10):
+        step_with_recall()
+    torch.cuda.synchronize()
+    bd.profile_enable(0)
+    kern = {}
+    for i, nm in enumerate(bd.PROF_NAMES):
+        n, ms = bd.profile_read(i)
+        if n:
+            kern[nm] = round(ms / n * 1e3, 2)
+    # the index launch must read each stored list and write each output list once
+    rec_bytes = int(sum(Hkv * (k_in + k_out) * 4 for k_in, k_out in zip(inc_d, cnt)))
+    rec_us = kern.get("recall", float("nan"))
+    gbps = rec_bytes / (rec_us * 1e-6) / 1e9
+    print(json.dumps({
+        "recall": w.name, "n_sink": n_sink, "n_recent": n_recent, "n_draft": len(dra),
+        "stored_per_head": int(inc_d.mean()), "recalled_per_head": float(np.mean(cnt)),
+        "step_us_stored_lists": round(t_plain, 1), "recall_launch_us_back_to_back": round(t_recall, 1),
+        "step_us_with_recall": round(t_both, 1), "kernel_us_with_recall": kern,
+        "recall_roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
+                            "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 5),
+                            "algorithmic_bytes_per_launch": rec_bytes}}), flush=True)
+
+
 # --------------------------------------------------------------------------- #
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
@@ -283,6 +343,9 @@ def main():
                     help="only run the draft-only sparsity sweep and print its JSON line")
     ap.add_argument("--unified-vs-sequential", action="store_true",
                     help="only compare the unified step with the three entry points in sequence")
+    ap.add_argument("--recall", type=int, nargs=2, default=None, metavar=("SINKS", "RECENT"),
+                    help="only measure the recallable index (SINKS sink tokens, RECENT recent "
+                         "tokens) on the workload's drafts and print its JSON line")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 5 plain device copies of MIB MiB (reference for the HBM "
                          "byte counters) and exit")
@@ -315,6 +378,9 @@ def main():
     if args.unified_vs_sequential:
         unified_vs_sequential(w, dev, args.steps, args.warmup)
         return
+    if args.recall:
+        recall_measure(w, dev, args.steps, args.warmup, args.recall[0], args.recall[1])
+        return
     print(f"[bench] generating {w.name} on {dev}", file=sys.stderr, flush=True)
     b = synth.make_batch(w, device=dev)
     bufs = bd.StepBuffers(b)
@@ -326,10 +392,8 @@ def main():
         bufs.step()
     torch.cuda.synchronize()
 
-    # timed region: K steps back to back; the attention launch is bracketed by
-    # HIP events recorded on its own stream
-    bd.profile_reset()
-    bd.profile_enable((1 << bd.PROF_ATTN) | (1 << bd.PROF_ATTN_DRAFT) | (1 << bd.PROF_ATTN_SPAN))
+    # timed region: K steps back to back with nothing but the two bracketing
+    # events (the library's per-launch events would add their own gaps)
     t_ev0 = torch.cuda.Event(enable_timing=True)
     t_ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -340,15 +404,31 @@ def main():
     t_ev1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    bd.profile_enable(0)
-    n_attn, ms_attn = bd.profile_read(bd.PROF_ATTN)
-    n_attn_d, ms_attn_d = bd.profile_read(bd.PROF_ATTN_DRAFT)
-    n_span, ms_span = bd.profile_read(bd.PROF_ATTN_SPAN)
-    overlapped = n_attn_d > 0  # verify and draft attention ran as two launches
     ms_total = t_ev0.elapsed_time(t_ev1)
     ms_step = ms_total / args.steps
     print(f"[bench] timed {args.steps} steps: {ms_step * 1e3:.1f} us/step "
           f"(host wall {wall * 1e6 / args.steps:.1f} us/step)", file=sys.stderr, flush=True)
+
+    # the same K steps again, now with the attention launch bracketed by HIP
+    # events recorded on the stream it is launched on
+    bd.profile_reset()
+    bd.profile_enable((1 << bd.PROF_ATTN) | (1 << bd.PROF_ATTN_DRAFT))
+    for _ in range(args.steps):
+        bufs.step()
+    torch.cuda.synchronize()
+    bd.profile_enable(0)
+    n_attn, ms_attn = bd.profile_read(bd.PROF_ATTN)
+    n_attn_d, ms_attn_d = bd.profile_read(bd.PROF_ATTN_DRAFT)
+    overlapped = n_attn_d > 0  # verify and draft attention ran as two launches
+    n_span, ms_span = 0, 0.0
+    if overlapped:  # first start to last end of the two concurrent launches
+        bd.profile_reset()
+        bd.profile_enable(1 << bd.PROF_ATTN_SPAN)
+        for _ in range(args.steps):
+            bufs.step()
+        torch.cuda.synchronize()
+        bd.profile_enable(0)
+        n_span, ms_span = bd.profile_read(bd.PROF_ATTN_SPAN)
 
     # per-kernel breakdown (separate pass, every kernel bracketed)
     bd.profile_reset()

@@ -17,7 +17,9 @@
  *               device memory; host pointers (h_*) are ordinary host memory read
  *               during the call only.  The library keeps a small ring of pinned
  *               host buffers (allocated on first use, grown on demand) holding
- *               each call's work plan, which the kernels read in place.
+ *               each call's work plan, which the kernels read in place, and a
+ *               few device-side work counters per plan buffer (static device
+ *               memory, zero at load, back at zero after every launch).
  *   Layouts     (H_q query heads, H_kv KV heads, G = H_q / H_kv, d = head_dim,
  *               element type per spa_layout.dtype: bf16 or fp32)
  *               k_pool, v_pool  [num_slots][H_kv][d]; one slot holds one token.
@@ -150,6 +152,30 @@ int32_t spa_unified_step(const spa_layout* layout, int32_t B, int32_t spec_k,
                          int32_t avg_row_begin, int32_t avg_row_count, void* d_ws,
                          size_t ws_bytes, void* stream);
 
+/* Recallable sparse index of B draft requests.  Page "全局的稀疏一瞥"
+ * (arxiv.org 2607.27735 as rendered on bittide.aicompass.dev), section 方法,
+ * Figure 3 caption: a draft's per-head index keeps the sink tokens, the
+ * important history positions chosen from the last verify's attention scores,
+ * and the recent tokens.  For request r and KV head g it writes, ascending, the
+ * set of positions j in [0, L_r) with j < n_sink, or j >= L_r - n_recent, or j
+ * an entry of the stored list d_idx_in + h_in_off[r] + g*h_in_count[r] (stored
+ * entries outside [0, L_r) name no position; order and duplicates in the stored
+ * list do not matter), to d_idx_out + h_out_off[r] + g*h_out_count[r], then -1
+ * up to h_out_count[r] entries; spa_draft_attn and spa_unified_step ignore -1.
+ * h_seq_lens[B]: the draft's current length L_r (1 <= L_r <= 1048576), so the
+ * recent window holds the tokens the draft itself appended since the verify.
+ * h_out_count[r] must be >= max(1, min(L_r, S + R + h_in_count[r])), S =
+ * min(n_sink, L_r), R = L_r - max(S, L_r - min(n_recent, L_r)).  Output lists
+ * may not overlap one another or any stored list (checked on the host from the
+ * addresses); d_idx_in may be NULL when every h_in_count[r] is 0.  One launch;
+ * the output then feeds spa_draft_attn or the draft requests of
+ * spa_unified_step with h_idx_count[r] = h_out_count[r]. */
+int32_t spa_recall_index(int32_t B, int32_t num_kv_heads, const int32_t* h_seq_lens,
+                         int32_t n_sink, int32_t n_recent, const int32_t* h_in_count,
+                         const int64_t* h_in_off, const int32_t* d_idx_in,
+                         const int32_t* h_out_count, const int64_t* h_out_off, int32_t* d_idx_out,
+                         void* stream);
+
 /* Process-wide switch for spa_unified_step on a batch holding both verify
  * and draft requests (default 0): 1 runs its draft attention as a second
  * launch on a library-owned stream (default priority, one per device) that is
@@ -172,7 +198,8 @@ int32_t spa_set_split(int32_t verify_chunk_tokens, int32_t draft_chunk_entries);
  * averaging; bit 2: the top-K selection launch; bit 3: the draft attention
  * launch of an overlapped unified step; bit 4: all attention of a call, from
  * the start of its first attention launch to the end of its last, over both
- * streams when overlapped); 0 turns it off.
+ * streams when overlapped; bit 5: the spa_recall_index launch); 0 turns it
+ * off.
  * Returns SPA_OK. */
 int32_t spa_profile_enable(int32_t kernel_mask);
 

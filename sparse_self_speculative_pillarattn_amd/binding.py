@@ -28,11 +28,11 @@ SPA_F32 = 1
 
 EXPORTED = ("spa_abi_version", "spa_last_error", "spa_workspace_bytes", "spa_verify_attn",
             "spa_pillar_topk", "spa_draft_attn", "spa_unified_step", "spa_set_split", "spa_set_overlap",
-            "spa_profile_enable", "spa_profile_read", "spa_profile_reset")
+            "spa_profile_enable", "spa_profile_read", "spa_profile_reset", "spa_recall_index")
 
 # kernel indices of the per-launch timer
-PROF_ATTN, PROF_POST, PROF_SELECT, PROF_ATTN_DRAFT, PROF_ATTN_SPAN = range(5)
-PROF_NAMES = ("attn", "post", "select", "attn_draft", "attn_span")
+PROF_ATTN, PROF_POST, PROF_SELECT, PROF_ATTN_DRAFT, PROF_ATTN_SPAN, PROF_RECALL = range(6)
+PROF_NAMES = ("attn", "post", "select", "attn_draft", "attn_span", "recall")
 
 
 class SpaError(RuntimeError):
@@ -79,6 +79,8 @@ def load(path: str = LIB_PATH):
     lib.spa_unified_step.argtypes = [L, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                      vp, vp, i32, i32, vp, sz, vp]
     lib.spa_unified_step.restype = i32
+    lib.spa_recall_index.argtypes = [i32, i32, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp]
+    lib.spa_recall_index.restype = i32
     lib.spa_profile_enable.argtypes = [i32]
     lib.spa_profile_enable.restype = i32
     lib.spa_profile_read.argtypes = [i32, C.POINTER(C.c_int64), C.POINTER(C.c_double)]
@@ -214,6 +216,22 @@ def unified_step(lay, B, spec_k, is_verify, seq_lens, q_indptr, page_table, q, k
         h.arr(idx_count, np.int32), h.arr(idx_off, np.int64), _dptr(idx), _dptr(o), _dptr(lse),
         _dptr(logits), h.arr(logits_off, np.int64), int(avg_row_begin), int(avg_row_count),
         _dptr(ws), ws.numel() * ws.element_size(), _stream(q)))
+
+
+def recall_length(L: int, stored: int, n_sink: int, n_recent: int) -> int:
+    """Smallest output length spa_recall_index accepts for one request."""
+    s = min(n_sink, L)
+    rec = L - max(s, L - min(n_recent, L))
+    return max(1, min(L, s + rec + stored))
+
+
+def recall_index(B, num_kv_heads, seq_lens, n_sink, n_recent, in_count, in_off,
+                 idx_in: Optional[torch.Tensor], out_count, out_off, idx_out: torch.Tensor):
+    h = _Host()
+    _check(load().spa_recall_index(
+        int(B), int(num_kv_heads), h.arr(seq_lens, np.int32), int(n_sink), int(n_recent),
+        h.arr(in_count, np.int32), h.arr(in_off, np.int64), _dptr(idx_in),
+        h.arr(out_count, np.int32), h.arr(out_off, np.int64), _dptr(idx_out), _stream(idx_out)))
 
 
 def workspace(nbytes: int, device) -> torch.Tensor:

@@ -3,11 +3,12 @@
 //
 // A call turns the host metadata into a work plan -- one record per workgroup
 // -- written into a slot of a pinned host ring that the kernels read in place
-// (no copy is enqueued).  Items of one (request, KV head) stay on one XCD:
-// workgroup i of a launch runs on XCD i % 8, so the attention plan interleaves
-// eight per-XCD queues balanced by bytes.  A call enqueues at most three
-// launches: the attention of every request, the post-pass (split-K merges and
-// score averaging), then the top-K selection.
+// (no copy is enqueued).  The attention plan lists its items longest first (8
+// byte-balanced queues, interleaved); attention workgroups draw the next item
+// from a per-launch device counter as they start, so work flows to whichever
+// XCD frees first.  A call enqueues at most three launches: the attention of
+// every request, the post-pass (split-K merges and score averaging), then the
+// top-K selection.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -399,7 +400,8 @@ enum {
   PROF_SELECT = 2,
   PROF_ATTN_DRAFT = 3,  // the draft attention launch of an overlapped unified step
   PROF_ATTN_SPAN = 4,   // all attention of a call: first launch start to last launch end
-  PROF_N = 5
+  PROF_RECALL = 5,      // the recallable-index launch
+  PROF_N = 6
 };
 std::mutex g_prof_mu;
 std::atomic<int32_t> g_prof_mask{0};
@@ -491,6 +493,7 @@ struct PlanSlot {
   bool pending = false;
 };
 constexpr int RING = 16;
+static_assert(2 * RING <= TICKET_SETS, "two attention item counters per plan slot");
 std::mutex g_ring_mu;
 PlanSlot g_ring[RING];
 char* g_arena_host = nullptr;
@@ -629,6 +632,9 @@ int32_t run(const Shape& s, const std::vector<Req>& rq, const Plan& pl, const Bu
     p.G = s.G;
     p.k = s.k;
     p.sm_scale = s.scale;
+    // the slot is reused only after this call has finished, so its two item
+    // counters are never shared by launches in flight
+    p.ticket_set = 2 * static_cast<int32_t>(slot - g_ring);
     ProfSpan span;
     span.start(st);
     if (pl.split) {
@@ -649,6 +655,7 @@ int32_t run(const Shape& s, const std::vector<Req>& rq, const Plan& pl, const Bu
       if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("fork wait: ") + hipGetErrorString(e));
       AttnParams pd = p;
       pd.items = reinterpret_cast<const Item*>(plan + pl.h_items_d);
+      pd.ticket_set = p.ticket_set + 1;
       {
         ProfScope ps(PROF_ATTN_DRAFT, side->stream);
         e = launch_attn(pd, s.dtype, s.d, pl.n_items_d, pl.nthr, pl.smem, true, side->stream);
@@ -777,6 +784,26 @@ int32_t collect(const Shape& s, int B, const uint8_t* is_verify, const int32_t* 
       if (q.verify) seg.push_back({q.logits_off, (int64_t)(s.k + 1) * s.Hq * q.L});
     int32_t rc = check_segments(seg, "logits offsets");
     if (rc) return rc;
+  }
+  return SPA_OK;
+}
+
+// Address ranges [begin, end) of int32 list segments; two output ranges, or an
+// output and an input range, must not share an element.
+struct Range {
+  uintptr_t begin, end;
+  bool out;
+};
+int32_t check_no_overlap(std::vector<Range> v) {
+  std::sort(v.begin(), v.end(),
+            [](const Range& a, const Range& b) { return a.begin < b.begin; });
+  // sweep: the furthest end so far of output ranges and of input ranges
+  uintptr_t out_end = 0, in_end = 0;
+  for (const Range& x : v) {
+    if (x.begin == x.end) continue;
+    if (x.begin < out_end || (x.out && x.begin < in_end))
+      return fail(SPA_ERR_INVALID_ARG, "output lists overlap each other or a stored list");
+    (x.out ? out_end : in_end) = std::max(x.out ? out_end : in_end, x.end);
   }
   return SPA_OK;
 }
@@ -1039,6 +1066,85 @@ int32_t spa_unified_step(const spa_layout* layout, int32_t B, int32_t spec_k,
   b.logits = d_logits;
   return run(s, rq, pl, b, avg_row_begin, avg_row_count, d_ws, ws_bytes,
              static_cast<hipStream_t>(stream));
+}
+
+int32_t spa_recall_index(int32_t B, int32_t num_kv_heads, const int32_t* h_seq_lens,
+                         int32_t n_sink, int32_t n_recent, const int32_t* h_in_count,
+                         const int64_t* h_in_off, const int32_t* d_idx_in,
+                         const int32_t* h_out_count, const int64_t* h_out_off, int32_t* d_idx_out,
+                         void* stream) {
+  if (B < 0) return fail(SPA_ERR_INVALID_ARG, "B < 0");
+  if (num_kv_heads <= 0) return fail(SPA_ERR_INVALID_ARG, "num_kv_heads must be positive");
+  if (n_sink < 0 || n_recent < 0) return fail(SPA_ERR_INVALID_ARG, "n_sink and n_recent must be >= 0");
+  if (B == 0) return SPA_OK;
+  if (!h_seq_lens || !h_in_count || !h_in_off || !h_out_count || !h_out_off || !d_idx_out)
+    return fail(SPA_ERR_INVALID_ARG, "a required pointer is NULL");
+  std::vector<Range> ranges;
+  ranges.reserve(2 * (size_t)B);
+  int max_len = 1;
+  bool any_in = false;
+  for (int r = 0; r < B; ++r) {
+    const int64_t L = h_seq_lens[r], n_in = h_in_count[r], n_out = h_out_count[r];
+    if (L < 1) return fail(SPA_ERR_INVALID_ARG, "request " + std::to_string(r) + ": L < 1");
+    if (L > MAX_RECALL_LEN)
+      return fail(SPA_ERR_UNSUPPORTED, "request " + std::to_string(r) + ": L above 1048576");
+    if (n_in < 0) return fail(SPA_ERR_INVALID_ARG, "request " + std::to_string(r) + ": stored count < 0");
+    const int64_t s_end = std::min<int64_t>(n_sink, L);
+    const int64_t r_begin = std::max<int64_t>(s_end, L - std::min<int64_t>(n_recent, L));
+    const int64_t bound = std::min<int64_t>(L, s_end + (L - r_begin) + n_in);
+    if (n_out < std::max<int64_t>(bound, 1))
+      return fail(SPA_ERR_INVALID_ARG, "request " + std::to_string(r) + ": output length " +
+                                           std::to_string(n_out) + " below " +
+                                           std::to_string(std::max<int64_t>(bound, 1)));
+    if (h_in_off[r] < 0 || h_out_off[r] < 0)
+      return fail(SPA_ERR_INVALID_ARG, "request " + std::to_string(r) + ": negative offset");
+    max_len = std::max<int>(max_len, (int)L);
+    if (n_in > 0) {
+      any_in = true;
+      const uintptr_t a = reinterpret_cast<uintptr_t>(d_idx_in) + (uintptr_t)h_in_off[r] * 4;
+      ranges.push_back(Range{a, a + (uintptr_t)(n_in * num_kv_heads) * 4, false});
+    }
+    const uintptr_t a = reinterpret_cast<uintptr_t>(d_idx_out) + (uintptr_t)h_out_off[r] * 4;
+    ranges.push_back(Range{a, a + (uintptr_t)(n_out * num_kv_heads) * 4, true});
+  }
+  if (any_in && !d_idx_in) return fail(SPA_ERR_INVALID_ARG, "d_idx_in is NULL");
+  int32_t rc = check_no_overlap(std::move(ranges));
+  if (rc) return rc;
+  if ((int64_t)B * num_kv_heads > 0x7fffffff)
+    return fail(SPA_ERR_UNSUPPORTED, "more than 2^31 - 1 (request, KV head) pairs");
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  std::lock_guard<std::mutex> lock(g_ring_mu);
+  Plan pl;
+  pl.h_bytes = (size_t)B * sizeof(RecallReq);
+  PlanSlot* slot = nullptr;
+  rc = acquire_slot(pl, &slot);
+  if (rc) return rc;
+  RecallReq* rec = reinterpret_cast<RecallReq*>(slot->host);
+  for (int r = 0; r < B; ++r) {
+    rec[r].L = h_seq_lens[r];
+    rec[r].in_count = h_in_count[r];
+    rec[r].out_count = h_out_count[r];
+    rec[r].pad_ = 0;
+    rec[r].in_off = h_in_off[r];
+    rec[r].out_off = h_out_off[r];
+  }
+  RecallParams rp;
+  rp.reqs = reinterpret_cast<const RecallReq*>(slot->dev);
+  rp.idx_in = d_idx_in;
+  rp.idx_out = d_idx_out;
+  rp.Hkv = num_kv_heads;
+  rp.n_sink = n_sink;
+  rp.n_recent = n_recent;
+  hipError_t e;
+  {
+    ProfScope ps(PROF_RECALL, st);
+    e = launch_recall(rp, B * num_kv_heads, recall_smem_bytes(max_len), st);
+  }
+  if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("recall launch: ") + hipGetErrorString(e));
+  e = hipEventRecord(slot->ev, st);
+  if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("event record: ") + hipGetErrorString(e));
+  slot->pending = true;
+  return SPA_OK;
 }
 
 }  // extern "C"

@@ -15,6 +15,8 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <mutex>
+#include <vector>
 
 #include "spa_kernels.h"
 #include "spa_plan.h"
@@ -160,8 +162,20 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 // 16 bytes per lane from global memory to LDS: lane l's piece lands at
 // dst + 16 l (dst is wave-uniform).
+// KV rows are read once per step, so their loads carry the non-temporal hint
+// (cache-policy bit NT): streaming them then leaves L2 and the Infinity Cache
+// to the logits, which the post-pass reads back right after this launch.
+constexpr int KV_LOAD_POLICY = 2;
+
 __device__ __forceinline__ void load_lds16(const void* src, char* dst) {
-  __builtin_amdgcn_global_load_lds(src, (lds_void*)dst, 16, 0, 0);
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)dst, 16, 0, KV_LOAD_POLICY);
+}
+
+// 16 bytes of a KV row into registers, with the same streaming hint.
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_kv16(const void* src) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src));
+  return make_uint4(v.x, v.y, v.z, v.w);
 }
 
 // Slots of one tile as the producer's lanes use them: lane l loads rows
@@ -194,6 +208,10 @@ __device__ __forceinline__ void issue_kv_tile(char* stage, const TileSlots<D>& s
     load_lds16(vp + row + 8 * (pc ^ vswz<NCH>(tau)), stage + STAGE + 1024 * j);
   }
 }
+
+// Item counters of the attention launches, one per (plan slot, launch); see
+// attn_loop.
+__device__ uint32_t g_item_ticket[TICKET_SETS];
 
 // Producer side of the per-tile barrier: wait until the awaited tile has
 // landed in LDS, `after` tiles having been issued behind it, then meet the
@@ -248,7 +266,8 @@ __device__ void dma_producer(const AttnParams& p, const Item& it, char* smem,
 
 template <int D>
 __device__ void dma_consumer(const AttnParams& p, const Item& it, char* smem,
-                             const int32_t* slots, bool is_list, int wave, int lane) {
+                             const int32_t* slots, bool is_list, int wave, int lane,
+                             int* next_item, uint32_t wrap) {
   constexpr int NCH = D / 8;   // 16-byte chunks per K/V row
   constexpr int KS = D / 32;   // k-steps of S^T = K Q^T
   constexpr int DT = D / 16;   // d tiles of O^T
@@ -307,8 +326,14 @@ __device__ void dma_consumer(const AttnParams& p, const Item& it, char* smem,
   // at or below it
   const int vis_all = L - rows_q;
 
+  // the workgroup's next item, drawn by wave 0 two tiles before the end so
+  // that the atomic's round trip passes under the last tiles
+  uint32_t next = 0u;
+  const int draw_at = max(n_tiles - 2, 0);
   for (int i = 0; i < n_tiles; ++i) {
     __syncthreads();  // tile i ready (and tile i-1 released)
+    if (wave == 0 && lane == 0 && i == draw_at)
+      next = atomicInc(&g_item_ticket[p.ticket_set], wrap);
     if (!wave_active) continue;
     const int t0 = jb + i * DMA_TT;
     const char* Ks = smem + (i % DMA_STAGES) * 2 * STAGE;
@@ -440,6 +465,7 @@ __device__ void dma_consumer(const AttnParams& p, const Item& it, char* smem,
     }
   }
 
+  if (wave == 0 && lane == 0) *next_item = (int)next;
   if (!wave_active) return;
   float l_tot = l_run + __shfl_xor(l_run, 16);
   l_tot += __shfl_xor(l_tot, 32);
@@ -473,7 +499,8 @@ __device__ void dma_consumer(const AttnParams& p, const Item& it, char* smem,
 // under the causal limit, logits dumped) or a draft chunk (list entries
 // [begin, end); an entry outside [0, L) is masked).
 template <int D>
-__device__ void attn_tile_dma(const AttnParams& p, const Item& it, char* smem, bool is_list) {
+__device__ void attn_tile_dma(const AttnParams& p, const Item& it, char* smem, bool is_list,
+                              int* next_item, uint32_t wrap) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // slots of the chunk, padded to whole tiles; -1 marks a masked entry
   int32_t* slots = reinterpret_cast<int32_t*>(smem + dma_smem_bytes<D>() +
@@ -499,7 +526,7 @@ __device__ void attn_tile_dma(const AttnParams& p, const Item& it, char* smem, b
   if (wave == (int)(blockDim.x >> 6) - 1)
     dma_producer<D>(p, it, smem, slots, lane);
   else
-    dma_consumer<D>(p, it, smem, slots, is_list, wave, lane);
+    dma_consumer<D>(p, it, smem, slots, is_list, wave, lane, next_item, wrap);
 }
 
 // ==========================================================================
@@ -571,8 +598,8 @@ __device__ void gather_tile_valu(const AttnParams& p, const Item& it, char* smem
       const int32_t sv = slots[min(t, nent - 1)];
       s_[i] = (t < nent) ? sv : -1;
       const int64_t off = ((int64_t)max(sv, 0) * Hkv + g) * D + c * E;
-      k_[i] = *reinterpret_cast<const uint4*>(kpool + off);
-      v_[i] = *reinterpret_cast<const uint4*>(vpool + off);
+      k_[i] = load_kv16(kpool + off);
+      v_[i] = load_kv16(vpool + off);
     }
   };
   auto process = [&](int b0, const int32_t (&sl)[TPT], const uint4 (&kr)[TPT],
@@ -705,12 +732,18 @@ __device__ void gather_tile_valu(const AttnParams& p, const Item& it, char* smem
   }
 }
 
+
+// Runs one item; returns true when it has stored the workgroup's next draw
+// at next_item (the MFMA path does so near its end), false when the caller
+// must draw.  The result is the same for every thread of the workgroup.
 template <int D, typename T, int GM>
-__device__ __forceinline__ void attn_body(const AttnParams& p, char* smem) {
-  const Item it = p.items[blockIdx.x];
-  if (it.kind == KIND_NOP) return;
+__device__ __forceinline__ bool attn_body(const AttnParams& p, int item, char* smem,
+                                          int* next_item, uint32_t wrap) {
+  const Item it = p.items[item];
+  if (it.kind == KIND_NOP) return false;
   if constexpr (sizeof(T) == 2) {
-    attn_tile_dma<D>(p, it, smem, it.kind == KIND_DRAFT);
+    attn_tile_dma<D>(p, it, smem, it.kind == KIND_DRAFT, next_item, wrap);
+    return true;
   } else if (it.kind == KIND_VERIFY) {
     const int qi = it.qi;
     const int last_vis = it.L - (p.k + 1) + qi;
@@ -719,6 +752,34 @@ __device__ __forceinline__ void attn_body(const AttnParams& p, char* smem) {
   } else {
     gather_tile_valu<D, T, GM>(p, it, smem, true, 0, 0x7fffffff, nullptr, 0, p.G);
   }
+  return false;
+}
+
+// Persistent workgroups: the launch has as many workgroups as fit on the chip
+// at once, and each one keeps drawing the next item of the plan (longest
+// first) until none is left.  Whichever CU frees first, on any XCD, takes the
+// next item, so an XCD that runs slower simply processes fewer items; with
+// one workgroup per item, workgroup i always runs on XCD i % 8 and every XCD
+// would own a fixed eighth of the work.  A launch of G workgroups over n items
+// makes exactly n + G draws (n items, then one draw per workgroup that finds
+// the plan exhausted), so atomicInc wrapping at n + G - 1 hands out every
+// value once and leaves the counter at 0 for the next launch that uses it.
+// The draw for the next item lands in the other entry of s_item, which every
+// thread finished reading before the previous iteration's closing barrier.
+template <int D, typename T, int GM>
+__device__ __forceinline__ void attn_loop(const AttnParams& p, char* smem) {
+  __shared__ int s_item[2];
+  const uint32_t wrap = (uint32_t)p.n_items + gridDim.x - 1u;
+  if (threadIdx.x == 0) s_item[0] = (int)atomicInc(&g_item_ticket[p.ticket_set], wrap);
+  __syncthreads();
+  for (int k = 0;; k ^= 1) {
+    const int item = s_item[k];
+    if (item >= p.n_items) break;  // the same value for the whole workgroup
+    const bool drew = attn_body<D, T, GM>(p, item, smem, &s_item[k ^ 1], wrap);
+    if (!drew && threadIdx.x == 0)
+      s_item[k ^ 1] = (int)atomicInc(&g_item_ticket[p.ticket_set], wrap);
+    __syncthreads();  // LDS is free and the next draw is visible
+  }
 }
 
 // All attention items of a call (or, for a mixed batch with overlap, its
@@ -726,7 +787,7 @@ __device__ __forceinline__ void attn_body(const AttnParams& p, char* smem) {
 template <int D, typename T, int GM>
 __global__ void __launch_bounds__(512) attn_kernel(AttnParams p) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  attn_body<D, T, GM>(p, smem);
+  attn_loop<D, T, GM>(p, smem);
 }
 
 // The draft items of a mixed batch, launched on the side stream (same work
@@ -734,7 +795,7 @@ __global__ void __launch_bounds__(512) attn_kernel(AttnParams p) {
 template <int D, typename T, int GM>
 __global__ void __launch_bounds__(512) attn_kernel_draft(AttnParams p) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  attn_body<D, T, GM>(p, smem);
+  attn_loop<D, T, GM>(p, smem);
 }
 
 // ==========================================================================
@@ -971,7 +1032,6 @@ __device__ void select_topk(const float* scores, int L, int K, int32_t* out, cha
     for (int d = 0; d < 16; ++d) acc[d] = 0u;
     for (int c0 = 0; c0 < L; c0 += span) {
       if (!resident) load(c0);
-      const int j0 = c0 + KPT * tid;
       // Positions past L hold key 0, the smallest value, and come after every
       // real position in the tie order, so counting them never moves the
       // K-th largest real key (K <= L); the compaction skips them.
@@ -1169,7 +1229,9 @@ __global__ void __launch_bounds__(POST_THREADS) post_kernel(PostParams p) {
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 16
     for (int x = 0; x < terms; ++x) {
-      const float4 v = *reinterpret_cast<const float4*>(lg + rowoff_s[x] + j4);
+      // each logit is read once here: a streaming load, like the KV rows
+      const f32x4 v4 = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(lg + rowoff_s[x] + j4));
+      const float4 v = make_float4(v4.x, v4.y, v4.z, v4.w);
       const float l2 = lse2_s[x];
       const float vv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -1203,6 +1265,70 @@ __global__ void __launch_bounds__(SELECT_THREADS) select_kernel(SelectParams sp)
 }
 
 // ==========================================================================
+// recallable index: sinks + stored important positions + recent tokens
+// ==========================================================================
+// The per-head index of a draft step keeps the sink tokens, the important
+// history positions picked by the last verify's scores, and the recent tokens
+// (arxiv.org 2607.27735 as rendered on bittide.aicompass.dev, "全局的稀疏一瞥",
+// section 方法, Figure 3 caption).  It is a set over positions [0, L): one
+// workgroup per (request, KV head) marks its members in an LDS bitmap -- sinks
+// and recent tokens by interval arithmetic, stored entries with LDS atomics, so
+// any order and any duplicates in the stored list are fine -- then ranks the
+// set bits with one block scan and writes the members ascending, followed by
+// -1 up to the output length.
+constexpr int RECALL_THREADS = 256;
+
+// Bits of the 32-position word starting at `lo` that fall in [a, b).
+__device__ __forceinline__ uint32_t span_bits(int lo, int a, int b) {
+  const int x = min(max(a - lo, 0), 32), y = min(max(b - lo, 0), 32);
+  if (y <= x) return 0u;
+  const uint32_t upto_y = y >= 32 ? 0xffffffffu : ((1u << y) - 1u);
+  const uint32_t below_x = x >= 32 ? 0xffffffffu : ((1u << x) - 1u);
+  return upto_y & ~below_x;
+}
+
+__global__ void __launch_bounds__(RECALL_THREADS) recall_kernel(RecallParams rp) {
+  extern __shared__ __attribute__((aligned(16))) uint32_t bitmap[];
+  const int r = blockIdx.x / rp.Hkv;
+  const int g = blockIdx.x - r * rp.Hkv;
+  const RecallReq q = rp.reqs[r];
+  const int L = q.L;
+  const int nw = (L + 31) >> 5;
+  uint32_t* wsum = bitmap + ((nw + 3) & ~3);
+  const int s_end = min(rp.n_sink, L);
+  const int r_begin = max(s_end, L - min(rp.n_recent, L));
+  for (int w = threadIdx.x; w < nw; w += RECALL_THREADS)
+    bitmap[w] = span_bits(w * 32, 0, s_end) | span_bits(w * 32, r_begin, L);
+  __syncthreads();
+  const int32_t* in = rp.idx_in + q.in_off + (int64_t)g * q.in_count;
+  for (int t = threadIdx.x; t < q.in_count; t += RECALL_THREADS) {
+    const int32_t p = in[t];
+    if (p >= 0 && p < L) atomicOr(&bitmap[p >> 5], 1u << (p & 31));
+  }
+  __syncthreads();
+  // each thread owns a run of consecutive words, so its members are a run of
+  // consecutive output entries starting at its exclusive prefix
+  const int per = (nw + RECALL_THREADS - 1) / RECALL_THREADS;
+  const int w0 = min(nw, (int)threadIdx.x * per), w1 = min(nw, w0 + per);
+  uint32_t c = 0;
+  for (int w = w0; w < w1; ++w) c += __popc(bitmap[w]);
+  uint32_t total;
+  uint32_t pos = block_exclusive_scan(c, wsum, &total);
+  int32_t* out = rp.idx_out + q.out_off + (int64_t)g * q.out_count;
+  const uint32_t cap = (uint32_t)q.out_count;
+  for (int w = w0; w < w1; ++w) {
+    uint32_t b = bitmap[w];
+    while (b) {
+      const int bit = __ffs(b) - 1;
+      if (pos < cap) out[pos] = w * 32 + bit;
+      ++pos;
+      b &= b - 1u;
+    }
+  }
+  for (uint32_t t = total + threadIdx.x; t < cap; t += RECALL_THREADS) out[t] = -1;
+}
+
+// ==========================================================================
 // host-side shapes and launchers
 // ==========================================================================
 static int group_template(int G) { return G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : G <= 5 ? 5 : 8; }
@@ -1226,16 +1352,49 @@ size_t attn_smem_bytes(int dtype, int head_dim, int G, int nthr, bool mfma, bool
   return s;
 }
 
+// Workgroups of a persistent launch: as many as are resident at once (the
+// occupancy of this kernel, block size and LDS times the CU count), at most
+// one per item.  Cached per (device, kernel, block size, LDS bytes).
+static int resident_grid(const void* kernel, int nthr, size_t smem, int nitems) {
+  struct Entry {
+    int dev;
+    const void* kernel;
+    int nthr;
+    size_t smem;
+    int blocks;
+  };
+  static std::mutex mu;
+  static std::vector<Entry> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return nitems;
+  std::lock_guard<std::mutex> lock(mu);
+  for (const Entry& e : cache)
+    if (e.dev == dev && e.kernel == kernel && e.nthr == nthr && e.smem == smem)
+      return std::min(nitems, e.blocks);
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, nthr, smem) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      per_cu < 1 || cus < 1) {
+    (void)hipGetLastError();
+    return nitems;  // one workgroup per item still drains the plan
+  }
+  cache.push_back(Entry{dev, kernel, nthr, smem, per_cu * cus});
+  return std::min(nitems, per_cu * cus);
+}
+
 template <int D, typename T>
 static hipError_t launch_attn_g(const AttnParams& p, int nitems, int nthr, size_t smem, bool draft,
                                 hipStream_t st) {
   const int G = p.G;
 #define SPA_ATTN(GMV)                                                                           \
   do {                                                                                          \
+    const void* kern = draft ? reinterpret_cast<const void*>(&attn_kernel_draft<D, T, GMV>)     \
+                             : reinterpret_cast<const void*>(&attn_kernel<D, T, GMV>);          \
+    const int grid = resident_grid(kern, nthr, smem, nitems);                                   \
     if (draft)                                                                                  \
-      hipLaunchKernelGGL((attn_kernel_draft<D, T, GMV>), dim3(nitems), dim3(nthr), smem, st, p); \
+      hipLaunchKernelGGL((attn_kernel_draft<D, T, GMV>), dim3(grid), dim3(nthr), smem, st, p);   \
     else                                                                                        \
-      hipLaunchKernelGGL((attn_kernel<D, T, GMV>), dim3(nitems), dim3(nthr), smem, st, p);       \
+      hipLaunchKernelGGL((attn_kernel<D, T, GMV>), dim3(grid), dim3(nthr), smem, st, p);         \
     return hipGetLastError();                                                                   \
   } while (0)
   if constexpr (sizeof(T) == 2) {
@@ -1250,9 +1409,11 @@ static hipError_t launch_attn_g(const AttnParams& p, int nitems, int nthr, size_
 #undef SPA_ATTN
 }
 
-hipError_t launch_attn(const AttnParams& p, int dtype, int head_dim, int nitems, int nthr,
+hipError_t launch_attn(const AttnParams& params, int dtype, int head_dim, int nitems, int nthr,
                        size_t smem, bool draft, hipStream_t st) {
   if (nitems == 0) return hipSuccess;
+  AttnParams p = params;
+  p.n_items = nitems;
   if (dtype == 0) {
     if (head_dim == 128) return launch_attn_g<128, uint16_t>(p, nitems, nthr, smem, draft, st);
     return launch_attn_g<64, uint16_t>(p, nitems, nthr, smem, draft, st);
@@ -1264,6 +1425,17 @@ hipError_t launch_attn(const AttnParams& p, int dtype, int head_dim, int nitems,
 hipError_t launch_select(const SelectParams& sp, int nitems, hipStream_t st) {
   if (nitems == 0) return hipSuccess;
   hipLaunchKernelGGL(select_kernel, dim3(nitems), dim3(SELECT_THREADS), 0, st, sp);
+  return hipGetLastError();
+}
+
+size_t recall_smem_bytes(int max_len) {
+  const size_t nw = ((size_t)(max_len + 31) / 32 + 3) / 4 * 4;
+  return (nw + RECALL_THREADS / 64) * 4;
+}
+
+hipError_t launch_recall(const RecallParams& rp, int nblocks, size_t smem, hipStream_t st) {
+  if (nblocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(recall_kernel, dim3(nblocks), dim3(RECALL_THREADS), smem, st, rp);
   return hipGetLastError();
 }
 

@@ -23,6 +23,8 @@ struct AttnParams {
   float* part_ml;
   int32_t Hq, Hkv, G, k;
   float sm_scale;
+  int32_t ticket_set;  // item counter of this launch, in [0, TICKET_SETS)
+  int32_t n_items;     // records at items; set by launch_attn
 };
 
 struct PostParams {
@@ -43,6 +45,14 @@ struct SelectParams {
   int32_t* idx_out;
 };
 
+struct RecallParams {
+  const RecallReq* reqs;  // pinned host plan, read in place
+  const int32_t* idx_in;
+  int32_t* idx_out;
+  int32_t Hkv;
+  int32_t n_sink, n_recent;
+};
+
 // LDS bytes the attention kernel needs for a launch shape.
 size_t attn_smem_bytes(int dtype, int head_dim, int G, int nthr, bool mfma, bool valu,
                        int max_chunk);
@@ -53,5 +63,8 @@ hipError_t launch_attn(const AttnParams& p, int dtype, int head_dim, int nitems,
 hipError_t launch_post(const PostParams& p, int dtype, int head_dim, int nitems, size_t smem,
                        hipStream_t st);
 hipError_t launch_select(const SelectParams& sp, int nitems, hipStream_t st);
+// LDS bytes of the recallable-index launch for the longest context of a batch.
+size_t recall_smem_bytes(int max_len);
+hipError_t launch_recall(const RecallParams& rp, int nblocks, size_t smem, hipStream_t st);
 
 }  // namespace spa

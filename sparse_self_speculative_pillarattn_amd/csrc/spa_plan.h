@@ -57,6 +57,21 @@ struct PostItem {
   int64_t pbar_off;    // POST_AVG: element offset of the (r, g) averaged scores
 };
 
+// ---- recallable index launch ------------------------------------------------
+// One record per request (32 bytes); the launch runs one workgroup per
+// (request, KV head).
+struct RecallReq {
+  int32_t L;          // current context length of the request
+  int32_t in_count;   // stored entries per KV head
+  int32_t out_count;  // output entries per KV head (members, then -1)
+  int32_t pad_;
+  int64_t in_off;     // element offset of the stored [H_kv][in_count] list
+  int64_t out_off;    // element offset of the output [H_kv][out_count] list
+};
+
+constexpr int MAX_RECALL_LEN = 1 << 20;  // positions covered by one LDS bitmap (128 KB)
+
+constexpr int TICKET_SETS = 32;        // attention item counters: (plan slot, launch) pairs
 constexpr int AVG_SPAN = 1024;         // positions per averaging item
 constexpr int VERIFY_MAX_CHUNK = 2048;
 constexpr int DRAFT_MAX_CHUNK = 2048;

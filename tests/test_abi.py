@@ -173,3 +173,57 @@ def test_other_entry_points_validate(lib, small_split):
     io, iop = _arr([0, 4000], np.int64)
     assert lib.spa_draft_attn(C.byref(lay), 2, lp, FAKE, cp, iop, FAKE, FAKE, FAKE, FAKE, FAKE,
                               FAKE, FAKE, 0, None) == bd.SPA_ERR_WORKSPACE_TOO_SMALL
+
+
+# --------------------------------------------------------------------------- #
+# spa_recall_index argument checks
+# --------------------------------------------------------------------------- #
+def _recall(lib, B=2, Hkv=2, lens=(100, 50), S=4, W=8, inc=(10, 5), inoff=(0, 100),
+            outc=None, outoff=(1000, 2000), in_ptr=0x10000, out_ptr=0x10000, null=()):
+    if outc is None:
+        outc = [bd.recall_length(L, n, S, W) for L, n in zip(lens, inc)]
+    len_a, len_p = _arr(lens, np.int32)
+    inc_a, inc_p = _arr(inc, np.int32)
+    ino_a, ino_p = _arr(inoff, np.int64)
+    outc_a, outc_p = _arr(outc, np.int32)
+    outo_a, outo_p = _arr(outoff, np.int64)
+    args = dict(lens=len_p, inc=inc_p, inoff=ino_p, idx_in=C.c_void_p(in_ptr), outc=outc_p,
+                outoff=outo_p, idx_out=C.c_void_p(out_ptr))
+    for n in null:
+        args[n] = None
+    return lib.spa_recall_index(B, Hkv, args["lens"], S, W, args["inc"], args["inoff"],
+                                args["idx_in"], args["outc"], args["outoff"], args["idx_out"],
+                                None)
+
+
+def test_recall_length_formula():
+    assert bd.recall_length(100, 10, 4, 8) == 22
+    assert bd.recall_length(100, 95, 4, 8) == 100       # never more than L
+    assert bd.recall_length(10, 0, 50, 0) == 10          # sinks cover everything
+    assert bd.recall_length(10, 0, 6, 6) == 10           # sinks and window overlap
+    assert bd.recall_length(1, 0, 0, 0) == 1             # at least one entry
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(S=-1), bd.SPA_ERR_INVALID_ARG),
+    (dict(W=-2), bd.SPA_ERR_INVALID_ARG),
+    (dict(Hkv=0), bd.SPA_ERR_INVALID_ARG),
+    (dict(B=-1), bd.SPA_ERR_INVALID_ARG),
+    (dict(lens=(0, 50)), bd.SPA_ERR_INVALID_ARG),
+    (dict(lens=((1 << 20) + 1, 50)), bd.SPA_ERR_UNSUPPORTED),
+    (dict(inc=(-1, 5)), bd.SPA_ERR_INVALID_ARG),
+    (dict(outc=(21, 17)), bd.SPA_ERR_INVALID_ARG),            # first needs 22
+    (dict(inoff=(-4, 100)), bd.SPA_ERR_INVALID_ARG),
+    (dict(outoff=(1000, 1030)), bd.SPA_ERR_INVALID_ARG),      # output lists overlap
+    (dict(outoff=(90, 2000)), bd.SPA_ERR_INVALID_ARG),        # output over a stored list
+    (dict(null=("idx_in",)), bd.SPA_ERR_INVALID_ARG),
+    (dict(null=("outc",)), bd.SPA_ERR_INVALID_ARG),
+    (dict(null=("idx_out",)), bd.SPA_ERR_INVALID_ARG),
+])
+def test_recall_invalid_arguments(lib, kw, code):
+    assert _recall(lib, **kw) == code
+    assert lib.spa_last_error()
+
+
+def test_recall_empty_batch_is_a_noop(lib):
+    assert _recall(lib, B=0) == bd.SPA_OK
