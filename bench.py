@@ -204,7 +204,7 @@ def sparsity_sweep(w, dev, steps: int, warmup: int):
         us = _time_steps(bufs.step, steps, warmup)
         bd.profile_reset()
         bd.profile_enable((1 << len(bd.PROF_NAMES)) - 1)
-        for _ in range(5):
+        for _ in range(10):
             bufs.step()
         torch.cuda.synchronize()
         bd.profile_enable(0)

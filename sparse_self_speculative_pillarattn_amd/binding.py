@@ -268,9 +268,28 @@ class StepBuffers:
         self.h_idx_off = np.ascontiguousarray(batch.idx_off, dtype=np.int64)
         self.h_logits_off = np.ascontiguousarray(np.maximum(batch.logits_off, 0), dtype=np.int64)
 
+        self._key = None
+        self._args = None
+
+    def _marshal(self):
+        """The ctypes arguments of one call (all but the stream), rebuilt only
+        when an output, index or workspace tensor has been replaced."""
+        key = (id(self.idx), id(self.o), id(self.lse), id(self.logits), id(self.ws))
+        if key != self._key:
+            b = self.batch
+            host = [np.ascontiguousarray(a) for a in (self.h_is_verify, self.h_seq_lens,
+                                                       self.h_q_indptr, self.h_idx_count,
+                                                       self.h_idx_off, self.h_logits_off)]
+            self._host = host
+            hp = [C.c_void_p(a.ctypes.data) for a in host]
+            self._args = (C.byref(self.lay), int(b.B), int(b.w.spec_k), hp[0], hp[1], hp[2],
+                          _dptr(b.page_table), _dptr(b.q), _dptr(b.k_pool), _dptr(b.v_pool),
+                          hp[3], hp[4], _dptr(self.idx), _dptr(self.o), _dptr(self.lse),
+                          _dptr(self.logits), hp[5], int(self.avg_row_begin),
+                          int(self.avg_row_count), _dptr(self.ws),
+                          self.ws.numel() * self.ws.element_size())
+            self._key = key
+        return self._args
+
     def step(self):
-        b = self.batch
-        unified_step(self.lay, b.B, b.w.spec_k, self.h_is_verify, self.h_seq_lens,
-                     self.h_q_indptr, b.page_table, b.q, b.k_pool, b.v_pool, self.h_idx_count,
-                     self.h_idx_off, self.idx, self.o, self.lse, self.logits, self.h_logits_off,
-                     self.ws, self.avg_row_begin, self.avg_row_count)
+        _check(load().spa_unified_step(*self._marshal(), _stream(self.batch.q)))

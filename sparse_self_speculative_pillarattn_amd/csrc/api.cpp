@@ -3,10 +3,9 @@
 //
 // A call turns the host metadata into a work plan -- one record per workgroup
 // -- written into a slot of a pinned host ring that the kernels read in place
-// (no copy is enqueued).  The attention plan lists its items longest first (8
-// byte-balanced queues, interleaved); attention workgroups draw the next item
-// from a per-launch device counter as they start, so work flows to whichever
-// XCD frees first.  A call enqueues at most three launches: the attention of
+// (no copy is enqueued).  The attention plan lists its items longest first;
+// persistent attention workgroups draw the next item from a per-launch device
+// counter, so work flows to whichever XCD frees first.  A call enqueues at most three launches: the attention of
 // every request, the post-pass (split-K merges and score averaging), then the
 // top-K selection.
 #include <hip/hip_runtime.h>
@@ -35,7 +34,6 @@ std::atomic<int32_t> g_overlap{0};
 
 constexpr int DEFAULT_VERIFY_CHUNK = 2048;  // fewer split-K partials; drafts fill the XCD queues
 constexpr int DEFAULT_DRAFT_CHUNK = 1024;
-constexpr int NUM_XCD = 8;
 
 int32_t fail(int32_t code, const std::string& msg) {
   g_err = msg;
@@ -60,24 +58,21 @@ struct Shape {
   float scale = 0.f;
 };
 
-// A call's work plan.  plan_size() fixes every count, offset and the XCD of
-// each (request, KV head); plan_write() then writes the records straight into
-// the pinned slot, so the host touches each record once.
+// A call's work plan.  plan_size() fixes every count, offset and the item
+// order; plan_write() then writes the records straight into the pinned slot,
+// so the host touches each record once.
 struct Plan {
   bool attn = false, topk = false;
   std::vector<int32_t> order;   // requests by estimated bytes, descending
-  std::vector<uint8_t> xcd;     // XCD queue of (r, g)
   std::vector<int32_t> nchunk;  // split-K chunks of request r
   std::vector<int64_t> part0;   // first split-K partial row of (r, 0); heads follow
   int max_nchunk = 1;           // most split-K chunks of any merged request
-  int qlen[8] = {0};            // items per XCD queue
-  int n_items = 0;              // attention records, NOP padding included
+  int n_items = 0;              // attention records
   // split: a mixed batch runs its draft items in a second attention launch on
   // a side stream, concurrently with verify attention, merge, averaging and
   // top-K on the caller's stream
   bool split = false;
-  int qlen_d[8] = {0};
-  int n_items_d = 0;            // draft launch records, NOP padding included
+  int n_items_d = 0;            // draft launch records
   int n_merge_d = 0;            // draft merges, run after the join
   int n_merge = 0, n_avg = 0, n_sel = 0;
   int64_t part_rows = 0;
@@ -141,7 +136,7 @@ int draft_chunk() {
 int avg_parts(int L) { return (L + AVG_SPAN - 1) / AVG_SPAN; }
 int64_t pbar_row(int L) { return (L + 3) / 4 * 4; }  // rows start 16-byte aligned
 
-// Counts, offsets and the XCD balance of the attention (attn) and/or PillarAttn
+// Counts, offsets and the item order of the attention (attn) and/or PillarAttn
 // selection (topk) plan for `rq`.
 int32_t plan_size(const Shape& s, const std::vector<Req>& rq, bool attn, bool topk, Plan* pl) {
   const int B = (int)rq.size();
@@ -186,34 +181,15 @@ int32_t plan_size(const Shape& s, const std::vector<Req>& rq, bool attn, bool to
       bytes[r] = v ? (double)q.L * (2.0 * D * esz + 4 + 4.0 * rows_v * G)
                    : (double)q.nlist * (2.0 * D * esz + 8);
     }
-    // longest-processing-time assignment of (r, g) to the XCD queues; all heads
-    // of a request weigh the same, so sorting the requests suffices
+    // persistent workgroups draw items in record order, so the records go
+    // longest first: requests by estimated bytes (all heads of a request weigh
+    // the same), each request's items together
     pl->order.resize(B);
     for (int r = 0; r < B; ++r) pl->order[r] = r;
     std::stable_sort(pl->order.begin(), pl->order.end(),
                      [&](int a, int b) { return bytes[a] > bytes[b]; });
-    pl->xcd.resize((size_t)B * Hkv);
-    double load[NUM_XCD] = {0}, load_d[NUM_XCD] = {0};
-    for (int r : pl->order) {
-      const bool own = pl->split && !rq[r].verify;  // the draft launch's queues
-      double* ld = own ? load_d : load;
-      int* ql = own ? pl->qlen_d : pl->qlen;
-      for (int g = 0; g < Hkv; ++g) {
-        int x = 0;
-        for (int y = 1; y < NUM_XCD; ++y)
-          if (ld[y] < ld[x]) x = y;
-        ld[x] += bytes[r];
-        ql[x] += nitems[r];
-        pl->xcd[(size_t)r * Hkv + g] = (uint8_t)x;
-      }
-    }
-    int maxlen = 0, maxlen_d = 0;
-    for (int x = 0; x < NUM_XCD; ++x) {
-      maxlen = std::max(maxlen, pl->qlen[x]);
-      maxlen_d = std::max(maxlen_d, pl->qlen_d[x]);
-    }
-    pl->n_items = maxlen * NUM_XCD;
-    pl->n_items_d = maxlen_d * NUM_XCD;
+    for (int r = 0; r < B; ++r)
+      ((pl->split && !rq[r].verify) ? pl->n_items_d : pl->n_items) += Hkv * nitems[r];
   }
   int64_t pbar = 0;
   if (topk)
@@ -282,7 +258,7 @@ void plan_write(const Shape& s, const std::vector<Req>& rq, const Plan& pl, char
   if (pl.attn) {
     Item* items_v = reinterpret_cast<Item*>(h + pl.h_items);
     Item* items_d = reinterpret_cast<Item*>(h + pl.h_items_d);
-    int cur_v[NUM_XCD] = {0}, cur_dr[NUM_XCD] = {0};
+    int cur_v = 0, cur_dr = 0;
     for (int r : pl.order) {
       const Req& q = rq[r];
       const bool v = q.verify;
@@ -292,9 +268,8 @@ void plan_write(const Shape& s, const std::vector<Req>& rq, const Plan& pl, char
       const int nq = (v && !bf16) ? rows_v : 1;
       const int64_t head_rows = (int64_t)nc * (v ? rows_v : 1) * G;
       Item* items = (pl.split && !v) ? items_d : items_v;
-      int* cur = (pl.split && !v) ? cur_dr : cur_v;
+      int& cur = (pl.split && !v) ? cur_dr : cur_v;
       for (int g = 0; g < Hkv; ++g) {
-        const int x = pl.xcd[(size_t)r * Hkv + g];
         Item it;
         std::memset(&it, 0, sizeof it);
         it.kind = v ? KIND_VERIFY : KIND_DRAFT;
@@ -312,17 +287,9 @@ void plan_write(const Shape& s, const std::vector<Req>& rq, const Plan& pl, char
             it.split = c;
             it.begin = c * chunk;
             it.end = std::min(span, (c + 1) * chunk);
-            items[(size_t)cur[x]++ * NUM_XCD + x] = it;
+            items[cur++] = it;
           }
       }
-    }
-    Item nop;
-    std::memset(&nop, 0, sizeof nop);
-    nop.kind = KIND_NOP;
-    const int maxlen = pl.n_items / NUM_XCD, maxlen_d = pl.n_items_d / NUM_XCD;
-    for (int x = 0; x < NUM_XCD; ++x) {
-      for (int i = cur_v[x]; i < maxlen; ++i) items_v[(size_t)i * NUM_XCD + x] = nop;
-      for (int i = cur_dr[x]; i < maxlen_d; ++i) items_d[(size_t)i * NUM_XCD + x] = nop;
     }
   }
   // post-pass: the averaging chunks of every verify (r, g), then the split-K

@@ -8,7 +8,7 @@ namespace spa {
 
 // ---- attention launch ------------------------------------------------------
 enum : int32_t {
-  KIND_NOP = 0,     // padding item (keeps the XCD interleave aligned); exits at once
+  KIND_NOP = 0,     // no work (the planner writes none; a workgroup that draws one moves on)
   KIND_VERIFY = 1,  // full attention of the verify rows over positions [begin, end)
   KIND_DRAFT = 2,   // sparse attention of one draft row over list entries [begin, end)
 };
