@@ -51,6 +51,9 @@ def _load(mutant: int = 0):
     lib.oracle_recall_index.argtypes = [C.c_int, C.c_int, C.c_int, C.c_int, _i32p, C.c_int,
                                         _i32p]
     lib.oracle_recall_index.restype = C.c_int
+    lib.oracle_list_quality.argtypes = [C.c_int, C.c_int, C.c_int, _f64p, _f64p, C.c_int, _i32p,
+                                        C.c_int, _i32p, _f64p, _f64p]
+    lib.oracle_list_quality.restype = C.c_int
     lib.oracle_mutant_id.restype = C.c_int
     _LIBS[mutant] = lib
     return lib
@@ -133,6 +136,25 @@ class Oracle:
         if u < 0:
             raise ValueError(f"oracle_recall_index failed ({u})")
         return out[:int(cap)], u
+
+    def list_quality(self, logits, lse, lists, T):
+        """logits [Hq][L] and lse [Hq] of one query row; lists [Hkv][n].
+        Returns (top [Hq][T] ascending, coverage [Hq], recall [Hq])."""
+        logits = np.ascontiguousarray(logits, np.float64)
+        lse = np.ascontiguousarray(lse, np.float64).reshape(-1)
+        Hq, L = logits.shape
+        lists = np.ascontiguousarray(lists, np.int32)
+        Hkv = lists.shape[0]
+        n = lists.shape[1] if lists.ndim == 2 else 0
+        lists = lists.reshape(-1) if lists.size else np.zeros((1,), np.int32)
+        top = np.empty((Hq, int(T)), np.int32)
+        cov = np.empty((Hq,), np.float64)
+        rec = np.empty((Hq,), np.float64)
+        rc = self.lib.oracle_list_quality(Hq, Hkv, L, logits, lse, n, lists, int(T), top.reshape(-1),
+                                          cov, rec)
+        if rc:
+            raise ValueError(f"oracle_list_quality failed ({rc})")
+        return top, cov, rec
 
     # -- whole batch --------------------------------------------------------------
     def step(self, *, k, Hq, Hkv, sm_scale, is_verify, seq_lens, q_indptr, page_table, q,

@@ -23,6 +23,11 @@
  *   oracle_step            the whole unified batch: verify requests run the
  *                          first three, draft requests the last (review,
  *                          "Unified batch scheduler + fused attention kernel").
+ *   oracle_list_quality    how well an index list covers one query row's exact
+ *                          attention: attention coverage (softmax mass on the
+ *                          list) and recall of the row's exact top-T (review,
+ *                          核心方法 / PillarAttn, the comparison with Quest:
+ *                          top-10 recall and attention coverage).
  *   oracle_recall_index    the recallable per-head index of a draft step: sink
  *                          tokens, the stored important positions and the
  *                          recent tokens (arxiv.org 2607.27735 as rendered on
@@ -383,6 +388,66 @@ int oracle_recall_index(int L, int n_sink, int n_recent, int n_in, const int32_t
   if (u > cap) return -1;
   for (int t = u; t < cap; ++t) out[t] = MUT(16) ? 0 : -1;
   return u;
+}
+
+/* ---- quality of an index list for one query row -----------------------------
+ * logits [Hq][L] (-inf where hidden) and lse [Hq] of the row; list [Hkv][n]
+ * positions per KV head (entries outside [0, L) name no position, repeats
+ * count once).  Query head h reads the list of KV head h / G, with softmax
+ * p_h[j] = exp(logits[h][j] - lse[h]):
+ *   coverage[h] = sum of p_h over the list's distinct valid positions;
+ *   top[h][0..T) = the T positions of largest p_h (ties to the lower
+ *                  position), ascending;
+ *   recall[h]   = |top[h] intersected with the list| / T.
+ * Returns 0, or -1 when T is not in [1, L].
+ */
+int oracle_list_quality(int Hq, int Hkv, int L, const double* logits, const double* lse, int n,
+                        const int32_t* list, int T, int32_t* top, double* coverage,
+                        double* recall) {
+  if (T < 1 || T > L) return -1;
+  const int G = Hq / Hkv;
+  unsigned char* member = (unsigned char*)malloc((size_t)L);
+  double* p = (double*)malloc(sizeof(double) * (size_t)L);
+  if (!member || !p) {
+    free(member);
+    free(p);
+    return -2;
+  }
+  for (int h = 0; h < Hq; ++h) {
+    const int g = MUT(3) ? h % Hkv : h / G;
+    memset(member, 0, (size_t)L);
+    for (int t = 0; t < n; ++t) {
+      const int32_t pos = list[(int64_t)g * n + t];
+      if (pos >= 0 && pos < L) member[pos] = 1;
+    }
+    double cov = 0.0;
+    for (int j = 0; j < L; ++j) {
+      const double l = logits[(int64_t)h * L + j];
+      p[j] = (l == -INFINITY) ? 0.0 : exp(l - (MUT(17) ? 0.0 : lse[h]));
+    }
+    if (MUT(18)) {
+      for (int t = 0; t < n; ++t) {
+        const int32_t pos = list[(int64_t)g * n + t];
+        if (pos >= 0 && pos < L) cov += p[pos];
+      }
+    } else {
+      for (int j = 0; j < L; ++j)
+        if (member[j]) cov += p[j];
+    }
+    coverage[h] = cov;
+    int32_t* th = top + (int64_t)h * T;
+    if (oracle_topk(L, T, p, th)) {
+      free(member);
+      free(p);
+      return -2;
+    }
+    int hits = 0;
+    for (int t = 0; t < T; ++t) hits += member[th[t]];
+    recall[h] = (double)hits / (double)T;
+  }
+  free(member);
+  free(p);
+  return 0;
 }
 
 int oracle_mutant_id(void) { return ORACLE_MUTANT; }

@@ -345,8 +345,72 @@ def pin_recall_set_properties(orc):
             assert p < S or p >= L - W or p in valid, (trial, p)
 
 
+# --------------------------------------------------------------------------- #
+# quality of an index list (attention coverage, recall of the exact top-T)
+# --------------------------------------------------------------------------- #
+def _row(seed, Hq=4, L=60, hide=0):
+    rng = np.random.default_rng(seed)
+    lg = torch.from_numpy(rng.standard_normal((Hq, L)) * 2.0)
+    if hide:
+        lg[:, L - hide:] = -math.inf
+    return lg, torch.logsumexp(lg, dim=1)
+
+
+def pin_quality_full_and_empty_lists(orc):
+    """Every position covers the whole softmax mass and recalls everything;
+    a list of positions outside the context covers nothing."""
+    lg, lse = _row(1, hide=5)
+    full = np.stack([np.arange(60), np.arange(60)]).astype(np.int32)
+    _, cov, rec = orc.list_quality(lg.numpy(), lse.numpy(), full, 7)
+    _close(cov, np.ones(4), 1e-12, "coverage of every position")
+    _close(rec, np.ones(4), 0, "recall of every position")
+    bad = np.array([[-1, 60, 99], [60, -5, 1 << 30]], np.int32)
+    _, cov, rec = orc.list_quality(lg.numpy(), lse.numpy(), bad, 7)
+    _close(cov, np.zeros(4), 0, "coverage of no position")
+    _close(rec, np.zeros(4), 0, "recall of no position")
+
+
+def pin_quality_vs_torch(orc):
+    """Coverage equals the softmax mass PyTorch assigns to the list's positions,
+    the top-T equals torch.topk (no ties here), and recall is the overlap."""
+    Hq, Hkv, L, T = 6, 2, 80, 10
+    lg, lse = _row(2, Hq=Hq, L=L)
+    rng = np.random.default_rng(3)
+    lists = np.stack([np.sort(rng.choice(L, 20, replace=False)) for _ in range(Hkv)]).astype(np.int32)
+    top, cov, rec = orc.list_quality(lg.numpy(), lse.numpy(), lists, T)
+    prob = torch.softmax(lg, dim=1)
+    for h in range(Hq):
+        g = h // (Hq // Hkv)
+        _close(cov[h], float(prob[h, torch.from_numpy(lists[g]).long()].sum()), 1e-12, f"coverage h{h}")
+        want = np.sort(torch.topk(prob[h], T).indices.numpy())
+        assert np.array_equal(top[h], want), (h, top[h], want)
+        _close(rec[h], len(set(want.tolist()) & set(lists[g].tolist())) / T, 0, f"recall h{h}")
+
+
+def pin_quality_ties_bruteforce(orc):
+    """Equal scores go to the lower position: brute force over all T-subsets
+    of a tiny row with many ties."""
+    L, T = 9, 4
+    lg = torch.tensor([[0.5, 1.0, 1.0, 0.2, 1.0, 0.5, -math.inf, 1.0, 0.2]], dtype=torch.float64)
+    lse = torch.logsumexp(lg, dim=1)
+    top, _, _ = orc.list_quality(lg.numpy(), lse.numpy(), np.array([[1]], np.int32), T)
+    assert np.array_equal(top[0], _brute_topk(lg[0].numpy(), T)), top
+
+
+def pin_quality_repeats_count_once(orc):
+    """Repeated list entries add their position's mass once."""
+    lg, lse = _row(4, Hq=2, L=30)
+    once = np.array([[3, 7, 11]], np.int32)
+    many = np.array([[3, 3, 7, 11, 11, 11]], np.int32)
+    _, c1, r1 = orc.list_quality(lg.numpy(), lse.numpy(), once, 3)
+    _, c2, r2 = orc.list_quality(lg.numpy(), lse.numpy(), many, 3)
+    _close(c1, c2, 1e-14, "coverage with repeats")
+    _close(r1, r2, 0, "recall with repeats")
+
+
 ALL_PINS = [pin_verify_vs_sdpa, pin_uniform_keys, pin_one_and_two_keys, pin_dump_consistency,
             pin_average, pin_topk_bruteforce, pin_topk_vs_torch, pin_topk_special,
             pin_draft_full_list, pin_draft_invariances, pin_draft_matches_last_verify_row,
             pin_bf16_widening, pin_recall_special_cases, pin_recall_newest_tokens,
-            pin_recall_set_properties]
+            pin_recall_set_properties, pin_quality_full_and_empty_lists, pin_quality_vs_torch,
+            pin_quality_ties_bruteforce, pin_quality_repeats_count_once]

@@ -21,6 +21,8 @@ MUTANTS = {
     14: "stored positions past the context clamped to the last position",
     15: "one sink too many",
     16: "recallable index padded with position 0 instead of -1",
+    17: "list coverage from exp(logit) without the LSE",
+    18: "list coverage counts repeated entries once per repeat",
 }
 
 
