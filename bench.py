@@ -327,6 +327,76 @@ def recall_measure(w, dev, steps: int, warmup: int, n_sink: int, n_recent: int):
                             "algorithmic_bytes_per_launch": rec_bytes}}), flush=True)
 
 
+def quality_measure(w, dev, steps: int, warmup: int, top_t: int):
+    """How well index lists capture the drafts' exact attention: each draft
+    query is scored over its whole context (spa_verify_attn, spec_k = 1, the
+    query in row 1), then spa_list_quality measures the stored list (stale:
+    the workload's pillar drift applies) and a fresh list (PillarAttn's top-K
+    of the draft row itself, averaged over its GQA group, same K)."""
+    b = synth.make_batch(w, device=dev)
+    Hq, Hkv, d = w.num_qo_heads, w.num_kv_heads, w.head_dim
+    dra = [r for r in range(b.B) if not b.is_verify[r]]
+    nd = len(dra)
+    q2 = torch.stack([torch.stack([b.q[b.q_indptr[r]], b.q[b.q_indptr[r]]]) for r in dra])
+    q2 = q2.reshape(-1, Hq, d).contiguous()
+    pt = torch.stack([b.page_table[r] for r in dra]).contiguous()
+    lens = [b.seq_lens[r] for r in dra]
+    K = [b.idx_count[r] for r in dra]
+    loff = np.concatenate([[0], np.cumsum([2 * Hq * L for L in lens])[:-1]]).astype(np.int64)
+    logits = torch.empty((int(sum(2 * Hq * L for L in lens)),), device=dev)
+    lse = torch.empty((2 * nd, Hq), device=dev)
+    o = torch.empty_like(q2)
+    lay = bd.layout(Hq, Hkv, d, b.q.dtype, b.num_slots, b.stride)
+    ws = bd.workspace(bd.workspace_bytes(lay, nd, 1, [1] * nd, lens, K), dev)
+    ioff = np.concatenate([[0], np.cumsum([Hkv * k for k in K])[:-1]]).astype(np.int64)
+    stale = torch.cat([b.idx[b.idx_off[r]:b.idx_off[r] + Hkv * b.idx_count[r]] for r in dra])
+    fresh = torch.zeros_like(stale)
+    qws = bd.workspace(bd.list_quality_workspace_bytes(nd, Hq, lens), dev)
+    top = torch.empty((nd, Hq, top_t), dtype=torch.int32, device=dev)
+    cov = torch.empty((nd, Hq), device=dev)
+    rec = torch.empty((nd, Hq), device=dev)
+
+    def score():
+        bd.verify_attn(lay, nd, 1, lens, pt, q2, b.k_pool, b.v_pool, o, lse, logits, loff, ws)
+
+    def quality(lists):
+        bd.list_quality(nd, 1, Hq, Hkv, 1, top_t, lens, logits, loff, lse, K, ioff, lists, top, cov,
+                        rec, qws)
+
+    score()
+    bd.pillar_topk(nd, 1, Hq, Hkv, 1, 1, lens, K, logits, loff, lse, fresh, ioff, ws)
+    out = {"quality": w.name, "n_draft": nd, "top_t": top_t,
+           "pillar_drift": w.pillar_drift, "mean_L": round(float(np.mean(lens)), 1),
+           "mean_K": round(float(np.mean(K)), 1)}
+    for name, lists in (("stale", stale), ("fresh", fresh)):
+        quality(lists)
+        torch.cuda.synchronize()
+        out[name] = {"coverage_mean": round(float(cov.mean()), 4),
+                     "coverage_p10": round(float(torch.quantile(cov.flatten(), 0.1)), 4),
+                     f"recall@{top_t}_mean": round(float(rec.mean()), 4),
+                     f"recall@{top_t}_p10": round(float(torch.quantile(rec.flatten(), 0.1)), 4)}
+    out["score_launch_us_back_to_back"] = round(_time_steps(score, steps, warmup), 1)
+    out["quality_launch_us_back_to_back"] = round(_time_steps(lambda: quality(stale), steps, warmup), 1)
+    bd.profile_reset()
+    bd.profile_enable(1 << bd.PROF_QUALITY)
+    for _ in range(10):
+        quality(stale)
+    torch.cuda.synchronize()
+    bd.profile_enable(0)
+    n, ms = bd.profile_read(bd.PROF_QUALITY)
+    q_us = ms / max(n, 1) * 1e3
+    # the row's logits read once, its softmax written once and read back by the
+    # selection, the lists read once; top-T, coverage and recall written
+    qbytes = int(sum(Hq * L * 4 * 3 for L in lens) + sum(Hkv * k * 4 for k in K)
+                 + nd * Hq * (top_t * 4 + 8))
+    out["quality_launch_us"] = round(q_us, 2)
+    out["quality_roofline"] = {"bound": "hbm", "achieved": round(qbytes / (q_us * 1e-6) / 1e9, 1),
+                               "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                               "frac": round(qbytes / (q_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+                               "algorithmic_bytes_per_launch": qbytes}
+    print(json.dumps(out), flush=True)
+
+
 # --------------------------------------------------------------------------- #
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
@@ -346,6 +416,9 @@ def main():
     ap.add_argument("--recall", type=int, nargs=2, default=None, metavar=("SINKS", "RECENT"),
                     help="only measure the recallable index (SINKS sink tokens, RECENT recent "
                          "tokens) on the workload's drafts and print its JSON line")
+    ap.add_argument("--quality", type=int, default=0, metavar="T",
+                    help="only measure stale and fresh index lists against the drafts' exact "
+                         "attention (coverage, recall of the top T) and print its JSON line")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 5 plain device copies of MIB MiB (reference for the HBM "
                          "byte counters) and exit")
@@ -380,6 +453,9 @@ def main():
         return
     if args.recall:
         recall_measure(w, dev, args.steps, args.warmup, args.recall[0], args.recall[1])
+        return
+    if args.quality:
+        quality_measure(w, dev, args.steps, args.warmup, args.quality)
         return
     print(f"[bench] generating {w.name} on {dev}", file=sys.stderr, flush=True)
     b = synth.make_batch(w, device=dev)

@@ -176,6 +176,35 @@ int32_t spa_recall_index(int32_t B, int32_t num_kv_heads, const int32_t* h_seq_l
                          const int32_t* h_out_count, const int64_t* h_out_off, int32_t* d_idx_out,
                          void* stream);
 
+/* Quality of index lists against one query row's exact attention.  Review
+ * of SparseSpec, 核心方法 / PillarAttn, the comparison with Quest: PillarAttn
+ * is judged by top-10 recall and attention coverage.  The row is row `row` of
+ * B requests whose logits and LSE came from spa_verify_attn with this spec_k
+ * (request r: logits [(spec_k+1)][H_q][L_r] at h_logits_off[r], LSE rows
+ * r*(spec_k+1) ... of d_lse [B(spec_k+1)][H_q]); with spec_k = 1 and a draft
+ * query placed in row 1, row 1 sees the draft's whole context.  For query
+ * head h of request r, with p_h = exp(logit - LSE) over positions [0, L_r)
+ * and the list of KV head h / G at d_list + h_list_off[r] + g*h_list_count[r]
+ * (entries outside [0, L_r) name no position; repeats count once):
+ *   d_top      [B][H_q][top_t]: the top_t positions of largest p_h (ties to
+ *              the lower position), ascending;
+ *   d_coverage [B][H_q]: the sum of p_h over the list's positions;
+ *   d_recall   [B][H_q]: |top_t positions on the list| / top_t.
+ * 1 <= top_t <= L_r <= 1048576.  d_ws: 16-byte aligned, at least
+ * spa_list_quality_workspace_bytes(B, H_q, h_seq_lens) bytes (the rows' p_h;
+ * contents on entry do not matter).  One launch. */
+int32_t spa_list_quality(int32_t B, int32_t spec_k, int32_t num_qo_heads, int32_t num_kv_heads,
+                         int32_t row, int32_t top_t, const int32_t* h_seq_lens,
+                         const float* d_logits, const int64_t* h_logits_off, const float* d_lse,
+                         const int32_t* h_list_count, const int64_t* h_list_off,
+                         const int32_t* d_list, int32_t* d_top, float* d_coverage,
+                         float* d_recall, void* d_ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes of spa_list_quality: sum over r of H_q * (L_r rounded up to
+ * a multiple of 4) * 4.  Returns 0 for B <= 0 or a NULL pointer. */
+size_t spa_list_quality_workspace_bytes(int32_t B, int32_t num_qo_heads,
+                                        const int32_t* h_seq_lens);
+
 /* Process-wide switch for spa_unified_step on a batch holding both verify
  * and draft requests (default 0): 1 runs its draft attention as a second
  * launch on a library-owned stream (default priority, one per device) that is
@@ -198,8 +227,8 @@ int32_t spa_set_split(int32_t verify_chunk_tokens, int32_t draft_chunk_entries);
  * averaging; bit 2: the top-K selection launch; bit 3: the draft attention
  * launch of an overlapped unified step; bit 4: all attention of a call, from
  * the start of its first attention launch to the end of its last, over both
- * streams when overlapped; bit 5: the spa_recall_index launch); 0 turns it
- * off.
+ * streams when overlapped; bit 5: the spa_recall_index launch; bit 6: the
+ * spa_list_quality launch); 0 turns it off.
  * Returns SPA_OK. */
 int32_t spa_profile_enable(int32_t kernel_mask);
 

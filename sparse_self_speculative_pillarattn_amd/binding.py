@@ -28,11 +28,13 @@ SPA_F32 = 1
 
 EXPORTED = ("spa_abi_version", "spa_last_error", "spa_workspace_bytes", "spa_verify_attn",
             "spa_pillar_topk", "spa_draft_attn", "spa_unified_step", "spa_set_split", "spa_set_overlap",
-            "spa_profile_enable", "spa_profile_read", "spa_profile_reset", "spa_recall_index")
+            "spa_profile_enable", "spa_profile_read", "spa_profile_reset", "spa_recall_index",
+            "spa_list_quality", "spa_list_quality_workspace_bytes")
 
 # kernel indices of the per-launch timer
-PROF_ATTN, PROF_POST, PROF_SELECT, PROF_ATTN_DRAFT, PROF_ATTN_SPAN, PROF_RECALL = range(6)
-PROF_NAMES = ("attn", "post", "select", "attn_draft", "attn_span", "recall")
+(PROF_ATTN, PROF_POST, PROF_SELECT, PROF_ATTN_DRAFT, PROF_ATTN_SPAN, PROF_RECALL,
+ PROF_QUALITY) = range(7)
+PROF_NAMES = ("attn", "post", "select", "attn_draft", "attn_span", "recall", "quality")
 
 
 class SpaError(RuntimeError):
@@ -81,6 +83,11 @@ def load(path: str = LIB_PATH):
     lib.spa_unified_step.restype = i32
     lib.spa_recall_index.argtypes = [i32, i32, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp]
     lib.spa_recall_index.restype = i32
+    lib.spa_list_quality.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp,
+                                     vp, vp, vp, sz, vp]
+    lib.spa_list_quality.restype = i32
+    lib.spa_list_quality_workspace_bytes.argtypes = [i32, i32, vp]
+    lib.spa_list_quality_workspace_bytes.restype = sz
     lib.spa_profile_enable.argtypes = [i32]
     lib.spa_profile_enable.restype = i32
     lib.spa_profile_read.argtypes = [i32, C.POINTER(C.c_int64), C.POINTER(C.c_double)]
@@ -232,6 +239,24 @@ def recall_index(B, num_kv_heads, seq_lens, n_sink, n_recent, in_count, in_off,
         int(B), int(num_kv_heads), h.arr(seq_lens, np.int32), int(n_sink), int(n_recent),
         h.arr(in_count, np.int32), h.arr(in_off, np.int64), _dptr(idx_in),
         h.arr(out_count, np.int32), h.arr(out_off, np.int64), _dptr(idx_out), _stream(idx_out)))
+
+
+def list_quality_workspace_bytes(B, num_qo_heads, seq_lens) -> int:
+    h = _Host()
+    return int(load().spa_list_quality_workspace_bytes(int(B), int(num_qo_heads),
+                                                       h.arr(seq_lens, np.int32)))
+
+
+def list_quality(B, spec_k, num_qo_heads, num_kv_heads, row, top_t, seq_lens, logits, logits_off,
+                 lse, list_count, list_off, lists: Optional[torch.Tensor], top: torch.Tensor,
+                 coverage: torch.Tensor, recall: torch.Tensor, ws: torch.Tensor):
+    h = _Host()
+    _check(load().spa_list_quality(
+        int(B), int(spec_k), int(num_qo_heads), int(num_kv_heads), int(row), int(top_t),
+        h.arr(seq_lens, np.int32), _dptr(logits), h.arr(logits_off, np.int64), _dptr(lse),
+        h.arr(list_count, np.int32), h.arr(list_off, np.int64), _dptr(lists), _dptr(top),
+        _dptr(coverage), _dptr(recall), _dptr(ws), ws.numel() * ws.element_size(),
+        _stream(logits)))
 
 
 def workspace(nbytes: int, device) -> torch.Tensor:

@@ -368,7 +368,8 @@ enum {
   PROF_ATTN_DRAFT = 3,  // the draft attention launch of an overlapped unified step
   PROF_ATTN_SPAN = 4,   // all attention of a call: first launch start to last launch end
   PROF_RECALL = 5,      // the recallable-index launch
-  PROF_N = 6
+  PROF_QUALITY = 6,     // the list-quality launch
+  PROF_N = 7
 };
 std::mutex g_prof_mu;
 std::atomic<int32_t> g_prof_mask{0};
@@ -1108,6 +1109,103 @@ int32_t spa_recall_index(int32_t B, int32_t num_kv_heads, const int32_t* h_seq_l
     e = launch_recall(rp, B * num_kv_heads, recall_smem_bytes(max_len), st);
   }
   if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("recall launch: ") + hipGetErrorString(e));
+  e = hipEventRecord(slot->ev, st);
+  if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("event record: ") + hipGetErrorString(e));
+  slot->pending = true;
+  return SPA_OK;
+}
+
+size_t spa_list_quality_workspace_bytes(int32_t B, int32_t num_qo_heads,
+                                        const int32_t* h_seq_lens) {
+  if (B <= 0 || num_qo_heads <= 0 || !h_seq_lens) return 0;
+  size_t total = 0;
+  for (int r = 0; r < B; ++r)
+    total += (size_t)num_qo_heads * (size_t)((std::max(h_seq_lens[r], 0) + 3) & ~3) * 4;
+  return total;
+}
+
+int32_t spa_list_quality(int32_t B, int32_t spec_k, int32_t num_qo_heads, int32_t num_kv_heads,
+                         int32_t row, int32_t top_t, const int32_t* h_seq_lens,
+                         const float* d_logits, const int64_t* h_logits_off, const float* d_lse,
+                         const int32_t* h_list_count, const int64_t* h_list_off,
+                         const int32_t* d_list, int32_t* d_top, float* d_coverage,
+                         float* d_recall, void* d_ws, size_t ws_bytes, void* stream) {
+  if (B < 0) return fail(SPA_ERR_INVALID_ARG, "B < 0");
+  if (num_qo_heads <= 0 || num_kv_heads <= 0 || num_qo_heads % num_kv_heads != 0)
+    return fail(SPA_ERR_INVALID_ARG, "head counts must be positive with H_q % H_kv == 0");
+  if (spec_k < 1) return fail(SPA_ERR_INVALID_ARG, "spec_k < 1");
+  if (row < 0 || row > spec_k) return fail(SPA_ERR_INVALID_ARG, "row must lie in [0, spec_k]");
+  if (top_t < 1) return fail(SPA_ERR_INVALID_ARG, "top_t < 1");
+  if (B == 0) return SPA_OK;
+  if (!h_seq_lens || !d_logits || !h_logits_off || !d_lse || !h_list_count || !h_list_off ||
+      !d_top || !d_coverage || !d_recall)
+    return fail(SPA_ERR_INVALID_ARG, "a required pointer is NULL");
+  if ((int64_t)B * num_qo_heads > 0x7fffffff)
+    return fail(SPA_ERR_UNSUPPORTED, "more than 2^31 - 1 (request, query head) pairs");
+  int max_len = 1;
+  bool any_list = false;
+  std::vector<std::pair<int64_t, int64_t>> seg;
+  for (int r = 0; r < B; ++r) {
+    const int32_t L = h_seq_lens[r];
+    const std::string who = "request " + std::to_string(r);
+    if (L < spec_k + 1) return fail(SPA_ERR_INVALID_ARG, who + ": L < spec_k + 1");
+    if (L > MAX_RECALL_LEN) return fail(SPA_ERR_UNSUPPORTED, who + ": L above 1048576");
+    if (top_t > L) return fail(SPA_ERR_INVALID_ARG, who + ": top_t > L");
+    if (h_list_count[r] < 0) return fail(SPA_ERR_INVALID_ARG, who + ": list count < 0");
+    if (h_logits_off[r] < 0 || h_list_off[r] < 0) return fail(SPA_ERR_INVALID_ARG, who + ": negative offset");
+    any_list |= h_list_count[r] > 0;
+    max_len = std::max<int>(max_len, L);
+    seg.push_back({h_logits_off[r], (int64_t)(spec_k + 1) * num_qo_heads * L});
+  }
+  if (any_list && !d_list) return fail(SPA_ERR_INVALID_ARG, "d_list is NULL");
+  int32_t rc = check_segments(std::move(seg), "logits offsets");
+  if (rc) return rc;
+  const size_t need = spa_list_quality_workspace_bytes(B, num_qo_heads, h_seq_lens);
+  if (ws_bytes < need)
+    return fail(SPA_ERR_WORKSPACE_TOO_SMALL,
+                "workspace of " + std::to_string(ws_bytes) + " bytes, need " + std::to_string(need));
+  if (!d_ws) return fail(SPA_ERR_INVALID_ARG, "d_ws is NULL");
+  if ((reinterpret_cast<uintptr_t>(d_ws) & 15) != 0)
+    return fail(SPA_ERR_INVALID_ARG, "d_ws must be 16-byte aligned");
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  std::lock_guard<std::mutex> lock(g_ring_mu);
+  Plan pl;
+  pl.h_bytes = (size_t)B * sizeof(QualityReq);
+  PlanSlot* slot = nullptr;
+  rc = acquire_slot(pl, &slot);
+  if (rc) return rc;
+  QualityReq* rec = reinterpret_cast<QualityReq*>(slot->host);
+  int64_t p_off = 0;
+  for (int r = 0; r < B; ++r) {
+    const int32_t L = h_seq_lens[r];
+    rec[r].L = L;
+    rec[r].n = h_list_count[r];
+    rec[r].logits_off = h_logits_off[r];
+    rec[r].list_off = h_list_off[r];
+    rec[r].p_off = p_off;
+    rec[r].lse_row = r * (spec_k + 1) + row;
+    rec[r].pad_ = 0;
+    p_off += (int64_t)num_qo_heads * ((L + 3) & ~3);
+  }
+  QualityParams qp;
+  qp.reqs = reinterpret_cast<const QualityReq*>(slot->dev);
+  qp.logits = d_logits;
+  qp.lse = d_lse;
+  qp.list = d_list;
+  qp.p = static_cast<float*>(d_ws);
+  qp.top = d_top;
+  qp.coverage = d_coverage;
+  qp.recall = d_recall;
+  qp.Hq = num_qo_heads;
+  qp.G = num_qo_heads / num_kv_heads;
+  qp.row = row;
+  qp.T = top_t;
+  hipError_t e;
+  {
+    ProfScope ps(PROF_QUALITY, st);
+    e = launch_quality(qp, B * num_qo_heads, quality_smem_bytes(max_len), st);
+  }
+  if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("quality launch: ") + hipGetErrorString(e));
   e = hipEventRecord(slot->ev, st);
   if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("event record: ") + hipGetErrorString(e));
   slot->pending = true;

@@ -1329,6 +1329,76 @@ __global__ void __launch_bounds__(RECALL_THREADS) recall_kernel(RecallParams rp)
 }
 
 // ==========================================================================
+// quality of an index list for one query row
+// ==========================================================================
+// How much of a query row's exact attention an index list captures: the
+// softmax mass on the list's positions (attention coverage) and the share of
+// the row's exact top-T positions the list holds (recall), the two measures
+// by which the review of SparseSpec compares PillarAttn with Quest (核心方法 /
+// PillarAttn).  One workgroup per (request, query head h): the list of KV head
+// h / G is marked in an LDS bitmap (repeats count once, entries outside [0, L)
+// name no position), the row's softmax p = exp(logit - LSE) goes to the
+// workspace while the marked positions' mass is summed, and the top-T of p is
+// chosen with the same radix selection as PillarAttn's top-K.
+constexpr int QUALITY_THREADS = SELECT_THREADS;
+constexpr size_t SELECT_SMEM = (24 + 16 * 64 + SELECT_FINISH) * 4;
+
+__global__ void __launch_bounds__(QUALITY_THREADS) quality_kernel(QualityParams qp) {
+  extern __shared__ __attribute__((aligned(16))) uint32_t member[];
+  const int r = blockIdx.x / qp.Hq;
+  const int h = blockIdx.x - r * qp.Hq;
+  const int g = h / qp.G;
+  const QualityReq q = qp.reqs[r];
+  const int L = q.L;
+  const int nw = (L + 31) >> 5;
+  const size_t bitmap_bytes = ((size_t)nw * 4 + 15) / 16 * 16;
+  char* sel_smem = reinterpret_cast<char*>(member) + bitmap_bytes;
+  float* red = reinterpret_cast<float*>(sel_smem + SELECT_SMEM);  // [QUALITY_THREADS / 64]
+  const int tid = threadIdx.x;
+  for (int w = tid; w < nw; w += QUALITY_THREADS) member[w] = 0u;
+  __syncthreads();
+  const int32_t* lst = qp.list + q.list_off + (int64_t)g * q.n;
+  for (int t = tid; t < q.n; t += QUALITY_THREADS) {
+    const int32_t pos = lst[t];
+    if (pos >= 0 && pos < L) atomicOr(&member[pos >> 5], 1u << (pos & 31));
+  }
+  __syncthreads();
+  const float* lg = qp.logits + q.logits_off + ((int64_t)qp.row * qp.Hq + h) * L;
+  const float lse = qp.lse[(int64_t)q.lse_row * qp.Hq + h];
+  float* p = qp.p + q.p_off + (int64_t)h * ((L + 3) & ~3);
+  float cov = 0.f;
+  for (int j = tid; j < L; j += QUALITY_THREADS) {
+    const float l = lg[j];
+    const float v = (l == NEG_INF || lse == NEG_INF) ? 0.f : fast_exp2((l - lse) * LOG2E);
+    p[j] = v;
+    if ((member[j >> 5] >> (j & 31)) & 1u) cov += v;
+  }
+  for (int off = 32; off > 0; off >>= 1) cov += __shfl_xor(cov, off);
+  if ((tid & 63) == 0) red[tid >> 6] = cov;
+  __syncthreads();  // also orders the p row's stores before the selection reads it
+  int32_t* top = qp.top + ((int64_t)r * qp.Hq + h) * qp.T;
+  select_topk<SELECT_KPT>(p, L, qp.T, top, sel_smem);
+  __syncthreads();
+  if (tid < 64) {
+    float c = 0.f;
+    for (int w = tid; w < QUALITY_THREADS / 64; w += 64) c += red[w];
+    int hits = 0;
+    for (int t = tid; t < qp.T; t += 64) {
+      const int32_t pos = top[t];
+      if (pos >= 0 && pos < L) hits += (int)((member[pos >> 5] >> (pos & 31)) & 1u);
+    }
+    for (int off = 32; off > 0; off >>= 1) {
+      c += __shfl_xor(c, off);
+      hits += __shfl_xor(hits, off);
+    }
+    if (tid == 0) {
+      qp.coverage[(int64_t)r * qp.Hq + h] = c;
+      qp.recall[(int64_t)r * qp.Hq + h] = (float)hits / (float)qp.T;
+    }
+  }
+}
+
+// ==========================================================================
 // host-side shapes and launchers
 // ==========================================================================
 static int group_template(int G) { return G <= 1 ? 1 : G <= 2 ? 2 : G <= 4 ? 4 : G <= 5 ? 5 : 8; }
@@ -1425,6 +1495,17 @@ hipError_t launch_attn(const AttnParams& params, int dtype, int head_dim, int ni
 hipError_t launch_select(const SelectParams& sp, int nitems, hipStream_t st) {
   if (nitems == 0) return hipSuccess;
   hipLaunchKernelGGL(select_kernel, dim3(nitems), dim3(SELECT_THREADS), 0, st, sp);
+  return hipGetLastError();
+}
+
+size_t quality_smem_bytes(int max_len) {
+  const size_t bitmap = ((size_t)(max_len + 31) / 32 * 4 + 15) / 16 * 16;
+  return bitmap + SELECT_SMEM + (QUALITY_THREADS / 64) * 4;
+}
+
+hipError_t launch_quality(const QualityParams& qp, int nblocks, size_t smem, hipStream_t st) {
+  if (nblocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(quality_kernel, dim3(nblocks), dim3(QUALITY_THREADS), smem, st, qp);
   return hipGetLastError();
 }
 

@@ -53,6 +53,18 @@ struct RecallParams {
   int32_t n_sink, n_recent;
 };
 
+struct QualityParams {
+  const QualityReq* reqs;  // pinned host plan, read in place
+  const float* logits;
+  const float* lse;
+  const int32_t* list;
+  float* p;                // workspace: the scored rows' softmax
+  int32_t* top;            // [B][H_q][T]
+  float* coverage;         // [B][H_q]
+  float* recall;           // [B][H_q]
+  int32_t Hq, G, row, T;
+};
+
 // LDS bytes the attention kernel needs for a launch shape.
 size_t attn_smem_bytes(int dtype, int head_dim, int G, int nthr, bool mfma, bool valu,
                        int max_chunk);
@@ -65,6 +77,8 @@ hipError_t launch_post(const PostParams& p, int dtype, int head_dim, int nitems,
 hipError_t launch_select(const SelectParams& sp, int nitems, hipStream_t st);
 // LDS bytes of the recallable-index launch for the longest context of a batch.
 size_t recall_smem_bytes(int max_len);
+size_t quality_smem_bytes(int max_len);
+hipError_t launch_quality(const QualityParams& qp, int nblocks, size_t smem, hipStream_t st);
 hipError_t launch_recall(const RecallParams& rp, int nblocks, size_t smem, hipStream_t st);
 
 }  // namespace spa

@@ -71,6 +71,19 @@ struct RecallReq {
 
 constexpr int MAX_RECALL_LEN = 1 << 20;  // positions covered by one LDS bitmap (128 KB)
 
+// ---- list quality launch ------------------------------------------------------
+// One record per request (40 bytes); the launch runs one workgroup per
+// (request, query head).
+struct QualityReq {
+  int32_t L;          // context length: positions [0, L) of the scored row
+  int32_t n;          // list entries per KV head
+  int64_t logits_off; // element offset of the request's [rows][H_q][L] logits
+  int64_t list_off;   // element offset of the request's [H_kv][n] list
+  int64_t p_off;      // element offset of the request's [H_q][L rounded to 4] workspace rows
+  int32_t lse_row;    // LSE row of the scored row: [rows][H_q] with rows per request
+  int32_t pad_;
+};
+
 constexpr int TICKET_SETS = 32;        // attention item counters: (plan slot, launch) pairs
 constexpr int AVG_SPAN = 1024;         // positions per averaging item
 constexpr int VERIFY_MAX_CHUNK = 2048;

@@ -227,3 +227,53 @@ def test_recall_invalid_arguments(lib, kw, code):
 
 def test_recall_empty_batch_is_a_noop(lib):
     assert _recall(lib, B=0) == bd.SPA_OK
+
+
+# --------------------------------------------------------------------------- #
+# spa_list_quality argument checks
+# --------------------------------------------------------------------------- #
+def _quality(lib, B=2, k=1, Hq=8, Hkv=2, row=1, T=10, lens=(100, 50), loff=(0, 1600),
+             cnt=(5, 3), coff=(0, 10), ws_bytes=1 << 30, ws=0x10000, null=()):
+    len_a, len_p = _arr(lens, np.int32)
+    lo_a, lo_p = _arr(loff, np.int64)
+    c_a, c_p = _arr(cnt, np.int32)
+    co_a, co_p = _arr(coff, np.int64)
+    args = dict(lens=len_p, logits=FAKE, loff=lo_p, lse=FAKE, cnt=c_p, coff=co_p, lst=FAKE,
+                top=FAKE, cov=FAKE, rec=FAKE, ws=C.c_void_p(ws))
+    for n in null:
+        args[n] = None
+    return lib.spa_list_quality(B, k, Hq, Hkv, row, T, args["lens"], args["logits"], args["loff"],
+                                args["lse"], args["cnt"], args["coff"], args["lst"], args["top"],
+                                args["cov"], args["rec"], args["ws"], ws_bytes, None)
+
+
+def test_list_quality_workspace_formula(lib):
+    assert bd.list_quality_workspace_bytes(2, 8, [100, 50]) == 8 * 4 * (100 + 52)
+    assert bd.list_quality_workspace_bytes(0, 8, [100]) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=-1), bd.SPA_ERR_INVALID_ARG),
+    (dict(k=0), bd.SPA_ERR_INVALID_ARG),
+    (dict(Hq=6, Hkv=4), bd.SPA_ERR_INVALID_ARG),
+    (dict(row=2), bd.SPA_ERR_INVALID_ARG),
+    (dict(row=-1), bd.SPA_ERR_INVALID_ARG),
+    (dict(T=0), bd.SPA_ERR_INVALID_ARG),
+    (dict(T=51), bd.SPA_ERR_INVALID_ARG),                     # above the second request's L
+    (dict(lens=(1, 50), T=1), bd.SPA_ERR_INVALID_ARG),        # L < spec_k + 1
+    (dict(lens=((1 << 20) + 1, 50)), bd.SPA_ERR_UNSUPPORTED),
+    (dict(cnt=(-1, 3)), bd.SPA_ERR_INVALID_ARG),
+    (dict(loff=(0, 1000)), bd.SPA_ERR_INVALID_ARG),           # logits segments overlap
+    (dict(coff=(-2, 10)), bd.SPA_ERR_INVALID_ARG),
+    (dict(ws_bytes=100), bd.SPA_ERR_WORKSPACE_TOO_SMALL),
+    (dict(ws=0x10004), bd.SPA_ERR_INVALID_ARG),               # workspace not 16-byte aligned
+    (dict(null=("lst",)), bd.SPA_ERR_INVALID_ARG),
+    (dict(null=("top",)), bd.SPA_ERR_INVALID_ARG),
+])
+def test_list_quality_invalid_arguments(lib, kw, code):
+    assert _quality(lib, **kw) == code
+    assert lib.spa_last_error()
+
+
+def test_list_quality_empty_batch_is_a_noop(lib):
+    assert _quality(lib, B=0) == bd.SPA_OK
