@@ -53,6 +53,10 @@
  *               not matter and need no initialisation.  Calls that share one
  *               workspace must be ordered on one stream.
  *   Threads     Entry points may be called from several host threads.
+ *   Graphs      Calls are not capturable into HIP graphs: each call writes its
+ *               work plan into pinned host memory at call time (a replay would
+ *               read whatever a later call left there) and may wait on the
+ *               event of an earlier call that used the same plan buffer.
  *   B == 0      is a successful no-op.
  */
 #ifndef SPA_H_
