@@ -99,10 +99,10 @@ def _lists(rng, L, Hkv, kind):
     raise ValueError(kind)
 
 
-@pytest.mark.parametrize("T", [1, 10, 64])
-def test_list_quality_matches_oracle(oracle, T):
-    w = synth.Workload(name=f"quality-{T}", batch=6, num_qo_heads=16, num_kv_heads=4, head_dim=128,
-                       dtype="bf16", spec_k=8, sparsity=Fraction(1, 20),
+@pytest.mark.parametrize("T,dtype", [(1, "bf16"), (10, "bf16"), (64, "bf16"), (10, "f32")])
+def test_list_quality_matches_oracle(oracle, T, dtype):
+    w = synth.Workload(name=f"quality-{T}-{dtype}", batch=6, num_qo_heads=16, num_kv_heads=4,
+                       head_dim=128, dtype=dtype, spec_k=8, sparsity=Fraction(1, 20),
                        lengths=("uniform", 70, 2500), n_verify=0, seed=40 + T)
     b = synth.make_batch(w, is_verify=[False] * 6)
     bd_ = b.to(DEV)
