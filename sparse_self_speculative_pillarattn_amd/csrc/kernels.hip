@@ -943,6 +943,7 @@ __device__ __forceinline__ uint32_t row_or_u32(uint32_t v) {
 }
 
 constexpr int SELECT_FINISH = 64;  // candidates ranked directly by one wave
+constexpr int SELECT_BATCH = 4;    // chunks loaded per batch when a row is longer than one chunk
 
 // Top-K of L non-negative fp32 scores (their bit patterns order like the
 // values).  MSB-first radix select with 4-bit digits finds the K-th largest
@@ -958,7 +959,7 @@ constexpr int SELECT_FINISH = 64;  // candidates ranked directly by one wave
 //   - Once the bucket holding the K-th key has at most 64 keys, they are
 //     gathered into LDS and one wave ranks them directly.
 template <int KPT>
-__device__ void select_topk(const float* scores, int L, int K, int32_t* out, char* smem) {
+__device__ __forceinline__ void select_topk(const float* scores, int L, int K, int32_t* out, char* smem) {
   static_assert(KPT % 4 == 0 && KPT <= 8, "keys are loaded four at a time; nibble counters");
   uint32_t* sv = reinterpret_cast<uint32_t*>(smem);  // prefix, rem, bucket count, and/or
   uint32_t* wsum = sv + 8;                           // [16] block scans
@@ -971,24 +972,46 @@ __device__ void select_topk(const float* scores, int L, int K, int32_t* out, cha
   const bool resident = L <= span;
   const bool vec = (reinterpret_cast<uintptr_t>(scores) & 15) == 0;
   uint32_t key[KPT];
-  auto load = [&](int c0) {
+  auto load_into = [&](uint32_t (&dst)[KPT], int c0) {
     const int j0 = c0 + KPT * tid;
 #pragma unroll
     for (int m = 0; m < KPT; m += 4) {
       const int j = j0 + m;
       if (vec && j + 4 <= L) {
         const uint4 v = *reinterpret_cast<const uint4*>(keys + j);
-        key[m] = v.x;
-        key[m + 1] = v.y;
-        key[m + 2] = v.z;
-        key[m + 3] = v.w;
+        dst[m] = v.x;
+        dst[m + 1] = v.y;
+        dst[m + 2] = v.z;
+        dst[m + 3] = v.w;
       } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) key[m + e] = (j + e < L) ? keys[j + e] : 0u;
+        for (int e = 0; e < 4; ++e) dst[m + e] = (j + e < L) ? keys[j + e] : 0u;
       }
     }
   };
-  if (resident) load(0);
+  // Calls body(c0) for every chunk with its keys in key[].  Rows longer than
+  // one chunk are re-read on every walk, SELECT_BATCH chunks per batch of loads
+  // so that a walk costs one round trip per batch, not per chunk.
+  auto each_chunk = [&](auto&& body) {
+    if (resident) {
+      body(0);
+      return;
+    }
+    for (int c0 = 0; c0 < L; c0 += SELECT_BATCH * span) {
+      uint32_t kb[SELECT_BATCH][KPT];
+#pragma unroll
+      for (int q = 0; q < SELECT_BATCH; ++q) load_into(kb[q], c0 + q * span);
+#pragma unroll
+      for (int q = 0; q < SELECT_BATCH; ++q) {
+        if (c0 + q * span < L) {  // the same for every thread
+#pragma unroll
+          for (int m = 0; m < KPT; ++m) key[m] = kb[q][m];
+          body(c0 + q * span);
+        }
+      }
+    }
+  };
+  if (resident) load_into(key, 0);
   // bits shared by every key: AND and OR over the block
   if (tid == 0) {
     sv[4] = 0xffffffffu;
@@ -997,8 +1020,7 @@ __device__ void select_topk(const float* scores, int L, int K, int32_t* out, cha
   __syncthreads();
   {
     uint32_t va = 0xffffffffu, vo = 0u;
-    for (int c0 = 0; c0 < L; c0 += span) {
-      if (!resident) load(c0);
+    each_chunk([&](int c0) {
       const int j0 = c0 + KPT * tid;
 #pragma unroll
       for (int m = 0; m < KPT; ++m)
@@ -1006,7 +1028,7 @@ __device__ void select_topk(const float* scores, int L, int K, int32_t* out, cha
           va &= key[m];
           vo |= key[m];
         }
-    }
+    });
     va = row_and_u32(va);
     vo = row_or_u32(vo);
     if ((lane & 15) == 0) {
@@ -1030,8 +1052,8 @@ __device__ void select_topk(const float* scores, int L, int K, int32_t* out, cha
     uint32_t acc[16];  // per row of 16 lanes
 #pragma unroll
     for (int d = 0; d < 16; ++d) acc[d] = 0u;
-    for (int c0 = 0; c0 < L; c0 += span) {
-      if (!resident) load(c0);
+    each_chunk([&](int c0) {
+      (void)c0;
       // Positions past L hold key 0, the smallest value, and come after every
       // real position in the tie order, so counting them never moves the
       // K-th largest real key (K <= L); the compaction skips them.
@@ -1053,7 +1075,7 @@ __device__ void select_topk(const float* scores, int L, int K, int32_t* out, cha
       for (int q = 0; q < 4; ++q)
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[8 * (q >> 1) + 2 * e + (q & 1)] += (w[q] >> (8 * e)) & 255u;
-    }
+    });
     if ((lane & 15) == 0) {
       uint32_t* row = tab + 16 * (wave * 4 + (lane >> 4));
 #pragma unroll
@@ -1093,8 +1115,7 @@ __device__ void select_topk(const float* scores, int L, int K, int32_t* out, cha
     // gather the keys of the chosen bucket and rank them in one wave
     const uint32_t prefix = sv[0];
     uint32_t base = 0u;
-    for (int c0 = 0; c0 < L; c0 += span) {
-      if (!resident) load(c0);
+    each_chunk([&](int c0) {
       const int j0 = c0 + KPT * tid;
       uint32_t n = 0u;
 #pragma unroll
@@ -1105,7 +1126,7 @@ __device__ void select_topk(const float* scores, int L, int K, int32_t* out, cha
       for (int m = 0; m < KPT; ++m)
         if (j0 + m < L && (key[m] & mask) == prefix) ckey[pos++] = key[m];
       base += tot;
-    }
+    });
     __syncthreads();
     if (wave == 0) {
       const int nc = (int)sv[2];
@@ -1126,8 +1147,7 @@ __device__ void select_topk(const float* scores, int L, int K, int32_t* out, cha
   }
   const uint32_t tau = sv[0], rem = sv[1];
   uint32_t base_eq = 0, base_gt = 0;
-  for (int c0 = 0; c0 < L; c0 += span) {
-    if (!resident) load(c0);
+  each_chunk([&](int c0) {
     const int j0 = c0 + KPT * tid;
     uint32_t n_gt = 0, n_eq = 0;
 #pragma unroll
@@ -1157,7 +1177,7 @@ __device__ void select_topk(const float* scores, int L, int K, int32_t* out, cha
     }
     base_gt += tot & 0xffffu;
     base_eq += tot >> 16;
-  }
+  });
 }
 
 constexpr int POST_THREADS = 256;
@@ -1186,38 +1206,62 @@ __global__ void __launch_bounds__(POST_THREADS) post_kernel(PostParams p) {
   const int L = it.L;
   float* lse2_s = reinterpret_cast<float*>(smem);
   int64_t* rowoff_s = reinterpret_cast<int64_t*>(smem + (terms * 4 + 7) / 8 * 8);
-  for (int x = tid; x < terms; x += blockDim.x) {
-    const int i = a + x / G, hh = x % G;
-    const int rho = i * G + hh;
-    float lse;
-    if (it.nchunk == 1) {
-      lse = p.lse[(int64_t)(it.row0 + i) * Hq + it.g * G + hh];
-    } else {
-      // one pass: running max with the sum rescaled as it grows
+  if (it.nchunk == 1) {
+    for (int x = tid; x < terms; x += blockDim.x) {
+      const int i = a + x / G, hh = x % G;
+      lse2_s[x] = p.lse[(int64_t)(it.row0 + i) * Hq + it.g * G + hh] * LOG2E;
+      rowoff_s[x] = ((int64_t)i * Hq + it.g * G + hh) * L;
+    }
+  } else {
+    // A group of tpt threads (a power of two within one wave) per term: each
+    // combines up to 8 chunks' (m, l) per batch of loads, running max with the
+    // sum rescaled as it grows, then the group merges its partial pairs with
+    // lane shuffles.  One round trip for up to 8 tpt chunks.
+    int tpt = 1;
+    while (tpt < 64 && tpt * 2 * terms <= (int)blockDim.x) tpt *= 2;
+    const int sub = tid & (tpt - 1), ngrp = (int)blockDim.x / tpt;
+    const int ns = it.nchunk;
+    for (int x0 = 0; x0 < terms; x0 += ngrp) {  // the same trip count in every lane
+      const int x = x0 + tid / tpt;
+      const bool live = x < terms;
+      const int i = a + (live ? x : 0) / G, hh = (live ? x : 0) % G;
+      const int rho = i * G + hh;
       float mstar = NEG_INF, lsum = 0.f;
-      for (int s0 = 0; s0 < it.nchunk; s0 += 8) {
-        float mm[8], ll[8];
+      if (live)
+        for (int s0 = sub; s0 < ns; s0 += 8 * tpt) {
+          float mm[8], ll[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int s = min(s0 + u, it.nchunk - 1);
-          const int64_t pr = it.part_row0 + (int64_t)s * R + rho;
-          mm[u] = p.part_ml[2 * pr];
-          ll[u] = p.part_ml[2 * pr + 1];
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          if (s0 + u >= it.nchunk || mm[u] == NEG_INF) continue;
-          if (mm[u] > mstar) {
-            lsum = (mstar == NEG_INF) ? 0.f : lsum * fast_exp2((mstar - mm[u]) * LOG2E);
-            mstar = mm[u];
+          for (int u = 0; u < 8; ++u) {
+            const int s = min(s0 + u * tpt, ns - 1);
+            const int64_t pr = it.part_row0 + (int64_t)s * R + rho;
+            mm[u] = p.part_ml[2 * pr];
+            ll[u] = p.part_ml[2 * pr + 1];
           }
-          lsum = fmaf(ll[u], fast_exp2((mm[u] - mstar) * LOG2E), lsum);
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            if (s0 + u * tpt >= ns || mm[u] == NEG_INF) continue;
+            if (mm[u] > mstar) {
+              lsum = (mstar == NEG_INF) ? 0.f : lsum * fast_exp2((mstar - mm[u]) * LOG2E);
+              mstar = mm[u];
+            }
+            lsum = fmaf(ll[u], fast_exp2((mm[u] - mstar) * LOG2E), lsum);
+          }
+        }
+      for (int off = 1; off < tpt; off <<= 1) {
+        const float m2 = __shfl_xor(mstar, off), l2 = __shfl_xor(lsum, off);
+        const float mx = fmaxf(mstar, m2);
+        if (mx != NEG_INF) {
+          lsum = (mstar == NEG_INF ? 0.f : lsum * fast_exp2((mstar - mx) * LOG2E)) +
+                 (m2 == NEG_INF ? 0.f : l2 * fast_exp2((m2 - mx) * LOG2E));
+          mstar = mx;
         }
       }
-      lse = lsum > 0.f ? mstar + logf(lsum) : NEG_INF;
+      if (live && sub == 0) {
+        const float lse = lsum > 0.f ? mstar + logf(lsum) : NEG_INF;
+        lse2_s[x] = lse * LOG2E;
+        rowoff_s[x] = ((int64_t)i * Hq + it.g * G + hh) * L;
+      }
     }
-    lse2_s[x] = lse * LOG2E;
-    rowoff_s[x] = ((int64_t)i * Hq + it.g * G + hh) * L;
   }
   __syncthreads();
   const float* lg = p.logits + it.logits_off;
