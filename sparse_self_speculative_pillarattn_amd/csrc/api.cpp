@@ -32,7 +32,8 @@ std::atomic<int32_t> g_verify_chunk{0};
 std::atomic<int32_t> g_draft_chunk{0};
 std::atomic<int32_t> g_overlap{0};
 
-constexpr int DEFAULT_VERIFY_CHUNK = 2048;  // fewer split-K partials; drafts fill the XCD queues
+constexpr int DEFAULT_VERIFY_CHUNK = 2048;  // fewer split-K partials
+constexpr int MIN_AUTO_VERIFY_CHUNK = 512;
 constexpr int DEFAULT_DRAFT_CHUNK = 1024;
 
 int32_t fail(int32_t code, const std::string& msg) {
@@ -67,6 +68,7 @@ struct Plan {
   std::vector<int32_t> nchunk;  // split-K chunks of request r
   std::vector<int64_t> part0;   // first split-K partial row of (r, 0); heads follow
   int max_nchunk = 1;           // most split-K chunks of any merged request
+  int cv = DEFAULT_VERIFY_CHUNK;  // positions per verify item
   int n_items = 0;              // attention records
   // split: a mixed batch runs its draft items in a second attention launch on
   // a side stream, concurrently with verify attention, merge, averaging and
@@ -124,9 +126,44 @@ int32_t check_segments(std::vector<std::pair<int64_t, int64_t>> seg, const char*
   return SPA_OK;
 }
 
-int verify_chunk() {
-  int v = g_verify_chunk.load();
-  return v > 0 ? std::min(v, VERIFY_MAX_CHUNK) : DEFAULT_VERIFY_CHUNK;
+// Compute units of the current device (cached per device; 256 if the query fails).
+int device_cus() {
+  static std::mutex mu;
+  static std::vector<int> cus;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  std::lock_guard<std::mutex> lock(mu);
+  if ((int)cus.size() <= dev) cus.resize(dev + 1, 0);
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) {
+      (void)hipGetLastError();
+      n = 256;
+    }
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
+// Positions per verify item.  Unless set by spa_set_split: the longest of
+// 2048, 1024 and 512 that still gives the verify requests at least 1.5 items
+// per CU.  A batch with few or short verify requests then spreads its long
+// items over the chip instead of leaving most CUs to the drafts (the
+// Qwen3-1.7B-shaped batch: 119 -> 96 us), while larger batches keep the
+// longer chunks, which need fewer split-K partials.
+int verify_chunk(const std::vector<Req>& rq, int Hkv) {
+  const int v = g_verify_chunk.load();
+  if (v > 0) return std::min(v, VERIFY_MAX_CHUNK);
+  const int64_t target = 3 * (int64_t)device_cus() / 2;
+  int c = DEFAULT_VERIFY_CHUNK;
+  while (c > MIN_AUTO_VERIFY_CHUNK) {
+    int64_t n = 0;
+    for (const Req& q : rq)
+      if (q.verify) n += (q.L + c - 1) / c;
+    if (n * Hkv >= target) break;
+    c /= 2;
+  }
+  return c;
 }
 int draft_chunk() {
   int v = g_draft_chunk.load();
@@ -144,7 +181,8 @@ int32_t plan_size(const Shape& s, const std::vector<Req>& rq, bool attn, bool to
   const int rows_v = s.k + 1;
   const bool bf16 = s.dtype == SPA_BF16;
   const int esz = bf16 ? 2 : 4;
-  const int CV = verify_chunk(), CD = draft_chunk();
+  const int CV = verify_chunk(rq, Hkv), CD = draft_chunk();
+  pl->cv = CV;
   if (s.k > 255) return fail(SPA_ERR_UNSUPPORTED, "spec_k above 255");
   pl->attn = attn;
   pl->topk = topk;
@@ -254,7 +292,7 @@ void plan_write(const Shape& s, const std::vector<Req>& rq, const Plan& pl, char
   const int G = s.G, Hkv = s.Hkv;
   const int rows_v = s.k + 1;
   const bool bf16 = s.dtype == SPA_BF16;
-  const int CV = verify_chunk(), CD = draft_chunk();
+  const int CV = pl.cv, CD = draft_chunk();
   if (pl.attn) {
     Item* items_v = reinterpret_cast<Item*>(h + pl.h_items);
     Item* items_d = reinterpret_cast<Item*>(h + pl.h_items_d);
