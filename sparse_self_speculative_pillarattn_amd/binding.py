@@ -298,8 +298,9 @@ class StepBuffers:
 
     def _marshal(self):
         """The ctypes arguments of one call (all but the stream), rebuilt only
-        when an output, index or workspace tensor has been replaced."""
-        key = (id(self.idx), id(self.o), id(self.lse), id(self.logits), id(self.ws))
+        when an output, index or workspace buffer has moved or resized."""
+        key = (self.idx.data_ptr(), self.o.data_ptr(), self.lse.data_ptr(),
+               self.logits.data_ptr(), self.ws.data_ptr(), self.ws.numel() * self.ws.element_size())
         if key != self._key:
             b = self.batch
             host = [np.ascontiguousarray(a) for a in (self.h_is_verify, self.h_seq_lens,
