@@ -41,9 +41,12 @@
  *               1/sqrt(d)).  A list entry outside [0, L_r) is ignored; a row
  *               whose list holds no valid entry gets O = 0 and LSE = -inf.
  *               Top-K orders by (averaged score descending, position ascending).
- *   Errors      Every entry point returns an spa_status.  Arguments are checked
- *               on the host before anything is enqueued; on any non-OK return
- *               nothing was enqueued and spa_last_error() describes why.
+ *   Errors      Every entry point returns an spa_status and spa_last_error()
+ *               describes a non-OK one.  Arguments are checked on the host
+ *               before anything is enqueued, so SPA_ERR_INVALID_ARG,
+ *               SPA_ERR_UNSUPPORTED and SPA_ERR_WORKSPACE_TOO_SMALL leave the
+ *               stream untouched; SPA_ERR_HIP (a failed launch or runtime call)
+ *               may come after earlier launches of the same call were enqueued.
  *   Streams     Work is enqueued on `stream` (a hipStream_t; NULL = default
  *               stream) and the call returns without waiting.  Faults inside a
  *               kernel surface at the caller's next synchronisation.
@@ -51,7 +54,10 @@
  *               spa_workspace_bytes(...) bytes for the same batch; it holds
  *               split-K partials and averaged scores.  Its contents on entry do
  *               not matter and need no initialisation.  Calls that share one
- *               workspace must be ordered on one stream.
+ *               workspace must be ordered on one stream.  The size depends on
+ *               the split settings (spa_set_split) and, with the automatic
+ *               verify chunk, on the device's compute-unit count: ask on the
+ *               device and with the settings the call will use.
  *   Threads     Entry points may be called from several host threads.
  *   Graphs      Calls are not capturable into HIP graphs: each call writes its
  *               work plan into pinned host memory at call time (a replay would
