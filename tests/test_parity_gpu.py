@@ -342,3 +342,26 @@ def test_concurrent_streams_match_sequential():
         got = [to_np(t) for t in (bu.o, bu.lse, bu.logits, bu.idx)]
         for name, a, g in zip(("O", "LSE", "logits", "idx"), want, got):
             assert np.array_equal(a.view(np.uint8), g.view(np.uint8)), f"{name} differs"
+
+
+def test_stepbuffers_rebinds_replaced_buffers():
+    """Replacing the workspace and an output after a step rebinds them: the
+    next step writes the new buffers and gives the same bits."""
+    w = synth.Workload(name="rebind", batch=5, num_qo_heads=32, num_kv_heads=8, head_dim=128,
+                       dtype="bf16", spec_k=8, sparsity=Fraction(1, 20),
+                       lengths=("uniform", 500, 2500), n_verify=2, seed=61)
+    b = synth.make_batch(w, device=DEV)
+    bufs = bd.StepBuffers(b)
+    bufs.step()
+    torch.cuda.synchronize()
+    first = [to_np(t).copy() for t in (bufs.o, bufs.lse, bufs.logits, bufs.idx)]
+    old_ws, old_o = bufs.ws, bufs.o
+    bufs.ws = torch.full((old_ws.numel() + 4096,), 0xFF, dtype=torch.uint8, device=DEV)
+    bufs.o = torch.full_like(old_o, float("nan"))
+    old_o.fill_(0.0)
+    bufs.step()
+    torch.cuda.synchronize()
+    assert bool((old_o == 0).all()), "the replaced output was written"
+    second = [to_np(t) for t in (bufs.o, bufs.lse, bufs.logits, bufs.idx)]
+    for name, a, g in zip(("O", "LSE", "logits", "idx"), first, second):
+        assert np.array_equal(a.view(np.uint8), g.view(np.uint8)), f"{name} differs"
