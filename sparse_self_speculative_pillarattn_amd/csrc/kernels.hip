@@ -1385,6 +1385,7 @@ __global__ void __launch_bounds__(RECALL_THREADS) recall_kernel(RecallParams rp)
 // workspace while the marked positions' mass is summed, and the top-T of p is
 // chosen with the same radix selection as PillarAttn's top-K.
 constexpr int QUALITY_THREADS = SELECT_THREADS;
+constexpr int QUALITY_BATCH = 8;
 constexpr size_t SELECT_SMEM = (24 + 16 * 64 + SELECT_FINISH) * 4;
 
 __global__ void __launch_bounds__(QUALITY_THREADS) quality_kernel(QualityParams qp) {
@@ -1401,21 +1402,41 @@ __global__ void __launch_bounds__(QUALITY_THREADS) quality_kernel(QualityParams 
   const int tid = threadIdx.x;
   for (int w = tid; w < nw; w += QUALITY_THREADS) member[w] = 0u;
   __syncthreads();
+  // loads are issued QUALITY_BATCH at a time, so a row costs one round trip
+  // per batch rather than per element
   const int32_t* lst = qp.list + q.list_off + (int64_t)g * q.n;
-  for (int t = tid; t < q.n; t += QUALITY_THREADS) {
-    const int32_t pos = lst[t];
-    if (pos >= 0 && pos < L) atomicOr(&member[pos >> 5], 1u << (pos & 31));
+  for (int t0 = 0; t0 < q.n; t0 += QUALITY_BATCH * QUALITY_THREADS) {
+    int32_t pos[QUALITY_BATCH];
+#pragma unroll
+    for (int u = 0; u < QUALITY_BATCH; ++u) {
+      const int t = t0 + u * QUALITY_THREADS + tid;
+      pos[u] = t < q.n ? lst[t] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < QUALITY_BATCH; ++u)
+      if (pos[u] >= 0 && pos[u] < L) atomicOr(&member[pos[u] >> 5], 1u << (pos[u] & 31));
   }
   __syncthreads();
   const float* lg = qp.logits + q.logits_off + ((int64_t)qp.row * qp.Hq + h) * L;
   const float lse = qp.lse[(int64_t)q.lse_row * qp.Hq + h];
   float* p = qp.p + q.p_off + (int64_t)h * ((L + 3) & ~3);
   float cov = 0.f;
-  for (int j = tid; j < L; j += QUALITY_THREADS) {
-    const float l = lg[j];
-    const float v = (l == NEG_INF || lse == NEG_INF) ? 0.f : fast_exp2((l - lse) * LOG2E);
-    p[j] = v;
-    if ((member[j >> 5] >> (j & 31)) & 1u) cov += v;
+  for (int j0 = 0; j0 < L; j0 += QUALITY_BATCH * QUALITY_THREADS) {
+    float l[QUALITY_BATCH];
+#pragma unroll
+    for (int u = 0; u < QUALITY_BATCH; ++u) {
+      const int j = j0 + u * QUALITY_THREADS + tid;
+      l[u] = j < L ? lg[j] : NEG_INF;
+    }
+#pragma unroll
+    for (int u = 0; u < QUALITY_BATCH; ++u) {
+      const int j = j0 + u * QUALITY_THREADS + tid;
+      if (j < L) {
+        const float v = (l[u] == NEG_INF || lse == NEG_INF) ? 0.f : fast_exp2((l[u] - lse) * LOG2E);
+        p[j] = v;
+        if ((member[j >> 5] >> (j & 31)) & 1u) cov += v;
+      }
+    }
   }
   for (int off = 32; off > 0; off >>= 1) cov += __shfl_xor(cov, off);
   if ((tid & 63) == 0) red[tid >> 6] = cov;
