@@ -82,7 +82,7 @@ struct Plan {
   // pinned plan layout
   size_t h_items = 0, h_items_d = 0, h_post = 0, h_post_d = 0, h_sel = 0, h_bytes = 0;
   // workspace layout
-  size_t off_part_o = 0, off_part_ml = 0, off_pbar = 0, total = 0;
+  size_t off_part_o = 0, off_part_ml = 0, off_pbar = 0, off_plan = 0, total = 0;
   int nthr = 256;
   size_t smem = 0;
 };
@@ -282,6 +282,9 @@ int32_t plan_size(const Shape& s, const std::vector<Req>& rq, bool attn, bool to
   o = align_up(o + (size_t)part_rows * 2 * 4, 256);
   pl->off_pbar = o;
   o = align_up(o + (size_t)pbar * 4, 256);
+  // the attention launch copies the post-pass and selection records here
+  pl->off_plan = o;
+  if (attn) o = align_up(o + (pl->h_bytes - pl->h_post), 256);
   pl->total = o;
   return SPA_OK;
 }
@@ -641,6 +644,10 @@ int32_t run(const Shape& s, const std::vector<Req>& rq, const Plan& pl, const Bu
     // the slot is reused only after this call has finished, so its two item
     // counters are never shared by launches in flight
     p.ticket_set = 2 * static_cast<int32_t>(slot - g_ring);
+    // the launch on `st` moves the records of the launches that follow it
+    p.plan_src = reinterpret_cast<const uint4*>(plan + pl.h_post);
+    p.plan_dst = reinterpret_cast<uint4*>(ws + pl.off_plan);
+    p.plan_n16 = pl.n_items > 0 ? static_cast<int32_t>((pl.h_bytes - pl.h_post) / 16) : 0;
     ProfSpan span;
     span.start(st);
     if (pl.split) {
@@ -662,6 +669,7 @@ int32_t run(const Shape& s, const std::vector<Req>& rq, const Plan& pl, const Bu
       AttnParams pd = p;
       pd.items = reinterpret_cast<const Item*>(plan + pl.h_items_d);
       pd.ticket_set = p.ticket_set + 1;
+      pd.plan_n16 = 0;
       {
         ProfScope ps(PROF_ATTN_DRAFT, side->stream);
         e = launch_attn(pd, s.dtype, s.d, pl.n_items_d, pl.nthr, pl.smem, true, side->stream);
@@ -673,9 +681,15 @@ int32_t run(const Shape& s, const std::vector<Req>& rq, const Plan& pl, const Bu
     }
     span.finish();
   }
+  // records of the launches below: the workspace copy when the attention
+  // launch on `st` made one, else the pinned plan
+  auto post_rec = [&](size_t h_off) {
+    return reinterpret_cast<const PostItem*>(pl.n_items > 0 ? ws + pl.off_plan + (h_off - pl.h_post)
+                                                            : plan + h_off);
+  };
   if (n_post > 0) {
     PostParams pp;
-    pp.items = reinterpret_cast<const PostItem*>(plan + pl.h_post);
+    pp.items = post_rec(pl.h_post);
     pp.part_o = part_o;
     pp.part_ml = part_ml;
     pp.o = b.o;
@@ -695,7 +709,7 @@ int32_t run(const Shape& s, const std::vector<Req>& rq, const Plan& pl, const Bu
   }
   if (pl.n_sel > 0) {
     SelectParams sp;
-    sp.items = reinterpret_cast<const PostItem*>(plan + pl.h_sel);
+    sp.items = post_rec(pl.h_sel);
     sp.pbar = reinterpret_cast<const float*>(ws + pl.off_pbar);
     sp.idx_out = b.idx_out;
     {
@@ -709,7 +723,7 @@ int32_t run(const Shape& s, const std::vector<Req>& rq, const Plan& pl, const Bu
     if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("join: ") + hipGetErrorString(e));
     if (pl.n_merge_d > 0) {  // merges of drafts split into several chunks
       PostParams pp;
-      pp.items = reinterpret_cast<const PostItem*>(plan + pl.h_post_d);
+      pp.items = post_rec(pl.h_post_d);
       pp.part_o = part_o;
       pp.part_ml = part_ml;
       pp.o = b.o;

@@ -774,7 +774,21 @@ __device__ __forceinline__ void attn_loop(const AttnParams& p, char* smem) {
   __syncthreads();
   for (int k = 0;; k ^= 1) {
     const int item = s_item[k];
-    if (item >= p.n_items) break;  // the same value for the whole workgroup
+    if (item >= p.n_items) {  // the same value for the whole workgroup
+      // Out of work.  Every workgroup draws exactly one ticket past the last
+      // item; the first half of those draws (workgroups that run out while
+      // others still finish their last items) copy the post-pass and selection
+      // records from the pinned plan into the workspace, one contiguous run of
+      // 16-byte pieces per workgroup and round.  The launches after this one
+      // then read their records from device memory instead of across PCIe,
+      // where the read is on their critical path.
+      const int e = item - p.n_items;
+      const int nc = max(1, (int)gridDim.x / 2);
+      if (e < nc)
+        for (int c = e * (int)blockDim.x + (int)threadIdx.x; c < p.plan_n16; c += nc * (int)blockDim.x)
+          p.plan_dst[c] = p.plan_src[c];
+      break;
+    }
     const bool drew = attn_body<D, T, GM>(p, item, smem, &s_item[k ^ 1], wrap);
     if (!drew && threadIdx.x == 0)
       s_item[k ^ 1] = (int)atomicInc(&g_item_ticket[p.ticket_set], wrap);

@@ -25,6 +25,12 @@ struct AttnParams {
   float sm_scale;
   int32_t ticket_set;  // item counter of this launch, in [0, TICKET_SETS)
   int32_t n_items;     // records at items; set by launch_attn
+  // The post-pass and selection records of the call, copied by this launch
+  // from the pinned plan into the workspace (plan_n16 16-byte pieces; 0 = no
+  // copy), so that the short launches after it read them from device memory.
+  const uint4* plan_src;
+  uint4* plan_dst;
+  int32_t plan_n16;
 };
 
 struct PostParams {
