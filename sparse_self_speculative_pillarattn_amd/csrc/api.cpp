@@ -17,6 +17,7 @@
 #include <cstring>
 #include <mutex>
 #include <string>
+#include <thread>
 #include <vector>
 
 #include "spa.h"
@@ -495,11 +496,20 @@ struct ProfSpan {
 // after the event recorded behind that kernel completes.  When a plan outgrows
 // the slots, every pending slot is waited for and the arena is reallocated
 // once for all of them, so pinned allocation happens only when plans grow.
+//
+// A call whose pinned plan is last read by its attention launch and that
+// then runs a post-pass on the same stream does without the event: the
+// post-pass stores the call's sequence number into the slot's word of a small
+// mapped, coherent host array as it starts, and the host waits for that value
+// instead.  Recording an event costs the stream a gap of about 5 us before the
+// next call's first launch; the store costs nothing measurable.
+enum SlotWait : int { WAIT_NONE = 0, WAIT_EVENT = 1, WAIT_SIGNAL = 2 };
 struct PlanSlot {
   char* host = nullptr;
   char* dev = nullptr;
   hipEvent_t ev = nullptr;
-  bool pending = false;
+  int wait = WAIT_NONE;
+  uint64_t seq = 0;  // WAIT_SIGNAL: the value the post-pass stores
 };
 constexpr int RING = 16;
 static_assert(2 * RING <= TICKET_SETS, "two attention item counters per plan slot");
@@ -509,15 +519,43 @@ char* g_arena_host = nullptr;
 char* g_arena_dev = nullptr;
 size_t g_slot_cap = 0;
 unsigned g_ring_next = 0;
+uint64_t* g_done_host = nullptr;  // [RING], written by the device
+uint64_t* g_done_dev = nullptr;
+uint64_t g_seq = 0;
+
+int32_t wait_slot(PlanSlot& s) {
+  if (s.wait == WAIT_EVENT) {
+    const hipError_t e = hipEventSynchronize(s.ev);
+    if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("plan slot wait: ") + hipGetErrorString(e));
+  } else if (s.wait == WAIT_SIGNAL) {
+    const uint64_t* w = g_done_host + (&s - g_ring);
+    while (__atomic_load_n(w, __ATOMIC_ACQUIRE) < s.seq) std::this_thread::yield();
+  }
+  s.wait = WAIT_NONE;
+  return SPA_OK;
+}
 
 int32_t grow_arena(size_t need) {
   hipError_t e;
-  for (auto& s : g_ring)
-    if (s.pending) {
-      e = hipEventSynchronize(s.ev);
-      if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("plan slot wait: ") + hipGetErrorString(e));
-      s.pending = false;
+  for (auto& s : g_ring) {
+    const int32_t rc = wait_slot(s);
+    if (rc) return rc;
+  }
+  if (!g_done_host) {
+    void* h = nullptr;
+    e = hipHostMalloc(&h, RING * sizeof(uint64_t),
+                      hipHostMallocMapped | hipHostMallocPortable | hipHostMallocCoherent);
+    if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("pinned done words: ") + hipGetErrorString(e));
+    void* d = nullptr;
+    e = hipHostGetDevicePointer(&d, h, 0);
+    if (e != hipSuccess) {
+      (void)hipHostFree(h);
+      return fail(SPA_ERR_HIP, std::string("pinned done words mapping: ") + hipGetErrorString(e));
     }
+    std::memset(h, 0, RING * sizeof(uint64_t));
+    g_done_host = static_cast<uint64_t*>(h);
+    g_done_dev = static_cast<uint64_t*>(d);
+  }
   if (g_arena_host) (void)hipHostFree(g_arena_host);
   g_arena_host = g_arena_dev = nullptr;
   g_slot_cap = 0;
@@ -548,13 +586,16 @@ int32_t acquire_slot(const Plan& pl, PlanSlot** out) {
     if (rc) return rc;
   }
   PlanSlot& s = g_ring[g_ring_next++ % RING];
-  if (s.pending) {
-    e = hipEventSynchronize(s.ev);
-    if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("plan slot wait: ") + hipGetErrorString(e));
-    s.pending = false;
-  }
+  const int32_t rc = wait_slot(s);
+  if (rc) return rc;
+  s.seq = ++g_seq;
   if (!s.ev) {
-    e = hipEventCreateWithFlags(&s.ev, hipEventDisableTiming);
+    // The event only tells the host that the GPU has finished reading the
+    // slot (host memory, read by the kernels; nothing flows back through it),
+    // so it skips the system-scope fence: with the fence, each call's event
+    // wrote back the caches and delayed the next call's first launch by
+    // about 6 us.
+    e = hipEventCreateWithFlags(&s.ev, hipEventDisableTiming | hipEventDisableSystemFence);
     if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("event create: ") + hipGetErrorString(e));
   }
   *out = &s;
@@ -683,6 +724,9 @@ int32_t run(const Shape& s, const std::vector<Req>& rq, const Plan& pl, const Bu
   }
   // records of the launches below: the workspace copy when the attention
   // launch on `st` made one, else the pinned plan
+  // the post-pass reports the slot free when the attention launch on `st`
+  // was the plan's last reader (no side-stream launch)
+  const bool signal = pl.n_items > 0 && n_post > 0 && !pl.split;
   auto post_rec = [&](size_t h_off) {
     return reinterpret_cast<const PostItem*>(pl.n_items > 0 ? ws + pl.off_plan + (h_off - pl.h_post)
                                                             : plan + h_off);
@@ -700,6 +744,8 @@ int32_t run(const Shape& s, const std::vector<Req>& rq, const Plan& pl, const Bu
     pp.G = s.G;
     pp.avg_row_begin = avg_begin;
     pp.avg_row_count = avg_count;
+    pp.done = signal ? g_done_dev + (slot - g_ring) : nullptr;
+    pp.done_val = slot->seq;
     {
       ProfScope ps(PROF_POST, st);
       e = launch_post(pp, s.dtype, s.d, n_post,
@@ -734,6 +780,8 @@ int32_t run(const Shape& s, const std::vector<Req>& rq, const Plan& pl, const Bu
       pp.G = s.G;
       pp.avg_row_begin = avg_begin;
       pp.avg_row_count = avg_count;
+      pp.done = nullptr;
+      pp.done_val = 0;
       {
         ProfScope ps(PROF_POST, st);
         e = launch_post(pp, s.dtype, s.d, pl.n_merge_d, post_smem_bytes(0, pl.max_nchunk), st);
@@ -741,9 +789,13 @@ int32_t run(const Shape& s, const std::vector<Req>& rq, const Plan& pl, const Bu
       if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("draft merge launch: ") + hipGetErrorString(e));
     }
   }
+  if (signal) {
+    slot->wait = WAIT_SIGNAL;
+    return SPA_OK;
+  }
   e = hipEventRecord(slot->ev, st);
   if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("event record: ") + hipGetErrorString(e));
-  slot->pending = true;
+  slot->wait = WAIT_EVENT;
   return SPA_OK;
 }
 
@@ -1163,7 +1215,7 @@ int32_t spa_recall_index(int32_t B, int32_t num_kv_heads, const int32_t* h_seq_l
   if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("recall launch: ") + hipGetErrorString(e));
   e = hipEventRecord(slot->ev, st);
   if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("event record: ") + hipGetErrorString(e));
-  slot->pending = true;
+  slot->wait = WAIT_EVENT;
   return SPA_OK;
 }
 
@@ -1260,7 +1312,7 @@ int32_t spa_list_quality(int32_t B, int32_t spec_k, int32_t num_qo_heads, int32_
   if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("quality launch: ") + hipGetErrorString(e));
   e = hipEventRecord(slot->ev, st);
   if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("event record: ") + hipGetErrorString(e));
-  slot->pending = true;
+  slot->wait = WAIT_EVENT;
   return SPA_OK;
 }
 

@@ -1204,6 +1204,8 @@ __global__ void __launch_bounds__(POST_THREADS) post_kernel(PostParams p) {
   // dynamic LDS (post_smem_bytes): the (m, l) pairs of MERGE_ROWS rows, or the
   // LSE and logits row offset of every averaged term
   extern __shared__ __attribute__((aligned(16))) char smem[];
+  if (p.done && blockIdx.x == 0 && threadIdx.x == 0)
+    __hip_atomic_store(p.done, p.done_val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
   const PostItem it = p.items[blockIdx.x];
   if (it.kind == POST_NOP) return;
   if (it.kind == POST_MERGE) {

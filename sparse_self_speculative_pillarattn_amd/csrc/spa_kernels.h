@@ -43,6 +43,11 @@ struct PostParams {
   float* pbar;
   int32_t Hq, G;
   int32_t avg_row_begin, avg_row_count;
+  // When set, the launch stores done_val there (mapped host memory) as it
+  // starts: the attention launch before it, the last reader of the call's
+  // pinned plan, has then finished, so the host may reuse the plan buffer.
+  uint64_t* done;
+  uint64_t done_val;
 };
 
 struct SelectParams {
