@@ -32,6 +32,7 @@ from sparse_self_speculative_pillarattn_amd import binding as bd  # noqa: E402
 from sparse_self_speculative_pillarattn_amd import synth  # noqa: E402
 
 HBM_PEAK_GBPS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix peak of MI355X
 METRIC = "mixed draft/verify attn steps/s; attended KV tok/s; HBM GB/s vs 8 TB/s peak"
 CSRC = os.path.join(ROOT, "sparse_self_speculative_pillarattn_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
@@ -88,6 +89,19 @@ def algorithmic_bytes(b) -> dict:
     return out
 
 
+def mfma_flops(b) -> dict:
+    """Dense multiply-add work of the attention launch's MFMA tiles, counted
+    as 2 FLOPs per multiply-add: S = Q K^T and O = P V over every (row, query
+    head, position) the method attends.  A verify request contributes
+    4*(k+1)*H_q*d*L, a draft request 4*H_q*d*K (the bf16 path runs both on the
+    MFMA tile; rows padded up to the 16-row MFMA tile are not counted)."""
+    w = b.w
+    Hq, d, k = w.num_qo_heads, w.head_dim, w.spec_k
+    fv = sum(4 * (k + 1) * Hq * d * b.seq_lens[r] for r in range(b.B) if b.is_verify[r])
+    fd = sum(4 * Hq * d * b.idx_count[r] for r in range(b.B) if not b.is_verify[r])
+    return {"verify": fv, "draft": fd, "total": fv + fd}
+
+
 # --------------------------------------------------------------------------- #
 # counter-based traffic, valid only for the kernel source it was taken on
 # --------------------------------------------------------------------------- #
@@ -98,6 +112,22 @@ def kernel_source_hash() -> str:
             with open(os.path.join(CSRC, name), "rb") as f:
                 h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
+
+
+def recorded_mfma(workload: str):
+    """MFMA counters of one attention launch (bf16 MFMA FLOPs issued, MFMA busy
+    share of the SIMDs) from a committed summary, or None when none exists for
+    this workload or the kernels changed since."""
+    path = os.path.join(PROFILES, f"attn_kernel_{workload}_mfma.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    src = re.search(r"source_sha256:\s*([0-9a-f]+)", text)
+    fl = re.search(r"mfma_flops_bf16_per_launch:\s*([0-9.eE+]+)", text)
+    ut = re.search(r"mfma_util_pct:\s*([0-9.eE+]+)", text)
+    if not src or not fl or not ut or src.group(1) != kernel_source_hash():
+        return None
+    return {"mfma_flops_issued_per_launch": float(fl.group(1)), "mfma_util_pct": float(ut.group(1))}
 
 
 def recorded_traffic(workload: str):
@@ -552,6 +582,18 @@ def main():
     verify_us = ms_attn / max(n_attn, 1) * 1e3
     draft_us = ms_attn_d / max(n_attn_d, 1) * 1e3 if n_attn_d else None
     traffic = recorded_traffic(w.name)
+    mf = mfma_flops(b)
+    mfma = None
+    if w.dtype == "bf16":
+        # MFMA work of the same launch against the dense bf16 peak: the
+        # contraction is real, but at 36-65 FLOP per KV byte the launch sits
+        # far below the ridge (about 310 FLOP/B), so this stays small
+        mfma = {"kernel": "attn_kernel", "dtype": "bf16",
+                "algorithmic_flops_per_launch": mf["total"], "verify_flops": mf["verify"],
+                "achieved_tflops": round(mf["total"] / (attn_us * 1e-6) / 1e12, 2),
+                "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
+                "frac": round(mf["total"] / (attn_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 5),
+                "counters": recorded_mfma(w.name)}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -597,6 +639,7 @@ def main():
                      "launch_us": round(attn_us, 2), "launches": n_span if overlapped else n_attn,
                      "verify_launch_us": round(verify_us, 2),
                      "draft_launch_us": round(draft_us, 2) if draft_us else None},
+        "mfma": mfma,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -689,6 +689,10 @@ int32_t run(const Shape& s, const std::vector<Req>& rq, const Plan& pl, const Bu
     p.plan_src = reinterpret_cast<const uint4*>(plan + pl.h_post);
     p.plan_dst = reinterpret_cast<uint4*>(ws + pl.off_plan);
     p.plan_n16 = pl.n_items > 0 ? static_cast<int32_t>((pl.h_bytes - pl.h_post) / 16) : 0;
+    // a call that is this one launch reports its slot free from the launch
+    const bool attn_only = pl.n_items > 0 && n_post == 0 && pl.n_sel == 0 && !pl.split;
+    p.done = attn_only ? g_done_dev + (slot - g_ring) : nullptr;
+    p.done_val = slot->seq;
     ProfSpan span;
     span.start(st);
     if (pl.split) {
@@ -711,6 +715,7 @@ int32_t run(const Shape& s, const std::vector<Req>& rq, const Plan& pl, const Bu
       pd.items = reinterpret_cast<const Item*>(plan + pl.h_items_d);
       pd.ticket_set = p.ticket_set + 1;
       pd.plan_n16 = 0;
+      pd.done = nullptr;
       {
         ProfScope ps(PROF_ATTN_DRAFT, side->stream);
         e = launch_attn(pd, s.dtype, s.d, pl.n_items_d, pl.nthr, pl.smem, true, side->stream);
@@ -722,11 +727,12 @@ int32_t run(const Shape& s, const std::vector<Req>& rq, const Plan& pl, const Bu
     }
     span.finish();
   }
+  // The device reports the slot free when the attention launch on `st` is
+  // the plan's last reader (no side-stream launch): the post-pass as it
+  // starts, or the attention launch itself when it is the call's only one.
+  const bool signal = pl.n_items > 0 && !pl.split && (n_post > 0 || pl.n_sel == 0);
   // records of the launches below: the workspace copy when the attention
   // launch on `st` made one, else the pinned plan
-  // the post-pass reports the slot free when the attention launch on `st`
-  // was the plan's last reader (no side-stream launch)
-  const bool signal = pl.n_items > 0 && n_post > 0 && !pl.split;
   auto post_rec = [&](size_t h_off) {
     return reinterpret_cast<const PostItem*>(pl.n_items > 0 ? ws + pl.off_plan + (h_off - pl.h_post)
                                                             : plan + h_off);

@@ -787,6 +787,10 @@ __device__ __forceinline__ void attn_loop(const AttnParams& p, char* smem) {
       if (e < nc)
         for (int c = e * (int)blockDim.x + (int)threadIdx.x; c < p.plan_n16; c += nc * (int)blockDim.x)
           p.plan_dst[c] = p.plan_src[c];
+      // The last of those draws comes after every other workgroup's: no
+      // plan record is read after it.
+      if (p.done && e == (int)gridDim.x - 1 && threadIdx.x == 0)
+        __hip_atomic_store(p.done, p.done_val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
       break;
     }
     const bool drew = attn_body<D, T, GM>(p, item, smem, &s_item[k ^ 1], wrap);

@@ -31,6 +31,11 @@ struct AttnParams {
   const uint4* plan_src;
   uint4* plan_dst;
   int32_t plan_n16;
+  // When set (only when plan_n16 is 0), the workgroup that draws the last
+  // ticket stores done_val there (mapped host memory): every workgroup has
+  // then read its last plan record, so the host may reuse the plan buffer.
+  uint64_t* done;
+  uint64_t done_val;
 };
 
 struct PostParams {
