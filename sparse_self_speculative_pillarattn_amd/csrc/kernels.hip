@@ -25,6 +25,7 @@ namespace spa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4u __attribute__((ext_vector_type(4), aligned(4)));  // 16 bytes at a 4-byte boundary
 
 constexpr float LOG2E = 1.4426950408889634f;
 #define NEG_INF (-__builtin_inff())
@@ -1254,8 +1255,9 @@ __global__ void __launch_bounds__(POST_THREADS) post_kernel(PostParams p) {
           for (int u = 0; u < 8; ++u) {
             const int s = min(s0 + u * tpt, ns - 1);
             const int64_t pr = it.part_row0 + (int64_t)s * R + rho;
-            mm[u] = p.part_ml[2 * pr];
-            ll[u] = p.part_ml[2 * pr + 1];
+            const float2 ml = reinterpret_cast<const float2*>(p.part_ml)[pr];  // (m, l) pair
+            mm[u] = ml.x;
+            ll[u] = ml.y;
           }
 #pragma unroll
           for (int u = 0; u < 8; ++u) {
@@ -1289,12 +1291,15 @@ __global__ void __launch_bounds__(POST_THREADS) post_kernel(PostParams p) {
   const float inv = 1.f / (float)terms;
   const int j4 = it.j0 + 4 * tid;
   if (j4 >= it.j1) return;
-  if (((it.logits_off | (int64_t)L) & 3) == 0 && j4 + 4 <= it.j1) {
+  if (j4 + 4 <= it.j1) {
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 16
     for (int x = 0; x < terms; ++x) {
-      // each logit is read once here: a streaming load, like the KV rows
-      const f32x4 v4 = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(lg + rowoff_s[x] + j4));
+      // each logit is read once here: a streaming load, like the KV rows.
+      // A row starts 16-byte aligned only when L and the request's logits
+      // offset are multiples of 4, so the load type asks for 4-byte alignment
+      // (gfx950 serves 16-byte global loads at any 4-byte boundary).
+      const f32x4u v4 = __builtin_nontemporal_load(reinterpret_cast<const f32x4u*>(lg + rowoff_s[x] + j4));
       const float4 v = make_float4(v4.x, v4.y, v4.z, v4.w);
       const float l2 = lse2_s[x];
       const float vv[4] = {v.x, v.y, v.z, v.w};
@@ -1305,16 +1310,23 @@ __global__ void __launch_bounds__(POST_THREADS) post_kernel(PostParams p) {
     *reinterpret_cast<float4*>(pbar + j4) =
         make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
   } else {
-    for (int e = 0; e < 4 && j4 + e < it.j1; ++e) {
-      const int j = j4 + e;
-      float sacc = 0.f;
-      for (int x = 0; x < terms; ++x) {
-        const float v = lg[rowoff_s[x] + j];
-        const float l2 = lse2_s[x];
-        sacc += (v == NEG_INF || l2 == NEG_INF) ? 0.f : fast_exp2(fmaf(v, LOG2E, -l2));
-      }
-      pbar[j] = sacc * inv;
+    // The item's last, partial group of positions: the same loop with four
+    // 4-byte loads per term.  Positions past j1 re-read the last valid one
+    // and are not stored.
+    const int ne = min(4, it.j1 - j4);
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+    for (int x = 0; x < terms; ++x) {
+      const float* row = lg + rowoff_s[x] + j4;
+      float vv[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) vv[e] = __builtin_nontemporal_load(row + min(e, ne - 1));
+      const float l2 = lse2_s[x];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        acc[e] += (vv[e] == NEG_INF || l2 == NEG_INF) ? 0.f : fast_exp2(fmaf(vv[e], LOG2E, -l2));
     }
+    for (int e = 0; e < ne; ++e) pbar[j4 + e] = acc[e] * inv;
   }
 }
 
