@@ -306,9 +306,11 @@ __device__ void dma_consumer(const AttnParams& p, const Item& it, char* smem,
   const int last_vis = is_list ? 0x7fffffff : L - rows_q + qi;
   float* lrow = is_list ? nullptr : p.logits + it.off + ((int64_t)qi * Hq + h) * L;
   const float sc = p.sm_scale;
-  const bool rows_aligned = ((it.off | (int64_t)L) & 3) == 0;  // every logits row 16-byte aligned
-  // Full aligned tiles go out through this wave's LDS staging: 8 lanes then
-  // write 128 contiguous bytes of one row (rows rA and rA + 8 of the wave).
+  // Full tiles go out through this wave's LDS staging: 8 lanes then write
+  // 128 contiguous bytes of one row (rows rA and rA + 8 of the wave).  A row
+  // starts 16-byte aligned only when L and the logits offset are multiples of
+  // 4; the 16-byte stores ask for 4-byte alignment (gfx950 serves them at any
+  // 4-byte boundary).
   float* stg = reinterpret_cast<float*>(smem + dma_smem_bytes<D>()) + wave * 16 * LSTG;
   const int rA = lane >> 3, cA = 4 * (lane & 7);
   float* lA = nullptr;
@@ -366,22 +368,17 @@ __device__ void dma_consumer(const AttnParams& p, const Item& it, char* smem,
           v[t][e] = sacc[t][e] * sc;
           mx = fmaxf(mx, v[t][e]);
         }
-      if (rows_aligned) {
+      {
         // lane (n, q) holds row n's tokens 16 t + 4 q .. + 3; a wave's LDS
         // accesses complete in order, so the read-back needs no barrier
 #pragma unroll
         for (int t = 0; t < 2; ++t)
           *reinterpret_cast<float4*>(stg + n * LSTG + 16 * t + 4 * q4) =
               make_float4(v[t][0], v[t][1], v[t][2], v[t][3]);
-        const float4 va = *reinterpret_cast<const float4*>(stg + rA * LSTG + cA);
-        const float4 vb = *reinterpret_cast<const float4*>(stg + (rA + 8) * LSTG + cA);
-        if (lA) *reinterpret_cast<float4*>(lA + t0 + cA) = va;
-        if (lB) *reinterpret_cast<float4*>(lB + t0 + cA) = vb;
-      } else if (row_ok) {
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) lrow[t0 + 16 * t + 4 * q4 + e] = v[t][e];
+        const f32x4 va = *reinterpret_cast<const f32x4*>(stg + rA * LSTG + cA);
+        const f32x4 vb = *reinterpret_cast<const f32x4*>(stg + (rA + 8) * LSTG + cA);
+        if (lA) *reinterpret_cast<f32x4u*>(lA + t0 + cA) = va;
+        if (lB) *reinterpret_cast<f32x4u*>(lB + t0 + cA) = vb;
       }
     } else {
       int ok[2][4];
@@ -417,8 +414,8 @@ __device__ void dma_consumer(const AttnParams& p, const Item& it, char* smem,
         for (int t = 0; t < 2; ++t) {
           const int tb = t0 + 16 * t + 4 * q4;
           float* dst = lrow + tb;
-          if (rows_aligned && tb + 4 <= je) {
-            *reinterpret_cast<float4*>(dst) = make_float4(v[t][0], v[t][1], v[t][2], v[t][3]);
+          if (tb + 4 <= je) {
+            *reinterpret_cast<f32x4u*>(dst) = f32x4u{v[t][0], v[t][1], v[t][2], v[t][3]};
           } else {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
