@@ -78,12 +78,13 @@ struct Plan {
   int n_items_d = 0;            // draft launch records
   int n_merge_d = 0;            // draft merges, run after the join
   int n_merge = 0, n_avg = 0, n_sel = 0;
+  int n_hist = 0;  // selected rows longer than SELECT_SPAN, each with a score histogram
   int64_t part_rows = 0;
   int64_t pbar_elems = 0;
   // pinned plan layout
   size_t h_items = 0, h_items_d = 0, h_post = 0, h_post_d = 0, h_sel = 0, h_bytes = 0;
   // workspace layout
-  size_t off_part_o = 0, off_part_ml = 0, off_pbar = 0, off_plan = 0, total = 0;
+  size_t off_part_o = 0, off_part_ml = 0, off_pbar = 0, off_plan = 0, off_hist = 0, total = 0;
   int nthr = 256;
   size_t smem = 0;
 };
@@ -236,6 +237,9 @@ int32_t plan_size(const Shape& s, const std::vector<Req>& rq, bool attn, bool to
       if (q.verify) {
         pl->n_avg += Hkv * avg_parts(q.L);
         pl->n_sel += Hkv;
+        // the histogram is cleared by the attention launch, so only a call
+        // with one keeps it
+        if (attn && q.L > SELECT_SPAN) pl->n_hist += Hkv;
         pbar += Hkv * pbar_row(q.L);
       }
   pl->part_rows = part_rows;
@@ -286,6 +290,8 @@ int32_t plan_size(const Shape& s, const std::vector<Req>& rq, bool attn, bool to
   // the attention launch copies the post-pass and selection records here
   pl->off_plan = o;
   if (attn) o = align_up(o + (pl->h_bytes - pl->h_post), 256);
+  pl->off_hist = o;
+  o = align_up(o + (size_t)pl->n_hist * HIST_BINS * 4, 256);
   pl->total = o;
   return SPA_OK;
 }
@@ -339,7 +345,7 @@ void plan_write(const Shape& s, const std::vector<Req>& rq, const Plan& pl, char
   PostItem* post = reinterpret_cast<PostItem*>(h + pl.h_post);
   PostItem* post_d = reinterpret_cast<PostItem*>(h + pl.h_post_d);
   PostItem* sel = reinterpret_cast<PostItem*>(h + pl.h_sel);
-  int np = 0, ns = 0, npd = 0;
+  int np = 0, ns = 0, npd = 0, nh = 0;
   if (pl.topk) {
     int64_t pbar = 0;
     for (int r = 0; r < B; ++r) {
@@ -363,6 +369,7 @@ void plan_write(const Shape& s, const std::vector<Req>& rq, const Plan& pl, char
         a.logits_off = q.logits_off;
         a.idx_off = q.idx_off + (int64_t)g * q.nlist;
         a.pbar_off = pbar;
+        a.hist_slot = (pl.n_hist > 0 && q.L > SELECT_SPAN) ? nh++ : -1;
         sel[ns++] = a;
         for (int pidx = 0; pidx < nparts; ++pidx) {
           a.j0 = pidx * AVG_SPAN;
@@ -383,6 +390,7 @@ void plan_write(const Shape& s, const std::vector<Req>& rq, const Plan& pl, char
         PostItem m;
         std::memset(&m, 0, sizeof m);
         m.kind = POST_MERGE;
+        m.hist_slot = -1;
         m.r = r;
         m.g = g;
         m.rows_q = rq_rows;
@@ -689,6 +697,9 @@ int32_t run(const Shape& s, const std::vector<Req>& rq, const Plan& pl, const Bu
     p.plan_src = reinterpret_cast<const uint4*>(plan + pl.h_post);
     p.plan_dst = reinterpret_cast<uint4*>(ws + pl.off_plan);
     p.plan_n16 = pl.n_items > 0 ? static_cast<int32_t>((pl.h_bytes - pl.h_post) / 16) : 0;
+    // ... and clears the long rows' score histograms the post-pass adds to
+    p.zero_dst = reinterpret_cast<uint4*>(ws + pl.off_hist);
+    p.zero_n16 = pl.n_items > 0 ? static_cast<int32_t>((size_t)pl.n_hist * HIST_BINS * 4 / 16) : 0;
     // a call that is this one launch reports its slot free from the launch
     const bool attn_only = pl.n_items > 0 && n_post == 0 && pl.n_sel == 0 && !pl.split;
     p.done = attn_only ? g_done_dev + (slot - g_ring) : nullptr;
@@ -715,6 +726,7 @@ int32_t run(const Shape& s, const std::vector<Req>& rq, const Plan& pl, const Bu
       pd.items = reinterpret_cast<const Item*>(plan + pl.h_items_d);
       pd.ticket_set = p.ticket_set + 1;
       pd.plan_n16 = 0;
+      pd.zero_n16 = 0;
       pd.done = nullptr;
       {
         ProfScope ps(PROF_ATTN_DRAFT, side->stream);
@@ -731,6 +743,8 @@ int32_t run(const Shape& s, const std::vector<Req>& rq, const Plan& pl, const Bu
   // the plan's last reader (no side-stream launch): the post-pass as it
   // starts, or the attention launch itself when it is the call's only one.
   const bool signal = pl.n_items > 0 && !pl.split && (n_post > 0 || pl.n_sel == 0);
+  // long rows' score histograms: cleared by the attention launch on `st`
+  uint32_t* hist = (pl.n_items > 0 && pl.n_hist > 0) ? reinterpret_cast<uint32_t*>(ws + pl.off_hist) : nullptr;
   // records of the launches below: the workspace copy when the attention
   // launch on `st` made one, else the pinned plan
   auto post_rec = [&](size_t h_off) {
@@ -752,10 +766,11 @@ int32_t run(const Shape& s, const std::vector<Req>& rq, const Plan& pl, const Bu
     pp.avg_row_count = avg_count;
     pp.done = signal ? g_done_dev + (slot - g_ring) : nullptr;
     pp.done_val = slot->seq;
+    pp.hist = hist;
     {
       ProfScope ps(PROF_POST, st);
       e = launch_post(pp, s.dtype, s.d, n_post,
-                      post_smem_bytes(pl.n_avg ? avg_count * s.G : 0, pl.max_nchunk), st);
+                      post_smem_bytes(pl.n_avg ? avg_count * s.G : 0, pl.max_nchunk, hist != nullptr), st);
     }
     if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("post-pass launch: ") + hipGetErrorString(e));
   }
@@ -764,6 +779,7 @@ int32_t run(const Shape& s, const std::vector<Req>& rq, const Plan& pl, const Bu
     sp.items = post_rec(pl.h_sel);
     sp.pbar = reinterpret_cast<const float*>(ws + pl.off_pbar);
     sp.idx_out = b.idx_out;
+    sp.hist = hist;
     {
       ProfScope ps(PROF_SELECT, st);
       e = launch_select(sp, pl.n_sel, st);
@@ -788,9 +804,10 @@ int32_t run(const Shape& s, const std::vector<Req>& rq, const Plan& pl, const Bu
       pp.avg_row_count = avg_count;
       pp.done = nullptr;
       pp.done_val = 0;
+      pp.hist = nullptr;
       {
         ProfScope ps(PROF_POST, st);
-        e = launch_post(pp, s.dtype, s.d, pl.n_merge_d, post_smem_bytes(0, pl.max_nchunk), st);
+        e = launch_post(pp, s.dtype, s.d, pl.n_merge_d, post_smem_bytes(0, pl.max_nchunk, false), st);
       }
       if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("draft merge launch: ") + hipGetErrorString(e));
     }

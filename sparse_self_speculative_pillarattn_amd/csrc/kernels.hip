@@ -782,9 +782,12 @@ __device__ __forceinline__ void attn_loop(const AttnParams& p, char* smem) {
       // where the read is on their critical path.
       const int e = item - p.n_items;
       const int nc = max(1, (int)gridDim.x / 2);
-      if (e < nc)
+      if (e < nc) {
         for (int c = e * (int)blockDim.x + (int)threadIdx.x; c < p.plan_n16; c += nc * (int)blockDim.x)
           p.plan_dst[c] = p.plan_src[c];
+        for (int c = e * (int)blockDim.x + (int)threadIdx.x; c < p.zero_n16; c += nc * (int)blockDim.x)
+          p.zero_dst[c] = make_uint4(0u, 0u, 0u, 0u);
+      }
       // The last of those draws comes after every other workgroup's: no
       // plan record is read after it.
       if (p.done && e == (int)gridDim.x - 1 && threadIdx.x == 0)
@@ -974,8 +977,14 @@ constexpr int SELECT_BATCH = 4;    // chunks loaded per batch when a row is long
 //     of 16 lanes with DPP (<= 128 per byte), then to 32 bits per digit.
 //   - Once the bucket holding the K-th key has at most 64 keys, they are
 //     gathered into LDS and one wave ranks them directly.
+//   - hist, when given, holds the row's keys counted by bits 30..20 (2048
+//     bins; the sign bit of a non-negative score is 0), summed by the
+//     launch that wrote the scores.  The bin of the K-th largest key then
+//     fixes those bits at once, replacing the AND/OR walk and three passes:
+//     on rows of many chunks every walk re-reads the row.
 template <int KPT>
-__device__ __forceinline__ void select_topk(const float* scores, int L, int K, int32_t* out, char* smem) {
+__device__ __forceinline__ void select_topk(const float* scores, int L, int K, int32_t* out, char* smem,
+                                            const uint32_t* hist = nullptr) {
   static_assert(KPT % 4 == 0 && KPT <= 8, "keys are loaded four at a time; nibble counters");
   uint32_t* sv = reinterpret_cast<uint32_t*>(smem);  // prefix, rem, bucket count, and/or
   uint32_t* wsum = sv + 8;                           // [16] block scans
@@ -1028,6 +1037,39 @@ __device__ __forceinline__ void select_topk(const float* scores, int L, int K, i
     }
   };
   if (resident) load_into(key, 0);
+  int shift;
+  uint32_t mask;
+  if (hist) {
+    // thread t sums bins 2047 - per t down to 2048 - per (t + 1); the scan
+    // then counts the keys in every higher bin
+    if (tid == 0) {  // stands only if no bin holds the K-th key (inconsistent input)
+      sv[0] = 0u;
+      sv[1] = (uint32_t)K;
+      sv[2] = 0xffffffffu;
+    }
+    const int per = HIST_BINS / nthr;
+    const int b0 = HIST_BINS - 1 - per * tid;
+    uint32_t mine = 0u;
+    for (int b = 0; b < per; ++b) mine += hist[b0 - b];
+    uint32_t tot;
+    const uint32_t above = block_exclusive_scan(mine, wsum, &tot);
+    if (above < (uint32_t)K && above + mine >= (uint32_t)K) {  // one thread owns the K-th key
+      uint32_t acc_above = above;
+      for (int b = 0; b < per; ++b) {
+        const uint32_t c = hist[b0 - b];
+        if (acc_above + c >= (uint32_t)K) {
+          sv[0] = (uint32_t)(b0 - b) << HIST_SHIFT;
+          sv[1] = (uint32_t)K - acc_above;
+          sv[2] = c;
+          break;
+        }
+        acc_above += c;
+      }
+    }
+    __syncthreads();
+    shift = HIST_SHIFT - 4;
+    mask = 0xffffffffu << HIST_SHIFT;
+  } else {
   // bits shared by every key: AND and OR over the block
   if (tid == 0) {
     sv[4] = 0xffffffffu;
@@ -1058,12 +1100,14 @@ __device__ __forceinline__ void select_topk(const float* scores, int L, int K, i
   }
   __syncthreads();
   const uint32_t diff = sv[4] ^ sv[5];
-  int shift = diff == 0u ? 0 : (31 - __builtin_clz(diff)) / 4 * 4;  // top differing digit
-  uint32_t mask = shift >= 28 ? 0u : 0xffffffffu << (shift + 4);
+  shift = diff == 0u ? 0 : (31 - __builtin_clz(diff)) / 4 * 4;  // top differing digit
+  mask = shift >= 28 ? 0u : 0xffffffffu << (shift + 4);
   if (tid == 0) sv[0] = sv[4] & mask;  // the shared leading digits
   __syncthreads();
-  bool finish = false;
-  for (; shift >= 0; shift -= 4) {
+  }
+  // a histogram bin small enough already goes straight to the direct ranking
+  bool finish = hist != nullptr && sv[2] <= (uint32_t)SELECT_FINISH;
+  for (; shift >= 0 && !finish; shift -= 4) {
     const uint32_t prefix = sv[0];
     uint32_t acc[16];  // per row of 16 lanes
 #pragma unroll
@@ -1140,7 +1184,10 @@ __device__ __forceinline__ void select_topk(const float* scores, int L, int K, i
       uint32_t pos = base + block_exclusive_scan(n, wsum, &tot);
 #pragma unroll
       for (int m = 0; m < KPT; ++m)
-        if (j0 + m < L && (key[m] & mask) == prefix) ckey[pos++] = key[m];
+        if (j0 + m < L && (key[m] & mask) == prefix) {
+          if (pos < (uint32_t)SELECT_FINISH) ckey[pos] = key[m];
+          ++pos;
+        }
       base += tot;
     });
     __syncthreads();
@@ -1197,6 +1244,12 @@ __device__ __forceinline__ void select_topk(const float* scores, int L, int K, i
 }
 
 constexpr int POST_THREADS = 256;
+
+// Dynamic LDS of an averaging item: the LSE (4 B) and logits row offset (8 B)
+// of every averaged term, then, for a long row, its 2048-bin histogram.
+__host__ __device__ constexpr size_t post_hist_offset(int terms) {
+  return ((size_t)(terms * 4 + 7) / 8 * 8 + (size_t)terms * 8 + 15) / 16 * 16;
+}
 static_assert(AVG_SPAN == 4 * POST_THREADS, "an averaging thread owns four positions");
 
 template <int D, typename T>
@@ -1282,13 +1335,20 @@ __global__ void __launch_bounds__(POST_THREADS) post_kernel(PostParams p) {
       }
     }
   }
+  // A long row's scores are also counted by bits 30..20 into the row's
+  // histogram: in LDS here, then added to the row's global counts.
+  const bool keep_hist = p.hist != nullptr && it.hist_slot >= 0;
+  uint32_t* hist_s = reinterpret_cast<uint32_t*>(smem + post_hist_offset(terms));
+  if (keep_hist)
+    for (int b = tid; b < HIST_BINS; b += blockDim.x) hist_s[b] = 0u;
   __syncthreads();
   const float* lg = p.logits + it.logits_off;
   float* pbar = p.pbar + it.pbar_off;
   const float inv = 1.f / (float)terms;
   const int j4 = it.j0 + 4 * tid;
-  if (j4 >= it.j1) return;
-  if (j4 + 4 <= it.j1) {
+  const int ne = max(0, min(4, it.j1 - j4));  // positions of this thread
+  float res[4] = {0.f, 0.f, 0.f, 0.f};
+  if (ne == 4) {
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 16
     for (int x = 0; x < terms; ++x) {
@@ -1304,13 +1364,13 @@ __global__ void __launch_bounds__(POST_THREADS) post_kernel(PostParams p) {
       for (int e = 0; e < 4; ++e)
         acc[e] += (vv[e] == NEG_INF || l2 == NEG_INF) ? 0.f : fast_exp2(fmaf(vv[e], LOG2E, -l2));
     }
-    *reinterpret_cast<float4*>(pbar + j4) =
-        make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
-  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) res[e] = acc[e] * inv;
+    *reinterpret_cast<float4*>(pbar + j4) = make_float4(res[0], res[1], res[2], res[3]);
+  } else if (ne > 0) {
     // The item's last, partial group of positions: the same loop with four
     // 4-byte loads per term.  Positions past j1 re-read the last valid one
     // and are not stored.
-    const int ne = min(4, it.j1 - j4);
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 8
     for (int x = 0; x < terms; ++x) {
@@ -1323,18 +1383,38 @@ __global__ void __launch_bounds__(POST_THREADS) post_kernel(PostParams p) {
       for (int e = 0; e < 4; ++e)
         acc[e] += (vv[e] == NEG_INF || l2 == NEG_INF) ? 0.f : fast_exp2(fmaf(vv[e], LOG2E, -l2));
     }
-    for (int e = 0; e < ne; ++e) pbar[j4 + e] = acc[e] * inv;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) res[e] = acc[e] * inv;
+    for (int e = 0; e < ne; ++e) pbar[j4 + e] = res[e];
+  }
+  if (keep_hist) {
+    // the selection orders keys as unsigned bit patterns; a score is >= +0,
+    // so its sign bit is 0 (a pattern with it set is not counted: no bin of
+    // the selection's search can hold it)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t key = __float_as_uint(res[e]);
+      if (e < ne && key < 0x80000000u) atomicAdd(&hist_s[key >> HIST_SHIFT], 1u);
+    }
+    __syncthreads();
+    uint32_t* hist_g = p.hist + (int64_t)it.hist_slot * HIST_BINS;
+    for (int b = tid; b < HIST_BINS; b += blockDim.x) {
+      const uint32_t c = hist_s[b];
+      if (c) atomicAdd(&hist_g[b], c);
+    }
   }
 }
 
 // Selection launch: one workgroup per verify (request, KV head).
 constexpr int SELECT_THREADS = 1024;
 constexpr int SELECT_KPT = 8;  // keys per thread kept in registers (8192 at 1024 threads)
+static_assert(SELECT_THREADS * SELECT_KPT == SELECT_SPAN, "rows above SELECT_SPAN scores get a histogram");
 
 __global__ void __launch_bounds__(SELECT_THREADS) select_kernel(SelectParams sp) {
   __shared__ __attribute__((aligned(16))) char smem[(24 + 16 * 64 + SELECT_FINISH) * 4];
   const PostItem it = sp.items[blockIdx.x];
-  select_topk<SELECT_KPT>(sp.pbar + it.pbar_off, it.L, it.K, sp.idx_out + it.idx_off, smem);
+  const uint32_t* hist = (sp.hist && it.hist_slot >= 0) ? sp.hist + (int64_t)it.hist_slot * HIST_BINS : nullptr;
+  select_topk<SELECT_KPT>(sp.pbar + it.pbar_off, it.L, it.K, sp.idx_out + it.idx_off, smem, hist);
 }
 
 // ==========================================================================
@@ -1614,8 +1694,9 @@ hipError_t launch_recall(const RecallParams& rp, int nblocks, size_t smem, hipSt
   return hipGetLastError();
 }
 
-size_t post_smem_bytes(int avg_terms, int max_nchunk) {
-  const size_t avg = (size_t)(avg_terms * 4 + 7) / 8 * 8 + (size_t)avg_terms * 8;
+size_t post_smem_bytes(int avg_terms, int max_nchunk, bool hist) {
+  const size_t avg = hist ? post_hist_offset(avg_terms) + (size_t)HIST_BINS * 4
+                          : (size_t)(avg_terms * 4 + 7) / 8 * 8 + (size_t)avg_terms * 8;
   const size_t merge = (size_t)2 * MERGE_ROWS * max_nchunk * 4;
   return std::max<size_t>(16, std::max(avg, merge));
 }

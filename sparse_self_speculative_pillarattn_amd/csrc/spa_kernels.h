@@ -31,6 +31,10 @@ struct AttnParams {
   const uint4* plan_src;
   uint4* plan_dst;
   int32_t plan_n16;
+  // Workspace the same workgroups clear (zero_n16 16-byte pieces): the long
+  // rows' score histograms that the post-pass then adds to.
+  uint4* zero_dst;
+  int32_t zero_n16;
   // When set (only when plan_n16 is 0), the workgroup that draws the last
   // ticket stores done_val there (mapped host memory): every workgroup has
   // then read its last plan record, so the host may reuse the plan buffer.
@@ -48,6 +52,9 @@ struct PostParams {
   float* pbar;
   int32_t Hq, G;
   int32_t avg_row_begin, avg_row_count;
+  // Long rows' score histograms (zeroed by the attention launch), added to
+  // by the averaging items of rows with hist_slot >= 0; null: none kept.
+  uint32_t* hist;
   // When set, the launch stores done_val there (mapped host memory) as it
   // starts: the attention launch before it, the last reader of the call's
   // pinned plan, has then finished, so the host may reuse the plan buffer.
@@ -59,6 +66,7 @@ struct SelectParams {
   const PostItem* items;  // one POST_AVG record of each selected (r, g)
   const float* pbar;
   int32_t* idx_out;
+  const uint32_t* hist;   // [slots][HIST_BINS] counts of long rows, or null
 };
 
 struct RecallParams {
@@ -84,7 +92,7 @@ struct QualityParams {
 // LDS bytes the attention kernel needs for a launch shape.
 size_t attn_smem_bytes(int dtype, int head_dim, int G, int nthr, bool mfma, bool valu,
                        int max_chunk);
-size_t post_smem_bytes(int avg_terms, int max_nchunk);
+size_t post_smem_bytes(int avg_terms, int max_nchunk, bool hist);
 
 hipError_t launch_attn(const AttnParams& p, int dtype, int head_dim, int nitems, int nthr,
                        size_t smem, bool draft, hipStream_t st);

@@ -117,6 +117,39 @@ def test_split_invariance(oracle, split):
     check(oracle, w)
 
 
+@pytest.mark.parametrize("L,s", [(8192, Fraction(1, 20)), (8193, Fraction(1, 20)),
+                                 (12289, Fraction(1, 20)), (20001, Fraction(1, 50)),
+                                 (40000, Fraction(1, 20)), (30001, Fraction(1, 2))])
+def test_long_rows(oracle, L, s):
+    """Rows longer than one selection workgroup's registers (8192 scores):
+    the post-pass counts their averaged scores into a histogram that seeds the
+    selection.  Lengths around the boundary, odd lengths (rows not 16-byte
+    aligned), and a large K (half the row)."""
+    w = synth.Workload(name=f"long-{L}", batch=3, num_qo_heads=8, num_kv_heads=2, head_dim=128,
+                       dtype="bf16", spec_k=2, sparsity=s, lengths=("fixed", L), n_verify=2,
+                       seed=L)
+    check(oracle, w)
+
+
+def test_long_row_all_scores_tied(oracle):
+    """Every position of a 10,000-token verify request reads the same K/V
+    slot, so all but the causally hidden tail tie: the selection, seeded by a
+    histogram whose one bin holds them all, must keep the lowest positions."""
+    L = 10000
+    w = synth.Workload(name="long-tied", batch=2, num_qo_heads=8, num_kv_heads=2, head_dim=128,
+                       dtype="bf16", spec_k=2, sparsity=Fraction(1, 20), lengths=("fixed", L),
+                       n_verify=1, seed=77)
+    b = synth.make_batch(w)
+    r = int(np.nonzero(b.is_verify)[0][0])
+    b.page_table[r, :L] = b.page_table[r, 0]
+    ref = oracle.step(**parity.oracle_inputs(b))
+    gpu = run_unified(b.to(DEV))
+    parity.compare_step(oracle, b, gpu, ref)
+    K = b.idx_count[r]
+    seg = to_np(gpu["idx"])[b.idx_off[r]:b.idx_off[r] + w.num_kv_heads * K].reshape(w.num_kv_heads, K)
+    assert np.array_equal(seg, np.tile(np.arange(K), (w.num_kv_heads, 1)))
+
+
 def test_topk_count_extremes(oracle):
     """K = 1 and K = L per verify request."""
     w = synth.Workload(name="kext", batch=2, num_qo_heads=8, num_kv_heads=2, head_dim=128,
