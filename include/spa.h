@@ -53,8 +53,8 @@
  *   Workspace   d_ws/ws_bytes is caller-owned device scratch of at least
  *               spa_workspace_bytes(...) bytes for the same batch; it holds
  *               split-K partials, averaged scores, a device copy of the
- *               post-pass and selection work records and the score histograms
- *               of rows longer than 8192 positions.  Its contents on entry do
+ *               post-pass and selection work records and the selected rows'
+ *               score histograms.  Its contents on entry do
  *               not matter and need no initialisation.  Calls that share one
  *               workspace must be ordered on one stream.  The size depends on
  *               the split settings (spa_set_split) and, with the automatic

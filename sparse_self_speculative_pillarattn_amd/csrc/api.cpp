@@ -78,7 +78,7 @@ struct Plan {
   int n_items_d = 0;            // draft launch records
   int n_merge_d = 0;            // draft merges, run after the join
   int n_merge = 0, n_avg = 0, n_sel = 0;
-  int n_hist = 0;  // selected rows longer than SELECT_SPAN, each with a score histogram
+  int n_hist = 0;  // selected rows with a score histogram (all of them when the call has attention)
   int64_t part_rows = 0;
   int64_t pbar_elems = 0;
   // pinned plan layout
@@ -239,7 +239,7 @@ int32_t plan_size(const Shape& s, const std::vector<Req>& rq, bool attn, bool to
         pl->n_sel += Hkv;
         // the histogram is cleared by the attention launch, so only a call
         // with one keeps it
-        if (attn && q.L > SELECT_SPAN) pl->n_hist += Hkv;
+        if (attn) pl->n_hist += Hkv;
         pbar += Hkv * pbar_row(q.L);
       }
   pl->part_rows = part_rows;
@@ -369,7 +369,7 @@ void plan_write(const Shape& s, const std::vector<Req>& rq, const Plan& pl, char
         a.logits_off = q.logits_off;
         a.idx_off = q.idx_off + (int64_t)g * q.nlist;
         a.pbar_off = pbar;
-        a.hist_slot = (pl.n_hist > 0 && q.L > SELECT_SPAN) ? nh++ : -1;
+        a.hist_slot = pl.n_hist > 0 ? nh++ : -1;
         sel[ns++] = a;
         for (int pidx = 0; pidx < nparts; ++pidx) {
           a.j0 = pidx * AVG_SPAN;
@@ -697,7 +697,7 @@ int32_t run(const Shape& s, const std::vector<Req>& rq, const Plan& pl, const Bu
     p.plan_src = reinterpret_cast<const uint4*>(plan + pl.h_post);
     p.plan_dst = reinterpret_cast<uint4*>(ws + pl.off_plan);
     p.plan_n16 = pl.n_items > 0 ? static_cast<int32_t>((pl.h_bytes - pl.h_post) / 16) : 0;
-    // ... and clears the long rows' score histograms the post-pass adds to
+    // ... and clears the score histograms the post-pass adds to
     p.zero_dst = reinterpret_cast<uint4*>(ws + pl.off_hist);
     p.zero_n16 = pl.n_items > 0 ? static_cast<int32_t>((size_t)pl.n_hist * HIST_BINS * 4 / 16) : 0;
     // a call that is this one launch reports its slot free from the launch
@@ -743,7 +743,7 @@ int32_t run(const Shape& s, const std::vector<Req>& rq, const Plan& pl, const Bu
   // the plan's last reader (no side-stream launch): the post-pass as it
   // starts, or the attention launch itself when it is the call's only one.
   const bool signal = pl.n_items > 0 && !pl.split && (n_post > 0 || pl.n_sel == 0);
-  // long rows' score histograms: cleared by the attention launch on `st`
+  // selected rows' score histograms: cleared by the attention launch on `st`
   uint32_t* hist = (pl.n_items > 0 && pl.n_hist > 0) ? reinterpret_cast<uint32_t*>(ws + pl.off_hist) : nullptr;
   // records of the launches below: the workspace copy when the attention
   // launch on `st` made one, else the pinned plan

@@ -980,8 +980,8 @@ constexpr int SELECT_BATCH = 4;    // chunks loaded per batch when a row is long
 //   - hist, when given, holds the row's keys counted by bits 30..20 (2048
 //     bins; the sign bit of a non-negative score is 0), summed by the
 //     launch that wrote the scores.  The bin of the K-th largest key then
-//     fixes those bits at once, replacing the AND/OR walk and three passes:
-//     on rows of many chunks every walk re-reads the row.
+//     fixes those bits at once, replacing the AND/OR walk and three passes
+//     (each a block-wide round, and on rows of many chunks a re-read).
 template <int KPT>
 __device__ __forceinline__ void select_topk(const float* scores, int L, int K, int32_t* out, char* smem,
                                             const uint32_t* hist = nullptr) {
@@ -1246,7 +1246,7 @@ __device__ __forceinline__ void select_topk(const float* scores, int L, int K, i
 constexpr int POST_THREADS = 256;
 
 // Dynamic LDS of an averaging item: the LSE (4 B) and logits row offset (8 B)
-// of every averaged term, then, for a long row, its 2048-bin histogram.
+// of every averaged term, then the row's 2048-bin score histogram.
 __host__ __device__ constexpr size_t post_hist_offset(int terms) {
   return ((size_t)(terms * 4 + 7) / 8 * 8 + (size_t)terms * 8 + 15) / 16 * 16;
 }
@@ -1335,8 +1335,8 @@ __global__ void __launch_bounds__(POST_THREADS) post_kernel(PostParams p) {
       }
     }
   }
-  // A long row's scores are also counted by bits 30..20 into the row's
-  // histogram: in LDS here, then added to the row's global counts.
+  // The scores are also counted by bits 30..20 into the row's histogram:
+  // in LDS here, then added to the row's global counts.
   const bool keep_hist = p.hist != nullptr && it.hist_slot >= 0;
   uint32_t* hist_s = reinterpret_cast<uint32_t*>(smem + post_hist_offset(terms));
   if (keep_hist)
@@ -1408,7 +1408,7 @@ __global__ void __launch_bounds__(POST_THREADS) post_kernel(PostParams p) {
 // Selection launch: one workgroup per verify (request, KV head).
 constexpr int SELECT_THREADS = 1024;
 constexpr int SELECT_KPT = 8;  // keys per thread kept in registers (8192 at 1024 threads)
-static_assert(SELECT_THREADS * SELECT_KPT == SELECT_SPAN, "rows above SELECT_SPAN scores get a histogram");
+static_assert(SELECT_THREADS * SELECT_KPT == SELECT_SPAN, "scores kept in registers");
 
 __global__ void __launch_bounds__(SELECT_THREADS) select_kernel(SelectParams sp) {
   __shared__ __attribute__((aligned(16))) char smem[(24 + 16 * 64 + SELECT_FINISH) * 4];

@@ -31,8 +31,8 @@ struct AttnParams {
   const uint4* plan_src;
   uint4* plan_dst;
   int32_t plan_n16;
-  // Workspace the same workgroups clear (zero_n16 16-byte pieces): the long
-  // rows' score histograms that the post-pass then adds to.
+  // Workspace the same workgroups clear (zero_n16 16-byte pieces): the
+  // selected rows' score histograms that the post-pass then adds to.
   uint4* zero_dst;
   int32_t zero_n16;
   // When set (only when plan_n16 is 0), the workgroup that draws the last
@@ -52,8 +52,8 @@ struct PostParams {
   float* pbar;
   int32_t Hq, G;
   int32_t avg_row_begin, avg_row_count;
-  // Long rows' score histograms (zeroed by the attention launch), added to
-  // by the averaging items of rows with hist_slot >= 0; null: none kept.
+  // Selected rows' score histograms (zeroed by the attention launch), added
+  // to by the averaging items of rows with hist_slot >= 0; null: none kept.
   uint32_t* hist;
   // When set, the launch stores done_val there (mapped host memory) as it
   // starts: the attention launch before it, the last reader of the call's
@@ -66,7 +66,7 @@ struct SelectParams {
   const PostItem* items;  // one POST_AVG record of each selected (r, g)
   const float* pbar;
   int32_t* idx_out;
-  const uint32_t* hist;   // [slots][HIST_BINS] counts of long rows, or null
+  const uint32_t* hist;   // [slots][HIST_BINS] counts of the selected rows, or null
 };
 
 struct RecallParams {

@@ -50,7 +50,7 @@ struct PostItem {
   int32_t nchunk;      // split-K partials per row (1 = the LSE array is already final)
   int32_t j0, j1;      // POST_AVG: positions; POST_MERGE: rows i*G + h of (r, g)
   int32_t K;           // positions to select
-  int32_t hist_slot;   // rows longer than SELECT_SPAN: the (r, g) histogram of averaged scores; else -1
+  int32_t hist_slot;   // the (r, g) histogram of averaged scores, or -1 (none kept)
   int64_t part_row0;   // first split-K partial row of (r, g)
   int64_t logits_off;  // POST_AVG: logits element offset of request r
   int64_t idx_off;     // POST_AVG: element offset of the (r, g) output list
@@ -94,7 +94,7 @@ constexpr int MAX_AVG_TERMS = 512;     // averaged (row, head) pairs per KV head
 constexpr int MAX_MERGE_CHUNKS = 256;  // split-K chunks per (r, g)
 constexpr int MERGE_ROWS = 8;          // rows per merge item
 constexpr int SELECT_SPAN = 8192;      // scores a selection workgroup keeps in registers
-constexpr int HIST_BINS = 2048;        // averaged-score histogram of a long row: bits 30..20
+constexpr int HIST_BINS = 2048;        // averaged-score histogram of a selected row: bits 30..20
 constexpr int HIST_SHIFT = 20;
 
 }  // namespace spa

@@ -121,9 +121,9 @@ def test_split_invariance(oracle, split):
                                  (12289, Fraction(1, 20)), (20001, Fraction(1, 50)),
                                  (40000, Fraction(1, 20)), (30001, Fraction(1, 2))])
 def test_long_rows(oracle, L, s):
-    """Rows longer than one selection workgroup's registers (8192 scores):
-    the post-pass counts their averaged scores into a histogram that seeds the
-    selection.  Lengths around the boundary, odd lengths (rows not 16-byte
+    """Rows longer than one selection workgroup's registers (8192 scores),
+    which the selection re-reads chunk by chunk after its histogram-seeded
+    start.  Lengths around the boundary, odd lengths (rows not 16-byte
     aligned), and a large K (half the row)."""
     w = synth.Workload(name=f"long-{L}", batch=3, num_qo_heads=8, num_kv_heads=2, head_dim=128,
                        dtype="bf16", spec_k=2, sparsity=s, lengths=("fixed", L), n_verify=2,
