@@ -398,3 +398,43 @@ def test_stepbuffers_rebinds_replaced_buffers():
     second = [to_np(t) for t in (bufs.o, bufs.lse, bufs.logits, bufs.idx)]
     for name, a, g in zip(("O", "LSE", "logits", "idx"), first, second):
         assert np.array_equal(a.view(np.uint8), g.view(np.uint8)), f"{name} differs"
+
+
+def test_plan_slots_released_every_way():
+    """Sixty calls on one stream without a synchronisation cycle the 16 plan
+    buffers almost four times while mixing the three ways a buffer is
+    released: a mixed batch (the post-pass reports it), a draft-only batch
+    (the attention launch reports it) and spa_pillar_topk alone (an event).
+    Every output ends bit for bit equal to the same call made alone, so no
+    buffer was rewritten while a launch still read it."""
+    def wl(name, B, nv, seed):
+        return synth.Workload(name=name, batch=B, num_qo_heads=16, num_kv_heads=8, head_dim=128,
+                              dtype="bf16", spec_k=4, sparsity=Fraction(1, 10),
+                              lengths=("uniform", 300, 2500), n_verify=nv, seed=seed)
+    mixed = synth.make_batch(wl("rel-mixed", 7, 2, 91), device=DEV)
+    drafts = synth.make_batch(wl("rel-draft", 6, 0, 92), device=DEV, is_verify=[False] * 6)
+    verify = synth.make_batch(wl("rel-verify", 3, 3, 93), device=DEV, is_verify=[True] * 3)
+    bm, bdr, bv = bd.StepBuffers(mixed), bd.StepBuffers(drafts), bd.StepBuffers(verify)
+    k, Hq, Hkv = 4, 16, 8
+    topk_idx = torch.full_like(bv.idx, -5)
+
+    def topk_call():
+        bd.pillar_topk(verify.B, k, Hq, Hkv, 1, k, verify.seq_lens, verify.idx_count, bv.logits,
+                       bv.h_logits_off, bv.lse, topk_idx, verify.idx_off, bv.ws)
+
+    def outputs():
+        return [to_np(t).copy() for t in (bm.o, bm.lse, bm.logits, bm.idx, bdr.o, bdr.lse,
+                                          bv.o, bv.lse, bv.logits, bv.idx, topk_idx)]
+
+    for f in (bm.step, bdr.step, bv.step, topk_call):
+        f()
+        torch.cuda.synchronize()
+    alone = outputs()
+    for _ in range(15):
+        bm.step()
+        bdr.step()
+        bv.step()
+        topk_call()
+    torch.cuda.synchronize()
+    for i, (a, g) in enumerate(zip(alone, outputs())):
+        assert np.array_equal(a.view(np.uint8), g.view(np.uint8)), f"output {i} differs"
