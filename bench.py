@@ -231,7 +231,10 @@ def sparsity_sweep(w, dev, steps: int, warmup: int):
         ws = replace(w, sparsity=s, name=f"{w.name}-draft-only-s{float(s)}")
         b = synth.uniform_batch(ws, w.batch, L, [0] * w.batch, device=dev, seed=w.seed)
         bufs = bd.StepBuffers(b)
-        us = _time_steps(bufs.step, steps, warmup)
+        # at least 50 warm-up and 200 timed steps: over a short window the
+        # first tens of calls on a new batch, still slow, set the average of
+        # steps this short
+        us = _time_steps(bufs.step, max(steps, 200), max(warmup, 50))
         bd.profile_reset()
         bd.profile_enable((1 << len(bd.PROF_NAMES)) - 1)
         for _ in range(10):
