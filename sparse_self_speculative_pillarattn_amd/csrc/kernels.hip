@@ -1070,40 +1070,40 @@ __device__ __forceinline__ void select_topk(const float* scores, int L, int K, i
     shift = HIST_SHIFT - 4;
     mask = 0xffffffffu << HIST_SHIFT;
   } else {
-  // bits shared by every key: AND and OR over the block
-  if (tid == 0) {
-    sv[4] = 0xffffffffu;
-    sv[5] = 0u;
-  }
-  __syncthreads();
-  {
-    uint32_t va = 0xffffffffu, vo = 0u;
-    each_chunk([&](int c0) {
-      const int j0 = c0 + KPT * tid;
-#pragma unroll
-      for (int m = 0; m < KPT; ++m)
-        if (j0 + m < L) {
-          va &= key[m];
-          vo |= key[m];
-        }
-    });
-    va = row_and_u32(va);
-    vo = row_or_u32(vo);
-    if ((lane & 15) == 0) {
-      atomicAnd(&sv[4], va);
-      atomicOr(&sv[5], vo);
+    // bits shared by every key: AND and OR over the block
+    if (tid == 0) {
+      sv[4] = 0xffffffffu;
+      sv[5] = 0u;
     }
-  }
-  if (tid == 0) {
-    sv[0] = 0u;
-    sv[1] = (uint32_t)K;
-  }
-  __syncthreads();
-  const uint32_t diff = sv[4] ^ sv[5];
-  shift = diff == 0u ? 0 : (31 - __builtin_clz(diff)) / 4 * 4;  // top differing digit
-  mask = shift >= 28 ? 0u : 0xffffffffu << (shift + 4);
-  if (tid == 0) sv[0] = sv[4] & mask;  // the shared leading digits
-  __syncthreads();
+    __syncthreads();
+    {
+      uint32_t va = 0xffffffffu, vo = 0u;
+      each_chunk([&](int c0) {
+        const int j0 = c0 + KPT * tid;
+#pragma unroll
+        for (int m = 0; m < KPT; ++m)
+          if (j0 + m < L) {
+            va &= key[m];
+            vo |= key[m];
+          }
+      });
+      va = row_and_u32(va);
+      vo = row_or_u32(vo);
+      if ((lane & 15) == 0) {
+        atomicAnd(&sv[4], va);
+        atomicOr(&sv[5], vo);
+      }
+    }
+    if (tid == 0) {
+      sv[0] = 0u;
+      sv[1] = (uint32_t)K;
+    }
+    __syncthreads();
+    const uint32_t diff = sv[4] ^ sv[5];
+    shift = diff == 0u ? 0 : (31 - __builtin_clz(diff)) / 4 * 4;  // top differing digit
+    mask = shift >= 28 ? 0u : 0xffffffffu << (shift + 4);
+    if (tid == 0) sv[0] = sv[4] & mask;  // the shared leading digits
+    __syncthreads();
   }
   // a histogram bin small enough already goes straight to the direct ranking
   bool finish = hist != nullptr && sv[2] <= (uint32_t)SELECT_FINISH;
