@@ -129,6 +129,22 @@ def test_workspace_bytes_matches_call_requirement(lib):
     assert _unified(lib, lay, ws_bytes=need - 1) == bd.SPA_ERR_WORKSPACE_TOO_SMALL
 
 
+def test_workspace_holds_a_histogram_per_selected_row(lib):
+    """Turning a draft into a verify request adds, besides its averaged
+    scores, one 2048-bin uint32 score histogram per KV head to the workspace
+    (the post-pass counts into it, the selection starts from it)."""
+    lay = _lay()
+    lens = np.array([100, 100], np.int32)
+    cnt = np.array([5, 5], np.int32)
+
+    def need(ver):
+        v = np.array(ver, np.uint8)
+        return lib.spa_workspace_bytes(C.byref(lay), 2, 4, v.ctypes.data_as(C.c_void_p),
+                                       lens.ctypes.data_as(C.c_void_p),
+                                       cnt.ctypes.data_as(C.c_void_p))
+    assert need([1, 1]) - need([1, 0]) >= lay.num_kv_heads * 2048 * 4
+
+
 def test_set_split_bounds(lib):
     assert lib.spa_set_split(-1, 0) == bd.SPA_ERR_INVALID_ARG
     assert lib.spa_set_split(4096, 0) == bd.SPA_ERR_INVALID_ARG
