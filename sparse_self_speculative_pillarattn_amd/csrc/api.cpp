@@ -147,24 +147,30 @@ int device_cus() {
   return cus[dev];
 }
 
-// Positions per verify item.  Unless set by spa_set_split: the longest of
-// 2048, 1024 and 512 that still gives the verify requests at least 1.5 items
-// per CU.  A batch with few or short verify requests then spreads its long
-// items over the chip instead of leaving most CUs to the drafts (the
-// Qwen3-1.7B-shaped batch: 119 -> 96 us), while larger batches keep the
-// longer chunks, which need fewer split-K partials.
+// Positions per verify item.  Unless set by spa_set_split: 2048 when the
+// verify requests bring at least two and a half such chunks per CU (positions
+// times KV heads over the CU count), else 512.  Measured in steady state
+// (200 steps after 60 warm-up, best of three interleaved runs), 2048 / 1024 /
+// 512-position chunks: Qwen3-8B-shaped batch (3584 positions per CU)
+// 190.6 / 192.5 / 187.0 us, Qwen3-1.7B-shaped (1438) 86.3 at 1024, 83.3 at
+// 512, Qwen3-14B-shaped (7191) 551 / 571 / 609 us, long context (6466) 356 /
+// 358 us (768: 364).  Short chunks spread a light verify load over the chip
+// and shorten the launch's tail; heavy loads keep the long chunks, which need
+// fewer split-K partials and merges.
 int verify_chunk(const std::vector<Req>& rq, int Hkv) {
   const int v = g_verify_chunk.load();
   if (v > 0) return std::min(v, VERIFY_MAX_CHUNK);
-  const int64_t target = 3 * (int64_t)device_cus() / 2;
-  int c = DEFAULT_VERIFY_CHUNK;
-  while (c > MIN_AUTO_VERIFY_CHUNK) {
-    int64_t n = 0;
-    for (const Req& q : rq)
-      if (q.verify) n += (q.L + c - 1) / c;
-    if (n * Hkv >= target) break;
-    c /= 2;
-  }
+  int64_t positions = 0;
+  int longest = 0;
+  for (const Req& q : rq)
+    if (q.verify) {
+      positions += q.L;
+      longest = std::max(longest, q.L);
+    }
+  const int64_t per_cu = positions * Hkv / device_cus();
+  int c = 2 * per_cu >= 5 * (int64_t)DEFAULT_VERIFY_CHUNK ? DEFAULT_VERIFY_CHUNK : MIN_AUTO_VERIFY_CHUNK;
+  // a request may not need more split-K chunks than a merge takes
+  while (c < DEFAULT_VERIFY_CHUNK && (longest + c - 1) / c > MAX_MERGE_CHUNKS) c *= 2;
   return c;
 }
 int draft_chunk() {
