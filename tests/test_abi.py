@@ -145,6 +145,21 @@ def test_workspace_holds_a_histogram_per_selected_row(lib):
     assert need([1, 1]) - need([1, 0]) >= lay.num_kv_heads * 2048 * 4
 
 
+def test_light_verify_load_with_a_very_long_request_is_planned(lib):
+    """A light verify load gets 512-position chunks, but not so many that one
+    request needs more than the 256 split-K chunks a merge takes: a lone
+    140,000-token verify request is still planned (longer chunks)."""
+    lay = _lay(page_table_stride=1 << 20)
+    for L in (131072, 140000, 1 << 19):
+        ver = np.array([1], np.uint8)
+        lens = np.array([L], np.int32)
+        cnt = np.array([L // 20], np.int32)
+        need = lib.spa_workspace_bytes(C.byref(lay), 1, 4, ver.ctypes.data_as(C.c_void_p),
+                                       lens.ctypes.data_as(C.c_void_p),
+                                       cnt.ctypes.data_as(C.c_void_p))
+        assert need > 0, (L, lib.spa_last_error())
+
+
 def test_set_split_bounds(lib):
     assert lib.spa_set_split(-1, 0) == bd.SPA_ERR_INVALID_ARG
     assert lib.spa_set_split(4096, 0) == bd.SPA_ERR_INVALID_ARG
