@@ -641,6 +641,8 @@ def main():
                      "achieved": round(attn_gbps, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(attn_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                     # the bytes the launch really moves (counted), per second
+                     "traffic_gbps": round(traffic / (attn_us * 1e-6) / 1e9, 1) if traffic else None,
                      "algorithmic_bytes_per_launch": attn_bytes,
                      "launch_us": round(attn_us, 2), "launches": n_span if overlapped else n_attn,
                      "verify_launch_us": round(verify_us, 2),
