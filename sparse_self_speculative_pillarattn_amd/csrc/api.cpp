@@ -287,8 +287,8 @@ int32_t plan_size(const Shape& s, const std::vector<Req>& rq, bool attn, bool to
   pl->h_bytes = h;
   // workspace layout
   size_t o = 0;
-  pl->off_part_o = o;
-  o = align_up(o + (size_t)part_rows * D * 4, 256);
+  pl->off_part_o = o;  // partial outputs in the output type
+  o = align_up(o + (size_t)part_rows * D * esz, 256);
   pl->off_part_ml = o;
   o = align_up(o + (size_t)part_rows * 2 * 4, 256);
   pl->off_pbar = o;
@@ -668,7 +668,7 @@ int32_t run(const Shape& s, const std::vector<Req>& rq, const Plan& pl, const Bu
   plan_write(s, rq, pl, static_cast<char*>(slot->host));
   const char* plan = static_cast<const char*>(slot->dev);
   char* ws = static_cast<char*>(d_ws);
-  float* part_o = reinterpret_cast<float*>(ws + pl.off_part_o);
+  void* part_o = ws + pl.off_part_o;
   float* part_ml = reinterpret_cast<float*>(ws + pl.off_part_ml);
   hipError_t e;
   Side* side = nullptr;

@@ -67,6 +67,19 @@ struct Piece<float> {
 
 template <typename T>
 __device__ __forceinline__ void store_out(T* dst, float v);
+// Four consecutive elements widened to float (bf16 as raw uint16 bits).
+template <typename T>
+__device__ __forceinline__ float4 load4(const T* src);
+template <>
+__device__ __forceinline__ float4 load4<uint16_t>(const uint16_t* src) {
+  const uint2 v = *reinterpret_cast<const uint2*>(src);
+  return make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u),
+                     __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u));
+}
+template <>
+__device__ __forceinline__ float4 load4<float>(const float* src) {
+  return *reinterpret_cast<const float4*>(src);
+}
 template <>
 __device__ __forceinline__ void store_out<uint16_t>(uint16_t* dst, float v) {
   *dst = (uint16_t)f2bf(v);
@@ -480,12 +493,17 @@ __device__ void dma_consumer(const AttnParams& p, const Item& it, char* smem,
     if (q4 == 0)
       p.lse[(int64_t)(it.row0 + qi) * Hq + h] = l_tot > 0.f ? m_run + logf(l_tot) : NEG_INF;
   } else {
+    // the chunk's own normalised output, rounded to bf16 like O itself; the
+    // merge weighs it by the chunk's share of the row's softmax mass
     const int64_t pr = it.part_row0 + (int64_t)it.split * R + rho;
-    float* po = p.part_o + pr * D;
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    uint16_t* po = reinterpret_cast<uint16_t*>(p.part_o) + pr * D;
 #pragma unroll
-    for (int dd = 0; dd < DT; ++dd)
-      *reinterpret_cast<float4*>(po + 16 * dd + 4 * q4) =
-          make_float4(oacc[dd][0], oacc[dd][1], oacc[dd][2], oacc[dd][3]);
+    for (int dd = 0; dd < DT; ++dd) {
+      const uint32_t b0 = f2bf(oacc[dd][0] * inv), b1 = f2bf(oacc[dd][1] * inv);
+      const uint32_t b2 = f2bf(oacc[dd][2] * inv), b3 = f2bf(oacc[dd][3] * inv);
+      *reinterpret_cast<uint2*>(po + 16 * dd + 4 * q4) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+    }
     if (q4 == 0) {
       p.part_ml[2 * pr] = m_run;
       p.part_ml[2 * pr + 1] = l_tot;
@@ -721,7 +739,7 @@ __device__ void gather_tile_valu(const AttnParams& p, const Item& it, char* smem
       if (d == 0) p.lse[orow] = l > 0.f ? m + logf(l) : NEG_INF;
     } else {
       const int64_t pr = it.part_row0 + (int64_t)it.split * Rr + rho0 + hh;
-      p.part_o[pr * D + d] = acc;
+      store_out<T>(reinterpret_cast<T*>(p.part_o) + pr * D + d, l > 0.f ? acc / l : 0.f);
       if (d == 0) {
         p.part_ml[2 * pr] = m;
         p.part_ml[2 * pr + 1] = l;
@@ -857,10 +875,12 @@ __device__ void merge_rows(const PostParams& p, const PostItem& it, char* smem) 
       }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) ls += __shfl_xor(ls, off);
+    // partials are each chunk's normalised output: weight = its share of the
+    // row's softmax mass, l_s e^{m_s - m*} / l*
     const float inv = ls > 0.f ? 1.f / ls : 0.f;
     for (int sidx = lane; sidx < ns; sidx += 64) {
       const float m = pr[2 * sidx];
-      pr[2 * sidx] = (m == NEG_INF || inv == 0.f) ? 0.f : fast_exp2((m - mx) * LOG2E) * inv;
+      pr[2 * sidx] = (m == NEG_INF || inv == 0.f) ? 0.f : fast_exp2((m - mx) * LOG2E) * pr[2 * sidx + 1] * inv;
     }
     if (lane == 0) {
       const int rho = rho0 + rr, qi = rho / G, hh = rho % G;
@@ -871,15 +891,15 @@ __device__ void merge_rows(const PostParams& p, const PostItem& it, char* smem) 
   if (tid >= nr * D4) return;
   const int rr = tid / D4, d4 = tid % D4;
   const int rho = rho0 + rr;
-  const float* src = p.part_o + (it.part_row0 + rho) * D + 4 * d4;
+  // partials are stored in the output's type (bf16 or fp32)
+  const T* src = reinterpret_cast<const T*>(p.part_o) + (it.part_row0 + rho) * D + 4 * d4;
   const int64_t sstride = (int64_t)R * D;
   const float* w = w_s + 2 * rr * ns;  // weight of chunk s at w[2 s]
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int s0 = 0; s0 < ns; s0 += 8) {
     float4 o[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
-      o[u] = *reinterpret_cast<const float4*>(src + min(s0 + u, ns - 1) * sstride);
+    for (int u = 0; u < 8; ++u) o[u] = load4<T>(src + min(s0 + u, ns - 1) * sstride);
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const float wu = (s0 + u < ns) ? w[2 * (s0 + u)] : 0.f;

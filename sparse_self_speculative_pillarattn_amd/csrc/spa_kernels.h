@@ -19,7 +19,7 @@ struct AttnParams {
   void* o;
   float* lse;
   float* logits;
-  float* part_o;
+  void* part_o;        // split-K partial outputs, normalised, in the output type [part_rows][d]
   float* part_ml;
   int32_t Hq, Hkv, G, k;
   float sm_scale;
@@ -44,7 +44,7 @@ struct AttnParams {
 
 struct PostParams {
   const PostItem* items;  // pinned host plan, read in place
-  const float* part_o;
+  const void* part_o;  // split-K partial outputs (see AttnParams)
   const float* part_ml;
   void* o;
   float* lse;
