@@ -63,8 +63,10 @@
  *   Threads     Entry points may be called from several host threads.
  *   Graphs      Calls are not capturable into HIP graphs: each call writes its
  *               work plan into pinned host memory at call time (a replay would
- *               read whatever a later call left there) and may wait on the
- *               event of an earlier call that used the same plan buffer.
+ *               read whatever a later call left there) and may first wait until
+ *               the GPU has finished reading that buffer for an earlier call
+ *               (an event, or a sequence number the earlier call's kernels
+ *               store into mapped host memory).
  *   B == 0      is a successful no-op.
  */
 #ifndef SPA_H_
