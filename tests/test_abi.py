@@ -16,6 +16,9 @@ FAKE = C.c_void_p(0x1000)  # never dereferenced on the paths below
 
 @pytest.fixture(scope="module")
 def lib():
+    if not os.path.exists(bd.LIB_PATH):  # a fresh checkout: cross-compile it (no GPU needed)
+        from sparse_self_speculative_pillarattn_amd import build
+        build.build()
     return bd.load()
 
 
