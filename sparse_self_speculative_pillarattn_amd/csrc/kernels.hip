@@ -1006,7 +1006,7 @@ template <int KPT>
 __device__ __forceinline__ void select_topk(const float* scores, int L, int K, int32_t* out, char* smem,
                                             const uint32_t* hist = nullptr) {
   static_assert(KPT % 4 == 0 && KPT <= 8, "keys are loaded four at a time; nibble counters");
-  uint32_t* sv = reinterpret_cast<uint32_t*>(smem);  // prefix, rem, bucket count, and/or
+  uint32_t* sv = reinterpret_cast<uint32_t*>(smem);  // prefix, rem, bucket count, gathered, and/or
   uint32_t* wsum = sv + 8;                           // [16] block scans
   uint32_t* tab = wsum + 16;                         // [waves * 4 rows][16 digits]
   uint32_t* ckey = tab + 16 * 64;                    // [SELECT_FINISH] candidate keys
@@ -1192,23 +1192,20 @@ __device__ __forceinline__ void select_topk(const float* scores, int L, int K, i
     }
   }
   if (finish) {
-    // gather the keys of the chosen bucket and rank them in one wave
+    // gather the keys of the chosen bucket (in any order: only their values
+    // are ranked) through an LDS counter, so the walk needs no block scans,
+    // and rank them in one wave
     const uint32_t prefix = sv[0];
-    uint32_t base = 0u;
+    if (tid == 0) sv[3] = 0u;
+    __syncthreads();
     each_chunk([&](int c0) {
       const int j0 = c0 + KPT * tid;
-      uint32_t n = 0u;
-#pragma unroll
-      for (int m = 0; m < KPT; ++m) n += (j0 + m < L && (key[m] & mask) == prefix) ? 1u : 0u;
-      uint32_t tot;
-      uint32_t pos = base + block_exclusive_scan(n, wsum, &tot);
 #pragma unroll
       for (int m = 0; m < KPT; ++m)
         if (j0 + m < L && (key[m] & mask) == prefix) {
+          const uint32_t pos = atomicAdd(&sv[3], 1u);
           if (pos < (uint32_t)SELECT_FINISH) ckey[pos] = key[m];
-          ++pos;
         }
-      base += tot;
     });
     __syncthreads();
     if (wave == 0) {
