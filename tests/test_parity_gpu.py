@@ -438,3 +438,54 @@ def test_plan_slots_released_every_way():
     torch.cuda.synchronize()
     for i, (a, g) in enumerate(zip(alone, outputs())):
         assert np.array_equal(a.view(np.uint8), g.view(np.uint8)), f"output {i} differs"
+
+
+def test_host_threads_share_the_plan_ring():
+    """Three host threads, each stepping its own batch on its own stream 25
+    times without synchronising (ctypes releases the interpreter lock during
+    the call, so the calls interleave inside the library), end bit for bit
+    equal to each batch stepped alone: the plan buffers, their release words
+    and the item counters are never shared by calls in flight."""
+    import threading
+    shapes = [(5, 2, 71), (7, 0, 72), (4, 4, 73)]
+    batches = []
+    for B, nv, seed in shapes:
+        w = synth.Workload(name=f"threads{seed}", batch=B, num_qo_heads=16, num_kv_heads=8,
+                           head_dim=128, dtype="bf16", spec_k=4, sparsity=Fraction(1, 10),
+                           lengths=("uniform", 200, 2200), n_verify=nv, seed=seed)
+        ver = [False] * B if nv == 0 else ([True] * B if nv == B else None)
+        batches.append(synth.make_batch(w, device=DEV, is_verify=ver))
+    alone = []
+    for b in batches:
+        bufs = bd.StepBuffers(b)
+        bufs.step()
+        torch.cuda.synchronize()
+        alone.append([to_np(t).copy() for t in (bufs.o, bufs.lse, bufs.logits, bufs.idx)])
+    bufs = [bd.StepBuffers(b) for b in batches]
+    streams = [torch.cuda.Stream() for _ in batches]
+    torch.cuda.synchronize()
+    errors = []
+
+    def run(bu, st):
+        try:
+            torch.cuda.set_device(DEV)
+            with torch.cuda.stream(st):
+                for _ in range(25):
+                    bu.step()
+        except Exception as e:  # reported below, on the test's thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=run, args=(bu, st)) for bu, st in zip(bufs, streams)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=120)
+    assert not any(t.is_alive() for t in threads), "a stepping thread did not finish"
+    assert not errors, errors
+    torch.cuda.synchronize()
+    for want, bu, b in zip(alone, bufs, batches):
+        got = [to_np(t) for t in (bu.o, bu.lse, bu.logits, bu.idx)]
+        for name, a, g in zip(("O", "LSE", "logits", "idx"), want, got):
+            if name == "logits" and not any(b.is_verify):
+                continue  # a draft-only batch writes no logits (its buffer is a placeholder)
+            assert np.array_equal(a.view(np.uint8), g.view(np.uint8)), f"{name} differs"
