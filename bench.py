@@ -649,6 +649,11 @@ def main():
                      "draft_launch_us": round(draft_us, 2) if draft_us else None},
         "mfma": mfma,
         "cpu_baseline": cpu,
+        "env": {"device": torch.cuda.get_device_name(dev),
+                "gcn_arch": getattr(torch.cuda.get_device_properties(dev), "gcnArchName", None),
+                "compute_units": torch.cuda.get_device_properties(dev).multi_processor_count,
+                "hip_runtime": torch.version.hip, "torch": torch.__version__,
+                "seed": w.seed, "libspa_abi": bd.abi_version()},
     }
     print(json.dumps(line), flush=True)
 
