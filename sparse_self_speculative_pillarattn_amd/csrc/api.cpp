@@ -12,6 +12,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <chrono>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -517,13 +518,18 @@ struct ProfSpan {
 // mapped, coherent host array as it starts, and the host waits for that value
 // instead.  Recording an event costs the stream a gap of about 5 us before the
 // next call's first launch; the store costs nothing measurable.
-enum SlotWait : int { WAIT_NONE = 0, WAIT_EVENT = 1, WAIT_SIGNAL = 2 };
+//
+// A call that returns an error after acquiring its slot leaves the slot
+// marked WAIT_DRAIN: before reuse the host drains the slot's device, since a
+// launch issued before the error may still read the slot.
+enum SlotWait : int { WAIT_NONE = 0, WAIT_EVENT = 1, WAIT_SIGNAL = 2, WAIT_DRAIN = 3 };
 struct PlanSlot {
   char* host = nullptr;
   char* dev = nullptr;
   hipEvent_t ev = nullptr;
   int wait = WAIT_NONE;
   uint64_t seq = 0;  // WAIT_SIGNAL: the value the post-pass stores
+  int device = 0;    // device of the call that used the slot
 };
 constexpr int RING = 16;
 static_assert(2 * RING <= TICKET_SETS, "two attention item counters per plan slot");
@@ -537,13 +543,38 @@ uint64_t* g_done_host = nullptr;  // [RING], written by the device
 uint64_t* g_done_dev = nullptr;
 uint64_t g_seq = 0;
 
+// Waits for all work on `device`; once it has drained, every launch of the
+// call that used a slot on it has finished.
+int32_t drain_device(int device) {
+  int cur = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e == hipSuccess && cur != device) e = hipSetDevice(device);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (cur != device) (void)hipSetDevice(cur);
+  if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("plan slot wait: ") + hipGetErrorString(e));
+  return SPA_OK;
+}
+
 int32_t wait_slot(PlanSlot& s) {
   if (s.wait == WAIT_EVENT) {
     const hipError_t e = hipEventSynchronize(s.ev);
     if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("plan slot wait: ") + hipGetErrorString(e));
   } else if (s.wait == WAIT_SIGNAL) {
     const uint64_t* w = g_done_host + (&s - g_ring);
-    while (__atomic_load_n(w, __ATOMIC_ACQUIRE) < s.seq) std::this_thread::yield();
+    const auto t0 = std::chrono::steady_clock::now();
+    while (__atomic_load_n(w, __ATOMIC_ACQUIRE) < s.seq) {
+      std::this_thread::yield();
+      // A long wait drains the device instead, so that a failed device is
+      // reported as an error rather than spun on.
+      if (std::chrono::steady_clock::now() - t0 > std::chrono::milliseconds(500)) {
+        const int32_t rc = drain_device(s.device);
+        if (rc) return rc;
+        break;
+      }
+    }
+  } else if (s.wait == WAIT_DRAIN) {
+    const int32_t rc = drain_device(s.device);
+    if (rc) return rc;
   }
   s.wait = WAIT_NONE;
   return SPA_OK;
@@ -603,6 +634,8 @@ int32_t acquire_slot(const Plan& pl, PlanSlot** out) {
   const int32_t rc = wait_slot(s);
   if (rc) return rc;
   s.seq = ++g_seq;
+  if (hipGetDevice(&s.device) != hipSuccess) return fail(SPA_ERR_HIP, "no current device");
+  s.wait = WAIT_DRAIN;  // until the call has queued its release
   if (!s.ev) {
     // The event only tells the host that the GPU has finished reading the
     // slot (host memory, read by the kernels; nothing flows back through it),
