@@ -66,7 +66,9 @@
  *               read whatever a later call left there) and may first wait until
  *               the GPU has finished reading that buffer for an earlier call
  *               (an event, or a sequence number the earlier call's kernels
- *               store into mapped host memory).
+ *               store into mapped host memory; after half a second without
+ *               it, or when the earlier call failed after taking the buffer,
+ *               the wait drains that call's device instead).
  *   B == 0      is a successful no-op.
  */
 #ifndef SPA_H_
