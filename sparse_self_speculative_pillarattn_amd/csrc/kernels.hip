@@ -1261,6 +1261,7 @@ __device__ __forceinline__ void select_topk(const float* scores, int L, int K, i
 }
 
 constexpr int POST_THREADS = 256;
+constexpr int AVG_PREFETCH = 8;  // averaged terms whose logits load before the LSE rebuild
 
 // Dynamic LDS of an averaging item: the LSE (4 B) and logits row offset (8 B)
 // of every averaged term, then the row's 2048-bin score histogram.
@@ -1294,6 +1295,22 @@ __global__ void __launch_bounds__(POST_THREADS) post_kernel(PostParams p) {
   const int L = it.L;
   float* lse2_s = reinterpret_cast<float*>(smem);
   int64_t* rowoff_s = reinterpret_cast<int64_t*>(smem + (terms * 4 + 7) / 8 * 8);
+  const float* lg = p.logits + it.logits_off;
+  const int j4 = it.j0 + 4 * tid;
+  const int ne = max(0, min(4, it.j1 - j4));  // positions of this thread
+  // The logits of the first AVG_PREFETCH terms do not depend on the LSE: they
+  // are requested before it is rebuilt, so that their round trip overlaps the
+  // one of the (m, l) partials.
+  f32x4u pre[AVG_PREFETCH];
+  if (ne == 4) {
+#pragma unroll
+    for (int x = 0; x < AVG_PREFETCH; ++x)
+      if (x < terms) {
+        const int i = a + x / G, hh = x % G;
+        pre[x] = __builtin_nontemporal_load(
+            reinterpret_cast<const f32x4u*>(lg + ((int64_t)i * Hq + it.g * G + hh) * L + j4));
+      }
+  }
   if (it.nchunk == 1) {
     for (int x = tid; x < terms; x += blockDim.x) {
       const int i = a + x / G, hh = x % G;
@@ -1359,16 +1376,22 @@ __global__ void __launch_bounds__(POST_THREADS) post_kernel(PostParams p) {
   if (keep_hist)
     for (int b = tid; b < HIST_BINS; b += blockDim.x) hist_s[b] = 0u;
   __syncthreads();
-  const float* lg = p.logits + it.logits_off;
   float* pbar = p.pbar + it.pbar_off;
   const float inv = 1.f / (float)terms;
-  const int j4 = it.j0 + 4 * tid;
-  const int ne = max(0, min(4, it.j1 - j4));  // positions of this thread
   float res[4] = {0.f, 0.f, 0.f, 0.f};
   if (ne == 4) {
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int x = 0; x < AVG_PREFETCH; ++x)
+      if (x < terms) {
+        const float l2 = lse2_s[x];
+        const float vv[4] = {pre[x].x, pre[x].y, pre[x].z, pre[x].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          acc[e] += (vv[e] == NEG_INF || l2 == NEG_INF) ? 0.f : fast_exp2(fmaf(vv[e], LOG2E, -l2));
+      }
 #pragma unroll 16
-    for (int x = 0; x < terms; ++x) {
+    for (int x = AVG_PREFETCH; x < terms; ++x) {
       // each logit is read once here: a streaming load, like the KV rows.
       // A row starts 16-byte aligned only when L and the request's logits
       // offset are multiples of 4, so the load type asks for 4-byte alignment
