@@ -80,6 +80,7 @@ struct Plan {
   int n_merge_d = 0;            // draft merges, run after the join
   int n_merge = 0, n_avg = 0, n_sel = 0;
   int n_hist = 0;  // selected rows with a score histogram (all of them when the call has attention)
+  int max_sel_len = 0;  // longest selected row
   int64_t part_rows = 0;
   int64_t pbar_elems = 0;
   // pinned plan layout
@@ -244,6 +245,7 @@ int32_t plan_size(const Shape& s, const std::vector<Req>& rq, bool attn, bool to
       if (q.verify) {
         pl->n_avg += Hkv * avg_parts(q.L);
         pl->n_sel += Hkv;
+        pl->max_sel_len = std::max(pl->max_sel_len, q.L);
         // the histogram is cleared by the attention launch, so only a call
         // with one keeps it
         if (attn) pl->n_hist += Hkv;
@@ -819,6 +821,7 @@ int32_t run(const Shape& s, const std::vector<Req>& rq, const Plan& pl, const Bu
     sp.pbar = reinterpret_cast<const float*>(ws + pl.off_pbar);
     sp.idx_out = b.idx_out;
     sp.hist = hist;
+    sp.bm_bits = select_bitmap_bits(pl.max_sel_len);
     {
       ProfScope ps(PROF_SELECT, st);
       e = launch_select(sp, pl.n_sel, st);

@@ -982,6 +982,14 @@ __device__ __forceinline__ uint32_t row_or_u32(uint32_t v) {
 }
 
 constexpr int SELECT_FINISH = 64;  // candidates ranked directly by one wave
+constexpr int SELECT_BITMAP_BITS = 1 << 18;  // longest row whose selected positions are marked in LDS
+
+// Bits of the selection launch's position bitmap for rows of at most max_len
+// scores: none when every row fits the register span.
+int select_bitmap_bits(int max_len) {
+  if (max_len <= SELECT_SPAN) return 0;
+  return std::min((max_len + 31) / 32 * 32, SELECT_BITMAP_BITS);
+}
 constexpr int SELECT_BATCH = 4;    // chunks loaded per batch when a row is longer than one chunk
 
 // Top-K of L non-negative fp32 scores (their bit patterns order like the
@@ -1004,7 +1012,8 @@ constexpr int SELECT_BATCH = 4;    // chunks loaded per batch when a row is long
 //     (each a block-wide round, and on rows of many chunks a re-read).
 template <int KPT>
 __device__ __forceinline__ void select_topk(const float* scores, int L, int K, int32_t* out, char* smem,
-                                            const uint32_t* hist = nullptr) {
+                                            const uint32_t* hist = nullptr, uint32_t* bm = nullptr,
+                                            int32_t* cpos = nullptr, int bm_bits = 0) {
   static_assert(KPT % 4 == 0 && KPT <= 8, "keys are loaded four at a time; nibble counters");
   uint32_t* sv = reinterpret_cast<uint32_t*>(smem);  // prefix, rem, bucket count, gathered, and/or
   uint32_t* wsum = sv + 8;                           // [16] block scans
@@ -1191,22 +1200,51 @@ __device__ __forceinline__ void select_topk(const float* scores, int L, int K, i
       break;
     }
   }
+  // A row longer than the register span, with a position bitmap in LDS: the
+  // gather of the final bucket also marks every position above the bucket,
+  // the ranking marks the bucket's chosen positions, and the list is written
+  // from the bitmap instead of from a second pass over the row.
+  const bool use_bm = finish && bm != nullptr && cpos != nullptr && !resident && L <= bm_bits;
   if (finish) {
     // gather the keys of the chosen bucket (in any order: only their values
     // are ranked) through an LDS counter, so the walk needs no block scans,
     // and rank them in one wave
     const uint32_t prefix = sv[0];
     if (tid == 0) sv[3] = 0u;
+    if (use_bm)
+      for (int w = tid; w < (L + 31) >> 5; w += nthr) bm[w] = 0u;
     __syncthreads();
-    each_chunk([&](int c0) {
-      const int j0 = c0 + KPT * tid;
+    if (use_bm) {
+      each_chunk([&](int c0) {
+        const int j0 = c0 + KPT * tid;  // a multiple of 8: the thread's positions share one bitmap word
+        uint32_t above = 0u;
 #pragma unroll
-      for (int m = 0; m < KPT; ++m)
-        if (j0 + m < L && (key[m] & mask) == prefix) {
-          const uint32_t pos = atomicAdd(&sv[3], 1u);
-          if (pos < (uint32_t)SELECT_FINISH) ckey[pos] = key[m];
-        }
-    });
+        for (int m = 0; m < KPT; ++m)
+          if (j0 + m < L) {
+            const uint32_t hk = key[m] & mask;
+            if (hk == prefix) {
+              const uint32_t pos = atomicAdd(&sv[3], 1u);
+              if (pos < (uint32_t)SELECT_FINISH) {
+                ckey[pos] = key[m];
+                cpos[pos] = j0 + m;
+              }
+            } else if (hk > prefix) {
+              above |= 1u << ((j0 + m) & 31);
+            }
+          }
+        if (above != 0u) atomicOr(&bm[j0 >> 5], above);
+      });
+    } else {
+      each_chunk([&](int c0) {
+        const int j0 = c0 + KPT * tid;
+#pragma unroll
+        for (int m = 0; m < KPT; ++m)
+          if (j0 + m < L && (key[m] & mask) == prefix) {
+            const uint32_t pos = atomicAdd(&sv[3], 1u);
+            if (pos < (uint32_t)SELECT_FINISH) ckey[pos] = key[m];
+          }
+      });
+    }
     __syncthreads();
     if (wave == 0) {
       const int nc = (int)sv[2];
@@ -1224,6 +1262,41 @@ __device__ __forceinline__ void select_topk(const float* scores, int L, int K, i
       }
     }
     __syncthreads();
+    if (use_bm) {
+      if (wave == 0) {
+        // the bucket's keys above the K-th, and its equal keys in position
+        // order until the remaining count is taken
+        const int nc = min((int)sv[2], min((int)sv[3], SELECT_FINISH));
+        const uint32_t tau = sv[0], req = sv[1];
+        const uint32_t mine = lane < nc ? ckey[lane] : 0u;
+        const int mpos = lane < nc ? cpos[lane] : 0;
+        uint32_t before = 0u;
+        for (int j = 0; j < nc; ++j) {
+          const uint32_t o = (uint32_t)__builtin_amdgcn_readlane((int)mine, j);
+          const int op = __builtin_amdgcn_readlane(mpos, j);
+          before += (o == tau && op < mpos) ? 1u : 0u;
+        }
+        const bool take = lane < nc && (mine > tau || (mine == tau && before < req));
+        if (take && mpos >= 0 && mpos < L) atomicOr(&bm[mpos >> 5], 1u << (mpos & 31));
+      }
+      __syncthreads();
+      const int words = (L + 31) >> 5;
+      const int wpt = (words + nthr - 1) / nthr;
+      const int w0 = tid * wpt, w1 = min(w0 + wpt, words);
+      uint32_t cnt = 0u;
+      for (int w = w0; w < w1; ++w) cnt += (uint32_t)__popc(bm[w]);
+      uint32_t tot;
+      uint32_t pos = block_exclusive_scan(cnt, wsum, &tot);
+      for (int w = w0; w < w1; ++w) {
+        uint32_t b = bm[w];
+        while (b != 0u) {
+          const int t = __builtin_ctz(b);
+          b &= b - 1u;
+          if (pos < (uint32_t)K) out[pos++] = (w << 5) + t;
+        }
+      }
+      return;
+    }
   }
   const uint32_t tau = sv[0], rem = sv[1];
   uint32_t base_eq = 0, base_gt = 0;
@@ -1452,9 +1525,15 @@ static_assert(SELECT_THREADS * SELECT_KPT == SELECT_SPAN, "scores kept in regist
 
 __global__ void __launch_bounds__(SELECT_THREADS) select_kernel(SelectParams sp) {
   __shared__ __attribute__((aligned(16))) char smem[(24 + 16 * 64 + SELECT_FINISH) * 4];
+  // dynamic LDS (long rows only): the positions of the final bucket's keys,
+  // then the bitmap of a row's selected positions
+  extern __shared__ __attribute__((aligned(16))) char dyn[];
+  int32_t* cpos = sp.bm_bits > 0 ? reinterpret_cast<int32_t*>(dyn) : nullptr;
+  uint32_t* bm = sp.bm_bits > 0 ? reinterpret_cast<uint32_t*>(dyn + SELECT_FINISH * 4) : nullptr;
   const PostItem it = sp.items[blockIdx.x];
   const uint32_t* hist = (sp.hist && it.hist_slot >= 0) ? sp.hist + (int64_t)it.hist_slot * HIST_BINS : nullptr;
-  select_topk<SELECT_KPT>(sp.pbar + it.pbar_off, it.L, it.K, sp.idx_out + it.idx_off, smem, hist);
+  select_topk<SELECT_KPT>(sp.pbar + it.pbar_off, it.L, it.K, sp.idx_out + it.idx_off, smem, hist, bm, cpos,
+                          sp.bm_bits);
 }
 
 // ==========================================================================
@@ -1708,7 +1787,8 @@ hipError_t launch_attn(const AttnParams& params, int dtype, int head_dim, int ni
 
 hipError_t launch_select(const SelectParams& sp, int nitems, hipStream_t st) {
   if (nitems == 0) return hipSuccess;
-  hipLaunchKernelGGL(select_kernel, dim3(nitems), dim3(SELECT_THREADS), 0, st, sp);
+  const size_t dyn = sp.bm_bits > 0 ? SELECT_FINISH * 4 + (size_t)sp.bm_bits / 8 : 0;
+  hipLaunchKernelGGL(select_kernel, dim3(nitems), dim3(SELECT_THREADS), dyn, st, sp);
   return hipGetLastError();
 }
 

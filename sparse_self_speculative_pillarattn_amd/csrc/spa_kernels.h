@@ -67,6 +67,7 @@ struct SelectParams {
   const float* pbar;
   int32_t* idx_out;
   const uint32_t* hist;   // [slots][HIST_BINS] counts of the selected rows, or null
+  int bm_bits;            // LDS position bitmap of long rows (select_bitmap_bits), 0 for none
 };
 
 struct RecallParams {
@@ -99,6 +100,7 @@ hipError_t launch_attn(const AttnParams& p, int dtype, int head_dim, int nitems,
 hipError_t launch_post(const PostParams& p, int dtype, int head_dim, int nitems, size_t smem,
                        hipStream_t st);
 hipError_t launch_select(const SelectParams& sp, int nitems, hipStream_t st);
+int select_bitmap_bits(int max_len);
 // LDS bytes of the recallable-index launch for the longest context of a batch.
 size_t recall_smem_bytes(int max_len);
 size_t quality_smem_bytes(int max_len);

@@ -150,6 +150,40 @@ def test_long_row_all_scores_tied(oracle):
     assert np.array_equal(seg, np.tile(np.arange(K), (w.num_kv_heads, 1)))
 
 
+@pytest.mark.parametrize("K", [5, 15])
+def test_long_row_tie_across_the_kth_score(oracle, K):
+    """A 20,001-token verify request whose 12 highest scores tie: 12 spread
+    positions read one K/V slot whose keys point along the request's mean query
+    of each group.  Long rows are written from a bitmap of the selected
+    positions; with K = 5 the five lowest tied positions must be taken, with
+    K = 15 all twelve and the three next-highest."""
+    L = 20001
+    w = synth.Workload(name=f"long-tie-{K}", batch=2, num_qo_heads=8, num_kv_heads=2,
+                       head_dim=128, dtype="bf16", spec_k=2, sparsity=Fraction(1, 20),
+                       lengths=("fixed", L), n_verify=1, seed=91)
+    b = synth.make_batch(w)
+    r = int(np.nonzero(b.is_verify)[0][0])
+    tied = [100, 1700, 3000, 9000, 9001, 12000, 15000, 16000, 17000, 18000, 19000, 19500]
+    slot = int(b.page_table[r, tied[0]])
+    b.page_table[r, torch.tensor(tied)] = slot
+    G, d = w.num_qo_heads // w.num_kv_heads, w.head_dim
+    qr = b.q[b.q_indptr[r]:b.q_indptr[r + 1]].float()
+    for g in range(w.num_kv_heads):
+        u = qr[:, g * G:(g + 1) * G].reshape(-1, d).mean(dim=0)
+        b.k_pool[slot, g] = (8.0 * d ** 0.5 * u / u.norm()).to(b.k_pool.dtype)
+    b.idx_count[r] = K
+    print(f"[case] tie K={K} r={r} slot={slot}", flush=True)
+    ref = oracle.step(**parity.oracle_inputs(b))
+    gpu = run_unified(b.to(DEV))
+    parity.compare_step(oracle, b, gpu, ref)
+    seg = to_np(gpu["idx"])[b.idx_off[r]:b.idx_off[r] + w.num_kv_heads * K].reshape(w.num_kv_heads, K)
+    for g in range(w.num_kv_heads):
+        if K < len(tied):
+            assert seg[g].tolist() == tied[:K], (g, seg[g])
+        else:
+            assert set(tied) <= set(seg[g].tolist()), (g, seg[g])
+
+
 def test_topk_count_extremes(oracle):
     """K = 1 and K = L per verify request."""
     w = synth.Workload(name="kext", batch=2, num_qo_heads=8, num_kv_heads=2, head_dim=128,
