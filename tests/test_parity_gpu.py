@@ -119,12 +119,15 @@ def test_split_invariance(oracle, split):
 
 @pytest.mark.parametrize("L,s", [(8192, Fraction(1, 20)), (8193, Fraction(1, 20)),
                                  (12289, Fraction(1, 20)), (20001, Fraction(1, 50)),
-                                 (40000, Fraction(1, 20)), (30001, Fraction(1, 2))])
+                                 (40000, Fraction(1, 20)), (30001, Fraction(1, 2)),
+                                 (270001, Fraction(1, 50))])
 def test_long_rows(oracle, L, s):
     """Rows longer than one selection workgroup's registers (8192 scores),
     which the selection re-reads chunk by chunk after its histogram-seeded
     start.  Lengths around the boundary, odd lengths (rows not 16-byte
-    aligned), and a large K (half the row)."""
+    aligned), a large K (half the row), and a row longer than the selection's
+    LDS position bitmap (262,144 positions), which is compacted by a second
+    pass over the row instead."""
     w = synth.Workload(name=f"long-{L}", batch=3, num_qo_heads=8, num_kv_heads=2, head_dim=128,
                        dtype="bf16", spec_k=2, sparsity=s, lengths=("fixed", L), n_verify=2,
                        seed=L)
