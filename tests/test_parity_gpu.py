@@ -309,6 +309,39 @@ def test_sequential_entry_points_match_unified(oracle):
         assert np.array_equal(to_np(lsed[j]), ul[b.q_indptr[r]])
 
 
+@pytest.mark.parametrize("lens", [(20001, 40000), (8193, 9000)])
+def test_pillar_topk_alone_long_rows(oracle, lens):
+    """spa_pillar_topk on its own starts the selection without a score
+    histogram (it has no attention launch to count one); on rows longer than
+    the selection's registers it must still pick what the unified step picks
+    from the same logits and LSE, and what the oracle's scores allow."""
+    w = synth.Workload(name="topk-long", batch=3, num_qo_heads=8, num_kv_heads=2, head_dim=128,
+                       dtype="bf16", spec_k=3, sparsity=Fraction(1, 20), lengths=("fixed", 64),
+                       n_verify=2, seed=lens[0])
+    b = synth.make_batch(w, seq_lens=[lens[0], lens[1], 5000], is_verify=[1, 1, 0])
+    print(f"[case] topk alone lens={b.seq_lens}", flush=True)
+    ref = oracle.step(**parity.oracle_inputs(b))
+    uni = run_unified(b.to(DEV))
+    parity.compare_step(oracle, b, uni, ref)
+    k, Hq, Hkv = w.spec_k, w.num_qo_heads, w.num_kv_heads
+    ver = [r for r in range(b.B) if b.is_verify[r]]
+    lv = [b.seq_lens[r] for r in ver]
+    Kv = [b.idx_count[r] for r in ver]
+    loff = np.array([b.logits_off[r] for r in ver], dtype=np.int64)
+    lsev = torch.cat([uni["lse"][b.q_indptr[r]:b.q_indptr[r + 1]] for r in ver]).contiguous()
+    ioff = np.concatenate([[0], np.cumsum([Hkv * K for K in Kv])[:-1]]).astype(np.int64)
+    idxv = torch.full((int(sum(Hkv * K for K in Kv)),), -7, dtype=torch.int32, device=DEV)
+    lay = bd.layout(Hq, Hkv, w.head_dim, b.q.dtype, b.num_slots, b.stride)
+    nb = bd.workspace_bytes(lay, len(ver), k, [1] * len(ver), lv, Kv)
+    ws = bd.workspace(nb, DEV)
+    bd.pillar_topk(len(ver), k, Hq, Hkv, 1, k, lv, Kv, uni["logits"], loff, lsev, idxv, ioff, ws)
+    torch.cuda.synchronize()
+    got, want = to_np(idxv), to_np(uni["idx"])
+    for j, r in enumerate(ver):
+        assert np.array_equal(got[ioff[j]:ioff[j] + Hkv * Kv[j]],
+                              want[b.idx_off[r]:b.idx_off[r] + Hkv * Kv[j]]), f"request {r}"
+
+
 def test_chained_verify_then_draft(oracle):
     """A verify step's selected lists feed the next step, where the same
     requests draft over them."""
