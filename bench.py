@@ -461,8 +461,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(run with --gpus 1).", file=sys.stderr)
+        print("bench.py measures one GPU only: the step has no multi-GPU path; each GPU "
+              "would run its own share of the batch (run with --gpus 1).", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
