@@ -15,6 +15,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <type_traits>
 #include <mutex>
 #include <vector>
 
@@ -896,19 +897,28 @@ __device__ void merge_rows(const PostParams& p, const PostItem& it, char* smem) 
   const int64_t sstride = (int64_t)R * D;
   const float* w = w_s + 2 * rr * ns;  // weight of chunk s at w[2 s]
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int s0 = 0; s0 < ns; s0 += 8) {
-    float4 o[8];
+  // NB partials per round trip (entries past ns re-read the last partial at
+  // weight 0): 16 when there are more than 8, so that 16 chunks take one
+  auto merge_in = [&](auto nb) {
+    constexpr int NB = decltype(nb)::value;
+    for (int s0 = 0; s0 < ns; s0 += NB) {
+      float4 o[NB];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) o[u] = load4<T>(src + min(s0 + u, ns - 1) * sstride);
+      for (int u = 0; u < NB; ++u) o[u] = load4<T>(src + min(s0 + u, ns - 1) * sstride);
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const float wu = (s0 + u < ns) ? w[2 * (s0 + u)] : 0.f;
-      acc.x = fmaf(wu, o[u].x, acc.x);
-      acc.y = fmaf(wu, o[u].y, acc.y);
-      acc.z = fmaf(wu, o[u].z, acc.z);
-      acc.w = fmaf(wu, o[u].w, acc.w);
+      for (int u = 0; u < NB; ++u) {
+        const float wu = (s0 + u < ns) ? w[2 * (s0 + u)] : 0.f;
+        acc.x = fmaf(wu, o[u].x, acc.x);
+        acc.y = fmaf(wu, o[u].y, acc.y);
+        acc.z = fmaf(wu, o[u].z, acc.z);
+        acc.w = fmaf(wu, o[u].w, acc.w);
+      }
     }
-  }
+  };
+  if (ns > 8)
+    merge_in(std::integral_constant<int, 16>{});
+  else
+    merge_in(std::integral_constant<int, 8>{});
   const int qi = rho / G, hh = rho % G;
   const int64_t orow = (int64_t)(it.row0 + qi) * p.Hq + it.g * G + hh;
   T* dst = reinterpret_cast<T*>(p.o) + orow * D + 4 * d4;
