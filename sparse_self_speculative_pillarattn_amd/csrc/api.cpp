@@ -550,9 +550,10 @@ uint64_t g_seq = 0;
 int32_t drain_device(int device) {
   int cur = 0;
   hipError_t e = hipGetDevice(&cur);
-  if (e == hipSuccess && cur != device) e = hipSetDevice(device);
+  const bool switched = e == hipSuccess && cur != device;
+  if (switched) e = hipSetDevice(device);
   if (e == hipSuccess) e = hipDeviceSynchronize();
-  if (cur != device) (void)hipSetDevice(cur);
+  if (switched) (void)hipSetDevice(cur);
   if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("plan slot wait: ") + hipGetErrorString(e));
   return SPA_OK;
 }
