@@ -219,6 +219,20 @@ def _time_steps(fn, steps: int, warmup: int) -> float:
     return e0.elapsed_time(e1) / steps * 1e3
 
 
+def launch_times(run, names, n: int) -> dict:
+    """Mean microseconds of each named launch over n calls of run(opts), every
+    call with its own timing events (recorded on the launch stream)."""
+    props = torch.cuda.get_device_properties(torch.cuda.current_device())
+    opts = [bd.Options(num_cus=props.multi_processor_count, timing=names) for _ in range(n)]
+    for o in opts:
+        run(o)
+    torch.cuda.synchronize()
+    out = {}
+    for nm in names:
+        out[nm] = float(np.mean([o.elapsed_ms(nm) for o in opts])) * 1e3
+    return out
+
+
 def sparsity_sweep(w, dev, steps: int, warmup: int):
     """Draft-only batches (every request a draft, the workload's shapes) at a
     range of sparsities: per-step time should fall close to proportionally to s."""
@@ -235,17 +249,7 @@ def sparsity_sweep(w, dev, steps: int, warmup: int):
         # first tens of calls on a new batch, still slow, set the average of
         # steps this short
         us = _time_steps(bufs.step, max(steps, 200), max(warmup, 50))
-        bd.profile_reset()
-        bd.profile_enable((1 << len(bd.PROF_NAMES)) - 1)
-        for _ in range(10):
-            bufs.step()
-        torch.cuda.synchronize()
-        bd.profile_enable(0)
-        kern = {}
-        for i, nm in enumerate(bd.PROF_NAMES):
-            n, ms = bd.profile_read(i)
-            if n:
-                kern[nm] = round(ms / n * 1e3, 1)
+        kern = {nm: round(v, 1) for nm, v in launch_times(bufs.step, ("attn",), 10).items()}
         alg = algorithmic_bytes(b)
         rows.append({"s": float(s), "K": b.idx_count[0], "us_per_step": round(us, 1), "kernel_us": kern,
                      "bytes_min": alg["bytes_min"],
@@ -335,17 +339,17 @@ def recall_measure(w, dev, steps: int, warmup: int, n_sink: int, n_recent: int):
     t_plain = _time_steps(plain.step, steps, warmup)
     t_recall = _time_steps(recall, steps, warmup)
     t_both = _time_steps(step_with_recall, steps, warmup)
-    bd.profile_reset()
-    bd.profile_enable((1 << len(bd.PROF_NAMES)) - 1)
-    for _ in range(10):
-        step_with_recall()
+    kern = {nm: round(v, 2) for nm, v in
+            launch_times(recalled.step, ("attn", "post", "select"), 10).items()}
+    # the index launch alone, between two events on the stream
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(10)]
+    for a, z in ev:
+        a.record()
+        recall()
+        z.record()
     torch.cuda.synchronize()
-    bd.profile_enable(0)
-    kern = {}
-    for i, nm in enumerate(bd.PROF_NAMES):
-        n, ms = bd.profile_read(i)
-        if n:
-            kern[nm] = round(ms / n * 1e3, 2)
+    kern["recall"] = round(float(np.mean([a.elapsed_time(z) for a, z in ev])) * 1e3, 2)
     # the index launch must read each stored list and write each output list once
     rec_bytes = int(sum(Hkv * (k_in + k_out) * 4 for k_in, k_out in zip(inc_d, cnt)))
     rec_us = kern.get("recall", float("nan"))
@@ -410,14 +414,14 @@ def quality_measure(w, dev, steps: int, warmup: int, top_t: int):
                      f"recall@{top_t}_p10": round(float(torch.quantile(rec.flatten(), 0.1)), 4)}
     out["score_launch_us_back_to_back"] = round(_time_steps(score, steps, warmup), 1)
     out["quality_launch_us_back_to_back"] = round(_time_steps(lambda: quality(stale), steps, warmup), 1)
-    bd.profile_reset()
-    bd.profile_enable(1 << bd.PROF_QUALITY)
-    for _ in range(10):
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(10)]
+    for a, z in ev:
+        a.record()
         quality(stale)
+        z.record()
     torch.cuda.synchronize()
-    bd.profile_enable(0)
-    n, ms = bd.profile_read(bd.PROF_QUALITY)
-    q_us = ms / max(n, 1) * 1e3
+    q_us = float(np.mean([a.elapsed_time(z) for a, z in ev])) * 1e3  # incl. the release launch
     # the row's logits read once, its softmax written once and read back by the
     # selection, the lists read once; top-T, coverage and recall written
     qbytes = int(sum(Hq * L * 4 * 3 for L in lens) + sum(Hkv * k * 4 for k in K)
@@ -427,6 +431,68 @@ def quality_measure(w, dev, steps: int, warmup: int, top_t: int):
                                "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                                "frac": round(qbytes / (q_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
                                "algorithmic_bytes_per_launch": qbytes}
+    print(json.dumps(out), flush=True)
+
+
+def per_call(w, dev, n: int):
+    """The first n calls on a freshly generated batch, each bracketed by its
+    own events (whole call, and the attention, post-pass and selection
+    launches): where the extra time of the first calls goes."""
+    b = synth.make_batch(w, device=dev)
+    bufs = bd.StepBuffers(b)
+    props = torch.cuda.get_device_properties(dev)
+    opts = [bd.Options(num_cus=props.multi_processor_count, timing=("attn", "post", "select"))
+            for _ in range(n)]
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    host = []
+    for i in range(n):
+        ev[i][0].record()
+        bufs.step(opts[i])
+        ev[i][1].record()
+        host.append(time.perf_counter() - t0)
+    torch.cuda.synchronize()
+    rows = []
+    for i in range(n):
+        rows.append({"call": i + 1, "step_us": round(ev[i][0].elapsed_time(ev[i][1]) * 1e3, 1),
+                     **{k: round(opts[i].elapsed_ms(k) * 1e3, 1) for k in ("attn", "post", "select")},
+                     "host_issue_ms": round(host[i] * 1e3, 3)})
+    print(json.dumps({"per_call": w.name, "calls": rows}), flush=True)
+
+
+def clock_ramp(w, dev, n: int = 150, group: int = 5):
+    """The same calls after the GPU sat idle and after it was kept busy with
+    unrelated HBM copies: per-call time in groups of `group` calls (one event
+    pair per group).  After an idle period the first tens of calls run slower
+    while the GPU's clocks settle; after busy work they do not."""
+    b = synth.make_batch(w, device=dev)
+    bufs = bd.StepBuffers(b)
+    big = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    big2 = torch.empty_like(big)
+    torch.cuda.synchronize()
+
+    def groups():
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(n // group + 1)]
+        ev[0].record()
+        for i in range(n // group):
+            for _ in range(group):
+                bufs.step()
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        return [round(ev[i].elapsed_time(ev[i + 1]) * 1e3 / group, 1) for i in range(n // group)]
+
+    out = {"clock_ramp": w.name, "calls_per_group": group}
+    groups()  # first use of the batch
+    time.sleep(0.2)
+    out["after_200ms_idle"] = groups()
+    for _ in range(150):  # about 40 ms of 1 GiB device copies
+        big2.copy_(big)
+    out["after_40ms_of_copies"] = groups()
+    out["back_to_back"] = groups()
+    time.sleep(0.05)
+    out["after_50ms_idle"] = groups()
     print(json.dumps(out), flush=True)
 
 
@@ -455,6 +521,12 @@ def main():
     ap.add_argument("--quality", type=int, default=0, metavar="T",
                     help="only measure stale and fresh index lists against the drafts' exact "
                          "attention (coverage, recall of the top T) and print its JSON line")
+    ap.add_argument("--per-call", type=int, default=0, metavar="N",
+                    help="only time the first N calls on a fresh batch one by one and print "
+                         "their JSON line")
+    ap.add_argument("--clock-ramp", action="store_true",
+                    help="only time calls after an idle period and after busy work (groups "
+                         "of 5) and print their JSON line")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 5 plain device copies of MIB MiB (reference for the HBM "
                          "byte counters) and exit")
@@ -493,11 +565,20 @@ def main():
     if args.quality:
         quality_measure(w, dev, args.steps, args.warmup, args.quality)
         return
+    if args.per_call:
+        per_call(w, dev, args.per_call)
+        return
+    if args.clock_ramp:
+        clock_ramp(w, dev)
+        return
     print(f"[bench] generating {w.name} on {dev}", file=sys.stderr, flush=True)
+    # make_batch queues its bulk device generation last and returns while it
+    # runs; the buffers are set up and the warm-up queued behind it, so the
+    # GPU does not sit idle before the measured steps (after an idle period
+    # its clocks take about 10 ms of load to settle: --clock-ramp)
     b = synth.make_batch(w, device=dev)
     bufs = bd.StepBuffers(b)
     alg = algorithmic_bytes(b)
-    torch.cuda.synchronize()
 
     # warm-up
     for _ in range(args.warmup):
@@ -522,38 +603,12 @@ def main():
           f"(host wall {wall * 1e6 / args.steps:.1f} us/step)", file=sys.stderr, flush=True)
 
     # the same K steps again, now with the attention launch bracketed by HIP
-    # events recorded on the stream it is launched on
-    bd.profile_reset()
-    bd.profile_enable((1 << bd.PROF_ATTN) | (1 << bd.PROF_ATTN_DRAFT))
-    for _ in range(args.steps):
-        bufs.step()
-    torch.cuda.synchronize()
-    bd.profile_enable(0)
-    n_attn, ms_attn = bd.profile_read(bd.PROF_ATTN)
-    n_attn_d, ms_attn_d = bd.profile_read(bd.PROF_ATTN_DRAFT)
-    overlapped = n_attn_d > 0  # verify and draft attention ran as two launches
-    n_span, ms_span = 0, 0.0
-    if overlapped:  # first start to last end of the two concurrent launches
-        bd.profile_reset()
-        bd.profile_enable(1 << bd.PROF_ATTN_SPAN)
-        for _ in range(args.steps):
-            bufs.step()
-        torch.cuda.synchronize()
-        bd.profile_enable(0)
-        n_span, ms_span = bd.profile_read(bd.PROF_ATTN_SPAN)
+    # events recorded on the stream it is launched on (each call its own pair)
+    attn_us = launch_times(bufs.step, ("attn",), args.steps)["attn"]
 
     # per-kernel breakdown (separate pass, every kernel bracketed)
-    bd.profile_reset()
-    bd.profile_enable((1 << len(bd.PROF_NAMES)) - 1)
-    for _ in range(10):
-        bufs.step()
-    torch.cuda.synchronize()
-    bd.profile_enable(0)
-    breakdown = {}
-    for i, name in enumerate(bd.PROF_NAMES):
-        n, ms = bd.profile_read(i)
-        if n:
-            breakdown[name] = round(ms / n * 1e3, 2)
+    breakdown = {nm: round(v, 2) for nm, v in
+                 launch_times(bufs.step, ("attn", "post", "select"), 10).items()}
 
     # cold steps: a 512 MB write between steps evicts the 256 MB Infinity Cache
     cold = None
@@ -579,14 +634,9 @@ def main():
     steps_per_s = 1e3 / ms_step
     gbps_method = alg["bytes_method"] / (ms_step * 1e-3) / 1e9
     gbps_min = alg["bytes_min"] / (ms_step * 1e-3) / 1e9
-    # the dominant work is all attention of the step: one launch (its own
-    # events), or with overlap two concurrent launches measured from the first
-    # start to the last end
-    attn_us = (ms_span / max(n_span, 1) if overlapped else ms_attn / max(n_attn, 1)) * 1e3
+    # the dominant work is all attention of the step, one launch
     attn_bytes = alg["attn_launch"]
     attn_gbps = attn_bytes / (attn_us * 1e-6) / 1e9
-    verify_us = ms_attn / max(n_attn, 1) * 1e3
-    draft_us = ms_attn_d / max(n_attn_d, 1) * 1e3 if n_attn_d else None
     traffic = recorded_traffic(w.name)
     mf = mfma_flops(b)
     mfma = None
@@ -599,7 +649,8 @@ def main():
                 "achieved_tflops": round(mf["total"] / (attn_us * 1e-6) / 1e12, 2),
                 "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
                 "frac": round(mf["total"] / (attn_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 5),
-                "counters": recorded_mfma(w.name)}
+                "counters": recorded_mfma(w.name),
+                "counters_source": f"profiles/attn_kernel_{w.name}_mfma.md (recorded)"}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -635,18 +686,18 @@ def main():
         "bytes_min_per_step": alg["bytes_min"],
         "kernel_us": breakdown,
         "cold": cold,
-        "roofline": {"bound": "hbm",
-                     "kernel": "attn_kernel + attn_kernel_draft (concurrent; first start to last end)"
-                               if overlapped else "attn_kernel",
+        "roofline": {"bound": "hbm", "kernel": "attn_kernel",
                      "achieved": round(attn_gbps, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(attn_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                     # where traffic comes from: recorded counter runs of these
+                     # kernel sources (profiles/), not this run
+                     "traffic_source": f"profiles/attn_kernel_{w.name}_traffic.md (recorded, "
+                                       f"source {kernel_source_hash()})" if traffic else None,
                      # the bytes the launch really moves (counted), per second
                      "traffic_gbps": round(traffic / (attn_us * 1e-6) / 1e9, 1) if traffic else None,
                      "algorithmic_bytes_per_launch": attn_bytes,
-                     "launch_us": round(attn_us, 2), "launches": n_span if overlapped else n_attn,
-                     "verify_launch_us": round(verify_us, 2),
-                     "draft_launch_us": round(draft_us, 2) if draft_us else None},
+                     "launch_us": round(attn_us, 2), "launches": args.steps},
         "mfma": mfma,
         "cpu_baseline": cpu,
         "env": {"device": torch.cuda.get_device_name(dev),

@@ -13,13 +13,12 @@
  *   - both kinds share one batch over a paged KV cache with page size 1.
  *
  * Conventions shared by every entry point
- *   Ownership   The caller owns every buffer.  Device pointers (d_*) are HIP
- *               device memory; host pointers (h_*) are ordinary host memory read
- *               during the call only.  The library keeps a small ring of pinned
- *               host buffers (allocated on first use, grown on demand) holding
- *               each call's work plan, which the kernels read in place, and a
- *               few device-side work counters per plan buffer (static device
- *               memory, zero at load, back at zero after every launch).
+ *   Ownership   The caller owns every buffer; the library allocates and frees
+ *               nothing, on the device or the host, and keeps no per-call
+ *               state between calls (it caches device properties and kernel
+ *               occupancies only).  Device pointers (d_*) are HIP device
+ *               memory; host pointers (h_*) are ordinary host memory read
+ *               during the call only, except the plan buffer below.
  *   Layouts     (H_q query heads, H_kv KV heads, G = H_q / H_kv, d = head_dim,
  *               element type per spa_layout.dtype: bf16 or fp32)
  *               k_pool, v_pool  [num_slots][H_kv][d]; one slot holds one token.
@@ -38,37 +37,55 @@
  *                               (not slots) starting at element h_idx_off[r],
  *                               ascending per KV head.
  *   Semantics   Query head h reads KV head h / G.  Softmax scale sm_scale (0 means
- *               1/sqrt(d)).  A list entry outside [0, L_r) is ignored; a row
- *               whose list holds no valid entry gets O = 0 and LSE = -inf.
- *               Top-K orders by (averaged score descending, position ascending).
+ *               1/sqrt(d)).  A list entry outside [0, L_r) is ignored (whatever
+ *               the pool holds anywhere it is not read); a row whose list holds
+ *               no valid entry gets O = 0 and LSE = -inf.  Top-K orders by
+ *               (averaged score descending, position ascending).
  *   Errors      Every entry point returns an spa_status and spa_last_error()
  *               describes a non-OK one.  Arguments are checked on the host
  *               before anything is enqueued, so SPA_ERR_INVALID_ARG,
- *               SPA_ERR_UNSUPPORTED and SPA_ERR_WORKSPACE_TOO_SMALL leave the
- *               stream untouched; SPA_ERR_HIP (a failed launch or runtime call)
- *               may come after earlier launches of the same call were enqueued.
+ *               SPA_ERR_UNSUPPORTED and the *_TOO_SMALL codes leave the stream
+ *               and the plan buffer untouched; SPA_ERR_HIP (a failed launch or
+ *               runtime call) may come after earlier launches of the same call
+ *               were enqueued.
  *   Streams     Work is enqueued on `stream` (a hipStream_t; NULL = default
  *               stream) and the call returns without waiting.  Faults inside a
  *               kernel surface at the caller's next synchronisation.
- *   Workspace   d_ws/ws_bytes is caller-owned device scratch of at least
- *               spa_workspace_bytes(...) bytes for the same batch; it holds
- *               split-K partials, averaged scores, a device copy of the
- *               post-pass and selection work records and the selected rows'
- *               score histograms.  Its contents on entry do
- *               not matter and need no initialisation.  Calls that share one
- *               workspace must be ordered on one stream.  The size depends on
- *               the split settings (spa_set_split) and, with the automatic
- *               verify chunk, on the device's compute-unit count: ask on the
- *               device and with the settings the call will use.
- *   Threads     Entry points may be called from several host threads.
- *   Graphs      Calls are not capturable into HIP graphs: each call writes its
- *               work plan into pinned host memory at call time (a replay would
- *               read whatever a later call left there) and may first wait until
- *               the GPU has finished reading that buffer for an earlier call
- *               (an event, or a sequence number the earlier call's kernels
- *               store into mapped host memory; after half a second without
- *               it, or when the earlier call failed after taking the buffer,
- *               the wait drains that call's device instead).
+ *   Workspace   d_ws/ws_bytes: caller-owned device scratch of at least
+ *               spa_workspace_bytes(...) bytes for the same batch and options,
+ *               256-byte aligned.  Its first 256 bytes hold the attention
+ *               launches' work counters: they must be zero before a workspace
+ *               is used for the first time (hipMemset, torch.zeros), and every
+ *               call leaves them zero again.  The rest (split-K partials,
+ *               averaged scores, a device copy of the post-pass and selection
+ *               work records, the selected rows' score histograms) needs no
+ *               initialisation.  Calls that share one workspace must be
+ *               ordered on one stream.
+ *   Plan buffer h_plan/plan_bytes: caller-owned pinned host memory
+ *               (hipHostMalloc, or a pinned torch tensor) of at least
+ *               spa_plan_bytes(...) bytes, 64-byte aligned.  A call writes its
+ *               work plan there and the kernels read it in place over the host
+ *               link (no copy is enqueued).  The first 256 bytes are a header
+ *               that needs no initialisation: when a buffer is passed again,
+ *               the call first waits until the GPU has finished reading what
+ *               the earlier call wrote (the kernels store the earlier call's
+ *               sequence number into the header when they no longer read the
+ *               plan; after half a second without it, or when the earlier call
+ *               failed after writing the buffer, the call drains that call's
+ *               device instead).  So several buffers used in turn let the host
+ *               run ahead of the GPU; one buffer serialises the host on the
+ *               GPU.  A buffer must stay allocated while the GPU may read it
+ *               and may not be passed to two calls running concurrently on
+ *               different host threads.
+ *   Options     opts may be NULL (all defaults); see spa_options.  The sizes
+ *               spa_workspace_bytes and spa_plan_bytes return depend on the
+ *               options, so pass the same options to the size query and the
+ *               call.
+ *   Threads     Entry points may be called from several host threads with
+ *               different plan buffers and workspaces.
+ *   Graphs      Calls are not capturable into HIP graphs: a call writes its
+ *               work plan into host memory at call time, so a replay would
+ *               read whatever a later call left there.
  *   B == 0      is a successful no-op.
  */
 #ifndef SPA_H_
@@ -81,14 +98,15 @@
 extern "C" {
 #endif
 
-#define SPA_ABI_VERSION 1
+#define SPA_ABI_VERSION 2
 
 typedef enum {
   SPA_OK = 0,
   SPA_ERR_INVALID_ARG = 1,         /* null pointer, bad size, bad offsets ...      */
   SPA_ERR_UNSUPPORTED = 2,         /* head_dim, dtype or row count not built       */
   SPA_ERR_WORKSPACE_TOO_SMALL = 3, /* ws_bytes < spa_workspace_bytes(...)          */
-  SPA_ERR_HIP = 4                  /* a HIP runtime call or launch failed          */
+  SPA_ERR_HIP = 4,                 /* a HIP runtime call or launch failed          */
+  SPA_ERR_PLAN_TOO_SMALL = 5       /* plan_bytes < spa_plan_bytes(...)             */
 } spa_status;
 
 typedef enum { SPA_BF16 = 0, SPA_F32 = 1 } spa_dtype;
@@ -103,18 +121,64 @@ typedef struct {
   int32_t page_table_stride; /* int32 elements per page_table row (>= max L_r)    */
 } spa_layout;
 
+/* Per-call options.  Zero-initialised options (or opts == NULL) are the
+ * defaults.  Results do not depend on the work split beyond floating-point
+ * summation order. */
+typedef struct {
+  /* Positions per verify work item (split-K chunk), 0 or 1..2048.  0: 2048
+   * when the batch's verify positions times H_kv reach 5120 per compute unit
+   * (num_cus below), else 512 (doubled while a request would need more than
+   * 256 chunks). */
+  int32_t verify_chunk;
+  /* List entries per draft work item, 0 or 1..2048; 0: 1024. */
+  int32_t draft_chunk;
+  /* Compute units the automatic verify chunk plans for; 0: 256 (MI355X).
+   * Only the automatic rule reads it, so sizes stay a pure function of the
+   * arguments. */
+  int32_t num_cus;
+  /* Nonzero: spa_unified_step on a batch holding both verify and draft
+   * requests runs its draft attention as a second launch on side_stream,
+   * forked from `stream` after the work already queued there (fork_event) and
+   * joined back before the call's last operation (join_event), so the call as
+   * a whole stays ordered on `stream` while verify attention, score averaging
+   * and top-K overlap the draft attention.  The streams and events (created
+   * by the caller with hipEventDisableTiming) may not be shared with calls
+   * in flight on other host threads.  Other entry points ignore it. */
+  int32_t overlap;
+  void* side_stream;  /* hipStream_t */
+  void* fork_event;   /* hipEvent_t  */
+  void* join_event;   /* hipEvent_t  */
+  /* Optional timing events (hipEvent_t, created by the caller; NULL entries
+   * are skipped), recorded on the launch stream right before and after:
+   * [0],[1] the attention launch (with overlap: the verify attention launch);
+   * [2],[3] the post-pass launch (split-K merges and score averaging);
+   * [4],[5] the top-K selection launch; [6],[7] the draft attention launch of
+   * an overlapped unified step (on side_stream).  A launch the call does not
+   * make records nothing. */
+  void* timing[8];
+} spa_options;
+
 /* Library ABI version (SPA_ABI_VERSION of the build). */
 int32_t spa_abi_version(void);
 
 /* Message describing the last non-OK status returned on this host thread. */
 const char* spa_last_error(void);
 
-/* Workspace bytes needed by any entry point below for this batch.  h_is_verify
- * may be NULL (all draft) and h_idx_count may be NULL for verify-only batches.
- * Returns 0 when the arguments are invalid (spa_last_error() says why). */
+/* Workspace bytes needed by spa_verify_attn, spa_pillar_topk, spa_draft_attn
+ * and spa_unified_step for this batch (the largest of their needs), a pure
+ * function of the arguments.  h_is_verify may be NULL (all draft) and
+ * h_idx_count may be NULL for verify-only batches.  Returns 0 when the
+ * arguments are invalid (spa_last_error() says why). */
 size_t spa_workspace_bytes(const spa_layout* layout, int32_t B, int32_t spec_k,
                            const uint8_t* h_is_verify, const int32_t* h_seq_lens,
-                           const int32_t* h_idx_count);
+                           const int32_t* h_idx_count, const spa_options* opts);
+
+/* Plan-buffer bytes needed by the same four entry points for this batch (the
+ * largest of their needs), a pure function of the arguments; 0 when they are
+ * invalid. */
+size_t spa_plan_bytes(const spa_layout* layout, int32_t B, int32_t spec_k,
+                      const uint8_t* h_is_verify, const int32_t* h_seq_lens,
+                      const int32_t* h_idx_count, const spa_options* opts);
 
 /* Full attention of B verify requests (k+1 rows each, rows r*(k+1)...), with
  * the logits and LSE kept.  Review of SparseSpec, PillarAttn, third bullet:
@@ -126,19 +190,24 @@ int32_t spa_verify_attn(const spa_layout* layout, int32_t B, int32_t spec_k,
                         const int32_t* h_seq_lens, const int32_t* d_page_table,
                         const void* d_q, const void* d_k_pool, const void* d_v_pool, void* d_o,
                         float* d_lse, float* d_logits, const int64_t* h_logits_off, void* d_ws,
-                        size_t ws_bytes, void* stream);
+                        size_t ws_bytes, void* h_plan, size_t plan_bytes,
+                        const spa_options* opts, void* stream);
 
 /* PillarAttn selection for B verify requests.  Review of SparseSpec,
  * PillarAttn, third and fourth bullets: exact scores exp(logit - LSE) are
  * averaged over rows [avg_row_begin, avg_row_begin + avg_row_count) (the k
  * draft rows are 1..k) and the G heads of each KV head, then the top
  * h_topk[r] = K_r positions per KV head are written ascending to
- * d_idx + h_idx_off[r] as [H_kv][K_r].  d_lse [B(k+1)][H_q]; logits as above. */
+ * d_idx + h_idx_off[r] as [H_kv][K_r].  d_lse [B(k+1)][H_q]; logits as above.
+ * Workspace and plan sizes: spa_workspace_bytes / spa_plan_bytes of a layout
+ * with these head counts, with every request a verify request and
+ * h_idx_count = h_topk. */
 int32_t spa_pillar_topk(int32_t B, int32_t spec_k, int32_t num_qo_heads, int32_t num_kv_heads,
                         int32_t avg_row_begin, int32_t avg_row_count, const int32_t* h_seq_lens,
                         const int32_t* h_topk, const float* d_logits,
                         const int64_t* h_logits_off, const float* d_lse, int32_t* d_idx,
-                        const int64_t* h_idx_off, void* d_ws, size_t ws_bytes, void* stream);
+                        const int64_t* h_idx_off, void* d_ws, size_t ws_bytes, void* h_plan,
+                        size_t plan_bytes, const spa_options* opts, void* stream);
 
 /* Sparse attention of B draft requests (one row each) over their stored lists.
  * Review of SparseSpec, PillarAttn, first two bullets; blog section 4.1: a
@@ -148,7 +217,8 @@ int32_t spa_draft_attn(const spa_layout* layout, int32_t B, const int32_t* h_seq
                        const int32_t* d_page_table, const int32_t* h_idx_count,
                        const int64_t* h_idx_off, const int32_t* d_idx, const void* d_q,
                        const void* d_k_pool, const void* d_v_pool, void* d_o, float* d_lse,
-                       void* d_ws, size_t ws_bytes, void* stream);
+                       void* d_ws, size_t ws_bytes, void* h_plan, size_t plan_bytes,
+                       const spa_options* opts, void* stream);
 
 /* One mixed batch: verify requests (h_is_verify[r] != 0) run spa_verify_attn
  * then spa_pillar_topk semantics and overwrite their own idx segment (K_r =
@@ -166,7 +236,8 @@ int32_t spa_unified_step(const spa_layout* layout, int32_t B, int32_t spec_k,
                          const int32_t* h_idx_count, const int64_t* h_idx_off, int32_t* d_idx,
                          void* d_o, float* d_lse, float* d_logits, const int64_t* h_logits_off,
                          int32_t avg_row_begin, int32_t avg_row_count, void* d_ws,
-                         size_t ws_bytes, void* stream);
+                         size_t ws_bytes, void* h_plan, size_t plan_bytes,
+                         const spa_options* opts, void* stream);
 
 /* Recallable sparse index of B draft requests.  Page "全局的稀疏一瞥"
  * (arxiv.org 2607.27735 as rendered on bittide.aicompass.dev), section 方法,
@@ -183,14 +254,19 @@ int32_t spa_unified_step(const spa_layout* layout, int32_t B, int32_t spec_k,
  * h_out_count[r] must be >= max(1, min(L_r, S + R + h_in_count[r])), S =
  * min(n_sink, L_r), R = L_r - max(S, L_r - min(n_recent, L_r)).  Output lists
  * may not overlap one another or any stored list (checked on the host from the
- * addresses); d_idx_in may be NULL when every h_in_count[r] is 0.  One launch;
- * the output then feeds spa_draft_attn or the draft requests of
- * spa_unified_step with h_idx_count[r] = h_out_count[r]. */
+ * addresses); d_idx_in may be NULL when every h_in_count[r] is 0.  Plan
+ * buffer: at least spa_recall_plan_bytes(B) bytes (same rules as above).  One
+ * launch, then a one-thread launch that releases the plan buffer; the output
+ * then feeds spa_draft_attn or the draft requests of spa_unified_step with
+ * h_idx_count[r] = h_out_count[r]. */
 int32_t spa_recall_index(int32_t B, int32_t num_kv_heads, const int32_t* h_seq_lens,
                          int32_t n_sink, int32_t n_recent, const int32_t* h_in_count,
                          const int64_t* h_in_off, const int32_t* d_idx_in,
                          const int32_t* h_out_count, const int64_t* h_out_off, int32_t* d_idx_out,
-                         void* stream);
+                         void* h_plan, size_t plan_bytes, void* stream);
+
+/* Plan-buffer bytes of spa_recall_index for B requests (0 for B < 0). */
+size_t spa_recall_plan_bytes(int32_t B);
 
 /* Quality of index lists against one query row's exact attention.  Review
  * of SparseSpec, 核心方法 / PillarAttn, the comparison with Quest: PillarAttn
@@ -208,53 +284,24 @@ int32_t spa_recall_index(int32_t B, int32_t num_kv_heads, const int32_t* h_seq_l
  *   d_recall   [B][H_q]: |top_t positions on the list| / top_t.
  * 1 <= top_t <= L_r <= 1048576.  d_ws: 16-byte aligned, at least
  * spa_list_quality_workspace_bytes(B, H_q, h_seq_lens) bytes (the rows' p_h;
- * contents on entry do not matter).  One launch. */
+ * contents on entry do not matter).  Plan buffer: at least
+ * spa_list_quality_plan_bytes(B) bytes.  One launch, then a one-thread launch
+ * that releases the plan buffer. */
 int32_t spa_list_quality(int32_t B, int32_t spec_k, int32_t num_qo_heads, int32_t num_kv_heads,
                          int32_t row, int32_t top_t, const int32_t* h_seq_lens,
                          const float* d_logits, const int64_t* h_logits_off, const float* d_lse,
                          const int32_t* h_list_count, const int64_t* h_list_off,
                          const int32_t* d_list, int32_t* d_top, float* d_coverage,
-                         float* d_recall, void* d_ws, size_t ws_bytes, void* stream);
+                         float* d_recall, void* d_ws, size_t ws_bytes, void* h_plan,
+                         size_t plan_bytes, void* stream);
 
 /* Workspace bytes of spa_list_quality: sum over r of H_q * (L_r rounded up to
  * a multiple of 4) * 4.  Returns 0 for B <= 0 or a NULL pointer. */
 size_t spa_list_quality_workspace_bytes(int32_t B, int32_t num_qo_heads,
                                         const int32_t* h_seq_lens);
 
-/* Process-wide switch for spa_unified_step on a batch holding both verify
- * and draft requests (default 0): 1 runs its draft attention as a second
- * launch on a library-owned stream (default priority, one per device) that is
- * forked from `stream` after the work already queued there and joined back
- * before the call's last operation, so the call as a whole stays ordered on
- * `stream` while the verify attention, score averaging and top-K overlap the
- * draft attention; 0 runs all attention items in one launch.  Results do not
- * depend on it.  Returns SPA_OK. */
-int32_t spa_set_overlap(int32_t enable);
-
-/* Process-wide split-K chunk sizes (tokens per verify work item, list entries
- * per draft work item); 0 restores the automatic choice.  Results do not
- * depend on them beyond floating-point summation order. */
-int32_t spa_set_split(int32_t verify_chunk_tokens, int32_t draft_chunk_entries);
-
-/* Per-launch timing.  With a nonzero kernel mask, every later launch of a
- * selected kernel is bracketed by a pair of HIP events recorded on the launch
- * stream (bit 0: the attention launch, or with overlap the verify attention
- * launch; bit 1: the post-pass launch holding the split-K merges and score
- * averaging; bit 2: the top-K selection launch; bit 3: the draft attention
- * launch of an overlapped unified step; bit 4: all attention of a call, from
- * the start of its first attention launch to the end of its last, over both
- * streams when overlapped; bit 5: the spa_recall_index launch; bit 6: the
- * spa_list_quality launch); 0 turns it off.
- * Returns SPA_OK. */
-int32_t spa_profile_enable(int32_t kernel_mask);
-
-/* Waits for the recorded launches of kernel `which` (bit index as above),
- * adds their durations to the running totals and returns them: number of
- * launches and summed milliseconds since the last spa_profile_reset(). */
-int32_t spa_profile_read(int32_t which, int64_t* count, double* total_ms);
-
-/* Drops the running totals and any launches not yet read. */
-int32_t spa_profile_reset(void);
+/* Plan-buffer bytes of spa_list_quality for B requests (0 for B < 0). */
+size_t spa_list_quality_plan_bytes(int32_t B);
 
 #ifdef __cplusplus
 }

@@ -1,15 +1,17 @@
 """ctypes binding of libspa (include/spa.h): argument marshalling only.
 
 Device buffers are PyTorch tensors on the current HIP device; host metadata are
-Python sequences or numpy arrays.  Every call enqueues on the current PyTorch
-stream of the tensors' device and returns without synchronising.  The library
-must be built (``python -m sparse_self_speculative_pillarattn_amd.build``);
-there is no fallback path.
+Python sequences or numpy arrays; plan buffers are pinned host tensors
+(``plan_buffer``).  Every call enqueues on the current PyTorch stream of the
+tensors' device and returns without synchronising.  The library must be built
+(``python -m sparse_self_speculative_pillarattn_amd.build``); there is no
+fallback path.
 """
 from __future__ import annotations
 
 import ctypes as C
 import os
+import threading
 from typing import Optional, Sequence
 
 import numpy as np
@@ -23,18 +25,18 @@ SPA_ERR_INVALID_ARG = 1
 SPA_ERR_UNSUPPORTED = 2
 SPA_ERR_WORKSPACE_TOO_SMALL = 3
 SPA_ERR_HIP = 4
+SPA_ERR_PLAN_TOO_SMALL = 5
 SPA_BF16 = 0
 SPA_F32 = 1
+ABI_VERSION = 2
 
-EXPORTED = ("spa_abi_version", "spa_last_error", "spa_workspace_bytes", "spa_verify_attn",
-            "spa_pillar_topk", "spa_draft_attn", "spa_unified_step", "spa_set_split", "spa_set_overlap",
-            "spa_profile_enable", "spa_profile_read", "spa_profile_reset", "spa_recall_index",
-            "spa_list_quality", "spa_list_quality_workspace_bytes")
+EXPORTED = ("spa_abi_version", "spa_last_error", "spa_workspace_bytes", "spa_plan_bytes",
+            "spa_verify_attn", "spa_pillar_topk", "spa_draft_attn", "spa_unified_step",
+            "spa_recall_index", "spa_recall_plan_bytes", "spa_list_quality",
+            "spa_list_quality_workspace_bytes", "spa_list_quality_plan_bytes")
 
-# kernel indices of the per-launch timer
-(PROF_ATTN, PROF_POST, PROF_SELECT, PROF_ATTN_DRAFT, PROF_ATTN_SPAN, PROF_RECALL,
- PROF_QUALITY) = range(7)
-PROF_NAMES = ("attn", "post", "select", "attn_draft", "attn_span", "recall", "quality")
+# indices into SpaOptions.timing: begin/end event pairs of each launch
+TIMING = {"attn": (0, 1), "post": (2, 3), "select": (4, 5), "attn_draft": (6, 7)}
 
 
 class SpaError(RuntimeError):
@@ -49,6 +51,12 @@ class SpaLayout(C.Structure):
                 ("num_slots", C.c_int64), ("page_table_stride", C.c_int32)]
 
 
+class SpaOptions(C.Structure):
+    _fields_ = [("verify_chunk", C.c_int32), ("draft_chunk", C.c_int32), ("num_cus", C.c_int32),
+                ("overlap", C.c_int32), ("side_stream", C.c_void_p), ("fork_event", C.c_void_p),
+                ("join_event", C.c_void_p), ("timing", C.c_void_p * 8)]
+
+
 _lib = None
 
 
@@ -61,38 +69,38 @@ def load(path: str = LIB_PATH):
         raise ImportError(f"{path} is missing: build it with "
                           "`python -m sparse_self_speculative_pillarattn_amd.build`")
     lib = C.CDLL(path)
-    vp, i32, i64, sz = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t
+    vp, i32, sz = C.c_void_p, C.c_int32, C.c_size_t
     L = C.POINTER(SpaLayout)
+    O = C.POINTER(SpaOptions)
     lib.spa_abi_version.restype = i32
     lib.spa_last_error.restype = C.c_char_p
-    lib.spa_set_split.argtypes = [i32, i32]
-    lib.spa_set_split.restype = i32
-    lib.spa_set_overlap.argtypes = [i32]
-    lib.spa_set_overlap.restype = i32
-    lib.spa_workspace_bytes.argtypes = [L, i32, i32, vp, vp, vp]
-    lib.spa_workspace_bytes.restype = sz
-    lib.spa_verify_attn.argtypes = [L, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    for name in ("spa_workspace_bytes", "spa_plan_bytes"):
+        f = getattr(lib, name)
+        f.argtypes = [L, i32, i32, vp, vp, vp, O]
+        f.restype = sz
+    lib.spa_verify_attn.argtypes = [L, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp,
+                                    sz, O, vp]
     lib.spa_verify_attn.restype = i32
     lib.spa_pillar_topk.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp,
-                                    sz, vp]
+                                    sz, vp, sz, O, vp]
     lib.spa_pillar_topk.restype = i32
-    lib.spa_draft_attn.argtypes = [L, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.spa_draft_attn.argtypes = [L, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, sz,
+                                   O, vp]
     lib.spa_draft_attn.restype = i32
     lib.spa_unified_step.argtypes = [L, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
-                                     vp, vp, i32, i32, vp, sz, vp]
+                                     vp, vp, i32, i32, vp, sz, vp, sz, O, vp]
     lib.spa_unified_step.restype = i32
-    lib.spa_recall_index.argtypes = [i32, i32, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp]
+    lib.spa_recall_index.argtypes = [i32, i32, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.spa_recall_index.restype = i32
+    lib.spa_recall_plan_bytes.argtypes = [i32]
+    lib.spa_recall_plan_bytes.restype = sz
     lib.spa_list_quality.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp,
-                                     vp, vp, vp, sz, vp]
+                                     vp, vp, vp, sz, vp, sz, vp]
     lib.spa_list_quality.restype = i32
     lib.spa_list_quality_workspace_bytes.argtypes = [i32, i32, vp]
     lib.spa_list_quality_workspace_bytes.restype = sz
-    lib.spa_profile_enable.argtypes = [i32]
-    lib.spa_profile_enable.restype = i32
-    lib.spa_profile_read.argtypes = [i32, C.POINTER(C.c_int64), C.POINTER(C.c_double)]
-    lib.spa_profile_read.restype = i32
-    lib.spa_profile_reset.restype = i32
+    lib.spa_list_quality_plan_bytes.argtypes = [i32]
+    lib.spa_list_quality_plan_bytes.restype = sz
     _lib = lib
     return lib
 
@@ -129,8 +137,23 @@ def _dptr(t: Optional[torch.Tensor]):
     return C.c_void_p(t.data_ptr())
 
 
+def _hptr(t: torch.Tensor):
+    """Address of a pinned host plan buffer."""
+    if t.is_cuda or not t.is_pinned():
+        raise ValueError("plan buffers must be pinned host tensors (plan_buffer)")
+    return C.c_void_p(t.data_ptr())
+
+
+def _nbytes(t: torch.Tensor) -> int:
+    return t.numel() * t.element_size()
+
+
 def _stream(t: torch.Tensor):
     return C.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _opts(o: Optional["Options"]):
+    return None if o is None else C.byref(o.c)
 
 
 def layout(num_qo_heads: int, num_kv_heads: int, head_dim: int, dtype: torch.dtype,
@@ -142,79 +165,158 @@ def layout(num_qo_heads: int, num_kv_heads: int, head_dim: int, dtype: torch.dty
                      int(page_table_stride))
 
 
+class Options:
+    """spa_options for one or more calls.  Streams and events are PyTorch
+    objects; they are kept alive here for as long as the options are."""
+
+    def __init__(self, verify_chunk: int = 0, draft_chunk: int = 0, num_cus: int = 0,
+                 overlap: bool = False, side_stream: Optional[torch.cuda.Stream] = None,
+                 timing: Optional[dict] = None):
+        self.c = SpaOptions()
+        self.c.verify_chunk = int(verify_chunk)
+        self.c.draft_chunk = int(draft_chunk)
+        self.c.num_cus = int(num_cus)
+        self.c.overlap = 1 if overlap else 0
+        self.keep = []
+        if overlap:
+            side = side_stream if side_stream is not None else torch.cuda.Stream()
+            fork, join = _event(False), _event(False)
+            self.keep += [side, fork, join]
+            self.c.side_stream = side.cuda_stream
+            self.c.fork_event = fork._as_parameter_.value
+            self.c.join_event = join._as_parameter_.value
+        self.timing = {}
+        for name in (timing or {}):
+            a, b = TIMING[name]
+            ea, eb = _event(True), _event(True)
+            self.timing[name] = (ea, eb)
+            self.c.timing[a] = ea._as_parameter_.value
+            self.c.timing[b] = eb._as_parameter_.value
+
+    def elapsed_ms(self, name: str) -> float:
+        """Milliseconds between the last recorded begin and end of a timed launch."""
+        ea, eb = self.timing[name]
+        eb.synchronize()
+        return ea.elapsed_time(eb)
+
+
+def _event(timing: bool) -> torch.cuda.Event:
+    """A created (recorded once) PyTorch event, so that its handle exists."""
+    ev = torch.cuda.Event(enable_timing=timing)
+    ev.record()
+    return ev
+
+
+def default_options(device=None) -> Options:
+    """Options with the device's compute-unit count for the automatic verify chunk."""
+    props = torch.cuda.get_device_properties(device if device is not None else
+                                             torch.cuda.current_device())
+    return Options(num_cus=props.multi_processor_count)
+
+
 def abi_version() -> int:
     return load().spa_abi_version()
 
 
-def set_overlap(enable: bool):
-    """Run the draft attention of a mixed unified step on a side stream (default off)."""
-    _check(load().spa_set_overlap(1 if enable else 0))
-
-
-def set_split(verify_chunk_tokens: int = 0, draft_chunk_entries: int = 0):
-    _check(load().spa_set_split(int(verify_chunk_tokens), int(draft_chunk_entries)))
-
-
-def profile_enable(mask: int):
-    _check(load().spa_profile_enable(int(mask)))
-
-
-def profile_reset():
-    _check(load().spa_profile_reset())
-
-
-def profile_read(which: int):
-    """(launch count, summed milliseconds) of kernel ``which`` since the last reset."""
-    n = C.c_int64(0)
-    ms = C.c_double(0.0)
-    _check(load().spa_profile_read(int(which), C.byref(n), C.byref(ms)))
-    return int(n.value), float(ms.value)
-
-
-def workspace_bytes(lay: SpaLayout, B: int, spec_k: int, is_verify: Optional[Sequence] ,
-                    seq_lens: Sequence, idx_count: Optional[Sequence]) -> int:
+def workspace_bytes(lay: SpaLayout, B: int, spec_k: int, is_verify: Optional[Sequence],
+                    seq_lens: Sequence, idx_count: Optional[Sequence],
+                    opts: Optional[Options] = None) -> int:
     h = _Host()
     n = load().spa_workspace_bytes(C.byref(lay), int(B), int(spec_k), h.arr(is_verify, np.uint8),
-                                   h.arr(seq_lens, np.int32), h.arr(idx_count, np.int32))
+                                   h.arr(seq_lens, np.int32), h.arr(idx_count, np.int32),
+                                   _opts(opts))
     if n == 0 and B > 0:
-        msg = load().spa_last_error().decode()
-        if msg:
-            raise SpaError(SPA_ERR_INVALID_ARG, msg)
+        raise SpaError(SPA_ERR_INVALID_ARG, load().spa_last_error().decode())
     return int(n)
 
 
+def plan_bytes(lay: SpaLayout, B: int, spec_k: int, is_verify: Optional[Sequence],
+               seq_lens: Sequence, idx_count: Optional[Sequence],
+               opts: Optional[Options] = None) -> int:
+    h = _Host()
+    n = load().spa_plan_bytes(C.byref(lay), int(B), int(spec_k), h.arr(is_verify, np.uint8),
+                              h.arr(seq_lens, np.int32), h.arr(idx_count, np.int32), _opts(opts))
+    if n == 0 and B > 0:
+        raise SpaError(SPA_ERR_INVALID_ARG, load().spa_last_error().decode())
+    return int(n)
+
+
+def workspace(nbytes: int, device) -> torch.Tensor:
+    """A workspace of at least ``nbytes``, zero-filled (its first 256 bytes are
+    work counters that must start at zero; calls leave them zero)."""
+    return torch.zeros((max(int(nbytes), 256),), dtype=torch.uint8, device=device)
+
+
+def plan_buffer(nbytes: int) -> torch.Tensor:
+    """A pinned host plan buffer of at least ``nbytes``, 64-byte aligned."""
+    raw = torch.empty((max(int(nbytes), 256) + 64,), dtype=torch.uint8, pin_memory=True)
+    skip = (-raw.data_ptr()) % 64
+    return raw[skip:skip + max(int(nbytes), 256)]
+
+
+_tls = threading.local()
+
+
+def _plan_for(nbytes: int) -> torch.Tensor:
+    """A plan buffer of at least ``nbytes`` from this thread's own ring, for
+    calls made without one.  A ring that is too small is replaced after the
+    device has drained (the GPU may still read the old buffers until then)."""
+    ring = getattr(_tls, "ring", None)
+    if ring is None or ring.nbytes < nbytes:
+        if ring is not None:
+            torch.cuda.synchronize()
+        ring = PlanRing(max(int(nbytes), 1 << 16))
+        _tls.ring = ring
+    return ring.next()
+
+
 def verify_attn(lay, B, spec_k, seq_lens, page_table, q, k_pool, v_pool, o, lse, logits,
-                logits_off, ws: torch.Tensor):
+                logits_off, ws: torch.Tensor, plan: Optional[torch.Tensor] = None,
+                opts: Optional[Options] = None):
+    """plan: a pinned plan buffer (plan_buffer), or None for this thread's ring."""
+    if plan is None:
+        plan = _plan_for(plan_bytes(lay, B, spec_k, [1] * int(B), seq_lens, [1] * int(B), opts))
     h = _Host()
     _check(load().spa_verify_attn(
         C.byref(lay), int(B), int(spec_k), h.arr(seq_lens, np.int32), _dptr(page_table), _dptr(q),
         _dptr(k_pool), _dptr(v_pool), _dptr(o), _dptr(lse), _dptr(logits),
-        h.arr(logits_off, np.int64), _dptr(ws), ws.numel() * ws.element_size(), _stream(q)))
+        h.arr(logits_off, np.int64), _dptr(ws), _nbytes(ws), _hptr(plan), _nbytes(plan),
+        _opts(opts), _stream(q)))
 
 
 def pillar_topk(B, spec_k, num_qo_heads, num_kv_heads, avg_row_begin, avg_row_count, seq_lens,
-                topk, logits, logits_off, lse, idx, idx_off, ws: torch.Tensor):
+                topk, logits, logits_off, lse, idx, idx_off, ws: torch.Tensor,
+                plan: Optional[torch.Tensor] = None, opts: Optional[Options] = None):
+    if plan is None:
+        lay = layout(num_qo_heads, num_kv_heads, 128, torch.bfloat16, 1, max(seq_lens))
+        plan = _plan_for(plan_bytes(lay, B, spec_k, [1] * int(B), seq_lens, topk, opts))
     h = _Host()
     _check(load().spa_pillar_topk(
         int(B), int(spec_k), int(num_qo_heads), int(num_kv_heads), int(avg_row_begin),
         int(avg_row_count), h.arr(seq_lens, np.int32), h.arr(topk, np.int32), _dptr(logits),
         h.arr(logits_off, np.int64), _dptr(lse), _dptr(idx), h.arr(idx_off, np.int64), _dptr(ws),
-        ws.numel() * ws.element_size(), _stream(logits)))
+        _nbytes(ws), _hptr(plan), _nbytes(plan), _opts(opts), _stream(logits)))
 
 
 def draft_attn(lay, B, seq_lens, page_table, idx_count, idx_off, idx, q, k_pool, v_pool, o, lse,
-               ws: torch.Tensor):
+               ws: torch.Tensor, plan: Optional[torch.Tensor] = None,
+               opts: Optional[Options] = None):
+    if plan is None:
+        plan = _plan_for(plan_bytes(lay, B, 1, None, seq_lens, idx_count, opts))
     h = _Host()
     _check(load().spa_draft_attn(
         C.byref(lay), int(B), h.arr(seq_lens, np.int32), _dptr(page_table),
         h.arr(idx_count, np.int32), h.arr(idx_off, np.int64), _dptr(idx), _dptr(q),
-        _dptr(k_pool), _dptr(v_pool), _dptr(o), _dptr(lse), _dptr(ws),
-        ws.numel() * ws.element_size(), _stream(q)))
+        _dptr(k_pool), _dptr(v_pool), _dptr(o), _dptr(lse), _dptr(ws), _nbytes(ws), _hptr(plan),
+        _nbytes(plan), _opts(opts), _stream(q)))
 
 
 def unified_step(lay, B, spec_k, is_verify, seq_lens, q_indptr, page_table, q, k_pool, v_pool,
                  idx_count, idx_off, idx, o, lse, logits, logits_off, ws: torch.Tensor,
-                 avg_row_begin: int = 1, avg_row_count: Optional[int] = None):
+                 plan: Optional[torch.Tensor] = None, avg_row_begin: int = 1,
+                 avg_row_count: Optional[int] = None, opts: Optional[Options] = None):
+    if plan is None:
+        plan = _plan_for(plan_bytes(lay, B, spec_k, is_verify, seq_lens, idx_count, opts))
     h = _Host()
     avg_row_count = spec_k if avg_row_count is None else avg_row_count
     _check(load().spa_unified_step(
@@ -222,7 +324,7 @@ def unified_step(lay, B, spec_k, is_verify, seq_lens, q_indptr, page_table, q, k
         h.arr(q_indptr, np.int32), _dptr(page_table), _dptr(q), _dptr(k_pool), _dptr(v_pool),
         h.arr(idx_count, np.int32), h.arr(idx_off, np.int64), _dptr(idx), _dptr(o), _dptr(lse),
         _dptr(logits), h.arr(logits_off, np.int64), int(avg_row_begin), int(avg_row_count),
-        _dptr(ws), ws.numel() * ws.element_size(), _stream(q)))
+        _dptr(ws), _nbytes(ws), _hptr(plan), _nbytes(plan), _opts(opts), _stream(q)))
 
 
 def recall_length(L: int, stored: int, n_sink: int, n_recent: int) -> int:
@@ -232,13 +334,21 @@ def recall_length(L: int, stored: int, n_sink: int, n_recent: int) -> int:
     return max(1, min(L, s + rec + stored))
 
 
+def recall_plan_bytes(B: int) -> int:
+    return int(load().spa_recall_plan_bytes(int(B)))
+
+
 def recall_index(B, num_kv_heads, seq_lens, n_sink, n_recent, in_count, in_off,
-                 idx_in: Optional[torch.Tensor], out_count, out_off, idx_out: torch.Tensor):
+                 idx_in: Optional[torch.Tensor], out_count, out_off, idx_out: torch.Tensor,
+                 plan: Optional[torch.Tensor] = None):
+    if plan is None:
+        plan = _plan_for(recall_plan_bytes(B))
     h = _Host()
     _check(load().spa_recall_index(
         int(B), int(num_kv_heads), h.arr(seq_lens, np.int32), int(n_sink), int(n_recent),
         h.arr(in_count, np.int32), h.arr(in_off, np.int64), _dptr(idx_in),
-        h.arr(out_count, np.int32), h.arr(out_off, np.int64), _dptr(idx_out), _stream(idx_out)))
+        h.arr(out_count, np.int32), h.arr(out_off, np.int64), _dptr(idx_out), _hptr(plan),
+        _nbytes(plan), _stream(idx_out)))
 
 
 def list_quality_workspace_bytes(B, num_qo_heads, seq_lens) -> int:
@@ -247,33 +357,62 @@ def list_quality_workspace_bytes(B, num_qo_heads, seq_lens) -> int:
                                                        h.arr(seq_lens, np.int32)))
 
 
+def list_quality_plan_bytes(B: int) -> int:
+    return int(load().spa_list_quality_plan_bytes(int(B)))
+
+
 def list_quality(B, spec_k, num_qo_heads, num_kv_heads, row, top_t, seq_lens, logits, logits_off,
                  lse, list_count, list_off, lists: Optional[torch.Tensor], top: torch.Tensor,
-                 coverage: torch.Tensor, recall: torch.Tensor, ws: torch.Tensor):
+                 coverage: torch.Tensor, recall: torch.Tensor, ws: torch.Tensor,
+                 plan: Optional[torch.Tensor] = None):
+    if plan is None:
+        plan = _plan_for(list_quality_plan_bytes(B))
     h = _Host()
     _check(load().spa_list_quality(
         int(B), int(spec_k), int(num_qo_heads), int(num_kv_heads), int(row), int(top_t),
         h.arr(seq_lens, np.int32), _dptr(logits), h.arr(logits_off, np.int64), _dptr(lse),
         h.arr(list_count, np.int32), h.arr(list_off, np.int64), _dptr(lists), _dptr(top),
-        _dptr(coverage), _dptr(recall), _dptr(ws), ws.numel() * ws.element_size(),
+        _dptr(coverage), _dptr(recall), _dptr(ws), _nbytes(ws), _hptr(plan), _nbytes(plan),
         _stream(logits)))
 
 
-def workspace(nbytes: int, device) -> torch.Tensor:
-    """A workspace of at least ``nbytes`` (its contents on entry do not matter)."""
-    return torch.empty((max(int(nbytes), 256),), dtype=torch.uint8, device=device)
+class PlanRing:
+    """A few pinned plan buffers used in turn, so the host can queue that many
+    calls ahead of the GPU (a call waits only for the buffer's previous use)."""
+
+    def __init__(self, nbytes: int, n: int = 4):
+        self.bufs = [plan_buffer(nbytes) for _ in range(n)]
+        self.args = [(_hptr(b), _nbytes(b)) for b in self.bufs]
+        self.i = 0
+
+    @property
+    def nbytes(self) -> int:
+        return _nbytes(self.bufs[0])
+
+    def next(self) -> torch.Tensor:
+        b = self.bufs[self.i]
+        self.i = (self.i + 1) % len(self.bufs)
+        return b
+
+    def next_args(self):
+        """(address, bytes) of the next buffer, as ctypes arguments."""
+        a = self.args[self.i]
+        self.i = (self.i + 1) % len(self.bufs)
+        return a
 
 
 # --------------------------------------------------------------------------- #
 # convenience: run one synthetic batch through the unified step
 # --------------------------------------------------------------------------- #
 class StepBuffers:
-    """Output and workspace tensors for one synthetic batch (see synth.Batch)."""
+    """Output, workspace and plan buffers for one synthetic batch (see synth.Batch)."""
 
-    def __init__(self, batch, avg_row_begin: int = 1, avg_row_count: Optional[int] = None):
+    def __init__(self, batch, avg_row_begin: int = 1, avg_row_count: Optional[int] = None,
+                 opts: Optional[Options] = None, n_plans: int = 4):
         w = batch.w
         dev = batch.q.device
         self.batch = batch
+        self.opts = opts if opts is not None else default_options(dev)
         self.lay = layout(w.num_qo_heads, w.num_kv_heads, w.head_dim, batch.q.dtype,
                           batch.num_slots, batch.stride)
         self.o = torch.empty_like(batch.q)
@@ -282,9 +421,10 @@ class StepBuffers:
         self.idx = batch.idx.clone()
         self.avg_row_begin = avg_row_begin
         self.avg_row_count = w.spec_k if avg_row_count is None else avg_row_count
-        nbytes = workspace_bytes(self.lay, batch.B, w.spec_k, batch.is_verify, batch.seq_lens,
-                                 batch.idx_count)
-        self.ws = workspace(nbytes, dev)
+        sizes = (self.lay, batch.B, w.spec_k, batch.is_verify, batch.seq_lens, batch.idx_count,
+                 self.opts)
+        self.ws = workspace(workspace_bytes(*sizes), dev)
+        self.plans = PlanRing(plan_bytes(*sizes), n_plans)
         # host metadata typed once, so a step only marshals pointers
         self.h_is_verify = np.ascontiguousarray(batch.is_verify, dtype=np.uint8)
         self.h_seq_lens = np.ascontiguousarray(batch.seq_lens, dtype=np.int32)
@@ -297,10 +437,10 @@ class StepBuffers:
         self._args = None
 
     def _marshal(self):
-        """The ctypes arguments of one call (all but the stream), rebuilt only
+        """The ctypes arguments of one call before the plan buffer, rebuilt only
         when an output, index or workspace buffer has moved or resized."""
         key = (self.idx.data_ptr(), self.o.data_ptr(), self.lse.data_ptr(),
-               self.logits.data_ptr(), self.ws.data_ptr(), self.ws.numel() * self.ws.element_size())
+               self.logits.data_ptr(), self.ws.data_ptr(), _nbytes(self.ws))
         if key != self._key:
             b = self.batch
             host = [np.ascontiguousarray(a) for a in (self.h_is_verify, self.h_seq_lens,
@@ -312,10 +452,12 @@ class StepBuffers:
                           _dptr(b.page_table), _dptr(b.q), _dptr(b.k_pool), _dptr(b.v_pool),
                           hp[3], hp[4], _dptr(self.idx), _dptr(self.o), _dptr(self.lse),
                           _dptr(self.logits), hp[5], int(self.avg_row_begin),
-                          int(self.avg_row_count), _dptr(self.ws),
-                          self.ws.numel() * self.ws.element_size())
+                          int(self.avg_row_count), _dptr(self.ws), _nbytes(self.ws))
             self._key = key
         return self._args
 
-    def step(self):
-        _check(load().spa_unified_step(*self._marshal(), _stream(self.batch.q)))
+    def step(self, opts: Optional[Options] = None):
+        """One unified step on the current stream (opts: instead of the buffers' own)."""
+        _check(load().spa_unified_step(*self._marshal(), *self.plans.next_args(),
+                                       _opts(self.opts if opts is None else opts),
+                                       _stream(self.batch.q)))

@@ -2,21 +2,22 @@
 // launches behind the C ABI of include/spa.h.
 //
 // A call turns the host metadata into a work plan -- one record per workgroup
-// -- written into a slot of a pinned host ring that the kernels read in place
-// (no copy is enqueued).  The attention plan lists its items longest first;
-// persistent attention workgroups draw the next item from a per-launch device
-// counter, so work flows to whichever XCD frees first.  A call enqueues at most three launches: the attention of
-// every request, the post-pass (split-K merges and score averaging), then the
-// top-K selection.
+// -- written into the caller's pinned plan buffer, which the kernels read in
+// place (no copy is enqueued).  The attention plan lists its items longest
+// first; persistent attention workgroups draw the next item from a work
+// counter in the caller's workspace, so work flows to whichever XCD frees
+// first.  A call enqueues at most three launches: the attention of every
+// request, the post-pass (split-K merges and score averaging), then the top-K
+// selection.  The library holds no per-call state: a plan buffer's header
+// carries the release protocol that tells a later call when the GPU no longer
+// reads it.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
-#include <atomic>
 #include <chrono>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
-#include <mutex>
 #include <string>
 #include <thread>
 #include <vector>
@@ -30,13 +31,11 @@ using namespace spa;
 namespace {
 
 thread_local std::string g_err;
-std::atomic<int32_t> g_verify_chunk{0};
-std::atomic<int32_t> g_draft_chunk{0};
-std::atomic<int32_t> g_overlap{0};
 
 constexpr int DEFAULT_VERIFY_CHUNK = 2048;  // fewer split-K partials
 constexpr int MIN_AUTO_VERIFY_CHUNK = 512;
 constexpr int DEFAULT_DRAFT_CHUNK = 1024;
+constexpr int DEFAULT_CUS = 256;  // MI355X
 
 int32_t fail(int32_t code, const std::string& msg) {
   g_err = msg;
@@ -71,6 +70,7 @@ struct Plan {
   std::vector<int64_t> part0;   // first split-K partial row of (r, 0); heads follow
   int max_nchunk = 1;           // most split-K chunks of any merged request
   int cv = DEFAULT_VERIFY_CHUNK;  // positions per verify item
+  int cd = DEFAULT_DRAFT_CHUNK;   // list entries per draft item
   int n_items = 0;              // attention records
   // split: a mixed batch runs its draft items in a second attention launch on
   // a side stream, concurrently with verify attention, merge, averaging and
@@ -85,11 +85,41 @@ struct Plan {
   int64_t pbar_elems = 0;
   // pinned plan layout
   size_t h_items = 0, h_items_d = 0, h_post = 0, h_post_d = 0, h_sel = 0, h_bytes = 0;
-  // workspace layout
+  // workspace layout (work counters at offset 0)
   size_t off_part_o = 0, off_part_ml = 0, off_pbar = 0, off_plan = 0, off_hist = 0, total = 0;
   int nthr = 256;
   size_t smem = 0;
 };
+
+// The options a call uses (spa_options with its defaults applied).
+struct Opts {
+  int verify_chunk = 0;  // 0: automatic
+  int draft_chunk = DEFAULT_DRAFT_CHUNK;
+  int num_cus = DEFAULT_CUS;
+  bool overlap = false;
+  hipStream_t side = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  hipEvent_t timing[8] = {};
+};
+
+int32_t check_opts(const spa_options* o, Opts* out) {
+  *out = Opts{};
+  if (!o) return SPA_OK;
+  if (o->verify_chunk < 0 || o->verify_chunk > VERIFY_MAX_CHUNK)
+    return fail(SPA_ERR_INVALID_ARG, "options: verify_chunk outside [0, 2048]");
+  if (o->draft_chunk < 0 || o->draft_chunk > DRAFT_MAX_CHUNK)
+    return fail(SPA_ERR_INVALID_ARG, "options: draft_chunk outside [0, 2048]");
+  if (o->num_cus < 0) return fail(SPA_ERR_INVALID_ARG, "options: num_cus < 0");
+  out->verify_chunk = o->verify_chunk;
+  if (o->draft_chunk > 0) out->draft_chunk = o->draft_chunk;
+  if (o->num_cus > 0) out->num_cus = o->num_cus;
+  out->overlap = o->overlap != 0;
+  out->side = static_cast<hipStream_t>(o->side_stream);
+  out->fork = static_cast<hipEvent_t>(o->fork_event);
+  out->join = static_cast<hipEvent_t>(o->join_event);
+  for (int i = 0; i < 8; ++i) out->timing[i] = static_cast<hipEvent_t>(o->timing[i]);
+  return SPA_OK;
+}
 
 int32_t check_layout(const spa_layout* lay, Shape* s) {
   if (!lay) return fail(SPA_ERR_INVALID_ARG, "layout is NULL");
@@ -130,28 +160,9 @@ int32_t check_segments(std::vector<std::pair<int64_t, int64_t>> seg, const char*
   return SPA_OK;
 }
 
-// Compute units of the current device (cached per device; 256 if the query fails).
-int device_cus() {
-  static std::mutex mu;
-  static std::vector<int> cus;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 256;
-  std::lock_guard<std::mutex> lock(mu);
-  if ((int)cus.size() <= dev) cus.resize(dev + 1, 0);
-  if (cus[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) {
-      (void)hipGetLastError();
-      n = 256;
-    }
-    cus[dev] = n;
-  }
-  return cus[dev];
-}
-
-// Positions per verify item.  Unless set by spa_set_split: 2048 when the
-// verify requests bring at least two and a half such chunks per CU (positions
-// times KV heads over the CU count), else 512.  Measured in steady state
+// Positions per verify item.  Unless set in the options: 2048 when the verify
+// requests bring at least two and a half such chunks per CU (positions times
+// KV heads over the options' CU count), else 512.  Measured in steady state
 // (200 steps after 60 warm-up, best of three interleaved runs), 2048 / 1024 /
 // 512-position chunks: Qwen3-8B-shaped batch (3584 positions per CU)
 // 190.6 / 192.5 / 187.0 us, Qwen3-1.7B-shaped (1438) 86.3 at 1024, 83.3 at
@@ -159,9 +170,8 @@ int device_cus() {
 // 358 us (768: 364).  Short chunks spread a light verify load over the chip
 // and shorten the launch's tail; heavy loads keep the long chunks, which need
 // fewer split-K partials and merges.
-int verify_chunk(const std::vector<Req>& rq, int Hkv) {
-  const int v = g_verify_chunk.load();
-  if (v > 0) return std::min(v, VERIFY_MAX_CHUNK);
+int verify_chunk(const std::vector<Req>& rq, int Hkv, const Opts& o) {
+  if (o.verify_chunk > 0) return o.verify_chunk;
   int64_t positions = 0;
   int longest = 0;
   for (const Req& q : rq)
@@ -169,15 +179,11 @@ int verify_chunk(const std::vector<Req>& rq, int Hkv) {
       positions += q.L;
       longest = std::max(longest, q.L);
     }
-  const int64_t per_cu = positions * Hkv / device_cus();
+  const int64_t per_cu = positions * Hkv / o.num_cus;
   int c = 2 * per_cu >= 5 * (int64_t)DEFAULT_VERIFY_CHUNK ? DEFAULT_VERIFY_CHUNK : MIN_AUTO_VERIFY_CHUNK;
   // a request may not need more split-K chunks than a merge takes
   while (c < DEFAULT_VERIFY_CHUNK && (longest + c - 1) / c > MAX_MERGE_CHUNKS) c *= 2;
   return c;
-}
-int draft_chunk() {
-  int v = g_draft_chunk.load();
-  return v > 0 ? std::min(v, DRAFT_MAX_CHUNK) : DEFAULT_DRAFT_CHUNK;
 }
 
 int avg_parts(int L) { return (L + AVG_SPAN - 1) / AVG_SPAN; }
@@ -185,21 +191,25 @@ int64_t pbar_row(int L) { return (L + 3) / 4 * 4; }  // rows start 16-byte align
 
 // Counts, offsets and the item order of the attention (attn) and/or PillarAttn
 // selection (topk) plan for `rq`.
-int32_t plan_size(const Shape& s, const std::vector<Req>& rq, bool attn, bool topk, Plan* pl) {
+int32_t plan_size(const Shape& s, const std::vector<Req>& rq, bool attn, bool topk, const Opts& o,
+                  Plan* pl) {
   const int B = (int)rq.size();
   const int G = s.G, Hkv = s.Hkv, D = s.d;
   const int rows_v = s.k + 1;
   const bool bf16 = s.dtype == SPA_BF16;
   const int esz = bf16 ? 2 : 4;
-  const int CV = verify_chunk(rq, Hkv), CD = draft_chunk();
+  const int CV = verify_chunk(rq, Hkv, o), CD = o.draft_chunk;
   pl->cv = CV;
+  pl->cd = CD;
   if (s.k > 255) return fail(SPA_ERR_UNSUPPORTED, "spec_k above 255");
   pl->attn = attn;
   pl->topk = topk;
 
   bool any_verify = false, any_draft = false;
   for (auto& q : rq) (q.verify ? any_verify : any_draft) = true;
-  pl->split = attn && topk && any_verify && any_draft && g_overlap.load() != 0;
+  pl->split = attn && topk && any_verify && any_draft && o.overlap;
+  if (pl->split && (!o.side || !o.fork || !o.join))
+    return fail(SPA_ERR_INVALID_ARG, "options: overlap needs side_stream, fork_event and join_event");
 
   pl->nchunk.assign(B, 1);
   pl->part0.assign(B, 0);
@@ -288,20 +298,21 @@ int32_t plan_size(const Shape& s, const std::vector<Req>& rq, bool attn, bool to
   pl->h_sel = h;
   h = align_up(h + (size_t)pl->n_sel * sizeof(PostItem), 256);
   pl->h_bytes = h;
-  // workspace layout
-  size_t o = 0;
-  pl->off_part_o = o;  // partial outputs in the output type
-  o = align_up(o + (size_t)part_rows * D * esz, 256);
-  pl->off_part_ml = o;
-  o = align_up(o + (size_t)part_rows * 2 * 4, 256);
-  pl->off_pbar = o;
-  o = align_up(o + (size_t)pbar * 4, 256);
-  // the attention launch copies the post-pass and selection records here
-  pl->off_plan = o;
-  if (attn) o = align_up(o + (pl->h_bytes - pl->h_post), 256);
-  pl->off_hist = o;
-  o = align_up(o + (size_t)pl->n_hist * HIST_BINS * 4, 256);
-  pl->total = o;
+  // workspace layout: the attention launches' work counters first
+  size_t w = WS_COUNTERS;
+  pl->off_part_o = w;  // partial outputs in the output type
+  w = align_up(w + (size_t)part_rows * D * esz, 256);
+  pl->off_part_ml = w;
+  w = align_up(w + (size_t)part_rows * 2 * 4, 256);
+  pl->off_pbar = w;
+  w = align_up(w + (size_t)pbar * 4, 256);
+  // the attention launch (or, without one, the post-pass) copies the records
+  // of the launches after it here
+  pl->off_plan = w;
+  if (attn || topk) w = align_up(w + (pl->h_bytes - pl->h_post), 256);
+  pl->off_hist = w;
+  w = align_up(w + (size_t)pl->n_hist * HIST_BINS * 4, 256);
+  pl->total = w;
   return SPA_OK;
 }
 
@@ -311,7 +322,7 @@ void plan_write(const Shape& s, const std::vector<Req>& rq, const Plan& pl, char
   const int G = s.G, Hkv = s.Hkv;
   const int rows_v = s.k + 1;
   const bool bf16 = s.dtype == SPA_BF16;
-  const int CV = pl.cv, CD = draft_chunk();
+  const int CV = pl.cv, CD = pl.cd;
   if (pl.attn) {
     Item* items_v = reinterpret_cast<Item*>(h + pl.h_items);
     Item* items_d = reinterpret_cast<Item*>(h + pl.h_items_d);
@@ -419,134 +430,26 @@ void plan_write(const Shape& s, const std::vector<Req>& rq, const Plan& pl, char
     }
 }
 
-// ---- opt-in per-launch timing ------------------------------------------------
-enum {
-  PROF_ATTN = 0,        // the attention launch (with overlap: the verify attention launch)
-  PROF_POST = 1,
-  PROF_SELECT = 2,
-  PROF_ATTN_DRAFT = 3,  // the draft attention launch of an overlapped unified step
-  PROF_ATTN_SPAN = 4,   // all attention of a call: first launch start to last launch end
-  PROF_RECALL = 5,      // the recallable-index launch
-  PROF_QUALITY = 6,     // the list-quality launch
-  PROF_N = 7
-};
-std::mutex g_prof_mu;
-std::atomic<int32_t> g_prof_mask{0};
-struct ProfPending {
-  int which;
-  hipEvent_t a, b;
-  hipEvent_t c = nullptr;  // a second end event (span over two streams), or null
-};
-std::vector<ProfPending> g_prof_pending;
-std::vector<hipEvent_t> g_prof_free;
-int64_t g_prof_count[PROF_N] = {0};
-double g_prof_ms[PROF_N] = {0};
-
-hipEvent_t prof_event() {
-  if (!g_prof_free.empty()) {
-    hipEvent_t e = g_prof_free.back();
-    g_prof_free.pop_back();
-    return e;
-  }
-  hipEvent_t e = nullptr;
-  if (hipEventCreate(&e) != hipSuccess) return nullptr;
-  return e;
-}
-
-// Brackets one launch with a pair of events when the kernel is selected.
-struct ProfScope {
-  int which;
-  hipStream_t st;
-  hipEvent_t a = nullptr;
-  ProfScope(int w, hipStream_t s) : which(w), st(s) {
-    if (!((g_prof_mask.load() >> which) & 1)) return;
-    std::lock_guard<std::mutex> lock(g_prof_mu);
-    a = prof_event();
-    if (a && hipEventRecord(a, st) != hipSuccess) a = nullptr;
-  }
-  ~ProfScope() {
-    if (!a) return;
-    std::lock_guard<std::mutex> lock(g_prof_mu);
-    hipEvent_t b = prof_event();
-    if (b && hipEventRecord(b, st) == hipSuccess) {
-      g_prof_pending.push_back(ProfPending{which, a, b});
-    } else {
-      g_prof_free.push_back(a);
-      if (b) g_prof_free.push_back(b);
-    }
-  }
-};
-
-// Span of all attention of one call: a start event on the caller's stream and
-// an end event behind each attention launch (one or two streams).
-struct ProfSpan {
-  hipEvent_t a = nullptr, b = nullptr, c = nullptr;
-  bool on = false;
-  void start(hipStream_t st) {
-    if (!((g_prof_mask.load() >> PROF_ATTN_SPAN) & 1)) return;
-    std::lock_guard<std::mutex> lock(g_prof_mu);
-    a = prof_event();
-    on = a && hipEventRecord(a, st) == hipSuccess;
-  }
-  void end(hipStream_t st, bool second) {
-    if (!on) return;
-    std::lock_guard<std::mutex> lock(g_prof_mu);
-    hipEvent_t e = prof_event();
-    if (e && hipEventRecord(e, st) != hipSuccess) e = nullptr;
-    (second ? c : b) = e;
-  }
-  void finish() {
-    if (!on) return;
-    std::lock_guard<std::mutex> lock(g_prof_mu);
-    if (b) {
-      g_prof_pending.push_back(ProfPending{PROF_ATTN_SPAN, a, b, c});
-    } else {
-      g_prof_free.push_back(a);
-      if (c) g_prof_free.push_back(c);
-    }
-  }
-};
-
-// ---- pinned plan ring ----------------------------------------------------------
-// RING slots carved from one pinned, device-mapped arena.  A slot holds one
-// call's plan until the call's last kernel has finished; it is reused only
-// after the event recorded behind that kernel completes.  When a plan outgrows
-// the slots, every pending slot is waited for and the arena is reallocated
-// once for all of them, so pinned allocation happens only when plans grow.
+// ---- caller plan buffers -------------------------------------------------------
+// A plan buffer starts with a PlanHeader.  A call that takes a buffer first
+// waits until the GPU no longer reads what the previous call wrote there: that
+// call's kernels stored its sequence number into each header word it armed
+// (done[0], and done[1] for an overlapped step's draft launch).  The last
+// reader stores it -- the post-pass or selection launch as it starts when a
+// launch before it on the stream was the last to read the pinned records, the
+// attention launch's last work draw when that launch is the call's only
+// reader, or a one-thread release launch.  Storing from the kernels instead
+// of recording an event keeps the stream free of markers: an event between
+// one call's last launch and the next call's first cost a gap of about 5 us.
 //
-// A call whose pinned plan is last read by its attention launch and that
-// then runs a post-pass on the same stream does without the event: the
-// post-pass stores the call's sequence number into the slot's word of a small
-// mapped, coherent host array as it starts, and the host waits for that value
-// instead.  Recording an event costs the stream a gap of about 5 us before the
-// next call's first launch; the store costs nothing measurable.
-//
-// A call that returns an error after acquiring its slot leaves the slot
-// marked WAIT_DRAIN: before reuse the host drains the slot's device, since a
-// launch issued before the error may still read the slot.
-enum SlotWait : int { WAIT_NONE = 0, WAIT_EVENT = 1, WAIT_SIGNAL = 2, WAIT_DRAIN = 3 };
-struct PlanSlot {
-  char* host = nullptr;
-  char* dev = nullptr;
-  hipEvent_t ev = nullptr;
-  int wait = WAIT_NONE;
-  uint64_t seq = 0;  // WAIT_SIGNAL: the value the post-pass stores
-  int device = 0;    // device of the call that used the slot
-};
-constexpr int RING = 16;
-static_assert(2 * RING <= TICKET_SETS, "two attention item counters per plan slot");
-std::mutex g_ring_mu;
-PlanSlot g_ring[RING];
-char* g_arena_host = nullptr;
-char* g_arena_dev = nullptr;
-size_t g_slot_cap = 0;
-unsigned g_ring_next = 0;
-uint64_t* g_done_host = nullptr;  // [RING], written by the device
-uint64_t* g_done_dev = nullptr;
-uint64_t g_seq = 0;
+// A call marks the header `drain` before its first launch and clears it once
+// every launch is queued, so a call that fails part-way leaves the buffer to
+// be reused only after its device has drained.  A wait that lasts half a
+// second drains the device too, so a failed device is reported instead of
+// spun on.
 
 // Waits for all work on `device`; once it has drained, every launch of the
-// call that used a slot on it has finished.
+// call that wrote a buffer on it has finished.
 int32_t drain_device(int device) {
   int cur = 0;
   hipError_t e = hipGetDevice(&cur);
@@ -554,128 +457,86 @@ int32_t drain_device(int device) {
   if (switched) e = hipSetDevice(device);
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (switched) (void)hipSetDevice(cur);
-  if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("plan slot wait: ") + hipGetErrorString(e));
+  if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("plan buffer wait: ") + hipGetErrorString(e));
   return SPA_OK;
 }
 
-int32_t wait_slot(PlanSlot& s) {
-  if (s.wait == WAIT_EVENT) {
-    const hipError_t e = hipEventSynchronize(s.ev);
-    if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("plan slot wait: ") + hipGetErrorString(e));
-  } else if (s.wait == WAIT_SIGNAL) {
-    const uint64_t* w = g_done_host + (&s - g_ring);
+// A call's hold on a plan buffer: host and device addresses of its records and
+// the header words its kernels store into.
+struct PlanRef {
+  PlanHeader* hdr = nullptr;
+  char* host = nullptr;        // records (after the header)
+  const char* dev = nullptr;   // the same records as the device addresses them
+  uint64_t* done_dev = nullptr;  // device address of hdr->done[0]
+  uint64_t seq = 0;
+};
+
+// Checks a plan buffer of `plan_bytes` for `need` bytes of records (no
+// side effect on failure).
+int32_t check_plan(void* h_plan, size_t plan_bytes, size_t need, char** dev_base) {
+  if (!h_plan) return fail(SPA_ERR_INVALID_ARG, "h_plan is NULL");
+  if ((reinterpret_cast<uintptr_t>(h_plan) & 63) != 0)
+    return fail(SPA_ERR_INVALID_ARG, "h_plan must be 64-byte aligned");
+  if (plan_bytes < PLAN_HEADER + need)
+    return fail(SPA_ERR_PLAN_TOO_SMALL, "plan buffer of " + std::to_string(plan_bytes) +
+                                            " bytes, need " + std::to_string(PLAN_HEADER + need));
+  void* d = nullptr;
+  const hipError_t e = hipHostGetDevicePointer(&d, h_plan, 0);
+  if (e != hipSuccess || !d) {
+    (void)hipGetLastError();
+    return fail(SPA_ERR_INVALID_ARG, "h_plan is not pinned host memory the device can read");
+  }
+  *dev_base = static_cast<char*>(d);
+  return SPA_OK;
+}
+
+// Takes a checked plan buffer for a new call: waits for (or drains) the
+// previous call's readers, then marks the buffer in use.
+int32_t acquire_plan(void* h_plan, char* dev_base, PlanRef* out) {
+  PlanHeader* h = static_cast<PlanHeader*>(h_plan);
+  uint64_t prev = 0;
+  if (h->magic == PLAN_MAGIC) {
+    prev = h->issued;
+    bool drain = h->drain != 0;
     const auto t0 = std::chrono::steady_clock::now();
-    while (__atomic_load_n(w, __ATOMIC_ACQUIRE) < s.seq) {
-      std::this_thread::yield();
-      // A long wait drains the device instead, so that a failed device is
-      // reported as an error rather than spun on.
-      if (std::chrono::steady_clock::now() - t0 > std::chrono::milliseconds(500)) {
-        const int32_t rc = drain_device(s.device);
-        if (rc) return rc;
-        break;
+    for (int b = 0; b < 2 && !drain; ++b) {
+      if (!((h->need >> b) & 1u)) continue;
+      while (__atomic_load_n(&h->done[b], __ATOMIC_ACQUIRE) < prev) {
+        std::this_thread::yield();
+        if (std::chrono::steady_clock::now() - t0 > std::chrono::milliseconds(500)) {
+          drain = true;
+          break;
+        }
       }
     }
-  } else if (s.wait == WAIT_DRAIN) {
-    const int32_t rc = drain_device(s.device);
-    if (rc) return rc;
-  }
-  s.wait = WAIT_NONE;
-  return SPA_OK;
-}
-
-int32_t grow_arena(size_t need) {
-  hipError_t e;
-  for (auto& s : g_ring) {
-    const int32_t rc = wait_slot(s);
-    if (rc) return rc;
-  }
-  if (!g_done_host) {
-    void* h = nullptr;
-    e = hipHostMalloc(&h, RING * sizeof(uint64_t),
-                      hipHostMallocMapped | hipHostMallocPortable | hipHostMallocCoherent);
-    if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("pinned done words: ") + hipGetErrorString(e));
-    void* d = nullptr;
-    e = hipHostGetDevicePointer(&d, h, 0);
-    if (e != hipSuccess) {
-      (void)hipHostFree(h);
-      return fail(SPA_ERR_HIP, std::string("pinned done words mapping: ") + hipGetErrorString(e));
+    if (drain) {
+      const int32_t rc = drain_device(h->device);
+      if (rc) return rc;
     }
-    std::memset(h, 0, RING * sizeof(uint64_t));
-    g_done_host = static_cast<uint64_t*>(h);
-    g_done_dev = static_cast<uint64_t*>(d);
   }
-  if (g_arena_host) (void)hipHostFree(g_arena_host);
-  g_arena_host = g_arena_dev = nullptr;
-  g_slot_cap = 0;
-  const size_t cap = align_up(std::max<size_t>(need * 2, 256 << 10), 4096);
-  void* h = nullptr;
-  e = hipHostMalloc(&h, cap * RING, hipHostMallocMapped | hipHostMallocPortable);
-  if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("pinned plan: ") + hipGetErrorString(e));
-  void* d = nullptr;
-  e = hipHostGetDevicePointer(&d, h, 0);
-  if (e != hipSuccess) {
-    (void)hipHostFree(h);
-    return fail(SPA_ERR_HIP, std::string("pinned plan mapping: ") + hipGetErrorString(e));
-  }
-  g_arena_host = static_cast<char*>(h);
-  g_arena_dev = static_cast<char*>(d);
-  g_slot_cap = cap;
-  for (int i = 0; i < RING; ++i) {
-    g_ring[i].host = g_arena_host + (size_t)i * cap;
-    g_ring[i].dev = g_arena_dev + (size_t)i * cap;
-  }
-  return SPA_OK;
-}
-
-int32_t acquire_slot(const Plan& pl, PlanSlot** out) {
-  hipError_t e;
-  if (g_slot_cap < pl.h_bytes) {
-    const int32_t rc = grow_arena(pl.h_bytes);
-    if (rc) return rc;
-  }
-  PlanSlot& s = g_ring[g_ring_next++ % RING];
-  const int32_t rc = wait_slot(s);
-  if (rc) return rc;
-  s.seq = ++g_seq;
-  if (hipGetDevice(&s.device) != hipSuccess) return fail(SPA_ERR_HIP, "no current device");
-  s.wait = WAIT_DRAIN;  // until the call has queued its release
-  if (!s.ev) {
-    // The event only tells the host that the GPU has finished reading the
-    // slot (host memory, read by the kernels; nothing flows back through it),
-    // so it skips the system-scope fence: with the fence, each call's event
-    // wrote back the caches and delayed the next call's first launch by
-    // about 6 us.
-    e = hipEventCreateWithFlags(&s.ev, hipEventDisableTiming | hipEventDisableSystemFence);
-    if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("event create: ") + hipGetErrorString(e));
-  }
-  *out = &s;
-  return SPA_OK;
-}
-
-// ---- side stream of the split attention launch --------------------------------
-// One per device, default priority; forked from and joined back to the
-// caller's stream with events, so the call stays ordered on that stream.
-struct Side {
-  hipStream_t stream = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
-};
-std::vector<Side> g_side;
-
-int32_t side_stream(Side** out) {
   int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("get device: ") + hipGetErrorString(e));
-  if ((int)g_side.size() <= dev) g_side.resize(dev + 1);
-  Side& sd = g_side[dev];
-  if (!sd.stream) {
-    e = hipStreamCreateWithFlags(&sd.stream, hipStreamNonBlocking);
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&sd.fork, hipEventDisableTiming);
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&sd.join, hipEventDisableTiming);
-    if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("side stream: ") + hipGetErrorString(e));
-  }
-  *out = &sd;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(SPA_ERR_HIP, "no current device");
+  h->need = 0;
+  h->drain = 1;  // until every launch of this call is queued
+  h->device = dev;
+  h->issued = prev + 1;
+  __atomic_store_n(&h->magic, PLAN_MAGIC, __ATOMIC_RELEASE);
+  out->hdr = h;
+  out->host = static_cast<char*>(h_plan) + PLAN_HEADER;
+  out->dev = dev_base + PLAN_HEADER;
+  out->done_dev = reinterpret_cast<uint64_t*>(dev_base + offsetof(PlanHeader, done));
+  out->seq = prev + 1;
   return SPA_OK;
 }
+
+// Every launch of the call is queued: a later call waits for the armed words.
+void arm_plan(PlanRef& pr, uint32_t need) {
+  pr.hdr->need = need;
+  __atomic_store_n(&pr.hdr->drain, 0, __ATOMIC_RELEASE);
+}
+
+// Records an optional timing event on a stream.
+hipError_t mark(hipEvent_t ev, hipStream_t st) { return ev ? hipEventRecord(ev, st) : hipSuccess; }
 
 struct Buffers {
   const int32_t* page_table = nullptr;
@@ -690,28 +551,29 @@ struct Buffers {
 };
 
 int32_t run(const Shape& s, const std::vector<Req>& rq, const Plan& pl, const Buffers& b,
-            int avg_begin, int avg_count, void* d_ws, size_t ws_bytes, hipStream_t st) {
+            int avg_begin, int avg_count, void* d_ws, size_t ws_bytes, void* h_plan,
+            size_t plan_bytes, const Opts& o, hipStream_t st) {
   if (ws_bytes < pl.total)
     return fail(SPA_ERR_WORKSPACE_TOO_SMALL,
                 "workspace of " + std::to_string(ws_bytes) + " bytes, need " + std::to_string(pl.total));
-  if (pl.total > 0 && !d_ws) return fail(SPA_ERR_INVALID_ARG, "d_ws is NULL");
+  if (!d_ws) return fail(SPA_ERR_INVALID_ARG, "d_ws is NULL");
+  if ((reinterpret_cast<uintptr_t>(d_ws) & 255) != 0)
+    return fail(SPA_ERR_INVALID_ARG, "d_ws must be 256-byte aligned");
   const int n_post = pl.n_avg + pl.n_merge;
   if (pl.n_items == 0 && pl.n_items_d == 0 && n_post == 0 && pl.n_sel == 0) return SPA_OK;
-  std::lock_guard<std::mutex> lock(g_ring_mu);
-  PlanSlot* slot = nullptr;
-  int32_t rc = acquire_slot(pl, &slot);
+  char* dev_base = nullptr;
+  int32_t rc = check_plan(h_plan, plan_bytes, pl.h_bytes, &dev_base);
   if (rc) return rc;
-  plan_write(s, rq, pl, static_cast<char*>(slot->host));
-  const char* plan = static_cast<const char*>(slot->dev);
+  PlanRef pr;
+  rc = acquire_plan(h_plan, dev_base, &pr);
+  if (rc) return rc;
+  plan_write(s, rq, pl, pr.host);
+  const char* plan = pr.dev;
   char* ws = static_cast<char*>(d_ws);
+  uint32_t* tickets = reinterpret_cast<uint32_t*>(ws);  // [0]: attention on `st`, [1]: draft launch
   void* part_o = ws + pl.off_part_o;
   float* part_ml = reinterpret_cast<float*>(ws + pl.off_part_ml);
-  hipError_t e;
-  Side* side = nullptr;
-  if (pl.split) {
-    rc = side_stream(&side);
-    if (rc) return rc;
-  }
+  hipError_t e = hipSuccess;
   if (pl.n_items > 0 || pl.n_items_d > 0) {
     AttnParams p;
     p.items = reinterpret_cast<const Item*>(plan + pl.h_items);
@@ -732,9 +594,7 @@ int32_t run(const Shape& s, const std::vector<Req>& rq, const Plan& pl, const Bu
     p.G = s.G;
     p.k = s.k;
     p.sm_scale = s.scale;
-    // the slot is reused only after this call has finished, so its two item
-    // counters are never shared by launches in flight
-    p.ticket_set = 2 * static_cast<int32_t>(slot - g_ring);
+    p.ticket = tickets;
     // the launch on `st` moves the records of the launches that follow it
     p.plan_src = reinterpret_cast<const uint4*>(plan + pl.h_post);
     p.plan_dst = reinterpret_cast<uint4*>(ws + pl.off_plan);
@@ -742,60 +602,52 @@ int32_t run(const Shape& s, const std::vector<Req>& rq, const Plan& pl, const Bu
     // ... and clears the score histograms the post-pass adds to
     p.zero_dst = reinterpret_cast<uint4*>(ws + pl.off_hist);
     p.zero_n16 = pl.n_items > 0 ? static_cast<int32_t>((size_t)pl.n_hist * HIST_BINS * 4 / 16) : 0;
-    // a call that is this one launch reports its slot free from the launch
+    // a call that is this one launch reports its plan free from the launch
     const bool attn_only = pl.n_items > 0 && n_post == 0 && pl.n_sel == 0 && !pl.split;
-    p.done = attn_only ? g_done_dev + (slot - g_ring) : nullptr;
-    p.done_val = slot->seq;
-    ProfSpan span;
-    span.start(st);
+    p.done = attn_only ? pr.done_dev : nullptr;
+    p.done_val = pr.seq;
     if (pl.split) {
       // the fork point: everything already on `st`, but not the verify attention
-      e = hipEventRecord(side->fork, st);
+      e = hipEventRecord(o.fork, st);
       if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("fork: ") + hipGetErrorString(e));
     }
     // verify (or all) attention first, so that its long items reach the CUs
     // before the draft launch's
     if (pl.n_items > 0) {
-      ProfScope ps(PROF_ATTN, st);
-      e = launch_attn(p, s.dtype, s.d, pl.n_items, pl.nthr, pl.smem, false, st);
+      e = mark(o.timing[0], st);
+      if (e == hipSuccess) e = launch_attn(p, s.dtype, s.d, pl.n_items, pl.nthr, pl.smem, false, st);
+      if (e == hipSuccess) e = mark(o.timing[1], st);
+      if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("attention launch: ") + hipGetErrorString(e));
     }
-    if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("attention launch: ") + hipGetErrorString(e));
-    span.end(st, false);
     if (pl.split) {
-      e = hipStreamWaitEvent(side->stream, side->fork, 0);
+      e = hipStreamWaitEvent(o.side, o.fork, 0);
       if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("fork wait: ") + hipGetErrorString(e));
       AttnParams pd = p;
       pd.items = reinterpret_cast<const Item*>(plan + pl.h_items_d);
-      pd.ticket_set = p.ticket_set + 1;
+      pd.ticket = tickets + 1;
       pd.plan_n16 = 0;
       pd.zero_n16 = 0;
-      pd.done = nullptr;
-      {
-        ProfScope ps(PROF_ATTN_DRAFT, side->stream);
-        e = launch_attn(pd, s.dtype, s.d, pl.n_items_d, pl.nthr, pl.smem, true, side->stream);
-      }
+      pd.done = pr.done_dev + 1;  // its last work draw releases its records
+      e = mark(o.timing[6], o.side);
+      if (e == hipSuccess)
+        e = launch_attn(pd, s.dtype, s.d, pl.n_items_d, pl.nthr, pl.smem, true, o.side);
+      if (e == hipSuccess) e = mark(o.timing[7], o.side);
       if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("draft attention launch: ") + hipGetErrorString(e));
-      span.end(side->stream, true);
-      e = hipEventRecord(side->join, side->stream);
+      e = hipEventRecord(o.join, o.side);
       if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("join record: ") + hipGetErrorString(e));
     }
-    span.finish();
   }
-  // The device reports the slot free when the attention launch on `st` is
-  // the plan's last reader (no side-stream launch): the post-pass as it
-  // starts, or the attention launch itself when it is the call's only one.
-  const bool signal = pl.n_items > 0 && !pl.split && (n_post > 0 || pl.n_sel == 0);
-  // selected rows' score histograms: cleared by the attention launch on `st`
-  uint32_t* hist = (pl.n_items > 0 && pl.n_hist > 0) ? reinterpret_cast<uint32_t*>(ws + pl.off_hist) : nullptr;
-  // records of the launches below: the workspace copy when the attention
-  // launch on `st` made one, else the pinned plan
-  auto post_rec = [&](size_t h_off) {
-    return reinterpret_cast<const PostItem*>(pl.n_items > 0 ? ws + pl.off_plan + (h_off - pl.h_post)
-                                                            : plan + h_off);
+  // records of the launches below: the workspace copy, made by the attention
+  // launch on `st` or (without one) by the post-pass for the selection launch
+  const bool attn_st = pl.n_items > 0;
+  auto ws_rec = [&](size_t h_off) {
+    return reinterpret_cast<const PostItem*>(ws + pl.off_plan + (h_off - pl.h_post));
   };
+  // selected rows' score histograms: cleared by the attention launch on `st`
+  uint32_t* hist = (attn_st && pl.n_hist > 0) ? reinterpret_cast<uint32_t*>(ws + pl.off_hist) : nullptr;
   if (n_post > 0) {
     PostParams pp;
-    pp.items = post_rec(pl.h_post);
+    pp.items = attn_st ? ws_rec(pl.h_post) : reinterpret_cast<const PostItem*>(plan + pl.h_post);
     pp.part_o = part_o;
     pp.part_ml = part_ml;
     pp.o = b.o;
@@ -806,35 +658,41 @@ int32_t run(const Shape& s, const std::vector<Req>& rq, const Plan& pl, const Bu
     pp.G = s.G;
     pp.avg_row_begin = avg_begin;
     pp.avg_row_count = avg_count;
-    pp.done = signal ? g_done_dev + (slot - g_ring) : nullptr;
-    pp.done_val = slot->seq;
+    // the attention launch before it read the pinned records last
+    pp.done = attn_st ? pr.done_dev : nullptr;
+    pp.done_val = pr.seq;
     pp.hist = hist;
-    {
-      ProfScope ps(PROF_POST, st);
+    pp.plan_src = reinterpret_cast<const uint4*>(plan + pl.h_sel);
+    pp.plan_dst = reinterpret_cast<uint4*>(ws + pl.off_plan + (pl.h_sel - pl.h_post));
+    pp.plan_n16 = attn_st ? 0 : static_cast<int32_t>((pl.h_bytes - pl.h_sel) / 16);
+    e = mark(o.timing[2], st);
+    if (e == hipSuccess)
       e = launch_post(pp, s.dtype, s.d, n_post,
                       post_smem_bytes(pl.n_avg ? avg_count * s.G : 0, pl.max_nchunk, hist != nullptr), st);
-    }
+    if (e == hipSuccess) e = mark(o.timing[3], st);
     if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("post-pass launch: ") + hipGetErrorString(e));
   }
   if (pl.n_sel > 0) {
     SelectParams sp;
-    sp.items = post_rec(pl.h_sel);
+    sp.items = ws_rec(pl.h_sel);
     sp.pbar = reinterpret_cast<const float*>(ws + pl.off_pbar);
     sp.idx_out = b.idx_out;
     sp.hist = hist;
     sp.bm_bits = select_bitmap_bits(pl.max_sel_len);
-    {
-      ProfScope ps(PROF_SELECT, st);
-      e = launch_select(sp, pl.n_sel, st);
-    }
+    // without an attention launch, the post-pass before it read the pinned records last
+    sp.done = attn_st ? nullptr : pr.done_dev;
+    sp.done_val = pr.seq;
+    e = mark(o.timing[4], st);
+    if (e == hipSuccess) e = launch_select(sp, pl.n_sel, st);
+    if (e == hipSuccess) e = mark(o.timing[5], st);
     if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("selection launch: ") + hipGetErrorString(e));
   }
   if (pl.split) {
-    e = hipStreamWaitEvent(st, side->join, 0);
+    e = hipStreamWaitEvent(st, o.join, 0);
     if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("join: ") + hipGetErrorString(e));
     if (pl.n_merge_d > 0) {  // merges of drafts split into several chunks
       PostParams pp;
-      pp.items = post_rec(pl.h_post_d);
+      pp.items = ws_rec(pl.h_post_d);
       pp.part_o = part_o;
       pp.part_ml = part_ml;
       pp.o = b.o;
@@ -848,20 +706,14 @@ int32_t run(const Shape& s, const std::vector<Req>& rq, const Plan& pl, const Bu
       pp.done = nullptr;
       pp.done_val = 0;
       pp.hist = nullptr;
-      {
-        ProfScope ps(PROF_POST, st);
-        e = launch_post(pp, s.dtype, s.d, pl.n_merge_d, post_smem_bytes(0, pl.max_nchunk, false), st);
-      }
+      pp.plan_src = nullptr;
+      pp.plan_dst = nullptr;
+      pp.plan_n16 = 0;
+      e = launch_post(pp, s.dtype, s.d, pl.n_merge_d, post_smem_bytes(0, pl.max_nchunk, false), st);
       if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("draft merge launch: ") + hipGetErrorString(e));
     }
   }
-  if (signal) {
-    slot->wait = WAIT_SIGNAL;
-    return SPA_OK;
-  }
-  e = hipEventRecord(slot->ev, st);
-  if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("event record: ") + hipGetErrorString(e));
-  slot->wait = WAIT_EVENT;
+  arm_plan(pr, pl.split ? 3u : 1u);
   return SPA_OK;
 }
 
@@ -950,121 +802,69 @@ int32_t check_no_overlap(std::vector<Range> v) {
 
 extern "C" {
 
-int32_t spa_profile_enable(int32_t kernel_mask) {
-  g_prof_mask.store(kernel_mask & ((1 << PROF_N) - 1));
-  return SPA_OK;
-}
-
-int32_t spa_profile_read(int32_t which, int64_t* count, double* total_ms) {
-  if (which < 0 || which >= PROF_N) return fail(SPA_ERR_INVALID_ARG, "unknown kernel index");
-  std::lock_guard<std::mutex> lock(g_prof_mu);
-  std::vector<ProfPending> keep;
-  for (auto& pp : g_prof_pending) {
-    if (pp.which != which) {
-      keep.push_back(pp);
-      continue;
-    }
-    hipError_t e = hipEventSynchronize(pp.b);
-    float ms = 0.f;
-    if (e == hipSuccess) e = hipEventElapsedTime(&ms, pp.a, pp.b);
-    if (e == hipSuccess && pp.c) {
-      float ms2 = 0.f;
-      e = hipEventSynchronize(pp.c);
-      if (e == hipSuccess) e = hipEventElapsedTime(&ms2, pp.a, pp.c);
-      ms = std::max(ms, ms2);
-    }
-    if (e != hipSuccess) {
-      g_prof_pending.swap(keep);
-      return fail(SPA_ERR_HIP, std::string("profile read: ") + hipGetErrorString(e));
-    }
-    g_prof_count[which] += 1;
-    g_prof_ms[which] += ms;
-    g_prof_free.push_back(pp.a);
-    g_prof_free.push_back(pp.b);
-    if (pp.c) g_prof_free.push_back(pp.c);
-  }
-  g_prof_pending.swap(keep);
-  if (count) *count = g_prof_count[which];
-  if (total_ms) *total_ms = g_prof_ms[which];
-  return SPA_OK;
-}
-
-int32_t spa_profile_reset(void) {
-  std::lock_guard<std::mutex> lock(g_prof_mu);
-  for (auto& pp : g_prof_pending) {
-    (void)hipEventSynchronize(pp.b);
-    if (pp.c) (void)hipEventSynchronize(pp.c);
-    g_prof_free.push_back(pp.a);
-    g_prof_free.push_back(pp.b);
-    if (pp.c) g_prof_free.push_back(pp.c);
-  }
-  g_prof_pending.clear();
-  for (int i = 0; i < PROF_N; ++i) {
-    g_prof_count[i] = 0;
-    g_prof_ms[i] = 0;
-  }
-  return SPA_OK;
-}
-
 int32_t spa_abi_version(void) { return SPA_ABI_VERSION; }
 
 const char* spa_last_error(void) { return g_err.c_str(); }
 
-int32_t spa_set_overlap(int32_t enable) {
-  g_overlap.store(enable != 0);
-  return SPA_OK;
-}
-
-int32_t spa_set_split(int32_t verify_chunk_tokens, int32_t draft_chunk_entries) {
-  if (verify_chunk_tokens < 0 || draft_chunk_entries < 0)
-    return fail(SPA_ERR_INVALID_ARG, "split sizes must be >= 0");
-  if (verify_chunk_tokens > VERIFY_MAX_CHUNK || draft_chunk_entries > DRAFT_MAX_CHUNK)
-    return fail(SPA_ERR_INVALID_ARG, "split sizes above 2048");
-  g_verify_chunk.store(verify_chunk_tokens);
-  g_draft_chunk.store(draft_chunk_entries);
-  return SPA_OK;
-}
-
-size_t spa_workspace_bytes(const spa_layout* layout, int32_t B, int32_t spec_k,
-                           const uint8_t* h_is_verify, const int32_t* h_seq_lens,
-                           const int32_t* h_idx_count) {
+namespace {
+// The unified step's plan for a batch: it needs the most workspace and plan
+// bytes of the four attention entry points.
+int32_t size_plan(const spa_layout* layout, int32_t B, int32_t spec_k, const uint8_t* h_is_verify,
+                  const int32_t* h_seq_lens, const int32_t* h_idx_count, const spa_options* opts,
+                  Plan* pl) {
   Shape s;
-  if (check_layout(layout, &s)) return 0;
-  if (B < 0) {
-    fail(SPA_ERR_INVALID_ARG, "B < 0");
-    return 0;
-  }
-  if (B == 0) return 0;
-  if (!h_seq_lens) {
-    fail(SPA_ERR_INVALID_ARG, "h_seq_lens is NULL");
-    return 0;
-  }
+  int32_t rc = check_layout(layout, &s);
+  if (rc) return rc;
+  Opts o;
+  rc = check_opts(opts, &o);
+  if (rc) return rc;
+  if (B < 0) return fail(SPA_ERR_INVALID_ARG, "B < 0");
+  if (B == 0) return SPA_OK;
+  if (!h_seq_lens) return fail(SPA_ERR_INVALID_ARG, "h_seq_lens is NULL");
   bool any_v = false;
   for (int r = 0; r < B && h_is_verify; ++r) any_v |= h_is_verify[r] != 0;
-  if (any_v && spec_k < 1) {
-    fail(SPA_ERR_INVALID_ARG, "spec_k < 1");
-    return 0;
-  }
+  if (any_v && spec_k < 1) return fail(SPA_ERR_INVALID_ARG, "spec_k < 1");
   s.k = std::max(spec_k, 0);
   std::vector<int32_t> counts(B);
   for (int r = 0; r < B; ++r) counts[r] = h_idx_count ? h_idx_count[r] : 1;
   std::vector<Req> rq;
-  if (collect(s, B, h_is_verify, h_seq_lens, nullptr, counts.data(), nullptr, nullptr, false,
-              false, &rq))
-    return 0;
-  // the unified step needs the most: attention plus selection
+  rc = collect(s, B, h_is_verify, h_seq_lens, nullptr, counts.data(), nullptr, nullptr, false,
+               false, &rq);
+  if (rc) return rc;
+  // sizes do not depend on the overlap streams being given
+  o.side = reinterpret_cast<hipStream_t>(1);
+  o.fork = o.join = reinterpret_cast<hipEvent_t>(1);
+  return plan_size(s, rq, true, true, o, pl);
+}
+}  // namespace
+
+size_t spa_workspace_bytes(const spa_layout* layout, int32_t B, int32_t spec_k,
+                           const uint8_t* h_is_verify, const int32_t* h_seq_lens,
+                           const int32_t* h_idx_count, const spa_options* opts) {
   Plan pl;
-  if (plan_size(s, rq, true, true, &pl)) return 0;
-  return pl.total;
+  if (size_plan(layout, B, spec_k, h_is_verify, h_seq_lens, h_idx_count, opts, &pl)) return 0;
+  return B == 0 ? 0 : pl.total;
+}
+
+size_t spa_plan_bytes(const spa_layout* layout, int32_t B, int32_t spec_k,
+                      const uint8_t* h_is_verify, const int32_t* h_seq_lens,
+                      const int32_t* h_idx_count, const spa_options* opts) {
+  Plan pl;
+  if (size_plan(layout, B, spec_k, h_is_verify, h_seq_lens, h_idx_count, opts, &pl)) return 0;
+  return B == 0 ? 0 : PLAN_HEADER + pl.h_bytes;
 }
 
 int32_t spa_verify_attn(const spa_layout* layout, int32_t B, int32_t spec_k,
                         const int32_t* h_seq_lens, const int32_t* d_page_table, const void* d_q,
                         const void* d_k_pool, const void* d_v_pool, void* d_o, float* d_lse,
                         float* d_logits, const int64_t* h_logits_off, void* d_ws,
-                        size_t ws_bytes, void* stream) {
+                        size_t ws_bytes, void* h_plan, size_t plan_bytes,
+                        const spa_options* opts, void* stream) {
   Shape s;
   int32_t rc = check_layout(layout, &s);
+  if (rc) return rc;
+  Opts o;
+  rc = check_opts(opts, &o);
   if (rc) return rc;
   if (B < 0) return fail(SPA_ERR_INVALID_ARG, "B < 0");
   if (spec_k < 1) return fail(SPA_ERR_INVALID_ARG, "spec_k < 1");
@@ -1079,7 +879,7 @@ int32_t spa_verify_attn(const spa_layout* layout, int32_t B, int32_t spec_k,
                &rq);
   if (rc) return rc;
   Plan pl;
-  rc = plan_size(s, rq, true, false, &pl);
+  rc = plan_size(s, rq, true, false, o, &pl);
   if (rc) return rc;
   Buffers b;
   b.page_table = d_page_table;
@@ -1089,18 +889,23 @@ int32_t spa_verify_attn(const spa_layout* layout, int32_t B, int32_t spec_k,
   b.o = d_o;
   b.lse = d_lse;
   b.logits = d_logits;
-  return run(s, rq, pl, b, 1, spec_k, d_ws, ws_bytes, static_cast<hipStream_t>(stream));
+  return run(s, rq, pl, b, 1, spec_k, d_ws, ws_bytes, h_plan, plan_bytes, o,
+             static_cast<hipStream_t>(stream));
 }
 
 int32_t spa_pillar_topk(int32_t B, int32_t spec_k, int32_t num_qo_heads, int32_t num_kv_heads,
                         int32_t avg_row_begin, int32_t avg_row_count, const int32_t* h_seq_lens,
                         const int32_t* h_topk, const float* d_logits,
                         const int64_t* h_logits_off, const float* d_lse, int32_t* d_idx,
-                        const int64_t* h_idx_off, void* d_ws, size_t ws_bytes, void* stream) {
+                        const int64_t* h_idx_off, void* d_ws, size_t ws_bytes, void* h_plan,
+                        size_t plan_bytes, const spa_options* opts, void* stream) {
   if (num_qo_heads <= 0 || num_kv_heads <= 0 || num_qo_heads % num_kv_heads != 0)
     return fail(SPA_ERR_INVALID_ARG, "head counts must be positive with H_q % H_kv == 0");
   if (B < 0) return fail(SPA_ERR_INVALID_ARG, "B < 0");
   if (spec_k < 1) return fail(SPA_ERR_INVALID_ARG, "spec_k < 1");
+  Opts o;
+  int32_t rc = check_opts(opts, &o);
+  if (rc) return rc;
   Shape s;
   s.Hq = num_qo_heads;
   s.Hkv = num_kv_heads;
@@ -1108,7 +913,7 @@ int32_t spa_pillar_topk(int32_t B, int32_t spec_k, int32_t num_qo_heads, int32_t
   s.d = 128;
   s.k = spec_k;
   s.stride = 0x7fffffff;
-  int32_t rc = check_avg_rows(spec_k, s.G, avg_row_begin, avg_row_count);
+  rc = check_avg_rows(spec_k, s.G, avg_row_begin, avg_row_count);
   if (rc) return rc;
   if (B == 0) return SPA_OK;
   if (!h_seq_lens || !h_topk || !d_logits || !h_logits_off || !d_lse || !d_idx || !h_idx_off)
@@ -1119,13 +924,13 @@ int32_t spa_pillar_topk(int32_t B, int32_t spec_k, int32_t num_qo_heads, int32_t
                &rq);
   if (rc) return rc;
   Plan pl;
-  rc = plan_size(s, rq, false, true, &pl);
+  rc = plan_size(s, rq, false, true, o, &pl);
   if (rc) return rc;
   Buffers b;
   b.logits = const_cast<float*>(d_logits);
   b.lse = const_cast<float*>(d_lse);
   b.idx_out = d_idx;
-  return run(s, rq, pl, b, avg_row_begin, avg_row_count, d_ws, ws_bytes,
+  return run(s, rq, pl, b, avg_row_begin, avg_row_count, d_ws, ws_bytes, h_plan, plan_bytes, o,
              static_cast<hipStream_t>(stream));
 }
 
@@ -1133,9 +938,13 @@ int32_t spa_draft_attn(const spa_layout* layout, int32_t B, const int32_t* h_seq
                        const int32_t* d_page_table, const int32_t* h_idx_count,
                        const int64_t* h_idx_off, const int32_t* d_idx, const void* d_q,
                        const void* d_k_pool, const void* d_v_pool, void* d_o, float* d_lse,
-                       void* d_ws, size_t ws_bytes, void* stream) {
+                       void* d_ws, size_t ws_bytes, void* h_plan, size_t plan_bytes,
+                       const spa_options* opts, void* stream) {
   Shape s;
   int32_t rc = check_layout(layout, &s);
+  if (rc) return rc;
+  Opts o;
+  rc = check_opts(opts, &o);
   if (rc) return rc;
   if (B < 0) return fail(SPA_ERR_INVALID_ARG, "B < 0");
   if (B == 0) return SPA_OK;
@@ -1148,7 +957,7 @@ int32_t spa_draft_attn(const spa_layout* layout, int32_t B, const int32_t* h_seq
                &rq);
   if (rc) return rc;
   Plan pl;
-  rc = plan_size(s, rq, true, false, &pl);
+  rc = plan_size(s, rq, true, false, o, &pl);
   if (rc) return rc;
   Buffers b;
   b.page_table = d_page_table;
@@ -1158,7 +967,8 @@ int32_t spa_draft_attn(const spa_layout* layout, int32_t B, const int32_t* h_seq
   b.idx_in = d_idx;
   b.o = d_o;
   b.lse = d_lse;
-  return run(s, rq, pl, b, 0, 1, d_ws, ws_bytes, static_cast<hipStream_t>(stream));
+  return run(s, rq, pl, b, 0, 1, d_ws, ws_bytes, h_plan, plan_bytes, o,
+             static_cast<hipStream_t>(stream));
 }
 
 int32_t spa_unified_step(const spa_layout* layout, int32_t B, int32_t spec_k,
@@ -1168,9 +978,13 @@ int32_t spa_unified_step(const spa_layout* layout, int32_t B, int32_t spec_k,
                          const int32_t* h_idx_count, const int64_t* h_idx_off, int32_t* d_idx,
                          void* d_o, float* d_lse, float* d_logits, const int64_t* h_logits_off,
                          int32_t avg_row_begin, int32_t avg_row_count, void* d_ws,
-                         size_t ws_bytes, void* stream) {
+                         size_t ws_bytes, void* h_plan, size_t plan_bytes,
+                         const spa_options* opts, void* stream) {
   Shape s;
   int32_t rc = check_layout(layout, &s);
+  if (rc) return rc;
+  Opts o;
+  rc = check_opts(opts, &o);
   if (rc) return rc;
   if (B < 0) return fail(SPA_ERR_INVALID_ARG, "B < 0");
   if (spec_k < 1) return fail(SPA_ERR_INVALID_ARG, "spec_k < 1");
@@ -1190,7 +1004,7 @@ int32_t spa_unified_step(const spa_layout* layout, int32_t B, int32_t spec_k,
                any_v, true, &rq);
   if (rc) return rc;
   Plan pl;
-  rc = plan_size(s, rq, true, true, &pl);
+  rc = plan_size(s, rq, true, true, o, &pl);
   if (rc) return rc;
   Buffers b;
   b.page_table = d_page_table;
@@ -1202,15 +1016,23 @@ int32_t spa_unified_step(const spa_layout* layout, int32_t B, int32_t spec_k,
   b.o = d_o;
   b.lse = d_lse;
   b.logits = d_logits;
-  return run(s, rq, pl, b, avg_row_begin, avg_row_count, d_ws, ws_bytes,
+  return run(s, rq, pl, b, avg_row_begin, avg_row_count, d_ws, ws_bytes, h_plan, plan_bytes, o,
              static_cast<hipStream_t>(stream));
+}
+
+size_t spa_recall_plan_bytes(int32_t B) {
+  return B < 0 ? 0 : PLAN_HEADER + (size_t)B * sizeof(RecallReq);
+}
+
+size_t spa_list_quality_plan_bytes(int32_t B) {
+  return B < 0 ? 0 : PLAN_HEADER + (size_t)B * sizeof(QualityReq);
 }
 
 int32_t spa_recall_index(int32_t B, int32_t num_kv_heads, const int32_t* h_seq_lens,
                          int32_t n_sink, int32_t n_recent, const int32_t* h_in_count,
                          const int64_t* h_in_off, const int32_t* d_idx_in,
                          const int32_t* h_out_count, const int64_t* h_out_off, int32_t* d_idx_out,
-                         void* stream) {
+                         void* h_plan, size_t plan_bytes, void* stream) {
   if (B < 0) return fail(SPA_ERR_INVALID_ARG, "B < 0");
   if (num_kv_heads <= 0) return fail(SPA_ERR_INVALID_ARG, "num_kv_heads must be positive");
   if (n_sink < 0 || n_recent < 0) return fail(SPA_ERR_INVALID_ARG, "n_sink and n_recent must be >= 0");
@@ -1251,13 +1073,13 @@ int32_t spa_recall_index(int32_t B, int32_t num_kv_heads, const int32_t* h_seq_l
   if ((int64_t)B * num_kv_heads > 0x7fffffff)
     return fail(SPA_ERR_UNSUPPORTED, "more than 2^31 - 1 (request, KV head) pairs");
   const hipStream_t st = static_cast<hipStream_t>(stream);
-  std::lock_guard<std::mutex> lock(g_ring_mu);
-  Plan pl;
-  pl.h_bytes = (size_t)B * sizeof(RecallReq);
-  PlanSlot* slot = nullptr;
-  rc = acquire_slot(pl, &slot);
+  char* dev_base = nullptr;
+  rc = check_plan(h_plan, plan_bytes, (size_t)B * sizeof(RecallReq), &dev_base);
   if (rc) return rc;
-  RecallReq* rec = reinterpret_cast<RecallReq*>(slot->host);
+  PlanRef pr;
+  rc = acquire_plan(h_plan, dev_base, &pr);
+  if (rc) return rc;
+  RecallReq* rec = reinterpret_cast<RecallReq*>(pr.host);
   for (int r = 0; r < B; ++r) {
     rec[r].L = h_seq_lens[r];
     rec[r].in_count = h_in_count[r];
@@ -1267,21 +1089,17 @@ int32_t spa_recall_index(int32_t B, int32_t num_kv_heads, const int32_t* h_seq_l
     rec[r].out_off = h_out_off[r];
   }
   RecallParams rp;
-  rp.reqs = reinterpret_cast<const RecallReq*>(slot->dev);
+  rp.reqs = reinterpret_cast<const RecallReq*>(pr.dev);
   rp.idx_in = d_idx_in;
   rp.idx_out = d_idx_out;
   rp.Hkv = num_kv_heads;
   rp.n_sink = n_sink;
   rp.n_recent = n_recent;
-  hipError_t e;
-  {
-    ProfScope ps(PROF_RECALL, st);
-    e = launch_recall(rp, B * num_kv_heads, recall_smem_bytes(max_len), st);
-  }
+  hipError_t e = launch_recall(rp, B * num_kv_heads, recall_smem_bytes(max_len), st);
   if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("recall launch: ") + hipGetErrorString(e));
-  e = hipEventRecord(slot->ev, st);
-  if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("event record: ") + hipGetErrorString(e));
-  slot->wait = WAIT_EVENT;
+  e = launch_release(pr.done_dev, pr.seq, st);
+  if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("release launch: ") + hipGetErrorString(e));
+  arm_plan(pr, 1u);
   return SPA_OK;
 }
 
@@ -1299,7 +1117,8 @@ int32_t spa_list_quality(int32_t B, int32_t spec_k, int32_t num_qo_heads, int32_
                          const float* d_logits, const int64_t* h_logits_off, const float* d_lse,
                          const int32_t* h_list_count, const int64_t* h_list_off,
                          const int32_t* d_list, int32_t* d_top, float* d_coverage,
-                         float* d_recall, void* d_ws, size_t ws_bytes, void* stream) {
+                         float* d_recall, void* d_ws, size_t ws_bytes, void* h_plan,
+                         size_t plan_bytes, void* stream) {
   if (B < 0) return fail(SPA_ERR_INVALID_ARG, "B < 0");
   if (num_qo_heads <= 0 || num_kv_heads <= 0 || num_qo_heads % num_kv_heads != 0)
     return fail(SPA_ERR_INVALID_ARG, "head counts must be positive with H_q % H_kv == 0");
@@ -1338,13 +1157,13 @@ int32_t spa_list_quality(int32_t B, int32_t spec_k, int32_t num_qo_heads, int32_
   if ((reinterpret_cast<uintptr_t>(d_ws) & 15) != 0)
     return fail(SPA_ERR_INVALID_ARG, "d_ws must be 16-byte aligned");
   const hipStream_t st = static_cast<hipStream_t>(stream);
-  std::lock_guard<std::mutex> lock(g_ring_mu);
-  Plan pl;
-  pl.h_bytes = (size_t)B * sizeof(QualityReq);
-  PlanSlot* slot = nullptr;
-  rc = acquire_slot(pl, &slot);
+  char* dev_base = nullptr;
+  rc = check_plan(h_plan, plan_bytes, (size_t)B * sizeof(QualityReq), &dev_base);
   if (rc) return rc;
-  QualityReq* rec = reinterpret_cast<QualityReq*>(slot->host);
+  PlanRef pr;
+  rc = acquire_plan(h_plan, dev_base, &pr);
+  if (rc) return rc;
+  QualityReq* rec = reinterpret_cast<QualityReq*>(pr.host);
   int64_t p_off = 0;
   for (int r = 0; r < B; ++r) {
     const int32_t L = h_seq_lens[r];
@@ -1358,7 +1177,7 @@ int32_t spa_list_quality(int32_t B, int32_t spec_k, int32_t num_qo_heads, int32_
     p_off += (int64_t)num_qo_heads * ((L + 3) & ~3);
   }
   QualityParams qp;
-  qp.reqs = reinterpret_cast<const QualityReq*>(slot->dev);
+  qp.reqs = reinterpret_cast<const QualityReq*>(pr.dev);
   qp.logits = d_logits;
   qp.lse = d_lse;
   qp.list = d_list;
@@ -1370,15 +1189,11 @@ int32_t spa_list_quality(int32_t B, int32_t spec_k, int32_t num_qo_heads, int32_
   qp.G = num_qo_heads / num_kv_heads;
   qp.row = row;
   qp.T = top_t;
-  hipError_t e;
-  {
-    ProfScope ps(PROF_QUALITY, st);
-    e = launch_quality(qp, B * num_qo_heads, quality_smem_bytes(max_len), st);
-  }
+  hipError_t e = launch_quality(qp, B * num_qo_heads, quality_smem_bytes(max_len), st);
   if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("quality launch: ") + hipGetErrorString(e));
-  e = hipEventRecord(slot->ev, st);
-  if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("event record: ") + hipGetErrorString(e));
-  slot->wait = WAIT_EVENT;
+  e = launch_release(pr.done_dev, pr.seq, st);
+  if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("release launch: ") + hipGetErrorString(e));
+  arm_plan(pr, 1u);
   return SPA_OK;
 }
 

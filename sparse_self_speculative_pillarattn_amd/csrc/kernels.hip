@@ -165,6 +165,7 @@ __device__ __forceinline__ int vswz(int tau) {
 }
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
@@ -223,10 +224,6 @@ __device__ __forceinline__ void issue_kv_tile(char* stage, const TileSlots<D>& s
     load_lds16(vp + row + 8 * (pc ^ vswz<NCH>(tau)), stage + STAGE + 1024 * j);
   }
 }
-
-// Item counters of the attention launches, one per (plan slot, launch); see
-// attn_loop.
-__device__ uint32_t g_item_ticket[TICKET_SETS];
 
 // Producer side of the per-tile barrier: wait until the awaited tile has
 // landed in LDS, `after` tiles having been issued behind it, then meet the
@@ -350,7 +347,7 @@ __device__ void dma_consumer(const AttnParams& p, const Item& it, char* smem,
   for (int i = 0; i < n_tiles; ++i) {
     __syncthreads();  // tile i ready (and tile i-1 released)
     if (wave == 0 && lane == 0 && i == draw_at)
-      next = atomicInc(&g_item_ticket[p.ticket_set], wrap);
+      next = atomicInc(p.ticket, wrap);
     if (!wave_active) continue;
     const int t0 = jb + i * DMA_TT;
     const char* Ks = smem + (i % DMA_STAGES) * 2 * STAGE;
@@ -374,6 +371,11 @@ __device__ void dma_consumer(const AttnParams& p, const Item& it, char* smem,
     const bool full = !is_list && t0 + DMA_TT <= je && t0 + DMA_TT - 1 <= vis_all;
     float v[2][4];
     float mx = NEG_INF;
+    // V^T operand halves of masked list entries are zeroed before the P V
+    // product: such an entry loads pool row 0 (whatever it holds), and its
+    // exact zero weight would still turn an Inf or NaN there into NaN.
+    // Element 4 t + e of a lane's V^T operand is token 16 t + 4 q + e.
+    u32x4v vkeep = u32x4v{~0u, ~0u, ~0u, ~0u};
     if (full) {
 #pragma unroll
       for (int t = 0; t < 2; ++t)
@@ -404,6 +406,8 @@ __device__ void dma_consumer(const AttnParams& p, const Item& it, char* smem,
           ok[t][1] = sv.y >= 0;
           ok[t][2] = sv.z >= 0;
           ok[t][3] = sv.w >= 0;
+          vkeep[2 * t] = (ok[t][0] ? 0x0000ffffu : 0u) | (ok[t][1] ? 0xffff0000u : 0u);
+          vkeep[2 * t + 1] = (ok[t][2] ? 0x0000ffffu : 0u) | (ok[t][3] ? 0xffff0000u : 0u);
         }
       } else {
 #pragma unroll
@@ -470,9 +474,11 @@ __device__ void dma_consumer(const AttnParams& p, const Item& it, char* smem,
           (lds_v4i16*)(Vs + vrow0 * NCH * 16 + 16 * (c ^ vswz<NCH>(vrow0)) + 8 * (vcol & 1)));
       const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (lds_v4i16*)(Vs + vrow1 * NCH * 16 + 16 * (c ^ vswz<NCH>(vrow1)) + 8 * (vcol & 1)));
-      const bf16x8 va = __builtin_bit_cast(
-          bf16x8, (short __attribute__((ext_vector_type(8)))){lo[0], lo[1], lo[2], lo[3], hi[0],
+      u32x4v vw = __builtin_bit_cast(
+          u32x4v, (short __attribute__((ext_vector_type(8)))){lo[0], lo[1], lo[2], lo[3], hi[0],
                                                               hi[1], hi[2], hi[3]});
+      if (is_list) vw &= vkeep;
+      const bf16x8 va = __builtin_bit_cast(bf16x8, vw);
       oacc[dd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, oacc[dd], 0, 0, 0);
     }
   }
@@ -787,7 +793,7 @@ template <int D, typename T, int GM>
 __device__ __forceinline__ void attn_loop(const AttnParams& p, char* smem) {
   __shared__ int s_item[2];
   const uint32_t wrap = (uint32_t)p.n_items + gridDim.x - 1u;
-  if (threadIdx.x == 0) s_item[0] = (int)atomicInc(&g_item_ticket[p.ticket_set], wrap);
+  if (threadIdx.x == 0) s_item[0] = (int)atomicInc(p.ticket, wrap);
   __syncthreads();
   for (int k = 0;; k ^= 1) {
     const int item = s_item[k];
@@ -815,7 +821,7 @@ __device__ __forceinline__ void attn_loop(const AttnParams& p, char* smem) {
     }
     const bool drew = attn_body<D, T, GM>(p, item, smem, &s_item[k ^ 1], wrap);
     if (!drew && threadIdx.x == 0)
-      s_item[k ^ 1] = (int)atomicInc(&g_item_ticket[p.ticket_set], wrap);
+      s_item[k ^ 1] = (int)atomicInc(p.ticket, wrap);
     __syncthreads();  // LDS is free and the next draw is visible
   }
 }
@@ -1362,6 +1368,8 @@ __global__ void __launch_bounds__(POST_THREADS) post_kernel(PostParams p) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   if (p.done && blockIdx.x == 0 && threadIdx.x == 0)
     __hip_atomic_store(p.done, p.done_val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  for (int c = blockIdx.x * blockDim.x + threadIdx.x; c < p.plan_n16; c += gridDim.x * blockDim.x)
+    p.plan_dst[c] = p.plan_src[c];
   const PostItem it = p.items[blockIdx.x];
   if (it.kind == POST_NOP) return;
   if (it.kind == POST_MERGE) {
@@ -1538,6 +1546,8 @@ __global__ void __launch_bounds__(SELECT_THREADS) select_kernel(SelectParams sp)
   // dynamic LDS (long rows only): the positions of the final bucket's keys,
   // then the bitmap of a row's selected positions
   extern __shared__ __attribute__((aligned(16))) char dyn[];
+  if (sp.done && blockIdx.x == 0 && threadIdx.x == 0)
+    __hip_atomic_store(sp.done, sp.done_val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
   int32_t* cpos = sp.bm_bits > 0 ? reinterpret_cast<int32_t*>(dyn) : nullptr;
   uint32_t* bm = sp.bm_bits > 0 ? reinterpret_cast<uint32_t*>(dyn + SELECT_FINISH * 4) : nullptr;
   const PostItem it = sp.items[blockIdx.x];
@@ -1821,6 +1831,16 @@ size_t recall_smem_bytes(int max_len) {
 hipError_t launch_recall(const RecallParams& rp, int nblocks, size_t smem, hipStream_t st) {
   if (nblocks == 0) return hipSuccess;
   hipLaunchKernelGGL(recall_kernel, dim3(nblocks), dim3(RECALL_THREADS), smem, st, rp);
+  return hipGetLastError();
+}
+
+// Releases a plan buffer once the launch before it on the stream has ended.
+__global__ void __launch_bounds__(64) release_kernel(uint64_t* done, uint64_t val) {
+  if (threadIdx.x == 0) __hip_atomic_store(done, val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
+hipError_t launch_release(uint64_t* done, uint64_t val, hipStream_t st) {
+  hipLaunchKernelGGL(release_kernel, dim3(1), dim3(64), 0, st, done, val);
   return hipGetLastError();
 }
 

@@ -23,7 +23,7 @@ struct AttnParams {
   float* part_ml;
   int32_t Hq, Hkv, G, k;
   float sm_scale;
-  int32_t ticket_set;  // item counter of this launch, in [0, TICKET_SETS)
+  uint32_t* ticket;    // item counter of this launch (workspace; zero before, zero after)
   int32_t n_items;     // records at items; set by launch_attn
   // The post-pass and selection records of the call, copied by this launch
   // from the pinned plan into the workspace (plan_n16 16-byte pieces; 0 = no
@@ -36,14 +36,15 @@ struct AttnParams {
   uint4* zero_dst;
   int32_t zero_n16;
   // When set (only when plan_n16 is 0), the workgroup that draws the last
-  // ticket stores done_val there (mapped host memory): every workgroup has
-  // then read its last plan record, so the host may reuse the plan buffer.
+  // ticket stores done_val there (the plan buffer's header, pinned host
+  // memory): every workgroup has then read its last plan record, so the host
+  // may reuse the plan buffer.
   uint64_t* done;
   uint64_t done_val;
 };
 
 struct PostParams {
-  const PostItem* items;  // pinned host plan, read in place
+  const PostItem* items;  // pinned host plan read in place, or its workspace copy
   const void* part_o;  // split-K partial outputs (see AttnParams)
   const float* part_ml;
   void* o;
@@ -55,11 +56,18 @@ struct PostParams {
   // Selected rows' score histograms (zeroed by the attention launch), added
   // to by the averaging items of rows with hist_slot >= 0; null: none kept.
   uint32_t* hist;
-  // When set, the launch stores done_val there (mapped host memory) as it
-  // starts: the attention launch before it, the last reader of the call's
+  // When set, the launch stores done_val there (the plan buffer's header) as
+  // it starts: the attention launch before it, the last reader of the call's
   // pinned plan, has then finished, so the host may reuse the plan buffer.
   uint64_t* done;
   uint64_t done_val;
+  // A call without an attention launch (top-K alone): the post-pass reads its
+  // own records from the pinned plan and copies the selection's records
+  // (plan_n16 16-byte pieces) into the workspace, where the selection launch
+  // reads them; 0 = no copy.
+  const uint4* plan_src;
+  uint4* plan_dst;
+  int32_t plan_n16;
 };
 
 struct SelectParams {
@@ -68,6 +76,10 @@ struct SelectParams {
   int32_t* idx_out;
   const uint32_t* hist;   // [slots][HIST_BINS] counts of the selected rows, or null
   int bm_bits;            // LDS position bitmap of long rows (select_bitmap_bits), 0 for none
+  // When set, the launch stores done_val there as it starts (the post-pass
+  // before it was the call's last reader of the pinned plan).
+  uint64_t* done;
+  uint64_t done_val;
 };
 
 struct RecallParams {
@@ -106,5 +118,8 @@ size_t recall_smem_bytes(int max_len);
 size_t quality_smem_bytes(int max_len);
 hipError_t launch_quality(const QualityParams& qp, int nblocks, size_t smem, hipStream_t st);
 hipError_t launch_recall(const RecallParams& rp, int nblocks, size_t smem, hipStream_t st);
+// One thread stores val at done (the plan buffer's header), after the work
+// queued before it on `st`.
+hipError_t launch_release(uint64_t* done, uint64_t val, hipStream_t st);
 
 }  // namespace spa

@@ -84,7 +84,23 @@ struct QualityReq {
   int32_t pad_;
 };
 
-constexpr int TICKET_SETS = 32;        // attention item counters: (plan slot, launch) pairs
+// First bytes of a caller's plan buffer: the release protocol (api.cpp).  The
+// device stores a call's sequence number into done[] once it no longer reads
+// the records that follow the header.
+struct PlanHeader {
+  uint64_t magic;   // PLAN_MAGIC once a call has used the buffer
+  uint64_t issued;  // sequence number of the last call that wrote the buffer
+  int32_t device;   // device of that call
+  int32_t drain;    // 1: that call failed after writing; drain `device` before reuse
+  uint32_t need;    // done[] words that call armed (bit b: done[b])
+  uint32_t pad_[9];
+  uint64_t done[2]; // written by the device: [0] main release, [1] draft launch of an overlapped step
+  uint64_t pad2_[22];
+};
+static_assert(sizeof(PlanHeader) == 256, "plan header is 256 bytes");
+constexpr uint64_t PLAN_MAGIC = 0x53504150'4c414e32ull;
+constexpr size_t PLAN_HEADER = sizeof(PlanHeader);
+constexpr size_t WS_COUNTERS = 256;    // work counters at the start of a workspace
 constexpr int AVG_SPAN = 1024;         // positions per averaging item
 constexpr int VERIFY_MAX_CHUNK = 2048;
 constexpr int DRAFT_MAX_CHUNK = 2048;

@@ -266,19 +266,11 @@ def make_batch(w: Workload, device="cpu", seed: Optional[int] = None,
         pt[r, :lens[r]] = perm[off:off + lens[r]]
         off += lens[r]
 
-    # Q, K, V
-    q = torch.randn((rows, Hq, d), generator=dg, device=dev, dtype=torch.float32).to(dt)
-    k_pool = torch.empty((nslots, Hkv, d), device=dev, dtype=dt)
-    v_pool = torch.empty((nslots, Hkv, d), device=dev, dtype=dt)
-    for s0 in range(0, nslots, chunk_slots):
-        s1 = min(nslots, s0 + chunk_slots)
-        k_pool[s0:s1] = torch.randn((s1 - s0, Hkv, d), generator=dg, device=dev,
-                                    dtype=torch.float32).to(dt)
-        v_pool[s0:s1] = torch.randn((s1 - s0, Hkv, d), generator=dg, device=dev,
-                                    dtype=torch.float32).to(dt)
-
-    # pillars: per (r, g) positions and a shared direction toward the queries
-    pt_dev = pt.to(dev)
+    # Host draws first (pillar positions, then the draft lists), so that the
+    # bulk device generation below is the last work of the setup: the GPU is
+    # still busy with it when the caller's first steps are queued, instead of
+    # idling through the host work (after an idle period the GPU's clocks take
+    # about 10 ms of load to settle again).
     pillar_pos = []
     for r in range(B):
         L = lens[r]
@@ -286,14 +278,6 @@ def make_batch(w: Workload, device="cpu", seed: Optional[int] = None,
         pos = torch.stack([torch.randperm(L, generator=hg)[:npil] for _ in range(Hkv)])
         pos, _ = pos.sort(dim=1)
         pillar_pos.append(pos)
-        qr = q[q_indptr[r]:q_indptr[r + 1]].float()                    # [rows_r][Hq][d]
-        qbar = qr.reshape(-1, Hkv, G, d).mean(dim=(0, 2))               # [Hkv][d]
-        u = qbar / qbar.norm(dim=1, keepdim=True).clamp_min(1e-30)
-        slots = pt_dev[r].long()[pos.to(dev)]                          # [Hkv][npil]
-        for g in range(Hkv):
-            sl = slots[g]
-            z = k_pool[sl, g].float()
-            k_pool[sl, g] = (z + 3.0 * math.sqrt(d) * u[g]).to(dt)
 
     # index lists: verify requests will write K_r entries, drafts read theirs
     idx_count, idx_off = meta.idx_count, meta.idx_off
@@ -316,10 +300,51 @@ def make_batch(w: Workload, device="cpu", seed: Optional[int] = None,
             lst, _ = torch.cat([pil, fill]).sort()
             idx[idx_off[r] + g * kr: idx_off[r] + (g + 1) * kr] = lst.to(torch.int32)
 
+    # every pillar key as (request, KV head, slot): slots are distinct within a
+    # request (a permutation) and across requests, so the planting below
+    # writes each (slot, head) once
+    pil_r, pil_g, pil_s = [], [], []
+    for r in range(B):
+        pos = pillar_pos[r]
+        pil_r.append(torch.full((pos.numel(),), r, dtype=torch.int64))
+        pil_g.append(torch.arange(Hkv, dtype=torch.int64).repeat_interleave(pos.shape[1]))
+        pil_s.append(pt[r].long()[pos.reshape(-1)])
+
+    # host-to-device copies of what the device work below needs, queued before
+    # it (a copy from pageable memory waits for the work queued ahead of it)
+    pt_dev, idx_dev = pt.to(dev), idx.to(dev)
+    per_row = torch.repeat_interleave(
+        torch.arange(B), torch.tensor([q_indptr[r + 1] - q_indptr[r] for r in range(B)],
+                                      dtype=torch.int64)).to(dev)
+    nrow = torch.tensor([(q_indptr[r + 1] - q_indptr[r]) * G for r in range(B)],
+                        dtype=torch.float32).to(dev)
+    rr, gg, ss = (torch.cat(t).to(dev) if B else None for t in (pil_r, pil_g, pil_s))
+
+    # Q, K, V
+    q = torch.randn((rows, Hq, d), generator=dg, device=dev, dtype=torch.float32).to(dt)
+    k_pool = torch.empty((nslots, Hkv, d), device=dev, dtype=dt)
+    v_pool = torch.empty((nslots, Hkv, d), device=dev, dtype=dt)
+    for s0 in range(0, nslots, chunk_slots):
+        s1 = min(nslots, s0 + chunk_slots)
+        k_pool[s0:s1] = torch.randn((s1 - s0, Hkv, d), generator=dg, device=dev,
+                                    dtype=torch.float32).to(dt)
+        v_pool[s0:s1] = torch.randn((s1 - s0, Hkv, d), generator=dg, device=dev,
+                                    dtype=torch.float32).to(dt)
+
+    # pillars: each key gets 3 sqrt(d) u added, u the unit mean of the
+    # request's query rows over the G heads of the key's KV head
+    if B > 0:
+        qsum = torch.zeros((B, Hkv, d), device=dev, dtype=torch.float32)
+        qsum.index_add_(0, per_row, q.float().reshape(rows, Hkv, G, d).sum(dim=2))
+        qbar = qsum / nrow[:, None, None]
+        u = qbar / qbar.norm(dim=2, keepdim=True).clamp_min(1e-30)       # [B][Hkv][d]
+        z = k_pool[ss, gg].float()
+        k_pool[ss, gg] = (z + 3.0 * math.sqrt(d) * u[rr, gg]).to(dt)
+
     return Batch(w=w, B=B, seq_lens=lens, is_verify=ver, q_indptr=q_indptr,
                  idx_count=idx_count, idx_off=idx_off, logits_off=meta.logits_off,
                  pillar_pos=pillar_pos, q=q, k_pool=k_pool, v_pool=v_pool,
-                 page_table=pt.to(dev), idx=idx.to(dev), num_slots=nslots, stride=stride,
+                 page_table=pt_dev, idx=idx_dev, num_slots=nslots, stride=stride,
                  logits_elems=meta.logits_elems, idx_elems=meta.idx_elems)
 
 

@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert lib.spa_abi_version() == 1
+    assert lib.spa_abi_version() == bd.ABI_VERSION == 2
 
 
 def _lay(**kw):
@@ -52,7 +52,8 @@ def _arr(a, dt):
 
 
 def _unified(lib, lay, B=2, k=4, ver=(1, 0), lens=(100, 50), indptr=(0, 5, 6), counts=(5, 3),
-             ioff=(0, 10), loff=(0, 0), ws_bytes=1 << 30, avg=(1, 4), null=()):
+             ioff=(0, 10), loff=(0, 0), ws_bytes=1 << 30, avg=(1, 4), null=(), plan=FAKE,
+             plan_bytes=1 << 30, opts=None):
     ver_a, ver_p = _arr(ver, np.uint8)
     len_a, len_p = _arr(lens, np.int32)
     ind_a, ind_p = _arr(indptr, np.int32)
@@ -61,13 +62,14 @@ def _unified(lib, lay, B=2, k=4, ver=(1, 0), lens=(100, 50), indptr=(0, 5, 6), c
     lo_a, lo_p = _arr(loff, np.int64)
     args = dict(ver=ver_p, lens=len_p, indptr=ind_p, pt=FAKE, q=FAKE, kp=FAKE, vp=FAKE,
                 cnt=cnt_p, ioff=io_p, idx=FAKE, o=FAKE, lse=FAKE, logits=FAKE, loff=lo_p,
-                ws=FAKE)
+                ws=FAKE, plan=plan)
     for n in null:
         args[n] = None
     return lib.spa_unified_step(C.byref(lay), B, k, args["ver"], args["lens"], args["indptr"],
                                 args["pt"], args["q"], args["kp"], args["vp"], args["cnt"],
                                 args["ioff"], args["idx"], args["o"], args["lse"], args["logits"],
-                                args["loff"], avg[0], avg[1], args["ws"], ws_bytes, None)
+                                args["loff"], avg[0], avg[1], args["ws"], ws_bytes, args["plan"],
+                                plan_bytes, None if opts is None else C.byref(opts), None)
 
 
 def test_valid_arguments_reach_workspace_check(lib):
@@ -105,6 +107,13 @@ def test_empty_batch_is_a_noop(lib):
     (dict(null=("q",)), bd.SPA_ERR_INVALID_ARG),
     (dict(null=("ws",), ws_bytes=1 << 30), bd.SPA_ERR_INVALID_ARG),
     (dict(null=("logits",)), bd.SPA_ERR_INVALID_ARG),
+    (dict(null=("plan",)), bd.SPA_ERR_INVALID_ARG),
+    (dict(plan=C.c_void_p(0x1010)), bd.SPA_ERR_INVALID_ARG),  # plan buffer not 64-byte aligned
+    (dict(plan_bytes=256), bd.SPA_ERR_PLAN_TOO_SMALL),
+    (dict(opts=bd.SpaOptions(verify_chunk=-1)), bd.SPA_ERR_INVALID_ARG),
+    (dict(opts=bd.SpaOptions(draft_chunk=2049)), bd.SPA_ERR_INVALID_ARG),
+    (dict(opts=bd.SpaOptions(num_cus=-4)), bd.SPA_ERR_INVALID_ARG),
+    (dict(opts=bd.SpaOptions(overlap=1)), bd.SPA_ERR_INVALID_ARG),  # no side stream or events
     (dict(lay=dict(num_qo_heads=192, num_kv_heads=8), ioff=(0, 100)),
      bd.SPA_ERR_UNSUPPORTED),  # (k+1) G = 120 rows exceed the 112-row MFMA budget
 ])
@@ -121,15 +130,39 @@ def test_two_verifies_need_disjoint_logits(lib):
     assert b"logits" in lib.spa_last_error()
 
 
+def _sizes(lib, lay, B, k, ver, lens, cnt, opts=None):
+    v, l, c = (np.ascontiguousarray(np.asarray(a, t)) for a, t in
+               ((ver, np.uint8), (lens, np.int32), (cnt, np.int32)))
+    args = (C.byref(lay), B, k, v.ctypes.data_as(C.c_void_p), l.ctypes.data_as(C.c_void_p),
+            c.ctypes.data_as(C.c_void_p), None if opts is None else C.byref(opts))
+    return lib.spa_workspace_bytes(*args), lib.spa_plan_bytes(*args)
+
+
 def test_workspace_bytes_matches_call_requirement(lib):
     lay = _lay()
-    ver = np.array([1, 0], np.uint8)
-    lens = np.array([100, 50], np.int32)
-    cnt = np.array([5, 3], np.int32)
-    need = lib.spa_workspace_bytes(C.byref(lay), 2, 4, ver.ctypes.data_as(C.c_void_p),
-                                   lens.ctypes.data_as(C.c_void_p), cnt.ctypes.data_as(C.c_void_p))
-    assert need > 0
+    need, plan = _sizes(lib, lay, 2, 4, [1, 0], [100, 50], [5, 3])
+    assert need > 256 and plan > 256
     assert _unified(lib, lay, ws_bytes=need - 1) == bd.SPA_ERR_WORKSPACE_TOO_SMALL
+    assert _unified(lib, lay, ws_bytes=need, plan_bytes=plan - 1) == bd.SPA_ERR_PLAN_TOO_SMALL
+
+
+def test_sizes_are_pure_functions_of_their_arguments(lib):
+    """Workspace and plan sizes depend on the batch and the options only: the
+    same arguments give the same sizes, the CU count the automatic verify
+    chunk plans for is an option, and invalid options give 0."""
+    lay = _lay(page_table_stride=8192)
+    args = (2, 4, [1, 1], [8000, 6000], [400, 300])
+    first = _sizes(lib, lay, *args)
+    assert first == _sizes(lib, lay, *args) == _sizes(lib, lay, *args, opts=bd.SpaOptions())
+    # 14000 positions x 2 KV heads on 256 CUs: a light load, 512-position
+    # chunks; planned for 4 CUs, 2048-position chunks and far fewer partials
+    few = _sizes(lib, lay, *args, opts=bd.SpaOptions(num_cus=4))
+    assert few[0] < first[0] and few[1] < first[1]
+    assert _sizes(lib, lay, *args, opts=bd.SpaOptions(num_cus=256)) == first
+    # an explicit chunk is used as given
+    assert _sizes(lib, lay, *args, opts=bd.SpaOptions(verify_chunk=2048)) == few
+    assert _sizes(lib, lay, *args, opts=bd.SpaOptions(verify_chunk=4096)) == (0, 0)
+    assert b"verify_chunk" in lib.spa_last_error()
 
 
 def test_workspace_holds_a_histogram_per_selected_row(lib):
@@ -141,10 +174,7 @@ def test_workspace_holds_a_histogram_per_selected_row(lib):
     cnt = np.array([5, 5], np.int32)
 
     def need(ver):
-        v = np.array(ver, np.uint8)
-        return lib.spa_workspace_bytes(C.byref(lay), 2, 4, v.ctypes.data_as(C.c_void_p),
-                                       lens.ctypes.data_as(C.c_void_p),
-                                       cnt.ctypes.data_as(C.c_void_p))
+        return _sizes(lib, lay, 2, 4, ver, lens, cnt)[0]
     assert need([1, 1]) - need([1, 0]) >= lay.num_kv_heads * 2048 * 4
 
 
@@ -157,63 +187,62 @@ def test_light_verify_load_with_a_very_long_request_is_planned(lib):
         ver = np.array([1], np.uint8)
         lens = np.array([L], np.int32)
         cnt = np.array([L // 20], np.int32)
-        need = lib.spa_workspace_bytes(C.byref(lay), 1, 4, ver.ctypes.data_as(C.c_void_p),
-                                       lens.ctypes.data_as(C.c_void_p),
-                                       cnt.ctypes.data_as(C.c_void_p))
+        need = _sizes(lib, lay, 1, 4, ver, lens, cnt)[0]
         assert need > 0, (L, lib.spa_last_error())
 
 
-def test_set_split_bounds(lib):
-    assert lib.spa_set_split(-1, 0) == bd.SPA_ERR_INVALID_ARG
-    assert lib.spa_set_split(4096, 0) == bd.SPA_ERR_INVALID_ARG
-    assert lib.spa_set_split(0, 0) == bd.SPA_OK
+def test_unpinned_plan_buffer_is_rejected(lib):
+    """A plan buffer the device cannot read (ordinary host memory) is refused
+    before anything is enqueued."""
+    buf = np.zeros(1 << 16, np.uint8)
+    addr = (buf.ctypes.data + 63) // 64 * 64
+    rc = _unified(lib, _lay(), plan=C.c_void_p(addr), plan_bytes=(1 << 16) - 64)
+    assert rc == bd.SPA_ERR_INVALID_ARG
+    assert b"pinned" in lib.spa_last_error()
+    assert not buf.any(), "the rejected buffer was written"
 
 
-@pytest.fixture
-def small_split(lib):
-    """Work chunks of 512 positions / 256 list entries for the test's duration."""
-    assert lib.spa_set_split(512, 256) == bd.SPA_OK
-    yield
-    assert lib.spa_set_split(0, 0) == bd.SPA_OK
-
-
-def test_other_entry_points_validate(lib, small_split):
+def test_other_entry_points_validate(lib):
+    # work chunks of 512 positions / 256 list entries
+    opts = C.byref(bd.SpaOptions(verify_chunk=512, draft_chunk=256))
+    P, PB = FAKE, 1 << 30
     lay = _lay(page_table_stride=2048)
     # lengths above one work chunk, so that every call below needs workspace
     lens, lp = _arr([1000, 800], np.int32)
     lo, lop = _arr([0, 5 * 8 * 1000], np.int64)
     # verify-only: k+1 rows per request, L >= k+1
     assert lib.spa_verify_attn(C.byref(lay), 2, 0, lp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
-                               lop, FAKE, 0, None) == bd.SPA_ERR_INVALID_ARG
+                               lop, FAKE, 0, P, PB, opts, None) == bd.SPA_ERR_INVALID_ARG
     assert lib.spa_verify_attn(C.byref(lay), 2, 4, lp, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
-                               lop, FAKE, 0, None) == bd.SPA_ERR_WORKSPACE_TOO_SMALL
+                               lop, FAKE, 0, P, PB, opts, None) == bd.SPA_ERR_WORKSPACE_TOO_SMALL
     # top-K: K within [1, L], rows within [0, k]
     kk, kp = _arr([5, 801], np.int32)
     io, iop = _arr([0, 4000], np.int64)
     assert lib.spa_pillar_topk(2, 4, 8, 2, 1, 4, lp, kp, FAKE, lop, FAKE, FAKE, iop, FAKE, 0,
-                               None) == bd.SPA_ERR_INVALID_ARG
+                               P, PB, opts, None) == bd.SPA_ERR_INVALID_ARG
     kk, kp = _arr([5, 8], np.int32)
     assert lib.spa_pillar_topk(2, 4, 8, 2, 1, 5, lp, kp, FAKE, lop, FAKE, FAKE, iop, FAKE, 0,
-                               None) == bd.SPA_ERR_INVALID_ARG
+                               P, PB, opts, None) == bd.SPA_ERR_INVALID_ARG
     assert lib.spa_pillar_topk(2, 4, 8, 3, 1, 4, lp, kp, FAKE, lop, FAKE, FAKE, iop, FAKE, 0,
-                               None) == bd.SPA_ERR_INVALID_ARG
+                               P, PB, opts, None) == bd.SPA_ERR_INVALID_ARG
     assert lib.spa_pillar_topk(2, 4, 8, 2, 1, 4, lp, kp, FAKE, lop, FAKE, FAKE, iop, FAKE, 0,
-                               None) == bd.SPA_ERR_WORKSPACE_TOO_SMALL
+                               P, PB, opts, None) == bd.SPA_ERR_WORKSPACE_TOO_SMALL
     # draft-only: non-empty lists, disjoint segments
     cnt, cp = _arr([4, 0], np.int32)
     assert lib.spa_draft_attn(C.byref(lay), 2, lp, FAKE, cp, iop, FAKE, FAKE, FAKE, FAKE, FAKE,
-                              FAKE, FAKE, 0, None) == bd.SPA_ERR_INVALID_ARG
+                              FAKE, FAKE, 0, P, PB, opts, None) == bd.SPA_ERR_INVALID_ARG
     cnt, cp = _arr([1500, 4], np.int32)
     io, iop = _arr([0, 4000], np.int64)
     assert lib.spa_draft_attn(C.byref(lay), 2, lp, FAKE, cp, iop, FAKE, FAKE, FAKE, FAKE, FAKE,
-                              FAKE, FAKE, 0, None) == bd.SPA_ERR_WORKSPACE_TOO_SMALL
+                              FAKE, FAKE, 0, P, PB, opts, None) == bd.SPA_ERR_WORKSPACE_TOO_SMALL
 
 
 # --------------------------------------------------------------------------- #
 # spa_recall_index argument checks
 # --------------------------------------------------------------------------- #
 def _recall(lib, B=2, Hkv=2, lens=(100, 50), S=4, W=8, inc=(10, 5), inoff=(0, 100),
-            outc=None, outoff=(1000, 2000), in_ptr=0x10000, out_ptr=0x10000, null=()):
+            outc=None, outoff=(1000, 2000), in_ptr=0x10000, out_ptr=0x10000, null=(),
+            plan_bytes=1 << 20):
     if outc is None:
         outc = [bd.recall_length(L, n, S, W) for L, n in zip(lens, inc)]
     len_a, len_p = _arr(lens, np.int32)
@@ -222,12 +251,12 @@ def _recall(lib, B=2, Hkv=2, lens=(100, 50), S=4, W=8, inc=(10, 5), inoff=(0, 10
     outc_a, outc_p = _arr(outc, np.int32)
     outo_a, outo_p = _arr(outoff, np.int64)
     args = dict(lens=len_p, inc=inc_p, inoff=ino_p, idx_in=C.c_void_p(in_ptr), outc=outc_p,
-                outoff=outo_p, idx_out=C.c_void_p(out_ptr))
+                outoff=outo_p, idx_out=C.c_void_p(out_ptr), plan=FAKE)
     for n in null:
         args[n] = None
     return lib.spa_recall_index(B, Hkv, args["lens"], S, W, args["inc"], args["inoff"],
                                 args["idx_in"], args["outc"], args["outoff"], args["idx_out"],
-                                None)
+                                args["plan"], plan_bytes, None)
 
 
 def test_recall_length_formula():
@@ -253,6 +282,8 @@ def test_recall_length_formula():
     (dict(null=("idx_in",)), bd.SPA_ERR_INVALID_ARG),
     (dict(null=("outc",)), bd.SPA_ERR_INVALID_ARG),
     (dict(null=("idx_out",)), bd.SPA_ERR_INVALID_ARG),
+    (dict(null=("plan",)), bd.SPA_ERR_INVALID_ARG),
+    (dict(plan_bytes=256 + 32), bd.SPA_ERR_PLAN_TOO_SMALL),   # two 32-byte records
 ])
 def test_recall_invalid_arguments(lib, kw, code):
     assert _recall(lib, **kw) == code
@@ -267,23 +298,30 @@ def test_recall_empty_batch_is_a_noop(lib):
 # spa_list_quality argument checks
 # --------------------------------------------------------------------------- #
 def _quality(lib, B=2, k=1, Hq=8, Hkv=2, row=1, T=10, lens=(100, 50), loff=(0, 1600),
-             cnt=(5, 3), coff=(0, 10), ws_bytes=1 << 30, ws=0x10000, null=()):
+             cnt=(5, 3), coff=(0, 10), ws_bytes=1 << 30, ws=0x10000, null=(), plan_bytes=1 << 20):
     len_a, len_p = _arr(lens, np.int32)
     lo_a, lo_p = _arr(loff, np.int64)
     c_a, c_p = _arr(cnt, np.int32)
     co_a, co_p = _arr(coff, np.int64)
     args = dict(lens=len_p, logits=FAKE, loff=lo_p, lse=FAKE, cnt=c_p, coff=co_p, lst=FAKE,
-                top=FAKE, cov=FAKE, rec=FAKE, ws=C.c_void_p(ws))
+                top=FAKE, cov=FAKE, rec=FAKE, ws=C.c_void_p(ws), plan=FAKE)
     for n in null:
         args[n] = None
     return lib.spa_list_quality(B, k, Hq, Hkv, row, T, args["lens"], args["logits"], args["loff"],
                                 args["lse"], args["cnt"], args["coff"], args["lst"], args["top"],
-                                args["cov"], args["rec"], args["ws"], ws_bytes, None)
+                                args["cov"], args["rec"], args["ws"], ws_bytes, args["plan"],
+                                plan_bytes, None)
 
 
 def test_list_quality_workspace_formula(lib):
     assert bd.list_quality_workspace_bytes(2, 8, [100, 50]) == 8 * 4 * (100 + 52)
     assert bd.list_quality_workspace_bytes(0, 8, [100]) == 0
+
+
+def test_plan_bytes_of_recall_and_quality(lib):
+    assert lib.spa_recall_plan_bytes(3) == 256 + 3 * 32
+    assert lib.spa_list_quality_plan_bytes(3) == 256 + 3 * 40
+    assert lib.spa_recall_plan_bytes(-1) == 0 and lib.spa_list_quality_plan_bytes(-1) == 0
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -303,6 +341,8 @@ def test_list_quality_workspace_formula(lib):
     (dict(ws=0x10004), bd.SPA_ERR_INVALID_ARG),               # workspace not 16-byte aligned
     (dict(null=("lst",)), bd.SPA_ERR_INVALID_ARG),
     (dict(null=("top",)), bd.SPA_ERR_INVALID_ARG),
+    (dict(null=("plan",)), bd.SPA_ERR_INVALID_ARG),
+    (dict(plan_bytes=256 + 40), bd.SPA_ERR_PLAN_TOO_SMALL),   # two 40-byte records
 ])
 def test_list_quality_invalid_arguments(lib, kw, code):
     assert _quality(lib, **kw) == code

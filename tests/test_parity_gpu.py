@@ -20,15 +20,8 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
 
-@pytest.fixture(autouse=True)
-def _default_split():
-    bd.set_split(0, 0)
-    yield
-    bd.set_split(0, 0)
-
-
-def run_unified(b, avg_row_begin=1, avg_row_count=None):
-    bufs = bd.StepBuffers(b, avg_row_begin, avg_row_count)
+def run_unified(b, avg_row_begin=1, avg_row_count=None, opts=None):
+    bufs = bd.StepBuffers(b, avg_row_begin, avg_row_count, opts=opts)
     bufs.logits.fill_(float("nan"))
     bufs.o.fill_(float("nan"))
     bufs.lse.fill_(float("nan"))
@@ -37,11 +30,11 @@ def run_unified(b, avg_row_begin=1, avg_row_count=None):
     return {"o": bufs.o, "lse": bufs.lse, "logits": bufs.logits, "idx": bufs.idx}
 
 
-def check(oracle, w, seed=0, avg_row_begin=1, avg_row_count=None, **kw):
+def check(oracle, w, seed=0, avg_row_begin=1, avg_row_count=None, opts=None, **kw):
     b = synth.make_batch(w, seed=seed, **kw)
     print(f"[case] {w.name} seed={seed} lens={b.seq_lens} verify={b.is_verify}", flush=True)
     ref = oracle.step(**parity.oracle_inputs(b, avg_row_begin, avg_row_count))
-    gpu = run_unified(b.to(DEV), avg_row_begin, avg_row_count)
+    gpu = run_unified(b.to(DEV), avg_row_begin, avg_row_count, opts)
     parity.compare_step(oracle, b, gpu, ref, avg_row_begin, avg_row_count)
     return b, gpu, ref
 
@@ -98,23 +91,18 @@ def test_ragged_lengths(oracle, L):
 def test_overlap_switch(oracle, overlap):
     """The unified step with the draft attention on the side stream and in one
     launch with the verify attention: same results."""
-    bd.set_overlap(overlap)
-    try:
-        w = synth.Workload(name=f"ovl{int(overlap)}", batch=9, num_qo_heads=32, num_kv_heads=8,
-                           head_dim=128, dtype="bf16", spec_k=8, sparsity=Fraction(1, 4),
-                           lengths=("uniform", 300, 5000), n_verify=3, seed=41)
-        check(oracle, w)
-    finally:
-        bd.set_overlap(False)
+    w = synth.Workload(name=f"ovl{int(overlap)}", batch=9, num_qo_heads=32, num_kv_heads=8,
+                       head_dim=128, dtype="bf16", spec_k=8, sparsity=Fraction(1, 4),
+                       lengths=("uniform", 300, 5000), n_verify=3, seed=41)
+    check(oracle, w, opts=bd.Options(overlap=overlap))
 
 
 @pytest.mark.parametrize("split", [(64, 16), (2048, 2048), (320, 100), (40, 7)])
 def test_split_invariance(oracle, split):
-    bd.set_split(*split)
     w = synth.Workload(name="split", batch=6, num_qo_heads=32, num_kv_heads=8, head_dim=128,
                        dtype="bf16", spec_k=8, sparsity=Fraction(1, 5),
                        lengths=("uniform", 900, 2600), n_verify=2, seed=5)
-    check(oracle, w)
+    check(oracle, w, opts=bd.Options(verify_chunk=split[0], draft_chunk=split[1]))
 
 
 @pytest.mark.parametrize("L,s", [(8192, Fraction(1, 20)), (8193, Fraction(1, 20)),
@@ -235,6 +223,7 @@ def _draft_only(oracle, b, lists, counts):
                                       1.0 / np.sqrt(w.head_dim))
         parity.assert_o(to_np(o[r]), ro, w.dtype, f"draft {r} O")
         parity.assert_lse_like(to_np(lse[r]), rl, f"draft {r} LSE")
+    return o, lse
 
 
 def test_draft_list_edge_cases(oracle):
@@ -253,6 +242,71 @@ def test_draft_list_edge_cases(oracle):
     lists.append(np.stack([np.arange(400)] * 2)); counts.append(400)
     lists.append(np.stack([rng.permutation(400)[:50], rng.permutation(400)[:50]])); counts.append(50)
     _draft_only(oracle, b, lists, counts)
+
+
+def _poison_slot0(b):
+    """Moves every token stored in pool slot 0 to an unused slot, then fills
+    slot 0's K and V rows with NaN, +Inf and -Inf: no request references it, so
+    no output may depend on it."""
+    used = set()
+    for r in range(b.B):
+        used.update(b.page_table[r, :b.seq_lens[r]].tolist())
+    free = next(x for x in range(1, b.num_slots) if x not in used)
+    for r in range(b.B):
+        row = b.page_table[r, :b.seq_lens[r]]
+        hit = (row == 0).nonzero().flatten()
+        if len(hit):
+            row[hit] = free
+            b.k_pool[free] = b.k_pool[0]
+            b.v_pool[free] = b.v_pool[0]
+    bad = torch.tensor([float("nan"), float("inf"), float("-inf"), float("nan")])
+    for pool in (b.k_pool, b.v_pool):
+        pool[0] = bad.repeat(pool.shape[-1] // 4).to(pool.dtype)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_masked_entries_ignore_nonfinite_pool_row(oracle, dtype):
+    """Masked list entries (out of range, negative, and the padding of chunks
+    that are not a whole number of 32-entry tiles) read pool row 0 on the MFMA
+    path; with NaN and Inf there, every draft still matches the oracle, and a
+    list with no valid entry gives O = 0 and LSE = -inf exactly."""
+    w = synth.Workload(name=f"nanrow-{dtype}", batch=6, num_qo_heads=8, num_kv_heads=2,
+                       head_dim=128, dtype=dtype, spec_k=4, sparsity=Fraction(1, 20),
+                       lengths=("fixed", 400), n_verify=0, seed=44)
+    b = synth.make_batch(w, is_verify=[False] * 6)
+    _poison_slot0(b)
+    rng = np.random.default_rng(3)
+    lists, counts = [], []
+    base = np.sort(rng.choice(400, 30, replace=False))
+    lists.append(np.stack([np.concatenate([base, [400, -1, 1 << 30, -7]])] * 2)); counts.append(34)
+    lists.append(np.stack([np.array([400, -1, 4000])] * 2)); counts.append(3)
+    lists.append(np.stack([np.array([-1] * 40 + [7])] * 2)); counts.append(41)
+    lists.append(np.stack([np.concatenate([rng.choice(400, 33), [-1] * 12])] * 2)); counts.append(45)
+    lists.append(np.stack([np.array([123])] * 2)); counts.append(1)
+    lists.append(np.stack([np.arange(400)] * 2)); counts.append(400)
+    o, lse = _draft_only(oracle, b, lists, counts)
+    assert bool((o[1].float() == 0).all()), "all-invalid list: O is not 0"
+    assert bool(torch.isneginf(lse[1]).all()), "all-invalid list: LSE is not -inf"
+    assert bool(torch.isfinite(o.float()).all()), "non-finite O"
+
+
+def test_masked_entries_nonfinite_pool_row_unified(oracle):
+    """The same poisoned pool row under a mixed unified step whose drafts read
+    lists padded with -1 (the recallable index's padding)."""
+    w = synth.Workload(name="nanrow-unified", batch=7, num_qo_heads=32, num_kv_heads=8,
+                       head_dim=128, dtype="bf16", spec_k=8, sparsity=Fraction(1, 20),
+                       lengths=("uniform", 300, 1500), n_verify=2, seed=45)
+    b = synth.make_batch(w)
+    _poison_slot0(b)
+    for r in range(b.B):
+        if not b.is_verify[r]:
+            K = b.idx_count[r]
+            seg = b.idx[b.idx_off[r]:b.idx_off[r] + w.num_kv_heads * K].view(w.num_kv_heads, K)
+            seg[:, -(K // 3):] = -1
+    print(f"[case] {w.name} lens={b.seq_lens}", flush=True)
+    ref = oracle.step(**parity.oracle_inputs(b))
+    gpu = run_unified(b.to(DEV))
+    parity.compare_step(oracle, b, gpu, ref)
 
 
 def test_sequential_entry_points_match_unified(oracle):
@@ -361,9 +415,10 @@ def test_chained_verify_then_draft(oracle):
 
 
 def test_workspace_reuse_across_batches(oracle):
-    """One workspace serves differently shaped batches back to back; it is
-    poisoned with NaN bytes before each call, so a read of anything a call did
-    not write itself shows up in the outputs."""
+    """One workspace serves differently shaped batches back to back; all of it
+    but the work counters is poisoned with NaN bytes before each call, so a
+    read of anything a call did not write itself shows up in the outputs, and
+    every call leaves the counters at zero."""
     shapes = [(5, ("uniform", 600, 2500), 2, 3), (3, ("uniform", 100, 1300), 1, 4),
               (6, ("uniform", 1500, 3000), 3, 5)]
     batches = []
@@ -378,11 +433,12 @@ def test_workspace_reuse_across_batches(oracle):
         need = max(need, bd.workspace_bytes(lay, b.B, 8, b.is_verify, b.seq_lens, b.idx_count))
     ws = bd.workspace(need, DEV)
     for b in batches:
-        ws.fill_(0xFF)
+        ws[256:].fill_(0xFF)  # all but the work counters, which calls leave at zero
         bufs = bd.StepBuffers(b.to(DEV))
         bufs.ws = ws
         bufs.step()
         torch.cuda.synchronize()
+        assert not bool(ws[:256].any()), "the work counters were not left at zero"
         ref = oracle.step(**parity.oracle_inputs(b))
         parity.compare_step(oracle, b, {"o": bufs.o, "lse": bufs.lse, "logits": bufs.logits,
                                         "idx": bufs.idx}, ref)
@@ -460,6 +516,7 @@ def test_stepbuffers_rebinds_replaced_buffers():
     first = [to_np(t).copy() for t in (bufs.o, bufs.lse, bufs.logits, bufs.idx)]
     old_ws, old_o = bufs.ws, bufs.o
     bufs.ws = torch.full((old_ws.numel() + 4096,), 0xFF, dtype=torch.uint8, device=DEV)
+    bufs.ws[:256] = 0  # a new workspace's work counters start at zero
     bufs.o = torch.full_like(old_o, float("nan"))
     old_o.fill_(0.0)
     bufs.step()
@@ -470,13 +527,15 @@ def test_stepbuffers_rebinds_replaced_buffers():
         assert np.array_equal(a.view(np.uint8), g.view(np.uint8)), f"{name} differs"
 
 
-def test_plan_slots_released_every_way():
-    """Sixty calls on one stream without a synchronisation cycle the 16 plan
-    buffers almost four times while mixing the three ways a buffer is
-    released: a mixed batch (the post-pass reports it), a draft-only batch
-    (the attention launch reports it) and spa_pillar_topk alone (an event).
-    Every output ends bit for bit equal to the same call made alone, so no
-    buffer was rewritten while a launch still read it."""
+def test_plan_buffers_released_every_way(oracle):
+    """Eighty calls on one stream without a synchronisation share two plan
+    buffers, so every call waits for a buffer the GPU may still be reading,
+    while mixing the four ways a buffer is released: a mixed batch (the
+    post-pass reports it), a draft-only batch (the attention launch's last work
+    draw), spa_pillar_topk alone (the selection launch) and spa_recall_index
+    (a one-thread release launch).  Every output ends bit for bit equal to the
+    same call made alone, so no buffer was rewritten while a launch still read
+    it."""
     def wl(name, B, nv, seed):
         return synth.Workload(name=name, batch=B, num_qo_heads=16, num_kv_heads=8, head_dim=128,
                               dtype="bf16", spec_k=4, sparsity=Fraction(1, 10),
@@ -487,35 +546,83 @@ def test_plan_slots_released_every_way():
     bm, bdr, bv = bd.StepBuffers(mixed), bd.StepBuffers(drafts), bd.StepBuffers(verify)
     k, Hq, Hkv = 4, 16, 8
     topk_idx = torch.full_like(bv.idx, -5)
+    rec_cnt = [bd.recall_length(L, K, 4, 16) for L, K in zip(drafts.seq_lens, drafts.idx_count)]
+    rec_off = np.concatenate([[0], np.cumsum([Hkv * c for c in rec_cnt])[:-1]]).astype(np.int64)
+    rec_out = torch.full((int(sum(Hkv * c for c in rec_cnt)),), -9, dtype=torch.int32, device=DEV)
+    need = max(bm.plans.nbytes, bdr.plans.nbytes, bv.plans.nbytes,
+               bd.recall_plan_bytes(drafts.B))
+    shared = bd.PlanRing(need, n=2)
+    for sb in (bm, bdr, bv):
+        sb.plans = shared
 
     def topk_call():
         bd.pillar_topk(verify.B, k, Hq, Hkv, 1, k, verify.seq_lens, verify.idx_count, bv.logits,
-                       bv.h_logits_off, bv.lse, topk_idx, verify.idx_off, bv.ws)
+                       bv.h_logits_off, bv.lse, topk_idx, verify.idx_off, bv.ws,
+                       plan=shared.next())
+
+    def recall_call():
+        bd.recall_index(drafts.B, Hkv, drafts.seq_lens, 4, 16, drafts.idx_count, drafts.idx_off,
+                        bdr.idx, rec_cnt, rec_off, rec_out, plan=shared.next())
 
     def outputs():
         return [to_np(t).copy() for t in (bm.o, bm.lse, bm.logits, bm.idx, bdr.o, bdr.lse,
-                                          bv.o, bv.lse, bv.logits, bv.idx, topk_idx)]
+                                          bv.o, bv.lse, bv.logits, bv.idx, topk_idx, rec_out)]
 
-    for f in (bm.step, bdr.step, bv.step, topk_call):
+    for f in (bm.step, bdr.step, bv.step, topk_call, recall_call):
         f()
         torch.cuda.synchronize()
     alone = outputs()
-    for _ in range(15):
+    for _ in range(16):
         bm.step()
         bdr.step()
         bv.step()
         topk_call()
+        recall_call()
     torch.cuda.synchronize()
     for i, (a, g) in enumerate(zip(alone, outputs())):
         assert np.array_equal(a.view(np.uint8), g.view(np.uint8)), f"output {i} differs"
 
 
-def test_host_threads_share_the_plan_ring():
+def test_one_plan_buffer_across_two_streams():
+    """A single plan buffer used by calls alternating between two streams: each
+    call waits until the GPU has finished reading the previous call's plan, so
+    the results match each batch stepped alone."""
+    shapes = [(6, ("uniform", 400, 3000), 2, 51), (5, ("uniform", 100, 2000), 0, 52)]
+    batches = []
+    for B, lengths, nv, seed in shapes:
+        w = synth.Workload(name=f"oneplan{seed}", batch=B, num_qo_heads=32, num_kv_heads=8,
+                           head_dim=128, dtype="bf16", spec_k=8, sparsity=Fraction(1, 20),
+                           lengths=lengths, n_verify=nv, seed=seed)
+        ver = [False] * B if nv == 0 else None
+        batches.append(synth.make_batch(w, device=DEV, is_verify=ver))
+    alone = []
+    for b in batches:
+        bufs = bd.StepBuffers(b)
+        bufs.step()
+        torch.cuda.synchronize()
+        alone.append([to_np(t).copy() for t in (bufs.o, bufs.lse, bufs.idx)])
+    bufs = [bd.StepBuffers(b, n_plans=1) for b in batches]
+    one = bd.PlanRing(max(bu.plans.nbytes for bu in bufs), n=1)
+    for bu in bufs:
+        bu.plans = one
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    torch.cuda.synchronize()
+    for _ in range(15):
+        for s, bu in zip(streams, bufs):
+            with torch.cuda.stream(s):
+                bu.step()
+    torch.cuda.synchronize()
+    for want, bu in zip(alone, bufs):
+        got = [to_np(t) for t in (bu.o, bu.lse, bu.idx)]
+        for name, a, g in zip(("O", "LSE", "idx"), want, got):
+            assert np.array_equal(a.view(np.uint8), g.view(np.uint8)), f"{name} differs"
+
+
+def test_host_threads_step_concurrently():
     """Three host threads, each stepping its own batch on its own stream 25
     times without synchronising (ctypes releases the interpreter lock during
     the call, so the calls interleave inside the library), end bit for bit
-    equal to each batch stepped alone: the plan buffers, their release words
-    and the item counters are never shared by calls in flight."""
+    equal to each batch stepped alone: calls share no state in the library."""
     import threading
     shapes = [(5, 2, 71), (7, 0, 72), (4, 4, 73)]
     batches = []
