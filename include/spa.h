@@ -16,7 +16,8 @@
  *   Ownership   The caller owns every buffer; the library allocates and frees
  *               nothing, on the device or the host, and keeps no per-call
  *               state between calls (it caches device properties and kernel
- *               occupancies only).  Device pointers (d_*) are HIP device
+ *               occupancies only; spa_unified_step_static alone uses a
+ *               library-held device array, see there).  Device pointers (d_*) are HIP device
  *               memory; host pointers (h_*) are ordinary host memory read
  *               during the call only, except the plan buffer below.
  *   Layouts     (H_q query heads, H_kv KV heads, G = H_q / H_kv, d = head_dim,
@@ -238,6 +239,33 @@ int32_t spa_unified_step(const spa_layout* layout, int32_t B, int32_t spec_k,
                          int32_t avg_row_begin, int32_t avg_row_count, void* d_ws,
                          size_t ws_bytes, void* h_plan, size_t plan_bytes,
                          const spa_options* opts, void* stream);
+
+/* Bytes of the static workspace of spa_unified_step_static (32 MiB). */
+#define SPA_STATIC_WORKSPACE_BYTES (32u << 20)
+
+/* spa_unified_step without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, semantics and results
+ * as spa_unified_step; the workspace is a library-held device array of
+ * SPA_STATIC_WORKSPACE_BYTES per GPU (held until the process ends), whose
+ * address is looked up once per device on the first call made with that
+ * device current.  A batch whose spa_workspace_bytes(...) exceeds it is
+ * rejected with SPA_ERR_UNSUPPORTED before anything is enqueued.  The call
+ * allocates nothing, on the device or in pinned host memory (the caller still
+ * passes the plan buffer, inputs and outputs).  Every call on a GPU shares
+ * that GPU's array: calls that may overlap on one GPU (other streams, other
+ * host threads) race and must be ordered by the caller.  The array's work
+ * counters are zero when the library loads and every call leaves them zero;
+ * nothing else in it needs to start at any value. */
+int32_t spa_unified_step_static(const spa_layout* layout, int32_t B, int32_t spec_k,
+                                const uint8_t* h_is_verify, const int32_t* h_seq_lens,
+                                const int32_t* h_q_indptr, const int32_t* d_page_table,
+                                const void* d_q, const void* d_k_pool, const void* d_v_pool,
+                                const int32_t* h_idx_count, const int64_t* h_idx_off,
+                                int32_t* d_idx, void* d_o, float* d_lse, float* d_logits,
+                                const int64_t* h_logits_off, int32_t avg_row_begin,
+                                int32_t avg_row_count, void* h_plan, size_t plan_bytes,
+                                const spa_options* opts, void* stream);
 
 /* Recallable sparse index of B draft requests.  Page "全局的稀疏一瞥"
  * (arxiv.org 2607.27735 as rendered on bittide.aicompass.dev), section 方法,

@@ -30,8 +30,11 @@ SPA_BF16 = 0
 SPA_F32 = 1
 ABI_VERSION = 2
 
+STATIC_WORKSPACE_BYTES = 32 << 20  # SPA_STATIC_WORKSPACE_BYTES
+
 EXPORTED = ("spa_abi_version", "spa_last_error", "spa_workspace_bytes", "spa_plan_bytes",
             "spa_verify_attn", "spa_pillar_topk", "spa_draft_attn", "spa_unified_step",
+            "spa_unified_step_static",
             "spa_recall_index", "spa_recall_plan_bytes", "spa_list_quality",
             "spa_list_quality_workspace_bytes", "spa_list_quality_plan_bytes")
 
@@ -90,6 +93,9 @@ def load(path: str = LIB_PATH):
     lib.spa_unified_step.argtypes = [L, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                      vp, vp, i32, i32, vp, sz, vp, sz, O, vp]
     lib.spa_unified_step.restype = i32
+    lib.spa_unified_step_static.argtypes = [L, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                            vp, vp, vp, vp, i32, i32, vp, sz, O, vp]
+    lib.spa_unified_step_static.restype = i32
     lib.spa_recall_index.argtypes = [i32, i32, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.spa_recall_index.restype = i32
     lib.spa_recall_plan_bytes.argtypes = [i32]
@@ -325,6 +331,24 @@ def unified_step(lay, B, spec_k, is_verify, seq_lens, q_indptr, page_table, q, k
         h.arr(idx_count, np.int32), h.arr(idx_off, np.int64), _dptr(idx), _dptr(o), _dptr(lse),
         _dptr(logits), h.arr(logits_off, np.int64), int(avg_row_begin), int(avg_row_count),
         _dptr(ws), _nbytes(ws), _hptr(plan), _nbytes(plan), _opts(opts), _stream(q)))
+
+
+def unified_step_static(lay, B, spec_k, is_verify, seq_lens, q_indptr, page_table, q, k_pool,
+                        v_pool, idx_count, idx_off, idx, o, lse, logits, logits_off,
+                        plan: Optional[torch.Tensor] = None, avg_row_begin: int = 1,
+                        avg_row_count: Optional[int] = None, opts: Optional[Options] = None):
+    """spa_unified_step_static: the unified step with the library's static
+    device workspace (no workspace argument; nothing is allocated)."""
+    if plan is None:
+        plan = _plan_for(plan_bytes(lay, B, spec_k, is_verify, seq_lens, idx_count, opts))
+    h = _Host()
+    avg_row_count = spec_k if avg_row_count is None else avg_row_count
+    _check(load().spa_unified_step_static(
+        C.byref(lay), int(B), int(spec_k), h.arr(is_verify, np.uint8), h.arr(seq_lens, np.int32),
+        h.arr(q_indptr, np.int32), _dptr(page_table), _dptr(q), _dptr(k_pool), _dptr(v_pool),
+        h.arr(idx_count, np.int32), h.arr(idx_off, np.int64), _dptr(idx), _dptr(o), _dptr(lse),
+        _dptr(logits), h.arr(logits_off, np.int64), int(avg_row_begin), int(avg_row_count),
+        _hptr(plan), _nbytes(plan), _opts(opts), _stream(q)))
 
 
 def recall_length(L: int, stored: int, n_sink: int, n_recent: int) -> int:

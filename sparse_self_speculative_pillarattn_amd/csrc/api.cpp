@@ -18,6 +18,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <thread>
 #include <vector>
@@ -1018,6 +1019,81 @@ int32_t spa_unified_step(const spa_layout* layout, int32_t B, int32_t spec_k,
   b.logits = d_logits;
   return run(s, rq, pl, b, avg_row_begin, avg_row_count, d_ws, ws_bytes, h_plan, plan_bytes, o,
              static_cast<hipStream_t>(stream));
+}
+
+// ---- the entry point that allocates nothing ---------------------------------
+// spa_unified_step_static runs the unified step with its workspace in this
+// file-scope device array instead of a caller buffer.  Each GPU holds its own
+// copy until the process ends; host code reaches it only through the address
+// hipGetSymbolAddress returns on that device (the array's name is a host-side
+// stand-in, not a device address).  Its first bytes are the attention work
+// counters: zero at load, and every call leaves them zero.
+static __device__ __align__(256) char scratch[SPA_STATIC_WORKSPACE_BYTES];
+}  // extern "C"
+
+namespace {
+// Device address of `scratch` on the current device, looked up once per
+// device with that device current.
+int32_t scratch_address(void** out) {
+  static std::mutex mu;
+  static std::vector<void*> addr;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("get device: ") + hipGetErrorString(e));
+  std::lock_guard<std::mutex> lock(mu);
+  if ((int)addr.size() <= dev) addr.resize(dev + 1, nullptr);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return fail(SPA_ERR_HIP, std::string("static workspace address: ") + hipGetErrorString(e));
+    }
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return SPA_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int32_t spa_unified_step_static(const spa_layout* layout, int32_t B, int32_t spec_k,
+                                const uint8_t* h_is_verify, const int32_t* h_seq_lens,
+                                const int32_t* h_q_indptr, const int32_t* d_page_table,
+                                const void* d_q, const void* d_k_pool, const void* d_v_pool,
+                                const int32_t* h_idx_count, const int64_t* h_idx_off,
+                                int32_t* d_idx, void* d_o, float* d_lse, float* d_logits,
+                                const int64_t* h_logits_off, int32_t avg_row_begin,
+                                int32_t avg_row_count, void* h_plan, size_t plan_bytes,
+                                const spa_options* opts, void* stream) {
+  // the arguments are checked and the batch sized before the array is used
+  if (B > 0) {
+    const size_t need = spa_workspace_bytes(layout, B, spec_k, h_is_verify, h_seq_lens,
+                                            h_idx_count, opts);
+    if (need == 0) {
+      // invalid sizes: the full call reports the precise reason
+      return spa_unified_step(layout, B, spec_k, h_is_verify, h_seq_lens, h_q_indptr,
+                              d_page_table, d_q, d_k_pool, d_v_pool, h_idx_count, h_idx_off,
+                              d_idx, d_o, d_lse, d_logits, h_logits_off, avg_row_begin,
+                              avg_row_count, nullptr, 0, h_plan, plan_bytes, opts, stream);
+    }
+    if (need > SPA_STATIC_WORKSPACE_BYTES)
+      return fail(SPA_ERR_UNSUPPORTED,
+                  "batch needs a workspace of " + std::to_string(need) +
+                      " bytes, above the static workspace's " +
+                      std::to_string((size_t)SPA_STATIC_WORKSPACE_BYTES) +
+                      "; use spa_unified_step with a caller workspace");
+  }
+  void* ws = nullptr;
+  if (B > 0) {
+    const int32_t rc = scratch_address(&ws);
+    if (rc) return rc;
+  }
+  return spa_unified_step(layout, B, spec_k, h_is_verify, h_seq_lens, h_q_indptr, d_page_table,
+                          d_q, d_k_pool, d_v_pool, h_idx_count, h_idx_off, d_idx, d_o, d_lse,
+                          d_logits, h_logits_off, avg_row_begin, avg_row_count, ws,
+                          SPA_STATIC_WORKSPACE_BYTES, h_plan, plan_bytes, opts, stream);
 }
 
 size_t spa_recall_plan_bytes(int32_t B) {

@@ -1,0 +1,90 @@
+"""spa_unified_step_static, the unified step without a caller workspace (its
+workspace is a library-held device array), against spa_unified_step on the
+same inputs: two calls in a row, the second on a smaller batch, so the second
+call runs over what the first left in the shared array."""
+import ctypes as C
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+from conftest import to_np, widen
+import parity
+from sparse_self_speculative_pillarattn_amd import binding as bd
+from sparse_self_speculative_pillarattn_amd import synth
+
+DEV = "cuda:0"
+
+
+def _static_outputs(b, bufs):
+    """Fresh outputs of spa_unified_step_static on the same batch as bufs."""
+    o = torch.full_like(bufs.o, float("nan"))
+    lse = torch.full_like(bufs.lse, float("nan"))
+    logits = torch.full_like(bufs.logits, float("nan"))
+    idx = b.idx.clone()
+    bd.unified_step_static(bufs.lay, b.B, b.w.spec_k, b.is_verify, b.seq_lens, b.q_indptr,
+                           b.page_table, b.q, b.k_pool, b.v_pool, b.idx_count, b.idx_off, idx, o,
+                           lse, logits, bufs.h_logits_off, opts=bufs.opts)
+    return {"o": o, "lse": lse, "logits": logits, "idx": idx}
+
+
+@pytest.mark.gpu
+def test_static_workspace_matches_caller_workspace(oracle):
+    shapes = [(12, ("uniform", 2000, 6000), 3, 81), (5, ("uniform", 300, 1500), 2, 82)]
+    for B, lengths, nv, seed in shapes:  # the second call is the smaller batch
+        w = synth.Workload(name=f"static{seed}", batch=B, num_qo_heads=32, num_kv_heads=8,
+                           head_dim=128, dtype="bf16", spec_k=8, sparsity=Fraction(1, 20),
+                           lengths=lengths, n_verify=nv, seed=seed)
+        b = synth.make_batch(w)
+        print(f"[case] static B={B} lens={b.seq_lens}", flush=True)
+        bdev = b.to(DEV)
+        bufs = bd.StepBuffers(bdev)
+        assert bd.workspace_bytes(bufs.lay, b.B, w.spec_k, b.is_verify, b.seq_lens,
+                                  b.idx_count) <= bd.STATIC_WORKSPACE_BYTES
+        bufs.step()
+        torch.cuda.synchronize()
+        want = {"o": bufs.o, "lse": bufs.lse, "logits": bufs.logits, "idx": bufs.idx}
+        got = _static_outputs(bdev, bufs)
+        torch.cuda.synchronize()
+        # the bar of the parity tests (tolerances; index lists exact) ...
+        parity.assert_o(to_np(got["o"]), widen(to_np(want["o"])), w.dtype, "O")
+        parity.assert_lse_like(to_np(got["lse"]), to_np(want["lse"]), "LSE")
+        parity.assert_lse_like(to_np(got["logits"]), to_np(want["logits"]), "logits")
+        assert np.array_equal(to_np(got["idx"]), to_np(want["idx"])), "index lists differ"
+        # ... and, since the two entry points run the same kernels on the same
+        # plan, the same bits
+        for name in ("o", "lse", "logits"):
+            assert np.array_equal(to_np(got[name]).view(np.uint8),
+                                  to_np(want[name]).view(np.uint8)), f"{name} bits differ"
+        # and the static path against the oracle itself
+        ref = oracle.step(**parity.oracle_inputs(b))
+        parity.compare_step(oracle, b, got, ref)
+
+
+def test_static_rejects_a_batch_above_its_workspace():
+    """Checked on the host before anything else: no device call is made."""
+    if not os.path.exists(bd.LIB_PATH):
+        from sparse_self_speculative_pillarattn_amd import build
+        build.build()
+    lib = bd.load()
+    lay = bd.SpaLayout(32, 8, 128, 0.0, 0, 1 << 24, 1 << 17)
+    B = 64
+    ver = np.ones(B, np.uint8)
+    lens = np.full(B, 1 << 17, np.int32)
+    cnt = np.full(B, 100, np.int32)
+    need = lib.spa_workspace_bytes(C.byref(lay), B, 8, ver.ctypes.data_as(C.c_void_p),
+                                   lens.ctypes.data_as(C.c_void_p),
+                                   cnt.ctypes.data_as(C.c_void_p), None)
+    assert need > bd.STATIC_WORKSPACE_BYTES
+    indptr = np.arange(0, 9 * B + 1, 9, dtype=np.int32)
+    off = np.arange(B, dtype=np.int64) * 8 * 100
+    loff = np.arange(B, dtype=np.int64) * 9 * 32 * (1 << 17)
+    F = C.c_void_p(0x1000)
+    p = lambda a: a.ctypes.data_as(C.c_void_p)
+    rc = lib.spa_unified_step_static(C.byref(lay), B, 8, p(ver), p(lens), p(indptr), F, F, F, F,
+                                     p(cnt), p(off), F, F, F, F, p(loff), 1, 8, F, 1 << 30, None,
+                                     None)
+    assert rc == bd.SPA_ERR_UNSUPPORTED
+    assert b"static workspace" in lib.spa_last_error()
