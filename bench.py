@@ -506,6 +506,9 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default=synth.QWEN3_8B.name, choices=sorted(synth.WORKLOADS))
+    ap.add_argument("--settle-copies", type=int, default=150,
+                    help="1 GiB device copies run at the end of the setup, before the warm-up, "
+                         "so that the measured steps start from loaded clocks (0: none)")
     ap.add_argument("--cold-steps", type=int, default=20,
                     help="steps timed one by one after a 512 MB cache-flushing write")
     ap.add_argument("--cpu-repeats", type=int, default=15,
@@ -572,18 +575,34 @@ def main():
         clock_ramp(w, dev)
         return
     print(f"[bench] generating {w.name} on {dev}", file=sys.stderr, flush=True)
-    # make_batch queues its bulk device generation last and returns while it
-    # runs; the buffers are set up and the warm-up queued behind it, so the
-    # GPU does not sit idle before the measured steps (after an idle period
-    # its clocks take about 10 ms of load to settle: --clock-ramp)
     b = synth.make_batch(w, device=dev)
     bufs = bd.StepBuffers(b)
     alg = algorithmic_bytes(b)
 
-    # warm-up
+    # Clock settling, the last part of the setup: after an idle period (here
+    # the host-side part of the batch generation) the GPU's clocks take about
+    # 10 ms of load to settle, and calls made meanwhile run up to 10% slower
+    # (--clock-ramp); after ~40 ms of plain device copies they do not.  A
+    # serving loop keeps the GPU loaded between attention steps, so the
+    # measured steps start from loaded clocks.  The copies are unrelated to
+    # the step and end before the warm-up steps start.
+    settle = None
+    if args.settle_copies > 0:
+        src = torch.empty((1 << 30,), dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.settle_copies):
+            dst.copy_(src)
+        e1.record()
+        del src, dst  # freed in stream order, after the copies
+
+    # warm-up, queued right behind the settling copies
     for _ in range(args.warmup):
         bufs.step()
     torch.cuda.synchronize()
+    if args.settle_copies > 0:
+        settle = {"copies_of_1GiB": args.settle_copies, "ms": round(e0.elapsed_time(e1), 1)}
 
     # timed region: K steps back to back with nothing but the two bracketing
     # events (the library's per-launch events would add their own gaps)
@@ -685,6 +704,7 @@ def main():
         "bytes_method_per_step": alg["bytes_method"],
         "bytes_min_per_step": alg["bytes_min"],
         "kernel_us": breakdown,
+        "clock_settle": settle,
         "cold": cold,
         "roofline": {"bound": "hbm", "kernel": "attn_kernel",
                      "achieved": round(attn_gbps, 1),
