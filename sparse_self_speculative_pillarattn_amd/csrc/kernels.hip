@@ -652,6 +652,7 @@ __device__ void gather_tile_valu(const AttnParams& p, const Item& it, char* smem
         const int hh = x / TB, u = x % TB;
         if (b0 + u < nent) lrow[(int64_t)hh * L + it.begin + b0 + u] = scs[hh * TB + u];
       }
+      __syncthreads();  // the loop below rewrites scs in place
     }
     for (int hh = wave; hh < G; hh += nwaves) {
       float mx = NEG_INF;
