@@ -72,6 +72,7 @@ struct Plan {
   int max_nchunk = 1;           // most split-K chunks of any merged request
   int cv = DEFAULT_VERIFY_CHUNK;  // positions per verify item
   int cd = DEFAULT_DRAFT_CHUNK;   // list entries per draft item
+  int ng = 1;                   // KV heads per item of an unsplit draft request (MFMA path)
   int n_items = 0;              // attention records
   // split: a mixed batch runs its draft items in a second attention launch on
   // a side stream, concurrently with verify attention, merge, averaging and
@@ -216,6 +217,26 @@ int32_t plan_size(const Shape& s, const std::vector<Req>& rq, bool attn, bool to
   pl->part0.assign(B, 0);
   int64_t part_rows = 0;
   if (attn) {
+    // Packed drafts (MFMA path): an unsplit draft request's KV heads go ng to
+    // an item, so that an item's startup (record, list and page-table reads,
+    // first tile: about 8 us at load) is paid once per ng lists.  Packing
+    // doubles ng while the lists are short (ng times the longest one's tiles
+    // below 24), every workgroup of two per CU still gets a draft item, and
+    // the slots and the staged query rows fit LDS.
+    if (bf16) {
+      int64_t lists = 0;
+      int tiles = 0;
+      for (const Req& q : rq)
+        if (!q.verify && q.nlist <= CD) {
+          lists += Hkv;
+          tiles = std::max(tiles, (q.nlist + TILE_TOKENS - 1) / TILE_TOKENS);
+        }
+      while (lists > 0 && Hkv % (2 * pl->ng) == 0 && 2 * pl->ng * tiles <= PACK_TILES &&
+             lists / (2 * pl->ng) >= 2 * (int64_t)o.num_cus &&
+             2 * pl->ng * tiles * TILE_TOKENS <= VERIFY_MAX_CHUNK &&
+             2 * pl->ng * G * D * esz <= PACK_Q_BYTES)
+        pl->ng *= 2;
+    }
     std::vector<double> bytes(B);
     std::vector<int> nitems(B);
     for (int r = 0; r < B; ++r) {
@@ -228,6 +249,7 @@ int32_t plan_size(const Shape& s, const std::vector<Req>& rq, bool attn, bool to
       pl->nchunk[r] = nc;
       if (nc > 1) pl->max_nchunk = std::max(pl->max_nchunk, nc);
       nitems[r] = nc * ((v && !bf16) ? rows_v : 1);  // fp32 verify: one item per query row
+      if (!v && nc == 1 && pl->ng > 1) nitems[r] = -pl->ng;  // ng KV heads per item
       if (nc > 1) {
         pl->part0[r] = part_rows;
         part_rows += (int64_t)Hkv * nc * (v ? rows_v : 1) * G;
@@ -248,7 +270,8 @@ int32_t plan_size(const Shape& s, const std::vector<Req>& rq, bool attn, bool to
     std::stable_sort(pl->order.begin(), pl->order.end(),
                      [&](int a, int b) { return bytes[a] > bytes[b]; });
     for (int r = 0; r < B; ++r)
-      ((pl->split && !rq[r].verify) ? pl->n_items_d : pl->n_items) += Hkv * nitems[r];
+      ((pl->split && !rq[r].verify) ? pl->n_items_d : pl->n_items) +=
+          nitems[r] < 0 ? Hkv / -nitems[r] : Hkv * nitems[r];
   }
   int64_t pbar = 0;
   if (topk)
@@ -282,8 +305,16 @@ int32_t plan_size(const Shape& s, const std::vector<Req>& rq, bool attn, bool to
   if (need_valu && G > MAX_GROUP)
     return fail(SPA_ERR_UNSUPPORTED, "GQA group above 8 on the fp32 path");
   pl->nthr = nthr;
-  int max_chunk = 1;  // longest item: positions (verify) or list entries (draft)
-  for (auto& q : rq) max_chunk = std::max(max_chunk, std::min(q.verify ? q.L : q.nlist, q.verify ? CV : CD));
+  // LDS slot entries of the longest item: positions (verify) or list entries
+  // (draft; a packed item's lists each padded to whole tiles, then its query
+  // rows, two bf16 per entry)
+  int max_chunk = 1;
+  for (auto& q : rq) {
+    max_chunk = std::max(max_chunk, std::min(q.verify ? q.L : q.nlist, q.verify ? CV : CD));
+    if (attn && !q.verify && pl->ng > 1 && q.nlist <= CD)
+      max_chunk = std::max(max_chunk, pl->ng * ((q.nlist + TILE_TOKENS - 1) / TILE_TOKENS) * TILE_TOKENS +
+                                          pl->ng * G * D * esz / 4);
+  }
   pl->smem = attn ? attn_smem_bytes(s.dtype, D, G, nthr, need_mfma, need_valu, max_chunk) : 0;
 
   // pinned plan layout
@@ -338,7 +369,8 @@ void plan_write(const Shape& s, const std::vector<Req>& rq, const Plan& pl, char
       const int64_t head_rows = (int64_t)nc * (v ? rows_v : 1) * G;
       Item* items = (pl.split && !v) ? items_d : items_v;
       int& cur = (pl.split && !v) ? cur_dr : cur_v;
-      for (int g = 0; g < Hkv; ++g) {
+      const int ng = (!v && nc == 1) ? pl.ng : 1;
+      for (int g = 0; g < Hkv; g += ng) {
         Item it;
         std::memset(&it, 0, sizeof it);
         it.kind = v ? KIND_VERIFY : KIND_DRAFT;
@@ -350,6 +382,7 @@ void plan_write(const Shape& s, const std::vector<Req>& rq, const Plan& pl, char
         it.list_len = q.nlist;
         it.off = v ? q.logits_off : q.idx_off + (int64_t)g * q.nlist;
         it.part_row0 = nc > 1 ? pl.part0[r] + g * head_rows : 0;
+        it.ng = ng;
         for (int c = 0; c < nc; ++c)
           for (int qi = 0; qi < nq; ++qi) {
             it.qi = qi;

@@ -140,7 +140,7 @@ __device__ __forceinline__ float group_sum(float v) {
 // Consumers only read LDS, run MFMA and store.  One barrier per tile hands a
 // stage from the producer to the consumers and, a tile later, back.
 // ==========================================================================
-constexpr int DMA_TT = 32;     // tokens per stage
+constexpr int DMA_TT = TILE_TOKENS;  // tokens per stage
 constexpr int DMA_STAGES = 4;  // LDS stages; DMA_STAGES - 1 tiles in flight
 
 template <int D>
@@ -252,9 +252,13 @@ __device__ void dma_producer(const AttnParams& p, const Item& it, char* smem,
   constexpr int PER_TILE = 2 * (DMA_TT * NCH / 64);  // load instructions per tile
   constexpr int STAGE2 = 2 * DMA_TT * D * 2;
   static_assert(DMA_STAGES == 3 || DMA_STAGES == 4, "the waits below allow at most two tiles behind");
-  const int n = (it.end - it.begin + DMA_TT - 1) / DMA_TT;
-  const uint16_t* kp = reinterpret_cast<const uint16_t*>(p.k_pool) + it.g * D;
-  const uint16_t* vp = reinterpret_cast<const uint16_t*>(p.v_pool) + it.g * D;
+  // a draft item may hold the lists of ng consecutive KV heads, tph tiles each
+  const int tph = (it.end - it.begin + DMA_TT - 1) / DMA_TT;
+  const int n = tph * max(1, it.ng);
+  const uint16_t* kp0 = reinterpret_cast<const uint16_t*>(p.k_pool) + it.g * D;
+  const uint16_t* vp0 = reinterpret_cast<const uint16_t*>(p.v_pool) + it.g * D;
+  auto kp = [&](int t) { return kp0 + (t / tph) * D; };
+  auto vp = [&](int t) { return vp0 + (t / tph) * D; };
   const int64_t rs = (int64_t)p.Hkv * D;
   // The slots of the next tile are read from LDS right after a tile is issued,
   // so that their latency (LDS is busy with the consumers' operand reads)
@@ -262,14 +266,14 @@ __device__ void dma_producer(const AttnParams& p, const Item& it, char* smem,
   TileSlots<D> ts;
   read_tile_slots<D>(ts, slots, lane);
   for (int i = 0; i < min(n, DMA_STAGES - 1); ++i) {
-    issue_kv_tile<D>(smem + i * STAGE2, ts, kp, vp, rs, lane);
+    issue_kv_tile<D>(smem + i * STAGE2, ts, kp(i), vp(i), rs, lane);
     if (i + 1 < n) read_tile_slots<D>(ts, slots + (i + 1) * DMA_TT, lane);
   }
   producer_barrier<PER_TILE>(min(n, DMA_STAGES - 1) - 1);  // tile 0 ready
   for (int i = 0; i + 1 < n; ++i) {
     const int t = i + DMA_STAGES - 1;  // into the stage tile i-1 used
     if (t < n) {
-      issue_kv_tile<D>(smem + (t % DMA_STAGES) * STAGE2, ts, kp, vp, rs, lane);
+      issue_kv_tile<D>(smem + (t % DMA_STAGES) * STAGE2, ts, kp(t), vp(t), rs, lane);
       if (t + 1 < n) read_tile_slots<D>(ts, slots + (t + 1) * DMA_TT, lane);
     }
     producer_barrier<PER_TILE>(min(n - 1, t) - (i + 1));  // tile i+1 ready
@@ -289,7 +293,8 @@ __device__ void dma_consumer(const AttnParams& p, const Item& it, char* smem,
   const int R = rows_q * G;
   const int L = it.L;
   const int jb = it.begin, je = it.end;
-  const int n_tiles = (je - jb + DMA_TT - 1) / DMA_TT;
+  const int n_tiles = (je - jb + DMA_TT - 1) / DMA_TT;  // per KV head
+  const int ng = max(1, it.ng);  // KV heads of a packed draft item (1 otherwise)
 
   const int n = lane & 15, q4 = lane >> 4;
   const int rho = wave * 16 + n;
@@ -297,23 +302,11 @@ __device__ void dma_consumer(const AttnParams& p, const Item& it, char* smem,
   const bool row_ok = rho < R;
   const int qi = row_ok ? rho / G : 0;
   const int hh = row_ok ? rho % G : 0;
-  const int h = it.g * G + hh;
+  int h = it.g * G + hh;
 
   bf16x8 qop[KS];
-  {
-    const uint16_t* qrow =
-        reinterpret_cast<const uint16_t*>(p.q) + ((int64_t)(it.row0 + qi) * Hq + h) * D;
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (row_ok) v = *reinterpret_cast<const uint4*>(qrow + 8 * (4 * s + q4));
-      qop[s] = __builtin_bit_cast(bf16x8, v);
-    }
-  }
   float m_run = NEG_INF, l_run = 0.f;
   f32x4 oacc[DT];
-#pragma unroll
-  for (int i = 0; i < DT; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int last_vis = is_list ? 0x7fffffff : L - rows_q + qi;
   float* lrow = is_list ? nullptr : p.logits + it.off + ((int64_t)qi * Hq + h) * L;
   const float sc = p.sm_scale;
@@ -343,14 +336,34 @@ __device__ void dma_consumer(const AttnParams& p, const Item& it, char* smem,
   // the workgroup's next item, drawn by wave 0 two tiles before the end so
   // that the atomic's round trip passes under the last tiles
   uint32_t next = 0u;
-  const int draw_at = max(n_tiles - 2, 0);
+  const int draw_at = max(ng * n_tiles - 2, 0);
+  // query rows of a packed item's heads, staged in LDS with its slots
+  const uint16_t* qst = reinterpret_cast<const uint16_t*>(slots + ng * n_tiles * DMA_TT);
+  for (int hd = 0; hd < ng; ++hd) {
+  h = (it.g + hd) * G + hh;
+  {
+    const uint16_t* qrow =
+        ng > 1 ? qst + (int64_t)(hd * G + hh) * D
+               : reinterpret_cast<const uint16_t*>(p.q) + ((int64_t)(it.row0 + qi) * Hq + h) * D;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (row_ok) v = *reinterpret_cast<const uint4*>(qrow + 8 * (4 * s + q4));
+      qop[s] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+  m_run = NEG_INF;
+  l_run = 0.f;
+#pragma unroll
+  for (int i = 0; i < DT; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int i = 0; i < n_tiles; ++i) {
-    __syncthreads();  // tile i ready (and tile i-1 released)
-    if (wave == 0 && lane == 0 && i == draw_at)
+    const int tt = hd * n_tiles + i;  // tile of the item: LDS stage and slots
+    __syncthreads();  // tile tt ready (and tile tt-1 released)
+    if (wave == 0 && lane == 0 && tt == draw_at)
       next = atomicInc(p.ticket, wrap);
     if (!wave_active) continue;
     const int t0 = jb + i * DMA_TT;
-    const char* Ks = smem + (i % DMA_STAGES) * 2 * STAGE;
+    const char* Ks = smem + (tt % DMA_STAGES) * 2 * STAGE;
     const char* Vs = Ks + STAGE;
     f32x4 sacc[2];
 #pragma unroll
@@ -401,7 +414,7 @@ __device__ void dma_consumer(const AttnParams& p, const Item& it, char* smem,
       if (is_list) {
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-          const int4 sv = *reinterpret_cast<const int4*>(slots + i * DMA_TT + 16 * t + 4 * q4);
+          const int4 sv = *reinterpret_cast<const int4*>(slots + tt * DMA_TT + 16 * t + 4 * q4);
           ok[t][0] = sv.x >= 0;
           ok[t][1] = sv.y >= 0;
           ok[t][2] = sv.z >= 0;
@@ -483,11 +496,10 @@ __device__ void dma_consumer(const AttnParams& p, const Item& it, char* smem,
     }
   }
 
-  if (wave == 0 && lane == 0) *next_item = (int)next;
-  if (!wave_active) return;
+  if (!wave_active) continue;
   float l_tot = l_run + __shfl_xor(l_run, 16);
   l_tot += __shfl_xor(l_tot, 32);
-  if (!row_ok) return;
+  if (!row_ok) continue;
   if (it.nchunk == 1) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     uint16_t* orow = reinterpret_cast<uint16_t*>(p.o) + ((int64_t)(it.row0 + qi) * Hq + h) * D;
@@ -516,6 +528,8 @@ __device__ void dma_consumer(const AttnParams& p, const Item& it, char* smem,
       p.part_ml[2 * pr + 1] = l_tot;
     }
   }
+  }  // KV heads of the item
+  if (wave == 0 && lane == 0) *next_item = (int)next;
 }
 
 // One attention item on the MFMA path: a verify chunk (positions [begin, end)
@@ -532,14 +546,24 @@ __device__ void attn_tile_dma(const AttnParams& p, const Item& it, char* smem, b
   const int padded = (je - jb + DMA_TT - 1) / DMA_TT * DMA_TT;
   const int32_t* pt = p.page_table + (int64_t)it.r * p.pt_stride;
   if (is_list) {
-    const int32_t* list = p.idx_in + it.off;
-    for (int j = tid; j < padded; j += blockDim.x) {
+    // the list of each packed KV head is padded to whole tiles
+    const int ng = max(1, it.ng);
+    for (int x = tid; x < ng * padded; x += blockDim.x) {
+      const int hd = x / padded, j = x - hd * padded;
+      const int32_t* list = p.idx_in + it.off + (int64_t)hd * it.list_len;
       int32_t sl = -1;
       if (jb + j < je) {
         const int pos = list[jb + j];
         if (pos >= 0 && pos < it.L) sl = (int32_t)clamp_slot(pt[pos], p.num_slots);
       }
-      slots[j] = sl;
+      slots[x] = sl;
+    }
+    if (ng > 1) {  // the G query rows of every packed head, after the slots
+      uint4* qst = reinterpret_cast<uint4*>(slots + ng * padded);
+      const uint4* qsrc =
+          reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(p.q) +
+                                         ((int64_t)it.row0 * p.Hq + it.g * p.G) * D);
+      for (int x = tid; x < ng * p.G * D / 8; x += blockDim.x) qst[x] = qsrc[x];
     }
   } else {
     for (int j = tid; j < padded; j += blockDim.x)

@@ -26,7 +26,7 @@ struct Item {
   int32_t nchunk;     // split-K chunks of (r, g); 1 = outputs written directly
   int32_t split;      // chunk index of this item within (r, g)
   int32_t list_len;   // draft: entries per KV head
-  int32_t pad_;
+  int32_t ng;         // MFMA draft items: KV heads g .. g+ng-1 whose lists the item holds (1 otherwise)
   int64_t off;        // verify: logits element offset of request r; draft: list offset of (r, g)
   int64_t part_row0;  // first split-K partial row of (r, g)
 };
@@ -105,6 +105,9 @@ constexpr int AVG_SPAN = 1024;         // positions per averaging item
 constexpr int VERIFY_MAX_CHUNK = 2048;
 constexpr int DRAFT_MAX_CHUNK = 2048;
 constexpr int MAX_GROUP = 8;           // query heads per KV head on the VALU path
+constexpr int TILE_TOKENS = 32;        // KV rows per LDS tile of the MFMA path
+constexpr int PACK_TILES = 32;         // a packed draft item stops growing at this many tiles
+constexpr int PACK_Q_BYTES = 4096;     // query rows a packed draft item stages in LDS
 constexpr int MAX_ROW_TILES = 7;       // 16-row MFMA tiles (one wave each + a producer, 512 threads max)
 constexpr int MAX_AVG_TERMS = 512;     // averaged (row, head) pairs per KV head
 constexpr int MAX_MERGE_CHUNKS = 256;  // split-K chunks per (r, g)

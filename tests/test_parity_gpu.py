@@ -199,7 +199,7 @@ def test_averaged_rows_parameter(oracle):
     check(oracle, w, avg_row_begin=0, avg_row_count=6)
 
 
-def _draft_only(oracle, b, lists, counts):
+def _draft_only(oracle, b, lists, counts, opts=None):
     """Run spa_draft_attn on B draft rows with explicit lists; compare with the oracle."""
     w = b.w
     Hkv = w.num_kv_heads
@@ -209,11 +209,11 @@ def _draft_only(oracle, b, lists, counts):
     lay = bd.layout(w.num_qo_heads, Hkv, w.head_dim, b.q.dtype, b.num_slots, b.stride)
     o = torch.full_like(dq, float("nan"), device=DEV)
     lse = torch.full((len(counts), w.num_qo_heads), float("nan"), device=DEV)
-    nbytes = bd.workspace_bytes(lay, len(counts), 1, None, b.seq_lens[:len(counts)], counts)
+    nbytes = bd.workspace_bytes(lay, len(counts), 1, None, b.seq_lens[:len(counts)], counts, opts)
     ws = bd.workspace(nbytes, DEV)
     bd.draft_attn(lay, len(counts), b.seq_lens[:len(counts)], b.page_table.to(DEV), counts, offs,
                   torch.from_numpy(flat).to(DEV), dq.to(DEV), b.k_pool.to(DEV), b.v_pool.to(DEV),
-                  o, lse, ws)
+                  o, lse, ws, opts=opts)
     torch.cuda.synchronize()
     qn, kn, vn, ptn = to_np(dq), to_np(b.k_pool), to_np(b.v_pool), to_np(b.page_table)
     for r, (lst, c) in enumerate(zip(lists, counts)):
@@ -264,8 +264,8 @@ def _poison_slot0(b):
         pool[0] = bad.repeat(pool.shape[-1] // 4).to(pool.dtype)
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_masked_entries_ignore_nonfinite_pool_row(oracle, dtype):
+@pytest.mark.parametrize("dtype,packed", [("bf16", False), ("f32", False), ("bf16", True)])
+def test_masked_entries_ignore_nonfinite_pool_row(oracle, dtype, packed):
     """Masked list entries (out of range, negative, and the padding of chunks
     that are not a whole number of 32-entry tiles) read pool row 0 on the MFMA
     path; with NaN and Inf there, every draft still matches the oracle, and a
@@ -284,7 +284,8 @@ def test_masked_entries_ignore_nonfinite_pool_row(oracle, dtype):
     lists.append(np.stack([np.concatenate([rng.choice(400, 33), [-1] * 12])] * 2)); counts.append(45)
     lists.append(np.stack([np.array([123])] * 2)); counts.append(1)
     lists.append(np.stack([np.arange(400)] * 2)); counts.append(400)
-    o, lse = _draft_only(oracle, b, lists, counts)
+    # packed: planned for one CU, so every draft item holds both KV heads
+    o, lse = _draft_only(oracle, b, lists, counts, bd.Options(num_cus=1) if packed else None)
     assert bool((o[1].float() == 0).all()), "all-invalid list: O is not 0"
     assert bool(torch.isneginf(lse[1]).all()), "all-invalid list: LSE is not -inf"
     assert bool(torch.isfinite(o.float()).all()), "non-finite O"
@@ -307,6 +308,32 @@ def test_masked_entries_nonfinite_pool_row_unified(oracle):
     ref = oracle.step(**parity.oracle_inputs(b))
     gpu = run_unified(b.to(DEV))
     parity.compare_step(oracle, b, gpu, ref)
+
+
+PACKED = [
+    # (H_q, H_kv, d, lengths, s): the plan for one CU packs up to 4 KV heads
+    # of a draft request into one item (2 for H_kv = 2, 8 for G = 2, none for G = 16)
+    (32, 8, 128, ("uniform", 50, 3000), Fraction(1, 20)),
+    (16, 8, 128, ("uniform", 20, 900), Fraction(1, 10)),
+    (8, 2, 64, ("uniform", 40, 2000), Fraction(1, 50)),
+    (64, 4, 128, ("uniform", 100, 800), Fraction(1, 20)),
+]
+
+
+@pytest.mark.parametrize("shape", PACKED, ids=lambda s: f"h{s[0]}kv{s[1]}d{s[2]}")
+def test_packed_draft_items(oracle, shape):
+    """Draft items holding the lists of several KV heads (planned for one CU,
+    so that even a small batch packs): every output matches the oracle, and
+    the same bits as the unpacked plan."""
+    Hq, Hkv, d, lengths, s = shape
+    w = synth.Workload(name=f"pack-{Hq}-{Hkv}-{d}", batch=9, num_qo_heads=Hq, num_kv_heads=Hkv,
+                       head_dim=d, dtype="bf16", spec_k=4, sparsity=s, lengths=lengths,
+                       n_verify=2, seed=Hq + d)
+    b, packed, ref = check(oracle, w, opts=bd.Options(num_cus=1, verify_chunk=512))
+    # the same verify chunks, drafts unpacked
+    plain = run_unified(b.to(DEV), opts=bd.Options(verify_chunk=512))
+    for name in ("o", "lse", "logits", "idx"):
+        assert np.array_equal(to_np(packed[name]).view(np.uint8), to_np(plain[name]).view(np.uint8)), name
 
 
 def test_sequential_entry_points_match_unified(oracle):
