@@ -496,6 +496,89 @@ def clock_ramp(w, dev, n: int = 150, group: int = 5):
     print(json.dumps(out), flush=True)
 
 
+def scheduler_measure(w, dev, steps: int, warmup: int, modes=("plain", "delayed"),
+                      output=(64, 1024)):
+    """Decode steps under the phase-bucket scheduler (include/spa_sched.h),
+    with and without delayed verification: w.batch slots, the workload's heads,
+    k and s, prompts from its length recipe (a log-normal recipe is drawn
+    uniformly over its clip range here), outputs uniform over `output` so that
+    requests retire and new ones join during the run.  Each step is planned on
+    the host (scheduler, initial lists of new requests), launched and
+    committed.  Two host disciplines per mode: "host_waits" -- before planning
+    a step the host waits for the step whose verify outcomes it needs (the one
+    before, or with delayed verification the one before that), as a server
+    that reads verify results back must; "run_ahead" -- the host never waits
+    (the GPU-bound rate).  Reports steps/s over the timed steps and the
+    per-step verify count and query rows against slots/C and (2k+1)/(k+1) B.
+    Python's cyclic garbage collector is paused during the timed steps (a
+    full collection in a process that has imported torch takes tens of ms)."""
+    import gc
+    from sparse_self_speculative_pillarattn_amd.sched_driver import SchedDriver
+    kind = w.lengths[0]
+    prompt = (w.lengths[1], w.lengths[1]) if kind == "fixed" else \
+        (w.lengths[1], w.lengths[2]) if kind == "uniform" else (w.lengths[3], w.lengths[4])
+    props = torch.cuda.get_device_properties(dev)
+    out = {"scheduler": w.name, "slots": w.batch, "spec_k": w.spec_k,
+           "sparsity": str(w.sparsity), "prompt": list(prompt), "output": list(output),
+           "steps": steps, "warmup": warmup, "modes": {}}
+    for mode in modes:
+        delayed = mode == "delayed"
+        print(f"[bench] scheduler {w.name} delayed={delayed}", file=sys.stderr, flush=True)
+        drv = SchedDriver(w.batch, w.spec_k, w.num_qo_heads, w.num_kv_heads, w.head_dim,
+                          w.sparsity, prompt, output, delayed=delayed, seed=w.seed, device=dev,
+                          dtype=torch.bfloat16 if w.dtype == "bf16" else torch.float32,
+                          num_cus=props.multi_processor_count)
+        res = {}
+        for waits in (True, False):
+            for _ in range(warmup):
+                drv.step(dependent=waits)
+            torch.cuda.synchronize()
+            s0 = drv.sched.stats()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            rows, nv, kv = [], [], []
+            gc.collect()
+            gc.disable()
+            wall0 = time.perf_counter()
+            e0.record()
+            for _ in range(steps):
+                st = drv.step(dependent=waits)
+                a = drv.last[1]
+                rows.append(st.rows)
+                nv.append(st.n_verify)
+                kv.append(int(np.where(a["is_verify"] == 1, a["seq_lens"].astype(np.int64),
+                                       a["idx_count"]).sum()))
+            e1.record()
+            torch.cuda.synchronize()
+            wall = time.perf_counter() - wall0
+            gc.enable()
+            gpu_ms = e0.elapsed_time(e1)
+            s1 = drv.sched.stats()
+            k, S = w.spec_k, w.batch
+            C = k + 1 + int(delayed)
+            rows_np = np.asarray(rows, np.float64)
+            res["host_waits" if waits else "run_ahead"] = {
+                "steps_per_s": round(steps / (gpu_ms * 1e-3), 1),
+                "us_per_step": round(gpu_ms * 1e3 / steps, 1),
+                "host_wall_us_per_step": round(wall * 1e6 / steps, 1),
+                "verify_per_step": {"min": int(min(nv)), "max": int(max(nv)),
+                                    "mean": round(float(np.mean(nv)), 3),
+                                    "slots_over_C": round(S / C, 3)},
+                "rows_per_step": {"min": int(rows_np.min()), "max": int(rows_np.max()),
+                                  "mean": round(float(rows_np.mean()), 2),
+                                  "cv": round(float(rows_np.std() / rows_np.mean()), 4),
+                                  "2k+1_over_k+1_B": round((2 * k + 1) / (k + 1) * S, 2)},
+                "attended_kv_tokens_per_s": round(float(np.sum(kv)) / (gpu_ms * 1e-3), 1),
+                "tokens_committed_per_s": round((s1["committed"] - s0["committed"]) /
+                                                (gpu_ms * 1e-3), 1),
+                "accepted_per_verify": round((s1["accepted"] - s0["accepted"]) /
+                                             max(1, s1["verifies"] - s0["verifies"]), 3),
+                "new_requests": s1["retired"] - s0["retired"]}
+        out["modes"]["delayed" if delayed else "plain"] = res
+        del drv
+        torch.cuda.empty_cache()
+    print(json.dumps(out), flush=True)
+
+
 # --------------------------------------------------------------------------- #
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
@@ -530,6 +613,11 @@ def main():
     ap.add_argument("--clock-ramp", action="store_true",
                     help="only time calls after an idle period and after busy work (groups "
                          "of 5) and print their JSON line")
+    ap.add_argument("--scheduler", nargs="?", const="both", default=None,
+                    choices=("both", "plain", "delayed"),
+                    help="only run decode steps under the phase-bucket scheduler (plain and/or "
+                         "delayed verification; --steps timed after --warmup) and print their "
+                         "JSON line")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 5 plain device copies of MIB MiB (reference for the HBM "
                          "byte counters) and exit")
@@ -573,6 +661,10 @@ def main():
         return
     if args.clock_ramp:
         clock_ramp(w, dev)
+        return
+    if args.scheduler:
+        modes = ("plain", "delayed") if args.scheduler == "both" else (args.scheduler,)
+        scheduler_measure(w, dev, args.steps, args.warmup, modes)
         return
     print(f"[bench] generating {w.name} on {dev}", file=sys.stderr, flush=True)
     b = synth.make_batch(w, device=dev)

@@ -157,6 +157,13 @@ typedef struct {
    * an overlapped unified step (on side_stream).  A launch the call does not
    * make records nothing. */
   void* timing[8];
+  /* Optional host array [B]: request r reads page_table row
+   * page_table_rows[r] instead of row r, so a caller that keeps one
+   * page-table row per batch slot can run any subset of its slots
+   * (attention calls only; NULL: row r).  page_table_row_count is the
+   * number of rows of d_page_table; every entry must lie in [0, it). */
+  const int32_t* page_table_rows;
+  int32_t page_table_row_count;
 } spa_options;
 
 /* Library ABI version (SPA_ABI_VERSION of the build). */

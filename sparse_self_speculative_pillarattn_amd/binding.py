@@ -37,6 +37,12 @@ EXPORTED = ("spa_abi_version", "spa_last_error", "spa_workspace_bytes", "spa_pla
             "spa_unified_step_static",
             "spa_recall_index", "spa_recall_plan_bytes", "spa_list_quality",
             "spa_list_quality_workspace_bytes", "spa_list_quality_plan_bytes")
+# include/spa_sched.h
+SCHED_EXPORTED = ("spa_sched_bytes", "spa_sched_capacity", "spa_sched_init", "spa_sched_next",
+                  "spa_sched_commit", "spa_sched_stats_read", "spa_sched_buckets")
+# per-token acceptance probability whose leading-run mean over k = 8 drafts is
+# 6.16 accepted tokens (the review's PillarAttn acceptance, 实验与结果)
+ACCEPT_PROB_6_16_OF_8 = 0.9415853644089122
 
 # indices into SpaOptions.timing: begin/end event pairs of each launch
 TIMING = {"attn": (0, 1), "post": (2, 3), "select": (4, 5), "attn_draft": (6, 7)}
@@ -57,7 +63,31 @@ class SpaLayout(C.Structure):
 class SpaOptions(C.Structure):
     _fields_ = [("verify_chunk", C.c_int32), ("draft_chunk", C.c_int32), ("num_cus", C.c_int32),
                 ("overlap", C.c_int32), ("side_stream", C.c_void_p), ("fork_event", C.c_void_p),
-                ("join_event", C.c_void_p), ("timing", C.c_void_p * 8)]
+                ("join_event", C.c_void_p), ("timing", C.c_void_p * 8),
+                ("page_table_rows", C.c_void_p), ("page_table_row_count", C.c_int32)]
+
+
+class SpaSchedConfig(C.Structure):
+    _fields_ = [("slots", C.c_int32), ("spec_k", C.c_int32), ("delayed", C.c_int32),
+                ("num_qo_heads", C.c_int32), ("num_kv_heads", C.c_int32),
+                ("sparsity_num", C.c_int32), ("sparsity_den", C.c_int32),
+                ("prompt_min", C.c_int32), ("prompt_max", C.c_int32),
+                ("output_min", C.c_int32), ("output_max", C.c_int32), ("max_len", C.c_int32),
+                ("accept_prob", C.c_float), ("seed", C.c_uint64)]
+
+
+class SpaSchedStep(C.Structure):
+    _fields_ = [("step", C.c_int64), ("B", C.c_int32), ("rows", C.c_int32),
+                ("n_verify", C.c_int32), ("n_draft", C.c_int32), ("n_waiting", C.c_int32),
+                ("n_new", C.c_int32), ("is_verify", C.c_void_p), ("seq_lens", C.c_void_p),
+                ("q_indptr", C.c_void_p), ("idx_count", C.c_void_p), ("idx_off", C.c_void_p),
+                ("logits_off", C.c_void_p), ("slot", C.c_void_p), ("new_slots", C.c_void_p),
+                ("new_len", C.c_void_p), ("new_count", C.c_void_p), ("logits_elems", C.c_int64)]
+
+
+class SpaSchedStats(C.Structure):
+    _fields_ = [(n, C.c_int64) for n in ("steps", "verifies", "drafts", "waits", "drafted",
+                                         "accepted", "committed", "retired", "rows")]
 
 
 _lib = None
@@ -107,6 +137,22 @@ def load(path: str = LIB_PATH):
     lib.spa_list_quality_workspace_bytes.restype = sz
     lib.spa_list_quality_plan_bytes.argtypes = [i32]
     lib.spa_list_quality_plan_bytes.restype = sz
+    SC = C.POINTER(SpaSchedConfig)
+    lib.spa_sched_bytes.argtypes = [SC]
+    lib.spa_sched_bytes.restype = sz
+    lib.spa_sched_capacity.argtypes = [SC, C.POINTER(C.c_int64), C.POINTER(C.c_int64),
+                                       C.POINTER(C.c_int32)]
+    lib.spa_sched_capacity.restype = i32
+    lib.spa_sched_init.argtypes = [vp, sz, SC]
+    lib.spa_sched_init.restype = i32
+    lib.spa_sched_next.argtypes = [vp, C.POINTER(SpaSchedStep)]
+    lib.spa_sched_next.restype = i32
+    lib.spa_sched_commit.argtypes = [vp]
+    lib.spa_sched_commit.restype = i32
+    lib.spa_sched_stats_read.argtypes = [vp, C.POINTER(SpaSchedStats)]
+    lib.spa_sched_stats_read.restype = i32
+    lib.spa_sched_buckets.argtypes = [vp, C.POINTER(C.c_int32), i32]
+    lib.spa_sched_buckets.restype = i32
     _lib = lib
     return lib
 
@@ -177,8 +223,13 @@ class Options:
 
     def __init__(self, verify_chunk: int = 0, draft_chunk: int = 0, num_cus: int = 0,
                  overlap: bool = False, side_stream: Optional[torch.cuda.Stream] = None,
-                 timing: Optional[dict] = None):
+                 timing: Optional[dict] = None, page_table_rows=None,
+                 page_table_row_count: int = 0):
         self.c = SpaOptions()
+        if page_table_rows is not None:
+            self.rows = np.ascontiguousarray(page_table_rows, dtype=np.int32)
+            self.c.page_table_rows = self.rows.ctypes.data
+            self.c.page_table_row_count = int(page_table_row_count)
         self.c.verify_chunk = int(verify_chunk)
         self.c.draft_chunk = int(draft_chunk)
         self.c.num_cus = int(num_cus)
@@ -485,3 +536,75 @@ class StepBuffers:
         _check(load().spa_unified_step(*self._marshal(), *self.plans.next_args(),
                                        _opts(self.opts if opts is None else opts),
                                        _stream(self.batch.q)))
+
+
+# --------------------------------------------------------------------------- #
+# the scheduler of include/spa_sched.h
+# --------------------------------------------------------------------------- #
+class Scheduler:
+    """Phase buckets and delayed verification over ``slots`` batch slots; the
+    state lives in a host buffer owned here.  next() plans a step (numpy views
+    of the scheduler's arrays, valid until the following call), commit()
+    applies it."""
+
+    def __init__(self, slots, spec_k, num_qo_heads, num_kv_heads, sparsity, prompt, output,
+                 max_len, delayed=False, accept_prob=ACCEPT_PROB_6_16_OF_8, seed=0):
+        from fractions import Fraction
+        s = Fraction(str(sparsity)) if isinstance(sparsity, float) else Fraction(sparsity)
+        self.cfg = SpaSchedConfig(int(slots), int(spec_k), 1 if delayed else 0, int(num_qo_heads),
+                                  int(num_kv_heads), s.numerator, s.denominator, int(prompt[0]),
+                                  int(prompt[1]), int(output[0]), int(output[1]), int(max_len),
+                                  float(accept_prob), int(seed))
+        lib = load()
+        n = lib.spa_sched_bytes(C.byref(self.cfg))
+        if n == 0:
+            raise SpaError(SPA_ERR_INVALID_ARG, lib.spa_last_error().decode())
+        raw = np.zeros(n + 64, np.uint8)
+        skip = (-raw.ctypes.data) % 64
+        self._raw = raw
+        self.state = raw[skip:skip + n]
+        self.ptr = C.c_void_p(self.state.ctypes.data)
+        _check(lib.spa_sched_init(self.ptr, n, C.byref(self.cfg)))
+        ie, le, rw = C.c_int64(), C.c_int64(), C.c_int32()
+        _check(lib.spa_sched_capacity(C.byref(self.cfg), C.byref(ie), C.byref(le), C.byref(rw)))
+        self.idx_elems, self.logits_elems, self.max_rows = int(ie.value), int(le.value), int(rw.value)
+        self.cycle = int(spec_k) + 1 + (1 if delayed else 0)
+        self.step_c = SpaSchedStep()
+
+    def next(self) -> SpaSchedStep:
+        """Plans the next step; returns the step record (ctypes, pointers into the state)."""
+        _check(load().spa_sched_next(self.ptr, C.byref(self.step_c)))
+        return self.step_c
+
+    def commit(self):
+        _check(load().spa_sched_commit(self.ptr))
+
+    def stats(self) -> dict:
+        st = SpaSchedStats()
+        _check(load().spa_sched_stats_read(self.ptr, C.byref(st)))
+        return {n: int(getattr(st, n)) for n, _ in SpaSchedStats._fields_}
+
+    def buckets(self) -> np.ndarray:
+        out = np.zeros(self.cycle, np.int32)
+        _check(load().spa_sched_buckets(self.ptr, out.ctypes.data_as(C.POINTER(C.c_int32)),
+                                        self.cycle))
+        return out
+
+    @staticmethod
+    def view(ptr, n, dtype):
+        """numpy copy-free view of n elements of a scheduler array."""
+        if n == 0:
+            return np.zeros(0, dtype)
+        ct = {np.uint8: C.c_uint8, np.int32: C.c_int32, np.int64: C.c_int64}[dtype]
+        return np.ctypeslib.as_array(C.cast(ptr, C.POINTER(ct)), shape=(n,))
+
+    def arrays(self, st: SpaSchedStep) -> dict:
+        """The step's arrays as numpy views."""
+        v = self.view
+        return {"is_verify": v(st.is_verify, st.B, np.uint8), "seq_lens": v(st.seq_lens, st.B, np.int32),
+                "q_indptr": v(st.q_indptr, st.B + 1, np.int32),
+                "idx_count": v(st.idx_count, st.B, np.int32), "idx_off": v(st.idx_off, st.B, np.int64),
+                "logits_off": v(st.logits_off, st.B, np.int64), "slot": v(st.slot, st.B, np.int32),
+                "new_slots": v(st.new_slots, st.n_new, np.int32),
+                "new_len": v(st.new_len, st.n_new, np.int32),
+                "new_count": v(st.new_count, st.n_new, np.int32)}

@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libspa.so")
-SOURCES = ["api.cpp", "kernels.hip"]
+SOURCES = ["api.cpp", "kernels.hip", "sched.cpp"]
 ARCH = os.environ.get("SPA_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

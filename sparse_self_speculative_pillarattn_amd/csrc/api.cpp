@@ -24,14 +24,22 @@
 #include <vector>
 
 #include "spa.h"
+#include "spa_error.h"
 #include "spa_kernels.h"
 #include "spa_plan.h"
 
 using namespace spa;
 
 namespace {
-
 thread_local std::string g_err;
+}  // namespace
+
+int32_t spa::set_error(int32_t code, const std::string& msg) {
+  g_err = msg;
+  return code;
+}
+
+namespace {
 
 constexpr int DEFAULT_VERIFY_CHUNK = 2048;  // fewer split-K partials
 constexpr int MIN_AUTO_VERIFY_CHUNK = 512;
@@ -47,6 +55,7 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct Req {
   int32_t L = 0;
+  int32_t pt_row = 0;  // page-table row
   bool verify = false;
   int32_t row0 = 0;
   int32_t nlist = 0;  // draft: entries per KV head; verify: K_r
@@ -102,6 +111,8 @@ struct Opts {
   hipStream_t side = nullptr;
   hipEvent_t fork = nullptr, join = nullptr;
   hipEvent_t timing[8] = {};
+  const int32_t* pt_rows = nullptr;  // page-table row of each request (null: row r)
+  int32_t pt_row_count = 0;
 };
 
 int32_t check_opts(const spa_options* o, Opts* out) {
@@ -120,6 +131,25 @@ int32_t check_opts(const spa_options* o, Opts* out) {
   out->fork = static_cast<hipEvent_t>(o->fork_event);
   out->join = static_cast<hipEvent_t>(o->join_event);
   for (int i = 0; i < 8; ++i) out->timing[i] = static_cast<hipEvent_t>(o->timing[i]);
+  out->pt_rows = o->page_table_rows;
+  out->pt_row_count = o->page_table_row_count;
+  if (out->pt_rows && out->pt_row_count < 1)
+    return fail(SPA_ERR_INVALID_ARG, "options: page_table_row_count must be positive");
+  return SPA_OK;
+}
+
+
+
+// Page-table row of each request: options.page_table_rows[r] (checked
+// against the row count) or r.
+int32_t apply_pt_rows(const Opts& o, std::vector<Req>* rq) {
+  for (size_t r = 0; r < rq->size(); ++r) {
+    const int32_t x = o.pt_rows ? o.pt_rows[r] : (int32_t)r;
+    if (o.pt_rows && (x < 0 || x >= o.pt_row_count))
+      return fail(SPA_ERR_INVALID_ARG, "options: page_table_rows[" + std::to_string(r) +
+                                           "] outside [0, " + std::to_string(o.pt_row_count) + ")");
+    (*rq)[r].pt_row = x;
+  }
   return SPA_OK;
 }
 
@@ -374,7 +404,7 @@ void plan_write(const Shape& s, const std::vector<Req>& rq, const Plan& pl, char
         Item it;
         std::memset(&it, 0, sizeof it);
         it.kind = v ? KIND_VERIFY : KIND_DRAFT;
-        it.r = r;
+        it.r = q.pt_row;
         it.g = g;
         it.L = q.L;
         it.row0 = q.row0;
@@ -912,6 +942,8 @@ int32_t spa_verify_attn(const spa_layout* layout, int32_t B, int32_t spec_k,
   rc = collect(s, B, ver.data(), h_seq_lens, nullptr, nullptr, nullptr, h_logits_off, true, false,
                &rq);
   if (rc) return rc;
+  rc = apply_pt_rows(o, &rq);
+  if (rc) return rc;
   Plan pl;
   rc = plan_size(s, rq, true, false, o, &pl);
   if (rc) return rc;
@@ -990,6 +1022,8 @@ int32_t spa_draft_attn(const spa_layout* layout, int32_t B, const int32_t* h_seq
   rc = collect(s, B, nullptr, h_seq_lens, nullptr, h_idx_count, h_idx_off, nullptr, false, true,
                &rq);
   if (rc) return rc;
+  rc = apply_pt_rows(o, &rq);
+  if (rc) return rc;
   Plan pl;
   rc = plan_size(s, rq, true, false, o, &pl);
   if (rc) return rc;
@@ -1036,6 +1070,8 @@ int32_t spa_unified_step(const spa_layout* layout, int32_t B, int32_t spec_k,
   std::vector<Req> rq;
   rc = collect(s, B, h_is_verify, h_seq_lens, h_q_indptr, h_idx_count, h_idx_off, h_logits_off,
                any_v, true, &rq);
+  if (rc) return rc;
+  rc = apply_pt_rows(o, &rq);
   if (rc) return rc;
   Plan pl;
   rc = plan_size(s, rq, true, true, o, &pl);

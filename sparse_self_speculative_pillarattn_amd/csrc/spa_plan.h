@@ -16,7 +16,7 @@ enum : int32_t {
 // One attention work item (64 bytes): KV head g of request r.
 struct Item {
   int32_t kind;
-  int32_t r;
+  int32_t r;          // the request's page-table row
   int32_t g;
   int32_t qi;         // fp32 verify items: the single query row handled
   int32_t begin;      // positions (verify) or list entries (draft)

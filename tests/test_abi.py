@@ -22,17 +22,36 @@ def lib():
     return bd.load()
 
 
-def declared_symbols():
-    src = open(os.path.join(ROOT, "include", "spa.h")).read()
+def declared_symbols(header="spa.h"):
+    src = open(os.path.join(ROOT, "include", header)).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     return sorted(set(re.findall(r"\b(spa_[a-z_]+)\s*\(", src)))
 
 
-def test_exports_every_declared_symbol(lib):
-    names = declared_symbols()
-    assert set(names) == set(bd.EXPORTED), names
+@pytest.mark.parametrize("header,exported", [("spa.h", bd.EXPORTED),
+                                             ("spa_sched.h", bd.SCHED_EXPORTED)])
+def test_exports_every_declared_symbol(lib, header, exported):
+    names = declared_symbols(header)
+    assert set(names) == set(exported), names
     for n in names:
         assert hasattr(lib, n), n
+
+
+def test_scheduler_structs_match_the_header():
+    """Field counts and sizes of the ctypes mirrors of include/spa_sched.h."""
+    src = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "spa_sched.h")).read(),
+                 flags=re.S)
+    for name, cls in (("spa_sched_config", bd.SpaSchedConfig), ("spa_sched_step", bd.SpaSchedStep),
+                      ("spa_sched_stats", bd.SpaSchedStats)):
+        body = re.search(r"typedef struct \{([^{}]*)\}\s*" + name + ";", src, flags=re.S).group(1)
+        fields = []
+        for decl in body.split(";"):
+            decl = decl.strip()
+            if decl:
+                fields += [f.strip().lstrip("*") for f in decl.split(None, 1)[1].split(",")]
+        if name == "spa_sched_step":  # pointer declarators carry the type's const
+            fields = [f.split()[-1].lstrip("*") for f in fields]
+        assert [f for f, _ in cls._fields_] == fields, name
 
 
 def test_abi_version(lib):
@@ -82,6 +101,17 @@ def test_empty_batch_is_a_noop(lib):
     assert _unified(lib, _lay(), B=0, ws_bytes=0) == bd.SPA_OK
 
 
+_PT_KEEP = []
+
+
+def _pt_rows(rows, count):
+    """Options that map request r to page-table row rows[r] (of `count`)."""
+    a = np.asarray(rows, np.int32)
+    _PT_KEEP.append(a)
+    return bd.SpaOptions(page_table_rows=a.ctypes.data,
+                         page_table_row_count=count)
+
+
 @pytest.mark.parametrize("kw,code", [
     (dict(lay=dict(num_qo_heads=6, num_kv_heads=4)), bd.SPA_ERR_INVALID_ARG),
     (dict(lay=dict(num_kv_heads=0)), bd.SPA_ERR_INVALID_ARG),
@@ -114,6 +144,9 @@ def test_empty_batch_is_a_noop(lib):
     (dict(opts=bd.SpaOptions(draft_chunk=2049)), bd.SPA_ERR_INVALID_ARG),
     (dict(opts=bd.SpaOptions(num_cus=-4)), bd.SPA_ERR_INVALID_ARG),
     (dict(opts=bd.SpaOptions(overlap=1)), bd.SPA_ERR_INVALID_ARG),  # no side stream or events
+    (dict(opts=_pt_rows((0, 2), 2)), bd.SPA_ERR_INVALID_ARG),       # row index past the count
+    (dict(opts=_pt_rows((-1, 0), 2)), bd.SPA_ERR_INVALID_ARG),      # negative row index
+    (dict(opts=_pt_rows((0, 1), 0)), bd.SPA_ERR_INVALID_ARG),       # rows given, count 0
     (dict(lay=dict(num_qo_heads=192, num_kv_heads=8), ioff=(0, 100)),
      bd.SPA_ERR_UNSUPPORTED),  # (k+1) G = 120 rows exceed the 112-row MFMA budget
 ])
