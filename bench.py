@@ -434,6 +434,39 @@ def quality_measure(w, dev, steps: int, warmup: int, top_t: int):
     print(json.dumps(out), flush=True)
 
 
+def stride_quality_measure(w, dev, sigmas, top_t: int = 10, n_req=None):
+    """The verify's PillarAttn lists against the k drafts of the following
+    stride (stride_quality.StrideRun): per stride position i = 1..k, the
+    mean and 10th percentile over (request, query head) of attention coverage
+    and recall@top_t, for the verify's lists and for a fresh top-K of each
+    draft row (same K), at each query drift sigma."""
+    from sparse_self_speculative_pillarattn_amd.stride_quality import StrideRun
+    b, vlens = synth.stride_batch(w, device=dev, n_req=n_req)
+    out = {"stride_quality": w.name, "requests": b.B, "spec_k": w.spec_k,
+           "sparsity": str(w.sparsity), "top_t": top_t, "mean_L": round(float(np.mean(vlens)), 1),
+           "sigmas": {}}
+
+    def stats(x):
+        x = x.flatten().float()
+        return {"mean": round(float(x.mean()), 4), "p10": round(float(torch.quantile(x, 0.1)), 4)}
+
+    for sigma in sigmas:
+        print(f"[bench] stride quality {w.name} sigma={sigma}", file=sys.stderr, flush=True)
+        res = StrideRun(b, vlens, sigma, seed=w.seed, top_t=top_t).run()
+        per = []
+        for i in sorted(res):
+            row = {"i": i}
+            for kind in ("pillar", "fresh"):
+                cov, rec = res[i][kind]
+                row[kind] = {"coverage": stats(cov), f"recall@{top_t}": stats(rec)}
+            per.append(row)
+        out["sigmas"][str(sigma)] = {"cos_q_i_vs_verify_row_k": [
+            round(1.0 / float(np.sqrt(1 + i * sigma * sigma)), 4) for i in range(1, w.spec_k + 1)],
+            "positions": per}
+        torch.cuda.empty_cache()
+    print(json.dumps(out), flush=True)
+
+
 def per_call(w, dev, n: int):
     """The first n calls on a freshly generated batch, each bracketed by its
     own events (whole call, and the attention, post-pass and selection
@@ -618,6 +651,11 @@ def main():
                     help="only run decode steps under the phase-bucket scheduler (plain and/or "
                          "delayed verification; --steps timed after --warmup) and print their "
                          "JSON line")
+    ap.add_argument("--stride-quality", type=float, nargs="+", default=None, metavar="SIGMA",
+                    help="only measure the verify's PillarAttn lists against the next k drafts "
+                         "(queries drifting by SIGMA per step) and print the JSON line")
+    ap.add_argument("--stride-requests", type=int, default=None,
+                    help="with --stride-quality: the first N requests of the workload")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 5 plain device copies of MIB MiB (reference for the HBM "
                          "byte counters) and exit")
@@ -661,6 +699,9 @@ def main():
         return
     if args.clock_ramp:
         clock_ramp(w, dev)
+        return
+    if args.stride_quality:
+        stride_quality_measure(w, dev, args.stride_quality, n_req=args.stride_requests)
         return
     if args.scheduler:
         modes = ("plain", "delayed") if args.scheduler == "both" else (args.scheduler,)

@@ -354,3 +354,42 @@ def uniform_batch(w: Workload, B: int, L: int, verify_mask: list, device="cpu",
     from dataclasses import replace
     w2 = replace(w, batch=B, lengths=("fixed", L))
     return make_batch(w2, device=device, seed=seed, is_verify=verify_mask)
+
+
+def stride_batch(w: Workload, device="cpu", seed: Optional[int] = None,
+                 n_req: Optional[int] = None) -> tuple:
+    """Inputs of one speculation stride: a batch whose requests all verify
+    (k+1 rows each) at context L_r, with K/V and page-table entries for L_r + k
+    positions, so that the k drafts after the verify (contexts L_r + 1 ..
+    L_r + k) read positions the pool holds.  Lengths, pool, Q, K, V and pillar
+    planting follow ``make_batch`` (pillars are drawn over [0, L_r + k) and
+    point along the verify rows' mean query direction); ``n_req`` takes the
+    first n_req requests of the workload's length draw.  Returns (batch over
+    L_r + k, [L_r]): the verify runs with the shorter lengths."""
+    from dataclasses import replace
+    seed = w.seed if seed is None else seed
+    lens = make_meta(w, seed).seq_lens
+    if n_req is not None:
+        lens = lens[:n_req]
+    B, k = len(lens), w.spec_k
+    lens = [max(L, k + 1) for L in lens]
+    w2 = replace(w, batch=B)
+    b = make_batch(w2, device=device, seed=seed, seq_lens=[L + k for L in lens],
+                   is_verify=[True] * B)
+    return b, lens
+
+
+def drift_queries(q0: torch.Tensor, steps: int, sigma: float, seed: int) -> torch.Tensor:
+    """Draft queries that drift away from q0 [B][H_q][d] over ``steps`` decode
+    steps: a seeded random walk, q_i = (q0 + sigma * (e_1 + ... + e_i)) /
+    sqrt(1 + i sigma^2) with e_j ~ N(0, 1) i.i.d., so q_i keeps q0's per-entry
+    variance and cos(q0, q_i) is about 1 / sqrt(1 + i sigma^2).  Returns
+    [steps][B][H_q][d] in q0's dtype (computed in fp32)."""
+    g = torch.Generator(device=q0.device).manual_seed(int(seed) * 104729 + 3)
+    base = q0.float()
+    walk = torch.zeros_like(base)
+    out = []
+    for i in range(1, steps + 1):
+        walk += torch.randn(base.shape, generator=g, device=q0.device, dtype=torch.float32)
+        out.append(((base + sigma * walk) / math.sqrt(1.0 + i * sigma * sigma)).to(q0.dtype))
+    return torch.stack(out)

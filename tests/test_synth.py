@@ -117,3 +117,34 @@ def test_step_equals_per_request_calls(oracle):
             o, lse = oracle.draft_request(q[r0], kp, vp, pt[r, :L], L, lst, 2, inp["sm_scale"])
             assert np.array_equal(res["o"][r0], o)
             assert np.array_equal(res["lse"][r0], lse)
+
+
+def test_stride_batch_holds_the_stride():
+    """Every request verifies at L_r with K/V for L_r + k positions."""
+    w = synth.Workload(name="stride", batch=5, num_qo_heads=8, num_kv_heads=2, head_dim=64,
+                       dtype="bf16", spec_k=4, sparsity=Fraction(1, 10),
+                       lengths=("uniform", 3, 400), seed=3)
+    b, vlens = synth.stride_batch(w)
+    assert b.B == 5 and all(b.is_verify)
+    assert [L + 4 for L in vlens] == b.seq_lens and min(vlens) >= 5
+    assert b.q.shape == (5 * 5, 8, 64)
+    b2, v2 = synth.stride_batch(w, n_req=2)
+    assert v2 == vlens[:2] and b2.B == 2
+
+
+@pytest.mark.parametrize("sigma", [0.0, 0.3, 1.0])
+def test_drift_queries_walk_away_at_the_stated_rate(sigma):
+    """q_i keeps unit per-entry variance, cos(q0, q_i) follows
+    1 / sqrt(1 + i sigma^2), and the draw is seeded."""
+    g = torch.Generator().manual_seed(0)
+    q0 = torch.randn((64, 8, 128), generator=g)
+    q = synth.drift_queries(q0, 6, sigma, seed=2)
+    assert q.shape == (6, 64, 8, 128) and q.dtype == q0.dtype
+    assert torch.equal(q, synth.drift_queries(q0, 6, sigma, seed=2))
+    for i in range(1, 7):
+        qi = q[i - 1].flatten()
+        cos = float(q0.flatten() @ qi / (q0.norm() * qi.norm()))
+        assert abs(cos - 1 / np.sqrt(1 + i * sigma * sigma)) < 0.02, (i, cos)
+        assert abs(float(qi.std()) - 1.0) < 0.02
+    if sigma == 0.0:
+        assert torch.equal(q[3], q0)
