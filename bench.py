@@ -105,12 +105,17 @@ def mfma_flops(b) -> dict:
 # --------------------------------------------------------------------------- #
 # counter-based traffic, valid only for the kernel source it was taken on
 # --------------------------------------------------------------------------- #
+# the sources that decide what the step's kernels do and move: the kernels,
+# their parameter and plan layouts, and the host planning in api.cpp (the
+# scheduler and the bandwidth probe are left out)
+STEP_SOURCES = ("api.cpp", "kernels.hip", "spa_kernels.h", "spa_plan.h")
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
-        if name.endswith((".hip", ".h", ".cpp")):
-            with open(os.path.join(CSRC, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+    for name in STEP_SOURCES:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
 
 
@@ -467,6 +472,93 @@ def stride_quality_measure(w, dev, sigmas, top_t: int = 10, n_req=None):
     print(json.dumps(out), flush=True)
 
 
+def _mix_setup(w):
+    """Tiles, stores per tile and pool size of the workload's attention launch
+    for the probe (include/spa_probe.h)."""
+    meta = synth.make_meta(w)
+    Hkv = w.num_kv_heads
+    chunks = 0
+    for r in range(w.batch):
+        n = meta.seq_lens[r] if meta.is_verify[r] else meta.idx_count[r]
+        chunks += Hkv * (-(-n // 32))
+    logits_bytes = sum((w.spec_k + 1) * w.num_qo_heads * meta.seq_lens[r] * 4
+                       for r in range(w.batch) if meta.is_verify[r])
+    wbytes = min(4096, (logits_bytes // chunks) // 16 * 16)
+    return meta, chunks, wbytes
+
+
+def mix_ceiling(w, dev, mixes, configs, reps: int = 20, settle: bool = True) -> dict:
+    """Runs the probe over `mixes` (name -> (scattered, with_stores)) and
+    `configs` ((depth, workgroups) pairs); returns per mix every run and the
+    best."""
+    assert w.head_dim == 128 and w.dtype == "bf16", "the probe replays 256-byte bf16 rows"
+    meta, chunks, wbytes = _mix_setup(w)
+    Hkv, nslots = w.num_kv_heads, meta.num_slots
+    pool_bytes = nslots * Hkv * 256
+    read_bytes = chunks * 2 * 32 * 256
+    kp = torch.empty((pool_bytes,), dtype=torch.uint8, device=dev)
+    vp = torch.empty_like(kp)
+    out = torch.empty((max(wbytes, 16) * chunks,), dtype=torch.uint8, device=dev)
+    sink = torch.zeros((4,), dtype=torch.int32, device=dev)
+    if settle:  # loaded clocks first (see the settling copies of the main measurement)
+        src = torch.empty((1 << 30,), dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(150):
+            dst.copy_(src)
+        del src, dst
+    res = {"tiles": chunks, "pool_bytes_each": pool_bytes, "read_bytes": read_bytes,
+           "write_bytes_per_tile": wbytes, "write_bytes": wbytes * chunks, "reps": reps,
+           "mixes": {}}
+    for name, (rnd, stores) in mixes.items():
+        wb = wbytes if stores else 0
+        runs = []
+        for depth, grid in configs:
+            fn = lambda: bd.probe_ceiling(kp, vp, nslots, Hkv, chunks, rnd, depth,
+                                          out if wb else None, wb, grid, sink)
+            for _ in range(3):
+                fn()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / reps
+            runs.append({"depth": depth, "grid": grid, "us": round(us, 1),
+                         "GB_s": round((read_bytes + wb * chunks) / (us * 1e-6) / 1e9, 1)})
+        best = max(runs, key=lambda x: x["GB_s"])
+        res["mixes"][name] = {"best": best, "frac_of_peak": round(best["GB_s"] / HBM_PEAK_GBPS, 4),
+                              "runs": runs}
+    del kp, vp, out
+    torch.cuda.empty_cache()
+    return res
+
+
+MIXES = {"launch_mix": (True, True), "scattered_reads": (True, False),
+         "sequential_mix": (False, True), "sequential_reads": (False, False)}
+
+
+def ceiling_measure(w, dev, reps: int = 20):
+    """Attainable bandwidth of the attention launch's own access mix
+    (include/spa_probe.h): the workload's (request, KV head) tiles of 32
+    positions, each reading the K and V rows (256 bytes each, non-temporal) of
+    32 slots of a pool the workload's size, plus dependent sequential stores
+    of the verify logits' total spread over the tiles (the launch's
+    read:write ratio).  Four mixes -- scattered or consecutive slots, with or
+    without the stores -- at 1, 2 and 4 tiles in flight per workgroup and
+    1024 to 4096 workgroups; the best of each mix is its ceiling."""
+    from types import SimpleNamespace
+    meta, chunks, wbytes = _mix_setup(w)
+    print(f"[bench] ceiling {w.name}: {chunks} tiles, {wbytes} B stored per tile",
+          file=sys.stderr, flush=True)
+    configs = [(d, g) for d in (1, 2, 4) for g in (1024, 2048, 4096)]
+    res = {"ceiling": w.name, **mix_ceiling(w, dev, MIXES, configs, reps)}
+    alg = algorithmic_bytes(SimpleNamespace(w=w, B=w.batch, is_verify=meta.is_verify,
+                                            seq_lens=meta.seq_lens, idx_count=meta.idx_count))
+    res["attn_launch_algorithmic_bytes"] = alg["attn_launch"]
+    print(json.dumps(res), flush=True)
+
+
 def per_call(w, dev, n: int):
     """The first n calls on a freshly generated batch, each bracketed by its
     own events (whole call, and the attention, post-pass and selection
@@ -630,6 +722,8 @@ def main():
     ap.add_argument("--cpu-repeats", type=int, default=15,
                     help="oracle runs of the whole step (about 0.8 s each on 16 EPYC cores)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the access-mix ceiling measurement of the main line")
     ap.add_argument("--sparsity-sweep", action="store_true",
                     help="only run the draft-only sparsity sweep and print its JSON line")
     ap.add_argument("--unified-vs-sequential", action="store_true",
@@ -656,6 +750,9 @@ def main():
                          "(queries drifting by SIGMA per step) and print the JSON line")
     ap.add_argument("--stride-requests", type=int, default=None,
                     help="with --stride-quality: the first N requests of the workload")
+    ap.add_argument("--ceiling", action="store_true",
+                    help="only measure the attainable bandwidth of the attention launch's access "
+                         "mix (libspa_probe) on the workload and print its JSON line")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 5 plain device copies of MIB MiB (reference for the HBM "
                          "byte counters) and exit")
@@ -699,6 +796,9 @@ def main():
         return
     if args.clock_ramp:
         clock_ramp(w, dev)
+        return
+    if args.ceiling:
+        ceiling_measure(w, dev)
         return
     if args.stride_quality:
         stride_quality_measure(w, dev, args.stride_quality, n_req=args.stride_requests)
@@ -804,6 +904,18 @@ def main():
                 "counters": recorded_mfma(w.name),
                 "counters_source": f"profiles/attn_kernel_{w.name}_mfma.md (recorded)"}
 
+    # the attainable bandwidth of the launch's own access mix on this device,
+    # measured now (libspa_probe; the two best settings of the full sweep)
+    ceiling = None
+    if w.dtype == "bf16" and w.head_dim == 128 and not args.no_ceiling:
+        print("[bench] measuring the access-mix ceiling", file=sys.stderr, flush=True)
+        cres = mix_ceiling(w, dev, {"launch_mix": MIXES["launch_mix"]}, [(4, 4096), (2, 4096)],
+                           settle=False)
+        cbest = cres["mixes"]["launch_mix"]["best"]
+        ceiling = {"mix": "launch_mix", "GB_s": cbest["GB_s"], "depth": cbest["depth"],
+                   "workgroups": cbest["grid"], "tiles": cres["tiles"],
+                   "bytes": cres["read_bytes"] + cres["write_bytes"]}
+
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on host cores", file=sys.stderr, flush=True)
@@ -850,7 +962,12 @@ def main():
                      # the bytes the launch really moves (counted), per second
                      "traffic_gbps": round(traffic / (attn_us * 1e-6) / 1e9, 1) if traffic else None,
                      "algorithmic_bytes_per_launch": attn_bytes,
-                     "launch_us": round(attn_us, 2), "launches": args.steps},
+                     "launch_us": round(attn_us, 2), "launches": args.steps,
+                     # the same achieved rate against what this device attains for
+                     # the launch's access mix (scattered 256-byte KV rows plus
+                     # the logits stores, no arithmetic), measured in this run
+                     "mix_ceiling": ceiling,
+                     "frac_of_mix_ceiling": round(attn_gbps / ceiling["GB_s"], 4) if ceiling else None},
         "mfma": mfma,
         "cpu_baseline": cpu,
         "env": {"device": torch.cuda.get_device_name(dev),

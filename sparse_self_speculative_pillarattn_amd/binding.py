@@ -451,6 +451,36 @@ def list_quality(B, spec_k, num_qo_heads, num_kv_heads, row, top_t, seq_lens, lo
         _stream(logits)))
 
 
+_probe = None
+PROBE_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libspa_probe.so")
+
+
+def load_probe():
+    """libspa_probe.so (include/spa_probe.h); raises if it was not built."""
+    global _probe
+    if _probe is None:
+        if not os.path.exists(PROBE_LIB_PATH):
+            raise RuntimeError(f"{PROBE_LIB_PATH} is missing: run "
+                               "`python -m sparse_self_speculative_pillarattn_amd.build`")
+        lib = C.CDLL(PROBE_LIB_PATH)
+        vp, i32, i64 = C.c_void_p, C.c_int32, C.c_int64
+        lib.spa_probe_ceiling.argtypes = [vp, vp, i64, i32, i64, i32, i32, vp, i64, i32, i32, vp, vp]
+        lib.spa_probe_ceiling.restype = i32
+        _probe = lib
+    return _probe
+
+
+def probe_ceiling(k_pool, v_pool, num_slots, num_kv_heads, chunks, random, depth, out,
+                  write_bytes_per_chunk, grid, sink):
+    rc = load_probe().spa_probe_ceiling(
+        _dptr(k_pool), _dptr(v_pool), int(num_slots), int(num_kv_heads), int(chunks),
+        1 if random else 0, int(depth), _dptr(out), 0 if out is None else _nbytes(out),
+        int(write_bytes_per_chunk), int(grid), _dptr(sink), _stream(k_pool))
+    if rc:
+        raise SpaError(SPA_ERR_INVALID_ARG if rc == 1 else SPA_ERR_HIP,
+                       f"spa_probe_ceiling failed ({rc})")
+
+
 class PlanRing:
     """A few pinned plan buffers used in turn, so the host can queue that many
     calls ahead of the GPU (a call waits only for the buffer's previous use)."""

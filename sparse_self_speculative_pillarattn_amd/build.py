@@ -1,4 +1,4 @@
-"""Build libspa.so (HIP, gfx950) in-tree with hipcc.
+"""Build libspa.so and libspa_probe.so (HIP, gfx950) in-tree with hipcc.
 
     python -m sparse_self_speculative_pillarattn_amd.build
 
@@ -20,6 +20,9 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libspa.so")
 SOURCES = ["api.cpp", "kernels.hip", "sched.cpp"]
+# the bandwidth probe of include/spa_probe.h: a library of its own
+PROBE_LIB = os.path.join(PKG, "libspa_probe.so")
+PROBE_SOURCES = ["probe.hip"]
 ARCH = os.environ.get("SPA_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -44,18 +47,25 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib):
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("link failed:\n" + res.stderr)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    with ThreadPoolExecutor(max_workers=len(srcs)) as ex:
+        objs = dict(zip(srcs, ex.map(_compile, srcs)))
+    _link([objs[s] for s in SOURCES], LIB)
+    _link([objs[s] for s in PROBE_SOURCES], PROBE_LIB)
     if verbose:
         print(LIB)
+        print(PROBE_LIB)
     return LIB
 
 

@@ -384,3 +384,24 @@ def test_list_quality_invalid_arguments(lib, kw, code):
 
 def test_list_quality_empty_batch_is_a_noop(lib):
     assert _quality(lib, B=0) == bd.SPA_OK
+
+
+def test_probe_library_exports_and_rejects():
+    """libspa_probe exports what include/spa_probe.h declares and rejects bad
+    arguments before launching anything."""
+    if not os.path.exists(bd.PROBE_LIB_PATH):
+        from sparse_self_speculative_pillarattn_amd import build
+        build.build()
+    lib = bd.load_probe()
+    assert declared_symbols("spa_probe.h") == ["spa_probe_ceiling"]
+    f = lib.spa_probe_ceiling
+    ok = dict(k=FAKE, v=FAKE, ns=1024, h=8, ch=10, rnd=1, dep=2, out=FAKE, ob=3200, wb=320,
+              grid=64, sink=FAKE)
+    for bad in (dict(k=None), dict(ns=0), dict(h=0), dict(ch=-1), dict(dep=3), dict(wb=8),
+                dict(wb=4112), dict(ob=3000), dict(out=None), dict(grid=0), dict(sink=None)):
+        a = dict(ok, **bad)
+        assert f(a["k"], a["v"], a["ns"], a["h"], a["ch"], a["rnd"], a["dep"], a["out"], a["ob"],
+                 a["wb"], a["grid"], a["sink"], None) == 1, bad
+    a = dict(ok, ch=0)  # nothing to do: returns before any launch
+    assert f(a["k"], a["v"], a["ns"], a["h"], a["ch"], a["rnd"], a["dep"], a["out"], a["ob"],
+             a["wb"], a["grid"], a["sink"], None) == 0
