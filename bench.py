@@ -559,6 +559,92 @@ def ceiling_measure(w, dev, reps: int = 20):
     print(json.dumps(res), flush=True)
 
 
+def offload_measure(w, dev, steps: int, warmup: int, mb_per_step=(0.52, 4.0, 18.9),
+                    block_slots: int = 64, concurrent_only: bool = False):
+    """Host-link traffic beside the step (include/spa_kvcache.h): per step,
+    KV blocks leave the device for pinned host chunks and as many come back,
+    on a copy stream, while the unified step runs back to back on the compute
+    stream.  X is the MB moved per step, both directions together: 18.9 MB is the new KV of one
+    decode step of the whole Qwen3-8B model at batch 128 (36 layers x 8 KV
+    heads x 128 x 2 (K, V) x 2 bytes x 128 requests), the pages' ~18 MB per
+    step; 0.52 MB is one layer's share of it.  Blocks of block_slots slots are
+    moved in consecutive runs (one copy per pool per run) and, for the worst
+    case, every other block (one copy per block).  Reports per X: the step
+    time alone and with the copies running, the copies' GB/s alone and beside
+    the step, and whether the copy stream kept up.  concurrent_only: only the
+    consecutive runs beside the steps (for a trace of the overlap)."""
+    b = synth.make_batch(w, device=dev)
+    bufs = bd.StepBuffers(b)
+    lay = bd.layout(w.num_qo_heads, w.num_kv_heads, w.head_dim, b.q.dtype, 4096 * block_slots,
+                    b.stride)
+    bb = bd.kv_block_bytes(lay, block_slots)
+    nblk = 4096
+    kp = torch.zeros((nblk * bb,), dtype=torch.uint8, device=dev)
+    vp = torch.zeros_like(kp)
+    ka = torch.zeros((nblk * bb,), dtype=torch.uint8, pin_memory=True)
+    va = torch.zeros_like(ka, pin_memory=True)
+    copy = torch.cuda.Stream(dev)
+    comp = torch.cuda.current_stream(dev)
+
+    def moves(i, n, scattered):
+        # step i's blocks: a window that walks through the pool; offload the
+        # first half, prefetch the second (different blocks and chunks)
+        step = 2 if scattered else 1
+        base = (i * 2 * n * step) % (nblk - 2 * n * step)
+        ids = base + np.arange(2 * n) * step
+        return ids[:n], ids[n:]
+
+    def copies(i, n, scattered):
+        off, pre = moves(i, n, scattered)
+        if len(off):
+            bd.kv_offload(lay, block_slots, off, off, kp, vp, ka, va, stream=copy)
+        if len(pre):
+            bd.kv_prefetch(lay, block_slots, pre, pre, ka, va, kp, vp, stream=copy)
+
+    def timed(with_steps, with_copies, n, scattered):
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        c1 = torch.cuda.Event(enable_timing=True)
+        e0.record(comp)
+        copy.wait_event(e0)
+        for i in range(steps):
+            if with_copies:
+                copies(i, n, scattered)
+            if with_steps:
+                bufs.step()
+        e1.record(comp)
+        c1.record(copy)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3, e0.elapsed_time(c1) * 1e3
+
+    for _ in range(warmup):
+        bufs.step()
+    copies(0, 4, False)
+    torch.cuda.synchronize()
+    base_us, _ = timed(True, False, 0, False)
+    out = {"offload": w.name, "block_slots": block_slots, "block_bytes_per_pool": bb,
+           "steps": steps, "step_us_alone": round(base_us / steps, 1), "runs": []}
+    for mb in mb_per_step:
+        # n blocks each way: 2 n blocks x 2 pools x bb bytes = mb * 1e6
+        n = max(1, int(round(mb * 1e6 / (4 * bb))))
+        moved = 4 * n * bb
+        for scattered in ((False,) if concurrent_only else (False, True)):
+            c_alone = float("nan") if concurrent_only else timed(False, True, n, scattered)[1]
+            t_both, c_both = timed(True, True, n, scattered)
+            out["runs"].append({
+                "mb_per_step": round(moved / 1e6, 3), "blocks_each_way": n,
+                "copies_per_step": 4 * (n if scattered else 1),
+                "runs": "scattered" if scattered else "consecutive",
+                "copy_gbps_alone": None if concurrent_only else
+                round(moved * steps / (c_alone * 1e-6) / 1e9, 1),
+                "step_us_with_copies": round(t_both / steps, 1),
+                "step_slowdown": round(t_both / base_us - 1, 4),
+                "copy_gbps_beside_steps": round(moved * steps / (c_both * 1e-6) / 1e9, 1),
+                "copies_kept_up": bool(c_both <= t_both * 1.02)})
+    print(json.dumps(out), flush=True)
+
+
 def per_call(w, dev, n: int):
     """The first n calls on a freshly generated batch, each bracketed by its
     own events (whole call, and the attention, post-pass and selection
@@ -753,6 +839,11 @@ def main():
     ap.add_argument("--ceiling", action="store_true",
                     help="only measure the attainable bandwidth of the attention launch's access "
                          "mix (libspa_probe) on the workload and print its JSON line")
+    ap.add_argument("--offload", type=float, nargs="*", default=None, metavar="MB",
+                    help="only measure host offload/prefetch copies of MB per step (default "
+                         "0.52 4 18.9) beside the step and print their JSON line")
+    ap.add_argument("--offload-concurrent-only", action="store_true",
+                    help="with --offload: only the consecutive-block runs beside the steps")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 5 plain device copies of MIB MiB (reference for the HBM "
                          "byte counters) and exit")
@@ -796,6 +887,10 @@ def main():
         return
     if args.clock_ramp:
         clock_ramp(w, dev)
+        return
+    if args.offload is not None:
+        offload_measure(w, dev, args.steps, args.warmup, tuple(args.offload) or (0.52, 4.0, 18.9),
+                        concurrent_only=args.offload_concurrent_only)
         return
     if args.ceiling:
         ceiling_measure(w, dev)

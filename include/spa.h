@@ -107,7 +107,8 @@ typedef enum {
   SPA_ERR_UNSUPPORTED = 2,         /* head_dim, dtype or row count not built       */
   SPA_ERR_WORKSPACE_TOO_SMALL = 3, /* ws_bytes < spa_workspace_bytes(...)          */
   SPA_ERR_HIP = 4,                 /* a HIP runtime call or launch failed          */
-  SPA_ERR_PLAN_TOO_SMALL = 5       /* plan_bytes < spa_plan_bytes(...)             */
+  SPA_ERR_PLAN_TOO_SMALL = 5,      /* plan_bytes < spa_plan_bytes(...)             */
+  SPA_ERR_KV_FULL = 6              /* spa_kvm_*: no free device block or host chunk */
 } spa_status;
 
 typedef enum { SPA_BF16 = 0, SPA_F32 = 1 } spa_dtype;

@@ -26,6 +26,7 @@ SPA_ERR_UNSUPPORTED = 2
 SPA_ERR_WORKSPACE_TOO_SMALL = 3
 SPA_ERR_HIP = 4
 SPA_ERR_PLAN_TOO_SMALL = 5
+SPA_ERR_KV_FULL = 6
 SPA_BF16 = 0
 SPA_F32 = 1
 ABI_VERSION = 2
@@ -40,6 +41,9 @@ EXPORTED = ("spa_abi_version", "spa_last_error", "spa_workspace_bytes", "spa_pla
 # include/spa_sched.h
 SCHED_EXPORTED = ("spa_sched_bytes", "spa_sched_capacity", "spa_sched_init", "spa_sched_next",
                   "spa_sched_commit", "spa_sched_stats_read", "spa_sched_buckets")
+KV_EXPORTED = ("spa_kv_block_bytes", "spa_kv_offload", "spa_kv_prefetch", "spa_kvm_bytes",
+               "spa_kvm_init", "spa_kvm_reserve", "spa_kvm_release", "spa_kvm_plan_offload",
+               "spa_kvm_plan_prefetch", "spa_kvm_page_row", "spa_kvm_where", "spa_kvm_stats_read")
 # per-token acceptance probability whose leading-run mean over k = 8 drafts is
 # 6.16 accepted tokens (the review's PillarAttn acceptance, 实验与结果)
 ACCEPT_PROB_6_16_OF_8 = 0.9415853644089122
@@ -88,6 +92,18 @@ class SpaSchedStep(C.Structure):
 class SpaSchedStats(C.Structure):
     _fields_ = [(n, C.c_int64) for n in ("steps", "verifies", "drafts", "waits", "drafted",
                                          "accepted", "committed", "retired", "rows")]
+
+
+class SpaKvmConfig(C.Structure):
+    _fields_ = [(n, C.c_int32) for n in ("dev_blocks", "host_chunks", "block_slots",
+                                         "max_requests", "max_blocks")]
+
+
+class SpaKvmStats(C.Structure):
+    _fields_ = ([(n, C.c_int32) for n in ("resident", "offloaded", "free_dev_blocks",
+                                          "free_host_chunks")] +
+                [(n, C.c_int64) for n in ("offloads", "prefetches", "blocks_offloaded",
+                                          "blocks_prefetched")])
 
 
 _lib = None
@@ -153,6 +169,32 @@ def load(path: str = LIB_PATH):
     lib.spa_sched_stats_read.restype = i32
     lib.spa_sched_buckets.argtypes = [vp, C.POINTER(C.c_int32), i32]
     lib.spa_sched_buckets.restype = i32
+    KC = C.POINTER(SpaKvmConfig)
+    pi = C.POINTER(C.c_int32)
+    lib.spa_kv_block_bytes.argtypes = [L, i32]
+    lib.spa_kv_block_bytes.restype = sz
+    lib.spa_kv_offload.argtypes = [L, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp, vp, vp]
+    lib.spa_kv_offload.restype = i32
+    lib.spa_kv_prefetch.argtypes = [L, i32, i32, vp, vp, vp, vp, sz, vp, vp, vp, vp, vp]
+    lib.spa_kv_prefetch.restype = i32
+    lib.spa_kvm_bytes.argtypes = [KC]
+    lib.spa_kvm_bytes.restype = sz
+    lib.spa_kvm_init.argtypes = [vp, sz, KC]
+    lib.spa_kvm_init.restype = i32
+    lib.spa_kvm_reserve.argtypes = [vp, i32, i32]
+    lib.spa_kvm_reserve.restype = i32
+    lib.spa_kvm_release.argtypes = [vp, i32]
+    lib.spa_kvm_release.restype = i32
+    lib.spa_kvm_plan_offload.argtypes = [vp, i32, vp, i32, i32, vp, vp, pi, vp, pi]
+    lib.spa_kvm_plan_offload.restype = i32
+    lib.spa_kvm_plan_prefetch.argtypes = [vp, i32, i32, vp, vp, pi, vp, pi]
+    lib.spa_kvm_plan_prefetch.restype = i32
+    lib.spa_kvm_page_row.argtypes = [vp, i32, i32, vp]
+    lib.spa_kvm_page_row.restype = i32
+    lib.spa_kvm_where.argtypes = [vp, i32]
+    lib.spa_kvm_where.restype = i32
+    lib.spa_kvm_stats_read.argtypes = [vp, C.POINTER(SpaKvmStats)]
+    lib.spa_kvm_stats_read.restype = i32
     _lib = lib
     return lib
 
@@ -190,9 +232,9 @@ def _dptr(t: Optional[torch.Tensor]):
 
 
 def _hptr(t: torch.Tensor):
-    """Address of a pinned host plan buffer."""
+    """Address of a pinned host buffer (plan buffer, KV arena)."""
     if t.is_cuda or not t.is_pinned():
-        raise ValueError("plan buffers must be pinned host tensors (plan_buffer)")
+        raise ValueError("plan buffers and KV arenas must be pinned host tensors")
     return C.c_void_p(t.data_ptr())
 
 
@@ -449,6 +491,120 @@ def list_quality(B, spec_k, num_qo_heads, num_kv_heads, row, top_t, seq_lens, lo
         h.arr(list_count, np.int32), h.arr(list_off, np.int64), _dptr(lists), _dptr(top),
         _dptr(coverage), _dptr(recall), _dptr(ws), _nbytes(ws), _hptr(plan), _nbytes(plan),
         _stream(logits)))
+
+
+def kv_block_bytes(lay: SpaLayout, block_slots: int) -> int:
+    return int(load().spa_kv_block_bytes(C.byref(lay), int(block_slots)))
+
+
+def _i32(a):
+    a = np.ascontiguousarray(np.asarray(a, np.int32))
+    return a, a.ctypes.data_as(C.c_void_p)
+
+
+def kv_offload(lay, block_slots, dev_blocks, host_chunks, k_pool, v_pool, k_arena, v_arena,
+               stream=None, wait_event=None, done_event=None):
+    """Device blocks -> host chunks of the pinned arenas, on `stream`
+    (a torch.cuda.Stream; None: the current stream)."""
+    b, bp = _i32(dev_blocks)
+    c, cp = _i32(host_chunks)
+    assert len(b) == len(c)
+    st = (stream or torch.cuda.current_stream(k_pool.device)).cuda_stream
+    _check(load().spa_kv_offload(
+        C.byref(lay), int(block_slots), len(b), bp, cp, _dptr(k_pool), _dptr(v_pool),
+        _hptr(k_arena), _hptr(v_arena), _nbytes(k_arena),
+        None if wait_event is None else C.c_void_p(wait_event.cuda_event),
+        None if done_event is None else C.c_void_p(done_event.cuda_event), C.c_void_p(st)))
+
+
+def kv_prefetch(lay, block_slots, host_chunks, dev_blocks, k_arena, v_arena, k_pool, v_pool,
+                stream=None, wait_event=None, done_event=None):
+    """Host chunks of the pinned arenas -> device blocks, on `stream`."""
+    c, cp = _i32(host_chunks)
+    b, bp = _i32(dev_blocks)
+    assert len(b) == len(c)
+    st = (stream or torch.cuda.current_stream(k_pool.device)).cuda_stream
+    _check(load().spa_kv_prefetch(
+        C.byref(lay), int(block_slots), len(b), cp, bp, _hptr(k_arena), _hptr(v_arena),
+        _nbytes(k_arena), _dptr(k_pool), _dptr(v_pool),
+        None if wait_event is None else C.c_void_p(wait_event.cuda_event),
+        None if done_event is None else C.c_void_p(done_event.cuda_event), C.c_void_p(st)))
+
+
+class KVManager:
+    """The block manager of include/spa_kvcache.h over a host state buffer
+    owned here."""
+
+    def __init__(self, dev_blocks, host_chunks, block_slots, max_requests, max_blocks):
+        self.cfg = SpaKvmConfig(int(dev_blocks), int(host_chunks), int(block_slots),
+                                int(max_requests), int(max_blocks))
+        lib = load()
+        n = lib.spa_kvm_bytes(C.byref(self.cfg))
+        if n == 0:
+            raise SpaError(SPA_ERR_INVALID_ARG, lib.spa_last_error().decode())
+        raw = np.zeros(n + 64, np.uint8)
+        skip = (-raw.ctypes.data) % 64
+        self._raw = raw
+        self.ptr = C.c_void_p(raw[skip:].ctypes.data)
+        _check(lib.spa_kvm_init(self.ptr, n, C.byref(self.cfg)))
+        R = int(max_requests)
+        self._reqs = np.zeros(R, np.int32)
+        self._cap = 0
+        self._a = self._b = np.zeros(0, np.int32)
+
+    def reserve(self, req, length) -> bool:
+        """True when the request now holds blocks for `length` positions;
+        False when the device blocks ran out (nothing changed)."""
+        rc = load().spa_kvm_reserve(self.ptr, int(req), int(length))
+        if rc == SPA_ERR_KV_FULL:
+            return False
+        _check(rc)
+        return True
+
+    def release(self, req):
+        _check(load().spa_kvm_release(self.ptr, int(req)))
+
+    def _moves(self, cap):
+        if cap > self._cap:
+            self._cap = cap
+            self._a = np.zeros(cap, np.int32)
+            self._b = np.zeros(cap, np.int32)
+        return self._a, self._b
+
+    def plan_offload(self, need_free, keep=(), cap=1 << 16):
+        """(dev_blocks, host_chunks, requests) to move off the device."""
+        a, b = self._moves(cap)
+        kp = np.ascontiguousarray(np.asarray(keep, np.int32))
+        nm, nr = C.c_int32(), C.c_int32()
+        _check(load().spa_kvm_plan_offload(
+            self.ptr, int(need_free), kp.ctypes.data_as(C.c_void_p) if kp.size else None,
+            int(kp.size), int(cap), a.ctypes.data_as(C.c_void_p), b.ctypes.data_as(C.c_void_p),
+            C.byref(nm), self._reqs.ctypes.data_as(C.c_void_p), C.byref(nr)))
+        return a[:nm.value].copy(), b[:nm.value].copy(), self._reqs[:nr.value].copy()
+
+    def plan_prefetch(self, keep_free=0, cap=1 << 16):
+        """(host_chunks, dev_blocks, requests) to bring back."""
+        a, b = self._moves(cap)
+        nm, nr = C.c_int32(), C.c_int32()
+        _check(load().spa_kvm_plan_prefetch(
+            self.ptr, int(keep_free), int(cap), a.ctypes.data_as(C.c_void_p),
+            b.ctypes.data_as(C.c_void_p), C.byref(nm), self._reqs.ctypes.data_as(C.c_void_p),
+            C.byref(nr)))
+        return a[:nm.value].copy(), b[:nm.value].copy(), self._reqs[:nr.value].copy()
+
+    def page_row(self, req, length) -> np.ndarray:
+        out = np.zeros(max(int(length), 1), np.int32)
+        _check(load().spa_kvm_page_row(self.ptr, int(req), int(length),
+                                       out.ctypes.data_as(C.c_void_p)))
+        return out[:int(length)]
+
+    def where(self, req) -> int:
+        return int(load().spa_kvm_where(self.ptr, int(req)))
+
+    def stats(self) -> dict:
+        st = SpaKvmStats()
+        _check(load().spa_kvm_stats_read(self.ptr, C.byref(st)))
+        return {n: int(getattr(st, n)) for n, _ in SpaKvmStats._fields_}
 
 
 _probe = None

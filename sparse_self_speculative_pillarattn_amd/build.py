@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libspa.so")
-SOURCES = ["api.cpp", "kernels.hip", "sched.cpp"]
+SOURCES = ["api.cpp", "kernels.hip", "sched.cpp", "kvcache.cpp"]
 # the bandwidth probe of include/spa_probe.h: a library of its own
 PROBE_LIB = os.path.join(PKG, "libspa_probe.so")
 PROBE_SOURCES = ["probe.hip"]

@@ -29,7 +29,8 @@ def declared_symbols(header="spa.h"):
 
 
 @pytest.mark.parametrize("header,exported", [("spa.h", bd.EXPORTED),
-                                             ("spa_sched.h", bd.SCHED_EXPORTED)])
+                                             ("spa_sched.h", bd.SCHED_EXPORTED),
+                                             ("spa_kvcache.h", bd.KV_EXPORTED)])
 def test_exports_every_declared_symbol(lib, header, exported):
     names = declared_symbols(header)
     assert set(names) == set(exported), names
