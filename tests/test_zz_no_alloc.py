@@ -50,8 +50,8 @@ def test_static_workspace_matches_caller_workspace(oracle):
         torch.cuda.synchronize()
         # the bar of the parity tests (tolerances; index lists exact) ...
         parity.assert_o(to_np(got["o"]), widen(to_np(want["o"])), w.dtype, "O")
-        parity.assert_lse_like(to_np(got["lse"]), to_np(want["lse"]), "LSE")
-        parity.assert_lse_like(to_np(got["logits"]), to_np(want["logits"]), "logits")
+        parity.assert_lse(to_np(got["lse"]), to_np(want["lse"]), "LSE")
+        parity.assert_logits(to_np(got["logits"]), to_np(want["logits"]), "logits")
         assert np.array_equal(to_np(got["idx"]), to_np(want["idx"])), "index lists differ"
         # ... and, since the two entry points run the same kernels on the same
         # plan, the same bits
