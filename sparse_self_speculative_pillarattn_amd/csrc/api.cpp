@@ -94,6 +94,7 @@ struct Plan {
   int max_sel_len = 0;  // longest selected row
   int64_t part_rows = 0;
   int64_t pbar_elems = 0;
+  int64_t avg_logit_bytes = 0;  // logits the verify requests dump, which the averaging reads back
   // pinned plan layout
   size_t h_items = 0, h_items_d = 0, h_post = 0, h_post_d = 0, h_sel = 0, h_bytes = 0;
   // workspace layout (work counters at offset 0)
@@ -308,6 +309,7 @@ int32_t plan_size(const Shape& s, const std::vector<Req>& rq, bool attn, bool to
     for (auto& q : rq)
       if (q.verify) {
         pl->n_avg += Hkv * avg_parts(q.L);
+        pl->avg_logit_bytes += (int64_t)q.L * s.Hq * 4 * (s.k + 1);
         pl->n_sel += Hkv;
         pl->max_sel_len = std::max(pl->max_sel_len, q.L);
         // the histogram is cleared by the attention launch, so only a call
@@ -722,6 +724,9 @@ int32_t run(const Shape& s, const std::vector<Req>& rq, const Plan& pl, const Bu
     pp.G = s.G;
     pp.avg_row_begin = avg_begin;
     pp.avg_row_count = avg_count;
+    // logits that the Infinity Cache can still hold when the post-pass reads
+    // them back: plain loads, which hit there; otherwise the streaming hint
+    pp.logits_cached = attn_st && pl.avg_logit_bytes <= LOGITS_CACHED_BYTES;
     // the attention launch before it read the pinned records last
     pp.done = attn_st ? pr.done_dev : nullptr;
     pp.done_val = pr.seq;
@@ -767,6 +772,7 @@ int32_t run(const Shape& s, const std::vector<Req>& rq, const Plan& pl, const Bu
       pp.G = s.G;
       pp.avg_row_begin = avg_begin;
       pp.avg_row_count = avg_count;
+      pp.logits_cached = false;
       pp.done = nullptr;
       pp.done_val = 0;
       pp.hist = nullptr;

@@ -1,16 +1,29 @@
 // kernels.hip -- device code of libspa for gfx950 (CDNA4).
 //
-// attn_kernel   one launch for all attention work of a batch.  Each workgroup
-//               takes one plan item: a verify item (request r, KV head g, a chunk
-//               of positions) runs the MFMA tile, a draft item (r, g, a chunk of
-//               its index list) runs the VALU gather tile.  Both kinds share the
-//               launch ("Unified batch scheduler + fused attention kernel",
-//               SparseSpec review).  Outputs are final when (r, g) is one chunk,
-//               split-K partials otherwise.  No workgroup waits for another.
-// post_kernel   the PillarAttn post-pass: split-K merges, and the exact scores
-//               exp(logit - LSE) averaged over the draft rows and the GQA group
-//               in position chunks; the last chunk of a verify (r, g) selects its
-//               top-K by a radix select (PillarAttn, SparseSpec review).
+// A unified step is up to three launches on the caller's stream (pages: the
+// SparseSpec review, 核心方法 -> PillarAttn and "Unified batch scheduler +
+// fused attention kernel"):
+// attn_kernel    persistent workgroups draw plan items from a ticket counter:
+//                a verify item (request r, KV head g, a chunk of positions) or a
+//                draft item (r, one or several KV heads, a chunk of the index
+//                list).  In bf16 both run the wave-specialised MFMA tile: a
+//                producer wave streams K/V rows into a 4-stage LDS ring with
+//                global->LDS loads, consumer waves compute S = K Q^T and
+//                O = P V; verify tiles dump their logits.  fp32 runs the VALU
+//                gather tile.  Outputs are final when (r, g) is one chunk,
+//                split-K partials otherwise.  No workgroup waits for another.
+// attn_kernel_draft  the same loop for the draft items of a step whose drafts
+//                run as a second launch on a side stream (the overlap option).
+// post_kernel    split-K log-sum-exp merges, and the exact scores
+//                exp(logit - LSE) averaged over the draft rows and the GQA group
+//                in 1024-position items, counted into a per-(r, g) histogram.
+// select_kernel  one workgroup per verify (r, g): the top-K by a radix select
+//                seeded by that histogram, written ascending.
+// release_kernel one thread that marks a plan buffer free when no other launch
+//                of the call does.
+// recall_kernel, quality_kernel  the neighbours of the step: index lists with
+//                sinks and recent positions appended, and the coverage / recall
+//                of lists against one query row's exact attention.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -978,7 +991,7 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
 
 // Block-wide exclusive prefix of per-thread counts (DPP wave scan + per-wave
 // totals in LDS).  Returns the prefix; *total receives the block sum.
-__device__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* wsum, uint32_t* total) {
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* wsum, uint32_t* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = blockDim.x >> 6;
   const uint32_t incl = wave_incl_scan(v);
   if (lane == 63) wsum[wave] = incl;
@@ -1374,6 +1387,27 @@ __device__ __forceinline__ void select_topk(const float* scores, int L, int K, i
   });
 }
 
+// Four logits of an averaged row.  A row starts 16-byte aligned only when L
+// and the request's logits offset are multiples of 4, so the load type asks for
+// 4-byte alignment (gfx950 serves 16-byte global loads at any 4-byte
+// boundary).  The attention launch wrote these logits just before: when all of
+// the step's logits fit the Infinity Cache, plain loads find them there;
+// otherwise the streaming hint (each logit is read once) is faster.
+template <bool CACHED>
+__device__ __forceinline__ f32x4u load_logits4(const float* src) {
+  if constexpr (CACHED)
+    return *reinterpret_cast<const f32x4u*>(src);
+  else
+    return __builtin_nontemporal_load(reinterpret_cast<const f32x4u*>(src));
+}
+template <bool CACHED>
+__device__ __forceinline__ float load_logit(const float* src) {
+  if constexpr (CACHED)
+    return *src;
+  else
+    return __builtin_nontemporal_load(src);
+}
+
 constexpr int POST_THREADS = 256;
 constexpr int AVG_PREFETCH = 8;  // averaged terms whose logits load before the LSE rebuild
 
@@ -1384,7 +1418,7 @@ __host__ __device__ constexpr size_t post_hist_offset(int terms) {
 }
 static_assert(AVG_SPAN == 4 * POST_THREADS, "an averaging thread owns four positions");
 
-template <int D, typename T>
+template <int D, typename T, bool CACHED>
 __global__ void __launch_bounds__(POST_THREADS) post_kernel(PostParams p) {
   // merge: (m, l) pairs then weights of MERGE_ROWS rows; averaging: LSE and
   // logits row offsets of the averaged terms
@@ -1423,8 +1457,7 @@ __global__ void __launch_bounds__(POST_THREADS) post_kernel(PostParams p) {
     for (int x = 0; x < AVG_PREFETCH; ++x)
       if (x < terms) {
         const int i = a + x / G, hh = x % G;
-        pre[x] = __builtin_nontemporal_load(
-            reinterpret_cast<const f32x4u*>(lg + ((int64_t)i * Hq + it.g * G + hh) * L + j4));
+        pre[x] = load_logits4<CACHED>(lg + ((int64_t)i * Hq + it.g * G + hh) * L + j4);
       }
   }
   if (it.nchunk == 1) {
@@ -1508,11 +1541,7 @@ __global__ void __launch_bounds__(POST_THREADS) post_kernel(PostParams p) {
       }
 #pragma unroll 16
     for (int x = AVG_PREFETCH; x < terms; ++x) {
-      // each logit is read once here: a streaming load, like the KV rows.
-      // A row starts 16-byte aligned only when L and the request's logits
-      // offset are multiples of 4, so the load type asks for 4-byte alignment
-      // (gfx950 serves 16-byte global loads at any 4-byte boundary).
-      const f32x4u v4 = __builtin_nontemporal_load(reinterpret_cast<const f32x4u*>(lg + rowoff_s[x] + j4));
+      const f32x4u v4 = load_logits4<CACHED>(lg + rowoff_s[x] + j4);
       const float4 v = make_float4(v4.x, v4.y, v4.z, v4.w);
       const float l2 = lse2_s[x];
       const float vv[4] = {v.x, v.y, v.z, v.w};
@@ -1533,7 +1562,7 @@ __global__ void __launch_bounds__(POST_THREADS) post_kernel(PostParams p) {
       const float* row = lg + rowoff_s[x] + j4;
       float vv[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) vv[e] = __builtin_nontemporal_load(row + min(e, ne - 1));
+      for (int e = 0; e < 4; ++e) vv[e] = load_logit<CACHED>(row + min(e, ne - 1));
       const float l2 = lse2_s[x];
 #pragma unroll
       for (int e = 0; e < 4; ++e)
@@ -1879,17 +1908,25 @@ size_t post_smem_bytes(int avg_terms, int max_nchunk, bool hist) {
 hipError_t launch_post(const PostParams& p, int dtype, int head_dim, int nitems, size_t smem,
                        hipStream_t st) {
   if (nitems == 0) return hipSuccess;
+#define SPA_POST(DV, TV)                                                                         \
+  do {                                                                                           \
+    if (p.logits_cached)                                                                         \
+      hipLaunchKernelGGL((post_kernel<DV, TV, true>), dim3(nitems), dim3(POST_THREADS), smem, st, p); \
+    else                                                                                         \
+      hipLaunchKernelGGL((post_kernel<DV, TV, false>), dim3(nitems), dim3(POST_THREADS), smem, st, p); \
+  } while (0)
   if (dtype == 0) {
     if (head_dim == 128)
-      hipLaunchKernelGGL((post_kernel<128, uint16_t>), dim3(nitems), dim3(POST_THREADS), smem, st, p);
+      SPA_POST(128, uint16_t);
     else
-      hipLaunchKernelGGL((post_kernel<64, uint16_t>), dim3(nitems), dim3(POST_THREADS), smem, st, p);
+      SPA_POST(64, uint16_t);
   } else {
     if (head_dim == 128)
-      hipLaunchKernelGGL((post_kernel<128, float>), dim3(nitems), dim3(POST_THREADS), smem, st, p);
+      SPA_POST(128, float);
     else
-      hipLaunchKernelGGL((post_kernel<64, float>), dim3(nitems), dim3(POST_THREADS), smem, st, p);
+      SPA_POST(64, float);
   }
+#undef SPA_POST
   return hipGetLastError();
 }
 

@@ -53,6 +53,9 @@ struct PostParams {
   float* pbar;
   int32_t Hq, G;
   int32_t avg_row_begin, avg_row_count;
+  // Read the logits with plain loads (they are expected in the caches) rather
+  // than with the streaming hint.
+  bool logits_cached;
   // Selected rows' score histograms (zeroed by the attention launch), added
   // to by the averaging items of rows with hist_slot >= 0; null: none kept.
   uint32_t* hist;
