@@ -293,10 +293,14 @@ __device__ void dma_producer(const AttnParams& p, const Item& it, char* smem,
   }
 }
 
-template <int D>
+// IS_LIST: a draft item (list tiles; masked entries) or a verify item
+// (causal tiles; logits dumped).  Two instantiations, so that each kind's tile
+// loop carries only its own masking and outputs.
+template <int D, bool IS_LIST>
 __device__ void dma_consumer(const AttnParams& p, const Item& it, char* smem,
-                             const int32_t* slots, bool is_list, int wave, int lane,
-                             int* next_item, uint32_t wrap) {
+                             const int32_t* slots, int wave, int lane, int* next_item,
+                             uint32_t wrap) {
+  constexpr bool is_list = IS_LIST;
   constexpr int NCH = D / 8;   // 16-byte chunks per K/V row
   constexpr int KS = D / 32;   // k-steps of S^T = K Q^T
   constexpr int DT = D / 16;   // d tiles of O^T
@@ -585,8 +589,10 @@ __device__ void attn_tile_dma(const AttnParams& p, const Item& it, char* smem, b
   __syncthreads();
   if (wave == (int)(blockDim.x >> 6) - 1)
     dma_producer<D>(p, it, smem, slots, lane);
+  else if (is_list)
+    dma_consumer<D, true>(p, it, smem, slots, wave, lane, next_item, wrap);
   else
-    dma_consumer<D>(p, it, smem, slots, is_list, wave, lane, next_item, wrap);
+    dma_consumer<D, false>(p, it, smem, slots, wave, lane, next_item, wrap);
 }
 
 // ==========================================================================
