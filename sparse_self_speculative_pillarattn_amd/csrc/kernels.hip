@@ -311,7 +311,7 @@ __device__ void dma_consumer(const AttnParams& p, const Item& it, char* smem,
   const int L = it.L;
   const int jb = it.begin, je = it.end;
   const int n_tiles = (je - jb + DMA_TT - 1) / DMA_TT;  // per KV head
-  const int ng = max(1, it.ng);  // KV heads of a packed draft item (1 otherwise)
+  const int ng = IS_LIST ? max(1, it.ng) : 1;  // KV heads of a packed draft item (1 otherwise)
 
   const int n = lane & 15, q4 = lane >> 4;
   const int rho = wave * 16 + n;
@@ -833,6 +833,8 @@ __device__ __forceinline__ bool attn_body(const AttnParams& p, int item, char* s
 // value once and leaves the counter at 0 for the next launch that uses it.
 // The draw for the next item lands in the other entry of s_item, which every
 // thread finished reading before the previous iteration's closing barrier.
+// (Starting workgroup b on item b without a draw was measured: 0.7% faster
+// on the Qwen3-8B-shaped step, 1.5% slower on the Qwen3-14B-shaped one.)
 template <int D, typename T, int GM>
 __device__ __forceinline__ void attn_loop(const AttnParams& p, char* smem) {
   __shared__ int s_item[2];
