@@ -1101,24 +1101,32 @@ __device__ __forceinline__ void select_topk(const float* scores, int L, int K, i
   const int nrows = (nthr >> 6) * 4;
   const int span = KPT * nthr;
   const bool resident = L <= span;
-  const bool vec = (reinterpret_cast<uintptr_t>(scores) & 15) == 0;
   uint32_t key[KPT];
-  auto load_into = [&](uint32_t (&dst)[KPT], int c0) {
+  // Every load of a batch is issued before any of them is used, at an address
+  // clamped to the quad holding position L-1, and positions at or past L are
+  // set to key 0 only afterwards.  A per-thread branch between two loads makes
+  // the compiler wait for the first before issuing the second (a batch was one
+  // round trip per load), and a scalar fallback path for unaligned rows was
+  // merged with this one into 4-byte loads.  The row starts 16-byte aligned and
+  // its storage extends to L rounded up to a multiple of 4 (both callers' rows
+  // are workspace rows laid out so), so that quad is read whole.
+  const int jq = (L - 1) & ~3;
+  auto load_raw = [&](uint32_t (&dst)[KPT], int c0) {
     const int j0 = c0 + KPT * tid;
 #pragma unroll
     for (int m = 0; m < KPT; m += 4) {
-      const int j = j0 + m;
-      if (vec && j + 4 <= L) {
-        const uint4 v = *reinterpret_cast<const uint4*>(keys + j);
-        dst[m] = v.x;
-        dst[m + 1] = v.y;
-        dst[m + 2] = v.z;
-        dst[m + 3] = v.w;
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) dst[m + e] = (j + e < L) ? keys[j + e] : 0u;
-      }
+      const uint4 v = *reinterpret_cast<const uint4*>(keys + min(j0 + m, jq));
+      dst[m] = v.x;
+      dst[m + 1] = v.y;
+      dst[m + 2] = v.z;
+      dst[m + 3] = v.w;
     }
+  };
+  auto mask_past_end = [&](uint32_t (&dst)[KPT], int c0) {
+    const int j0 = c0 + KPT * tid;
+#pragma unroll
+    for (int m = 0; m < KPT; ++m)
+      if (j0 + m >= L) dst[m] = 0u;
   };
   // Calls body(c0) for every chunk with its keys in key[].  Rows longer than
   // one chunk are re-read on every walk, SELECT_BATCH chunks per batch of loads
@@ -1131,18 +1139,22 @@ __device__ __forceinline__ void select_topk(const float* scores, int L, int K, i
     for (int c0 = 0; c0 < L; c0 += SELECT_BATCH * span) {
       uint32_t kb[SELECT_BATCH][KPT];
 #pragma unroll
-      for (int q = 0; q < SELECT_BATCH; ++q) load_into(kb[q], c0 + q * span);
+      for (int q = 0; q < SELECT_BATCH; ++q) load_raw(kb[q], c0 + q * span);
 #pragma unroll
       for (int q = 0; q < SELECT_BATCH; ++q) {
         if (c0 + q * span < L) {  // the same for every thread
 #pragma unroll
           for (int m = 0; m < KPT; ++m) key[m] = kb[q][m];
+          mask_past_end(key, c0 + q * span);
           body(c0 + q * span);
         }
       }
     }
   };
-  if (resident) load_into(key, 0);
+  if (resident) {
+    load_raw(key, 0);
+    mask_past_end(key, 0);
+  }
   int shift;
   uint32_t mask;
   if (hist) {
