@@ -842,23 +842,36 @@ __device__ __forceinline__ bool attn_body(const AttnParams& p, int item, char* s
 // first) until none is left.  Whichever CU frees first, on any XCD, takes the
 // next item, so an XCD that runs slower simply processes fewer items; with
 // one workgroup per item, workgroup i always runs on XCD i % 8 and every XCD
-// would own a fixed eighth of the work.  A launch of G workgroups over n items
-// makes exactly n + G draws (n items, then one draw per workgroup that finds
-// the plan exhausted), so atomicInc wrapping at n + G - 1 hands out every
-// value once and leaves the counter at 0 for the next launch that uses it.
-// The draw for the next item lands in the other entry of s_item, which every
-// thread finished reading before the previous iteration's closing barrier.
-// (Starting workgroup b on item b without a draw was measured: 0.7% faster
-// on the Qwen3-8B-shaped step, 1.5% slower on the Qwen3-14B-shaped one.)
+// would own a fixed eighth of the work.
+// Workgroup b starts on item b without a draw: all G workgroups drawing from
+// one counter at once queue at that address, and the last got its first item
+// about 6 us after the launch began (3 us on average, measured on 512
+// workgroups).  The counter then hands out draw t = 0, 1, ...: items G, G+1,
+// ... while S = max(n - G, 0) of them last, then one past-the-end draw per
+// workgroup (index e = t - S).  That is S + G draws, so atomicInc wrapping at
+// S + G - 1 hands out every value once and leaves the counter at 0 for the
+// next launch that uses it.  A workgroup without a first item (b >= n) draws
+// its past-the-end ticket at once.  The draw for the next item lands in the
+// other entry of s_item, which every thread finished reading before the
+// previous iteration's closing barrier.  (Measured against drawing every item:
+// draft-only Qwen3-8B-shaped batches 11-15% faster at s <= 0.05, the mixed
+// Qwen3-1.7B, Qwen3-8B and long-context steps 0.6-1.5% faster, the
+// Qwen3-14B-shaped step 1.5% slower.  Mapping draws to items in the consumer
+// wave instead of here made both Qwen3 steps 5% slower.)
 template <int D, typename T, int GM>
 __device__ __forceinline__ void attn_loop(const AttnParams& p, char* smem) {
   __shared__ int s_item[2];
-  const uint32_t wrap = (uint32_t)p.n_items + gridDim.x - 1u;
-  if (threadIdx.x == 0) s_item[0] = (int)atomicInc(p.ticket, wrap);
-  __syncthreads();
-  for (int k = 0;; k ^= 1) {
-    const int item = s_item[k];
-    if (item >= p.n_items) {  // the same value for the whole workgroup
+  const int G = (int)gridDim.x, n = p.n_items, S = max(n - G, 0);
+  const uint32_t wrap = (uint32_t)(S + G) - 1u;
+  const bool static_first = (int)blockIdx.x < n;
+  if (!static_first) {
+    if (threadIdx.x == 0) s_item[0] = (int)atomicInc(p.ticket, wrap);
+    __syncthreads();
+  }
+  for (int k = 0, first = static_first ? 1 : 0;; k ^= 1, first = 0) {
+    const int t = first ? 0 : s_item[k];
+    const int item = first ? (int)blockIdx.x : (t < S ? G + t : n + (t - S));
+    if (item >= n) {  // the same value for the whole workgroup
       // Out of work.  Every workgroup draws exactly one ticket past the last
       // item; the first half of those draws (workgroups that run out while
       // others still finish their last items) copy the post-pass and selection
@@ -866,8 +879,8 @@ __device__ __forceinline__ void attn_loop(const AttnParams& p, char* smem) {
       // 16-byte pieces per workgroup and round.  The launches after this one
       // then read their records from device memory instead of across PCIe,
       // where the read is on their critical path.
-      const int e = item - p.n_items;
-      const int nc = max(1, (int)gridDim.x / 2);
+      const int e = item - n;
+      const int nc = max(1, G / 2);
       if (e < nc) {
         for (int c = e * (int)blockDim.x + (int)threadIdx.x; c < p.plan_n16; c += nc * (int)blockDim.x)
           p.plan_dst[c] = p.plan_src[c];
@@ -876,7 +889,7 @@ __device__ __forceinline__ void attn_loop(const AttnParams& p, char* smem) {
       }
       // The last of those draws comes after every other workgroup's: no
       // plan record is read after it.
-      if (p.done && e == (int)gridDim.x - 1 && threadIdx.x == 0)
+      if (p.done && e == G - 1 && threadIdx.x == 0)
         __hip_atomic_store(p.done, p.done_val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
       break;
     }
