@@ -165,6 +165,7 @@ constexpr size_t dma_smem_bytes() {  // the stage ring; logits staging and slots
 constexpr int LSTG = DMA_TT + 4;  // floats per staged row
 constexpr size_t logit_stage_bytes(int consumer_waves) { return (size_t)consumer_waves * 16 * LSTG * 4; }
 constexpr int VERIFY_SLOT_BATCH = 8;  // verify slots a thread stages per round
+constexpr int LIST_SLOT_BATCH = 4;    // draft list entries a thread stages per round
 
 // LDS chunk swizzles of a stage.  K: the 16 consecutive rows one MFMA operand
 // read touches land on distinct bank groups.  V: the eight rows (two 16-byte
@@ -566,15 +567,27 @@ __device__ void attn_tile_dma(const AttnParams& p, const Item& it, char* smem, b
   if (is_list) {
     // the list of each packed KV head is padded to whole tiles
     const int ng = max(1, it.ng);
-    for (int x = tid; x < ng * padded; x += blockDim.x) {
-      const int hd = x / padded, j = x - hd * padded;
-      const int32_t* list = p.idx_in + it.off + (int64_t)hd * it.list_len;
-      int32_t sl = -1;
-      if (jb + j < je) {
-        const int pos = list[jb + j];
-        if (pos >= 0 && pos < it.L) sl = (int32_t)clamp_slot(pt[pos], p.num_slots);
+    // LIST_SLOT_BATCH entries per thread and round: their list loads, then
+    // their page-table loads, each group in flight together
+    const int n = ng * padded, nthr = (int)blockDim.x;
+    const int32_t* list0 = p.idx_in + it.off;
+    for (int b0 = 0; b0 < n; b0 += LIST_SLOT_BATCH * nthr) {
+      int32_t pos[LIST_SLOT_BATCH];
+#pragma unroll
+      for (int u = 0; u < LIST_SLOT_BATCH; ++u) {
+        const int x = b0 + u * nthr + tid;
+        const int hd = x / padded, j = x - hd * padded;
+        pos[u] = (x < n && jb + j < je) ? list0[(int64_t)hd * it.list_len + jb + j] : -1;
       }
-      slots[x] = sl;
+      int32_t sl[LIST_SLOT_BATCH];
+#pragma unroll
+      for (int u = 0; u < LIST_SLOT_BATCH; ++u)
+        sl[u] = (pos[u] >= 0 && pos[u] < it.L) ? pt[pos[u]] : -1;
+#pragma unroll
+      for (int u = 0; u < LIST_SLOT_BATCH; ++u) {
+        const int x = b0 + u * nthr + tid;
+        if (x < n) slots[x] = sl[u] < 0 ? -1 : (int32_t)clamp_slot(sl[u], p.num_slots);
+      }
     }
     if (ng > 1) {  // the G query rows of every packed head, after the slots
       uint4* qst = reinterpret_cast<uint4*>(slots + ng * padded);
