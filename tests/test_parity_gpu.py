@@ -471,6 +471,32 @@ def test_workspace_reuse_across_batches(oracle):
                                         "idx": bufs.idx}, ref)
 
 
+@pytest.mark.parametrize("B", [63, 64, 65, 127, 128, 129])
+def test_item_counts_around_the_grid(oracle, B):
+    """Draft-only batches whose attention item counts sit around the launch's
+    workgroup count: workgroup b starts on item b and only later items come
+    from the counter, so fewer, as many and a few more items than workgroups
+    all occur.  With 256-thread workgroups, two per CU on 256 CUs, B = 63, 64
+    and 65 give 504, 512 and 520 items (one KV head's list each), and B = 127,
+    128 and 129 give 1016, 512 and 516 (from 128 drafts on, two lists per
+    item).  Every output matches the oracle, and the work counters are back
+    at zero after the call."""
+    w = synth.Workload(name=f"grid{B}", batch=B, num_qo_heads=32, num_kv_heads=8, head_dim=128,
+                       dtype="bf16", spec_k=8, sparsity=Fraction(1, 20), lengths=("fixed", 1024),
+                       seed=B)
+    b = synth.uniform_batch(w, B, 1024, [0] * B, seed=B)
+    print(f"[case] grid B={B}", flush=True)
+    ref = oracle.step(**parity.oracle_inputs(b))
+    bufs = bd.StepBuffers(b.to(DEV))
+    bufs.o.fill_(float("nan"))
+    bufs.lse.fill_(float("nan"))
+    bufs.step()
+    torch.cuda.synchronize()
+    assert not bool(bufs.ws[:256].any()), "the work counters were not left at zero"
+    parity.compare_step(oracle, b, {"o": bufs.o, "lse": bufs.lse, "logits": bufs.logits,
+                                    "idx": bufs.idx}, ref)
+
+
 FULL = [synth.QWEN3_1_7B.name, synth.QWEN3_8B.name, synth.QWEN3_14B.name, synth.LONG_CTX.name]
 
 
