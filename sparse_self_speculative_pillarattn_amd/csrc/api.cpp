@@ -92,13 +92,20 @@ struct Plan {
   int n_merge = 0, n_avg = 0, n_sel = 0;
   int n_hist = 0;  // selected rows with a score histogram (all of them when the call has attention)
   int max_sel_len = 0;  // longest selected row
+  int max_row_sel_len = 0;  // longest row selected by one workgroup
+  int n_chunks = 0;  // chunks of the long rows selected in chunks (SEL_CHUNKED_MIN)
+  int n_chunked_rows = 0;  // selected rows of those
   int64_t part_rows = 0;
   int64_t pbar_elems = 0;
   int64_t avg_logit_bytes = 0;  // logits the verify requests dump, which the averaging reads back
   // pinned plan layout
-  size_t h_items = 0, h_items_d = 0, h_post = 0, h_post_d = 0, h_sel = 0, h_bytes = 0;
+  size_t h_items = 0, h_items_d = 0, h_post = 0, h_post_d = 0, h_sel = 0, h_chunks = 0, h_bytes = 0;
   // workspace layout (work counters at offset 0)
   size_t off_part_o = 0, off_part_ml = 0, off_pbar = 0, off_plan = 0, off_hist = 0, total = 0;
+  // chunked long-row selection: candidate counts (cleared with the
+  // histograms), row boundaries, the chunks' counts above the boundary bin,
+  // the candidates
+  size_t hist_zero_bytes = 0, off_row_info = 0, off_cnt_above = 0, off_cand_key = 0, off_cand_pos = 0;
   int nthr = 256;
   size_t smem = 0;
 };
@@ -315,6 +322,12 @@ int32_t plan_size(const Shape& s, const std::vector<Req>& rq, bool attn, bool to
         // the histogram is cleared by the attention launch, so only a call
         // with one keeps it
         if (attn) pl->n_hist += Hkv;
+        if (attn && q.L > SEL_CHUNKED_MIN) {
+          pl->n_chunks += Hkv * ((q.L + SELECT_SPAN - 1) / SELECT_SPAN);
+          pl->n_chunked_rows += Hkv;
+        }
+        else
+          pl->max_row_sel_len = std::max(pl->max_row_sel_len, q.L);
         pbar += Hkv * pbar_row(q.L);
       }
   pl->part_rows = part_rows;
@@ -361,6 +374,8 @@ int32_t plan_size(const Shape& s, const std::vector<Req>& rq, bool attn, bool to
   h = align_up(h + (size_t)pl->n_merge_d * sizeof(PostItem), 256);
   pl->h_sel = h;
   h = align_up(h + (size_t)pl->n_sel * sizeof(PostItem), 256);
+  pl->h_chunks = h;  // copied to the workspace with the selection records
+  h = align_up(h + (size_t)pl->n_chunks * sizeof(SelChunk), 256);
   pl->h_bytes = h;
   // workspace layout: the attention launches' work counters first
   size_t w = WS_COUNTERS;
@@ -375,7 +390,21 @@ int32_t plan_size(const Shape& s, const std::vector<Req>& rq, bool attn, bool to
   pl->off_plan = w;
   if (attn || topk) w = align_up(w + (pl->h_bytes - pl->h_post), 256);
   pl->off_hist = w;
-  w = align_up(w + (size_t)pl->n_hist * HIST_BINS * 4, 256);
+  w += (size_t)pl->n_hist * HIST_BINS * 4;
+  if (pl->n_chunks > 0) w += (size_t)pl->n_hist * 4;  // candidate counts, cleared with the histograms
+  w = align_up(w, 16);
+  pl->hist_zero_bytes = w - pl->off_hist;
+  w = align_up(w, 256);
+  if (pl->n_chunks > 0) {
+    pl->off_row_info = w;
+    w = align_up(w + (size_t)pl->n_hist * 16, 256);
+    pl->off_cnt_above = w;
+    w = align_up(w + (size_t)pl->n_chunks * 4, 256);
+    pl->off_cand_key = w;
+    w = align_up(w + (size_t)pl->n_hist * SEL_CAND_CAP * 4, 256);
+    pl->off_cand_pos = w;
+    w = align_up(w + (size_t)pl->n_hist * SEL_CAND_CAP * 4, 256);
+  }
   pl->total = w;
   return SPA_OK;
 }
@@ -431,6 +460,8 @@ void plan_write(const Shape& s, const std::vector<Req>& rq, const Plan& pl, char
   PostItem* post = reinterpret_cast<PostItem*>(h + pl.h_post);
   PostItem* post_d = reinterpret_cast<PostItem*>(h + pl.h_post_d);
   PostItem* sel = reinterpret_cast<PostItem*>(h + pl.h_sel);
+  SelChunk* chunks = reinterpret_cast<SelChunk*>(h + pl.h_chunks);
+  int nck = 0;
   int np = 0, ns = 0, npd = 0, nh = 0;
   if (pl.topk) {
     int64_t pbar = 0;
@@ -457,6 +488,8 @@ void plan_write(const Shape& s, const std::vector<Req>& rq, const Plan& pl, char
         a.pbar_off = pbar;
         a.hist_slot = pl.n_hist > 0 ? nh++ : -1;
         sel[ns++] = a;
+        if (pl.n_chunks > 0 && q.L > SEL_CHUNKED_MIN)
+          for (int c = 0; c * SELECT_SPAN < q.L; ++c) chunks[nck++] = SelChunk{ns - 1, c};
         for (int pidx = 0; pidx < nparts; ++pidx) {
           a.j0 = pidx * AVG_SPAN;
           a.j1 = std::min(q.L, (pidx + 1) * AVG_SPAN);
@@ -667,7 +700,7 @@ int32_t run(const Shape& s, const std::vector<Req>& rq, const Plan& pl, const Bu
     p.plan_n16 = pl.n_items > 0 ? static_cast<int32_t>((pl.h_bytes - pl.h_post) / 16) : 0;
     // ... and clears the score histograms the post-pass adds to
     p.zero_dst = reinterpret_cast<uint4*>(ws + pl.off_hist);
-    p.zero_n16 = pl.n_items > 0 ? static_cast<int32_t>((size_t)pl.n_hist * HIST_BINS * 4 / 16) : 0;
+    p.zero_n16 = pl.n_items > 0 ? static_cast<int32_t>(pl.hist_zero_bytes / 16) : 0;
     // a call that is this one launch reports its plan free from the launch
     const bool attn_only = pl.n_items > 0 && n_post == 0 && pl.n_sel == 0 && !pl.split;
     p.done = attn_only ? pr.done_dev : nullptr;
@@ -747,12 +780,27 @@ int32_t run(const Shape& s, const std::vector<Req>& rq, const Plan& pl, const Bu
     sp.pbar = reinterpret_cast<const float*>(ws + pl.off_pbar);
     sp.idx_out = b.idx_out;
     sp.hist = hist;
-    sp.bm_bits = select_bitmap_bits(pl.max_sel_len);
+    // long rows in chunks (their histograms are there), every other row by
+    // one workgroup, through the LDS position bitmap when it is long
+    const bool chunked = hist != nullptr && pl.n_chunks > 0;
+    sp.bm_bits = select_bitmap_bits(chunked ? pl.max_row_sel_len : pl.max_sel_len);
+    sp.n_sel = pl.n_sel;
+    sp.n_chunks = chunked ? pl.n_chunks : 0;
+    sp.chunks = reinterpret_cast<const SelChunk*>(ws + pl.off_plan + (pl.h_chunks - pl.h_post));
+    sp.cand_n = reinterpret_cast<uint32_t*>(ws + pl.off_hist + (size_t)pl.n_hist * HIST_BINS * 4);
+    sp.row_info = reinterpret_cast<uint32_t*>(ws + pl.off_row_info);
+    sp.cnt_above = reinterpret_cast<uint32_t*>(ws + pl.off_cnt_above);
+    sp.cand_key = reinterpret_cast<uint32_t*>(ws + pl.off_cand_key);
+    sp.cand_pos = reinterpret_cast<int32_t*>(ws + pl.off_cand_pos);
     // without an attention launch, the post-pass before it read the pinned records last
     sp.done = attn_st ? nullptr : pr.done_dev;
     sp.done_val = pr.seq;
     e = mark(o.timing[4], st);
-    if (e == hipSuccess) e = launch_select(sp, pl.n_sel, st);
+    // the per-row launch only when some row is not chunked
+    const bool rows = !chunked || pl.n_chunked_rows < pl.n_sel;
+    if (e == hipSuccess) e = launch_select_count(sp, st);
+    if (e == hipSuccess && rows) e = launch_select(sp, pl.n_sel, st);
+    if (e == hipSuccess) e = launch_select_chunks(sp, st);
     if (e == hipSuccess) e = mark(o.timing[5], st);
     if (e != hipSuccess) return fail(SPA_ERR_HIP, std::string("selection launch: ") + hipGetErrorString(e));
   }

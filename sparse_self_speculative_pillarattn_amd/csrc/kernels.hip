@@ -1656,6 +1656,260 @@ constexpr int SELECT_THREADS = 1024;
 constexpr int SELECT_KPT = 8;  // keys per thread kept in registers (8192 at 1024 threads)
 static_assert(SELECT_THREADS * SELECT_KPT == SELECT_SPAN, "scores kept in registers");
 
+// ---- long rows, one workgroup per SELECT_SPAN-score chunk --------------------
+// The boundary bin of the K-th largest key from a row's histogram: sv[0] =
+// bin << HIST_SHIFT, sv[1] = K minus the keys in higher bins (the K-th key's
+// rank inside the bin), sv[2] = the keys in the bin, or 0xffffffff when no bin
+// holds the K-th key (inconsistent counts).
+__device__ __forceinline__ void hist_boundary(const uint32_t* hist, int K, uint32_t* sv, uint32_t* wsum) {
+  const int tid = threadIdx.x, nthr = blockDim.x;
+  if (tid == 0) {
+    sv[0] = 0u;
+    sv[1] = (uint32_t)K;
+    sv[2] = 0xffffffffu;
+  }
+  const int per = HIST_BINS / nthr;
+  const int b0 = HIST_BINS - 1 - per * tid;
+  uint32_t mine = 0u;
+  for (int b = 0; b < per; ++b) mine += hist[b0 - b];
+  uint32_t tot;
+  const uint32_t above = block_exclusive_scan(mine, wsum, &tot);
+  if (above < (uint32_t)K && above + mine >= (uint32_t)K) {  // one thread owns the K-th key
+    uint32_t acc = above;
+    for (int b = 0; b < per; ++b) {
+      const uint32_t c = hist[b0 - b];
+      if (acc + c >= (uint32_t)K) {
+        sv[0] = (uint32_t)(b0 - b) << HIST_SHIFT;
+        sv[1] = (uint32_t)K - acc;
+        sv[2] = c;
+        break;
+      }
+      acc += c;
+    }
+  }
+  __syncthreads();
+}
+
+// The SELECT_KPT consecutive keys of thread t in the chunk starting at c0,
+// their loads in flight together; positions at or past L read as key 0.  The
+// row starts 16-byte aligned and its storage extends to L rounded up to a
+// multiple of 4.
+__device__ __forceinline__ void chunk_keys(const float* scores, int L, int c0, uint32_t (&key)[SELECT_KPT]) {
+  const uint32_t* keys = reinterpret_cast<const uint32_t*>(scores);
+  const int j0 = c0 + SELECT_KPT * (int)threadIdx.x, jq = (L - 1) & ~3;
+#pragma unroll
+  for (int m = 0; m < SELECT_KPT; m += 4) {
+    const uint4 v = *reinterpret_cast<const uint4*>(keys + min(j0 + m, jq));
+    key[m] = v.x;
+    key[m + 1] = v.y;
+    key[m + 2] = v.z;
+    key[m + 3] = v.w;
+  }
+#pragma unroll
+  for (int m = 0; m < SELECT_KPT; ++m)
+    if (j0 + m >= L) key[m] = 0u;
+}
+
+// Count launch: chunk record blockIdx.x counts its keys above the boundary
+// bin and appends the bin's keys (with their positions) to the row's
+// candidates; chunk 0 also records the boundary for the selection launch.
+__global__ void __launch_bounds__(SELECT_THREADS) select_count_kernel(SelectParams sp) {
+  __shared__ uint32_t sv[8];
+  __shared__ uint32_t wsum[16];
+  const int tid = threadIdx.x;
+  const SelChunk c = sp.chunks[blockIdx.x];
+  const PostItem it = sp.items[c.sel];
+  const int c0 = c.chunk * SELECT_SPAN;
+  uint32_t key[SELECT_KPT];
+  chunk_keys(sp.pbar + it.pbar_off, it.L, c0, key);  // in flight with the histogram's loads
+  hist_boundary(sp.hist + (int64_t)it.hist_slot * HIST_BINS, it.K, sv, wsum);
+  const uint32_t bin = sv[0] >> HIST_SHIFT;
+  const bool ok = sv[2] != 0xffffffffu;
+  if (c.chunk == 0 && tid < 3) sp.row_info[(int64_t)it.hist_slot * 4 + tid] = sv[tid];
+  const int j0 = c0 + SELECT_KPT * tid;
+  uint32_t n_above = 0u, n_bin = 0u;
+#pragma unroll
+  for (int m = 0; m < SELECT_KPT; ++m)
+    if (j0 + m < it.L) {
+      const uint32_t b = key[m] >> HIST_SHIFT;
+      n_above += b > bin ? 1u : 0u;
+      n_bin += b == bin ? 1u : 0u;
+    }
+  // both counts in one scan (each at most SELECT_SPAN per chunk)
+  uint32_t tot;
+  const uint32_t pre = block_exclusive_scan(n_above | (n_bin << 16), wsum, &tot);
+  if (tid == 0) {
+    sp.cnt_above[blockIdx.x] = tot & 0xffffu;
+    sv[3] = ok ? atomicAdd(&sp.cand_n[it.hist_slot], tot >> 16) : 0u;
+  }
+  __syncthreads();
+  if (!ok) return;
+  uint32_t pos = sv[3] + (pre >> 16);
+  uint32_t* ck = sp.cand_key + (int64_t)it.hist_slot * SEL_CAND_CAP;
+  int32_t* cp = sp.cand_pos + (int64_t)it.hist_slot * SEL_CAND_CAP;
+#pragma unroll
+  for (int m = 0; m < SELECT_KPT; ++m)
+    if (j0 + m < it.L && (key[m] >> HIST_SHIFT) == bin) {
+      if (pos < (uint32_t)SEL_CAND_CAP) {
+        ck[pos] = key[m];
+        cp[pos] = j0 + m;
+      }
+      ++pos;
+    }
+}
+
+// Selection launch, chunk record `rec` of a long row: the row's candidates
+// give the K-th key tau and how many keys equal to it are kept (lowest
+// positions first); the chunk's positions above tau, and its share of those
+// equal to it, go to the list at the offset the earlier chunks leave.
+__device__ __forceinline__ void select_chunk(const SelectParams& sp, int rec, char* smem, char* dyn) {
+  uint32_t* sv = reinterpret_cast<uint32_t*>(smem);
+  uint32_t* wsum = sv + 8;
+  uint32_t* cnt16 = wsum + 16;
+  const int tid = threadIdx.x, nthr = blockDim.x, lane = tid & 63, wave = tid >> 6;
+  const SelChunk c = sp.chunks[rec];
+  const PostItem it = sp.items[c.sel];
+  const float* scores = sp.pbar + it.pbar_off;
+  int32_t* out = sp.idx_out + it.idx_off;
+  const int c0 = c.chunk * SELECT_SPAN;
+  uint32_t key[SELECT_KPT];
+  chunk_keys(scores, it.L, c0, key);  // in flight while the candidates are ranked
+  const uint32_t* ri = sp.row_info + (int64_t)it.hist_slot * 4;
+  uint32_t prefix = ri[0], rem = ri[1];
+  const uint32_t hcnt = ri[2];
+  const uint32_t nc = sp.cand_n[it.hist_slot];
+  if (hcnt == 0xffffffffu || nc != hcnt || nc > (uint32_t)SEL_CAND_CAP) {
+    // too many keys in the boundary bin (or counts that disagree): the row's
+    // first chunk selects the whole row alone, by the full radix walk
+    if (c.chunk == 0) select_topk<SELECT_KPT>(scores, it.L, it.K, out, smem);
+    return;
+  }
+  const uint32_t* gk = sp.cand_key + (int64_t)it.hist_slot * SEL_CAND_CAP;
+  const int32_t* gp = sp.cand_pos + (int64_t)it.hist_slot * SEL_CAND_CAP;
+  if (nc <= 64u) {
+    // one wave ranks the candidates directly
+    if (wave == 0) {
+      if (lane == 0) {  // stands only if no lane holds the K-th key (inconsistent input)
+        sv[4] = 0u;
+        sv[5] = 0u;
+      }
+      const uint32_t mk = lane < (int)nc ? gk[lane] : 0u;
+      const int mp = lane < (int)nc ? gp[lane] : 0x7fffffff;
+      uint32_t gt = 0u, eq = 0u;
+      for (int j = 0; j < (int)nc; ++j) {
+        const uint32_t o = (uint32_t)__builtin_amdgcn_readlane((int)mk, j);
+        gt += o > mk ? 1u : 0u;
+        eq += o == mk ? 1u : 0u;
+      }
+      // lanes holding the K-th key (equal keys agree on both values)
+      if (lane < (int)nc && gt < rem && gt + eq >= rem) {
+        sv[4] = mk;
+        sv[5] = rem - gt;
+      }
+      __builtin_amdgcn_wave_barrier();
+      const uint32_t tau = sv[4];
+      const uint64_t gt_b = __ballot(lane < (int)nc && mp < c0 && mk > tau);
+      const uint64_t eq_b = __ballot(lane < (int)nc && mp < c0 && mk == tau);
+      if (lane == 0) {
+        sv[6] = (uint32_t)__popcll(gt_b);
+        sv[7] = (uint32_t)__popcll(eq_b);
+      }
+    }
+    __syncthreads();
+  } else {
+    // 4-bit digits below the bin, counted in LDS over the staged candidates
+    uint32_t* ck = reinterpret_cast<uint32_t*>(dyn);
+    int32_t* cp = reinterpret_cast<int32_t*>(dyn + SEL_CAND_CAP * 4);
+    for (int i = tid; i < (int)nc; i += nthr) {
+      ck[i] = gk[i];
+      cp[i] = gp[i];
+    }
+    uint32_t mask = 0xffffffffu << HIST_SHIFT;
+    for (int shift = HIST_SHIFT - 4; shift >= 0; shift -= 4) {
+      if (tid < 16) cnt16[tid] = 0u;
+      __syncthreads();
+      for (int i = tid; i < (int)nc; i += nthr)
+        if ((ck[i] & mask) == prefix) atomicAdd(&cnt16[(ck[i] >> shift) & 15u], 1u);
+      __syncthreads();
+      if (tid == 0) {
+        uint32_t acc = 0u;
+        for (int d = 15; d >= 0; --d) {
+          const uint32_t n = cnt16[d];
+          if (acc + n >= rem) {
+            sv[4] = prefix | ((uint32_t)d << shift);
+            sv[5] = rem - acc;
+            break;
+          }
+          acc += n;
+        }
+      }
+      __syncthreads();
+      prefix = sv[4];
+      rem = sv[5];
+      mask |= 15u << shift;
+      __syncthreads();  // sv[4], sv[5] and cnt16 are rewritten next round
+    }
+    const uint32_t tau = sv[4];
+    uint32_t gt_m = 0u, eq_m = 0u;
+    for (int i = tid; i < (int)nc; i += nthr)
+      if (cp[i] < c0) {
+        gt_m += ck[i] > tau ? 1u : 0u;
+        eq_m += ck[i] == tau ? 1u : 0u;
+      }
+    uint32_t tot;
+    (void)block_exclusive_scan(gt_m | (eq_m << 16), wsum, &tot);  // each count below 2^16
+    if (tid == 0) {
+      sv[6] = tot & 0xffffu;
+      sv[7] = tot >> 16;
+    }
+    __syncthreads();
+  }
+  const uint32_t tau = sv[4], eq_take = sv[5], gt_b = sv[6], eq_b = sv[7];
+  // keys above the bin in the row's earlier chunks
+  uint32_t above_m = 0u;
+  for (int i = tid; i < c.chunk; i += nthr) above_m += sp.cnt_above[rec - c.chunk + i];
+  uint32_t above_b;
+  (void)block_exclusive_scan(above_m, wsum, &above_b);
+  const uint32_t base = above_b + gt_b + min(eq_b, eq_take);
+  const uint32_t quota = eq_take > eq_b ? eq_take - eq_b : 0u;
+  const int j0 = c0 + SELECT_KPT * tid;
+  uint32_t n_eq = 0u;
+#pragma unroll
+  for (int m = 0; m < SELECT_KPT; ++m) n_eq += (j0 + m < it.L && key[m] == tau) ? 1u : 0u;
+  uint32_t te;
+  uint32_t eq_rank = block_exclusive_scan(n_eq, wsum, &te);  // equal keys before this thread's
+  bool take[SELECT_KPT];
+  uint32_t n_take = 0u;
+#pragma unroll
+  for (int m = 0; m < SELECT_KPT; ++m) {
+    const bool in = j0 + m < it.L;
+    bool t = in && key[m] > tau;
+    if (in && key[m] == tau) {
+      t = eq_rank < quota;
+      ++eq_rank;
+    }
+    take[m] = t;
+    n_take += t ? 1u : 0u;
+  }
+  uint32_t tt;
+  uint32_t pos = base + block_exclusive_scan(n_take, wsum, &tt);
+#pragma unroll
+  for (int m = 0; m < SELECT_KPT; ++m)
+    if (take[m]) {
+      if (pos < (uint32_t)it.K) out[pos] = j0 + m;
+      ++pos;
+    }
+}
+
+// Chunk launch: one workgroup per chunk record (a separate kernel, so that the
+// per-row launch keeps its own code: sharing one kernel cost the Qwen3-8B-shaped
+// selection 0.7 us).
+__global__ void __launch_bounds__(SELECT_THREADS) select_chunk_kernel(SelectParams sp) {
+  __shared__ __attribute__((aligned(16))) char smem[(24 + 16 * 64 + SELECT_FINISH) * 4];
+  extern __shared__ __attribute__((aligned(16))) char dyn[];  // the row's candidate keys and positions
+  select_chunk(sp, (int)blockIdx.x, smem, dyn);
+}
+
 __global__ void __launch_bounds__(SELECT_THREADS) select_kernel(SelectParams sp) {
   __shared__ __attribute__((aligned(16))) char smem[(24 + 16 * 64 + SELECT_FINISH) * 4];
   // dynamic LDS (long rows only): the positions of the final bucket's keys,
@@ -1666,6 +1920,7 @@ __global__ void __launch_bounds__(SELECT_THREADS) select_kernel(SelectParams sp)
   int32_t* cpos = sp.bm_bits > 0 ? reinterpret_cast<int32_t*>(dyn) : nullptr;
   uint32_t* bm = sp.bm_bits > 0 ? reinterpret_cast<uint32_t*>(dyn + SELECT_FINISH * 4) : nullptr;
   const PostItem it = sp.items[blockIdx.x];
+  if (sp.n_chunks > 0 && it.L > SEL_CHUNKED_MIN) return;  // the chunk launch selects it
   const uint32_t* hist = (sp.hist && it.hist_slot >= 0) ? sp.hist + (int64_t)it.hist_slot * HIST_BINS : nullptr;
   select_topk<SELECT_KPT>(sp.pbar + it.pbar_off, it.L, it.K, sp.idx_out + it.idx_off, smem, hist, bm, cpos,
                           sp.bm_bits);
@@ -1918,6 +2173,19 @@ hipError_t launch_attn(const AttnParams& params, int dtype, int head_dim, int ni
   }
   if (head_dim == 128) return launch_attn_g<128, float>(p, nitems, nthr, smem, draft, st);
   return launch_attn_g<64, float>(p, nitems, nthr, smem, draft, st);
+}
+
+hipError_t launch_select_count(const SelectParams& sp, hipStream_t st) {
+  if (sp.n_chunks == 0) return hipSuccess;
+  hipLaunchKernelGGL(select_count_kernel, dim3(sp.n_chunks), dim3(SELECT_THREADS), 0, st, sp);
+  return hipGetLastError();
+}
+
+hipError_t launch_select_chunks(const SelectParams& sp, hipStream_t st) {
+  if (sp.n_chunks == 0) return hipSuccess;
+  hipLaunchKernelGGL(select_chunk_kernel, dim3(sp.n_chunks), dim3(SELECT_THREADS), (size_t)SEL_CAND_CAP * 8,
+                     st, sp);
+  return hipGetLastError();
 }
 
 hipError_t launch_select(const SelectParams& sp, int nitems, hipStream_t st) {

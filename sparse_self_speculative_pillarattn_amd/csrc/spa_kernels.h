@@ -79,6 +79,16 @@ struct SelectParams {
   int32_t* idx_out;
   const uint32_t* hist;   // [slots][HIST_BINS] counts of the selected rows, or null
   int bm_bits;            // LDS position bitmap of long rows (select_bitmap_bits), 0 for none
+  // Chunked long rows (n_chunks records; 0 for none).  The per-row launch's
+  // workgroups of chunked rows return at once; the count and chunk launches
+  // run one workgroup per chunk record.
+  const SelChunk* chunks;
+  int32_t n_sel, n_chunks;
+  uint32_t* cand_n;       // [hist slots] boundary-bin keys appended (cleared by the attention launch)
+  uint32_t* row_info;     // [hist slots][4]: boundary bin << HIST_SHIFT, rank in it, its count
+  uint32_t* cand_key;     // [hist slots][SEL_CAND_CAP]
+  int32_t* cand_pos;      // [hist slots][SEL_CAND_CAP]
+  uint32_t* cnt_above;    // [n_chunks] keys above the boundary bin in each chunk
   // When set, the launch stores done_val there as it starts (the post-pass
   // before it was the call's last reader of the pinned plan).
   uint64_t* done;
@@ -115,6 +125,8 @@ hipError_t launch_attn(const AttnParams& p, int dtype, int head_dim, int nitems,
 hipError_t launch_post(const PostParams& p, int dtype, int head_dim, int nitems, size_t smem,
                        hipStream_t st);
 hipError_t launch_select(const SelectParams& sp, int nitems, hipStream_t st);
+hipError_t launch_select_count(const SelectParams& sp, hipStream_t st);
+hipError_t launch_select_chunks(const SelectParams& sp, hipStream_t st);
 int select_bitmap_bits(int max_len);
 // LDS bytes of the recallable-index launch for the longest context of a batch.
 size_t recall_smem_bytes(int max_len);

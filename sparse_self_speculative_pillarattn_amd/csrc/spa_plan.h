@@ -120,5 +120,21 @@ constexpr int MERGE_ROWS = 8;          // rows per merge item
 constexpr int SELECT_SPAN = 8192;      // scores a selection workgroup keeps in registers
 constexpr int HIST_BINS = 2048;        // averaged-score histogram of a selected row: bits 30..20
 constexpr int HIST_SHIFT = 20;
+// Rows longer than SEL_CHUNKED_MIN scores, in a call whose attention launch
+// counted their histograms, are selected by one workgroup per SELECT_SPAN-score
+// chunk: a count launch (keys above the histogram's boundary bin per chunk,
+// the bin's keys appended to the row's candidates), then the selection launch
+// (the candidates ranked, each chunk's positions written at its offset).  A
+// row keeps at most SEL_CAND_CAP boundary-bin keys; with more, one workgroup
+// selects it alone.
+constexpr int SEL_CHUNKED_MIN = 4 * SELECT_SPAN;
+constexpr int SEL_CAND_CAP = 2048;
+// One chunk of a long selected row: selection record `sel`, positions
+// [chunk * SELECT_SPAN, (chunk + 1) * SELECT_SPAN).  A row's chunks are
+// consecutive records, chunk 0 first.
+struct SelChunk {
+  int32_t sel;
+  int32_t chunk;
+};
 
 }  // namespace spa

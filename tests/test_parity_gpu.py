@@ -175,6 +175,70 @@ def test_long_row_tie_across_the_kth_score(oracle, K):
             assert set(tied) <= set(seg[g].tolist()), (g, seg[g])
 
 
+# chunk edges of a 40,000-score row (position 39,999 is visible to the last
+# averaged row only, so its score would not tie)
+CHUNK_EDGES = [8191, 8192, 16383, 16384, 24575, 24576, 32767, 32768, 39998]
+
+
+@pytest.mark.parametrize("n_tied,K", [(12, 5), (12, 15), (300, 150), (300, 305)])
+def test_chunked_long_row_ties(oracle, n_tied, K):
+    """A 40,000-token verify request, longer than 32,768 scores, is selected
+    by one workgroup per 8192-score chunk.  Its n_tied highest scores tie, at
+    positions spread over every chunk and on the chunks' edges, so each chunk
+    must know how many tied positions the earlier chunks took.  With K below
+    n_tied the lowest K tied positions are taken; above it, all of them and the
+    next highest.  Twelve tied keys are ranked by one wave; three hundred are
+    more than a wave ranks directly and are walked digit by digit in LDS."""
+    L = 40000
+    w = synth.Workload(name=f"chunk-tie-{n_tied}-{K}", batch=2, num_qo_heads=8, num_kv_heads=2,
+                       head_dim=128, dtype="bf16", spec_k=2, sparsity=Fraction(1, 20),
+                       lengths=("fixed", L), n_verify=1, seed=93)
+    b = synth.make_batch(w)
+    r = int(np.nonzero(b.is_verify)[0][0])
+    rng = np.random.default_rng(n_tied)
+    rest = rng.choice(np.setdiff1d(np.arange(L - 2), CHUNK_EDGES), n_tied - len(CHUNK_EDGES),
+                      replace=False)
+    tied = sorted(CHUNK_EDGES + [int(x) for x in rest])
+    slot = int(b.page_table[r, tied[0]])
+    b.page_table[r, torch.tensor(tied)] = slot
+    G, d = w.num_qo_heads // w.num_kv_heads, w.head_dim
+    qr = b.q[b.q_indptr[r]:b.q_indptr[r + 1]].float()
+    for g in range(w.num_kv_heads):
+        u = qr[:, g * G:(g + 1) * G].reshape(-1, d).mean(dim=0)
+        b.k_pool[slot, g] = (8.0 * d ** 0.5 * u / u.norm()).to(b.k_pool.dtype)
+    b.idx_count[r] = K
+    print(f"[case] chunked tie n={n_tied} K={K} r={r} slot={slot}", flush=True)
+    ref = oracle.step(**parity.oracle_inputs(b))
+    gpu = run_unified(b.to(DEV))
+    parity.compare_step(oracle, b, gpu, ref)
+    seg = to_np(gpu["idx"])[b.idx_off[r]:b.idx_off[r] + w.num_kv_heads * K].reshape(w.num_kv_heads, K)
+    for g in range(w.num_kv_heads):
+        if K < len(tied):
+            assert seg[g].tolist() == tied[:K], (g, seg[g][:20])
+        else:
+            assert set(tied) <= set(seg[g].tolist()), g
+
+
+def test_chunked_long_row_all_scores_tied(oracle):
+    """Every position of a 40,000-token verify request reads one K/V slot:
+    the boundary bin holds more keys than a chunked row keeps as candidates,
+    so the row's first chunk workgroup selects it alone; the lowest positions
+    are kept."""
+    L = 40000
+    w = synth.Workload(name="chunk-tied", batch=2, num_qo_heads=8, num_kv_heads=2, head_dim=128,
+                       dtype="bf16", spec_k=2, sparsity=Fraction(1, 20), lengths=("fixed", L),
+                       n_verify=1, seed=78)
+    b = synth.make_batch(w)
+    r = int(np.nonzero(b.is_verify)[0][0])
+    b.page_table[r, :L] = b.page_table[r, 0]
+    ref = oracle.step(**parity.oracle_inputs(b))
+    gpu = run_unified(b.to(DEV))
+    parity.compare_step(oracle, b, gpu, ref)
+    K = b.idx_count[r]
+    seg = to_np(gpu["idx"])[b.idx_off[r]:b.idx_off[r] + w.num_kv_heads * K].reshape(w.num_kv_heads, K)
+    assert np.array_equal(seg, np.tile(np.arange(K), (w.num_kv_heads, 1)))
+
+
 def test_topk_count_extremes(oracle):
     """K = 1 and K = L per verify request."""
     w = synth.Workload(name="kext", batch=2, num_qo_heads=8, num_kv_heads=2, head_dim=128,
