@@ -1,6 +1,7 @@
 // kernels.hip -- device code of libspa for gfx950 (CDNA4).
 //
-// A unified step is up to three launches on the caller's stream (pages: the
+// A unified step is three launches on the caller's stream, five with rows
+// longer than 32,768 scores (pages: the
 // SparseSpec review, 核心方法 -> PillarAttn and "Unified batch scheduler +
 // fused attention kernel"):
 // attn_kernel    persistent workgroups draw plan items from a ticket counter:
@@ -19,6 +20,10 @@
 //                in 1024-position items, counted into a per-(r, g) histogram.
 // select_kernel  one workgroup per verify (r, g): the top-K by a radix select
 //                seeded by that histogram, written ascending.
+// select_count_kernel, select_chunk_kernel  rows longer than 32,768 scores,
+//                one workgroup per 8192-score chunk: counts above the
+//                histogram's boundary bin and that bin's keys, then each
+//                chunk's positions written at its offset in the list.
 // release_kernel one thread that marks a plan buffer free when no other launch
 //                of the call does.
 // recall_kernel, quality_kernel  the neighbours of the step: index lists with
