@@ -239,6 +239,16 @@ def test_chunked_long_row_all_scores_tied(oracle):
     assert np.array_equal(seg, np.tile(np.arange(K), (w.num_kv_heads, 1)))
 
 
+def test_chunked_long_rows_with_overlap(oracle):
+    """Rows selected in chunks while the drafts run as a second attention
+    launch on a side stream (the overlap option): the count and chunk launches
+    follow the post-pass on the caller's stream."""
+    w = synth.Workload(name="chunk-overlap", batch=5, num_qo_heads=8, num_kv_heads=2, head_dim=128,
+                       dtype="bf16", spec_k=2, sparsity=Fraction(1, 20), lengths=("fixed", 36001),
+                       n_verify=2, seed=95)
+    check(oracle, w, opts=bd.Options(overlap=True))
+
+
 def test_topk_count_extremes(oracle):
     """K = 1 and K = L per verify request."""
     w = synth.Workload(name="kext", batch=2, num_qo_heads=8, num_kv_heads=2, head_dim=128,

@@ -32,8 +32,11 @@ def _static_outputs(b, bufs):
 
 @pytest.mark.gpu
 def test_static_workspace_matches_caller_workspace(oracle):
-    shapes = [(12, ("uniform", 2000, 6000), 3, 81), (5, ("uniform", 300, 1500), 2, 82)]
-    for B, lengths, nv, seed in shapes:  # the second call is the smaller batch
+    # each call's batch is smaller than the one before; the first holds
+    # 40,000-token verify requests, whose rows are selected in chunks
+    shapes = [(3, ("fixed", 40000), 2, 80), (12, ("uniform", 2000, 6000), 3, 81),
+              (5, ("uniform", 300, 1500), 2, 82)]
+    for B, lengths, nv, seed in shapes:
         w = synth.Workload(name=f"static{seed}", batch=B, num_qo_heads=32, num_kv_heads=8,
                            head_dim=128, dtype="bf16", spec_k=8, sparsity=Fraction(1, 20),
                            lengths=lengths, n_verify=nv, seed=seed)
