@@ -59,8 +59,9 @@
  *               is used for the first time (hipMemset, torch.zeros), and every
  *               call leaves them zero again.  The rest (split-K partials,
  *               averaged scores, a device copy of the post-pass and selection
- *               work records, the selected rows' score histograms) needs no
- *               initialisation.  Calls that share one workspace must be
+ *               work records, the selected rows' score histograms, and for
+ *               rows longer than 32,768 positions their per-chunk counts and
+ *               boundary-bin candidates) needs no initialisation.  Calls that share one workspace must be
  *               ordered on one stream.
  *   Plan buffer h_plan/plan_bytes: caller-owned pinned host memory
  *               (hipHostMalloc, or a pinned torch tensor) of at least
@@ -154,9 +155,10 @@ typedef struct {
    * are skipped), recorded on the launch stream right before and after:
    * [0],[1] the attention launch (with overlap: the verify attention launch);
    * [2],[3] the post-pass launch (split-K merges and score averaging);
-   * [4],[5] the top-K selection launch; [6],[7] the draft attention launch of
-   * an overlapped unified step (on side_stream).  A launch the call does not
-   * make records nothing. */
+   * [4],[5] the top-K selection (with rows longer than 32,768 positions:
+   * its count, per-row and chunk launches together); [6],[7] the draft
+   * attention launch of an overlapped unified step (on side_stream).  A launch
+   * the call does not make records nothing. */
   void* timing[8];
   /* Optional host array [B]: request r reads page_table row
    * page_table_rows[r] instead of row r, so a caller that keeps one
