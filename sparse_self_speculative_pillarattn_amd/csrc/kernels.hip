@@ -861,34 +861,39 @@ __device__ __forceinline__ bool attn_body(const AttnParams& p, int item, char* s
 // next item, so an XCD that runs slower simply processes fewer items; with
 // one workgroup per item, workgroup i always runs on XCD i % 8 and every XCD
 // would own a fixed eighth of the work.
-// Workgroup b starts on item b without a draw: all G workgroups drawing from
-// one counter at once queue at that address, and the last got its first item
-// about 6 us after the launch began (3 us on average, measured on 512
-// workgroups).  The counter then hands out draw t = 0, 1, ...: items G, G+1,
-// ... while S = max(n - G, 0) of them last, then one past-the-end draw per
+// When two workgroups fit per CU, workgroup b starts on item b without a
+// draw: all G workgroups drawing from one counter at once queue at that
+// address, and the last got its first item about 6 us after the launch began
+// (3 us on average, measured on 512 workgroups).  With F such first items
+// (min(G, n), or none), the counter hands out draw t = 0, 1, ...: items F,
+// F+1, ... while S = n - F of them last, then one past-the-end draw per
 // workgroup (index e = t - S).  That is S + G draws, so atomicInc wrapping at
 // S + G - 1 hands out every value once and leaves the counter at 0 for the
-// next launch that uses it.  A workgroup without a first item (b >= n) draws
-// its past-the-end ticket at once.  The draw for the next item lands in the
-// other entry of s_item, which every thread finished reading before the
-// previous iteration's closing barrier.  (Measured against drawing every item:
-// draft-only Qwen3-8B-shaped batches 11-15% faster at s <= 0.05, the mixed
-// Qwen3-1.7B, Qwen3-8B and long-context steps 0.6-1.5% faster, the
-// Qwen3-14B-shaped step 1.5% slower.  Mapping draws to items in the consumer
-// wave instead of here made both Qwen3 steps 5% slower.)
+// next launch that uses it.  A workgroup without a first item (b >= F) draws
+// at once.  The draw for the next item lands in the other entry of s_item,
+// which every thread finished reading before the previous iteration's closing
+// barrier.  (Measured against drawing every item: draft-only Qwen3-8B-shaped
+// batches 11-15% faster at s <= 0.05, the mixed Qwen3-1.7B, Qwen3-8B and
+// long-context steps 0.6-1.5% faster; the Qwen3-14B-shaped step, one
+// workgroup per CU, 1.3% slower, so such launches draw every item.  Mapping
+// draws to items in the consumer wave instead of here made both Qwen3 steps
+// 5% slower.)
 template <int D, typename T, int GM>
 __device__ __forceinline__ void attn_loop(const AttnParams& p, char* smem) {
   __shared__ int s_item[2];
-  const int G = (int)gridDim.x, n = p.n_items, S = max(n - G, 0);
+  // F workgroups start on their own item (none when the launch draws every
+  // item); the counter hands out the S = n - F others, then G past-the-end
+  // draws
+  const int G = (int)gridDim.x, n = p.n_items, F = p.first_static ? min(G, n) : 0, S = n - F;
   const uint32_t wrap = (uint32_t)(S + G) - 1u;
-  const bool static_first = (int)blockIdx.x < n;
+  const bool static_first = (int)blockIdx.x < F;
   if (!static_first) {
     if (threadIdx.x == 0) s_item[0] = (int)atomicInc(p.ticket, wrap);
     __syncthreads();
   }
   for (int k = 0, first = static_first ? 1 : 0;; k ^= 1, first = 0) {
     const int t = first ? 0 : s_item[k];
-    const int item = first ? (int)blockIdx.x : (t < S ? G + t : n + (t - S));
+    const int item = first ? (int)blockIdx.x : (t < S ? F + t : n + (t - S));
     if (item >= n) {  // the same value for the whole workgroup
       // Out of work.  Every workgroup draws exactly one ticket past the last
       // item; the first half of those draws (workgroups that run out while
@@ -2172,6 +2177,9 @@ hipError_t launch_attn(const AttnParams& params, int dtype, int head_dim, int ni
   if (nitems == 0) return hipSuccess;
   AttnParams p = params;
   p.n_items = nitems;
+  // workgroups start on their own item when two fit per CU (measured; with one
+  // workgroup per CU, drawing every item was 1.5% faster)
+  p.first_static = nthr <= 256 ? 1 : 0;
   if (dtype == 0) {
     if (head_dim == 128) return launch_attn_g<128, uint16_t>(p, nitems, nthr, smem, draft, st);
     return launch_attn_g<64, uint16_t>(p, nitems, nthr, smem, draft, st);

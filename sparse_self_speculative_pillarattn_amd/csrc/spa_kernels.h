@@ -25,6 +25,7 @@ struct AttnParams {
   float sm_scale;
   uint32_t* ticket;    // item counter of this launch (workspace; zero before, zero after)
   int32_t n_items;     // records at items; set by launch_attn
+  int32_t first_static;  // workgroup b starts on item b without a draw; set by launch_attn
   // The post-pass and selection records of the call, copied by this launch
   // from the pinned plan into the workspace (plan_n16 16-byte pieces; 0 = no
   // copy), so that the short launches after it read them from device memory.
