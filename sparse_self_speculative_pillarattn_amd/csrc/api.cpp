@@ -93,7 +93,7 @@ struct Plan {
   int n_hist = 0;  // selected rows with a score histogram (all of them when the call has attention)
   int max_sel_len = 0;  // longest selected row
   int max_row_sel_len = 0;  // longest row selected by one workgroup
-  int n_chunks = 0;  // chunks of the long rows selected in chunks (SEL_CHUNKED_MIN)
+  int n_chunks = 0;  // chunks of the long rows selected in chunks (sel_chunked)
   int n_chunked_rows = 0;  // selected rows of those
   int64_t part_rows = 0;
   int64_t pbar_elems = 0;
@@ -102,10 +102,10 @@ struct Plan {
   size_t h_items = 0, h_items_d = 0, h_post = 0, h_post_d = 0, h_sel = 0, h_chunks = 0, h_bytes = 0;
   // workspace layout (work counters at offset 0)
   size_t off_part_o = 0, off_part_ml = 0, off_pbar = 0, off_plan = 0, off_hist = 0, total = 0;
-  // chunked long-row selection: candidate counts (cleared with the
-  // histograms), row boundaries, the chunks' counts above the boundary bin,
-  // the candidates
-  size_t hist_zero_bytes = 0, off_row_info = 0, off_cnt_above = 0, off_cand_key = 0, off_cand_pos = 0;
+  // chunked long-row selection: row boundaries, each chunk's counts above and
+  // in the boundary bin, each chunk's candidates
+  size_t hist_zero_bytes = 0, off_row_info = 0, off_cnt_above = 0, off_cnt_bin = 0, off_cand_key = 0,
+         off_cand_pos = 0;
   int nthr = 256;
   size_t smem = 0;
 };
@@ -322,7 +322,7 @@ int32_t plan_size(const Shape& s, const std::vector<Req>& rq, bool attn, bool to
         // the histogram is cleared by the attention launch, so only a call
         // with one keeps it
         if (attn) pl->n_hist += Hkv;
-        if (attn && q.L > SEL_CHUNKED_MIN) {
+        if (attn && sel_chunked(q.L)) {
           pl->n_chunks += Hkv * ((q.L + SELECT_SPAN - 1) / SELECT_SPAN);
           pl->n_chunked_rows += Hkv;
         }
@@ -391,7 +391,6 @@ int32_t plan_size(const Shape& s, const std::vector<Req>& rq, bool attn, bool to
   if (attn || topk) w = align_up(w + (pl->h_bytes - pl->h_post), 256);
   pl->off_hist = w;
   w += (size_t)pl->n_hist * HIST_BINS * 4;
-  if (pl->n_chunks > 0) w += (size_t)pl->n_hist * 4;  // candidate counts, cleared with the histograms
   w = align_up(w, 16);
   pl->hist_zero_bytes = w - pl->off_hist;
   w = align_up(w, 256);
@@ -400,10 +399,12 @@ int32_t plan_size(const Shape& s, const std::vector<Req>& rq, bool attn, bool to
     w = align_up(w + (size_t)pl->n_hist * 16, 256);
     pl->off_cnt_above = w;
     w = align_up(w + (size_t)pl->n_chunks * 4, 256);
+    pl->off_cnt_bin = w;
+    w = align_up(w + (size_t)pl->n_chunks * 4, 256);
     pl->off_cand_key = w;
-    w = align_up(w + (size_t)pl->n_hist * SEL_CAND_CAP * 4, 256);
+    w = align_up(w + (size_t)pl->n_chunks * SEL_CAND_CAP * 4, 256);
     pl->off_cand_pos = w;
-    w = align_up(w + (size_t)pl->n_hist * SEL_CAND_CAP * 4, 256);
+    w = align_up(w + (size_t)pl->n_chunks * SEL_CAND_CAP * 4, 256);
   }
   pl->total = w;
   return SPA_OK;
@@ -488,8 +489,11 @@ void plan_write(const Shape& s, const std::vector<Req>& rq, const Plan& pl, char
         a.pbar_off = pbar;
         a.hist_slot = pl.n_hist > 0 ? nh++ : -1;
         sel[ns++] = a;
-        if (pl.n_chunks > 0 && q.L > SEL_CHUNKED_MIN)
-          for (int c = 0; c * SELECT_SPAN < q.L; ++c) chunks[nck++] = SelChunk{ns - 1, c};
+        if (pl.n_chunks > 0 && sel_chunked(q.L)) {
+          const int first = nck, n = (q.L + SELECT_SPAN - 1) / SELECT_SPAN;
+          for (int c = 0; c < n; ++c)
+            chunks[nck++] = SelChunk{c, first, n, q.L, q.nlist, a.hist_slot, a.pbar_off, a.idx_off};
+        }
         for (int pidx = 0; pidx < nparts; ++pidx) {
           a.j0 = pidx * AVG_SPAN;
           a.j1 = std::min(q.L, (pidx + 1) * AVG_SPAN);
@@ -787,9 +791,9 @@ int32_t run(const Shape& s, const std::vector<Req>& rq, const Plan& pl, const Bu
     sp.n_sel = pl.n_sel;
     sp.n_chunks = chunked ? pl.n_chunks : 0;
     sp.chunks = reinterpret_cast<const SelChunk*>(ws + pl.off_plan + (pl.h_chunks - pl.h_post));
-    sp.cand_n = reinterpret_cast<uint32_t*>(ws + pl.off_hist + (size_t)pl.n_hist * HIST_BINS * 4);
     sp.row_info = reinterpret_cast<uint32_t*>(ws + pl.off_row_info);
     sp.cnt_above = reinterpret_cast<uint32_t*>(ws + pl.off_cnt_above);
+    sp.cnt_bin = reinterpret_cast<uint32_t*>(ws + pl.off_cnt_bin);
     sp.cand_key = reinterpret_cast<uint32_t*>(ws + pl.off_cand_key);
     sp.cand_pos = reinterpret_cast<int32_t*>(ws + pl.off_cand_pos);
     // without an attention launch, the post-pass before it read the pinned records last

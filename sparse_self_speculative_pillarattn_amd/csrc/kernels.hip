@@ -1095,6 +1095,9 @@ __device__ __forceinline__ uint32_t row_or_u32(uint32_t v) {
 }
 
 constexpr int SELECT_FINISH = 64;  // candidates ranked directly by one wave
+constexpr int SELECT_THREADS = 1024;  // every selection workgroup
+constexpr int HIST_PER = HIST_BINS / SELECT_THREADS;  // histogram bins per thread
+static_assert(HIST_PER * SELECT_THREADS == HIST_BINS, "bins split evenly");
 constexpr int SELECT_BITMAP_BITS = 1 << 18;  // longest row whose selected positions are marked in LDS
 
 // Bits of the selection launch's position bitmap for rows of at most max_len
@@ -1104,6 +1107,43 @@ int select_bitmap_bits(int max_len) {
   return std::min((max_len + 31) / 32 * 32, SELECT_BITMAP_BITS);
 }
 constexpr int SELECT_BATCH = 4;    // chunks loaded per batch when a row is longer than one chunk
+
+// The boundary bin of the K-th largest key from a row's histogram: sv[0] =
+// bin << HIST_SHIFT, sv[1] = K minus the keys in higher bins (the K-th key's
+// rank inside the bin), sv[2] = the keys in the bin, or 0xffffffff when no bin
+// holds the K-th key (inconsistent counts).
+__device__ __forceinline__ void hist_boundary(const uint32_t* hist, int K, uint32_t* sv, uint32_t* wsum) {
+  const int tid = threadIdx.x;
+  if (tid == 0) {
+    sv[0] = 0u;
+    sv[1] = (uint32_t)K;
+    sv[2] = 0xffffffffu;
+  }
+  // thread t holds bins 2047 - HIST_PER t down to 2048 - HIST_PER (t + 1)
+  const int b0 = HIST_BINS - 1 - HIST_PER * tid;
+  uint32_t hv[HIST_PER];
+  uint32_t mine = 0u;
+#pragma unroll
+  for (int b = 0; b < HIST_PER; ++b) {
+    hv[b] = hist[b0 - b];
+    mine += hv[b];
+  }
+  uint32_t tot;
+  const uint32_t above = block_exclusive_scan(mine, wsum, &tot);
+  if (above < (uint32_t)K && above + mine >= (uint32_t)K) {  // one thread owns the K-th key
+    uint32_t acc = above;
+#pragma unroll
+    for (int b = 0; b < HIST_PER; ++b) {
+      if (acc < (uint32_t)K && acc + hv[b] >= (uint32_t)K) {
+        sv[0] = (uint32_t)(b0 - b) << HIST_SHIFT;
+        sv[1] = (uint32_t)K - acc;
+        sv[2] = hv[b];
+      }
+      acc += hv[b];
+    }
+  }
+  __syncthreads();
+}
 
 // Top-K of L non-negative fp32 scores (their bit patterns order like the
 // values).  MSB-first radix select with 4-bit digits finds the K-th largest
@@ -1194,33 +1234,9 @@ __device__ __forceinline__ void select_topk(const float* scores, int L, int K, i
   int shift;
   uint32_t mask;
   if (hist) {
-    // thread t sums bins 2047 - per t down to 2048 - per (t + 1); the scan
-    // then counts the keys in every higher bin
-    if (tid == 0) {  // stands only if no bin holds the K-th key (inconsistent input)
-      sv[0] = 0u;
-      sv[1] = (uint32_t)K;
-      sv[2] = 0xffffffffu;
-    }
-    const int per = HIST_BINS / nthr;
-    const int b0 = HIST_BINS - 1 - per * tid;
-    uint32_t mine = 0u;
-    for (int b = 0; b < per; ++b) mine += hist[b0 - b];
-    uint32_t tot;
-    const uint32_t above = block_exclusive_scan(mine, wsum, &tot);
-    if (above < (uint32_t)K && above + mine >= (uint32_t)K) {  // one thread owns the K-th key
-      uint32_t acc_above = above;
-      for (int b = 0; b < per; ++b) {
-        const uint32_t c = hist[b0 - b];
-        if (acc_above + c >= (uint32_t)K) {
-          sv[0] = (uint32_t)(b0 - b) << HIST_SHIFT;
-          sv[1] = (uint32_t)K - acc_above;
-          sv[2] = c;
-          break;
-        }
-        acc_above += c;
-      }
-    }
-    __syncthreads();
+    // the bin of the K-th key fixes bits 30..20 (a bin count of 0xffffffff,
+    // when no bin holds it, sends the walk through every digit below)
+    hist_boundary(hist, K, sv, wsum);
     shift = HIST_SHIFT - 4;
     mask = 0xffffffffu << HIST_SHIFT;
   } else {
@@ -1662,44 +1678,10 @@ __global__ void __launch_bounds__(POST_THREADS) post_kernel(PostParams p) {
 }
 
 // Selection launch: one workgroup per verify (request, KV head).
-constexpr int SELECT_THREADS = 1024;
 constexpr int SELECT_KPT = 8;  // keys per thread kept in registers (8192 at 1024 threads)
 static_assert(SELECT_THREADS * SELECT_KPT == SELECT_SPAN, "scores kept in registers");
 
 // ---- long rows, one workgroup per SELECT_SPAN-score chunk --------------------
-// The boundary bin of the K-th largest key from a row's histogram: sv[0] =
-// bin << HIST_SHIFT, sv[1] = K minus the keys in higher bins (the K-th key's
-// rank inside the bin), sv[2] = the keys in the bin, or 0xffffffff when no bin
-// holds the K-th key (inconsistent counts).
-__device__ __forceinline__ void hist_boundary(const uint32_t* hist, int K, uint32_t* sv, uint32_t* wsum) {
-  const int tid = threadIdx.x, nthr = blockDim.x;
-  if (tid == 0) {
-    sv[0] = 0u;
-    sv[1] = (uint32_t)K;
-    sv[2] = 0xffffffffu;
-  }
-  const int per = HIST_BINS / nthr;
-  const int b0 = HIST_BINS - 1 - per * tid;
-  uint32_t mine = 0u;
-  for (int b = 0; b < per; ++b) mine += hist[b0 - b];
-  uint32_t tot;
-  const uint32_t above = block_exclusive_scan(mine, wsum, &tot);
-  if (above < (uint32_t)K && above + mine >= (uint32_t)K) {  // one thread owns the K-th key
-    uint32_t acc = above;
-    for (int b = 0; b < per; ++b) {
-      const uint32_t c = hist[b0 - b];
-      if (acc + c >= (uint32_t)K) {
-        sv[0] = (uint32_t)(b0 - b) << HIST_SHIFT;
-        sv[1] = (uint32_t)K - acc;
-        sv[2] = c;
-        break;
-      }
-      acc += c;
-    }
-  }
-  __syncthreads();
-}
-
 // The SELECT_KPT consecutive keys of thread t in the chunk starting at c0,
 // their loads in flight together; positions at or past L read as key 0.  The
 // row starts 16-byte aligned and its storage extends to L rounded up to a
@@ -1721,26 +1703,26 @@ __device__ __forceinline__ void chunk_keys(const float* scores, int L, int c0, u
 }
 
 // Count launch: chunk record blockIdx.x counts its keys above the boundary
-// bin and appends the bin's keys (with their positions) to the row's
-// candidates; chunk 0 also records the boundary for the selection launch.
+// bin and in it, and stores the bin's keys (with their positions) in its own
+// candidate region; chunk 0 also records the boundary for the selection
+// launch.
 __global__ void __launch_bounds__(SELECT_THREADS) select_count_kernel(SelectParams sp) {
   __shared__ uint32_t sv[8];
   __shared__ uint32_t wsum[16];
-  const int tid = threadIdx.x;
-  const SelChunk c = sp.chunks[blockIdx.x];
-  const PostItem it = sp.items[c.sel];
+  const int tid = threadIdx.x, rec = (int)blockIdx.x;
+  const SelChunk c = sp.chunks[rec];
   const int c0 = c.chunk * SELECT_SPAN;
   uint32_t key[SELECT_KPT];
-  chunk_keys(sp.pbar + it.pbar_off, it.L, c0, key);  // in flight with the histogram's loads
-  hist_boundary(sp.hist + (int64_t)it.hist_slot * HIST_BINS, it.K, sv, wsum);
+  chunk_keys(sp.pbar + c.pbar_off, c.L, c0, key);  // in flight with the histogram's loads
+  hist_boundary(sp.hist + (int64_t)c.hist_slot * HIST_BINS, c.K, sv, wsum);
   const uint32_t bin = sv[0] >> HIST_SHIFT;
   const bool ok = sv[2] != 0xffffffffu;
-  if (c.chunk == 0 && tid < 3) sp.row_info[(int64_t)it.hist_slot * 4 + tid] = sv[tid];
+  if (c.chunk == 0 && tid < 3) sp.row_info[(int64_t)c.hist_slot * 4 + tid] = sv[tid];
   const int j0 = c0 + SELECT_KPT * tid;
   uint32_t n_above = 0u, n_bin = 0u;
 #pragma unroll
   for (int m = 0; m < SELECT_KPT; ++m)
-    if (j0 + m < it.L) {
+    if (j0 + m < c.L) {
       const uint32_t b = key[m] >> HIST_SHIFT;
       n_above += b > bin ? 1u : 0u;
       n_bin += b == bin ? 1u : 0u;
@@ -1749,17 +1731,16 @@ __global__ void __launch_bounds__(SELECT_THREADS) select_count_kernel(SelectPara
   uint32_t tot;
   const uint32_t pre = block_exclusive_scan(n_above | (n_bin << 16), wsum, &tot);
   if (tid == 0) {
-    sp.cnt_above[blockIdx.x] = tot & 0xffffu;
-    sv[3] = ok ? atomicAdd(&sp.cand_n[it.hist_slot], tot >> 16) : 0u;
+    sp.cnt_above[rec] = tot & 0xffffu;
+    sp.cnt_bin[rec] = tot >> 16;
   }
-  __syncthreads();
-  if (!ok) return;
-  uint32_t pos = sv[3] + (pre >> 16);
-  uint32_t* ck = sp.cand_key + (int64_t)it.hist_slot * SEL_CAND_CAP;
-  int32_t* cp = sp.cand_pos + (int64_t)it.hist_slot * SEL_CAND_CAP;
+  if (!ok) return;  // the selection launch then selects the row by one workgroup
+  uint32_t pos = pre >> 16;
+  uint32_t* ck = sp.cand_key + (int64_t)rec * SEL_CAND_CAP;
+  int32_t* cp = sp.cand_pos + (int64_t)rec * SEL_CAND_CAP;
 #pragma unroll
   for (int m = 0; m < SELECT_KPT; ++m)
-    if (j0 + m < it.L && (key[m] >> HIST_SHIFT) == bin) {
+    if (j0 + m < c.L && (key[m] >> HIST_SHIFT) == bin) {
       if (pos < (uint32_t)SEL_CAND_CAP) {
         ck[pos] = key[m];
         cp[pos] = j0 + m;
@@ -1769,33 +1750,76 @@ __global__ void __launch_bounds__(SELECT_THREADS) select_count_kernel(SelectPara
 }
 
 // Selection launch, chunk record `rec` of a long row: the row's candidates
-// give the K-th key tau and how many keys equal to it are kept (lowest
-// positions first); the chunk's positions above tau, and its share of those
-// equal to it, go to the list at the offset the earlier chunks leave.
+// (every chunk's region, gathered into LDS) give the K-th key tau and how many
+// keys equal to it are kept (lowest positions first); the chunk's positions
+// above tau, and its share of those equal to it, go to the list at the offset
+// the earlier chunks leave.
 __device__ __forceinline__ void select_chunk(const SelectParams& sp, int rec, char* smem, char* dyn) {
   uint32_t* sv = reinterpret_cast<uint32_t*>(smem);
   uint32_t* wsum = sv + 8;
   uint32_t* cnt16 = wsum + 16;
+  // dynamic LDS: the row's candidate keys and positions, then each chunk's
+  // candidate offset and count
+  uint32_t* ck = reinterpret_cast<uint32_t*>(dyn);
+  int32_t* cp = reinterpret_cast<int32_t*>(dyn + SEL_CAND_CAP * 4);
+  uint32_t* coff = reinterpret_cast<uint32_t*>(dyn + SEL_CAND_CAP * 8);
+  uint32_t* ccnt = coff + SEL_MAX_ROW_CHUNKS;
   const int tid = threadIdx.x, nthr = blockDim.x, lane = tid & 63, wave = tid >> 6;
   const SelChunk c = sp.chunks[rec];
-  const PostItem it = sp.items[c.sel];
-  const float* scores = sp.pbar + it.pbar_off;
-  int32_t* out = sp.idx_out + it.idx_off;
+  const float* scores = sp.pbar + c.pbar_off;
+  int32_t* out = sp.idx_out + c.idx_off;
   const int c0 = c.chunk * SELECT_SPAN;
   uint32_t key[SELECT_KPT];
-  chunk_keys(scores, it.L, c0, key);  // in flight while the candidates are ranked
-  const uint32_t* ri = sp.row_info + (int64_t)it.hist_slot * 4;
+  chunk_keys(scores, c.L, c0, key);  // in flight while the candidates are ranked
+  const uint32_t* ri = sp.row_info + (int64_t)c.hist_slot * 4;
   uint32_t prefix = ri[0], rem = ri[1];
   const uint32_t hcnt = ri[2];
-  const uint32_t nc = sp.cand_n[it.hist_slot];
+  // The row's chunk counts give each chunk's candidate offset, the row's
+  // candidate count nc and the keys above the bin in earlier chunks.  A row of
+  // at most 64 chunks has them in every wave's lanes, without block barriers;
+  // a longer one takes one chunk per thread and two block scans.
+  uint32_t nc, above_b;
+  const bool in_wave = c.n <= 64;
+  uint32_t cbv = 0u, offv = 0u;  // lane l: chunk l's count and offset (rows of at most 64 chunks)
+  if (in_wave) {
+    cbv = lane < c.n ? sp.cnt_bin[c.first + lane] : 0u;
+    const uint32_t ca = lane < c.chunk ? sp.cnt_above[c.first + lane] : 0u;
+    const uint32_t incl = wave_incl_scan(cbv);
+    offv = incl - cbv;
+    nc = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+    above_b = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(ca), 63);
+  } else {
+    uint32_t cb = 0u, ca = 0u;
+    if (tid < c.n) {
+      cb = sp.cnt_bin[c.first + tid];
+      ca = sp.cnt_above[c.first + tid];
+    }
+    const uint32_t off = block_exclusive_scan(cb, wsum, &nc);
+    if (tid < c.n) {
+      coff[tid] = off;
+      ccnt[tid] = cb;
+    }
+    (void)block_exclusive_scan(tid < c.chunk ? ca : 0u, wsum, &above_b);
+  }
   if (hcnt == 0xffffffffu || nc != hcnt || nc > (uint32_t)SEL_CAND_CAP) {
     // too many keys in the boundary bin (or counts that disagree): the row's
     // first chunk selects the whole row alone, by the full radix walk
-    if (c.chunk == 0) select_topk<SELECT_KPT>(scores, it.L, it.K, out, smem);
+    if (c.chunk == 0) select_topk<SELECT_KPT>(scores, c.L, c.K, out, smem);
     return;
   }
-  const uint32_t* gk = sp.cand_key + (int64_t)it.hist_slot * SEL_CAND_CAP;
-  const int32_t* gp = sp.cand_pos + (int64_t)it.hist_slot * SEL_CAND_CAP;
+  // gather: wave w copies the regions of chunks w, w + 16, ...
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  for (int ci = wv; ci < c.n; ci += nthr >> 6) {
+    const uint32_t o = in_wave ? (uint32_t)__builtin_amdgcn_readlane((int)offv, ci) : coff[ci];
+    const uint32_t n = in_wave ? (uint32_t)__builtin_amdgcn_readlane((int)cbv, ci) : ccnt[ci];
+    const uint32_t* gk = sp.cand_key + (int64_t)(c.first + ci) * SEL_CAND_CAP;
+    const int32_t* gp = sp.cand_pos + (int64_t)(c.first + ci) * SEL_CAND_CAP;
+    for (uint32_t i = lane; i < n; i += 64) {
+      ck[o + i] = gk[i];
+      cp[o + i] = gp[i];
+    }
+  }
+  __syncthreads();
   if (nc <= 64u) {
     // one wave ranks the candidates directly
     if (wave == 0) {
@@ -1803,8 +1827,8 @@ __device__ __forceinline__ void select_chunk(const SelectParams& sp, int rec, ch
         sv[4] = 0u;
         sv[5] = 0u;
       }
-      const uint32_t mk = lane < (int)nc ? gk[lane] : 0u;
-      const int mp = lane < (int)nc ? gp[lane] : 0x7fffffff;
+      const uint32_t mk = lane < (int)nc ? ck[lane] : 0u;
+      const int mp = lane < (int)nc ? cp[lane] : 0x7fffffff;
       uint32_t gt = 0u, eq = 0u;
       for (int j = 0; j < (int)nc; ++j) {
         const uint32_t o = (uint32_t)__builtin_amdgcn_readlane((int)mk, j);
@@ -1827,13 +1851,7 @@ __device__ __forceinline__ void select_chunk(const SelectParams& sp, int rec, ch
     }
     __syncthreads();
   } else {
-    // 4-bit digits below the bin, counted in LDS over the staged candidates
-    uint32_t* ck = reinterpret_cast<uint32_t*>(dyn);
-    int32_t* cp = reinterpret_cast<int32_t*>(dyn + SEL_CAND_CAP * 4);
-    for (int i = tid; i < (int)nc; i += nthr) {
-      ck[i] = gk[i];
-      cp[i] = gp[i];
-    }
+    // 4-bit digits below the bin, counted in LDS over the gathered candidates
     uint32_t mask = 0xffffffffu << HIST_SHIFT;
     for (int shift = HIST_SHIFT - 4; shift >= 0; shift -= 4) {
       if (tid < 16) cnt16[tid] = 0u;
@@ -1875,24 +1893,19 @@ __device__ __forceinline__ void select_chunk(const SelectParams& sp, int rec, ch
     __syncthreads();
   }
   const uint32_t tau = sv[4], eq_take = sv[5], gt_b = sv[6], eq_b = sv[7];
-  // keys above the bin in the row's earlier chunks
-  uint32_t above_m = 0u;
-  for (int i = tid; i < c.chunk; i += nthr) above_m += sp.cnt_above[rec - c.chunk + i];
-  uint32_t above_b;
-  (void)block_exclusive_scan(above_m, wsum, &above_b);
   const uint32_t base = above_b + gt_b + min(eq_b, eq_take);
   const uint32_t quota = eq_take > eq_b ? eq_take - eq_b : 0u;
   const int j0 = c0 + SELECT_KPT * tid;
   uint32_t n_eq = 0u;
 #pragma unroll
-  for (int m = 0; m < SELECT_KPT; ++m) n_eq += (j0 + m < it.L && key[m] == tau) ? 1u : 0u;
+  for (int m = 0; m < SELECT_KPT; ++m) n_eq += (j0 + m < c.L && key[m] == tau) ? 1u : 0u;
   uint32_t te;
   uint32_t eq_rank = block_exclusive_scan(n_eq, wsum, &te);  // equal keys before this thread's
   bool take[SELECT_KPT];
   uint32_t n_take = 0u;
 #pragma unroll
   for (int m = 0; m < SELECT_KPT; ++m) {
-    const bool in = j0 + m < it.L;
+    const bool in = j0 + m < c.L;
     bool t = in && key[m] > tau;
     if (in && key[m] == tau) {
       t = eq_rank < quota;
@@ -1906,7 +1919,7 @@ __device__ __forceinline__ void select_chunk(const SelectParams& sp, int rec, ch
 #pragma unroll
   for (int m = 0; m < SELECT_KPT; ++m)
     if (take[m]) {
-      if (pos < (uint32_t)it.K) out[pos] = j0 + m;
+      if (pos < (uint32_t)c.K) out[pos] = j0 + m;
       ++pos;
     }
 }
@@ -1916,7 +1929,7 @@ __device__ __forceinline__ void select_chunk(const SelectParams& sp, int rec, ch
 // selection 0.7 us).
 __global__ void __launch_bounds__(SELECT_THREADS) select_chunk_kernel(SelectParams sp) {
   __shared__ __attribute__((aligned(16))) char smem[(24 + 16 * 64 + SELECT_FINISH) * 4];
-  extern __shared__ __attribute__((aligned(16))) char dyn[];  // the row's candidate keys and positions
+  extern __shared__ __attribute__((aligned(16))) char dyn[];  // the row's candidates, chunk offsets
   select_chunk(sp, (int)blockIdx.x, smem, dyn);
 }
 
@@ -1930,7 +1943,7 @@ __global__ void __launch_bounds__(SELECT_THREADS) select_kernel(SelectParams sp)
   int32_t* cpos = sp.bm_bits > 0 ? reinterpret_cast<int32_t*>(dyn) : nullptr;
   uint32_t* bm = sp.bm_bits > 0 ? reinterpret_cast<uint32_t*>(dyn + SELECT_FINISH * 4) : nullptr;
   const PostItem it = sp.items[blockIdx.x];
-  if (sp.n_chunks > 0 && it.L > SEL_CHUNKED_MIN) return;  // the chunk launch selects it
+  if (sp.n_chunks > 0 && sel_chunked(it.L)) return;  // the chunk launches select it
   const uint32_t* hist = (sp.hist && it.hist_slot >= 0) ? sp.hist + (int64_t)it.hist_slot * HIST_BINS : nullptr;
   select_topk<SELECT_KPT>(sp.pbar + it.pbar_off, it.L, it.K, sp.idx_out + it.idx_off, smem, hist, bm, cpos,
                           sp.bm_bits);
@@ -2196,8 +2209,8 @@ hipError_t launch_select_count(const SelectParams& sp, hipStream_t st) {
 
 hipError_t launch_select_chunks(const SelectParams& sp, hipStream_t st) {
   if (sp.n_chunks == 0) return hipSuccess;
-  hipLaunchKernelGGL(select_chunk_kernel, dim3(sp.n_chunks), dim3(SELECT_THREADS), (size_t)SEL_CAND_CAP * 8,
-                     st, sp);
+  hipLaunchKernelGGL(select_chunk_kernel, dim3(sp.n_chunks), dim3(SELECT_THREADS),
+                     (size_t)SEL_CAND_CAP * 8 + (size_t)SEL_MAX_ROW_CHUNKS * 8, st, sp);
   return hipGetLastError();
 }
 

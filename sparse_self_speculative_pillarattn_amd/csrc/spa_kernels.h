@@ -85,11 +85,11 @@ struct SelectParams {
   // run one workgroup per chunk record.
   const SelChunk* chunks;
   int32_t n_sel, n_chunks;
-  uint32_t* cand_n;       // [hist slots] boundary-bin keys appended (cleared by the attention launch)
   uint32_t* row_info;     // [hist slots][4]: boundary bin << HIST_SHIFT, rank in it, its count
-  uint32_t* cand_key;     // [hist slots][SEL_CAND_CAP]
-  int32_t* cand_pos;      // [hist slots][SEL_CAND_CAP]
+  uint32_t* cand_key;     // [n_chunks][SEL_CAND_CAP] each chunk's boundary-bin keys
+  int32_t* cand_pos;      // [n_chunks][SEL_CAND_CAP] and their positions
   uint32_t* cnt_above;    // [n_chunks] keys above the boundary bin in each chunk
+  uint32_t* cnt_bin;      // [n_chunks] keys in the boundary bin in each chunk
   // When set, the launch stores done_val there as it starts (the post-pass
   // before it was the call's last reader of the pinned plan).
   uint64_t* done;

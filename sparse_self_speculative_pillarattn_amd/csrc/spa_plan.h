@@ -120,21 +120,34 @@ constexpr int MERGE_ROWS = 8;          // rows per merge item
 constexpr int SELECT_SPAN = 8192;      // scores a selection workgroup keeps in registers
 constexpr int HIST_BINS = 2048;        // averaged-score histogram of a selected row: bits 30..20
 constexpr int HIST_SHIFT = 20;
-// Rows longer than SEL_CHUNKED_MIN scores, in a call whose attention launch
-// counted their histograms, are selected by one workgroup per SELECT_SPAN-score
-// chunk: a count launch (keys above the histogram's boundary bin per chunk,
-// the bin's keys appended to the row's candidates), then the selection launch
-// (the candidates ranked, each chunk's positions written at its offset).  A
-// row keeps at most SEL_CAND_CAP boundary-bin keys; with more, one workgroup
-// selects it alone.
+// Rows longer than SEL_CHUNKED_MIN scores (and of at most SEL_MAX_ROW_CHUNKS
+// chunks), in a call whose attention launch counted their histograms, are
+// selected by one workgroup per SELECT_SPAN-score chunk: a count launch (each
+// chunk counts its keys above the histogram's boundary bin and stores the
+// bin's keys in a region of its own), then the selection launch (the row's
+// candidates gathered and ranked, each chunk's positions written at its
+// offset).  A row keeps at most SEL_CAND_CAP boundary-bin keys; with more, one
+// workgroup selects it alone.
 constexpr int SEL_CHUNKED_MIN = 4 * SELECT_SPAN;
 constexpr int SEL_CAND_CAP = 2048;
-// One chunk of a long selected row: selection record `sel`, positions
-// [chunk * SELECT_SPAN, (chunk + 1) * SELECT_SPAN).  A row's chunks are
-// consecutive records, chunk 0 first.
+constexpr int SEL_MAX_ROW_CHUNKS = 1024;  // one per thread of a selection workgroup
+// One chunk of a long selected row, positions [chunk * SELECT_SPAN,
+// (chunk + 1) * SELECT_SPAN), with the row's fields that both launches need.
+// A row's n chunks are consecutive records, chunk 0 (record `first`) first.
 struct SelChunk {
-  int32_t sel;
   int32_t chunk;
+  int32_t first;
+  int32_t n;
+  int32_t L;          // the row's scores
+  int32_t K;          // its list length
+  int32_t hist_slot;  // its histogram, boundary record and candidate counts
+  int64_t pbar_off;   // its averaged scores
+  int64_t idx_off;    // its list
 };
+static_assert(sizeof(SelChunk) == 40, "chunk record layout");
+// Whether a row of L scores with a histogram is selected in chunks.
+__host__ __device__ constexpr bool sel_chunked(int L) {
+  return L > SEL_CHUNKED_MIN && (L + SELECT_SPAN - 1) / SELECT_SPAN <= SEL_MAX_ROW_CHUNKS;
+}
 
 }  // namespace spa
