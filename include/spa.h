@@ -60,9 +60,9 @@
  *               call leaves them zero again.  The rest (split-K partials,
  *               averaged scores, a device copy of the post-pass and selection
  *               work records, the selected rows' score histograms, and for
- *               rows of 32,769 to 8,388,608 positions their per-chunk counts
- *               and boundary-bin candidates, 16 KiB per 8192 positions) needs
- *               no initialisation.  Calls that share one workspace must be
+ *               rows longer than 32,768 positions their per-chunk counts and
+ *               boundary-bin candidates, 16 KiB per 8192 positions) needs no
+ *               initialisation.  Calls that share one workspace must be
  *               ordered on one stream.
  *   Plan buffer h_plan/plan_bytes: caller-owned pinned host memory
  *               (hipHostMalloc, or a pinned torch tensor) of at least

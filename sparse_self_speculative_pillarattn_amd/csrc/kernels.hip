@@ -1758,12 +1758,9 @@ __device__ __forceinline__ void select_chunk(const SelectParams& sp, int rec, ch
   uint32_t* sv = reinterpret_cast<uint32_t*>(smem);
   uint32_t* wsum = sv + 8;
   uint32_t* cnt16 = wsum + 16;
-  // dynamic LDS: the row's candidate keys and positions, then each chunk's
-  // candidate offset and count
+  // dynamic LDS: the row's candidate keys and positions
   uint32_t* ck = reinterpret_cast<uint32_t*>(dyn);
   int32_t* cp = reinterpret_cast<int32_t*>(dyn + SEL_CAND_CAP * 4);
-  uint32_t* coff = reinterpret_cast<uint32_t*>(dyn + SEL_CAND_CAP * 8);
-  uint32_t* ccnt = coff + SEL_MAX_ROW_CHUNKS;
   const int tid = threadIdx.x, nthr = blockDim.x, lane = tid & 63, wave = tid >> 6;
   const SelChunk c = sp.chunks[rec];
   const float* scores = sp.pbar + c.pbar_off;
@@ -1774,33 +1771,15 @@ __device__ __forceinline__ void select_chunk(const SelectParams& sp, int rec, ch
   const uint32_t* ri = sp.row_info + (int64_t)c.hist_slot * 4;
   uint32_t prefix = ri[0], rem = ri[1];
   const uint32_t hcnt = ri[2];
-  // The row's chunk counts give each chunk's candidate offset, the row's
-  // candidate count nc and the keys above the bin in earlier chunks.  A row of
-  // at most 64 chunks has them in every wave's lanes, without block barriers;
-  // a longer one takes one chunk per thread and two block scans.
-  uint32_t nc, above_b;
-  const bool in_wave = c.n <= 64;
-  uint32_t cbv = 0u, offv = 0u;  // lane l: chunk l's count and offset (rows of at most 64 chunks)
-  if (in_wave) {
-    cbv = lane < c.n ? sp.cnt_bin[c.first + lane] : 0u;
-    const uint32_t ca = lane < c.chunk ? sp.cnt_above[c.first + lane] : 0u;
-    const uint32_t incl = wave_incl_scan(cbv);
-    offv = incl - cbv;
-    nc = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
-    above_b = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(ca), 63);
-  } else {
-    uint32_t cb = 0u, ca = 0u;
-    if (tid < c.n) {
-      cb = sp.cnt_bin[c.first + tid];
-      ca = sp.cnt_above[c.first + tid];
-    }
-    const uint32_t off = block_exclusive_scan(cb, wsum, &nc);
-    if (tid < c.n) {
-      coff[tid] = off;
-      ccnt[tid] = cb;
-    }
-    (void)block_exclusive_scan(tid < c.chunk ? ca : 0u, wsum, &above_b);
-  }
+  // The row's chunk counts (at most 64 chunks: lane l of every wave holds
+  // chunk l's) give each chunk's candidate offset, the row's candidate count
+  // nc and the keys above the bin in earlier chunks, without block barriers.
+  const uint32_t cbv = lane < c.n ? sp.cnt_bin[c.first + lane] : 0u;
+  const uint32_t ca = lane < c.chunk ? sp.cnt_above[c.first + lane] : 0u;
+  const uint32_t incl = wave_incl_scan(cbv);
+  const uint32_t offv = incl - cbv;
+  const uint32_t nc = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+  const uint32_t above_b = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(ca), 63);
   if (hcnt == 0xffffffffu || nc != hcnt || nc > (uint32_t)SEL_CAND_CAP) {
     // too many keys in the boundary bin (or counts that disagree): the row's
     // first chunk selects the whole row alone, by the full radix walk
@@ -1810,8 +1789,8 @@ __device__ __forceinline__ void select_chunk(const SelectParams& sp, int rec, ch
   // gather: wave w copies the regions of chunks w, w + 16, ...
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   for (int ci = wv; ci < c.n; ci += nthr >> 6) {
-    const uint32_t o = in_wave ? (uint32_t)__builtin_amdgcn_readlane((int)offv, ci) : coff[ci];
-    const uint32_t n = in_wave ? (uint32_t)__builtin_amdgcn_readlane((int)cbv, ci) : ccnt[ci];
+    const uint32_t o = (uint32_t)__builtin_amdgcn_readlane((int)offv, ci);
+    const uint32_t n = (uint32_t)__builtin_amdgcn_readlane((int)cbv, ci);
     const uint32_t* gk = sp.cand_key + (int64_t)(c.first + ci) * SEL_CAND_CAP;
     const int32_t* gp = sp.cand_pos + (int64_t)(c.first + ci) * SEL_CAND_CAP;
     for (uint32_t i = lane; i < n; i += 64) {
@@ -1929,7 +1908,7 @@ __device__ __forceinline__ void select_chunk(const SelectParams& sp, int rec, ch
 // selection 0.7 us).
 __global__ void __launch_bounds__(SELECT_THREADS) select_chunk_kernel(SelectParams sp) {
   __shared__ __attribute__((aligned(16))) char smem[(24 + 16 * 64 + SELECT_FINISH) * 4];
-  extern __shared__ __attribute__((aligned(16))) char dyn[];  // the row's candidates, chunk offsets
+  extern __shared__ __attribute__((aligned(16))) char dyn[];  // the row's candidate keys and positions
   select_chunk(sp, (int)blockIdx.x, smem, dyn);
 }
 
@@ -2209,8 +2188,8 @@ hipError_t launch_select_count(const SelectParams& sp, hipStream_t st) {
 
 hipError_t launch_select_chunks(const SelectParams& sp, hipStream_t st) {
   if (sp.n_chunks == 0) return hipSuccess;
-  hipLaunchKernelGGL(select_chunk_kernel, dim3(sp.n_chunks), dim3(SELECT_THREADS),
-                     (size_t)SEL_CAND_CAP * 8 + (size_t)SEL_MAX_ROW_CHUNKS * 8, st, sp);
+  hipLaunchKernelGGL(select_chunk_kernel, dim3(sp.n_chunks), dim3(SELECT_THREADS), (size_t)SEL_CAND_CAP * 8,
+                     st, sp);
   return hipGetLastError();
 }
 

@@ -120,8 +120,8 @@ constexpr int MERGE_ROWS = 8;          // rows per merge item
 constexpr int SELECT_SPAN = 8192;      // scores a selection workgroup keeps in registers
 constexpr int HIST_BINS = 2048;        // averaged-score histogram of a selected row: bits 30..20
 constexpr int HIST_SHIFT = 20;
-// Rows longer than SEL_CHUNKED_MIN scores (and of at most SEL_MAX_ROW_CHUNKS
-// chunks), in a call whose attention launch counted their histograms, are
+// Rows longer than SEL_CHUNKED_MIN scores, in a call whose attention launch
+// counted their histograms, are
 // selected by one workgroup per SELECT_SPAN-score chunk: a count launch (each
 // chunk counts its keys above the histogram's boundary bin and stores the
 // bin's keys in a region of its own), then the selection launch (the row's
@@ -130,7 +130,11 @@ constexpr int HIST_SHIFT = 20;
 // workgroup selects it alone.
 constexpr int SEL_CHUNKED_MIN = 4 * SELECT_SPAN;
 constexpr int SEL_CAND_CAP = 2048;
-constexpr int SEL_MAX_ROW_CHUNKS = 1024;  // one per thread of a selection workgroup
+// A verify row is at most MAX_MERGE_CHUNKS * VERIFY_MAX_CHUNK positions, so a
+// chunked row has at most 64 chunks: one per lane of a wave.
+constexpr int SEL_MAX_ROW_CHUNKS = 64;
+static_assert((int64_t)MAX_MERGE_CHUNKS * VERIFY_MAX_CHUNK <= (int64_t)SEL_MAX_ROW_CHUNKS * SELECT_SPAN,
+              "every verify row fits the chunked selection");
 // One chunk of a long selected row, positions [chunk * SELECT_SPAN,
 // (chunk + 1) * SELECT_SPAN), with the row's fields that both launches need.
 // A row's n chunks are consecutive records, chunk 0 (record `first`) first.
@@ -147,7 +151,7 @@ struct SelChunk {
 static_assert(sizeof(SelChunk) == 40, "chunk record layout");
 // Whether a row of L scores with a histogram is selected in chunks.
 __host__ __device__ constexpr bool sel_chunked(int L) {
-  return L > SEL_CHUNKED_MIN && (L + SELECT_SPAN - 1) / SELECT_SPAN <= SEL_MAX_ROW_CHUNKS;
+  return L > SEL_CHUNKED_MIN && L <= SEL_MAX_ROW_CHUNKS * SELECT_SPAN;
 }
 
 }  // namespace spa

@@ -225,6 +225,19 @@ def test_light_verify_load_with_a_very_long_request_is_planned(lib):
         assert need > 0, (L, lib.spa_last_error())
 
 
+def test_verify_row_beyond_the_split_k_limit_is_refused(lib):
+    """524,288 positions (256 split-K chunks of 2048) is the longest verify
+    row; one position more is refused before anything is enqueued."""
+    lay = _lay(page_table_stride=1 << 20)
+    ver = np.array([1], np.uint8)
+    for L, ok in ((1 << 19, True), ((1 << 19) + 1, False)):
+        lens = np.array([L], np.int32)
+        cnt = np.array([L // 50], np.int32)
+        need = _sizes(lib, lay, 1, 4, ver, lens, cnt)[0]
+        assert (need > 0) == ok, (L, lib.spa_last_error())
+    assert b"256 split-K chunks" in lib.spa_last_error()
+
+
 def test_unpinned_plan_buffer_is_rejected(lib):
     """A plan buffer the device cannot read (ordinary host memory) is refused
     before anything is enqueued."""

@@ -239,6 +239,18 @@ def test_chunked_long_row_all_scores_tied(oracle):
     assert np.array_equal(seg, np.tile(np.arange(K), (w.num_kv_heads, 1)))
 
 
+def test_chunked_row_of_the_longest_verify(oracle):
+    """The longest verify row the split-K merge takes (256 chunks of 2048
+    positions, 524,288 scores) is 64 selection chunks, one per lane of the
+    wave that scans the chunks' counts.  One KV head of 64 dimensions keeps
+    the oracle's work small."""
+    L = 524288
+    w = synth.Workload(name=f"chunks-{L}", batch=2, num_qo_heads=2, num_kv_heads=1, head_dim=64,
+                       dtype="bf16", spec_k=2, sparsity=Fraction(1, 50), lengths=("fixed", L),
+                       n_verify=1, seed=288)
+    check(oracle, w)
+
+
 def test_chunked_long_rows_with_overlap(oracle):
     """Rows selected in chunks while the drafts run as a second attention
     launch on a side stream (the overlap option): the count and chunk launches
