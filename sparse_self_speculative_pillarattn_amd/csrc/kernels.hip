@@ -1709,11 +1709,12 @@ __device__ __forceinline__ void chunk_keys(const float* scores, int L, int c0, u
 __global__ void __launch_bounds__(SELECT_THREADS) select_count_kernel(SelectParams sp) {
   __shared__ uint32_t sv[8];
   __shared__ uint32_t wsum[16];
-  const int tid = threadIdx.x, rec = (int)blockIdx.x;
+  const int tid = threadIdx.x, rec = (int)blockIdx.x, lane = tid & 63, wave = tid >> 6;
   const SelChunk c = sp.chunks[rec];
   const int c0 = c.chunk * SELECT_SPAN;
   uint32_t key[SELECT_KPT];
   chunk_keys(sp.pbar + c.pbar_off, c.L, c0, key);  // in flight with the histogram's loads
+  if (tid == 0) sv[3] = 0u;  // candidates appended (published by the boundary's barriers)
   hist_boundary(sp.hist + (int64_t)c.hist_slot * HIST_BINS, c.K, sv, wsum);
   const uint32_t bin = sv[0] >> HIST_SHIFT;
   const bool ok = sv[2] != 0xffffffffu;
@@ -1727,26 +1728,31 @@ __global__ void __launch_bounds__(SELECT_THREADS) select_count_kernel(SelectPara
       n_above += b > bin ? 1u : 0u;
       n_bin += b == bin ? 1u : 0u;
     }
-  // both counts in one scan (each at most SELECT_SPAN per chunk)
-  uint32_t tot;
-  const uint32_t pre = block_exclusive_scan(n_above | (n_bin << 16), wsum, &tot);
+  // the bin's keys go to the chunk's region in any order (their ranking
+  // does not depend on it), through an LDS counter
+  if (ok && n_bin != 0u) {
+    uint32_t* ck = sp.cand_key + (int64_t)rec * SEL_CAND_CAP;
+    int32_t* cp = sp.cand_pos + (int64_t)rec * SEL_CAND_CAP;
+#pragma unroll
+    for (int m = 0; m < SELECT_KPT; ++m)
+      if (j0 + m < c.L && (key[m] >> HIST_SHIFT) == bin) {
+        const uint32_t pos = atomicAdd(&sv[3], 1u);
+        if (pos < (uint32_t)SEL_CAND_CAP) {
+          ck[pos] = key[m];
+          cp[pos] = j0 + m;
+        }
+      }
+  }
+  // both counts summed over the block in one word (each at most SELECT_SPAN)
+  const uint32_t wtot = wave_incl_scan(n_above | (n_bin << 16));
+  if (lane == 63) wsum[wave] = wtot;
+  __syncthreads();
   if (tid == 0) {
+    uint32_t tot = 0u;
+    for (int w = 0; w < (int)(blockDim.x >> 6); ++w) tot += wsum[w];
     sp.cnt_above[rec] = tot & 0xffffu;
     sp.cnt_bin[rec] = tot >> 16;
   }
-  if (!ok) return;  // the selection launch then selects the row by one workgroup
-  uint32_t pos = pre >> 16;
-  uint32_t* ck = sp.cand_key + (int64_t)rec * SEL_CAND_CAP;
-  int32_t* cp = sp.cand_pos + (int64_t)rec * SEL_CAND_CAP;
-#pragma unroll
-  for (int m = 0; m < SELECT_KPT; ++m)
-    if (j0 + m < c.L && (key[m] >> HIST_SHIFT) == bin) {
-      if (pos < (uint32_t)SEL_CAND_CAP) {
-        ck[pos] = key[m];
-        cp[pos] = j0 + m;
-      }
-      ++pos;
-    }
 }
 
 // Selection launch, chunk record `rec` of a long row: the row's candidates
@@ -1803,6 +1809,7 @@ __device__ __forceinline__ void select_chunk(const SelectParams& sp, int rec, ch
     // one wave ranks the candidates directly
     if (wave == 0) {
       if (lane == 0) {  // stands only if no lane holds the K-th key (inconsistent input)
+        sv[3] = 0xffffffffu;
         sv[4] = 0u;
         sv[5] = 0u;
       }
@@ -1814,8 +1821,9 @@ __device__ __forceinline__ void select_chunk(const SelectParams& sp, int rec, ch
         gt += o > mk ? 1u : 0u;
         eq += o == mk ? 1u : 0u;
       }
-      // lanes holding the K-th key (equal keys agree on both values)
+      // lanes holding the K-th key (equal keys agree on all three values)
       if (lane < (int)nc && gt < rem && gt + eq >= rem) {
+        sv[3] = eq;
         sv[4] = mk;
         sv[5] = rem - gt;
       }
@@ -1840,9 +1848,11 @@ __device__ __forceinline__ void select_chunk(const SelectParams& sp, int rec, ch
       __syncthreads();
       if (tid == 0) {
         uint32_t acc = 0u;
+        sv[3] = 0xffffffffu;  // stands only if no digit holds the K-th key
         for (int d = 15; d >= 0; --d) {
           const uint32_t n = cnt16[d];
           if (acc + n >= rem) {
+            sv[3] = n;  // after the last digit: the row's keys equal to tau
             sv[4] = prefix | ((uint32_t)d << shift);
             sv[5] = rem - acc;
             break;
@@ -1871,15 +1881,19 @@ __device__ __forceinline__ void select_chunk(const SelectParams& sp, int rec, ch
     }
     __syncthreads();
   }
-  const uint32_t tau = sv[4], eq_take = sv[5], gt_b = sv[6], eq_b = sv[7];
+  const uint32_t tau = sv[4], eq_take = sv[5], gt_b = sv[6], eq_b = sv[7], eq_all = sv[3];
   const uint32_t base = above_b + gt_b + min(eq_b, eq_take);
   const uint32_t quota = eq_take > eq_b ? eq_take - eq_b : 0u;
   const int j0 = c0 + SELECT_KPT * tid;
-  uint32_t n_eq = 0u;
+  // equal keys before this thread's; not needed when the row keeps all of them
+  uint32_t eq_rank = 0u;
+  if (eq_take < eq_all) {
+    uint32_t n_eq = 0u;
 #pragma unroll
-  for (int m = 0; m < SELECT_KPT; ++m) n_eq += (j0 + m < c.L && key[m] == tau) ? 1u : 0u;
-  uint32_t te;
-  uint32_t eq_rank = block_exclusive_scan(n_eq, wsum, &te);  // equal keys before this thread's
+    for (int m = 0; m < SELECT_KPT; ++m) n_eq += (j0 + m < c.L && key[m] == tau) ? 1u : 0u;
+    uint32_t te;
+    eq_rank = block_exclusive_scan(n_eq, wsum, &te);
+  }
   bool take[SELECT_KPT];
   uint32_t n_take = 0u;
 #pragma unroll
