@@ -251,6 +251,16 @@ def test_chunked_row_of_the_longest_verify(oracle):
     check(oracle, w)
 
 
+def test_chunked_long_rows_fp32(oracle):
+    """Rows selected in chunks on the fp32 path: two verify requests of
+    47,661 and 38,684 scores (six and five chunks, the last ones partial),
+    from the VALU attention tile's logits."""
+    w = synth.Workload(name="chunk-f32", batch=4, num_qo_heads=4, num_kv_heads=2, head_dim=64,
+                       dtype="f32", spec_k=2, sparsity=Fraction(1, 20),
+                       lengths=("uniform", 36001, 49153), n_verify=2, seed=97)
+    check(oracle, w)
+
+
 def test_chunked_long_rows_with_overlap(oracle):
     """Rows selected in chunks while the drafts run as a second attention
     launch on a side stream (the overlap option): the count and chunk launches
