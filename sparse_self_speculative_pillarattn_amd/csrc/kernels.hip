@@ -1496,7 +1496,7 @@ __device__ __forceinline__ float load_logit(const float* src) {
 }
 
 constexpr int POST_THREADS = 256;
-constexpr int AVG_PREFETCH = 8;  // averaged terms whose logits load before the LSE rebuild
+constexpr int AVG_PREFETCH = 12;  // averaged terms whose logits load before the LSE rebuild (of 4-16)
 
 // Dynamic LDS of an averaging item: the LSE (4 B) and logits row offset (8 B)
 // of every averaged term, then the row's 2048-bin score histogram.
