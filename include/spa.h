@@ -129,10 +129,12 @@ typedef struct {
  * defaults.  Results do not depend on the work split beyond floating-point
  * summation order. */
 typedef struct {
-  /* Positions per verify work item (split-K chunk), 0 or 1..2048.  0: 2048
-   * when the batch's verify positions times H_kv reach 5120 per compute unit
-   * (num_cus below), else 512 (doubled while a request would need more than
-   * 256 chunks). */
+  /* Positions per verify work item (split-K chunk), 0 or 1..2048.  0: the
+   * longest of 2048, 1536 and 1024 that gives the batch's verify requests at
+   * least two items per resident attention workgroup (two workgroups per
+   * compute unit, num_cus below, when (k+1) * H_q / H_kv <= 48 on bf16, else
+   * one), else 512; lengthened up to 2048 while a request would need more
+   * than 256 chunks. */
   int32_t verify_chunk;
   /* List entries per draft work item, 0 or 1..2048; 0: 1024. */
   int32_t draft_chunk;

@@ -200,29 +200,38 @@ int32_t check_segments(std::vector<std::pair<int64_t, int64_t>> seg, const char*
   return SPA_OK;
 }
 
-// Positions per verify item.  Unless set in the options: 2048 when the verify
-// requests bring at least two and a half such chunks per CU (positions times
-// KV heads over the options' CU count), else 512.  Measured in steady state
-// (200 steps after 60 warm-up, best of three interleaved runs), 2048 / 1024 /
-// 512-position chunks: Qwen3-8B-shaped batch (3584 positions per CU)
-// 190.6 / 192.5 / 187.0 us, Qwen3-1.7B-shaped (1438) 86.3 at 1024, 83.3 at
-// 512, Qwen3-14B-shaped (7191) 551 / 571 / 609 us, long context (6466) 356 /
-// 358 us (768: 364).  Short chunks spread a light verify load over the chip
-// and shorten the launch's tail; heavy loads keep the long chunks, which need
-// fewer split-K partials and merges.
-int verify_chunk(const std::vector<Req>& rq, int Hkv, const Opts& o) {
+// Positions per verify item.  Unless set in the options: the longest of 2048,
+// 1536 and 1024 positions that still gives the verify requests at least two
+// items per resident attention workgroup (two per CU when a workgroup has at
+// most four waves, that is at most 48 query rows per KV head on the MFMA
+// path; one otherwise), else 512.  Long chunks need fewer split-K partials and
+// merges; enough items let workgroups that finish early take more, which
+// shortens the launch's tail.  Measured (steady state, same box): Qwen3-8B
+// shape 179.5 us at 512 (640: 182.9, 768: 186.9, 1024: 192.2), Qwen3-14B
+// shape best at 2048, long context 294.1 us at 2048 and 289.5 at 1536; the
+// rule picks 512, 2048 and 1536 for them.  Only the verify requests count, so
+// a verify-only call and a mixed one split alike.
+int verify_chunk(const std::vector<Req>& rq, int Hkv, int rows_v, int G, bool bf16, const Opts& o) {
   if (o.verify_chunk > 0) return o.verify_chunk;
-  int64_t positions = 0;
   int longest = 0;
   for (const Req& q : rq)
-    if (q.verify) {
-      positions += q.L;
-      longest = std::max(longest, q.L);
+    if (q.verify) longest = std::max(longest, q.L);
+  const int64_t slots = (int64_t)o.num_cus * ((bf16 && rows_v * G > 48) ? 1 : 2);
+  auto items = [&](int c) {
+    int64_t n = 0;
+    for (const Req& q : rq)
+      if (q.verify) n += (int64_t)((q.L + c - 1) / c) * Hkv * (bf16 ? 1 : rows_v);
+    return n;
+  };
+  int c = MIN_AUTO_VERIFY_CHUNK;
+  for (const int cand : {DEFAULT_VERIFY_CHUNK, 1536, 1024})
+    if (items(cand) >= 2 * slots) {
+      c = cand;
+      break;
     }
-  const int64_t per_cu = positions * Hkv / o.num_cus;
-  int c = 2 * per_cu >= 5 * (int64_t)DEFAULT_VERIFY_CHUNK ? DEFAULT_VERIFY_CHUNK : MIN_AUTO_VERIFY_CHUNK;
   // a request may not need more split-K chunks than a merge takes
-  while (c < DEFAULT_VERIFY_CHUNK && (longest + c - 1) / c > MAX_MERGE_CHUNKS) c *= 2;
+  while (c < DEFAULT_VERIFY_CHUNK && (longest + c - 1) / c > MAX_MERGE_CHUNKS)
+    c = std::min(2 * c, DEFAULT_VERIFY_CHUNK);
   return c;
 }
 
@@ -238,7 +247,7 @@ int32_t plan_size(const Shape& s, const std::vector<Req>& rq, bool attn, bool to
   const int rows_v = s.k + 1;
   const bool bf16 = s.dtype == SPA_BF16;
   const int esz = bf16 ? 2 : 4;
-  const int CV = verify_chunk(rq, Hkv, o), CD = o.draft_chunk;
+  const int CV = verify_chunk(rq, Hkv, s.k + 1, G, s.dtype == SPA_BF16, o), CD = o.draft_chunk;
   pl->cv = CV;
   pl->cd = CD;
   if (s.k > 255) return fail(SPA_ERR_UNSUPPORTED, "spec_k above 255");
