@@ -213,6 +213,29 @@ def test_workspace_holds_a_histogram_per_selected_row(lib):
     assert need([1, 1]) - need([1, 0]) >= lay.num_kv_heads * 2048 * 4
 
 
+@pytest.mark.parametrize("lens,want", [
+    ([8192] * 14, 512),          # 14 x 16 x 8 = 1792 items at 512, 896 at 1024 (< 2 x 512)
+    ([80558, 126350], 1536),     # 1088 items at 1536 (>= 1024), 816 at 2048
+    ([13500] * 20, 2048),        # 7 x 20 x 8 = 1120 items at 2048 with one workgroup per CU
+])
+def test_automatic_verify_chunk(lib, lens, want):
+    """The automatic verify chunk is the longest of 2048, 1536 and 1024 that
+    gives at least two verify items per resident attention workgroup (two per
+    CU up to 48 query rows per KV head, one above), else 512: the workspace
+    equals the one planned with that chunk given explicitly."""
+    G = 5 if want == 2048 else 4    # (k+1) G = 45 rows or more: one workgroup per CU
+    k = 12 if want == 2048 else 8
+    lay = _lay(num_qo_heads=8 * G, num_kv_heads=8, page_table_stride=1 << 17)
+    B = len(lens)
+    args = (B, k, [1] * B, lens, [max(1, L // 20) for L in lens])
+    auto = _sizes(lib, lay, *args)
+    assert auto[0] > 0, lib.spa_last_error()
+    assert auto == _sizes(lib, lay, *args, opts=bd.SpaOptions(verify_chunk=want))
+    for other in (512, 1024, 1536, 2048):
+        if other != want:
+            assert _sizes(lib, lay, *args, opts=bd.SpaOptions(verify_chunk=other)) != auto, other
+
+
 def test_light_verify_load_with_a_very_long_request_is_planned(lib):
     """A light verify load gets 512-position chunks, but not so many that one
     request needs more than the 256 split-K chunks a merge takes: a lone
