@@ -236,6 +236,26 @@ def test_automatic_verify_chunk(lib, lens, want):
             assert _sizes(lib, lay, *args, opts=bd.SpaOptions(verify_chunk=other)) != auto, other
 
 
+def test_draft_packing_beside_verify_items(lib):
+    """Short draft lists go two KV heads to an item while the draft items
+    still number one per CU beside verify items, or two per CU in a
+    draft-only call (Qwen3-8B shape: 114 drafts x 8 KV heads of 13-tile
+    lists; 64-byte records)."""
+    lay = _lay(num_qo_heads=32, num_kv_heads=8, page_table_stride=8192)
+    nv, nd = 14, 114
+    ver = [1] * nv + [0] * nd
+    lens = [8192] * (nv + nd)
+    cnt = [410] * (nv + nd)
+    mixed = _sizes(lib, lay, nv + nd, 8, ver, lens, cnt)[1]
+    verify_only = _sizes(lib, lay, nv, 8, ver[:nv], lens[:nv], cnt[:nv])[1]
+    draft_only = _sizes(lib, lay, nd, 8, ver[nv:], lens[nv:], cnt[nv:])[1]
+    empty = _sizes(lib, lay, 0, 8, [], [], [])[1]
+    drafts_beside_verify = (mixed - verify_only) // 64
+    drafts_alone = (draft_only - empty) // 64
+    assert abs(drafts_beside_verify - nd * 8 // 2) <= 4, drafts_beside_verify   # 456 items
+    assert abs(drafts_alone - nd * 8) <= 4, drafts_alone                        # 912 items
+
+
 def test_light_verify_load_with_a_very_long_request_is_planned(lib):
     """A light verify load gets 512-position chunks, but not so many that one
     request needs more than the 256 split-K chunks a merge takes: a lone
